@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs for the FP8 relu^2 MLP workloads.
+
+This module only draws random numbers and rounds them to bf16; it holds none
+of the method's arithmetic.  Both the HIP path (through tests and the
+benchmark) and the CPU oracle consume the same bytes from here.
+
+Recipe (one generator per tensor, seed = 1000 * workload_id + tensor_id):
+  * numpy ``Generator(PCG64(seed))`` draws fp32 standard normals, multiplied
+    by the standard deviation sigma (the second argument of N(0, sigma) is a
+    standard deviation, as in the GPT-2 style init the decomputer.nl page
+    mentions under "Wat niet werkte").
+  * "outliers x100": exactly round(0.001 * n) distinct positions, drawn
+    without replacement by a second generator (tensor id + 50), are scaled
+    by 100 in fp32.
+  * values are rounded to bf16 (round-to-nearest-even) by torch's CPU cast.
+Shapes follow the little-lm appendix configuration on the decomputer.nl page
+(hidden 3072, intermediate 12288, vocab 50257 padded to 50304, bf16).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+def _to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def normal_bf16(shape, sigma: float, seed: int, outlier_frac: float = 0.0,
+                outlier_mult: float = 100.0) -> np.ndarray:
+    """bf16 bit patterns of N(0, sigma) draws, optionally with outliers."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = int(np.prod(shape))
+    x = rng.standard_normal(n, dtype=np.float32) * np.float32(sigma)
+    if outlier_frac > 0.0:
+        k = int(round(outlier_frac * n))
+        if k > 0:
+            rng2 = np.random.Generator(np.random.PCG64(seed + 50))
+            pos = rng2.choice(n, size=k, replace=False)
+            x[pos] *= np.float32(outlier_mult)
+    return _to_bf16_bits(x).reshape(shape)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class MLPWorkload:
+    """relu^2 MLP block: X [M,d], W_up [h,d], W_down [d,h], dY [M,d]."""
+    wid: int
+    M: int
+    d: int
+    h: int
+    sigma_x: float = 1.0
+    sigma_up: float = 0.02
+    sigma_down: float = 0.02
+    sigma_dy: float = 1e-3
+    dy_outliers: float = 1e-3
+    name: str = ""
+
+    def tensors(self):
+        s = 1000 * self.wid
+        x = normal_bf16((self.M, self.d), self.sigma_x, s + 1)
+        w_up = normal_bf16((self.h, self.d), self.sigma_up, s + 2)
+        w_down = normal_bf16((self.d, self.h), self.sigma_down, s + 3)
+        dy = normal_bf16((self.M, self.d), self.sigma_dy, s + 4, self.dy_outliers)
+        return x, w_up, w_down, dy
+
+    @property
+    def flops(self) -> int:
+        """GEMM FLOPs of one fwd+bwd: six GEMMs of 2*M*d*h each."""
+        return 12 * self.M * self.d * self.h
+
+
+@dataclass
+class LinearWorkload:
+    """Single FP8 linear forward: X [M,K], W [N,K]."""
+    wid: int
+    M: int
+    N: int
+    K: int
+    sigma_x: float = 1.0
+    sigma_w: float = 0.02
+    name: str = ""
+
+    def tensors(self):
+        s = 1000 * self.wid
+        return (normal_bf16((self.M, self.K), self.sigma_x, s + 1),
+                normal_bf16((self.N, self.K), self.sigma_w, s + 2))
+
+
+@dataclass
+class ProjectionSetWorkload:
+    """All six projections of one decoder layer at M tokens (fwd+bwd)."""
+    wid: int
+    M: int
+    projections: tuple = (("q", 3072, 3072), ("k", 3072, 1024), ("v", 3072, 1024),
+                          ("o", 3072, 3072), ("up", 3072, 12288), ("down", 12288, 3072))
+    name: str = ""
+
+    def weight(self, i: int):
+        _, fin, fout = self.projections[i]
+        return normal_bf16((fout, fin), 1.0 / math.sqrt(fin), 1000 * self.wid + 11 + i)
+
+    def flops(self) -> int:
+        return 6 * self.M * sum(fin * fout for _, fin, fout in self.projections)
+
+
+@dataclass
+class LMHeadWorkload:
+    """LM head linear fwd+bwd: X [M,K], W [N,K] (rows >= n_valid zero), dLogits [M,N]."""
+    wid: int
+    M: int
+    K: int
+    N: int
+    n_valid: int = 50257
+    name: str = ""
+
+    def tensors(self):
+        s = 1000 * self.wid
+        x = normal_bf16((self.M, self.K), 1.0, s + 1)
+        w = normal_bf16((self.n_valid, self.K), 0.02, s + 2)
+        g = normal_bf16((self.M, self.n_valid), 1e-4, s + 4)
+        if self.N > self.n_valid:
+            w = np.concatenate([w, np.zeros((self.N - self.n_valid, self.K), np.uint16)], 0)
+            g = np.concatenate([g, np.zeros((self.M, self.N - self.n_valid), np.uint16)], 1)
+        return x, w, g
+
+    @property
+    def flops(self) -> int:
+        return 6 * self.M * self.K * self.N
+
+
+# The five workloads: a single linear, a small block, the 3.8B-model block,
+# the full projection set and the LM head (padded / unpadded vocabulary).
+LINEAR_SMALL = LinearWorkload(1, 256, 1024, 512, name="fp8 linear fwd 256x1024x512")
+MLP_SMALL = MLPWorkload(2, 2048, 768, 3072, sigma_up=1 / math.sqrt(768),
+                        sigma_down=1 / math.sqrt(3072), name="relu2 MLP M=2048 d=768 h=3072")
+MLP_3P8B = MLPWorkload(3, 8192, 3072, 12288, name="relu2 MLP M=8192 d=3072 h=12288")
+PROJ_SET = ProjectionSetWorkload(4, 32768, name="decoder projection set M=32768")
+LM_HEAD_PADDED = LMHeadWorkload(5, 16384, 3072, 50304, name="LM head M=16384 K=3072 N=50304")
+LM_HEAD_UNPADDED = LMHeadWorkload(5, 16384, 3072, 50257, name="LM head M=16384 K=3072 N=50257")

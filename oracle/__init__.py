@@ -1,0 +1,267 @@
+"""CPU oracle for FP8 tensorwise-scaled linears and the relu^2 MLP block.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product library
+never calls it, and it imports nothing from the product package.
+
+The arithmetic lives in ``fp8_oracle.c`` (plain C, fp64, OpenMP over output
+rows); this module loads it with ctypes and composes the block from its
+steps.  Every function takes and returns numpy arrays: bf16 tensors as
+``uint16`` bit patterns, FP8 tensors as ``uint8`` codes.
+
+Sources (the pages' statement of the method):
+  * "Het trainen van een 3.8B LLM tot 0.384 CORE voor $998" (decomputer.nl),
+    "Vroege experimenten" item 4 and the first bullet of "Doorvoer
+    verhogen": all three GEMMs of every linear (one forward, two backward)
+    in FP8 with dynamic tensorwise scaling, through a scaled matmul.
+  * Same page, "Appendix: De configuratie": non-gated relu2 MLP with a 4x
+    intermediate size, bf16 model dtype.
+  * "little-lm" summary on manulx.blog (Japanese page), FP8 paragraph: the
+    scaled matmul is torch._scaled_mm with dynamic per-tensor scales.
+Readings where the pages are silent (formats, scale formula, rounding,
+saturation, zero amax, operand layouts) are listed in the C file's header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+E4M3 = 0
+E5M2 = 1
+FMAX = {E4M3: 448.0, E5M2: 57344.0}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp8_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            i64, f32, c_int = ctypes.c_int64, ctypes.c_float, ctypes.c_int
+            vp = ctypes.c_void_p
+            lib.orc_decode.restype = ctypes.c_double
+            lib.orc_decode.argtypes = [c_int, c_int]
+            lib.orc_encode_rne.restype = c_int
+            lib.orc_encode_rne.argtypes = [c_int, ctypes.c_double]
+            lib.orc_double_to_bf16.restype = ctypes.c_uint16
+            lib.orc_double_to_bf16.argtypes = [ctypes.c_double]
+            lib.orc_double_to_bf16_array.restype = None
+            lib.orc_double_to_bf16_array.argtypes = [vp, i64, vp]
+            lib.orc_amax.restype = f32
+            lib.orc_amax.argtypes = [vp, i64, i64, i64]
+            lib.orc_scale_from_amax.restype = f32
+            lib.orc_scale_from_amax.argtypes = [f32, c_int]
+            lib.orc_cast.restype = None
+            lib.orc_cast.argtypes = [vp, i64, i64, i64, f32, c_int, vp, i64]
+            lib.orc_cast_f32.restype = None
+            lib.orc_cast_f32.argtypes = [vp, i64, f32, c_int, vp]
+            lib.orc_quant.restype = None
+            lib.orc_quant.argtypes = [vp, i64, i64, i64, c_int, vp, i64, vp, vp]
+            for name in ("orc_gemm_nt", "orc_gemm_nn", "orc_gemm_tn"):
+                fn = getattr(lib, name)
+                fn.restype = None
+                fn.argtypes = [vp, i64, c_int, f32, vp, i64, c_int, f32, i64, i64, i64, vp, i64, vp, i64]
+            lib.orc_relu2.restype = None
+            lib.orc_relu2.argtypes = [vp, i64, vp]
+            lib.orc_relu2_bwd.restype = None
+            lib.orc_relu2_bwd.argtypes = [vp, vp, i64, vp]
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+# ------------------------------------------------------------------ formats
+def decode(fmt: int, code: int) -> float:
+    return _load().orc_decode(fmt, int(code))
+
+
+def decode_table(fmt: int) -> np.ndarray:
+    return np.array([decode(fmt, c) for c in range(256)], dtype=np.float64)
+
+
+def encode_rne(fmt: int, value: float) -> int:
+    return _load().orc_encode_rne(fmt, float(value))
+
+
+def double_to_bf16(x) -> np.ndarray:
+    """Round fp64 values to bf16 (one RNE step); returns bf16 bit patterns."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_double_to_bf16_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------ quantisation
+def amax(x: np.ndarray) -> float:
+    x = _c(x, np.uint16)
+    r, c = x.shape
+    return float(_load().orc_amax(_ptr(x), r, c, c))
+
+
+def scale_from_amax(a: float, fmt: int) -> float:
+    return float(np.float32(_load().orc_scale_from_amax(np.float32(a), fmt)))
+
+
+def cast(x: np.ndarray, s: float, fmt: int) -> np.ndarray:
+    """q = RNE_fp8(clamp(RN32(x / s), +-fmax)) for a given fp32 scale s."""
+    x = _c(x, np.uint16)
+    r, c = x.shape
+    q = np.empty((r, c), dtype=np.uint8)
+    _load().orc_cast(_ptr(x), r, c, c, np.float32(s), fmt, _ptr(q), c)
+    return q
+
+
+def cast_f32(x: np.ndarray, s: float, fmt: int) -> np.ndarray:
+    x = _c(np.asarray(x, dtype=np.float32), np.float32)
+    q = np.empty(x.shape, dtype=np.uint8)
+    _load().orc_cast_f32(_ptr(x), x.size, np.float32(s), fmt, _ptr(q))
+    return q
+
+
+def quant(x: np.ndarray, fmt: int):
+    """Dynamic tensorwise quantisation: returns (codes, scale, amax)."""
+    x = _c(x, np.uint16)
+    r, c = x.shape
+    q = np.empty((r, c), dtype=np.uint8)
+    s = np.zeros(1, dtype=np.float32)
+    a = np.zeros(1, dtype=np.float32)
+    _load().orc_quant(_ptr(x), r, c, c, fmt, _ptr(q), c, _ptr(s), _ptr(a))
+    return q, float(s[0]), float(a[0])
+
+
+# ------------------------------------------------------------------- GEMMs
+def _gemm(name, a, fa, sa, b, fb, sb, M, N, K, out_rows, out_cols, rows):
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    idx = None
+    n = 0
+    if rows is not None:
+        idx = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = idx.size
+        out_rows = n
+    y = np.empty((out_rows, out_cols), dtype=np.uint16)
+    getattr(_load(), name)(_ptr(a), a.shape[1], fa, np.float32(sa), _ptr(b), b.shape[1], fb,
+                           np.float32(sb), M, N, K, _ptr(y), out_cols,
+                           None if idx is None else _ptr(idx), n)
+    return y
+
+
+def gemm_nt(a, fa, sa, b, fb, sb, rows=None):
+    """y[m,n] = RN_bf16(RN32(sa*sb) * sum_k dec(a[m,k]) dec(b[n,k]))."""
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    return _gemm("orc_gemm_nt", a, fa, sa, b, fb, sb, M, N, K, M, N, rows)
+
+
+def gemm_nn(a, fa, sa, b, fb, sb, rows=None):
+    """y[m,k] = RN_bf16(RN32(sa*sb) * sum_n dec(a[m,n]) dec(b[n,k]))."""
+    M, N = a.shape
+    N2, K = b.shape
+    assert N == N2
+    return _gemm("orc_gemm_nn", a, fa, sa, b, fb, sb, M, N, K, M, K, rows)
+
+
+def gemm_tn(a, fa, sa, b, fb, sb, rows=None):
+    """y[n,k] = RN_bf16(RN32(sa*sb) * sum_m dec(a[m,n]) dec(b[m,k]))."""
+    M, N = a.shape
+    M2, K = b.shape
+    assert M == M2
+    return _gemm("orc_gemm_tn", a, fa, sa, b, fb, sb, M, N, K, N, K, rows)
+
+
+# --------------------------------------------------------------- relu^2
+def relu2(h: np.ndarray) -> np.ndarray:
+    h = _c(h, np.uint16)
+    a = np.empty_like(h)
+    _load().orc_relu2(_ptr(h), h.size, _ptr(a))
+    return a
+
+
+def relu2_bwd(h: np.ndarray, da: np.ndarray) -> np.ndarray:
+    h = _c(h, np.uint16)
+    da = _c(da, np.uint16)
+    assert h.shape == da.shape
+    dh = np.empty_like(h)
+    _load().orc_relu2_bwd(_ptr(h), _ptr(da), h.size, _ptr(dh))
+    return dh
+
+
+# ------------------------------------------------------- FP8 linear layer
+def linear_fwd(xq, fx, sx, wq, fw, sw, rows=None):
+    """Forward GEMM of one FP8 linear: Y = X W^T (W stored [out, in])."""
+    return gemm_nt(xq, fx, sx, wq, fw, sw, rows)
+
+
+def linear_dgrad(dyq, fdy, sdy, wq, fw, sw, rows=None):
+    """Grad-input GEMM: dX = dY W."""
+    return gemm_nn(dyq, fdy, sdy, wq, fw, sw, rows)
+
+
+def linear_wgrad(dyq, fdy, sdy, xq, fx, sx, rows=None):
+    """Grad-weight GEMM: dW = dY^T X (overwrites; no accumulation)."""
+    return gemm_tn(dyq, fdy, sdy, xq, fx, sx, rows)
+
+
+# ------------------------------------------------------- relu^2 MLP block
+def mlp_fwd(x, w_up, w_down):
+    """Forward of Y = relu(X W_up^T)^2 W_down^T with FP8 on both GEMMs.
+
+    X [M,d], W_up [h,d], W_down [d,h] as bf16 bits.  Returns every stage.
+    """
+    xq, sx, _ = quant(x, E4M3)
+    uq, su, _ = quant(w_up, E4M3)
+    dq, sd, _ = quant(w_down, E4M3)
+    h = gemm_nt(xq, E4M3, sx, uq, E4M3, su)
+    a = relu2(h)
+    aq, sa, amax_a = quant(a, E4M3)
+    y = gemm_nt(aq, E4M3, sa, dq, E4M3, sd)
+    return dict(xq=xq, sx=sx, uq=uq, su=su, dq=dq, sd=sd, h=h, a=a, aq=aq, sa=sa,
+                amax_a=amax_a, y=y)
+
+
+def mlp_bwd(dy, saved):
+    """Backward of the block given dY [M,d] (bf16 bits) and the forward stages."""
+    gq, sg, _ = quant(dy, E5M2)
+    dw_down = gemm_tn(gq, E5M2, sg, saved["aq"], E4M3, saved["sa"])
+    da = gemm_nn(gq, E5M2, sg, saved["dq"], E4M3, saved["sd"])
+    dh = relu2_bwd(saved["h"], da)
+    hq, sh, amax_dh = quant(dh, E5M2)
+    dw_up = gemm_tn(hq, E5M2, sh, saved["xq"], E4M3, saved["sx"])
+    dx = gemm_nn(hq, E5M2, sh, saved["uq"], E4M3, saved["su"])
+    return dict(gq=gq, sg=sg, dw_down=dw_down, da=da, dh=dh, hq=hq, sh=sh, amax_dh=amax_dh,
+                dw_up=dw_up, dx=dx)
