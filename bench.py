@@ -1,0 +1,190 @@
+"""Benchmark: FP8 relu^2 MLP block fwd+bwd on one MI355X.
+
+One step = relu2_mlp_fwd + relu2_mlp_bwd on the 3.8B-model block
+(M=8192 tokens, d=3072, h=12288): three quantisations of the inputs, the
+relu^2 cast, the dY and dH casts and all six FP8 GEMMs, with inputs resident
+in HBM.  The metric counts GEMM FLOPs only (12*M*d*h per step), the
+convention of the pages' TFLOP/s figure.
+
+Prints one JSON line (rank 0).  --gpus > 1 is not supported: this build runs
+on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, rows_per_gemm: int = 16):
+    """Oracle GEMM rate on a bounded sample: rows_per_gemm output rows of each
+    of the six GEMMs of the block (FP8 operands from the oracle's quantiser)."""
+    import numpy as np
+
+    import oracle
+
+    x, wu, wd, dy = w.tensors()
+    t0 = time.perf_counter()
+    xq, sx, _ = oracle.quant(x, oracle.E4M3)
+    uq, su, _ = oracle.quant(wu, oracle.E4M3)
+    dq, sd, _ = oracle.quant(wd, oracle.E4M3)
+    gq, sg, _ = oracle.quant(dy, oracle.E5M2)
+    t_quant = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    rm = rng.choice(w.M, rows_per_gemm, replace=False)
+    rh = rng.choice(w.h, rows_per_gemm, replace=False)
+    rd = rng.choice(w.d, rows_per_gemm, replace=False)
+    # [M, h] stand-ins with the formats of the block's A (E4M3) and dH (E5M2)
+    aq, sa = np.ascontiguousarray(np.tile(xq, (1, w.h // w.d))), sx
+    hq_src = np.ascontiguousarray(np.tile(gq, (1, w.h // w.d)))
+    flops = 0
+    t0 = time.perf_counter()
+    oracle.gemm_nt(xq, 0, sx, uq, 0, su, rows=rm); flops += 2 * rows_per_gemm * w.h * w.d      # up fwd
+    oracle.gemm_nt(aq, 0, sa, dq, 0, sd, rows=rm); flops += 2 * rows_per_gemm * w.d * w.h      # down fwd
+    oracle.gemm_tn(gq, 1, sg, aq, 0, sa, rows=rd); flops += 2 * rows_per_gemm * w.h * w.M      # down wgrad
+    oracle.gemm_nn(gq, 1, sg, dq, 0, sd, rows=rm); flops += 2 * rows_per_gemm * w.h * w.d      # down dgrad
+    oracle.gemm_tn(hq_src, 1, sg, xq, 0, sx, rows=rh); flops += 2 * rows_per_gemm * w.d * w.M  # up wgrad
+    oracle.gemm_nn(hq_src, 1, sg, uq, 0, su, rows=rm); flops += 2 * rows_per_gemm * w.d * w.h  # up dgrad
+    t_gemm = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": flops / t_gemm / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{rows_per_gemm} output rows of each of the six GEMMs of the M={w.M} d={w.d} h={w.h} "
+                  f"block ({flops / 1e9:.1f} GFLOP, fp64 accumulation, {t_gemm:.1f} s); the four input "
+                  f"quantisations took {t_quant:.1f} s",
+        "gemm_seconds": t_gemm,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemm-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "
+              "GPU (no sharding, no collectives)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from fp8_tensorwise_scaled_amd import api, synth
+
+    w = synth.MLP_3P8B
+    M, d, h = w.M, w.d, w.h
+    dev = torch.device("cuda:0")
+    log(f"generating inputs M={M} d={d} h={h}")
+    x, wu, wd, dy = w.tensors()
+    t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    X, WU, WD, DY = t(x), t(wu), t(wd), t(dy)
+    Y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    saved = api.Relu2MlpSaved.empty(M, d, h, dev)
+    ws_f = api.relu2_mlp_fwd_workspace(M, d, h, dev)
+    ws_b = api.relu2_mlp_bwd_workspace(M, d, h, dev)
+    DX = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    DWU = torch.empty((h, d), dtype=torch.bfloat16, device=dev)
+    DWD = torch.empty((d, h), dtype=torch.bfloat16, device=dev)
+    BSC = torch.empty(2, dtype=torch.float32, device=dev)
+
+    def step():
+        api.relu2_mlp_fwd(X, WU, WD, y=Y, saved=saved, ws=ws_f)
+        api.relu2_mlp_bwd(DY, saved, dx=DX, dw_up=DWU, dw_down=DWD, bwd_scales=BSC, ws=ws_b)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = w.flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall / args.steps * 1e3:.3f} ms/step)")
+
+    # Dominant kernel: the FP8 GEMM.  Its down-projection forward instance
+    # (E4M3 x E4M3, plain bf16 store; M=8192 N=3072 K=12288) is timed on the
+    # block's own operands Aq, Dq, on the same stream, averaged over launches.
+    offs = api.workspace_layout("fwd", M, d, h)
+    aq = ws_f[offs[3]:offs[3] + M * h].view(M, h)
+    dq = ws_f[offs[2]:offs[2] + d * h].view(d, h)
+    sa, sd = saved.scales[3:4], saved.scales[2:3]
+    out = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        api.fp8_linear_fwd(aq, sa, dq, sd, out=out)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.gemm_reps):
+        api.fp8_linear_fwd(aq, sa, dq, sd, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = ev0.elapsed_time(ev1) / args.gemm_reps
+    gemm_flops = 2 * M * d * h
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    log(f"down-proj GEMM {gemm_ms * 1e3:.1f} us, {gemm_tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": "FP8 relu² MLP fwd+bwd TFLOP/s (d=3072,h=12288) and % of dense FP8 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded N(0,1) X, N(0,0.02) weights, N(0,1e-3) dY with 0.1% x100 outliers; bf16)",
+        "config": {"workload": "relu2 MLP block fwd+bwd M=8192 d=3072 h=12288", "M": M, "d": d, "h": h,
+                   "formats": "E4M3 activations/weights, E5M2 gradients, fp32 accumulate, bf16 out"},
+        "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+        "tokens_per_s_equiv": round(M / (ms * 1e-3)),
+        "roofline": {
+            "kernel": "gemm_nt_kernel<E4M3,E4M3,256,256,store> (down-projection fwd, 8192x3072x12288)",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(gemm_ms * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 6)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

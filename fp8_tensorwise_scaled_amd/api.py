@@ -1,0 +1,187 @@
+"""Python binding of the FP8 relu^2 MLP library (same names as the C ABI).
+
+Marshalling only: torch tensors provide device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  bf16
+tensors are torch.bfloat16, FP8 codes torch.uint8, scales float32 device
+scalars.  Outputs that are not given are allocated with torch.empty.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _native
+from ._native import E4M3, E5M2
+
+FMAX = {E4M3: 448.0, E5M2: 57344.0}
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU (no CPU path)")
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def fp8_amax_quant(x: torch.Tensor, fmt: int = E4M3, *, q: torch.Tensor | None = None,
+                   qt: torch.Tensor | None = None, want_q: bool = True, want_qt: bool = False,
+                   scale: torch.Tensor | None = None, amax: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None):
+    """Dynamic tensorwise quantisation of a bf16 matrix.
+
+    Returns (q, qt, scale, amax): codes [rows, cols] (or None), transposed
+    codes [cols, rows] (or None), scale and amax as 1-element float32 tensors.
+    """
+    _check_dev(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    rows, cols = x.shape
+    dev = x.device
+    if q is None and want_q:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if qt is None and want_qt:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    L = _native.lib()
+    need = L.fp8_amax_quant_workspace_bytes(rows, cols)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _native.call("fp8_amax_quant", _p(x), rows, cols, _ld(x), fmt, _p(q), 0 if q is None else _ld(q),
+                 _p(qt), 0 if qt is None else _ld(qt), _p(scale), _p(amax), _p(ws), ws.numel(), _stream())
+    return q, qt, scale, amax
+
+
+def _gemm(name, a, fa, sa, b, fb, sb, M, N, K, out, out_shape):
+    _check_dev(a, b, sa, sb)
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.bfloat16, device=a.device)
+    _native.call(name, _p(a), _ld(a), fa, _p(sa), _p(b), _ld(b), fb, _p(sb), M, N, K, _p(out), _ld(out),
+                 _stream())
+    return out
+
+
+def fp8_linear_fwd(xq, sx, wq, sw, fx: int = E4M3, fw: int = E4M3, out=None):
+    """Y[M,N] = RN_bf16(RN32(sx*sw) * Xq[M,K] . Wq[N,K]^T)."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    return _gemm("fp8_linear_fwd", xq, fx, sx, wq, fw, sw, M, N, K, out, (M, N))
+
+
+def fp8_linear_dgrad(dyq, sdy, wqt, sw, fdy: int = E5M2, fw: int = E4M3, out=None):
+    """dX[M,K] = RN_bf16(RN32(sdy*sw) * dYq[M,N] . W[N,K]); wqt = W codes transposed [K,N]."""
+    M, N = dyq.shape
+    K = wqt.shape[0]
+    return _gemm("fp8_linear_dgrad", dyq, fdy, sdy, wqt, fw, sw, M, N, K, out, (M, K))
+
+
+def fp8_linear_wgrad(dyqt, sdy, xqt, sx, fdy: int = E5M2, fx: int = E4M3, out=None):
+    """dW[N,K] = RN_bf16(RN32(sdy*sx) * dY^T . X); dyqt [N,M], xqt [K,M] transposed codes."""
+    N, M = dyqt.shape
+    K = xqt.shape[0]
+    return _gemm("fp8_linear_wgrad", dyqt, fdy, sdy, xqt, fx, sx, M, N, K, out, (N, K))
+
+
+@dataclass
+class Relu2MlpSaved:
+    """Forward quantities the backward pass reads (device tensors)."""
+    xq_t: torch.Tensor
+    uq_t: torch.Tensor
+    dq_t: torch.Tensor
+    aq_t: torch.Tensor
+    h: torch.Tensor
+    scales: torch.Tensor  # sx, su, sd, sa
+    M: int
+    d: int
+    hid: int
+
+    @staticmethod
+    def empty(M: int, d: int, h: int, device) -> "Relu2MlpSaved":
+        u8 = dict(dtype=torch.uint8, device=device)
+        return Relu2MlpSaved(torch.empty((d, M), **u8), torch.empty((d, h), **u8), torch.empty((h, d), **u8),
+                             torch.empty((h, M), **u8), torch.empty((M, h), dtype=torch.bfloat16, device=device),
+                             torch.empty(4, dtype=torch.float32, device=device), M, d, h)
+
+    def c_struct(self) -> _native.Relu2MlpSaved:
+        return _native.Relu2MlpSaved(self.xq_t.data_ptr(), self.uq_t.data_ptr(), self.dq_t.data_ptr(),
+                                     self.aq_t.data_ptr(), self.h.data_ptr(), self.scales.data_ptr())
+
+
+def relu2_mlp_fwd_workspace(M: int, d: int, h: int, device) -> torch.Tensor:
+    n = _native.lib().relu2_mlp_fwd_workspace_bytes(M, d, h)
+    if n == 0:
+        raise ValueError(f"unsupported MLP shape M={M} d={d} h={h}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def relu2_mlp_bwd_workspace(M: int, d: int, h: int, device) -> torch.Tensor:
+    n = _native.lib().relu2_mlp_bwd_workspace_bytes(M, d, h)
+    if n == 0:
+        raise ValueError(f"unsupported MLP shape M={M} d={d} h={h}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def workspace_layout(kind: str, M: int, d: int, h: int):
+    offs = (ctypes.c_size_t * 8)()
+    _native.call(f"relu2_mlp_{kind}_workspace_layout", M, d, h, offs, 8)
+    return list(offs)
+
+
+def relu2_mlp_fwd(x, w_up, w_down, *, y=None, saved: Relu2MlpSaved | None = None, ws=None):
+    """Y = relu(X W_up^T)^2 W_down^T with FP8 GEMMs.  Returns (y, saved)."""
+    _check_dev(x, w_up, w_down)
+    M, d = x.shape
+    h = w_up.shape[0]
+    if w_up.shape != (h, d) or w_down.shape != (d, h):
+        raise ValueError("shapes: x [M,d], w_up [h,d], w_down [d,h]")
+    for t in (x, w_up, w_down):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("x, w_up, w_down must be contiguous bfloat16")
+    if y is None:
+        y = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    if saved is None:
+        saved = Relu2MlpSaved.empty(M, d, h, x.device)
+    if ws is None:
+        ws = relu2_mlp_fwd_workspace(M, d, h, x.device)
+    cs = saved.c_struct()
+    _native.call("relu2_mlp_fwd", _p(x), _p(w_up), _p(w_down), M, d, h, _p(y), ctypes.byref(cs), _p(ws),
+                 ws.numel(), _stream())
+    return y, saved
+
+
+def relu2_mlp_bwd(dy, saved: Relu2MlpSaved, *, dx=None, dw_up=None, dw_down=None, bwd_scales=None, ws=None):
+    """Backward of the block.  Returns (dx, dw_up, dw_down, bwd_scales[sg, sh])."""
+    _check_dev(dy)
+    M, d, h = saved.M, saved.d, saved.hid
+    dev = dy.device
+    if dy.shape != (M, d) or dy.dtype != torch.bfloat16 or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous bfloat16 [M, d] tensor")
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, d), **bf) if dx is None else dx
+    dw_up = torch.empty((h, d), **bf) if dw_up is None else dw_up
+    dw_down = torch.empty((d, h), **bf) if dw_down is None else dw_down
+    if bwd_scales is None:
+        bwd_scales = torch.empty(2, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = relu2_mlp_bwd_workspace(M, d, h, dev)
+    cs = saved.c_struct()
+    _native.call("relu2_mlp_bwd", _p(dy), ctypes.byref(cs), M, d, h, _p(dx), _p(dw_up), _p(dw_down),
+                 _p(bwd_scales), _p(ws), ws.numel(), _stream())
+    return dx, dw_up, dw_down, bwd_scales

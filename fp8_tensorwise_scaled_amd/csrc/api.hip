@@ -1,0 +1,312 @@
+// C ABI of the FP8 tensorwise-scaled linear layer and relu^2 MLP block
+// (declarations and the numeric contract: include/fp8mlp.h).
+//
+// Every entry point validates its arguments on the host before enqueuing
+// anything, never allocates, never synchronises, and launches only on the
+// caller's stream.
+#include "../../include/fp8mlp.h"
+#include "internal.h"
+
+using namespace fp8mlp;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool a2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+bool fmt_ok(int f) { return f == FP8MLP_E4M3 || f == FP8MLP_E5M2; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8MLP_OK : FP8MLP_EHIP; }
+
+// GEMM operand tiles are addressed with 32-bit buffer offsets.
+constexpr int64_t kTileRows = 256;
+bool tile_range_ok(int64_t ld, int64_t K) { return (kTileRows - 1) * ld + K < (int64_t(1) << 31); }
+
+int check_gemm(const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8_t* b, int64_t ldb,
+               int fb, const float* sb, int64_t M, int64_t N, int64_t K, const uint16_t* c,
+               int64_t ldc) {
+  if (!a || !b || !sa || !sb || !c) return FP8MLP_EINVAL;
+  if (M <= 0 || N <= 0 || K <= 0) return FP8MLP_EINVAL;
+  if (lda < K || ldb < K || ldc < N) return FP8MLP_EINVAL;
+  if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MLP_EINVAL;
+  if (K % 16 != 0) return FP8MLP_ENOTSUP;
+  if (!a16(a) || !a16(b) || lda % 16 || ldb % 16 || !a2(c)) return FP8MLP_EALIGN;
+  if (!tile_range_ok(lda, K) || !tile_range_ok(ldb, K)) return FP8MLP_ENOTSUP;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return FP8MLP_ENOTSUP;
+  return FP8MLP_OK;
+}
+
+int run_gemm(const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8_t* b, int64_t ldb,
+             int fb, const float* sb, int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc,
+             void* stream) {
+  int st = check_gemm(a, lda, fa, sa, b, ldb, fb, sb, M, N, K, c, ldc);
+  if (st) return st;
+  GemmArgs g{};
+  g.a = a; g.b = b; g.lda = lda; g.ldb = ldb; g.fa = fa; g.fb = fb; g.sa = sa; g.sb = sb;
+  g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc; g.epi = kEpiStore;
+  return hip_status(launch_gemm(g, (hipStream_t)stream));
+}
+
+// ---- MLP workspace layouts (offsets in bytes from ws)
+enum FwdSlot { F_XQ, F_UQ, F_DQ, F_AQ, F_PX, F_PU, F_PD, F_PH, F_COUNT };
+enum BwdSlot { B_GQ, B_GQT, B_DH, B_HQ, B_HQT, B_PG, B_PDH, B_SC, B_COUNT };
+
+size_t layout_fwd(int64_t M, int64_t d, int64_t h, size_t* off) {
+  const size_t sz[F_COUNT] = {
+      (size_t)(M * d), (size_t)(h * d), (size_t)(d * h), (size_t)(M * h),
+      (size_t)amax_parts_for(M, d) * 4, (size_t)amax_parts_for(h, d) * 4,
+      (size_t)amax_parts_for(d, h) * 4, (size_t)gemm_max_tiles(M, h) * 4};
+  size_t o = 0;
+  for (int i = 0; i < F_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
+  return o;
+}
+
+size_t layout_bwd(int64_t M, int64_t d, int64_t h, size_t* off) {
+  const size_t sz[B_COUNT] = {
+      (size_t)(M * d), (size_t)(d * M), (size_t)(M * h) * 2, (size_t)(M * h), (size_t)(h * M),
+      (size_t)amax_parts_for(M, d) * 4, (size_t)gemm_max_tiles(M, h) * 4, 8};
+  size_t o = 0;
+  for (int i = 0; i < B_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
+  return o;
+}
+
+int check_mlp_dims(int64_t M, int64_t d, int64_t h) {
+  if (M <= 0 || d <= 0 || h <= 0) return FP8MLP_EINVAL;
+  if (M % 16 || d % 16 || h % 16) return FP8MLP_ENOTSUP;
+  if (!tile_range_ok(M, M) || !tile_range_ok(h, h) || !tile_range_ok(d, d)) return FP8MLP_ENOTSUP;
+  if (M > INT32_MAX / 2 || d > INT32_MAX / 2 || h > INT32_MAX / 2) return FP8MLP_ENOTSUP;
+  return FP8MLP_OK;
+}
+
+QuantJob make_job(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                  int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale, float* amax,
+                  uint32_t* partials, int nparts, int mode) {
+  QuantJob j{};
+  j.x = x; j.rows = rows; j.cols = cols; j.ldx = ldx; j.q = q; j.ldq = ldq; j.qt = qt;
+  j.ldqt = ldqt; j.scale = scale; j.amax_out = amax; j.partials = partials; j.nparts = nparts;
+  j.fmt = fmt; j.mode = mode;
+  return j;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8mlp_abi_version(void) { return FP8MLP_ABI_VERSION; }
+
+const char* fp8mlp_status_string(int status) {
+  switch (status) {
+    case FP8MLP_OK: return "ok";
+    case FP8MLP_EINVAL: return "invalid argument (null pointer, non-positive size, ld < cols or unknown format)";
+    case FP8MLP_EALIGN: return "misaligned pointer or leading dimension";
+    case FP8MLP_EWORKSPACE: return "workspace missing or too small";
+    case FP8MLP_EHIP: return "HIP launch failed";
+    case FP8MLP_ENOTSUP: return "shape not supported (K % 16, or tile offsets beyond 2 GiB)";
+    default: return "unknown status";
+  }
+}
+
+size_t fp8_amax_quant_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return align_up((size_t)amax_parts_for(rows, cols) * 4);
+}
+
+int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                   int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale, float* amax, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (!x || !scale || (!q && !qt)) return FP8MLP_EINVAL;
+  if (rows <= 0 || cols <= 0 || ldx < cols || !fmt_ok(fmt)) return FP8MLP_EINVAL;
+  if ((q && ldq < cols) || (qt && ldqt < rows)) return FP8MLP_EINVAL;
+  if ((const void*)q == (const void*)x || (const void*)qt == (const void*)x) return FP8MLP_EINVAL;
+  if (!a2(x)) return FP8MLP_EALIGN;
+  if (!ws || ws_bytes < fp8_amax_quant_workspace_bytes(rows, cols)) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+  QuantBatch b{};
+  b.njobs = 1;
+  b.job[0] = make_job(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, (uint32_t*)ws,
+                      amax_parts_for(rows, cols), kModePlain);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_amax_partials(b, st);
+  if (e != hipSuccess) return FP8MLP_EHIP;
+  return hip_status(launch_cast(b, st));
+}
+
+int fp8_linear_fwd(const uint8_t* xq, int64_t ldx, int fx, const float* sx, const uint8_t* wq,
+                   int64_t ldw, int fw, const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                   int64_t ldy, void* stream) {
+  return run_gemm(xq, ldx, fx, sx, wq, ldw, fw, sw, M, N, K, y, ldy, stream);
+}
+
+int fp8_linear_dgrad(const uint8_t* dyq, int64_t lddy, int fdy, const float* sdy, const uint8_t* wqt,
+                     int64_t ldwt, int fw, const float* sw, int64_t M, int64_t N, int64_t K,
+                     uint16_t* dx, int64_t lddx, void* stream) {
+  // dX[M,K] = sum_n dY[m,n] W^T[k,n]: an NT GEMM with reduction length N
+  return run_gemm(dyq, lddy, fdy, sdy, wqt, ldwt, fw, sw, M, K, N, dx, lddx, stream);
+}
+
+int fp8_linear_wgrad(const uint8_t* dyqt, int64_t lddyt, int fdy, const float* sdy, const uint8_t* xqt,
+                     int64_t ldxt, int fx, const float* sx, int64_t M, int64_t N, int64_t K,
+                     uint16_t* dw, int64_t lddw, void* stream) {
+  // dW[N,K] = sum_m dY^T[n,m] X^T[k,m]: an NT GEMM with reduction length M
+  return run_gemm(dyqt, lddyt, fdy, sdy, xqt, ldxt, fx, sx, N, K, M, dw, lddw, stream);
+}
+
+size_t relu2_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h) {
+  if (check_mlp_dims(M, d, h)) return 0;
+  size_t off[F_COUNT];
+  return layout_fwd(M, d, h, off);
+}
+
+size_t relu2_mlp_bwd_workspace_bytes(int64_t M, int64_t d, int64_t h) {
+  if (check_mlp_dims(M, d, h)) return 0;
+  size_t off[B_COUNT];
+  return layout_bwd(M, d, h, off);
+}
+
+int relu2_mlp_fwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n) {
+  if (check_mlp_dims(M, d, h) || !offsets || n < F_COUNT) return FP8MLP_EINVAL;
+  layout_fwd(M, d, h, offsets);
+  return FP8MLP_OK;
+}
+
+int relu2_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n) {
+  if (check_mlp_dims(M, d, h) || !offsets || n < B_COUNT) return FP8MLP_EINVAL;
+  layout_bwd(M, d, h, offsets);
+  return FP8MLP_OK;
+}
+
+int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_down, int64_t M,
+                  int64_t d, int64_t h, uint16_t* y, const relu2_mlp_saved* saved, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (!x || !w_up || !w_down || !y || !saved) return FP8MLP_EINVAL;
+  if (!saved->xq_t || !saved->uq_t || !saved->dq_t || !saved->aq_t || !saved->h || !saved->scales)
+    return FP8MLP_EINVAL;
+  int st = check_mlp_dims(M, d, h);
+  if (st) return st;
+  const void* ptrs[] = {x, w_up, w_down, y, saved->xq_t, saved->uq_t, saved->dq_t, saved->aq_t, saved->h};
+  for (const void* p : ptrs)
+    if (!a16(p)) return FP8MLP_EALIGN;
+  if (((uintptr_t)saved->scales & 3u) != 0) return FP8MLP_EALIGN;
+  size_t off[F_COUNT];
+  const size_t need = layout_fwd(M, d, h, off);
+  if (!ws || ws_bytes < need) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+
+  uint8_t* w8 = (uint8_t*)ws;
+  uint8_t *xq = w8 + off[F_XQ], *uq = w8 + off[F_UQ], *dq = w8 + off[F_DQ], *aq = w8 + off[F_AQ];
+  uint32_t* px = (uint32_t*)(w8 + off[F_PX]);
+  uint32_t* pu = (uint32_t*)(w8 + off[F_PU]);
+  uint32_t* pd = (uint32_t*)(w8 + off[F_PD]);
+  uint32_t* ph = (uint32_t*)(w8 + off[F_PH]);
+  float* sc = saved->scales;
+  hipStream_t s = (hipStream_t)stream;
+
+  // 1-2. quantise X, W_up, W_down (E4M3) in one amax launch and one cast launch
+  QuantBatch b{};
+  b.njobs = 3;
+  b.job[0] = make_job(x, M, d, d, FP8MLP_E4M3, xq, d, saved->xq_t, M, &sc[0], nullptr, px,
+                      amax_parts_for(M, d), kModePlain);
+  b.job[1] = make_job(w_up, h, d, d, FP8MLP_E4M3, uq, d, saved->uq_t, h, &sc[1], nullptr, pu,
+                      amax_parts_for(h, d), kModePlain);
+  b.job[2] = make_job(w_down, d, h, h, FP8MLP_E4M3, dq, h, saved->dq_t, d, &sc[2], nullptr, pd,
+                      amax_parts_for(d, h), kModePlain);
+  if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 3. H = Xq . Uq^T with the relu^2 max epilogue
+  GemmArgs g{};
+  g.a = xq; g.lda = d; g.fa = FP8MLP_E4M3; g.sa = &sc[0];
+  g.b = uq; g.ldb = d; g.fb = FP8MLP_E4M3; g.sb = &sc[1];
+  g.M = M; g.N = h; g.K = d; g.c = saved->h; g.ldc = h; g.epi = kEpiRelu2Max; g.partials = ph;
+  if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 4. Aq = quant(RN_bf16(relu(H)^2)), amax from the epilogue's partials
+  QuantBatch ba{};
+  ba.njobs = 1;
+  ba.job[0] = make_job(saved->h, M, h, h, FP8MLP_E4M3, aq, h, saved->aq_t, M, &sc[3], nullptr, ph,
+                       (int)gemm_num_tiles(M, h), kModeRelu2);
+  if (launch_cast(ba, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 5. Y = Aq . Dq^T
+  GemmArgs g2{};
+  g2.a = aq; g2.lda = h; g2.fa = FP8MLP_E4M3; g2.sa = &sc[3];
+  g2.b = dq; g2.ldb = h; g2.fb = FP8MLP_E4M3; g2.sb = &sc[2];
+  g2.M = M; g2.N = d; g2.K = h; g2.c = y; g2.ldc = d; g2.epi = kEpiStore;
+  return hip_status(launch_gemm(g2, s));
+}
+
+int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, int64_t d, int64_t h,
+                  uint16_t* dx, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (!dy || !saved || !dx || !dw_up || !dw_down) return FP8MLP_EINVAL;
+  if (!saved->xq_t || !saved->uq_t || !saved->dq_t || !saved->aq_t || !saved->h || !saved->scales)
+    return FP8MLP_EINVAL;
+  int st = check_mlp_dims(M, d, h);
+  if (st) return st;
+  const void* ptrs[] = {dy, dx, dw_up, dw_down, saved->xq_t, saved->uq_t, saved->dq_t, saved->aq_t,
+                        saved->h};
+  for (const void* p : ptrs)
+    if (!a16(p)) return FP8MLP_EALIGN;
+  if (((uintptr_t)saved->scales & 3u) != 0 || ((uintptr_t)bwd_scales & 3u) != 0) return FP8MLP_EALIGN;
+  size_t off[B_COUNT];
+  const size_t need = layout_bwd(M, d, h, off);
+  if (!ws || ws_bytes < need) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+
+  uint8_t* w8 = (uint8_t*)ws;
+  uint8_t *gq = w8 + off[B_GQ], *gqt = w8 + off[B_GQT], *hq = w8 + off[B_HQ], *hqt = w8 + off[B_HQT];
+  uint16_t* dh = (uint16_t*)(w8 + off[B_DH]);
+  uint32_t* pg = (uint32_t*)(w8 + off[B_PG]);
+  uint32_t* pdh = (uint32_t*)(w8 + off[B_PDH]);
+  float* bsc = bwd_scales ? bwd_scales : (float*)(w8 + off[B_SC]);
+  const float* sc = saved->scales;
+  hipStream_t s = (hipStream_t)stream;
+
+  // 1. Gq = quant(dY) (E5M2), row-major and transposed
+  QuantBatch b{};
+  b.njobs = 1;
+  b.job[0] = make_job(dy, M, d, d, FP8MLP_E5M2, gq, d, gqt, M, &bsc[0], nullptr, pg,
+                      amax_parts_for(M, d), kModePlain);
+  if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 2. dW_down[d,h] = Gq^T . Aq   (reduction over the M tokens)
+  GemmArgs g{};
+  g.a = gqt; g.lda = M; g.fa = FP8MLP_E5M2; g.sa = &bsc[0];
+  g.b = saved->aq_t; g.ldb = M; g.fb = FP8MLP_E4M3; g.sb = &sc[3];
+  g.M = d; g.N = h; g.K = M; g.c = dw_down; g.ldc = h; g.epi = kEpiStore;
+  if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 3. dA = Gq . Dq (reduction over d), fused dH = RN_bf16(2 relu(H) dA) and max |dH|
+  GemmArgs g2{};
+  g2.a = gq; g2.lda = d; g2.fa = FP8MLP_E5M2; g2.sa = &bsc[0];
+  g2.b = saved->dq_t; g2.ldb = d; g2.fb = FP8MLP_E4M3; g2.sb = &sc[2];
+  g2.M = M; g2.N = h; g2.K = d; g2.c = dh; g2.ldc = h; g2.epi = kEpiRelu2Bwd;
+  g2.aux = saved->h; g2.ldaux = h; g2.partials = pdh;
+  if (launch_gemm(g2, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 4. Hq = quant(dH) (E5M2), amax from the epilogue's partials
+  QuantBatch bh{};
+  bh.njobs = 1;
+  bh.job[0] = make_job(dh, M, h, h, FP8MLP_E5M2, hq, h, hqt, M, &bsc[1], nullptr, pdh,
+                       (int)gemm_num_tiles(M, h), kModePlain);
+  if (launch_cast(bh, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 5. dW_up[h,d] = Hq^T . Xq   (reduction over the M tokens)
+  GemmArgs g3{};
+  g3.a = hqt; g3.lda = M; g3.fa = FP8MLP_E5M2; g3.sa = &bsc[1];
+  g3.b = saved->xq_t; g3.ldb = M; g3.fb = FP8MLP_E4M3; g3.sb = &sc[0];
+  g3.M = h; g3.N = d; g3.K = M; g3.c = dw_up; g3.ldc = d; g3.epi = kEpiStore;
+  if (launch_gemm(g3, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 6. dX[M,d] = Hq . Uq   (reduction over h)
+  GemmArgs g4{};
+  g4.a = hq; g4.lda = h; g4.fa = FP8MLP_E5M2; g4.sa = &bsc[1];
+  g4.b = saved->uq_t; g4.ldb = h; g4.fb = FP8MLP_E4M3; g4.sb = &sc[1];
+  g4.M = M; g4.N = d; g4.K = h; g4.c = dx; g4.ldc = d; g4.epi = kEpiStore;
+  return hip_status(launch_gemm(g4, s));
+}
+
+}  // extern "C"

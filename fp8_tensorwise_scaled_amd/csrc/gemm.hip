@@ -1,0 +1,309 @@
+// FP8 GEMM on the gfx950 matrix cores:  C = RN_bf16(RN32(sa*sb) * A . B^T)
+// with A [M,K] and B [N,K] both stored K-contiguous.
+//
+// All three GEMMs of an FP8 linear layer (decomputer.nl, "Doorvoer
+// verhogen", first bullet: one forward and two backward GEMMs in FP8) map to
+// this one kernel because the quantiser also writes transposed codes: the
+// grad-input GEMM reduces over the output features (dY . W with W^T stored
+// K-contiguous) and the grad-weight GEMM over the tokens (dY^T . X with both
+// stored transposed).
+//
+// Design for CDNA4:
+//  * v_mfma_f32_32x32x64_f8f6f4 (K = 64 per instruction, per-operand E4M3 or
+//    E5M2 selected by the instruction), fp32 accumulation.
+//  * 256 threads = 4 waves in a 2x2 grid; a 256x256 block tile gives each
+//    wave a 128x128 tile (4x4 MFMA tiles, 256 accumulator registers), which
+//    keeps LDS traffic per MFMA at its lowest.
+//  * K is consumed 128 bytes per stage; stages are double-buffered in LDS,
+//    loaded with 16-byte buffer loads into registers one stage ahead.  Rows
+//    are 128 bytes; the 16-byte chunk c of row r is stored at c ^ (r & 7) so
+//    that the ds_read_b128 fragment reads of eight consecutive rows hit
+//    distinct banks.  Buffer-descriptor range checks return zeros for rows
+//    past M/N and chunks past K, which handles ragged edges.
+//  * The MFMA is issued with the B fragment first, so each lane holds four
+//    consecutive output columns of one row: the epilogue packs them to bf16,
+//    stages the tile in LDS and writes 16-byte row chunks to HBM.
+//  * Workgroups are dispatched round-robin over the 8 XCDs; tile ids are
+//    remapped so each XCD works on a contiguous run of tiles, grouped 4 tile
+//    rows deep, so concurrently running tiles share operands in that XCD's L2.
+#include "device_common.h"
+#include "internal.h"
+
+namespace fp8mlp {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 128;  // bytes of K per stage
+constexpr int kGroupM = 4;
+
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int FA, int FB, int BM, int BN, int EPI>
+struct Gemm {
+  static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / (kThreads * 16);  // per thread per stage
+  static constexpr int B_LOADS = B_BYTES / (kThreads * 16);
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static constexpr int CLD = BN * 2 + 16;  // epilogue C tile row stride (bytes)
+  static constexpr int LDS = (2 * STAGE > BM * CLD) ? 2 * STAGE : BM * CLD;
+};
+
+template <int FA, int FB, int BM, int BN, int EPI>
+__global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  using G = Gemm<FA, FB, BM, BN, EPI>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
+  __shared__ uint32_t red[kThreads / 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid & 1, wn = wid >> 1;
+
+  // ---- tile id: XCD-contiguous runs, grouped kGroupM tile-rows deep
+  const int nt = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3, per = nt >> 3, rem = nt & 7;
+  const int t = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  const int in_group = kGroupM * tiles_n;
+  const int first_m = (t / in_group) * kGroupM;
+  const int gm = min(kGroupM, tiles_m - first_m);
+  const int tm = first_m + (t % in_group) % gm;
+  const int tn = (t % in_group) / gm;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int K = (int)g.K;
+  const int rows_a = (int)min<int64_t>(BM, g.M - m0);
+  const int rows_b = (int)min<int64_t>(BN, g.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a + m0 * g.lda, (uint32_t)((rows_a - 1) * g.lda + K));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b + n0 * g.ldb, (uint32_t)((rows_b - 1) * g.ldb + K));
+
+  // Per-thread 16-byte chunks loaded each stage: chunk id = tid + 256*j,
+  // row = id / 8, logical column chunk = id % 8 (eight lanes cover one
+  // 128-byte row, so a wave load is 8 full rows).  In LDS the chunk goes to
+  // position logical ^ (row & 7) of its row.
+  uint32_t offa[G::A_LOADS], offb[G::B_LOADS];
+  int colka[G::A_LOADS], colkb[G::B_LOADS];
+  uint32_t ldsa[G::A_LOADS], ldsb[G::B_LOADS];
+#pragma unroll
+  for (int j = 0; j < G::A_LOADS; ++j) {
+    const int id = tid + kThreads * j;
+    const int row = id >> 3, logical = id & 7;
+    colka[j] = logical * 16;
+    offa[j] = (uint32_t)(row * g.lda) + colka[j];
+    ldsa[j] = row * kBK + ((logical ^ (row & 7)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < G::B_LOADS; ++j) {
+    const int id = tid + kThreads * j;
+    const int row = id >> 3, logical = id & 7;
+    colkb[j] = logical * 16;
+    offb[j] = (uint32_t)(row * g.ldb) + colkb[j];
+    ldsb[j] = G::A_BYTES + row * kBK + ((logical ^ (row & 7)) << 4);
+  }
+
+  v4u sta[G::A_LOADS], stb[G::B_LOADS];  // staging registers for one stage
+  auto gload = [&](int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int j = 0; j < G::A_LOADS; ++j) {
+      const uint32_t off = (k0 + colka[j] < K) ? offa[j] + k0 : 0x80000000u;  // out of range -> 0
+      sta[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < G::B_LOADS; ++j) {
+      const uint32_t off = (k0 + colkb[j] < K) ? offb[j] + k0 : 0x80000000u;
+      stb[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+    }
+  };
+  auto swrite = [&](int buf) {
+    uint8_t* base = smem + buf * G::STAGE;
+#pragma unroll
+    for (int j = 0; j < G::A_LOADS; ++j) *reinterpret_cast<v4u*>(base + ldsa[j]) = sta[j];
+#pragma unroll
+    for (int j = 0; j < G::B_LOADS; ++j) *reinterpret_cast<v4u*>(base + ldsb[j]) = stb[j];
+  };
+
+  v16f acc[G::FM][G::FN];
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) acc[i][j] = v16f{};
+
+  // fragment addressing: lane reads row (lane & 31) of a 32-row block, the
+  // 32 bytes of K starting at ks*64 + (lane >> 5)*32
+  const int frow = lane & 31, fhalf = lane >> 5;
+  auto load_frags = [&](const uint8_t* sbase, int ks, v8i* af, v8i* bf) {
+    const int c0 = ks * 4 + fhalf * 2;
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i) {
+      const int row = wm * G::WM + i * 32 + frow;
+      const uint8_t* rp = sbase + row * kBK;
+      const v4i lo = *reinterpret_cast<const v4i*>(rp + ((c0 ^ (row & 7)) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(rp + (((c0 + 1) ^ (row & 7)) << 4));
+      af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const int row = wn * G::WN + j * 32 + frow;
+      const uint8_t* rp = sbase + G::A_BYTES + row * kBK;
+      const v4i lo = *reinterpret_cast<const v4i*>(rp + ((c0 ^ (row & 7)) << 4));
+      const v4i hi = *reinterpret_cast<const v4i*>(rp + (((c0 + 1) ^ (row & 7)) << 4));
+      bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  auto mfmas = [&](const v8i* af, const v8i* bf) {
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], FB, FA,
+                                                                    0, 0, 0, 0);
+  };
+
+  // Pipeline: stage kt+1 waits in registers while stage kt is consumed from
+  // LDS; it is written to the other LDS buffer right after, and the loads of
+  // stage kt+2 are issued.  One barrier per stage.
+  const int nk = (K + kBK - 1) / kBK;
+  gload(0);
+  swrite(0);
+  if (nk > 1) gload(1);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const uint8_t* sbase = smem + buf * G::STAGE;
+    v8i af0[G::FM], bf0[G::FN], af1[G::FM], bf1[G::FN];
+    load_frags(sbase, 0, af0, bf0);
+    load_frags(sbase, 1, af1, bf1);
+    mfmas(af0, bf0);
+    mfmas(af1, bf1);
+    if (kt + 1 < nk) swrite(buf ^ 1);
+    if (kt + 2 < nk) gload(kt + 2);
+    __syncthreads();
+  }
+
+  // ---- epilogue: scale, round to bf16, stage the tile in LDS
+  const float p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i) {
+    const int row = wm * G::WM + i * 32 + frow;
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * G::WN + j * 32 + q * 8 + fhalf * 4;
+        const v16f& a = acc[i][j];
+        const __bf16 h0 = (__bf16)(a[4 * q + 0] * p), h1 = (__bf16)(a[4 * q + 1] * p);
+        const __bf16 h2 = (__bf16)(a[4 * q + 2] * p), h3 = (__bf16)(a[4 * q + 3] * p);
+        v2u w;
+        w[0] = (uint32_t)__builtin_bit_cast(unsigned short, h0) |
+               ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
+        w[1] = (uint32_t)__builtin_bit_cast(unsigned short, h2) |
+               ((uint32_t)__builtin_bit_cast(unsigned short, h3) << 16);
+        *reinterpret_cast<v2u*>(smem + row * G::CLD + col * 2) = w;
+      }
+    }
+  }
+  __syncthreads();
+
+  const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
+  const bool vec_aux = EPI != kEpiRelu2Bwd ||
+                       (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0));
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  uint32_t mx = 0;             // epilogue max (bit pattern of a non-negative value)
+#pragma unroll 4
+  for (int it = 0; it < BM * CPR / kThreads; ++it) {
+    const int id = tid + kThreads * it;
+    const int row = id / CPR, c8 = id % CPR;
+    const int64_t gr = m0 + row, gc = n0 + c8 * 8;
+    if (gr >= g.M || gc >= g.N) continue;
+    v4u v = *reinterpret_cast<const v4u*>(smem + row * G::CLD + c8 * 16);
+    const bool full = gc + 8 <= g.N && vec_c && vec_aux;
+    if constexpr (EPI == kEpiRelu2Max) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // bf16 pairs -> fp32 bit patterns; negatives (sign set) count as 0
+        const uint32_t lo = v[e] << 16, hi = v[e] & 0xFFFF0000u;
+        const bool ok_lo = full || gc + 2 * e < g.N, ok_hi = full || gc + 2 * e + 1 < g.N;
+        if (ok_lo && !(lo >> 31)) mx = mx > lo ? mx : lo;
+        if (ok_hi && !(hi >> 31)) mx = mx > hi ? mx : hi;
+      }
+    }
+    if constexpr (EPI == kEpiRelu2Bwd) {
+      v4u hv;
+      if (full) {
+        hv = *reinterpret_cast<const v4u*>(g.aux + gr * g.ldaux + gc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = gc + 2 * e < g.N ? g.aux[gr * g.ldaux + gc + 2 * e] : 0u;
+          const uint32_t hi = gc + 2 * e + 1 < g.N ? g.aux[gr * g.ldaux + gc + 2 * e + 1] : 0u;
+          hv[e] = lo | (hi << 16);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t out = 0;
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const float h = bf16_to_f32((hv[e] >> (16 * hlf)) & 0xFFFFu);
+          const float da = bf16_to_f32((v[e] >> (16 * hlf)) & 0xFFFFu);
+          const float r = h > 0.0f ? h : 0.0f;
+          const __bf16 dh = (__bf16)((2.0f * r) * da);  // exact product, one rounding
+          const uint32_t bits = __builtin_bit_cast(unsigned short, dh);
+          out |= bits << (16 * hlf);
+          const bool ok = full || gc + 2 * e + hlf < g.N;
+          const uint32_t mag = bits & 0x7FFFu;
+          if (ok) mx = mx > mag ? mx : mag;
+        }
+        v[e] = out;
+      }
+    }
+    if (full) {
+      *reinterpret_cast<v4u*>(g.c + gr * g.ldc + gc) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gc + e < g.N) g.c[gr * g.ldc + gc + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+  if constexpr (EPI != kEpiStore) {
+    mx = block_max_u32(mx, red);
+    if (tid == 0) g.partials[t] = mx;
+  }
+}
+
+template <int FA, int FB, int BM, int BN, int EPI>
+hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
+  const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, BM, BN, EPI>), dim3(tiles_m * tiles_n), dim3(kThreads),
+                     0, st, g, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int FA, int FB>
+hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
+  switch (g.epi) {
+    case kEpiRelu2Max: return launch_cfg<FA, FB, 256, 256, kEpiRelu2Max>(g, st);
+    case kEpiRelu2Bwd: return launch_cfg<FA, FB, 256, 256, kEpiRelu2Bwd>(g, st);
+    default: return launch_cfg<FA, FB, 256, 256, kEpiStore>(g, st);
+  }
+}
+
+}  // namespace
+
+int64_t gemm_num_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+int64_t gemm_max_tiles(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+  if (g.fa == kE4M3 && g.fb == kE4M3) return launch_fmt<kE4M3, kE4M3>(g, st);
+  if (g.fa == kE5M2 && g.fb == kE4M3) return launch_fmt<kE5M2, kE4M3>(g, st);
+  if (g.fa == kE4M3 && g.fb == kE5M2) return launch_fmt<kE4M3, kE5M2>(g, st);
+  return launch_fmt<kE5M2, kE5M2>(g, st);
+}
+
+}  // namespace fp8mlp

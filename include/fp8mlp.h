@@ -1,0 +1,179 @@
+/*
+ * fp8mlp.h - C ABI of the MI355X (gfx950) FP8 tensorwise-scaled linear layer
+ * and non-gated relu^2 MLP block.
+ *
+ * The method (decomputer.nl, "Het trainen van een 3.8B LLM tot 0.384 CORE
+ * voor $998", section "Vroege experimenten" item 4 and the first bullet of
+ * "Doorvoer verhogen"; the manulx.blog summary's FP8 paragraph): every
+ * linear layer runs its three GEMMs - one forward, two backward - in FP8,
+ * each operand carrying one scale per tensor that is recomputed from that
+ * tensor on every call (dynamic tensorwise scaling), with bf16 tensors around
+ * them.  The block is the page's non-gated relu2 MLP at 4x width (appendix
+ * configuration: hidden_act relu2, gated_mlp false, intermediate 12288 for
+ * hidden 3072).
+ *
+ * Numeric contract (the pages leave these open; this is the reading used):
+ *   formats   OCP E4M3 ("fn", max 448) for activations and weights,
+ *             OCP E5M2 (max 57344) for gradients;
+ *   scale     s = RN32(amax / fmax), amax = max |x| over the tensor;
+ *             s = 1 when amax == 0.  s is the dequantisation scale;
+ *   codes     q = RNE_fp8( clamp( RN32(x / s), -fmax, +fmax ) ), the sign of
+ *             zero kept (RN32 = binary32 round-to-nearest-even division);
+ *   GEMM      out = RN_bf16( RN32(sa * sb) * sum_k a_k b_k ), fp32
+ *             accumulation of exact fp8 products, bf16 output.
+ *
+ * Conventions for every entry point:
+ *   - Pointers to tensors are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors) unless marked otherwise.  Matrices are row-major with an
+ *     explicit leading dimension in elements (ld >= number of columns).
+ *     bf16 values are passed as uint16_t bit patterns, FP8 values as
+ *     uint8_t codes.  Scales are fp32 scalars in device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream: no host synchronisation, no device
+ *     memory allocation, no host<->device copies.
+ *   - Buffers are owned by the caller.  The library keeps no state between
+ *     calls; calls on different streams must not share output or workspace
+ *     buffers.
+ *   - Errors: arguments are validated before anything is launched; an invalid
+ *     call returns a non-zero status and touches no memory.  A failed launch
+ *     returns FP8MLP_EHIP.  Faults inside kernels surface at the caller's
+ *     next synchronisation.  Overflow is never an error (casts saturate).
+ *   - Inputs and outputs must not overlap.
+ */
+#ifndef FP8MLP_H
+#define FP8MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8MLP_ABI_VERSION 1
+
+/* FP8 formats (OCP 8-bit floating point). */
+#define FP8MLP_E4M3 0 /* 1-4-3, bias 7, no infinities, max 448        */
+#define FP8MLP_E5M2 1 /* 1-5-2, bias 15, IEEE-like specials, max 57344 */
+
+/* Status codes. */
+#define FP8MLP_OK 0
+#define FP8MLP_EINVAL 1     /* NULL pointer, size <= 0, ld < cols, bad format   */
+#define FP8MLP_EALIGN 2     /* pointer or leading dimension misaligned          */
+#define FP8MLP_EWORKSPACE 3 /* workspace missing or smaller than the query      */
+#define FP8MLP_EHIP 4       /* a HIP launch failed                              */
+#define FP8MLP_ENOTSUP 5    /* shape outside what this build supports           */
+
+int fp8mlp_abi_version(void);
+/* Static string describing a status code (never NULL). */
+const char* fp8mlp_status_string(int status);
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic tensorwise quantisation (amax reduction + scale + cast).          */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes fp8_amax_quant needs for a rows x cols tensor. */
+size_t fp8_amax_quant_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * x      [rows, cols] bf16, leading dim ldx.
+ * fmt    FP8MLP_E4M3 or FP8MLP_E5M2.
+ * q      [rows, cols] codes, leading dim ldq (may be NULL if qt is given).
+ * qt     [cols, rows] codes of x transposed, leading dim ldqt (may be NULL).
+ *        The GEMMs below take their reduction dimension contiguous; qt is the
+ *        form of an operand that a backward GEMM reduces over its rows.
+ * scale  out: 1 float, s = RN32(amax/fmax) (1 when amax == 0).
+ * amax   out: 1 float, max |x| (may be NULL).
+ * ws     workspace of at least fp8_amax_quant_workspace_bytes(rows, cols)
+ *        bytes, 16-byte aligned; its contents need no initialisation.
+ * Requires x to be 2-byte aligned; 16-byte aligned x/q/qt and ld multiples of
+ * 16 take the vectorised path, anything else a correct element-wise path.
+ */
+int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                   uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale,
+                   float* amax, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The three FP8 GEMMs of one linear layer.                                 */
+/*                                                                          */
+/* All three compute  C[r, c] = RN_bf16( RN32(sa*sb) * sum_k A[r,k] B[c,k] ) */
+/* with both operands stored with the reduction index k contiguous (the     */
+/* fast layout for the gfx950 FP8 matrix cores); the names say which        */
+/* operands of the linear layer they take.  Weight W is stored [out, in].   */
+/* Requirements: K % 16 == 0; operand pointers 16-byte aligned and their    */
+/* leading dimensions multiples of 16; rows and columns of C any size >= 1  */
+/* (ragged edges are masked).  C is overwritten (no accumulation).           */
+/* ------------------------------------------------------------------------ */
+
+/* Forward  Y[M,N] = X[M,K] . W[N,K]^T.
+ * xq [M,K] (ldx), wq [N,K] (ldw), y [M,N] bf16 (ldy). */
+int fp8_linear_fwd(const uint8_t* xq, int64_t ldx, int fx, const float* sx, const uint8_t* wq,
+                   int64_t ldw, int fw, const float* sw, int64_t M, int64_t N, int64_t K,
+                   uint16_t* y, int64_t ldy, void* stream);
+
+/* Grad-input  dX[M,K] = dY[M,N] . W[N,K], reduction over N.
+ * dyq [M,N] (lddy), wqt = codes of W transposed, [K,N] (ldwt) - the `qt`
+ * output of fp8_amax_quant on W; dx [M,K] bf16 (lddx).  N % 16 == 0. */
+int fp8_linear_dgrad(const uint8_t* dyq, int64_t lddy, int fdy, const float* sdy,
+                     const uint8_t* wqt, int64_t ldwt, int fw, const float* sw, int64_t M,
+                     int64_t N, int64_t K, uint16_t* dx, int64_t lddx, void* stream);
+
+/* Grad-weight  dW[N,K] = dY[M,N]^T . X[M,K], reduction over the M tokens.
+ * dyqt = dY codes transposed [N,M] (lddyt), xqt = X codes transposed [K,M]
+ * (ldxt) - the `qt` outputs of fp8_amax_quant; dw [N,K] bf16 (lddw).
+ * M % 16 == 0. */
+int fp8_linear_wgrad(const uint8_t* dyqt, int64_t lddyt, int fdy, const float* sdy,
+                     const uint8_t* xqt, int64_t ldxt, int fx, const float* sx, int64_t M,
+                     int64_t N, int64_t K, uint16_t* dw, int64_t lddw, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Non-gated relu^2 MLP block: Y = relu(X W_up^T)^2 W_down^T, FP8 GEMMs.    */
+/*   X [M,d], W_up [h,d], W_down [d,h], Y [M,d], all bf16, densely packed.  */
+/*   Forward (E4M3 everywhere):                                             */
+/*     Xq,Uq,Dq = quant(X), quant(W_up), quant(W_down)                      */
+/*     H  = gemm(Xq, Uq)                     bf16 [M,h]                     */
+/*     A  = RN_bf16(relu(H)^2)               (fused: never stored)          */
+/*     Aq = quant(A);  Y = gemm(Aq, Dq)                                     */
+/*   Backward (gradients E5M2):                                             */
+/*     Gq = quant(dY);  dW_down = gemm(Gq^T, Aq^T)                          */
+/*     dA = gemm(Gq, Dq^T);  dH = RN_bf16(2 relu(H) dA)  (fused epilogue)   */
+/*     Hq = quant(dH);  dW_up = gemm(Hq^T, Xq^T);  dX = gemm(Hq, Uq^T)      */
+/* Requirements: M, d, h multiples of 16; all pointers 16-byte aligned.      */
+/* ------------------------------------------------------------------------ */
+
+/* Forward quantities the backward pass reads.  Caller-allocated device
+ * buffers, all densely packed; written by relu2_mlp_fwd. */
+typedef struct {
+  uint8_t* xq_t; /* [d, M] E4M3 codes of X, transposed      */
+  uint8_t* uq_t; /* [d, h] E4M3 codes of W_up, transposed   */
+  uint8_t* dq_t; /* [h, d] E4M3 codes of W_down, transposed */
+  uint8_t* aq_t; /* [h, M] E4M3 codes of A, transposed      */
+  uint16_t* h;   /* [M, h] bf16 pre-activation H            */
+  float* scales; /* [4]: sx, su, sd, sa                     */
+} relu2_mlp_saved;
+
+size_t relu2_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
+size_t relu2_mlp_bwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
+
+/* Byte offsets of the intermediates inside the workspaces, for inspection.
+ * Forward (n >= 8): Xq [M,d], Uq [h,d], Dq [d,h], Aq [M,h] codes, then the
+ * amax partials of X, W_up, W_down and the per-tile max(H) partials.
+ * Backward (n >= 8): Gq [M,d], Gq^T [d,M], dH [M,h] bf16, Hq [M,h],
+ * Hq^T [h,M], the amax partials of dY and of dH, 2 floats of scales. */
+int relu2_mlp_fwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
+int relu2_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
+
+int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_down, int64_t M,
+                  int64_t d, int64_t h, uint16_t* y, const relu2_mlp_saved* saved, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* dx [M,d], dw_up [h,d], dw_down [d,h] are overwritten.  `bwd_scales`
+ * (may be NULL) receives 2 floats: sg (scale of dY), sh (scale of dH). */
+int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, int64_t d,
+                  int64_t h, uint16_t* dx, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales,
+                  void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8MLP_H */

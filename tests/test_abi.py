@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+declared in include/*.h, and rejects invalid arguments before launching
+anything (these calls never reach the GPU)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from fp8_tensorwise_scaled_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**([a-z_][a-z0-9_]*)\s*\(", src, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_exports_all_symbols():
+    L = _native.lib()
+    decl = declared_functions()
+    assert len(decl) >= 12
+    for name in decl:
+        assert hasattr(L, name), name
+    assert decl == set(_native.EXPORTS), decl ^ set(_native.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    L = _native.lib()
+    assert L.fp8mlp_abi_version() == 1
+    for s in range(0, 7):
+        assert len(_native.status_string(s)) > 0
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x10001)
+
+
+def q(*args):
+    return _native.lib().fp8_amax_quant(*args)
+
+
+def test_quant_validation():
+    ws_n = _native.lib().fp8_amax_quant_workspace_bytes(64, 64)
+    assert ws_n > 0
+    ok = [FAKE, 64, 64, 64, 0, FAKE, 64, None, 0, FAKE, None, FAKE, ws_n, None]
+    bad = dict(x=(0, None), rows=(1, 0), cols=(2, -1), ldx=(3, 32), fmt=(4, 7), ldq=(6, 10),
+               scale=(9, None))
+    for _, (i, v) in bad.items():
+        a = list(ok)
+        a[i] = v
+        assert q(*a) == 1, _
+    a = list(ok); a[5] = None                     # neither q nor qt
+    assert q(*a) == 1
+    a = list(ok); a[5] = FAKE; a[0] = FAKE        # q aliases x
+    assert q(*a) == 1
+    a = list(ok); a[0] = FAKE_ODD; a[5] = ctypes.c_void_p(0x20000)
+    assert q(*a) == 2                             # x not 2-byte aligned
+    a = list(ok); a[5] = ctypes.c_void_p(0x20000); a[11] = None
+    assert q(*a) == 3                             # no workspace
+    a[11] = FAKE; a[12] = ws_n - 1
+    assert q(*a) == 3                             # workspace too small
+    a = list(ok); a[5] = None; a[7] = ctypes.c_void_p(0x20000); a[8] = 10
+    assert q(*a) == 1                             # ldqt < rows
+
+
+def test_gemm_validation():
+    L = _native.lib()
+    base = [FAKE, 64, 0, FAKE, FAKE, 64, 0, FAKE, 32, 48, 64, FAKE, 48, None]
+    for fn in (L.fp8_linear_fwd,):
+        assert fn(*[None] + base[1:]) == 1
+        a = list(base); a[8] = 0
+        assert fn(*a) == 1                          # M = 0
+        a = list(base); a[1] = 32
+        assert fn(*a) == 1                          # lda < K
+        a = list(base); a[10] = 40; a[1] = 48; a[5] = 48
+        assert fn(*a) == 5                          # K % 16
+        a = list(base); a[1] = 72
+        assert fn(*a) == 2                          # lda % 16
+        a = list(base); a[0] = ctypes.c_void_p(0x10008)
+        assert fn(*a) == 2                          # A not 16-byte aligned
+        a = list(base); a[2] = 3
+        assert fn(*a) == 1                          # unknown format
+        a = list(base); a[12] = 40
+        assert fn(*a) == 1                          # ldc < N
+    # dgrad: reduction length is N (K argument is the output width)
+    a = [FAKE, 40, 1, FAKE, FAKE, 40, 0, FAKE, 32, 40, 64, FAKE, 64, None]
+    assert L.fp8_linear_dgrad(*a) == 5
+    # wgrad: reduction length is M
+    a = [FAKE, 40, 1, FAKE, FAKE, 40, 0, FAKE, 40, 64, 64, FAKE, 64, None]
+    assert L.fp8_linear_wgrad(*a) == 5
+
+
+def test_mlp_validation():
+    L = _native.lib()
+    assert L.relu2_mlp_fwd_workspace_bytes(2048, 768, 3072) > 2048 * 768 + 3072 * 768 * 2
+    assert L.relu2_mlp_bwd_workspace_bytes(2048, 768, 3072) > 2048 * 3072 * 4
+    assert L.relu2_mlp_fwd_workspace_bytes(100, 768, 3072) == 0      # M % 16
+    saved = _native.Relu2MlpSaved(0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
+    n = L.relu2_mlp_fwd_workspace_bytes(64, 64, 256)
+    args = [FAKE, FAKE, FAKE, 64, 64, 256, FAKE, ctypes.byref(saved), FAKE, n - 1, None]
+    assert L.relu2_mlp_fwd(*args) == 3
+    args[3] = 65
+    assert L.relu2_mlp_fwd(*args) == 5
+    args = [FAKE, FAKE, FAKE, 64, 64, 256, None, ctypes.byref(saved), FAKE, n, None]
+    assert L.relu2_mlp_fwd(*args) == 1
+    bad_saved = _native.Relu2MlpSaved(0x10000, 0, 0x10000, 0x10000, 0x10000, 0x10000)
+    args = [FAKE, FAKE, FAKE, 64, 64, 256, FAKE, ctypes.byref(bad_saved), FAKE, n, None]
+    assert L.relu2_mlp_fwd(*args) == 1
+    nb = L.relu2_mlp_bwd_workspace_bytes(64, 64, 256)
+    args = [FAKE, ctypes.byref(saved), 64, 64, 256, FAKE, FAKE, FAKE, None, FAKE, nb - 1, None]
+    assert L.relu2_mlp_bwd(*args) == 3
+    args = [FAKE, ctypes.byref(saved), 64, 64, 256, ctypes.c_void_p(0x10008), FAKE, FAKE, None, FAKE, nb, None]
+    assert L.relu2_mlp_bwd(*args) == 2
+    offs = (ctypes.c_size_t * 8)()
+    assert L.relu2_mlp_bwd_workspace_layout(64, 64, 256, offs, 8) == 0
+    assert list(offs) == sorted(offs) and offs[0] == 0

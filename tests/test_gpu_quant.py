@@ -1,0 +1,110 @@
+"""GPU parity of fp8_amax_quant: codes, transposed codes and scales are
+bit-identical to the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_tensorwise_scaled_amd import synth
+from tests.gpu_util import bf16_bits, f32, to_dev_bf16, u8
+
+pytestmark = pytest.mark.gpu
+FMTS = [oracle.E4M3, oracle.E5M2]
+
+
+def run_quant(x_np, fmt, ld=None, qt=True):
+    from fp8_tensorwise_scaled_amd import api
+
+    rows, cols = x_np.shape
+    if ld is None:
+        xd = to_dev_bf16(x_np)
+    else:
+        buf = np.zeros((rows, ld), np.uint16)
+        buf[:, :cols] = x_np
+        xd = to_dev_bf16(buf)[:, :cols]
+    q, qt_, s, a = api.fp8_amax_quant(xd, fmt, want_qt=qt)
+    torch.cuda.synchronize()
+    return u8(q), (u8(qt_) if qt else None), float(f32(s)[0]), float(f32(a)[0])
+
+
+def check_against_oracle(x_np, fmt, **kw):
+    q, qt, s, a = run_quant(x_np, fmt, **kw)
+    rq, rs, ra = oracle.quant(x_np, fmt)
+    assert np.float32(s) == np.float32(rs) and np.float32(a) == np.float32(ra), (s, rs, a, ra)
+    bad = np.argwhere(q != rq)
+    assert bad.size == 0, [(tuple(i), hex(x_np[tuple(i)]), q[tuple(i)], rq[tuple(i)]) for i in bad[:5]]
+    if qt is not None:
+        assert (qt == rq.T).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_exhaustive_bf16_patterns(fmt):
+    """Every finite bf16 value, with amax set by the largest one present:
+    the full tensor and a sweep of 48 amax cut-offs."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = b[np.isfinite(synth.bf16_bits_to_f32(b))]
+    check_against_oracle(fin.reshape(-1, 256), fmt)   # 255 x 256: vector path
+    mags = np.unique(fin & 0x7FFF)
+    rng = np.random.default_rng(fmt)
+    cuts = np.concatenate([mags[[1, 2, 100, 0x80, 0x300]], rng.choice(mags[1:], 43, replace=False)])
+    for c in cuts:
+        sel = fin[(fin & 0x7FFF) <= c]
+        sel = np.concatenate([sel, [c]]).astype(np.uint16)
+        n = sel.size
+        cols = 128 if n >= 128 else n
+        rows = -(-n // cols)
+        pad = np.zeros(rows * cols, np.uint16)
+        pad[:n] = sel
+        check_against_oracle(pad.reshape(rows, cols), fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(256, 512), (1024, 512), (300, 200), (1, 8), (129, 130), (7, 1000)])
+def test_workload_like_shapes(fmt, shape):
+    sigma = 1.0 if fmt == oracle.E4M3 else 1e-3
+    x = synth.normal_bf16(shape, sigma, 1000 + shape[0] * 7 + shape[1], outlier_frac=1e-3)
+    check_against_oracle(x, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_strided_and_unaligned(fmt):
+    x = synth.normal_bf16((200, 333), 1.0, 77)
+    check_against_oracle(x, fmt, ld=341)     # odd leading dimension: element path
+    x = synth.normal_bf16((256, 256), 1.0, 78)
+    check_against_oracle(x, fmt, ld=264)     # aligned ld > cols: vector path
+    q, qt, s, a = run_quant(x, fmt, qt=False)
+    assert qt is None and (q == oracle.quant(x, fmt)[0]).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_zero_and_tiny(fmt):
+    x = np.zeros((64, 64), np.uint16)
+    x[3, 5] = 0x8000
+    check_against_oracle(x, fmt)
+    for amax_bits in (0x0001, 0x0080, 0x1000, 0x1380, 0x1400):  # 2^-133 .. 2^-87
+        xx = synth.normal_bf16((64, 64), 1.0, int(amax_bits))
+        xx = (xx & 0x8000) | np.minimum(xx & 0x7FFF, amax_bits).astype(np.uint16)
+        xx[0, 0] = amax_bits
+        check_against_oracle(xx, fmt)
+
+
+@pytest.mark.parametrize("wl", ["linear", "mlp_small", "mlp_3p8b"])
+def test_workload_tensors(wl):
+    if wl == "linear":
+        tensors = [(t, oracle.E4M3) for t in synth.LINEAR_SMALL.tensors()]
+    else:
+        w = synth.MLP_SMALL if wl == "mlp_small" else synth.MLP_3P8B
+        x, wu, wd, dy = w.tensors()
+        tensors = [(x, oracle.E4M3), (wu, oracle.E4M3), (wd, oracle.E4M3), (dy, oracle.E5M2)]
+    for t, fmt in tensors:
+        check_against_oracle(t, fmt)
+
+
+def test_deterministic():
+    from fp8_tensorwise_scaled_amd import api
+
+    x = to_dev_bf16(synth.normal_bf16((1024, 1536), 1.0, 5, outlier_frac=1e-3))
+    outs = [api.fp8_amax_quant(x, oracle.E5M2, want_qt=True) for _ in range(5)]
+    torch.cuda.synchronize()
+    for q, qt, s, a in outs[1:]:
+        assert torch.equal(q, outs[0][0]) and torch.equal(qt, outs[0][1]) and torch.equal(s, outs[0][2])
