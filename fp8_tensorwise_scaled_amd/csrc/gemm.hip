@@ -16,8 +16,8 @@
 //    keeps LDS traffic per MFMA at its lowest.
 //  * K is consumed 128 bytes per stage; stages are double-buffered in LDS,
 //    loaded with 16-byte buffer loads into registers one stage ahead.  Rows
-//    are 128 bytes; the 16-byte chunk c of row r is stored at c ^ (r & 7) so
-//    that the ds_read_b128 fragment reads of eight consecutive rows hit
+//    are 128 bytes; the 16-byte chunk c of row r is stored at c ^ ((r>>1)&7)
+//    so that the ds_read_b128 fragment reads of sixteen consecutive rows hit
 //    distinct banks.  Buffer-descriptor range checks return zeros for rows
 //    past M/N and chunks past K, which handles ragged edges.
 //  * The MFMA is issued with the B fragment first, so each lane holds four
@@ -26,6 +26,8 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs; tile ids are
 //    remapped so each XCD works on a contiguous run of tiles, grouped 4 tile
 //    rows deep, so concurrently running tiles share operands in that XCD's L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -37,6 +39,13 @@ constexpr int kThreads = 256;
 constexpr int kBK = 128;  // bytes of K per stage
 constexpr int kGroupM = 4;
 
+
+// LDS placement of the 16-byte chunk c of tile row r: c ^ swz(r).  gfx950
+// serves a 128-bit LDS access 16 lanes at a time across 64 four-byte banks,
+// i.e. 256 bytes; 128-byte rows put rows r and r+1 in opposite bank halves,
+// so the XOR key only has to differ between the 8 row pairs of any 16
+// consecutive rows.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -85,47 +94,28 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int ti
   // Per-thread 16-byte chunks loaded each stage: chunk id = tid + 256*j,
   // row = id / 8, logical column chunk = id % 8 (eight lanes cover one
   // 128-byte row, so a wave load is 8 full rows).  In LDS the chunk goes to
-  // position logical ^ (row & 7) of its row.
-  uint32_t offa[G::A_LOADS], offb[G::B_LOADS];
-  int colka[G::A_LOADS], colkb[G::B_LOADS];
-  uint32_t ldsa[G::A_LOADS], ldsb[G::B_LOADS];
+  // position logical ^ swz(row) of its row.  Loads j < A_LOADS are A rows,
+  // the rest B rows.
+  uint32_t goff[G::LOADS], ldsoff[G::LOADS];
+  int colk[G::LOADS];
 #pragma unroll
-  for (int j = 0; j < G::A_LOADS; ++j) {
-    const int id = tid + kThreads * j;
+  for (int j = 0; j < G::LOADS; ++j) {
+    const bool is_a = j < G::A_LOADS;
+    const int id = tid + kThreads * (is_a ? j : j - G::A_LOADS);
     const int row = id >> 3, logical = id & 7;
-    colka[j] = logical * 16;
-    offa[j] = (uint32_t)(row * g.lda) + colka[j];
-    ldsa[j] = row * kBK + ((logical ^ (row & 7)) << 4);
-  }
-#pragma unroll
-  for (int j = 0; j < G::B_LOADS; ++j) {
-    const int id = tid + kThreads * j;
-    const int row = id >> 3, logical = id & 7;
-    colkb[j] = logical * 16;
-    offb[j] = (uint32_t)(row * g.ldb) + colkb[j];
-    ldsb[j] = G::A_BYTES + row * kBK + ((logical ^ (row & 7)) << 4);
+    colk[j] = logical * 16;
+    goff[j] = (uint32_t)(row * (is_a ? g.lda : g.ldb)) + colk[j];
+    ldsoff[j] = (is_a ? 0 : G::A_BYTES) + row * kBK + ((logical ^ swz(row)) << 4);
   }
 
-  v4u sta[G::A_LOADS], stb[G::B_LOADS];  // staging registers for one stage
-  auto gload = [&](int kt) {
+  v4u stg[G::LOADS];  // one stage in flight in registers
+  auto gload_one = [&](int j, int kt) {
     const int k0 = kt * kBK;
-#pragma unroll
-    for (int j = 0; j < G::A_LOADS; ++j) {
-      const uint32_t off = (k0 + colka[j] < K) ? offa[j] + k0 : 0x80000000u;  // out of range -> 0
-      sta[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < G::B_LOADS; ++j) {
-      const uint32_t off = (k0 + colkb[j] < K) ? offb[j] + k0 : 0x80000000u;
-      stb[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-    }
+    const uint32_t off = (k0 + colk[j] < K) ? goff[j] + k0 : 0x80000000u;  // out of range -> 0
+    stg[j] = __builtin_amdgcn_raw_buffer_load_b128(j < G::A_LOADS ? ra : rb, off, 0, 0);
   };
-  auto swrite = [&](int buf) {
-    uint8_t* base = smem + buf * G::STAGE;
-#pragma unroll
-    for (int j = 0; j < G::A_LOADS; ++j) *reinterpret_cast<v4u*>(base + ldsa[j]) = sta[j];
-#pragma unroll
-    for (int j = 0; j < G::B_LOADS; ++j) *reinterpret_cast<v4u*>(base + ldsb[j]) = stb[j];
+  auto swrite_one = [&](int j, int buf) {
+    *reinterpret_cast<v4u*>(smem + buf * G::STAGE + ldsoff[j]) = stg[j];
   };
 
   v16f acc[G::FM][G::FN];
@@ -134,57 +124,96 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int ti
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) acc[i][j] = v16f{};
 
-  // fragment addressing: lane reads row (lane & 31) of a 32-row block, the
-  // 32 bytes of K starting at ks*64 + (lane >> 5)*32
+  // Fragments: lane reads row (lane & 31) of a 32-row block, the 32 bytes of
+  // K starting at ks*64 + (lane >> 5)*32, as two 16-byte LDS reads.  Read r
+  // of a fragment set (r < NR) is half r&1 of fragment r>>1 (A fragments
+  // first, then B).
+  constexpr int NM = G::FM * G::FN;        // MFMAs per 64-byte K substep
+  constexpr int NR = 2 * (G::FM + G::FN);  // 16-byte LDS reads per substep
   const int frow = lane & 31, fhalf = lane >> 5;
-  auto load_frags = [&](const uint8_t* sbase, int ks, v8i* af, v8i* bf) {
-    const int c0 = ks * 4 + fhalf * 2;
-#pragma unroll
-    for (int i = 0; i < G::FM; ++i) {
-      const int row = wm * G::WM + i * 32 + frow;
-      const uint8_t* rp = sbase + row * kBK;
-      const v4i lo = *reinterpret_cast<const v4i*>(rp + ((c0 ^ (row & 7)) << 4));
-      const v4i hi = *reinterpret_cast<const v4i*>(rp + (((c0 + 1) ^ (row & 7)) << 4));
-      af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-#pragma unroll
-    for (int j = 0; j < G::FN; ++j) {
-      const int row = wn * G::WN + j * 32 + frow;
-      const uint8_t* rp = sbase + G::A_BYTES + row * kBK;
-      const v4i lo = *reinterpret_cast<const v4i*>(rp + ((c0 ^ (row & 7)) << 4));
-      const v4i hi = *reinterpret_cast<const v4i*>(rp + (((c0 + 1) ^ (row & 7)) << 4));
-      bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+  typedef v4i Frag[G::FM + G::FN][2];
+  auto read_one = [&](int r, int buf, int ks, Frag& f) {
+    const int fi = r >> 1, h = r & 1;
+    const bool is_a = fi < G::FM;
+    const int row = is_a ? wm * G::WM + fi * 32 + frow : wn * G::WN + (fi - G::FM) * 32 + frow;
+    const int c = ks * 4 + fhalf * 2 + h;
+    f[fi][h] = *reinterpret_cast<const v4i*>(smem + buf * G::STAGE + (is_a ? 0 : G::A_BYTES) + row * kBK +
+                                             ((c ^ swz(row)) << 4));
   };
-  auto mfmas = [&](const v8i* af, const v8i* bf) {
-#pragma unroll
-    for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < G::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af[i], acc[i][j], FB, FA,
-                                                                    0, 0, 0, 0);
+  auto mfma_one = [&](int t, const Frag& f) {
+    const int i = t / G::FN, j = t % G::FN;
+    const v4i* a = f[i];
+    const v4i* b = f[G::FM + j];
+    const v8i av = v8i{a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
+    const v8i bv = v8i{b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], FB, FA, 0, 0, 0, 0);
   };
 
-  // Pipeline: stage kt+1 waits in registers while stage kt is consumed from
-  // LDS; it is written to the other LDS buffer right after, and the loads of
-  // stage kt+2 are issued.  One barrier per stage.
+  // Software pipeline over 128-byte K stages, two LDS buffers, one stage in
+  // registers.  Iteration kt (stage kt in LDS buffer kt&1, its first-half
+  // fragments F0 already in registers):
+  //   A: MFMAs on F0; step t also issues read t of the second-half fragments
+  //      F1, LDS write t of stage kt+1 (registers -> other buffer) and global
+  //      load t of stage kt+2 into the register just written out;
+  //   B: MFMAs on F1; the barrier that publishes stage kt+1 sits before the
+  //      last kTail MFMAs, which hide the reads of stage kt+1's F0.
+  // sched_barrier fences keep this order through instruction scheduling.
+  constexpr int kTail = 4;
+  constexpr int STEPS_A = NM > NR ? (NM > G::LOADS ? NM : G::LOADS) : (NR > G::LOADS ? NR : G::LOADS);
   const int nk = (K + kBK - 1) / kBK;
-  gload(0);
-  swrite(0);
-  if (nk > 1) gload(1);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const uint8_t* sbase = smem + buf * G::STAGE;
-    v8i af0[G::FM], bf0[G::FN], af1[G::FM], bf1[G::FN];
-    load_frags(sbase, 0, af0, bf0);
-    load_frags(sbase, 1, af1, bf1);
-    mfmas(af0, bf0);
-    mfmas(af1, bf1);
-    if (kt + 1 < nk) swrite(buf ^ 1);
-    if (kt + 2 < nk) gload(kt + 2);
-    __syncthreads();
+  Frag f0, f1;
+
+#pragma unroll
+  for (int j = 0; j < G::LOADS; ++j) gload_one(j, 0);
+#pragma unroll
+  for (int j = 0; j < G::LOADS; ++j) swrite_one(j, 0);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < G::LOADS; ++j) gload_one(j, 1);
   }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NR; ++r) read_one(r, 0, 0, f0);
+
+  auto iteration = [&](int kt, auto has_next, auto has_next2) {
+    constexpr bool HN = decltype(has_next)::value, HN2 = decltype(has_next2)::value;
+    const int cur = kt & 1, nxt = cur ^ 1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < STEPS_A; ++t) {
+      if (t < NM) mfma_one(t, f0);
+      if (t < NR) read_one(t, cur, 1, f1);
+      if constexpr (HN) {
+        if (t < G::LOADS) {
+          swrite_one(t, nxt);
+          if constexpr (HN2) gload_one(t, kt + 2);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < NM - kTail; ++t) mfma_one(t, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (HN) __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = NM - kTail; t < NM; ++t) {
+      mfma_one(t, f1);
+      if constexpr (HN) {
+#pragma unroll
+        for (int r = (t - (NM - kTail)) * NR / kTail; r < (t - (NM - kTail) + 1) * NR / kTail; ++r)
+          read_one(r, nxt, 0, f0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) iteration(kt, T{}, T{});
+  if (kt + 1 < nk) { iteration(kt, T{}, F{}); ++kt; }
+  iteration(kt, F{}, F{});
+  __syncthreads();
 
   // ---- epilogue: scale, round to bf16, stage the tile in LDS
   const float p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
@@ -285,18 +314,38 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Block tile width: 256x192 tiles when they fill the 256 CUs in whole waves
+// better than 256x256 (e.g. an 8192x3072 output is 384 tiles of 256x256 =
+// 1.5 waves, but 512 tiles of 256x192 = 2 waves).
+int pick_bn(int64_t M, int64_t N) {
+  auto eff = [&](int bn) {
+    const int64_t t = ((M + 255) / 256) * ((N + bn - 1) / bn);
+    const int64_t waves = (t + 255) / 256;
+    return (double)(M * N) / (double)(waves * 256 * 256 * bn);
+  };
+  return eff(192) > eff(256) * 1.02 ? 192 : 256;
+}
+
+template <int FA, int FB, int BN>
+hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
+  switch (g.epi) {
+    case kEpiRelu2Max: return launch_cfg<FA, FB, 256, BN, kEpiRelu2Max>(g, st);
+    case kEpiRelu2Bwd: return launch_cfg<FA, FB, 256, BN, kEpiRelu2Bwd>(g, st);
+    default: return launch_cfg<FA, FB, 256, BN, kEpiStore>(g, st);
+  }
+}
+
 template <int FA, int FB>
 hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
-  switch (g.epi) {
-    case kEpiRelu2Max: return launch_cfg<FA, FB, 256, 256, kEpiRelu2Max>(g, st);
-    case kEpiRelu2Bwd: return launch_cfg<FA, FB, 256, 256, kEpiRelu2Bwd>(g, st);
-    default: return launch_cfg<FA, FB, 256, 256, kEpiStore>(g, st);
-  }
+  return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192>(g, st) : launch_bn<FA, FB, 256>(g, st);
 }
 
 }  // namespace
 
-int64_t gemm_num_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+int64_t gemm_num_tiles(int64_t M, int64_t N) {
+  const int bn = pick_bn(M, N);
+  return ((M + 255) / 256) * ((N + bn - 1) / bn);
+}
 int64_t gemm_max_tiles(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
