@@ -215,7 +215,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int ti
   iteration(kt, F{}, F{});
   __syncthreads();
 
-  // ---- epilogue: scale, round to bf16, stage the tile in LDS
+  // ---- epilogue
+  // Each thread owns NCH 16-byte chunks of the output tile: chunk id
+  // tid + 256*it is row id / CPR, 8-column group id % CPR.
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  constexpr int NCH = BM * CPR / kThreads;
+  const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
+  const bool vec_aux = EPI != kEpiRelu2Bwd ||
+                       (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0));
+  // scale, round to bf16 and stage the tile in LDS
   const float p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
 #pragma unroll
   for (int i = 0; i < G::FM; ++i) {
@@ -239,65 +247,75 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int ti
   }
   __syncthreads();
 
-  const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
-  const bool vec_aux = EPI != kEpiRelu2Bwd ||
-                       (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0));
-  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
-  uint32_t mx = 0;             // epilogue max (bit pattern of a non-negative value)
-#pragma unroll 4
-  for (int it = 0; it < BM * CPR / kThreads; ++it) {
+  // The relu^2-backward epilogue needs H at its chunks: issue all those loads
+  // together (the accumulators are dead once staged) before processing.
+  v4u hv[EPI == kEpiRelu2Bwd ? NCH : 1];
+  if constexpr (EPI == kEpiRelu2Bwd) {
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+      const int id = tid + kThreads * it;
+      const int64_t gr = m0 + id / CPR, gc = n0 + (id % CPR) * 8;
+      hv[it] = v4u{0u, 0u, 0u, 0u};
+      if (gr < g.M && gc < g.N) {
+        if (gc + 8 <= g.N && vec_c && vec_aux) {
+          hv[it] = *reinterpret_cast<const v4u*>(g.aux + gr * g.ldaux + gc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = gc + 2 * e < g.N ? g.aux[gr * g.ldaux + gc + 2 * e] : 0u;
+            const uint32_t hi = gc + 2 * e + 1 < g.N ? g.aux[gr * g.ldaux + gc + 2 * e + 1] : 0u;
+            hv[it][e] = lo | (hi << 16);
+          }
+        }
+      }
+    }
+  }
+
+  uint32_t mx = 0;  // epilogue max (bit pattern of a non-negative value)
+#pragma unroll
+  for (int it = 0; it < NCH; ++it) {
     const int id = tid + kThreads * it;
     const int row = id / CPR, c8 = id % CPR;
     const int64_t gr = m0 + row, gc = n0 + c8 * 8;
-    if (gr >= g.M || gc >= g.N) continue;
-    v4u v = *reinterpret_cast<const v4u*>(smem + row * G::CLD + c8 * 16);
-    const bool full = gc + 8 <= g.N && vec_c && vec_aux;
-    if constexpr (EPI == kEpiRelu2Max) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // bf16 pairs -> fp32 bit patterns; negatives (sign set) count as 0
-        const uint32_t lo = v[e] << 16, hi = v[e] & 0xFFFF0000u;
-        const bool ok_lo = full || gc + 2 * e < g.N, ok_hi = full || gc + 2 * e + 1 < g.N;
-        if (ok_lo && !(lo >> 31)) mx = mx > lo ? mx : lo;
-        if (ok_hi && !(hi >> 31)) mx = mx > hi ? mx : hi;
-      }
-    }
-    if constexpr (EPI == kEpiRelu2Bwd) {
-      v4u hv;
-      if (full) {
-        hv = *reinterpret_cast<const v4u*>(g.aux + gr * g.ldaux + gc);
-      } else {
+    if (gr < g.M && gc < g.N) {
+      v4u v = *reinterpret_cast<const v4u*>(smem + row * G::CLD + c8 * 16);
+      const bool full = gc + 8 <= g.N && vec_c && vec_aux;
+      if constexpr (EPI == kEpiRelu2Max) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = gc + 2 * e < g.N ? g.aux[gr * g.ldaux + gc + 2 * e] : 0u;
-          const uint32_t hi = gc + 2 * e + 1 < g.N ? g.aux[gr * g.ldaux + gc + 2 * e + 1] : 0u;
-          hv[e] = lo | (hi << 16);
+          // bf16 pairs -> fp32 bit patterns; negatives (sign set) count as 0
+          const uint32_t lo = v[e] << 16, hi = v[e] & 0xFFFF0000u;
+          const bool ok_lo = full || gc + 2 * e < g.N, ok_hi = full || gc + 2 * e + 1 < g.N;
+          if (ok_lo && !(lo >> 31)) mx = mx > lo ? mx : lo;
+          if (ok_hi && !(hi >> 31)) mx = mx > hi ? mx : hi;
         }
       }
+      if constexpr (EPI == kEpiRelu2Bwd) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t out = 0;
+        for (int e = 0; e < 4; ++e) {
+          uint32_t out = 0;
 #pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const float h = bf16_to_f32((hv[e] >> (16 * hlf)) & 0xFFFFu);
-          const float da = bf16_to_f32((v[e] >> (16 * hlf)) & 0xFFFFu);
-          const float r = h > 0.0f ? h : 0.0f;
-          const __bf16 dh = (__bf16)((2.0f * r) * da);  // exact product, one rounding
-          const uint32_t bits = __builtin_bit_cast(unsigned short, dh);
-          out |= bits << (16 * hlf);
-          const bool ok = full || gc + 2 * e + hlf < g.N;
-          const uint32_t mag = bits & 0x7FFFu;
-          if (ok) mx = mx > mag ? mx : mag;
+          for (int hlf = 0; hlf < 2; ++hlf) {
+            const float h = bf16_to_f32((hv[it][e] >> (16 * hlf)) & 0xFFFFu);
+            const float da = bf16_to_f32((v[e] >> (16 * hlf)) & 0xFFFFu);
+            const float r = h > 0.0f ? h : 0.0f;
+            const __bf16 dh = (__bf16)((2.0f * r) * da);  // exact product, one rounding
+            const uint32_t bits = __builtin_bit_cast(unsigned short, dh);
+            out |= bits << (16 * hlf);
+            const bool ok = full || gc + 2 * e + hlf < g.N;
+            const uint32_t mag = bits & 0x7FFFu;
+            if (ok) mx = mx > mag ? mx : mag;
+          }
+          v[e] = out;
         }
-        v[e] = out;
       }
-    }
-    if (full) {
-      *reinterpret_cast<v4u*>(g.c + gr * g.ldc + gc) = v;
-    } else {
+      if (full) {
+        *reinterpret_cast<v4u*>(g.c + gr * g.ldc + gc) = v;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gc + e < g.N) g.c[gr * g.ldc + gc + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        for (int e = 0; e < 8; ++e)
+          if (gc + e < g.N) g.c[gr * g.ldc + gc + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      }
     }
   }
   if constexpr (EPI != kEpiStore) {

@@ -11,9 +11,9 @@
 //      as an integer max of the bf16 magnitude bits (monotone in the value,
 //      order independent, hence bit-deterministic);
 //   2. cast: every block first reduces the (<= 2048) partials of its tensor,
-//      derives s itself, then streams 128x128 tiles: row-major codes go
-//      straight to HBM, the transposed codes go through LDS so that both
-//      outputs are written in full 128-byte rows.
+//      derives s itself, then streams 128x256 tiles: row-major codes go
+//      straight to HBM, the transposed codes are built by byte permutes in
+//      registers, so both outputs are written in full 128-byte lines.
 #include "device_common.h"
 #include "internal.h"
 
@@ -21,9 +21,10 @@ namespace fp8mlp {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTile = 128;         // cast tile: 128 x 128 elements
-constexpr int kLdsT = kTile + 16;  // transposed-tile row stride in LDS (bytes)
+constexpr int kThreads = 256;      // amax kernel
+constexpr int kCastThreads = 512;  // cast kernel: 8 waves
+constexpr int kTR = 128;           // cast tile rows (8 waves x 16 rows)
+constexpr int kTC = 256;           // cast tile columns (64 lanes x 4 columns)
 
 __device__ __forceinline__ const QuantJob& job_of(const QuantBatch& b, int& local_blk) {
   int j = 0;
@@ -123,91 +124,96 @@ __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const Divid
   return pack4_fp8<FMT>(a, b, c, e);
 }
 
+// 4x4 byte transpose: r[i] holds bytes (i,0..3); c[j] gets bytes (0..3,j).
+__device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4]) {
+  // v_perm_b32(S0, S1, sel): selector byte values 0-3 pick bytes of S1, 4-7 bytes of S0
+  const uint32_t t0 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
+  const uint32_t t1 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
+  const uint32_t t2 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);  // r2b0 r3b0 r2b1 r3b1
+  const uint32_t t3 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);  // r2b2 r3b2 r2b3 r3b3
+  c[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  c[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  c[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  c[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// Tiles of kTR x kTC elements: wave w takes rows [16w, 16w+16), lane l the
+// 4 columns [4l, 4l+4).  Row-major codes leave as 4-byte stores (256
+// contiguous bytes per row and wave instruction); transposed codes are
+// assembled in registers, 16 rows of one column per 16-byte store, so each
+// transposed row receives 128 contiguous bytes from the block.
 template <int FMT, int MODE>
-__device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t* lds) {
+__device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d) {
   const int64_t rows = jb.rows, cols = jb.cols, ldx = jb.ldx;
   const uint16_t* x = jb.x;
   uint8_t* q = jb.q;
   uint8_t* qt = jb.qt;
-  const int64_t ntr = (rows + kTile - 1) / kTile, ntc = (cols + kTile - 1) / kTile;
+  const int64_t ntr = (rows + kTR - 1) / kTR, ntc = (cols + kTC - 1) / kTC;
   const int64_t ntiles = ntr * ntc;
-  const bool vec_in = aligned16(x) && (ldx % 8 == 0);
-  const bool vec_q = q == nullptr || (((reinterpret_cast<uintptr_t>(q) & 7u) == 0) && (jb.ldq % 8 == 0));
+  const bool vec_in = ((reinterpret_cast<uintptr_t>(x) & 7u) == 0) && (ldx % 4 == 0);
+  const bool vec_q = q == nullptr || (((reinterpret_cast<uintptr_t>(q) & 3u) == 0) && (jb.ldq % 4 == 0));
   const bool vec_qt = qt == nullptr || (aligned16(qt) && (jb.ldqt % 16 == 0));
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int64_t t = lb; t < ntiles; t += jb.nblocks) {
-    const int64_t r0 = (t / ntc) * kTile, c0 = (t % ntc) * kTile;
-    const bool full = r0 + kTile <= rows && c0 + kTile <= cols && vec_in && vec_q && vec_qt;
+    const int64_t r0 = (t / ntc) * kTR, c0 = (t % ntc) * kTC;
+    const bool full = r0 + kTR <= rows && c0 + kTC <= cols && vec_in && vec_q && vec_qt;
     if (full) {
+      const int64_t rb = r0 + wave * 16, cb = c0 + lane * 4;
+      v2u in[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int id = tid + kThreads * i;
-        const int row = id >> 4, c16 = id & 15;
-        const v4u v = __builtin_nontemporal_load(
-            reinterpret_cast<const v4u*>(x + (r0 + row) * ldx + c0 + c16 * 8));
-        const uint32_t lo = quant4<FMT, MODE>(v[0], v[1], d);
-        const uint32_t hi = quant4<FMT, MODE>(v[2], v[3], d);
-        if (q) {
-          v2u o = {lo, hi};
-          *reinterpret_cast<v2u*>(q + (r0 + row) * jb.ldq + c0 + c16 * 8) = o;
-        }
-        if (qt) {
-          uint8_t* col = lds + (c16 * 8) * kLdsT + row;
+      for (int i = 0; i < 16; ++i)
+        in[i] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(x + (rb + i) * ldx + cb));
+      uint32_t code[16];  // codes of the 4 columns of each row
 #pragma unroll
-          for (int e = 0; e < 4; ++e) col[e * kLdsT] = (uint8_t)(lo >> (8 * e));
+      for (int i = 0; i < 16; ++i) code[i] = quant4<FMT, MODE>(in[i][0], in[i][1], d);
+      if (q) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) col[(4 + e) * kLdsT] = (uint8_t)(hi >> (8 * e));
-        }
+        for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(q + (rb + i) * jb.ldq + cb) = code[i];
       }
       if (qt) {
-        __syncthreads();
+        uint32_t col[4][4];  // col[j][k]: column j, rows 4k..4k+3
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int id = tid + kThreads * i;
-          const int col = id >> 3, ch = id & 7;
-          const v4u v = *reinterpret_cast<const v4u*>(lds + col * kLdsT + ch * 16);
-          *reinterpret_cast<v4u*>(qt + (c0 + col) * jb.ldqt + r0 + ch * 16) = v;
+        for (int k = 0; k < 4; ++k) {
+          uint32_t c4[4];
+          transpose4x4(code + 4 * k, c4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) col[j][k] = c4[j];
         }
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v4u o = {col[j][0], col[j][1], col[j][2], col[j][3]};
+          *reinterpret_cast<v4u*>(qt + (cb + j) * jb.ldqt + rb) = o;
+        }
       }
     } else {
       // ragged or unaligned tile: element by element
-      for (int e = tid; e < kTile * kTile; e += kThreads) {
-        const int row = e >> 7, col = e & (kTile - 1);
+      for (int e = tid; e < kTR * kTC; e += kCastThreads) {
+        const int row = e / kTC, col = e % kTC;
         if (r0 + row < rows && c0 + col < cols) {
           const uint32_t bits = x[(r0 + row) * ldx + c0 + col];
           const uint32_t code = pack4_fp8<FMT>(div_rn(d, cast_value<MODE>(bits)), 0.f, 0.f, 0.f) & 0xFFu;
           if (q) q[(r0 + row) * jb.ldq + c0 + col] = (uint8_t)code;
-          if (qt) lds[col * kLdsT + row] = (uint8_t)code;
+          if (qt) qt[(c0 + col) * jb.ldqt + r0 + row] = (uint8_t)code;
         }
-      }
-      if (qt) {
-        __syncthreads();
-        for (int e = tid; e < kTile * kTile; e += kThreads) {
-          const int col = e >> 7, row = e & (kTile - 1);
-          if (r0 + row < rows && c0 + col < cols)
-            qt[(c0 + col) * jb.ldqt + r0 + row] = lds[col * kLdsT + row];
-        }
-        __syncthreads();
       }
     }
   }
 }
 
-__global__ void __launch_bounds__(kThreads) cast_kernel(QuantBatch b) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kTile * kLdsT];
-  __shared__ uint32_t red[kThreads / 64];
+template <int FMT, int MODE>
+__global__ void __launch_bounds__(kCastThreads) cast_kernel(QuantBatch b) {
+  __shared__ uint32_t red[kCastThreads / 64];
   int lb;
   const QuantJob& jb = job_of(b, lb);
   // 1. amax from the partials (integer max of non-negative bit patterns)
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < jb.nparts; i += kThreads) {
+  for (int i = threadIdx.x; i < jb.nparts; i += kCastThreads) {
     uint32_t v = jb.partials[i];
     m = m > v ? m : v;
   }
   m = block_max_u32(m, red);
   float amax;
-  if (jb.mode == kModeRelu2) {
+  if constexpr (MODE == kModeRelu2) {
     // max over the tensor of RN_bf16(relu(h)^2) = RN_bf16(relu(max h)^2)
     // (x -> x^2 and rounding are monotone on x >= 0)
     const float mh = __uint_as_float(m);
@@ -216,7 +222,7 @@ __global__ void __launch_bounds__(kThreads) cast_kernel(QuantBatch b) {
   } else {
     amax = bf16_to_f32(m);
   }
-  const float fm = fmt_max(jb.fmt);
+  constexpr float fm = FMT == kE4M3 ? kFmaxE4M3 : kFmaxE5M2;
   const float s = amax == 0.0f ? 1.0f : amax / fm;  // IEEE division, correctly rounded
   if (lb == 0 && threadIdx.x == 0) {
     *jb.scale = s;
@@ -224,17 +230,11 @@ __global__ void __launch_bounds__(kThreads) cast_kernel(QuantBatch b) {
   }
   const Divider d = make_divider(s, amax);
   // 2. cast
-  if (jb.fmt == kE4M3) {
-    if (jb.mode == kModeRelu2) cast_tiles<kE4M3, kModeRelu2>(jb, lb, d, lds);
-    else cast_tiles<kE4M3, kModePlain>(jb, lb, d, lds);
-  } else {
-    if (jb.mode == kModeRelu2) cast_tiles<kE5M2, kModeRelu2>(jb, lb, d, lds);
-    else cast_tiles<kE5M2, kModePlain>(jb, lb, d, lds);
-  }
+  cast_tiles<FMT, MODE>(jb, lb, d);
 }
 
 int cast_blocks_for(int64_t rows, int64_t cols) {
-  const int64_t tiles = ((rows + kTile - 1) / kTile) * ((cols + kTile - 1) / kTile);
+  const int64_t tiles = ((rows + kTR - 1) / kTR) * ((cols + kTC - 1) / kTC);
   return (int)(tiles < 2048 ? tiles : 2048);
 }
 
@@ -263,11 +263,21 @@ hipError_t launch_amax_partials(QuantBatch& b, hipStream_t st) {
 hipError_t launch_cast(QuantBatch& b, hipStream_t st) {
   int total = 0;
   for (int i = 0; i < b.njobs; ++i) {
+    // one launch handles jobs of a single format and mode
+    if (b.job[i].fmt != b.job[0].fmt || b.job[i].mode != b.job[0].mode) return hipErrorInvalidValue;
     b.job[i].blk_begin = total;
     b.job[i].nblocks = cast_blocks_for(b.job[i].rows, b.job[i].cols);
     total += b.job[i].nblocks;
   }
-  hipLaunchKernelGGL(cast_kernel, dim3(total), dim3(kThreads), 0, st, b);
+  const int fmt = b.job[0].fmt, mode = b.job[0].mode;
+  if (fmt == kE4M3 && mode == kModePlain)
+    hipLaunchKernelGGL((cast_kernel<kE4M3, kModePlain>), dim3(total), dim3(kCastThreads), 0, st, b);
+  else if (fmt == kE4M3)
+    hipLaunchKernelGGL((cast_kernel<kE4M3, kModeRelu2>), dim3(total), dim3(kCastThreads), 0, st, b);
+  else if (mode == kModePlain)
+    hipLaunchKernelGGL((cast_kernel<kE5M2, kModePlain>), dim3(total), dim3(kCastThreads), 0, st, b);
+  else
+    hipLaunchKernelGGL((cast_kernel<kE5M2, kModeRelu2>), dim3(total), dim3(kCastThreads), 0, st, b);
   return hipGetLastError();
 }
 
