@@ -28,7 +28,7 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, rows_per_gemm: int = 16):
+def cpu_baseline(w, rows_per_gemm: int = 384):
     """Oracle GEMM rate on a bounded sample: rows_per_gemm output rows of each
     of the six GEMMs of the block (FP8 operands from the oracle's quantiser)."""
     import numpy as np
@@ -71,6 +71,24 @@ def cpu_baseline(w, rows_per_gemm: int = 16):
     }
 
 
+def measured_traffic():
+    """HBM bytes per launch of the roofline kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (profiles/), or None when the
+    GEMM source has changed since those counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "gemm_down_proj_traffic.json")
+    src = os.path.join(ROOT, "fp8_tensorwise_scaled_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_hip_sha256") != digest:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,6 +96,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemm-reps", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 5 plain device copies of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "
@@ -150,6 +170,35 @@ def main() -> int:
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     log(f"down-proj GEMM {gemm_ms * 1e3:.1f} us, {gemm_tflops:.1f} TFLOP/s")
 
+    # HBM-bound kernel: quantisation of a [M, h] bf16 tensor (the dH shape) to
+    # row-major and transposed E5M2 codes, amax pass included.
+    qx = torch.empty((M, h), dtype=torch.bfloat16, device=dev)
+    qx.normal_(0.0, 1e-3)
+    qq = torch.empty((M, h), dtype=torch.uint8, device=dev)
+    qqt = torch.empty((h, M), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        api.fp8_amax_quant(qx, api.E5M2, q=qq, qt=qqt)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.gemm_reps):
+        api.fp8_amax_quant(qx, api.E5M2, q=qq, qt=qqt)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    quant_ms = ev0.elapsed_time(ev1) / args.gemm_reps
+    # algorithmic bytes: amax pass reads 2 B/elem; cast reads 2 B, writes 1 B + 1 B
+    quant_bytes = M * h * (2 + 2 + 1 + 1)
+    quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+    log(f"quantise [M,h] E5M2 + transpose: {quant_ms * 1e3:.1f} us, {quant_gbs:.0f} GB/s")
+
+    if args.copy_calibration:
+        cbytes = 256 << 20
+        src = torch.empty(cbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 5 copies of {cbytes} bytes")
+
     result = {
         "metric": "FP8 relu² MLP fwd+bwd TFLOP/s (d=3072,h=12288) and % of dense FP8 MFMA peak",
         "value": round(tflops, 2),
@@ -168,7 +217,8 @@ def main() -> int:
         "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "tokens_per_s_equiv": round(M / (ms * 1e-3)),
         "roofline": {
-            "kernel": "gemm_nt_kernel<E4M3,E4M3,256,256,store> (down-projection fwd, 8192x3072x12288)",
+            "kernel": "gemm_nt_kernel<0,0,256,192,0> (E4M3 x E4M3, plain store; down-projection fwd, "
+                      "M=8192 N=3072 K=12288)",
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),
             "peak": PEAK_FP8_TFLOPS,
@@ -177,7 +227,14 @@ def main() -> int:
             "traffic": None,
             "avg_launch_us": round(gemm_ms * 1e3, 2),
         },
+        "quantize": {
+            "what": "fp8_amax_quant of a [8192, 12288] bf16 tensor to E5M2 codes and transposed codes",
+            "bound": "hbm", "achieved_GBps": round(quant_gbs, 1), "peak_GBps": PEAK_HBM_GBS,
+            "frac": round(quant_gbs / PEAK_HBM_GBS, 4), "us": round(quant_ms * 1e3, 2),
+            "algorithmic_bytes": quant_bytes,
+        },
     }
+    result["roofline"]["traffic"] = measured_traffic()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w)
