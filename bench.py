@@ -89,6 +89,84 @@ def measured_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+def _time_steps(step, steps, warmup):
+    """Average ms per call of step() over `steps` calls after `warmup`, HIP
+    events on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def bench_other(args) -> int:
+    """Projection set (M=32768) or LM head (padded and unpadded vocabulary):
+    one step = forward + backward of every linear, quantisations included."""
+    import numpy as np
+    import torch
+
+    from fp8_tensorwise_scaled_amd import synth, workloads
+
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    common = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "unit": "TFLOP/s"}
+    if args.workload == "proj":
+        w = synth.PROJ_SET
+        log(f"generating projection-set inputs M={w.M}")
+        host = {n: w.input(n) for n in w.INPUTS}
+        host.update({n: w.grad(n) for n, _ in w.GRADS})
+        for i, (name, _, _) in enumerate(w.projections):
+            host["w_" + name] = w.weight(i)
+        tens = {k: t(v) for k, v in host.items()}
+        r = workloads.ProjectionSetRunner(w.M, dev)
+        ms = _time_steps(lambda: r.step(tens), args.steps, args.warmup)
+        tflops = r.flops / (ms * 1e-3) / 1e12
+        log(f"projection set: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
+        res = {"metric": "FP8 decoder projection set fwd+bwd TFLOP/s (Q,K,V,O + relu2 MLP)",
+               "value": round(tflops, 2), "ms_per_step": round(ms, 4),
+               "data": "synthetic (seeded N(0,1) inputs, N(0,1/sqrt(fan_in)) weights, N(0,1e-3) grads "
+                       "with 0.1% x100 outliers; bf16)",
+               "config": {"workload": "decoder projection set fwd+bwd M=32768 d=3072 (q 3072, k/v 1024, "
+                                      "o 3072, relu2 MLP 12288)", "M": w.M, "gemm_flops": r.flops},
+               "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+               "tokens_per_s_equiv": round(w.M / (ms * 1e-3))}
+    else:
+        w = synth.LM_HEAD_PADDED
+        n = synth.LM_HEAD_UNPADDED.N
+        log(f"generating LM-head inputs M={w.M} K={w.K} N={w.N}")
+        x, wt, g = w.tensors()
+        X = t(x)
+        out = {}
+        for N in (w.N, n):
+            W, G = t(wt[:N]), t(g[:, :N])
+            r = workloads.LMHeadRunner(w.M, w.K, N, dev)
+            ms = _time_steps(lambda: r.step(X, W, G), args.steps, args.warmup)
+            out[N] = (ms, r.flops / (ms * 1e-3) / 1e12)
+            log(f"LM head N={N}: {ms:.3f} ms/step, {out[N][1]:.1f} TFLOP/s")
+            del W, G, r
+        ms, tflops = out[w.N]
+        res = {"metric": "FP8 LM head fwd+bwd TFLOP/s (K=3072, vocabulary 50304 padded / 50257 unpadded)",
+               "value": round(tflops, 2), "ms_per_step": round(ms, 4),
+               "data": "synthetic (seeded N(0,1) X, N(0,0.02) W, N(0,1e-4) dLogits; padded rows/cols zero; bf16)",
+               "config": {"workload": f"LM head fwd+bwd M={w.M} K={w.K} N={w.N}", "M": w.M, "K": w.K,
+                          "N": w.N},
+               "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+               "unpadded": {"N": n, "ms_per_step": round(out[n][0], 4), "value": round(out[n][1], 2),
+                            "unit": "TFLOP/s", "pct_of_peak": round(100 * out[n][1] / PEAK_FP8_TFLOPS, 2)}}
+    res.update(common)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,11 +176,16 @@ def main() -> int:
     ap.add_argument("--gemm-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain device copies of 256 MiB (reference for HBM byte counters)")
+    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead"), default="mlp",
+                    help="mlp: the relu2 block M=8192 (default); proj: the decoder projection set at "
+                         "M=32768; lmhead: the LM head at vocabulary 50304 and 50257")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "
               "GPU (no sharding, no collectives)", file=sys.stderr)
         return 2
+    if args.workload != "mlp":
+        return bench_other(args)
 
     import numpy as np
     import torch

@@ -103,13 +103,53 @@ class ProjectionSetWorkload:
     projections: tuple = (("q", 3072, 3072), ("k", 3072, 1024), ("v", 3072, 1024),
                           ("o", 3072, 3072), ("up", 3072, 12288), ("down", 12288, 3072))
     name: str = ""
+    sigma_in: float = 1.0
+    sigma_grad: float = 1e-3
+    grad_outliers: float = 1e-3
 
     def weight(self, i: int):
+        """W_i [out, in] ~ N(0, 1/sqrt(in)); seeds 11..16 in projection order."""
         _, fin, fout = self.projections[i]
         return normal_bf16((fout, fin), 1.0 / math.sqrt(fin), 1000 * self.wid + 11 + i)
 
+    INPUTS = ("x_attn", "x_o", "x_mlp")
+    GRADS = (("dq", 3072), ("dk", 1024), ("dv", 1024), ("do", 3072), ("dy_mlp", 3072))
+
+    def input(self, name: str):
+        """Layer inputs [M, 3072] ~ N(0, 1): the attention input shared by Q,
+        K and V (seed 21), the output-projection input (22) and the MLP input
+        (23).  The down-projection input is the block's own relu^2 activation."""
+        i = self.INPUTS.index(name)
+        return normal_bf16((self.M, 3072), self.sigma_in, 1000 * self.wid + 21 + i)
+
+    def grad(self, name: str):
+        """Output gradients ~ N(0, 1e-3) with 0.1% x100 outliers: dQ, dK, dV,
+        dO and the MLP block's dY (seeds 31..35)."""
+        i = [g for g, _ in self.GRADS].index(name)
+        return normal_bf16((self.M, self.GRADS[i][1]), self.sigma_grad, 1000 * self.wid + 31 + i,
+                           self.grad_outliers)
+
+    def mlp(self) -> "MLPWorkload":
+        """The relu^2 block of the layer as an MLPWorkload-like view."""
+        return _ProjMLP(self)
+
     def flops(self) -> int:
         return 6 * self.M * sum(fin * fout for _, fin, fout in self.projections)
+
+
+class _ProjMLP:
+    """X, W_up, W_down, dY of the projection set's MLP block, in the order
+    MLPWorkload.tensors() returns them."""
+
+    def __init__(self, p: ProjectionSetWorkload):
+        self.p, self.M, self.d, self.h = p, p.M, 3072, 12288
+
+    def tensors(self):
+        return (self.p.input("x_mlp"), self.p.weight(4), self.p.weight(5), self.p.grad("dy_mlp"))
+
+    @property
+    def flops(self) -> int:
+        return 12 * self.M * self.d * self.h
 
 
 @dataclass

@@ -1,0 +1,170 @@
+"""Runners that sequence the library's C-ABI calls for the larger workloads.
+
+Only buffer management and call order live here (torch provides the device
+memory); every step runs in the library's kernels.
+
+* `LinearSet`: one FP8 linear layer (forward, grad-input, grad-weight) with
+  its own dynamic tensorwise scales - the unit the pages apply to every
+  linear (decomputer.nl, "Doorvoer verhogen", first bullet).
+* `ProjectionSetRunner`: the six projections of one decoder layer of the
+  3.8B model (appendix configuration: hidden 3072, 24 query heads and 8
+  key/value heads of 128, relu2 MLP at 12288): Q, K and V share one
+  quantised input, O has its own, and the MLP runs as the fused block.
+* `LMHeadRunner`: the LM head at the padded (50304, a multiple of 64) and
+  the unpadded (50257) vocabulary (decomputer.nl, "Vroege experimenten"
+  item 4; padded rows of W and columns of dLogits are zero).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import api
+from .api import E4M3, E5M2
+
+
+def _bf16(shape, device):
+    return torch.empty(shape, dtype=torch.bfloat16, device=device)
+
+
+def _u8(shape, device, zero=False):
+    f = torch.zeros if zero else torch.empty
+    return f(shape, dtype=torch.uint8, device=device)
+
+
+def _f32(n, device):
+    return torch.empty(n, dtype=torch.float32, device=device)
+
+
+@dataclass
+class QuantOut:
+    """Codes of a [rows, cols] tensor: q [rows, ld_q], qt [cols, ld_qt], scale."""
+    q: torch.Tensor
+    qt: torch.Tensor
+    scale: torch.Tensor
+    amax: torch.Tensor
+    ws: torch.Tensor
+
+    @staticmethod
+    def alloc(rows, cols, device, pad_cols_to=1, pad_rows_to=1):
+        """Row-major codes padded to a multiple of pad_cols_to columns and
+        transposed codes padded to pad_rows_to, padding zero-filled."""
+        cp = -(-cols // pad_cols_to) * pad_cols_to
+        rp = -(-rows // pad_rows_to) * pad_rows_to
+        q = _u8((rows, cp), device, zero=cp != cols)
+        qt = _u8((cols, rp), device, zero=rp != rows)
+        ws = torch.empty(max(api._native.lib().fp8_amax_quant_workspace_bytes(rows, cols), 16),
+                         dtype=torch.uint8, device=device)
+        return QuantOut(q, qt, _f32(1, device), _f32(1, device), ws)
+
+    def run(self, x, fmt, rows, cols):
+        api.fp8_amax_quant(x, fmt, q=self.q[:, :cols], qt=self.qt[:, :rows], scale=self.scale,
+                           amax=self.amax, ws=self.ws)
+        return self
+
+
+class LinearSet:
+    """Buffers and calls for one FP8 linear: Y = X W^T, dX = dY W, dW = dY^T X."""
+
+    def __init__(self, M, n_in, n_out, device, x_quant: QuantOut | None = None):
+        self.M, self.n_in, self.n_out = M, n_in, n_out
+        self.xq = x_quant or QuantOut.alloc(M, n_in, device)
+        self.wq = QuantOut.alloc(n_out, n_in, device)
+        self.gq = QuantOut.alloc(M, n_out, device)
+        self.y = _bf16((M, n_out), device)
+        self.dx = _bf16((M, n_in), device)
+        self.dw = _bf16((n_out, n_in), device)
+
+    def forward(self, x, w, quantize_x=True):
+        if quantize_x:
+            self.xq.run(x, E4M3, self.M, self.n_in)
+        self.wq.run(w, E4M3, self.n_out, self.n_in)
+        api.fp8_linear_fwd(self.xq.q[:, :self.n_in], self.xq.scale, self.wq.q[:, :self.n_in], self.wq.scale,
+                           out=self.y)
+        return self.y
+
+    def backward(self, dy):
+        self.gq.run(dy, E5M2, self.M, self.n_out)
+        api.fp8_linear_dgrad(self.gq.q[:, :self.n_out], self.gq.scale, self.wq.qt[:, :self.n_out],
+                             self.wq.scale, out=self.dx)
+        api.fp8_linear_wgrad(self.gq.qt[:, :self.M], self.gq.scale, self.xq.qt[:, :self.M], self.xq.scale,
+                             out=self.dw)
+        return self.dx, self.dw
+
+    @property
+    def flops(self):
+        return 6 * self.M * self.n_in * self.n_out
+
+
+class ProjectionSetRunner:
+    """Q, K, V (shared input), O and the relu^2 MLP block of one decoder layer."""
+
+    def __init__(self, M, device, d=3072, q_dim=3072, kv_dim=1024, h=12288):
+        self.M, self.d, self.h = M, d, h
+        self.x_attn_q = QuantOut.alloc(M, d, device)
+        self.q = LinearSet(M, d, q_dim, device, x_quant=self.x_attn_q)
+        self.k = LinearSet(M, d, kv_dim, device, x_quant=self.x_attn_q)
+        self.v = LinearSet(M, d, kv_dim, device, x_quant=self.x_attn_q)
+        self.o = LinearSet(M, q_dim, d, device)
+        self.saved = api.Relu2MlpSaved.empty(M, d, h, device)
+        self.ws_f = api.relu2_mlp_fwd_workspace(M, d, h, device)
+        self.ws_b = api.relu2_mlp_bwd_workspace(M, d, h, device)
+        self.y_mlp = _bf16((M, d), device)
+        self.dx_mlp = _bf16((M, d), device)
+        self.dw_up = _bf16((h, d), device)
+        self.dw_down = _bf16((d, h), device)
+        self.bsc = _f32(2, device)
+
+    def step(self, t):
+        """t: dict of bf16 tensors x_attn, w_q, w_k, w_v, x_o, w_o, x_mlp, w_up, w_down,
+        dq, dk, dv, do, dy_mlp.  One forward and backward of all six projections."""
+        self.x_attn_q.run(t["x_attn"], E4M3, self.M, self.d)
+        self.q.forward(None, t["w_q"], quantize_x=False)
+        self.k.forward(None, t["w_k"], quantize_x=False)
+        self.v.forward(None, t["w_v"], quantize_x=False)
+        self.o.forward(t["x_o"], t["w_o"])
+        api.relu2_mlp_fwd(t["x_mlp"], t["w_up"], t["w_down"], y=self.y_mlp, saved=self.saved, ws=self.ws_f)
+        self.q.backward(t["dq"])
+        self.k.backward(t["dk"])
+        self.v.backward(t["dv"])
+        self.o.backward(t["do"])
+        api.relu2_mlp_bwd(t["dy_mlp"], self.saved, dx=self.dx_mlp, dw_up=self.dw_up, dw_down=self.dw_down,
+                          bwd_scales=self.bsc, ws=self.ws_b)
+
+    @property
+    def flops(self):
+        return self.q.flops + self.k.flops + self.v.flops + self.o.flops + 12 * self.M * self.d * self.h
+
+
+class LMHeadRunner:
+    """LM head fwd+bwd for vocabulary N (padded or not).
+
+    The grad-input GEMM reduces over the vocabulary, which the kernel needs
+    in multiples of 16: the codes of dLogits and of W^T are written into
+    zero-filled buffers padded to a multiple of 16 along that axis, so the
+    reduction runs over the padded length with exact zeros past N."""
+
+    def __init__(self, M, K, N, device):
+        self.M, self.K, self.N = M, K, N
+        self.Np = -(-N // 16) * 16
+        self.xq = QuantOut.alloc(M, K, device)
+        self.wq = QuantOut.alloc(N, K, device, pad_rows_to=16)       # wq.qt: [K, Np]
+        self.gq = QuantOut.alloc(M, N, device, pad_cols_to=16)       # gq.q:  [M, Np]
+        self.y = _bf16((M, N), device)
+        self.dx = _bf16((M, K), device)
+        self.dw = _bf16((N, K), device)
+
+    def step(self, x, w, dlogits):
+        M, K, N, Np = self.M, self.K, self.N, self.Np
+        self.xq.run(x, E4M3, M, K)
+        self.wq.run(w, E4M3, N, K)
+        api.fp8_linear_fwd(self.xq.q, self.xq.scale, self.wq.q, self.wq.scale, out=self.y)
+        self.gq.run(dlogits, E5M2, M, N)
+        api.fp8_linear_dgrad(self.gq.q[:, :Np], self.gq.scale, self.wq.qt[:, :Np], self.wq.scale,
+                             out=self.dx)
+        api.fp8_linear_wgrad(self.gq.qt, self.gq.scale, self.xq.qt, self.xq.scale, out=self.dw)
+
+    @property
+    def flops(self):
+        return 6 * self.M * self.K * self.N

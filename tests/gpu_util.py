@@ -59,14 +59,28 @@ def gemm_bound(ref_bits: np.ndarray, sabs_bits: np.ndarray, K: int) -> np.ndarra
     return 1.5 * ulp_bf16(r) + (1 + 2.0 ** -8) * (HW_GROUP_TRUNC + (K / 64 + 2) * 2.0 ** -24) * sabs
 
 
+def within_floors(K):
+    """Aggregate floors (fraction within one and two bf16 ulps) that guard
+    against a bound grown loose.  Measured: 99.68-99.97% / >= 99.87% for
+    K <= 12288; the grad-weight GEMMs that reduce over 32768 tokens of a dY
+    with 0.1% x100 outliers reach 99.49-99.59% / 99.71-99.76% (more outputs
+    are small next to the sum of |products| their truncation error scales
+    with); the LM head's 50304-long reduction, without outliers, 99.92%."""
+    return (0.995, 0.998) if K is None or K <= 12288 else (0.99, 0.995)
+
+
 def gemm_close(got_bits: np.ndarray, ref_bits: np.ndarray, what: str = "", *, sabs_bits=None, K=None,
-               bound=None, min_within1=0.995, min_within2=0.998):
+               bound=None, min_within1=None, min_within2=None):
     """GEMM output parity.
 
     Element-wise: |gpu - oracle| <= gemm_bound (or an explicit `bound`).
     Aggregate: the fraction of elements within one bf16 ulp of the oracle is
-    at least min_within1, within two ulps at least min_within2.  Also prints
-    max|gpu - oracle| / max|oracle| and the one-ulp fraction."""
+    at least min_within1, within two ulps at least min_within2 (defaults from
+    within_floors(K)).  Also prints max|gpu - oracle| / max|oracle| and the
+    one-ulp fraction."""
+    f1, f2 = within_floors(K)
+    min_within1 = f1 if min_within1 is None else min_within1
+    min_within2 = f2 if min_within2 is None else min_within2
     g, r = bits_f64(got_bits), bits_f64(ref_bits)
     assert g.shape == r.shape, (g.shape, r.shape)
     err = np.abs(g - r)
@@ -107,3 +121,26 @@ def oracle_gemm(kind: str, a, fa, sa, b, fb, sb, rows=None):
 def check_gemm(got_bits, kind, a, fa, sa, b, fb, sb, what, rows=None):
     ref, sabs, K = oracle_gemm(kind, a, fa, sa, b, fb, sb, rows=rows)
     return gemm_close(got_bits, ref, what, sabs_bits=sabs, K=K)
+
+
+def collect_block(inputs, y, saved, ws_f, ws_b, dx, dwu, dwd, bsc) -> dict:
+    """Host copies of one relu^2 block pass: inputs, outputs, the saved
+    forward quantities and the workspace intermediates (codes, dH)."""
+    from fp8_tensorwise_scaled_amd import api
+
+    x, wu, wd, dy = inputs
+    M, d = x.shape
+    h = wu.shape[0]
+    of = api.workspace_layout("fwd", M, d, h)
+    ob = api.workspace_layout("bwd", M, d, h)
+    wf, wb = ws_f.cpu().numpy(), ws_b.cpu().numpy()
+    sl = lambda buf, o, n: buf[o:o + n]
+    return dict(
+        x=x, wu=wu, wd=wd, dy=dy, y=bf16_bits(y), dx=bf16_bits(dx), dw_up=bf16_bits(dwu),
+        dw_down=bf16_bits(dwd), h=bf16_bits(saved.h), scales=f32(saved.scales), bsc=f32(bsc),
+        xq_t=u8(saved.xq_t), uq_t=u8(saved.uq_t), dq_t=u8(saved.dq_t), aq_t=u8(saved.aq_t),
+        xq=sl(wf, of[0], M * d).reshape(M, d), uq=sl(wf, of[1], h * d).reshape(h, d),
+        dq=sl(wf, of[2], d * h).reshape(d, h), aq=sl(wf, of[3], M * h).reshape(M, h),
+        gq=sl(wb, ob[0], M * d).reshape(M, d), gq_t=sl(wb, ob[1], d * M).reshape(d, M),
+        dh=sl(wb, ob[2], 2 * M * h).view(np.uint16).reshape(M, h), hq=sl(wb, ob[3], M * h).reshape(M, h),
+        hq_t=sl(wb, ob[4], h * M).reshape(h, M))

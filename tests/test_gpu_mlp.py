@@ -1,16 +1,17 @@
 """GPU parity of the relu^2 MLP block (relu2_mlp_fwd / relu2_mlp_bwd).
 
-Stage-wise: every quantisation is bit-exact given the GPU's own inputs to
-it, every GEMM (with its fused epilogue) is within the GEMM tolerance given
-the GPU's own FP8 operands.  End to end: the oracle chain from the same bf16
-inputs, within max-relative 5e-3."""
+Every expected value is the oracle chain run on the same seeded bf16 inputs
+(tests/mlp_chain.py): each stage is bit-exact (codes, scales) or within the
+GEMM bound (GEMM outputs) wherever its inputs equal the oracle's bit for bit,
+and within the chain bar everywhere."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from fp8_tensorwise_scaled_amd import synth
-from tests.gpu_util import bf16_bits, bits_f64, check_gemm, f32, gemm_bound, gemm_close, oracle_gemm, to_dev_bf16, u8, ulp_bf16
+from tests.gpu_util import bits_f64, collect_block, to_dev_bf16, ulp_bf16
+from tests.mlp_chain import compare_block, full_chain_scales, golden_scales, sampled_chain
 
 pytestmark = pytest.mark.gpu
 E4, E5 = oracle.E4M3, oracle.E5M2
@@ -27,32 +28,7 @@ def run_block(w):
     y, saved = api.relu2_mlp_fwd(to_dev_bf16(x), to_dev_bf16(wu), to_dev_bf16(wd), ws=ws_f)
     dx, dwu, dwd, bsc = api.relu2_mlp_bwd(to_dev_bf16(dy), saved, ws=ws_b)
     torch.cuda.synchronize()
-    of = api.workspace_layout("fwd", M, d, h)
-    ob = api.workspace_layout("bwd", M, d, h)
-    wf, wb = ws_f.cpu().numpy(), ws_b.cpu().numpy()
-    sl = lambda buf, o, n: buf[o:o + n]
-    out = dict(
-        x=x, wu=wu, wd=wd, dy=dy, y=bf16_bits(y), dx=bf16_bits(dx), dw_up=bf16_bits(dwu),
-        dw_down=bf16_bits(dwd), h=bf16_bits(saved.h), scales=f32(saved.scales), bsc=f32(bsc),
-        xq_t=u8(saved.xq_t), uq_t=u8(saved.uq_t), dq_t=u8(saved.dq_t), aq_t=u8(saved.aq_t),
-        xq=sl(wf, of[0], M * d).reshape(M, d), uq=sl(wf, of[1], h * d).reshape(h, d),
-        dq=sl(wf, of[2], d * h).reshape(d, h), aq=sl(wf, of[3], M * h).reshape(M, h),
-        gq=sl(wb, ob[0], M * d).reshape(M, d), gq_t=sl(wb, ob[1], d * M).reshape(d, M),
-        dh=sl(wb, ob[2], 2 * M * h).view(np.uint16).reshape(M, h), hq=sl(wb, ob[3], M * h).reshape(M, h),
-        hq_t=sl(wb, ob[4], h * M).reshape(h, M))
-    return out
-
-
-def check_dh(dh_gpu, h, gq, sg, dq, sd, what, rows=None):
-    """dH = RN_bf16(2 relu(H) dA), dA the down-projection grad-input GEMM.
-    Tolerance: the GEMM bound on dA carried through the exact product with
-    2 relu(H), plus one bf16 ulp of dH for the final rounding."""
-    da, sabs, K = oracle_gemm("nn", gq, E5, sg, dq, E4, sd, rows=rows)
-    ref = oracle.relu2_bwd(h, da)
-    two_r = 2 * np.maximum(bits_f64(h), 0.0)
-    da_tol = gemm_bound(da, sabs, K)
-    bound = 1.5 * ulp_bf16(bits_f64(ref)) + (1 + 2.0 ** -8) * two_r * da_tol
-    gemm_close(dh_gpu, ref, what, bound=bound)
+    return collect_block((x, wu, wd, dy), y, saved, ws_f, ws_b, dx, dwu, dwd, bsc)
 
 
 @pytest.fixture(scope="module")
@@ -69,36 +45,14 @@ def test_fwd_quantisation_bit_exact(small):
         assert (q == rq).all() and (qt == rq.T).all(), name
 
 
-def test_up_gemm_and_relu2_cast(small):
+def test_small_block_every_stage(small):
+    """M=2048, d=768, h=3072: every stage on every row and column against
+    the oracle chain run on the same bf16 inputs."""
     g = small
-    sx, su, sd, sa = (float(v) for v in g["scales"])
-    check_gemm(g["h"], "nt", g["xq"], E4, sx, g["uq"], E4, su, "H")
-    # A = RN_bf16(relu(H)^2) quantised from the GPU's own H: bit-exact
-    a = oracle.relu2(g["h"])
-    rq, rs, _ = oracle.quant(a, E4)
-    assert np.float32(sa) == np.float32(rs)
-    assert (g["aq"] == rq).all() and (g["aq_t"] == rq.T).all()
-
-
-def test_down_gemm(small):
-    g = small
-    sx, su, sd, sa = (float(v) for v in g["scales"])
-    check_gemm(g["y"], "nt", g["aq"], E4, sa, g["dq"], E4, sd, "Y")
-
-
-def test_bwd_stages(small):
-    g = small
-    sx, su, sd, sa = (float(v) for v in g["scales"])
-    sg, sh = (float(v) for v in g["bsc"])
-    rq, rs, _ = oracle.quant(g["dy"], E5)
-    assert np.float32(sg) == np.float32(rs) and (g["gq"] == rq).all() and (g["gq_t"] == rq.T).all()
-    check_gemm(g["dw_down"], "tn", g["gq"], E5, sg, g["aq"], E4, sa, "dW_down")
-    # dH = RN_bf16(2 relu(H) dA) with dA the down-dgrad GEMM output
-    check_dh(g["dh"], g["h"], g["gq"], sg, g["dq"], sd, "dH")
-    hq, hs, _ = oracle.quant(g["dh"], E5)
-    assert np.float32(sh) == np.float32(hs) and (g["hq"] == hq).all() and (g["hq_t"] == hq.T).all()
-    check_gemm(g["dw_up"], "tn", g["hq"], E5, sh, g["xq"], E4, sx, "dW_up")
-    check_gemm(g["dx"], "nn", g["hq"], E5, sh, g["uq"], E4, su, "dX")
+    sc, _, _ = full_chain_scales(g["x"], g["wu"], g["wd"], g["dy"])
+    rows, cols = np.arange(g["x"].shape[0]), np.arange(g["wu"].shape[0])
+    o = sampled_chain(g["x"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
+    compare_block(g, o, sc, rows, cols)
 
 
 def test_end_to_end(small):
@@ -107,7 +61,7 @@ def test_end_to_end(small):
     value for E5M2) and a value near zero can cross the relu kink, so single
     elements of the chain can differ by several ulps: the comparison is a
     relative Frobenius error <= 1e-2 with >= 90% of elements within one bf16
-    ulp (stage-wise tests above carry the element-wise parity)."""
+    ulp (the stage comparison above carries the element-wise parity)."""
     g = small
     ref_f = oracle.mlp_fwd(g["x"], g["wu"], g["wd"])
     ref_b = oracle.mlp_bwd(g["dy"], ref_f)
@@ -122,29 +76,17 @@ def test_end_to_end(small):
 
 
 def test_3p8b_block_sampled():
-    """M=8192, d=3072, h=12288: quantisations bit-exact on whole tensors,
-    GEMM stages on 32 sampled rows (columns for the weight gradients)."""
-    g = run_block(synth.MLP_3P8B)
-    sx, su, sd, sa = (float(v) for v in g["scales"])
-    sg, sh = (float(v) for v in g["bsc"])
-    rq, rs, _ = oracle.quant(g["x"], E4)
-    assert np.float32(sx) == np.float32(rs) and (g["xq"] == rq).all()
-    rq, rs, _ = oracle.quant(g["wu"], E4)
-    assert np.float32(su) == np.float32(rs) and (g["uq"] == rq).all()
-    rq, rs, _ = oracle.quant(oracle.relu2(g["h"]), E4)
-    assert np.float32(sa) == np.float32(rs) and (g["aq"] == rq).all()
-    rq, rs, _ = oracle.quant(g["dh"], E5)
-    assert np.float32(sh) == np.float32(rs) and (g["hq"] == rq).all()
+    """M=8192, d=3072, h=12288: the block's tensor-wide scales against the
+    stored oracle values, every stage on 32 sampled token rows and 32 sampled
+    hidden columns against the oracle."""
+    w = synth.MLP_3P8B
+    g = run_block(w)
+    sc = golden_scales("mlp_3p8b", (g["x"], g["wu"], g["wd"], g["dy"]))
     rng = np.random.default_rng(11)
-    r = rng.choice(8192, 32, replace=False)
-    check_gemm(g["h"][r], "nt", g["xq"], E4, sx, g["uq"], E4, su, "H rows", rows=r)
-    check_gemm(g["y"][r], "nt", g["aq"], E4, sa, g["dq"], E4, sd, "Y rows", rows=r)
-    check_gemm(g["dx"][r], "nn", g["hq"], E5, sh, g["uq"], E4, su, "dX rows", rows=r)
-    check_dh(g["dh"][r], g["h"][r], g["gq"], sg, g["dq"], sd, "dH rows", rows=r)
-    ru = rng.choice(12288, 32, replace=False)
-    check_gemm(g["dw_up"][ru], "tn", g["hq"], E5, sh, g["xq"], E4, sx, "dW_up rows", rows=ru)
-    rd = rng.choice(3072, 32, replace=False)
-    check_gemm(g["dw_down"][rd], "tn", g["gq"], E5, sg, g["aq"], E4, sa, "dW_down rows", rows=rd)
+    rows = np.sort(rng.choice(w.M, 32, replace=False))
+    cols = np.sort(rng.choice(w.h, 32, replace=False))
+    o = sampled_chain(g["x"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
+    compare_block(g, o, sc, rows, cols)
 
 
 def test_deterministic_and_reuse():
