@@ -15,6 +15,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v3u __attribute__((ext_vector_type(3)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -106,6 +107,12 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   uint32_t m = 0;
   for (int i = 0; i < nw; ++i) m = m > red[i] ? m : red[i];
   return m;
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end return
+// zeros (the range check of the buffer unit), offsets are 32-bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 }  // namespace fp8mlp

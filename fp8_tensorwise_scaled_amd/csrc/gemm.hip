@@ -35,7 +35,6 @@ namespace fp8mlp {
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBK = 128;  // bytes of K per stage
 constexpr int kGroupM = 4;
 
@@ -47,31 +46,33 @@ constexpr int kGroupM = 4;
 // consecutive rows.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-template <int FA, int FB, int BM, int BN, int EPI>
+// WGM x WGN waves per block (64 * WGM * WGN threads), each owning a
+// (BM/WGM) x (BN/WGN) sub-tile.
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int EPI>
 struct Gemm {
-  static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
+  static constexpr int THREADS = 64 * WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
   static constexpr int FM = WM / 32, FN = WN / 32;
+  static_assert(FM * 32 == WM && FN * 32 == WN, "wave tile must be whole 32x32 MFMA tiles");
   static constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_LOADS = A_BYTES / (kThreads * 16);  // per thread per stage
-  static constexpr int B_LOADS = B_BYTES / (kThreads * 16);
+  static constexpr int A_LOADS = A_BYTES / (THREADS * 16);  // per thread per stage
+  static constexpr int B_LOADS = B_BYTES / (THREADS * 16);
+  static_assert(A_LOADS * THREADS * 16 == A_BYTES && B_LOADS * THREADS * 16 == B_BYTES, "whole loads");
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int CLD = BN * 2 + 16;  // epilogue C tile row stride (bytes)
   static constexpr int LDS = (2 * STAGE > BM * CLD) ? 2 * STAGE : BM * CLD;
 };
 
-template <int FA, int FB, int BM, int BN, int EPI>
-__global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int tiles_m, int tiles_n) {
-  using G = Gemm<FA, FB, BM, BN, EPI>;
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+  using G = Gemm<FA, FB, BM, BN, WGM, WGN, EPI>;
+  constexpr int kThreads = G::THREADS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
   __shared__ uint32_t red[kThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid & 1, wn = wid >> 1;
+  const int wm = wid % WGM, wn = wid / WGM;
 
   // ---- tile id: XCD-contiguous runs, grouped kGroupM tile-rows deep
   const int nt = tiles_m * tiles_n;
@@ -91,7 +92,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int ti
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a + m0 * g.lda, (uint32_t)((rows_a - 1) * g.lda + K));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b + n0 * g.ldb, (uint32_t)((rows_b - 1) * g.ldb + K));
 
-  // Per-thread 16-byte chunks loaded each stage: chunk id = tid + 256*j,
+  // Per-thread 16-byte chunks loaded each stage: chunk id = tid + THREADS*j,
   // row = id / 8, logical column chunk = id % 8 (eight lanes cover one
   // 128-byte row, so a wave load is 8 full rows).  In LDS the chunk goes to
   // position logical ^ swz(row) of its row.  Loads j < A_LOADS are A rows,
@@ -217,9 +218,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int ti
 
   // ---- epilogue
   // Each thread owns NCH 16-byte chunks of the output tile: chunk id
-  // tid + 256*it is row id / CPR, 8-column group id % CPR.
+  // tid + THREADS*it is row id / CPR, 8-column group id % CPR.
   constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
   constexpr int NCH = BM * CPR / kThreads;
+  static_assert(NCH * kThreads == BM * CPR, "whole epilogue chunks");
   const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
   const bool vec_aux = EPI != kEpiRelu2Bwd ||
                        (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0));
@@ -311,6 +313,25 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int ti
       }
       if (full) {
         *reinterpret_cast<v4u*>(g.c + gr * g.ldc + gc) = v;
+      } else if (gc + 8 <= g.N) {
+        // whole chunk, destination not 16-byte aligned (an odd or unaligned
+        // leading dimension): the widest stores its alignment allows
+        uint16_t* dst = g.c + gr * g.ldc + gc;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+        if ((a & 7u) == 0) {
+          reinterpret_cast<v2u*>(dst)[0] = v2u{v[0], v[1]};
+          reinterpret_cast<v2u*>(dst)[1] = v2u{v[2], v[3]};
+        } else if ((a & 3u) == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) reinterpret_cast<uint32_t*>(dst)[e] = v[e];
+        } else {
+          dst[0] = (uint16_t)v[0];
+          uint32_t* mid = reinterpret_cast<uint32_t*>(dst + 1);
+          mid[0] = __builtin_amdgcn_alignbyte(v[1], v[0], 2);
+          mid[1] = __builtin_amdgcn_alignbyte(v[2], v[1], 2);
+          mid[2] = __builtin_amdgcn_alignbyte(v[3], v[2], 2);
+          dst[7] = (uint16_t)(v[3] >> 16);
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -324,11 +345,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_nt_kernel(GemmArgs g, int ti
   }
 }
 
-template <int FA, int FB, int BM, int BN, int EPI>
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, BM, BN, EPI>), dim3(tiles_m * tiles_n), dim3(kThreads),
-                     0, st, g, tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, BM, BN, WGM, WGN, EPI>), dim3(tiles_m * tiles_n),
+                     dim3(64 * WGM * WGN), 0, st, g, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -344,18 +365,18 @@ int pick_bn(int64_t M, int64_t N) {
   return eff(192) > eff(256) * 1.02 ? 192 : 256;
 }
 
-template <int FA, int FB, int BN>
+template <int FA, int FB, int BN, int WGM, int WGN>
 hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
   switch (g.epi) {
-    case kEpiRelu2Max: return launch_cfg<FA, FB, 256, BN, kEpiRelu2Max>(g, st);
-    case kEpiRelu2Bwd: return launch_cfg<FA, FB, 256, BN, kEpiRelu2Bwd>(g, st);
-    default: return launch_cfg<FA, FB, 256, BN, kEpiStore>(g, st);
+    case kEpiRelu2Max: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Max>(g, st);
+    case kEpiRelu2Bwd: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Bwd>(g, st);
+    default: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStore>(g, st);
   }
 }
 
 template <int FA, int FB>
 hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
-  return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192>(g, st) : launch_bn<FA, FB, 256>(g, st);
+  return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192, 2, 2>(g, st) : launch_bn<FA, FB, 256, 2, 2>(g, st);
 }
 
 }  // namespace

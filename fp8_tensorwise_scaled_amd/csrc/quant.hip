@@ -61,9 +61,10 @@ __global__ void __launch_bounds__(kThreads) amax_partials_kernel(QuantBatch b) {
   const int nb = jb.nblocks;
   uint32_t m = 0;
   const bool vec = aligned16(x) && (ldx % 8 == 0) && (cols % 8 == 0);
-  if (vec && ldx == cols) {
-    // dense: one flat array of rows*cols/8 16-byte chunks
-    const int64_t nch = rows * cols / 8;
+  if (aligned16(x) && (ldx == cols || rows == 1)) {
+    // dense: one flat array of rows*cols/8 16-byte chunks and a tail
+    const int64_t n = rows * cols;
+    const int64_t nch = n / 8;
     const v4u* xv = reinterpret_cast<const v4u*>(x);
     int64_t i = (int64_t)lb * kThreads + threadIdx.x;
     const int64_t step = (int64_t)nb * kThreads;
@@ -80,6 +81,10 @@ __global__ void __launch_bounds__(kThreads) amax_partials_kernel(QuantBatch b) {
     }
     for (; i < nch; i += step) {
       uint32_t t = absmax8(xv[i]);
+      m = m > t ? m : t;
+    }
+    for (int64_t e = nch * 8 + (int64_t)lb * kThreads + threadIdx.x; e < n; e += step) {
+      uint32_t t = x[e] & 0x7FFFu;
       m = m > t ? m : t;
     }
   } else if (vec) {
@@ -151,18 +156,44 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d) {
   const int64_t ntr = (rows + kTR - 1) / kTR, ntc = (cols + kTC - 1) / kTC;
   const int64_t ntiles = ntr * ntc;
   const bool vec_in = ((reinterpret_cast<uintptr_t>(x) & 7u) == 0) && (ldx % 4 == 0);
+  // Rows that are not 8-byte aligned (odd leading dimension, unaligned base):
+  // a lane's 8 bytes come from dword-aligned buffer loads (8 bytes, or 12
+  // when they start mid-dword) realigned in registers.  The descriptor spans
+  // the dwords that hold tensor bytes, so every dword loaded holds at least
+  // one of them (and lies in the same page).
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
+  const uint32_t dlt = (uint32_t)(xa & 3u);
+  const int64_t xbytes = ((rows - 1) * ldx + cols) * 2 + dlt;
+  const bool buf_in = !vec_in && (xa & 1u) == 0 && xbytes < (int64_t{1} << 31);
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(reinterpret_cast<const void*>(xa - dlt), buf_in ? (uint32_t)((xbytes + 3) & ~int64_t{3}) : 0u);
   const bool vec_q = q == nullptr || (((reinterpret_cast<uintptr_t>(q) & 3u) == 0) && (jb.ldq % 4 == 0));
   const bool vec_qt = qt == nullptr || (aligned16(qt) && (jb.ldqt % 16 == 0));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int64_t t = lb; t < ntiles; t += jb.nblocks) {
     const int64_t r0 = (t / ntc) * kTR, c0 = (t % ntc) * kTC;
-    const bool full = r0 + kTR <= rows && c0 + kTC <= cols && vec_in && vec_q && vec_qt;
+    const bool full = r0 + kTR <= rows && c0 + kTC <= cols && (vec_in || buf_in) && vec_q && vec_qt;
     if (full) {
       const int64_t rb = r0 + wave * 16, cb = c0 + lane * 4;
       v2u in[16];
+      if (vec_in) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        in[i] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(x + (rb + i) * ldx + cb));
+        for (int i = 0; i < 16; ++i)
+          in[i] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(x + (rb + i) * ldx + cb));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // byte offset from the aligned base; its dword phase (0 or 2) is
+          // the same for every lane of the wave (row-uniform)
+          const uint32_t off = dlt + 2u * (uint32_t)((rb + i) * ldx + cb);
+          if ((off & 3u) == 0) {
+            in[i] = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, 0);
+          } else {
+            const v3u w = __builtin_amdgcn_raw_buffer_load_b96(rx, off - 2u, 0, 0);
+            in[i] = v2u{__builtin_amdgcn_alignbyte(w[1], w[0], 2), __builtin_amdgcn_alignbyte(w[2], w[1], 2)};
+          }
+        }
+      }
       uint32_t code[16];  // codes of the 4 columns of each row
 #pragma unroll
       for (int i = 0; i < 16; ++i) code[i] = quant4<FMT, MODE>(in[i][0], in[i][1], d);

@@ -92,6 +92,23 @@ def test_strided_output_and_operands():
     assert (Cb[:, N:] == 7).all()   # columns past N untouched
 
 
+def test_output_rows_not_16_byte_aligned():
+    """Odd leading dimension and a base 2 bytes off a dword: every store
+    alignment (2, 4, 8, 16 bytes) occurs among the rows."""
+    from fp8_tensorwise_scaled_amd import api
+
+    M, N, K = 264, 392, 256
+    qa, sa, qb, sb = quant_pair((M, K), (N, K), E4, E5, 98)
+    ldc = 401
+    flat = torch.full((1 + M * ldc,), 7, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    C = flat[1:].view(M, ldc)
+    api.fp8_linear_fwd(to_dev_u8(qa), scal(sa), to_dev_u8(qb), scal(sb), E4, E5, out=C[:, :N])
+    torch.cuda.synchronize()
+    Cb = bf16_bits(C)
+    check_gemm(Cb[:, :N], "nt", qa, E4, sa, qb, E5, sb, "odd ldc")
+    assert (Cb[:, N:] == 7).all() and int(bf16_bits(flat[:1])[0]) == 7   # nothing outside written
+
+
 @pytest.mark.parametrize("which", ["up_fwd", "down_dgrad", "up_wgrad"])
 def test_full_size_sampled_rows(which):
     """3.8B-model block shapes (M=8192, d=3072, h=12288) on the GPU, checked

@@ -12,16 +12,19 @@ pytestmark = pytest.mark.gpu
 FMTS = [oracle.E4M3, oracle.E5M2]
 
 
-def run_quant(x_np, fmt, ld=None, qt=True):
+def run_quant(x_np, fmt, ld=None, qt=True, offset=0):
+    """offset: elements between the allocation's start and x (2 bytes each,
+    so an odd offset leaves x off a dword boundary)."""
     from fp8_tensorwise_scaled_amd import api
 
     rows, cols = x_np.shape
-    if ld is None:
+    if ld is None and offset == 0:
         xd = to_dev_bf16(x_np)
     else:
-        buf = np.zeros((rows, ld), np.uint16)
-        buf[:, :cols] = x_np
-        xd = to_dev_bf16(buf)[:, :cols]
+        ld = cols if ld is None else ld
+        buf = np.zeros(offset + rows * ld, np.uint16)
+        buf[offset:].reshape(rows, ld)[:, :cols] = x_np
+        xd = to_dev_bf16(buf)[offset:].view(rows, ld)[:, :cols]
     q, qt_, s, a = api.fp8_amax_quant(xd, fmt, want_qt=qt)
     torch.cuda.synchronize()
     return u8(q), (u8(qt_) if qt else None), float(f32(s)[0]), float(f32(a)[0])
@@ -74,6 +77,19 @@ def test_strided_and_unaligned(fmt):
     check_against_oracle(x, fmt, ld=264)     # aligned ld > cols: vector path
     q, qt, s, a = run_quant(x, fmt, qt=False)
     assert qt is None and (q == oracle.quant(x, fmt)[0]).all()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_unaligned_rows_full_tiles(fmt):
+    """Rows that are not 8-byte aligned go through the realigning buffer-load
+    path on whole tiles (and the element path on the ragged edge)."""
+    x = synth.normal_bf16((300, 700), 1.0, 79)
+    check_against_oracle(x, fmt, ld=701)             # odd leading dimension
+    check_against_oracle(x, fmt, ld=702, offset=1)   # base off a dword boundary
+    x = synth.normal_bf16((257, 1001), 1.0, 80)
+    check_against_oracle(x, fmt)                     # dense, odd row length
+    x = synth.normal_bf16((128, 512), 1.0, 81)
+    check_against_oracle(x, fmt, ld=513, offset=3)   # whole tiles only, tensor ends mid-dword
 
 
 @pytest.mark.parametrize("fmt", FMTS)
