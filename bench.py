@@ -300,7 +300,7 @@ def main() -> int:
         "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "tokens_per_s_equiv": round(M / (ms * 1e-3)),
         "roofline": {
-            "kernel": "gemm_nt_kernel<0,0,256,192,0> (E4M3 x E4M3, plain store; down-projection fwd, "
+            "kernel": "gemm_nt_kernel<0,0,256,192,4,2,0> (E4M3 x E4M3, plain store, 8 waves; down-projection fwd, "
                       "M=8192 N=3072 K=12288)",
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),

@@ -11,9 +11,13 @@
 // Design for CDNA4:
 //  * v_mfma_f32_32x32x64_f8f6f4 (K = 64 per instruction, per-operand E4M3 or
 //    E5M2 selected by the instruction), fp32 accumulation.
-//  * 256 threads = 4 waves in a 2x2 grid; a 256x256 block tile gives each
-//    wave a 128x128 tile (4x4 MFMA tiles, 256 accumulator registers), which
-//    keeps LDS traffic per MFMA at its lowest.
+//  * 256x256 block tiles run 4 waves in a 2x2 grid, each wave a 128x128
+//    tile (4x4 MFMA tiles, 256 accumulator registers: LDS traffic per MFMA
+//    at its lowest).  256x192 tiles run 8 waves in a 4x2 grid of 64x96 wave
+//    tiles, two waves per SIMD, so one wave's LDS and barrier waits overlap
+//    the other's MFMAs.  With dense random FP8 operands the chip reaches its
+//    power limit near 1.4-1.6 GHz, so both layouts trade MFMA utilisation
+//    against the energy of the data they move.
 //  * K is consumed 128 bytes per stage; stages are double-buffered in LDS,
 //    loaded with 16-byte buffer loads into registers one stage ahead.  Rows
 //    are 128 bytes; the 16-byte chunk c of row r is stored at c ^ ((r>>1)&7)
@@ -376,7 +380,9 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
 
 template <int FA, int FB>
 hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
-  return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192, 2, 2>(g, st) : launch_bn<FA, FB, 256, 2, 2>(g, st);
+  // 256x192 tiles run 8 waves (4x2, 64x96 wave tiles, two waves per SIMD);
+  // 256x256 tiles 4 waves (2x2, 128x128 wave tiles)
+  return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192, 4, 2>(g, st) : launch_bn<FA, FB, 256, 2, 2>(g, st);
 }
 
 }  // namespace
