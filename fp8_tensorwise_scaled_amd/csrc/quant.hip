@@ -147,8 +147,19 @@ __device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t c[4])
 // contiguous bytes per row and wave instruction); transposed codes are
 // assembled in registers, 16 rows of one column per 16-byte store, so each
 // transposed row receives 128 contiguous bytes from the block.
+// Transposed tile image in LDS: row c (tile column, 0..255) holds the 128
+// codes of that column as eight 16-byte pieces k (tile rows 16k..16k+15).
+// Piece k of row c sits at slot k ^ ((c >> 2) & 7) of physical row
+// c ^ ((c >> 5) & 1): the 16 lanes of a 128-bit LDS access then hit 16
+// distinct bank groups both when a wave parks column pieces (lanes 4 columns
+// apart) and when it reads rows back (8 lanes per row).
+constexpr int kTImage = kTC * kTR;  // bytes
+__device__ __forceinline__ int timg_off(int c, int k) {
+  return (c ^ ((c >> 5) & 1)) * kTR + ((k ^ ((c >> 2) & 7)) << 4);
+}
+
 template <int FMT, int MODE>
-__device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d) {
+__device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t* tbuf) {
   const int64_t rows = jb.rows, cols = jb.cols, ldx = jb.ldx;
   const uint16_t* x = jb.x;
   uint8_t* q = jb.q;
@@ -170,6 +181,7 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d) {
   const bool vec_q = q == nullptr || (((reinterpret_cast<uintptr_t>(q) & 3u) == 0) && (jb.ldq % 4 == 0));
   const bool vec_qt = qt == nullptr || (aligned16(qt) && (jb.ldqt % 16 == 0));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tile_parity = 0;  // LDS image buffer of the next transposed tile
   for (int64_t t = lb; t < ntiles; t += jb.nblocks) {
     const int64_t r0 = (t / ntc) * kTR, c0 = (t % ntc) * kTC;
     const bool full = r0 + kTR <= rows && c0 + kTC <= cols && (vec_in || buf_in) && vec_q && vec_qt;
@@ -202,6 +214,12 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d) {
         for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(q + (rb + i) * jb.ldq + cb) = code[i];
       }
       if (qt) {
+        // Transposed codes go through LDS so that the stores write whole
+        // 128-byte rows of qt: the lane's 4x(16 rows) block is transposed
+        // in registers, parked as four 16-byte pieces of the tile's
+        // transposed image (256 rows of 128 bytes), and after one barrier
+        // eight consecutive lanes store one 128-byte row.
+        uint8_t* img = tbuf + (tile_parity & 1) * kTImage;
         uint32_t col[4][4];  // col[j][k]: column j, rows 4k..4k+3
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -212,9 +230,18 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d) {
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          v4u o = {col[j][0], col[j][1], col[j][2], col[j][3]};
-          *reinterpret_cast<v4u*>(qt + (cb + j) * jb.ldqt + rb) = o;
+          const int c = lane * 4 + j;
+          *reinterpret_cast<v4u*>(img + timg_off(c, wave)) = v4u{col[j][0], col[j][1], col[j][2], col[j][3]};
         }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kTC * (kTR / 16) / kCastThreads; ++i) {
+          const int id = tid + kCastThreads * i;
+          const int c = id >> 3, k = id & 7;
+          const v4u o = *reinterpret_cast<const v4u*>(img + timg_off(c, k));
+          *reinterpret_cast<v4u*>(qt + (c0 + c) * jb.ldqt + r0 + 16 * k) = o;
+        }
+        ++tile_parity;
       }
     } else {
       // ragged or unaligned tile: element by element
@@ -234,6 +261,7 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d) {
 template <int FMT, int MODE>
 __global__ void __launch_bounds__(kCastThreads) cast_kernel(QuantBatch b) {
   __shared__ uint32_t red[kCastThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[2 * kTImage];  // double-buffered transposed tile
   int lb;
   const QuantJob& jb = job_of(b, lb);
   // 1. amax from the partials (integer max of non-negative bit patterns)
@@ -261,7 +289,7 @@ __global__ void __launch_bounds__(kCastThreads) cast_kernel(QuantBatch b) {
   }
   const Divider d = make_divider(s, amax);
   // 2. cast
-  cast_tiles<FMT, MODE>(jb, lb, d);
+  cast_tiles<FMT, MODE>(jb, lb, d, tbuf);
 }
 
 int cast_blocks_for(int64_t rows, int64_t cols) {
