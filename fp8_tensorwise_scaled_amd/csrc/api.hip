@@ -27,12 +27,16 @@ bool tile_range_ok(int64_t ld, int64_t K) { return (kTileRows - 1) * ld + K < (i
 int check_gemm(const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8_t* b, int64_t ldb,
                int fb, const float* sb, int64_t M, int64_t N, int64_t K, const uint16_t* c,
                int64_t ldc) {
-  if (!a || !b || !sa || !sb || !c) return FP8MLP_EINVAL;
-  if (M <= 0 || N <= 0 || K <= 0) return FP8MLP_EINVAL;
-  if (lda < K || ldb < K || ldc < N) return FP8MLP_EINVAL;
+  if (!sa || !sb) return FP8MLP_EINVAL;
+  if (M < 0 || N < 0 || K < 0) return FP8MLP_EINVAL;
   if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MLP_EINVAL;
+  if (M == 0 || N == 0) return FP8MLP_OK;  // empty output: nothing read or written
+  if (!c || ldc < N) return FP8MLP_EINVAL;
+  if (!a2(c)) return FP8MLP_EALIGN;
+  if (K == 0) return FP8MLP_OK;  // empty sums: C = 0, the operands are not read
+  if (!a || !b || lda < K || ldb < K) return FP8MLP_EINVAL;
   if (K % 16 != 0) return FP8MLP_ENOTSUP;
-  if (!a16(a) || !a16(b) || lda % 16 || ldb % 16 || !a2(c)) return FP8MLP_EALIGN;
+  if (!a16(a) || !a16(b) || lda % 16 || ldb % 16) return FP8MLP_EALIGN;
   if (!tile_range_ok(lda, K) || !tile_range_ok(ldb, K)) return FP8MLP_ENOTSUP;
   if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return FP8MLP_ENOTSUP;
   return FP8MLP_OK;
@@ -43,8 +47,10 @@ int run_gemm(const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8
              void* stream) {
   int st = check_gemm(a, lda, fa, sa, b, ldb, fb, sb, M, N, K, c, ldc);
   if (st) return st;
+  if (M == 0 || N == 0) return FP8MLP_OK;  // empty output; K == 0 writes zeros
   GemmArgs g{};
   g.a = a; g.b = b; g.lda = lda; g.ldb = ldb; g.fa = fa; g.fb = fb; g.sa = sa; g.sb = sb;
+  if (K == 0) g.lda = g.ldb = 0;  // operand descriptors cover no bytes
   g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc; g.epi = kEpiStore;
   return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
@@ -73,7 +79,7 @@ size_t layout_bwd(int64_t M, int64_t d, int64_t h, size_t* off) {
 }
 
 int check_mlp_dims(int64_t M, int64_t d, int64_t h) {
-  if (M <= 0 || d <= 0 || h <= 0) return FP8MLP_EINVAL;
+  if (M < 0 || d <= 0 || h <= 0) return FP8MLP_EINVAL;
   if (M % 16 || d % 16 || h % 16) return FP8MLP_ENOTSUP;
   if (!tile_range_ok(M, M) || !tile_range_ok(h, h) || !tile_range_ok(d, d)) return FP8MLP_ENOTSUP;
   if (M > INT32_MAX / 2 || d > INT32_MAX / 2 || h > INT32_MAX / 2) return FP8MLP_ENOTSUP;
@@ -99,7 +105,7 @@ int fp8mlp_abi_version(void) { return FP8MLP_ABI_VERSION; }
 const char* fp8mlp_status_string(int status) {
   switch (status) {
     case FP8MLP_OK: return "ok";
-    case FP8MLP_EINVAL: return "invalid argument (null pointer, non-positive size, ld < cols or unknown format)";
+    case FP8MLP_EINVAL: return "invalid argument (null pointer, negative size, ld < cols or unknown format)";
     case FP8MLP_EALIGN: return "misaligned pointer or leading dimension";
     case FP8MLP_EWORKSPACE: return "workspace missing or too small";
     case FP8MLP_EHIP: return "HIP launch failed";
@@ -109,18 +115,22 @@ const char* fp8mlp_status_string(int status) {
 }
 
 size_t fp8_amax_quant_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows <= 0 || cols <= 0) return 0;
+  if (rows < 0 || cols < 0) return 0;
   return align_up((size_t)amax_parts_for(rows, cols) * 4);
 }
 
 int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
                    int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale, float* amax, void* ws,
                    size_t ws_bytes, void* stream) {
-  if (!x || !scale || (!q && !qt)) return FP8MLP_EINVAL;
-  if (rows <= 0 || cols <= 0 || ldx < cols || !fmt_ok(fmt)) return FP8MLP_EINVAL;
-  if ((q && ldq < cols) || (qt && ldqt < rows)) return FP8MLP_EINVAL;
-  if ((const void*)q == (const void*)x || (const void*)qt == (const void*)x) return FP8MLP_EINVAL;
-  if (!a2(x)) return FP8MLP_EALIGN;
+  if (!scale) return FP8MLP_EINVAL;
+  if (rows < 0 || cols < 0 || ldx < cols || !fmt_ok(fmt)) return FP8MLP_EINVAL;
+  if (rows > 0 && cols > 0) {  // an empty tensor only gets its scale (1) and amax (0)
+    if (!x || (!q && !qt)) return FP8MLP_EINVAL;
+    if ((q && ldq < cols) || (qt && ldqt < rows)) return FP8MLP_EINVAL;
+    if ((q && (const void*)q == (const void*)x) || (qt && (const void*)qt == (const void*)x))
+      return FP8MLP_EINVAL;
+    if (!a2(x)) return FP8MLP_EALIGN;
+  }
   if (!ws || ws_bytes < fp8_amax_quant_workspace_bytes(rows, cols)) return FP8MLP_EWORKSPACE;
   if (!a16(ws)) return FP8MLP_EALIGN;
   QuantBatch b{};
@@ -180,11 +190,11 @@ int relu2_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offs
 int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_down, int64_t M,
                   int64_t d, int64_t h, uint16_t* y, const relu2_mlp_saved* saved, void* ws,
                   size_t ws_bytes, void* stream) {
-  if (!x || !w_up || !w_down || !y || !saved) return FP8MLP_EINVAL;
-  if (!saved->xq_t || !saved->uq_t || !saved->dq_t || !saved->aq_t || !saved->h || !saved->scales)
-    return FP8MLP_EINVAL;
+  if (!w_up || !w_down || !saved || !saved->uq_t || !saved->dq_t || !saved->scales) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
+  // buffers with M rows may be NULL when M == 0 (no tokens)
+  if (M > 0 && (!x || !y || !saved->xq_t || !saved->aq_t || !saved->h)) return FP8MLP_EINVAL;
   const void* ptrs[] = {x, w_up, w_down, y, saved->xq_t, saved->uq_t, saved->dq_t, saved->aq_t, saved->h};
   for (const void* p : ptrs)
     if (!a16(p)) return FP8MLP_EALIGN;
@@ -240,11 +250,10 @@ int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_dow
 int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, int64_t d, int64_t h,
                   uint16_t* dx, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales, void* ws,
                   size_t ws_bytes, void* stream) {
-  if (!dy || !saved || !dx || !dw_up || !dw_down) return FP8MLP_EINVAL;
-  if (!saved->xq_t || !saved->uq_t || !saved->dq_t || !saved->aq_t || !saved->h || !saved->scales)
-    return FP8MLP_EINVAL;
+  if (!saved || !dw_up || !dw_down || !saved->uq_t || !saved->dq_t || !saved->scales) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
+  if (M > 0 && (!dy || !dx || !saved->xq_t || !saved->aq_t || !saved->h)) return FP8MLP_EINVAL;
   const void* ptrs[] = {dy, dx, dw_up, dw_down, saved->xq_t, saved->uq_t, saved->dq_t, saved->aq_t,
                         saved->h};
   for (const void* p : ptrs)

@@ -352,6 +352,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
 template <int FA, int FB, int BM, int BN, int WGM, int WGN, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
+  if (tiles_m == 0 || tiles_n == 0) return hipSuccess;  // empty output
   hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, BM, BN, WGM, WGN, EPI>), dim3(tiles_m * tiles_n),
                      dim3(64 * WGM * WGN), 0, st, g, tiles_m, tiles_n);
   return hipGetLastError();

@@ -294,7 +294,8 @@ __global__ void __launch_bounds__(kCastThreads) cast_kernel(QuantBatch b) {
 
 int cast_blocks_for(int64_t rows, int64_t cols) {
   const int64_t tiles = ((rows + kTR - 1) / kTR) * ((cols + kTC - 1) / kTC);
-  return (int)(tiles < 2048 ? tiles : 2048);
+  // at least one block: block 0 writes the scale even for an empty tensor
+  return (int)(tiles < 1 ? 1 : (tiles < 2048 ? tiles : 2048));
 }
 
 }  // namespace

@@ -58,7 +58,7 @@ extern "C" {
 
 /* Status codes. */
 #define FP8MLP_OK 0
-#define FP8MLP_EINVAL 1     /* NULL pointer, size <= 0, ld < cols, bad format   */
+#define FP8MLP_EINVAL 1     /* NULL pointer, size < 0, ld < cols, bad format    */
 #define FP8MLP_EALIGN 2     /* pointer or leading dimension misaligned          */
 #define FP8MLP_EWORKSPACE 3 /* workspace missing or smaller than the query      */
 #define FP8MLP_EHIP 4       /* a HIP launch failed                              */
@@ -86,8 +86,12 @@ size_t fp8_amax_quant_workspace_bytes(int64_t rows, int64_t cols);
  * amax   out: 1 float, max |x| (may be NULL).
  * ws     workspace of at least fp8_amax_quant_workspace_bytes(rows, cols)
  *        bytes, 16-byte aligned; its contents need no initialisation.
- * Requires x to be 2-byte aligned; 16-byte aligned x/q/qt and ld multiples of
- * 16 take the vectorised path, anything else a correct element-wise path.
+ * Requires x to be 2-byte aligned.  16-byte aligned q/qt with leading
+ * dimensions that are multiples of 16 take the vectorised path; x rows that
+ * are not 8-byte aligned are read with realigning loads; anything else (and
+ * ragged edges) takes a correct element-wise path.
+ * An empty tensor (rows == 0 or cols == 0) is valid: amax = 0, scale = 1,
+ * no codes written.
  */
 int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale,
@@ -101,8 +105,9 @@ int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, i
 /* fast layout for the gfx950 FP8 matrix cores); the names say which        */
 /* operands of the linear layer they take.  Weight W is stored [out, in].   */
 /* Requirements: K % 16 == 0; operand pointers 16-byte aligned and their    */
-/* leading dimensions multiples of 16; rows and columns of C any size >= 1  */
-/* (ragged edges are masked).  C is overwritten (no accumulation).           */
+/* leading dimensions multiples of 16; rows and columns of C any size >= 0  */
+/* (ragged edges are masked; M == 0 or N == 0 is a no-op, K == 0 writes      */
+/* zeros, the empty sum).  C is overwritten (no accumulation).               */
 /* ------------------------------------------------------------------------ */
 
 /* Forward  Y[M,N] = X[M,K] . W[N,K]^T.
@@ -138,7 +143,9 @@ int fp8_linear_wgrad(const uint8_t* dyqt, int64_t lddyt, int fdy, const float* s
 /*     Gq = quant(dY);  dW_down = gemm(Gq^T, Aq^T)                          */
 /*     dA = gemm(Gq, Dq^T);  dH = RN_bf16(2 relu(H) dA)  (fused epilogue)   */
 /*     Hq = quant(dH);  dW_up = gemm(Hq^T, Xq^T);  dX = gemm(Hq, Uq^T)      */
-/* Requirements: M, d, h multiples of 16; all pointers 16-byte aligned.      */
+/* Requirements: M, d, h multiples of 16 (d, h >= 16; M == 0, no tokens, is  */
+/* valid: Y and dX are empty, dW_up and dW_down zero, scales of X, A, dY    */
+/* and dH are 1); all pointers 16-byte aligned.                             */
 /* ------------------------------------------------------------------------ */
 
 /* Forward quantities the backward pass reads.  Caller-allocated device

@@ -51,7 +51,7 @@ def test_quant_validation():
     ws_n = _native.lib().fp8_amax_quant_workspace_bytes(64, 64)
     assert ws_n > 0
     ok = [FAKE, 64, 64, 64, 0, FAKE, 64, None, 0, FAKE, None, FAKE, ws_n, None]
-    bad = dict(x=(0, None), rows=(1, 0), cols=(2, -1), ldx=(3, 32), fmt=(4, 7), ldq=(6, 10),
+    bad = dict(x=(0, None), rows=(1, -1), cols=(2, -1), ldx=(3, 32), fmt=(4, 7), ldq=(6, 10),
                scale=(9, None))
     for _, (i, v) in bad.items():
         a = list(ok)
@@ -76,8 +76,12 @@ def test_gemm_validation():
     base = [FAKE, 64, 0, FAKE, FAKE, 64, 0, FAKE, 32, 48, 64, FAKE, 48, None]
     for fn in (L.fp8_linear_fwd,):
         assert fn(*[None] + base[1:]) == 1
+        a = list(base); a[8] = -1
+        assert fn(*a) == 1                          # M < 0
         a = list(base); a[8] = 0
-        assert fn(*a) == 1                          # M = 0
+        assert fn(*a) == 0                          # M = 0: empty output, nothing launched
+        a = list(base); a[9] = 0
+        assert fn(*a) == 0                          # N = 0
         a = list(base); a[1] = 32
         assert fn(*a) == 1                          # lda < K
         a = list(base); a[10] = 40; a[1] = 48; a[5] = 48
@@ -110,7 +114,10 @@ def test_mlp_validation():
     args[3] = 65
     assert L.relu2_mlp_fwd(*args) == 5
     args = [FAKE, FAKE, FAKE, 64, 64, 256, None, ctypes.byref(saved), FAKE, n, None]
-    assert L.relu2_mlp_fwd(*args) == 1
+    assert L.relu2_mlp_fwd(*args) == 1                               # y missing with M > 0
+    args = [FAKE, FAKE, FAKE, -16, 64, 256, FAKE, ctypes.byref(saved), FAKE, n, None]
+    assert L.relu2_mlp_fwd(*args) == 1                               # M < 0
+    assert L.relu2_mlp_fwd_workspace_bytes(0, 64, 256) > 0           # M = 0 is a valid shape
     bad_saved = _native.Relu2MlpSaved(0x10000, 0, 0x10000, 0x10000, 0x10000, 0x10000)
     args = [FAKE, FAKE, FAKE, 64, 64, 256, FAKE, ctypes.byref(bad_saved), FAKE, n, None]
     assert L.relu2_mlp_fwd(*args) == 1

@@ -92,6 +92,32 @@ def test_strided_output_and_operands():
     assert (Cb[:, N:] == 7).all()   # columns past N untouched
 
 
+def test_empty_sizes():
+    """K = 0 writes the empty sum (+0) everywhere; M = 0 or N = 0 is a no-op.
+    Each of the three GEMMs, with the oracle's result for the same shapes."""
+    from fp8_tensorwise_scaled_amd import api
+
+    dev = torch.device("cuda:0")
+    u8e = lambda r, c: torch.empty((r, c), dtype=torch.uint8, device=dev)
+    s1, s2 = scal(0.5), scal(3.0)
+    for name, call, ref in (
+            ("fwd K=0", lambda out: api.fp8_linear_fwd(u8e(40, 0), s1, u8e(24, 0), s2, out=out),
+             oracle.gemm_nt(np.zeros((40, 0), np.uint8), E4, 0.5, np.zeros((24, 0), np.uint8), E4, 3.0)),
+            ("dgrad N=0", lambda out: api.fp8_linear_dgrad(u8e(40, 0), s1, u8e(24, 0), s2, out=out),
+             oracle.gemm_nn(np.zeros((40, 0), np.uint8), E5, 0.5, np.zeros((0, 24), np.uint8), E4, 3.0)),
+            ("wgrad M=0", lambda out: api.fp8_linear_wgrad(u8e(40, 0), s1, u8e(24, 0), s2, out=out),
+             oracle.gemm_tn(np.zeros((0, 40), np.uint8), E5, 0.5, np.zeros((0, 24), np.uint8), E4, 3.0))):
+        out = torch.full((40, 24), 7, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        call(out)
+        torch.cuda.synchronize()
+        assert (bf16_bits(out) == ref).all() and (ref == 0).all(), name
+    # empty outputs: nothing to write, the call succeeds
+    y = api.fp8_linear_fwd(u8e(0, 64), s1, u8e(24, 64), s2)
+    y2 = api.fp8_linear_fwd(u8e(40, 64), s1, u8e(0, 64), s2)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 24) and tuple(y2.shape) == (40, 0)
+
+
 def test_output_rows_not_16_byte_aligned():
     """Odd leading dimension and a base 2 bytes off a dword: every store
     alignment (2, 4, 8, 16 bytes) occurs among the rows."""

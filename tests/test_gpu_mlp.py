@@ -89,6 +89,30 @@ def test_3p8b_block_sampled():
     compare_block(g, o, sc, rows, cols)
 
 
+def test_no_tokens():
+    """M = 0: empty Y and dX, activation and gradient scales 1, both weight
+    gradients zero (empty sums), weight codes and scales as the oracle's."""
+    from fp8_tensorwise_scaled_amd import api
+
+    w = synth.MLPWorkload(41, 16, 64, 256)
+    x, wu, wd, dy = w.tensors()
+    ref_f = oracle.mlp_fwd(x[:0], wu, wd)
+    ref_b = oracle.mlp_bwd(dy[:0], ref_f)
+    dev = torch.device("cuda:0")
+    y, saved = api.relu2_mlp_fwd(to_dev_bf16(x[:0]), to_dev_bf16(wu), to_dev_bf16(wd))
+    dwu = torch.full((256, 64), 7, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    dwd = torch.full((64, 256), 7, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    dx, dwu, dwd, bsc = api.relu2_mlp_bwd(to_dev_bf16(dy[:0]), saved, dw_up=dwu, dw_down=dwd)
+    torch.cuda.synchronize()
+    sc = saved.scales.cpu().numpy()
+    assert [float(v) for v in sc] == [ref_f["sx"], ref_f["su"], ref_f["sd"], ref_f["sa"]]
+    assert [float(v) for v in bsc.cpu().numpy()] == [ref_b["sg"], ref_b["sh"]] == [1.0, 1.0]
+    assert (saved.uq_t.cpu().numpy() == ref_f["uq"].T).all() and (saved.dq_t.cpu().numpy() == ref_f["dq"].T).all()
+    from tests.gpu_util import bf16_bits
+    assert (bf16_bits(dwu) == ref_b["dw_up"]).all() and (bf16_bits(dwd) == ref_b["dw_down"]).all()
+    assert tuple(y.shape) == (0, 64) and tuple(dx.shape) == (0, 64)
+
+
 def test_deterministic_and_reuse():
     """Two passes with the same buffers give identical bytes."""
     a = run_block(synth.MLPWorkload(21, 512, 256, 1024, sigma_up=1 / 16, sigma_down=1 / 32))

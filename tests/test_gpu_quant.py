@@ -93,6 +93,22 @@ def test_unaligned_rows_full_tiles(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(0, 64), (64, 0), (0, 0)])
+def test_empty_tensor(fmt, shape):
+    """No elements: amax 0 and scale 1, as the oracle defines them."""
+    from fp8_tensorwise_scaled_amd import api
+
+    x = torch.empty(shape, dtype=torch.bfloat16, device="cuda:0")
+    scale = torch.full((1,), 7.0, device="cuda:0")
+    amax = torch.full((1,), 7.0, device="cuda:0")
+    q, qt, s, a = api.fp8_amax_quant(x, fmt, want_qt=True, scale=scale, amax=amax)
+    torch.cuda.synchronize()
+    rq, rs, ra = oracle.quant(np.zeros(shape, np.uint16), fmt)
+    assert float(f32(s)[0]) == rs == 1.0 and float(f32(a)[0]) == ra == 0.0
+    assert tuple(q.shape) == shape and tuple(qt.shape) == shape[::-1]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_zero_and_tiny(fmt):
     x = np.zeros((64, 64), np.uint16)
     x[3, 5] = 0x8000

@@ -136,6 +136,16 @@ def test_special_cases():
     assert (np.diag(y) == 448 * 2.0 ** -9).all() and (y[~np.eye(4, dtype=bool)] == 0).all()
 
 
+def test_empty_reduction_and_empty_outputs():
+    """K = 0: every output is the empty sum, +0; M = 0 or N = 0: empty output."""
+    for fn, a, b, shape in ((oracle.gemm_nt, np.zeros((5, 0), np.uint8), np.zeros((3, 0), np.uint8), (5, 3)),
+                            (oracle.gemm_nn, np.zeros((5, 0), np.uint8), np.zeros((0, 3), np.uint8), (5, 3)),
+                            (oracle.gemm_tn, np.zeros((0, 5), np.uint8), np.zeros((0, 3), np.uint8), (5, 3))):
+        y = fn(a, E4, 0.5, b, E5, 3.0)
+        assert y.shape == shape and (y == 0).all()
+    assert oracle.gemm_nt(np.zeros((0, 16), np.uint8), E4, 1.0, np.ones((3, 16), np.uint8), E4, 1.0).shape == (0, 3)
+
+
 def test_row_sampling_matches_full():
     rng = np.random.default_rng(2)
     a = finite_codes(E5, rng, (50, 70))

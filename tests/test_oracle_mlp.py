@@ -89,6 +89,19 @@ def test_chain_uses_saved_forward_quantities(small_block):
     assert fwd["amax_a"] == float(synth.bf16_bits_to_f32(to_bf16_bits(np.array([m * m], np.float32)))[0])
 
 
+def test_chain_with_no_tokens():
+    """M = 0: the forward is empty, the activation and gradient scales are 1
+    (empty maxima), and both weight gradients are empty sums, i.e. zero."""
+    x, wu, wd, dy = synth.MLPWorkload(41, 16, 32, 64).tensors()
+    f = oracle.mlp_fwd(x[:0], wu, wd)
+    b = oracle.mlp_bwd(dy[:0], f)
+    assert f["y"].shape == (0, 32) and b["dx"].shape == (0, 32)
+    assert f["sx"] == 1.0 and f["sa"] == 1.0 and b["sg"] == 1.0 and b["sh"] == 1.0
+    assert f["su"] == oracle.quant(wu, oracle.E4M3)[1] and f["sd"] == oracle.quant(wd, oracle.E4M3)[1]
+    assert b["dw_up"].shape == (64, 32) and (b["dw_up"] == 0).all()
+    assert b["dw_down"].shape == (32, 64) and (b["dw_down"] == 0).all()
+
+
 def test_pages_shapes_and_parameter_table():
     cfg = json.load(open(os.path.join(HERE, "golden", "little_lm_config.json")))
     m = cfg["model"]

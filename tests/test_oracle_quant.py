@@ -75,6 +75,15 @@ def test_zero_tensor(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(0, 8), (8, 0), (0, 0)])
+def test_empty_tensor(fmt, shape):
+    """An empty tensor has no elements to take a maximum over: amax = 0,
+    hence s = 1 as for an all-zero tensor, and no codes."""
+    q, s, a = oracle.quant(np.zeros(shape, np.uint16), fmt)
+    assert q.shape == shape and s == 1.0 and a == 0.0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("amax_bits", [0x0080, 0x0001, 0x0005, 0x00F0])  # 2^-126, 2^-133, ...
 def test_tiny_amax(fmt, amax_bits):
     """Scales in the fp32 subnormal range: IEEE semantics, no flushing."""
