@@ -94,6 +94,11 @@ def test_gemm_validation():
         assert fn(*a) == 1                          # unknown format
         a = list(base); a[12] = 40
         assert fn(*a) == 1                          # ldc < N
+    # tile offsets are 32-bit: 255 rows of a 2^24-byte leading dimension do not fit
+    a = list(base); a[1] = 1 << 24
+    assert L.fp8_linear_fwd(*a) == 5
+    a = list(base); a[5] = 1 << 24
+    assert L.fp8_linear_fwd(*a) == 5
     # dgrad: reduction length is N (K argument is the output width)
     a = [FAKE, 40, 1, FAKE, FAKE, 40, 0, FAKE, 32, 40, 64, FAKE, 64, None]
     assert L.fp8_linear_dgrad(*a) == 5
