@@ -100,27 +100,31 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   // row = id / 8, logical column chunk = id % 8 (eight lanes cover one
   // 128-byte row, so a wave load is 8 full rows).  In LDS the chunk goes to
   // position logical ^ swz(row) of its row.  Loads j < A_LOADS are A rows,
-  // the rest B rows.
-  uint32_t goff[G::LOADS], ldsoff[G::LOADS];
-  int colk[G::LOADS];
-#pragma unroll
-  for (int j = 0; j < G::LOADS; ++j) {
-    const bool is_a = j < G::A_LOADS;
-    const int id = tid + kThreads * (is_a ? j : j - G::A_LOADS);
-    const int row = id >> 3, logical = id & 7;
-    colk[j] = logical * 16;
-    goff[j] = (uint32_t)(row * (is_a ? g.lda : g.ldb)) + colk[j];
-    ldsoff[j] = (is_a ? 0 : G::A_BYTES) + row * kBK + ((logical ^ swz(row)) << 4);
-  }
+  // the rest B rows.  Load j's row is row0 + j*(THREADS/8); THREADS/16 is a
+  // multiple of 8, so swz() and the column are the same for every j and the
+  // offsets are linear in j.
+  constexpr int kRowStep = kThreads / 8;
+  static_assert((kRowStep / 2) % 8 == 0, "swizzle must repeat every load step");
+  const int row0 = tid >> 3, logical0 = tid & 7;
+  const int colk0 = logical0 * 16;
+  const uint32_t goff_a = (uint32_t)(row0 * g.lda) + colk0, goff_b = (uint32_t)(row0 * g.ldb) + colk0;
+  const uint32_t gstep_a = (uint32_t)(kRowStep * g.lda), gstep_b = (uint32_t)(kRowStep * g.ldb);
+  const uint32_t lds0 = row0 * kBK + ((logical0 ^ swz(row0)) << 4);
 
   v4u stg[G::LOADS];  // one stage in flight in registers
   auto gload_one = [&](int j, int kt) {
     const int k0 = kt * kBK;
-    const uint32_t off = (k0 + colk[j] < K) ? goff[j] + k0 : 0x80000000u;  // out of range -> 0
-    stg[j] = __builtin_amdgcn_raw_buffer_load_b128(j < G::A_LOADS ? ra : rb, off, 0, 0);
+    const bool is_a = j < G::A_LOADS;
+    const int jj = is_a ? j : j - G::A_LOADS;
+    const uint32_t base = is_a ? goff_a + jj * gstep_a : goff_b + jj * gstep_b;
+    const uint32_t off = (k0 + colk0 < K) ? base + k0 : 0x80000000u;  // out of range -> 0
+    stg[j] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra : rb, off, 0, 0);
   };
   auto swrite_one = [&](int j, int buf) {
-    *reinterpret_cast<v4u*>(smem + buf * G::STAGE + ldsoff[j]) = stg[j];
+    const bool is_a = j < G::A_LOADS;
+    const int jj = is_a ? j : j - G::A_LOADS;
+    *reinterpret_cast<v4u*>(smem + buf * G::STAGE + (is_a ? 0 : G::A_BYTES) + lds0 + jj * kRowStep * kBK) =
+        stg[j];
   };
 
   v16f acc[G::FM][G::FN];
