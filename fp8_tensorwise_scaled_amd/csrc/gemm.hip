@@ -233,6 +233,34 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
   const bool vec_aux = EPI != kEpiRelu2Bwd ||
                        (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0));
+  // The relu^2-backward epilogue needs H at its chunks.  With two waves per
+  // SIMD (THREADS = 512) the loads are issued first, in flight while the tile
+  // is staged in LDS; the 4-wave layout has no registers to spare next to its
+  // 256 accumulators and issues them after staging.
+  constexpr bool kEarlyH = EPI == kEpiRelu2Bwd && kThreads == 512;
+  v4u hv[EPI == kEpiRelu2Bwd ? NCH : 1];
+  auto load_h = [&]() {
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+      const int id = tid + kThreads * it;
+      const int64_t gr = m0 + id / CPR, gc = n0 + (id % CPR) * 8;
+      hv[it] = v4u{0u, 0u, 0u, 0u};
+      if (gr < g.M && gc < g.N) {
+        if (gc + 8 <= g.N && vec_c && vec_aux) {
+          hv[it] = *reinterpret_cast<const v4u*>(g.aux + gr * g.ldaux + gc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = gc + 2 * e < g.N ? g.aux[gr * g.ldaux + gc + 2 * e] : 0u;
+            const uint32_t hi = gc + 2 * e + 1 < g.N ? g.aux[gr * g.ldaux + gc + 2 * e + 1] : 0u;
+            hv[it][e] = lo | (hi << 16);
+          }
+        }
+      }
+    }
+  };
+  if constexpr (kEarlyH) load_h();
+
   // scale, round to bf16 and stage the tile in LDS
   const float p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
 #pragma unroll
@@ -256,30 +284,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
     }
   }
   __syncthreads();
-
-  // The relu^2-backward epilogue needs H at its chunks: issue all those loads
-  // together (the accumulators are dead once staged) before processing.
-  v4u hv[EPI == kEpiRelu2Bwd ? NCH : 1];
-  if constexpr (EPI == kEpiRelu2Bwd) {
-#pragma unroll
-    for (int it = 0; it < NCH; ++it) {
-      const int id = tid + kThreads * it;
-      const int64_t gr = m0 + id / CPR, gc = n0 + (id % CPR) * 8;
-      hv[it] = v4u{0u, 0u, 0u, 0u};
-      if (gr < g.M && gc < g.N) {
-        if (gc + 8 <= g.N && vec_c && vec_aux) {
-          hv[it] = *reinterpret_cast<const v4u*>(g.aux + gr * g.ldaux + gc);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = gc + 2 * e < g.N ? g.aux[gr * g.ldaux + gc + 2 * e] : 0u;
-            const uint32_t hi = gc + 2 * e + 1 < g.N ? g.aux[gr * g.ldaux + gc + 2 * e + 1] : 0u;
-            hv[it][e] = lo | (hi << 16);
-          }
-        }
-      }
-    }
-  }
+  if constexpr (EPI == kEpiRelu2Bwd && !kEarlyH) load_h();
 
   uint32_t mx = 0;  // epilogue max (bit pattern of a non-negative value)
 #pragma unroll
