@@ -28,7 +28,7 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, rows_per_gemm: int = 384):
+def cpu_baseline(w, rows_per_gemm: int = 1536):
     """Oracle GEMM rate on a bounded sample: rows_per_gemm output rows of each
     of the six GEMMs of the block (FP8 operands from the oracle's quantiser)."""
     import numpy as np
