@@ -82,6 +82,8 @@ def _load():
                 fn = getattr(lib, name)
                 fn.restype = None
                 fn.argtypes = [vp, i64, c_int, f32, vp, i64, c_int, f32, i64, i64, i64, vp, i64, vp, i64]
+            lib.orc_gemm_tn_acc.restype = None
+            lib.orc_gemm_tn_acc.argtypes = [vp, i64, c_int, f32, vp, i64, c_int, f32, i64, i64, i64, vp, i64]
             lib.orc_relu2.restype = None
             lib.orc_relu2.argtypes = [vp, i64, vp]
             lib.orc_relu2_bwd.restype = None
@@ -204,6 +206,17 @@ def gemm_tn(a, fa, sa, b, fb, sb, rows=None):
     return _gemm("orc_gemm_tn", a, fa, sa, b, fb, sb, M, N, K, N, K, rows)
 
 
+def gemm_tn_acc(a, fa, sa, b, fb, sb, acc: np.ndarray) -> None:
+    """acc[n,k] += RN32(sa*sb) * sum_m dec(a[m,n]) dec(b[m,k]) in fp64, unrounded."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    M, N = a.shape
+    M2, K = b.shape
+    assert M == M2 and acc.shape == (N, K) and acc.dtype == np.float64 and acc.flags.c_contiguous
+    _load().orc_gemm_tn_acc(_ptr(a), N, fa, np.float32(sa), _ptr(b), K, fb, np.float32(sb), M, N, K,
+                            _ptr(acc), K)
+
+
 # --------------------------------------------------------------- relu^2
 def relu2(h: np.ndarray) -> np.ndarray:
     h = _c(h, np.uint16)
@@ -265,3 +278,78 @@ def mlp_bwd(dy, saved):
     dx = gemm_nn(hq, E5M2, sh, saved["uq"], E4M3, saved["su"])
     return dict(gq=gq, sg=sg, dw_down=dw_down, da=da, dh=dh, hq=hq, sh=sh, amax_dh=amax_dh,
                 dw_up=dw_up, dx=dx)
+
+
+# ------------------------------------------- LM head + softcapped cross-entropy
+def softcap_ce_rows(z_bits: np.ndarray, targets: np.ndarray, n_classes: int, softcap: float, n_valid: int):
+    """Softcapped cross-entropy on bf16 logits Z [R, V] (bit patterns), in fp64.
+
+    The model's logits are capped as S = c tanh(Z / c) (decomputer.nl,
+    appendix: logit_softcap 15.0; loss LigerFusedLinearCrossEntropyLoss with
+    softcap 15.0).  Over the first n_classes columns (the padded vocabulary
+    rows of W are not classes):
+      loss_r = logsumexp_j S_rj - S_r,t_r            (0 for ignored rows)
+      G_rj   = (softmax_j(S_r) - [j = t_r]) (1 - tanh^2(Z_rj / c)) / n_valid
+    with rows whose target is outside [0, n_classes) ignored (zero loss and
+    gradient) and G = 0 in the padded columns.  Returns (loss_r [R] fp64,
+    G [R, V] fp64, dZ = RN_bf16(G) bits)."""
+    R, V = z_bits.shape
+    z = bf16_bits_to_f64(z_bits)[:, :n_classes]
+    t = np.tanh(z / softcap)
+    s = softcap * t
+    m = s.max(axis=1, keepdims=True) if n_classes > 0 else np.zeros((R, 1))
+    lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+    tg = np.asarray(targets, dtype=np.int64)
+    valid = (tg >= 0) & (tg < n_classes)
+    safe_t = np.where(valid, tg, 0)
+    rows = np.arange(R)
+    loss = np.where(valid, lse - s[rows, safe_t], 0.0)
+    p = np.exp(s - lse[:, None])
+    p[rows[valid], safe_t[valid]] -= 1.0
+    g = np.zeros((R, V), dtype=np.float64)
+    g[:, :n_classes] = p * (1.0 - t * t) / max(n_valid, 1)
+    g[~valid] = 0.0
+    return loss, g, double_to_bf16(g)
+
+
+def lm_head_ce(x, w, targets, n_classes: int, softcap: float = 15.0, chunk: int | None = None):
+    """FP8 LM head fused with the softcapped cross-entropy, chunked over rows.
+
+    The head's GEMMs are FP8 linears with dynamic tensorwise scaling like
+    every other linear (decomputer.nl, "Vroege experimenten" item 4).  The
+    fusion (same page, "Doorvoer verhogen", fused linear cross-entropy
+    bullet) processes `chunk` rows at a time so the full logits never exist:
+      Xq, sx = Q(X, E4M3);  Wq, sw = Q(W, E4M3)        (whole tensors)
+      per chunk k:  Z_k  = gemm(Xq_k, Wq)               (bf16 [C, V])
+                    loss, dZ_k = softcap_ce_rows(Z_k)
+                    dZq_k, s_k = Q(dZ_k, E5M2)           (the chunk's own scale)
+                    dX_k = gemm(dZq_k, Wq)               (grad-input)
+                    acc += RN32(s_k sx) dZq_k^T Xq_k     (fp64, unrounded)
+      dW = RN_bf16(acc);  loss = sum of row losses / n_valid (0 if none).
+    The dZ chunk is the operand of the chunk's two gradient GEMMs and never
+    exists as a whole tensor, so its tensorwise scale is taken per chunk.
+    Returns a dict with loss (fp64), dx, dw (bf16 bits), the scales and the
+    per-chunk stages (z, g, dz, dzq, sdz, loss_rows)."""
+    M, K = x.shape
+    V = w.shape[0]
+    C = M if chunk is None else int(chunk)
+    tg = np.asarray(targets, dtype=np.int64)
+    n_valid = int(((tg >= 0) & (tg < n_classes)).sum())
+    xq, sx, _ = quant(x, E4M3)
+    wq, sw, _ = quant(w, E4M3)
+    acc = np.zeros((V, K), dtype=np.float64)
+    dx = np.empty((M, K), dtype=np.uint16)
+    loss_rows = np.zeros(M, dtype=np.float64)
+    chunks = []
+    for c0 in range(0, M, max(C, 1)):
+        c1 = min(c0 + C, M)
+        z = gemm_nt(xq[c0:c1], E4M3, sx, wq, E4M3, sw)
+        lr, g, dz = softcap_ce_rows(z, tg[c0:c1], n_classes, softcap, n_valid)
+        dzq, sdz, _ = quant(dz, E5M2)
+        dx[c0:c1] = gemm_nn(dzq, E5M2, sdz, wq, E4M3, sw)
+        gemm_tn_acc(dzq, E5M2, sdz, xq[c0:c1], E4M3, sx, acc)
+        loss_rows[c0:c1] = lr
+        chunks.append(dict(z=z, g=g, dz=dz, dzq=dzq, sdz=sdz))
+    loss = float(loss_rows.sum() / n_valid) if n_valid > 0 else 0.0
+    return dict(loss=loss, loss_rows=loss_rows, dx=dx, dw=double_to_bf16(acc), dw_acc=acc, xq=xq, sx=sx,
+                wq=wq, sw=sw, n_valid=n_valid, chunks=chunks)

@@ -294,6 +294,32 @@ void orc_gemm_tn(const uint8_t* a, int64_t lda, int fa, float sa,
   free(bd);
 }
 
+/* TN product added to an fp64 accumulator, without any rounding:          */
+/*   acc[n,k] += RN32(sa*sb) * sum_m dec(a[m,n]) dec(b[m,k])               */
+/* for a gradient summed over several chunks of rows before its single     */
+/* rounding to bf16 (the chunked LM-head cross-entropy's weight gradient). */
+void orc_gemm_tn_acc(const uint8_t* a, int64_t lda, int fa, float sa,
+                     const uint8_t* b, int64_t ldb, int fb, float sb,
+                     int64_t M, int64_t N, int64_t K, double* acc, int64_t ldacc) {
+  double* bd = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
+  double ta[256];
+  orc_decode_table(fa, ta);
+  decode_matrix(b, M, K, ldb, fb, bd);
+  double p = (double)scale_product(sa, sb);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < N; ++n) {
+    double* s = (double*)calloc((size_t)K + 1, sizeof(double));
+    for (int64_t m = 0; m < M; ++m) {
+      double av = ta[a[m * lda + n]];
+      const double* brow = bd + m * K;
+      for (int64_t k = 0; k < K; ++k) s[k] += av * brow[k];
+    }
+    for (int64_t k = 0; k < K; ++k) acc[n * ldacc + k] += s[k] * p;
+    free(s);
+  }
+  free(bd);
+}
+
 /* ---------------------------------------------------------------------- */
 /* relu^2 and its derivative on bf16 tensors.                              */
 /*   A  = RN_bf16( relu(H)^2 )             (exact square before rounding)  */
