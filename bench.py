@@ -139,6 +139,33 @@ def bench_other(args) -> int:
                                       "o 3072, relu2 MLP 12288)", "M": w.M, "gemm_flops": r.flops},
                "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
                "tokens_per_s_equiv": round(w.M / (ms * 1e-3))}
+    elif args.workload == "lmce":
+        from fp8_tensorwise_scaled_amd import api
+
+        w = synth.LM_HEAD_CE
+        log(f"generating LM-head CE inputs M={w.M} K={w.K} V={w.V}")
+        x, wt, tg = w.tensors()
+        X, W = t(x), t(wt)
+        T = torch.from_numpy(tg).to(dev)
+        ws = api.fp8_lm_head_ce_workspace(w.M, w.K, w.V, w.chunk, dev)
+        out = dict(loss=torch.empty(1, dtype=torch.float32, device=dev),
+                   dx=torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev),
+                   dw=torch.empty((w.V, w.K), dtype=torch.bfloat16, device=dev),
+                   scales=torch.empty(2 + (w.M + w.chunk - 1) // w.chunk, dtype=torch.float32, device=dev))
+        step = lambda: api.fp8_lm_head_ce(X, W, T, w.n_classes, w.softcap, w.chunk, ws=ws, **out)
+        ms = _time_steps(step, args.steps, args.warmup)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        log(f"LM head + CE: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s, loss {float(out['loss'][0]):.4f}")
+        res = {"metric": "FP8 LM head fused with softcapped cross-entropy, fwd+bwd TFLOP/s",
+               "value": round(tflops, 2), "ms_per_step": round(ms, 4),
+               "data": "synthetic (seeded N(0,1) X, N(0,0.02) W with zero padded rows, uniform targets, "
+                       "1% ignored; bf16)",
+               "config": {"workload": f"LM head + softcap-{w.softcap:g} CE M={w.M} K={w.K} V={w.V} "
+                                      f"classes={w.n_classes} chunk={w.chunk}", "M": w.M, "K": w.K,
+                          "V": w.V, "chunk": w.chunk, "workspace_bytes": ws.numel(),
+                          "logits_bytes_if_materialised": 2 * w.M * w.V},
+               "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+               "tokens_per_s_equiv": round(w.M / (ms * 1e-3))}
     else:
         w = synth.LM_HEAD_PADDED
         n = synth.LM_HEAD_UNPADDED.N
@@ -176,9 +203,10 @@ def main() -> int:
     ap.add_argument("--gemm-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain device copies of 256 MiB (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead"), default="mlp",
+    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead", "lmce"), default="mlp",
                     help="mlp: the relu2 block M=8192 (default); proj: the decoder projection set at "
-                         "M=32768; lmhead: the LM head at vocabulary 50304 and 50257")
+                         "M=32768; lmhead: the LM head at vocabulary 50304 and 50257; lmce: the LM head "
+                         "fused with the softcapped cross-entropy (chunks of 2048 rows)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "

@@ -39,6 +39,9 @@ _PROTOS = {
     "relu2_mlp_bwd_workspace_layout": (c_int, [i64, i64, i64, ctypes.POINTER(szt), c_int]),
     "relu2_mlp_fwd": (c_int, [vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(Relu2MlpSaved), vp, szt, vp]),
     "relu2_mlp_bwd": (c_int, [vp, ctypes.POINTER(Relu2MlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, szt, vp]),
+    "fp8_lm_head_ce_workspace_bytes": (szt, [i64, i64, i64, i64]),
+    "fp8_lm_head_ce_workspace_layout": (c_int, [i64, i64, i64, i64, ctypes.POINTER(szt), c_int]),
+    "fp8_lm_head_ce": (c_int, [vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i64, vp, vp, vp, vp, vp, szt, vp]),
 }
 
 EXPORTS = tuple(_PROTOS)

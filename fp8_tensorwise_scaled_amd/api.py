@@ -185,3 +185,46 @@ def relu2_mlp_bwd(dy, saved: Relu2MlpSaved, *, dx=None, dw_up=None, dw_down=None
     _native.call("relu2_mlp_bwd", _p(dy), ctypes.byref(cs), M, d, h, _p(dx), _p(dw_up), _p(dw_down),
                  _p(bwd_scales), _p(ws), ws.numel(), _stream())
     return dx, dw_up, dw_down, bwd_scales
+
+
+def fp8_lm_head_ce_workspace(M: int, K: int, V: int, chunk: int, device) -> torch.Tensor:
+    n = _native.lib().fp8_lm_head_ce_workspace_bytes(M, K, V, chunk)
+    if n == 0:
+        raise ValueError(f"unsupported LM-head shape M={M} K={K} V={V} chunk={chunk}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lm_head_ce_layout(M: int, K: int, V: int, chunk: int):
+    offs = (ctypes.c_size_t * 14)()
+    _native.call("fp8_lm_head_ce_workspace_layout", M, K, V, chunk, offs, 14)
+    return list(offs)
+
+
+def fp8_lm_head_ce(x, w, targets, n_classes: int, softcap: float = 15.0, chunk: int = 2048, *, loss=None,
+                   dx=None, dw=None, scales=None, ws=None):
+    """FP8 LM head fused with the softcapped cross-entropy, chunked over rows.
+
+    x [M, K] bf16, w [V, K] bf16, targets [M] int32 (ids outside
+    [0, n_classes) are ignored).  Returns (loss [1] fp32, dx [M, K] bf16,
+    dw [V, K] bf16, scales [2 + ceil(M/chunk)] fp32: sx, sw, per-chunk dZ)."""
+    _check_dev(x, w, targets)
+    M, K = x.shape
+    V = w.shape[0]
+    if w.shape[1] != K or targets.shape != (M,) or targets.dtype != torch.int32:
+        raise ValueError("shapes: x [M, K], w [V, K], targets [M] int32")
+    for t in (x, w):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("x and w must be contiguous bfloat16")
+    dev = x.device
+    nchunks = (M + chunk - 1) // chunk if M > 0 else 0
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if dx is None else dx
+    dw = torch.empty((V, K), dtype=torch.bfloat16, device=dev) if dw is None else dw
+    scales = torch.empty(2 + nchunks, dtype=torch.float32, device=dev) if scales is None else scales
+    if ws is None:
+        ws = fp8_lm_head_ce_workspace(M, K, V, chunk, dev)
+    if not targets.is_contiguous():
+        raise ValueError("targets must be contiguous")
+    _native.call("fp8_lm_head_ce", _p(x), _p(w), _p(targets), M, K, V, n_classes, float(softcap),
+                 chunk, _p(loss), _p(dx), _p(dw), _p(scales), _p(ws), ws.numel(), _stream())
+    return loss, dx, dw, scales

@@ -96,6 +96,33 @@ QuantJob make_job(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, in
   return j;
 }
 
+// ---- LM head + softcapped cross-entropy workspace
+enum LmSlot { L_XQ, L_XQT, L_WQ, L_WQT, L_Z, L_DZQ, L_DZQT, L_DWF, L_LOSS, L_PX, L_PW, L_PZ, L_NV, L_SC, L_COUNT };
+
+int64_t pad16(int64_t v) { return (v + 15) / 16 * 16; }
+
+size_t layout_lm_ce(int64_t M, int64_t K, int64_t V, int64_t C, size_t* off) {
+  const int64_t Vp = pad16(V), nchunks = M > 0 ? (M + C - 1) / C : 0;
+  const size_t sz[L_COUNT] = {
+      (size_t)(M * K), (size_t)(K * M), (size_t)(V * K), (size_t)(K * Vp), (size_t)(C * Vp) * 2,
+      (size_t)(C * Vp), (size_t)(V * C), (size_t)(V * K) * 4, (size_t)M * 4,
+      (size_t)amax_parts_for(M, K) * 4, (size_t)amax_parts_for(V, K) * 4, (size_t)C * 4, 16,
+      (size_t)(2 + nchunks) * 4};
+  size_t o = 0;
+  for (int i = 0; i < L_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
+  return o;
+}
+
+int check_lm_ce_dims(int64_t M, int64_t K, int64_t V, int64_t n_classes, int64_t C) {
+  if (M < 0 || K <= 0 || V <= 0 || C <= 0 || n_classes <= 0 || n_classes > V) return FP8MLP_EINVAL;
+  if (M % 16 || K % 16 || C % 16) return FP8MLP_ENOTSUP;
+  if (V > lm_ce_max_vocab()) return FP8MLP_ENOTSUP;
+  if (!tile_range_ok(K, K) || !tile_range_ok(M, M) || !tile_range_ok(pad16(V), pad16(V)) ||
+      !tile_range_ok(C, C))
+    return FP8MLP_ENOTSUP;
+  return FP8MLP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -316,6 +343,97 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
   g4.b = saved->uq_t; g4.ldb = h; g4.fb = FP8MLP_E4M3; g4.sb = &sc[1];
   g4.M = M; g4.N = d; g4.K = h; g4.c = dx; g4.ldc = d; g4.epi = kEpiStore;
   return hip_status(launch_gemm(g4, s));
+}
+
+size_t fp8_lm_head_ce_workspace_bytes(int64_t M, int64_t K, int64_t V, int64_t chunk) {
+  if (check_lm_ce_dims(M, K, V, 1, chunk)) return 0;
+  size_t off[L_COUNT];
+  return layout_lm_ce(M, K, V, chunk, off);
+}
+
+int fp8_lm_head_ce_workspace_layout(int64_t M, int64_t K, int64_t V, int64_t chunk, size_t* offsets, int n) {
+  if (check_lm_ce_dims(M, K, V, 1, chunk) || !offsets || n < L_COUNT) return FP8MLP_EINVAL;
+  layout_lm_ce(M, K, V, chunk, offsets);
+  return FP8MLP_OK;
+}
+
+int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets, int64_t M, int64_t K,
+                   int64_t V, int64_t n_classes, float softcap, int64_t chunk, float* loss, uint16_t* dx,
+                   uint16_t* dw, float* scales, void* ws, size_t ws_bytes, void* stream) {
+  if (!w || !dw || !loss) return FP8MLP_EINVAL;
+  int st = check_lm_ce_dims(M, K, V, n_classes, chunk);
+  if (st) return st;
+  if (!(softcap > 0.0f) || !(softcap < 1e30f)) return FP8MLP_EINVAL;
+  if (M > 0 && (!x || !targets || !dx)) return FP8MLP_EINVAL;
+  const void* ptrs[] = {x, w, dx, dw};
+  for (const void* p : ptrs)
+    if (!a16(p)) return FP8MLP_EALIGN;
+  if (((uintptr_t)loss & 3u) || ((uintptr_t)scales & 3u) || ((uintptr_t)targets & 3u)) return FP8MLP_EALIGN;
+  size_t off[L_COUNT];
+  const size_t need = layout_lm_ce(M, K, V, chunk, off);
+  if (!ws || ws_bytes < need) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+
+  const int64_t Vp = pad16(V), C = chunk;
+  uint8_t* w8 = (uint8_t*)ws;
+  uint8_t *xq = w8 + off[L_XQ], *xqt = w8 + off[L_XQT], *wq = w8 + off[L_WQ], *wqt = w8 + off[L_WQT];
+  uint16_t* zb = (uint16_t*)(w8 + off[L_Z]);
+  uint8_t *dzq = w8 + off[L_DZQ], *dzqt = w8 + off[L_DZQT];
+  float* dwf = (float*)(w8 + off[L_DWF]);
+  float* loss_rows = (float*)(w8 + off[L_LOSS]);
+  uint32_t* px = (uint32_t*)(w8 + off[L_PX]);
+  uint32_t* pw = (uint32_t*)(w8 + off[L_PW]);
+  uint32_t* pz = (uint32_t*)(w8 + off[L_PZ]);
+  int32_t* nv = (int32_t*)(w8 + off[L_NV]);
+  float* sc = scales ? scales : (float*)(w8 + off[L_SC]);
+  hipStream_t s = (hipStream_t)stream;
+
+  // 1. targets that count, then X and W quantised tensorwise (E4M3), both
+  //    row-major and transposed, in one amax and one cast launch
+  if (launch_count_valid(targets, M, n_classes, nv, s) != hipSuccess) return FP8MLP_EHIP;
+  QuantBatch b{};
+  b.njobs = 2;
+  b.job[0] = make_job(x, M, K, K, FP8MLP_E4M3, xq, K, xqt, M, &sc[0], nullptr, px, amax_parts_for(M, K),
+                      kModePlain);
+  b.job[1] = make_job(w, V, K, K, FP8MLP_E4M3, wq, K, wqt, Vp, &sc[1], nullptr, pw, amax_parts_for(V, K),
+                      kModePlain);
+  if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+  // reduction columns past V of the grad-input operands hold zero codes
+  if (launch_zero_cols(wqt, K, Vp, V, Vp, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_zero_cols(dzq, C, Vp, V, Vp, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 2. chunks of C rows: logits, loss and dZ, dZ codes, grad-input, grad-weight
+  int64_t k = 0;
+  for (int64_t c0 = 0; c0 < M; c0 += C, ++k) {
+    const int64_t rows = M - c0 < C ? M - c0 : C;
+    GemmArgs g{};  // Z = Xq_k . Wq^T  (bf16, leading dimension Vp)
+    g.a = xq + c0 * K; g.lda = K; g.fa = FP8MLP_E4M3; g.sa = &sc[0];
+    g.b = wq; g.ldb = K; g.fb = FP8MLP_E4M3; g.sb = &sc[1];
+    g.M = rows; g.N = V; g.K = K; g.c = zb; g.ldc = Vp; g.epi = kEpiStore;
+    if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
+    if (launch_softcap_ce(zb, rows, V, Vp, n_classes, softcap, targets + c0, nv, loss_rows + c0, pz, s) !=
+        hipSuccess)
+      return FP8MLP_EHIP;
+    QuantBatch bz{};  // dZ codes with this chunk's own scale (row partials)
+    bz.njobs = 1;
+    bz.job[0] = make_job(zb, rows, V, Vp, FP8MLP_E5M2, dzq, Vp, dzqt, C, &sc[2 + k], nullptr, pz, (int)rows,
+                         kModePlain);
+    if (launch_cast(bz, s) != hipSuccess) return FP8MLP_EHIP;
+    GemmArgs gd{};  // dX_k = dZq_k . Wq   (reduction over the padded vocabulary)
+    gd.a = dzq; gd.lda = Vp; gd.fa = FP8MLP_E5M2; gd.sa = &sc[2 + k];
+    gd.b = wqt; gd.ldb = Vp; gd.fb = FP8MLP_E4M3; gd.sb = &sc[1];
+    gd.M = rows; gd.N = K; gd.K = Vp; gd.c = dx + c0 * K; gd.ldc = K; gd.epi = kEpiStore;
+    if (launch_gemm(gd, s) != hipSuccess) return FP8MLP_EHIP;
+    GemmArgs gw{};  // dW (+)= RN32(s_k sx) dZq_k^T . Xq_k   (fp32, reduction over the chunk's rows)
+    gw.a = dzqt; gw.lda = C; gw.fa = FP8MLP_E5M2; gw.sa = &sc[2 + k];
+    gw.b = xqt + c0; gw.ldb = M; gw.fb = FP8MLP_E4M3; gw.sb = &sc[0];
+    gw.M = V; gw.N = K; gw.K = rows; gw.cf = dwf; gw.ldc = K; gw.epi = k == 0 ? kEpiStoreF32 : kEpiAccF32;
+    if (launch_gemm(gw, s) != hipSuccess) return FP8MLP_EHIP;
+  }
+
+  // 3. dW to bf16 (zeros without tokens) and the mean loss
+  return hip_status(launch_lm_ce_finalize(M > 0 ? dwf : nullptr, dw, V * K, loss_rows, M, nv, loss, s));
 }
 
 }  // extern "C"

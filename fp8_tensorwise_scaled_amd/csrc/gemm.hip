@@ -224,6 +224,38 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   iteration(kt, F{}, F{});
   __syncthreads();
 
+  // ---- fp32 epilogues: each lane writes its four consecutive columns of a
+  // row straight from the accumulators (a 256-row fp32 tile would not fit in
+  // LDS); the fp32 output is read-modify-written in place to accumulate.
+  if constexpr (EPI == kEpiStoreF32 || EPI == kEpiAccF32) {
+    const float p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
+    const bool vec = ((reinterpret_cast<uintptr_t>(g.cf) & 15u) == 0) && (g.ldc % 4 == 0);
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i) {
+      const int64_t gr = m0 + wm * G::WM + i * 32 + frow;
+      if (gr >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t gc = n0 + wn * G::WN + j * 32 + q * 8 + fhalf * 4;
+          const v16f& a = acc[i][j];
+          v4f v = {a[4 * q + 0] * p, a[4 * q + 1] * p, a[4 * q + 2] * p, a[4 * q + 3] * p};
+          float* dst = g.cf + gr * g.ldc + gc;
+          if (vec && gc + 4 <= g.N) {
+            if constexpr (EPI == kEpiAccF32) v += *reinterpret_cast<const v4f*>(dst);
+            *reinterpret_cast<v4f*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gc + e < g.N) dst[e] = EPI == kEpiAccF32 ? dst[e] + v[e] : v[e];
+          }
+        }
+      }
+    }
+    return;
+  }
+
   // ---- epilogue
   // Each thread owns NCH 16-byte chunks of the output tile: chunk id
   // tid + THREADS*it is row id / CPR, 8-column group id % CPR.
@@ -384,6 +416,15 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
   switch (g.epi) {
     case kEpiRelu2Max: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Max>(g, st);
     case kEpiRelu2Bwd: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Bwd>(g, st);
+    case kEpiStoreF32:
+    case kEpiAccF32:
+      // fp32 outputs are only produced for E5M2 x E4M3 (gradient x activation)
+      if constexpr (FA == kE5M2 && FB == kE4M3) {
+        return g.epi == kEpiStoreF32 ? launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStoreF32>(g, st)
+                                     : launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAccF32>(g, st);
+      } else {
+        return hipErrorInvalidValue;
+      }
     default: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStore>(g, st);
   }
 }

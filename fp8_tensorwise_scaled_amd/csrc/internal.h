@@ -50,6 +50,8 @@ enum Epilogue : int {
   kEpiRelu2Max = 1,   // C = H = RN_bf16(p * acc); partial[tile] = max over tile of max(H, 0)
   kEpiRelu2Bwd = 2,   // dA = RN_bf16(p * acc); C = dH = RN_bf16(2 relu(aux) dA);
                       // partial[tile] = max |dH| (bf16 bits)
+  kEpiStoreF32 = 3,   // Cf = RN32(p * acc)              (fp32 output, cf)
+  kEpiAccF32 = 4,     // Cf = RN32(Cf + RN32(p * acc))   (fp32 accumulation, cf)
 };
 
 struct GemmArgs {
@@ -66,11 +68,28 @@ struct GemmArgs {
   const uint16_t* aux;  // H for kEpiRelu2Bwd ([M, N], ldaux)
   int64_t ldaux;
   uint32_t* partials;  // one per tile for the max epilogues
+  float* cf;           // [M, N] fp32 (ldc) for the fp32 epilogues
 };
 
 // Number of output tiles the GEMM will use (size of `partials`).
 int64_t gemm_num_tiles(int64_t M, int64_t N);
 int64_t gemm_max_tiles(int64_t M, int64_t N);  // upper bound over tile configurations
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+
+// LM head fused with the softcapped cross-entropy (lm_head_ce.hip).
+// n_valid = number of targets in [0, n_classes).
+hipError_t launch_count_valid(const int32_t* targets, int64_t M, int64_t n_classes, int32_t* n_valid,
+                              hipStream_t st);
+// Rows [0, rows) of a chunk: logits Z (bf16, [rows, V], ld ldz) become dZ in
+// place; loss_rows[r] and partials[r] (max |dZ| as bf16 bits) are written.
+hipError_t launch_softcap_ce(uint16_t* z, int64_t rows, int64_t V, int64_t ldz, int64_t n_classes,
+                             float softcap, const int32_t* targets, const int32_t* n_valid,
+                             float* loss_rows, uint32_t* partials, hipStream_t st);
+// Zero columns [c0, c1) of a [rows, ld] byte matrix.
+hipError_t launch_zero_cols(uint8_t* base, int64_t rows, int64_t ld, int64_t c0, int64_t c1, hipStream_t st);
+// dw = RN_bf16(dwf) over n elements; loss = sum(loss_rows) / n_valid (0 if none).
+int64_t lm_ce_max_vocab();  // largest vocabulary the row kernel stages in LDS
+hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, const float* loss_rows, int64_t M,
+                                 const int32_t* n_valid, float* loss, hipStream_t st);
 
 }  // namespace fp8mlp

@@ -1,0 +1,248 @@
+// LM head fused with the softcapped cross-entropy on gfx950: the row kernel
+// that turns one chunk of logits into per-row losses and logit gradients, and
+// the small kernels around it (valid-target count, pad zeroing, finalisation).
+//
+// The loss (decomputer.nl, "Het trainen van een 3.8B LLM tot 0.384 CORE voor
+// $998", appendix: logit_softcap 15.0, loss LigerFusedLinearCrossEntropyLoss
+// with softcap 15.0; "Doorvoer verhogen", fused linear cross-entropy bullet:
+// the head's matmul runs chunk by chunk inside the loss so that the whole
+// logits tensor never exists):
+//   S = c tanh(Z / c)                       capped logits, |S| <= c
+//   loss_r = log sum_j exp(S_rj) - S_r,t_r  over the n_classes real classes
+//   dZ_rj = (softmax_j(S_r) - [j = t_r]) (1 - tanh^2(Z_rj / c)) / n_valid
+// Rows whose target lies outside [0, n_classes) are ignored (zero loss and
+// gradient); the padded vocabulary columns get a zero gradient.
+//
+// Design: one 512-thread block per row.  The row's bf16 logits are staged in
+// LDS once (up to 65536 columns, 128 KB), the sum of exponentials is taken
+// against the fixed offset c (|S| <= c, so exp(S - c) lies in [e^-2c, 1] and
+// neither overflows nor needs a running maximum), and a second sweep over LDS
+// writes dZ back over the logits in place.  Reductions use a fixed tree, so
+// results are bit-reproducible.
+#include "device_common.h"
+#include "internal.h"
+
+namespace fp8mlp {
+
+namespace {
+
+constexpr int kCeThreads = 512;
+constexpr int kMaxRow = 65536;  // bf16 columns staged in LDS
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// tanh(y) = (e - 1) / (e + 1) with e = exp(2y); |y| is clamped to 20, where
+// tanh is 1 to fp32 precision.
+__device__ __forceinline__ float tanh_fast(float y) {
+  const float yc = __builtin_fminf(__builtin_fmaxf(y, -20.0f), 20.0f);
+  const float e = exp_fast(2.0f * yc);
+  return (e - 1.0f) * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Fixed-order block sum (butterfly inside waves, then waves in order).
+__device__ float block_sum_f32(float v, float* red) {
+  v = wave_sum_f32(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float s = 0.0f;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+__global__ void __launch_bounds__(256) count_valid_kernel(const int32_t* targets, int64_t M, int64_t n_classes,
+                                                          int32_t* n_valid) {
+  __shared__ int red[4];
+  int c = 0;
+  for (int64_t i = threadIdx.x; i < M; i += 256) {
+    const int32_t t = targets[i];
+    c += (t >= 0 && t < n_classes) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) *n_valid = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ void __launch_bounds__(kCeThreads, 1) softcap_ce_kernel(uint16_t* z, int64_t V, int64_t ldz,
+                                                                   int64_t n_classes, float softcap,
+                                                                   const int32_t* targets,
+                                                                   const int32_t* n_valid, float* loss_rows,
+                                                                   uint32_t* partials) {
+  __shared__ __attribute__((aligned(16))) uint16_t row[kMaxRow];
+  __shared__ float redf[kCeThreads / 64];
+  __shared__ uint32_t redu[kCeThreads / 64];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  uint16_t* zr = z + (int64_t)r * ldz;
+  const int32_t t = targets[r];
+  const bool valid = t >= 0 && t < n_classes;
+  const int nch = (int)((V + 7) / 8);  // 8-column chunks (ldz is a multiple of 8)
+
+  if (!valid) {  // ignored row: zero gradient, zero loss
+    for (int c = tid; c < nch; c += kCeThreads) {
+      if (8 * c + 8 <= V) {
+        *reinterpret_cast<v4u*>(zr + 8 * c) = v4u{0u, 0u, 0u, 0u};
+      } else {
+        for (int e = 8 * c; e < V; ++e) zr[e] = 0;
+      }
+    }
+    if (tid == 0) {
+      loss_rows[r] = 0.0f;
+      partials[r] = 0u;
+    }
+    return;
+  }
+
+  // 1. stage the row and sum exp(S - c) over the classes
+  const float inv_c = 1.0f / softcap;
+  float sum = 0.0f;
+  for (int c = tid; c < nch; c += kCeThreads) {
+    const v4u v = *reinterpret_cast<const v4u*>(zr + 8 * c);
+    *reinterpret_cast<v4u*>(row + 8 * c) = v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * c + e;
+      if (j < n_classes) {
+        const float zj = bf16_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        const float s = softcap * tanh_fast(zj * inv_c);
+        sum += exp_fast(s - softcap);
+      }
+    }
+  }
+  sum = block_sum_f32(sum, redf);
+  const float lse = softcap + __logf(sum);
+  const float nv = (float)(*n_valid);
+  const float inv_nv = nv > 0.0f ? 1.0f / nv : 0.0f;
+  if (tid == 0) {
+    const float st = softcap * tanh_fast(bf16_to_f32(row[t]) * inv_c);
+    loss_rows[r] = lse - st;
+  }
+
+  // 2. dZ over the row, written over the logits
+  uint32_t mx = 0;
+  for (int c = tid; c < nch; c += kCeThreads) {
+    const v4u v = *reinterpret_cast<const v4u*>(row + 8 * c);
+    v4u o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = 8 * c + 2 * h + k;
+        uint32_t bits = 0;
+        if (j < n_classes) {
+          const float zj = bf16_to_f32((v[h] >> (16 * k)) & 0xFFFFu);
+          const float th = tanh_fast(zj * inv_c);
+          const float p = exp_fast(softcap * th - lse);
+          const float g = ((j == t ? p - 1.0f : p) * (1.0f - th * th)) * inv_nv;
+          bits = __builtin_bit_cast(unsigned short, (__bf16)g);
+          mx = mx > (bits & 0x7FFFu) ? mx : (bits & 0x7FFFu);
+        }
+        w |= bits << (16 * k);
+      }
+      o[h] = w;
+    }
+    if (8 * c + 8 <= V) {
+      *reinterpret_cast<v4u*>(zr + 8 * c) = o;
+    } else {
+      for (int e = 8 * c; e < V; ++e) zr[e] = (uint16_t)(o[(e - 8 * c) >> 1] >> (16 * ((e - 8 * c) & 1)));
+    }
+  }
+  mx = block_max_u32(mx, redu);
+  if (tid == 0) partials[r] = mx;
+}
+
+__global__ void __launch_bounds__(256) zero_cols_kernel(uint8_t* base, int64_t rows, int64_t ld, int64_t c0,
+                                                        int64_t c1) {
+  const int64_t w = c1 - c0, n = rows * w;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    base[(i / w) * ld + c0 + i % w] = 0;
+}
+
+// dw = RN_bf16(dwf), 8 elements per thread step (n % 8 == 0); dwf == nullptr
+// writes zeros.
+__global__ void __launch_bounds__(256) f32_to_bf16_kernel(const float* dwf, uint16_t* dw, int64_t n) {
+  const int64_t n8 = n / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    v4u o = {0u, 0u, 0u, 0u};
+    if (dwf) {
+      const v4f a = reinterpret_cast<const v4f*>(dwf)[2 * i];
+      const v4f b = reinterpret_cast<const v4f*>(dwf)[2 * i + 1];
+      o[0] = f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16);
+      o[1] = f32_to_bf16_rne(a[2]) | (f32_to_bf16_rne(a[3]) << 16);
+      o[2] = f32_to_bf16_rne(b[0]) | (f32_to_bf16_rne(b[1]) << 16);
+      o[3] = f32_to_bf16_rne(b[2]) | (f32_to_bf16_rne(b[3]) << 16);
+    }
+    reinterpret_cast<v4u*>(dw)[i] = o;
+  }
+}
+
+// loss = (sum over rows, in fp64, fixed order) / n_valid.
+__global__ void __launch_bounds__(256) loss_kernel(const float* loss_rows, int64_t M, const int32_t* n_valid,
+                                                   float* loss) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < M; i += 256) s += (double)loss_rows[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int nv = *n_valid;
+    *loss = nv > 0 ? (float)(red[0] / (double)nv) : 0.0f;
+  }
+}
+
+int grid_for(int64_t n, int per_block) {
+  const int64_t b = (n + per_block - 1) / per_block;
+  return (int)(b < 1 ? 1 : (b > 4096 ? 4096 : b));
+}
+
+}  // namespace
+
+hipError_t launch_count_valid(const int32_t* targets, int64_t M, int64_t n_classes, int32_t* n_valid,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(count_valid_kernel, dim3(1), dim3(256), 0, st, targets, M, n_classes, n_valid);
+  return hipGetLastError();
+}
+
+hipError_t launch_softcap_ce(uint16_t* z, int64_t rows, int64_t V, int64_t ldz, int64_t n_classes,
+                             float softcap, const int32_t* targets, const int32_t* n_valid,
+                             float* loss_rows, uint32_t* partials, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (V > kMaxRow || ldz % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(softcap_ce_kernel, dim3((unsigned)rows), dim3(kCeThreads), 0, st, z, V, ldz, n_classes,
+                     softcap, targets, n_valid, loss_rows, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_cols(uint8_t* base, int64_t rows, int64_t ld, int64_t c0, int64_t c1, hipStream_t st) {
+  if (rows <= 0 || c1 <= c0) return hipSuccess;
+  hipLaunchKernelGGL(zero_cols_kernel, dim3(grid_for(rows * (c1 - c0), 256)), dim3(256), 0, st, base, rows,
+                     ld, c0, c1);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, const float* loss_rows, int64_t M,
+                                 const int32_t* n_valid, float* loss, hipStream_t st) {
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(grid_for(n / 8, 256)), dim3(256), 0, st, dwf, dw, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, loss_rows, M, n_valid, loss);
+  return hipGetLastError();
+}
+
+int64_t lm_ce_max_vocab() { return kMaxRow; }
+
+}  // namespace fp8mlp

@@ -177,6 +177,41 @@ class LMHeadWorkload:
         return 6 * self.M * self.K * self.N
 
 
+@dataclass
+class LMHeadCEWorkload:
+    """LM head fused with the softcapped cross-entropy: X [M,K] ~ N(0,1),
+    W [V,K] ~ N(0, sigma_w) with rows >= n_classes zero, targets [M] int32
+    uniform over the classes with a fraction set to -100 (ignored)."""
+    wid: int
+    M: int
+    K: int
+    V: int
+    n_classes: int = 50257
+    chunk: int = 2048
+    softcap: float = 15.0
+    sigma_w: float = 0.02
+    ignored: float = 0.01
+    name: str = ""
+
+    def tensors(self):
+        s = 1000 * self.wid
+        x = normal_bf16((self.M, self.K), 1.0, s + 1)
+        w = normal_bf16((self.n_classes, self.K), self.sigma_w, s + 2)
+        if self.V > self.n_classes:
+            w = np.concatenate([w, np.zeros((self.V - self.n_classes, self.K), np.uint16)], 0)
+        rng = np.random.Generator(np.random.PCG64(s + 7))
+        t = rng.integers(0, self.n_classes, self.M).astype(np.int32)
+        k = int(round(self.ignored * self.M))
+        if k > 0:
+            t[np.random.Generator(np.random.PCG64(s + 57)).choice(self.M, size=k, replace=False)] = -100
+        return x, w, t
+
+    @property
+    def flops(self) -> int:
+        """GEMM FLOPs of the head: logits, grad-input, grad-weight."""
+        return 6 * self.M * self.K * self.V
+
+
 # The five workloads: a single linear, a small block, the 3.8B-model block,
 # the full projection set and the LM head (padded / unpadded vocabulary).
 LINEAR_SMALL = LinearWorkload(1, 256, 1024, 512, name="fp8 linear fwd 256x1024x512")
@@ -186,3 +221,4 @@ MLP_3P8B = MLPWorkload(3, 8192, 3072, 12288, name="relu2 MLP M=8192 d=3072 h=122
 PROJ_SET = ProjectionSetWorkload(4, 32768, name="decoder projection set M=32768")
 LM_HEAD_PADDED = LMHeadWorkload(5, 16384, 3072, 50304, name="LM head M=16384 K=3072 N=50304")
 LM_HEAD_UNPADDED = LMHeadWorkload(5, 16384, 3072, 50257, name="LM head M=16384 K=3072 N=50257")
+LM_HEAD_CE = LMHeadCEWorkload(6, 16384, 3072, 50304, name="LM head + softcapped CE M=16384 K=3072 V=50304")

@@ -180,6 +180,58 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
                   int64_t h, uint16_t* dx, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* FP8 LM head fused with the softcapped cross-entropy, chunked over rows.  */
+/*                                                                          */
+/* decomputer.nl, "Doorvoer verhogen", fused linear cross-entropy bullet:   */
+/* the head's matmul runs inside the loss, a chunk of rows at a time, so    */
+/* the whole [M, V] logits tensor is never stored; the appendix caps the    */
+/* logits at 15.0 (logit_softcap; loss LigerFusedLinearCrossEntropyLoss     */
+/* with softcap 15.0).  With c = softcap, for every chunk of `chunk` rows:  */
+/*   Z   = RN_bf16(RN32(sx*sw) Xq_k . Wq^T)        logits, bf16             */
+/*   S   = c tanh(Z / c)                                                    */
+/*   loss_r = log sum_j exp(S_rj) - S_r,t_r        over j < n_classes       */
+/*   dZ  = RN_bf16((softmax(S) - onehot(t)) (1 - tanh^2(Z/c)) / n_valid)     */
+/*   dZq, s_k = quant(dZ, E5M2)                    the chunk's own scale     */
+/*   dX_k = RN_bf16(RN32(s_k*sw) dZq . Wq)         grad-input (bf16)         */
+/*   dW  += RN32(s_k*sx) dZq^T . Xq_k              fp32, rounded once at end  */
+/* with Xq, sx and Wq, sw the E4M3 tensorwise quantisations of X and W.      */
+/* Rows whose target lies outside [0, n_classes) are ignored; n_valid counts */
+/* the others; loss = sum of row losses / n_valid (0 when n_valid == 0).     */
+/* The softmax, tanh and exp run in fp32; sums in a fixed order, so results  */
+/* are reproducible bit for bit.                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace for fp8_lm_head_ce (0 if the shape is not supported).  Holds Xq,
+ * Xq^T, Wq, Wq^T, one chunk of logits (bf16, chunk x V rounded up to 16) and
+ * its codes, the fp32 dW accumulator and small per-row / per-chunk arrays. */
+size_t fp8_lm_head_ce_workspace_bytes(int64_t M, int64_t K, int64_t V, int64_t chunk);
+
+/* Byte offsets (n >= 14) of the workspace regions, in this order: Xq [M,K],
+ * Xq^T [K,M], Wq [V,K], Wq^T [K,Vp], logits/dZ of the last chunk (bf16
+ * [chunk,Vp]), dZ codes [chunk,Vp], dZ^T codes [V,chunk], dW fp32 [V,K], row
+ * losses [M] fp32, amax partials of X and W, row partials, the valid-row
+ * count, scales; Vp = V rounded up to 16. */
+int fp8_lm_head_ce_workspace_layout(int64_t M, int64_t K, int64_t V, int64_t chunk, size_t* offsets, int n);
+
+/*
+ * x        [M, K] bf16 hidden states (dense rows); w [V, K] bf16 head weight
+ *          (V may include padding rows beyond n_classes).
+ * targets  [M] int32 class ids (device); ids outside [0, n_classes) are ignored.
+ * softcap  c > 0 (15.0 on the pages).
+ * chunk    rows per chunk, a multiple of 16 (the logits buffer is chunk x V).
+ * loss     out: 1 float (device), the mean loss over the counted rows.
+ * dx       out: [M, K] bf16.  dw  out: [V, K] bf16 (rows >= n_classes are 0
+ *          when the padded rows of w are zero).
+ * scales   out (may be NULL): 2 + ceil(M / chunk) floats: sx, sw, then the
+ *          dZ scale of every chunk.
+ * Requirements: M, K multiples of 16 (M == 0 valid: loss 0, dw 0);
+ *          1 <= n_classes <= V <= 65536; x, w, dx, dw 16-byte aligned.
+ */
+int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets, int64_t M, int64_t K,
+                   int64_t V, int64_t n_classes, float softcap, int64_t chunk, float* loss, uint16_t* dx,
+                   uint16_t* dw, float* scales, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

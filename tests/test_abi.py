@@ -134,3 +134,29 @@ def test_mlp_validation():
     offs = (ctypes.c_size_t * 8)()
     assert L.relu2_mlp_bwd_workspace_layout(64, 64, 256, offs, 8) == 0
     assert list(offs) == sorted(offs) and offs[0] == 0
+
+
+def test_lm_head_ce_validation():
+    L = _native.lib()
+    assert L.fp8_lm_head_ce_workspace_bytes(256, 256, 600, 64) > 256 * 256 * 2 + 600 * 256 * 6
+    assert L.fp8_lm_head_ce_workspace_bytes(256, 256, 600, 60) == 0        # chunk % 16
+    assert L.fp8_lm_head_ce_workspace_bytes(256, 256, 70000, 64) == 0      # vocabulary beyond the LDS row
+    n = L.fp8_lm_head_ce_workspace_bytes(256, 256, 600, 64)
+    f = ctypes.c_float
+    ok = [FAKE, FAKE, FAKE, 256, 256, 600, 590, f(15.0), 64, FAKE, FAKE, FAKE, None, FAKE, n, None]
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return L.fp8_lm_head_ce(*a)
+    assert call(a6=601) == 1                 # n_classes > V
+    assert call(a6=0) == 1                   # no classes
+    assert call(a7=f(0.0)) == 1              # softcap must be positive
+    assert call(a3=250) == 5                 # M % 16
+    assert call(a4=40) == 5                  # K % 16
+    assert call(a9=None) == 1                # loss missing
+    assert call(a14=n - 1) == 3              # workspace too small
+    assert call(a0=ctypes.c_void_p(0x10008)) == 2   # x not 16-byte aligned
+    offs = (ctypes.c_size_t * 14)()
+    assert L.fp8_lm_head_ce_workspace_layout(256, 256, 600, 64, offs, 14) == 0
+    assert list(offs) == sorted(offs) and offs[0] == 0

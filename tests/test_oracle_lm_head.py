@@ -62,6 +62,24 @@ def test_closed_forms():
     assert abs(loss2[0] - np.log(n)) < 1e-12 and np.abs(g2).max() < 1e-12
 
 
+def test_columns_match_rows():
+    """The column form (given each row's log-sum-exp) reproduces the row form."""
+    R, V, n = 20, 96, 90
+    z = _logits(R, V, 72, 6.0)
+    t = np.random.default_rng(2).integers(0, n, R)
+    t[4] = -100
+    t[9] = 93            # a padded class id: ignored
+    nv = int(((t >= 0) & (t < n)).sum())
+    _, g, dz = oracle.softcap_ce_rows(z, t, n, 15.0, nv)
+    zz = oracle.bf16_bits_to_f64(z)[:, :n]
+    s = 15.0 * np.tanh(zz / 15.0)
+    lse = np.log(np.exp(s).sum(axis=1))
+    cols = [0, 5, 89, 90, 95]
+    gt, dzt = oracle.softcap_ce_columns(np.ascontiguousarray(z[:, cols].T), cols, lse, t, n, 15.0, nv)
+    assert np.allclose(gt, g[:, cols].T, rtol=1e-12, atol=1e-18)
+    assert (g[9] == 0).all() and (gt[:, 9] == 0).all() and (gt[3:] == 0).all()
+
+
 def test_chunked_grad_weight_accumulation_is_exact():
     """Two chunks accumulated in fp64 equal one product over all rows, up to
     fp64 rounding; rounding the sum once equals the one-shot GEMM."""
