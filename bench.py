@@ -206,7 +206,7 @@ def main() -> int:
     ap.add_argument("--workload", choices=("mlp", "proj", "lmhead", "lmce"), default="mlp",
                     help="mlp: the relu2 block M=8192 (default); proj: the decoder projection set at "
                          "M=32768; lmhead: the LM head at vocabulary 50304 and 50257; lmce: the LM head "
-                         "fused with the softcapped cross-entropy (chunks of 2048 rows)")
+                         "fused with the softcapped cross-entropy (chunks of 4096 rows)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "

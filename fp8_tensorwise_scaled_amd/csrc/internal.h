@@ -88,7 +88,7 @@ hipError_t launch_softcap_ce(uint16_t* z, int64_t rows, int64_t V, int64_t ldz, 
 // Zero columns [c0, c1) of a [rows, ld] byte matrix.
 hipError_t launch_zero_cols(uint8_t* base, int64_t rows, int64_t ld, int64_t c0, int64_t c1, hipStream_t st);
 // dw = RN_bf16(dwf) over n elements; loss = sum(loss_rows) / n_valid (0 if none).
-int64_t lm_ce_max_vocab();  // largest vocabulary the row kernel stages in LDS
+int64_t lm_ce_max_vocab();  // largest vocabulary the row kernel takes
 hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, const float* loss_rows, int64_t M,
                                  const int32_t* n_valid, float* loss, hipStream_t st);
 

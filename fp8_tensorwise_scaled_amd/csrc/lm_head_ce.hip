@@ -13,12 +13,12 @@
 // Rows whose target lies outside [0, n_classes) are ignored (zero loss and
 // gradient); the padded vocabulary columns get a zero gradient.
 //
-// Design: one 512-thread block per row.  The row's bf16 logits are staged in
-// LDS once (up to 65536 columns, 128 KB), the sum of exponentials is taken
-// against the fixed offset c (|S| <= c, so exp(S - c) lies in [e^-2c, 1] and
-// neither overflows nor needs a running maximum), and a second sweep over LDS
-// writes dZ back over the logits in place.  Reductions use a fixed tree, so
-// results are bit-reproducible.
+// Design: one 512-thread block per row.  A first sweep over the row's bf16
+// logits sums the exponentials against the fixed offset c (|S| <= c, so
+// exp(S - c) lies in [e^-2c, 1] and neither overflows nor needs a running
+// maximum); a second sweep, served from L2 (a row is 100 KB), writes dZ back
+// over the logits in place.  No LDS beyond the reductions, so several rows
+// share a CU.  Reductions use a fixed tree, so results are bit-reproducible.
 #include "device_common.h"
 #include "internal.h"
 
@@ -27,7 +27,7 @@ namespace fp8mlp {
 namespace {
 
 constexpr int kCeThreads = 512;
-constexpr int kMaxRow = 65536;  // bf16 columns staged in LDS
+constexpr int64_t kMaxVocab = int64_t{1} << 22;  // columns per row (int offsets, tile ranges)
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
@@ -73,12 +73,10 @@ __global__ void __launch_bounds__(256) count_valid_kernel(const int32_t* targets
   if (threadIdx.x == 0) *n_valid = red[0] + red[1] + red[2] + red[3];
 }
 
-__global__ void __launch_bounds__(kCeThreads, 1) softcap_ce_kernel(uint16_t* z, int64_t V, int64_t ldz,
-                                                                   int64_t n_classes, float softcap,
-                                                                   const int32_t* targets,
-                                                                   const int32_t* n_valid, float* loss_rows,
-                                                                   uint32_t* partials) {
-  __shared__ __attribute__((aligned(16))) uint16_t row[kMaxRow];
+__global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int64_t V, int64_t ldz,
+                                                                int64_t n_classes, float softcap,
+                                                                const int32_t* targets, const int32_t* n_valid,
+                                                                float* loss_rows, uint32_t* partials) {
   __shared__ float redf[kCeThreads / 64];
   __shared__ uint32_t redu[kCeThreads / 64];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -102,12 +100,11 @@ __global__ void __launch_bounds__(kCeThreads, 1) softcap_ce_kernel(uint16_t* z, 
     return;
   }
 
-  // 1. stage the row and sum exp(S - c) over the classes
+  // 1. sum exp(S - c) over the classes
   const float inv_c = 1.0f / softcap;
   float sum = 0.0f;
   for (int c = tid; c < nch; c += kCeThreads) {
     const v4u v = *reinterpret_cast<const v4u*>(zr + 8 * c);
-    *reinterpret_cast<v4u*>(row + 8 * c) = v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = 8 * c + e;
@@ -118,19 +115,18 @@ __global__ void __launch_bounds__(kCeThreads, 1) softcap_ce_kernel(uint16_t* z, 
       }
     }
   }
-  sum = block_sum_f32(sum, redf);
+  const float zt = bf16_to_f32(zr[t]);  // read before any block writes the row
+  sum = block_sum_f32(sum, redf);       // (its barriers also order the reads above before the writes below)
   const float lse = softcap + __logf(sum);
   const float nv = (float)(*n_valid);
   const float inv_nv = nv > 0.0f ? 1.0f / nv : 0.0f;
-  if (tid == 0) {
-    const float st = softcap * tanh_fast(bf16_to_f32(row[t]) * inv_c);
-    loss_rows[r] = lse - st;
-  }
+  if (tid == 0) loss_rows[r] = lse - softcap * tanh_fast(zt * inv_c);
 
-  // 2. dZ over the row, written over the logits
+  // 2. dZ over the row, written over the logits (a second read of the row,
+  //    which the first sweep has just brought into L2)
   uint32_t mx = 0;
   for (int c = tid; c < nch; c += kCeThreads) {
-    const v4u v = *reinterpret_cast<const v4u*>(row + 8 * c);
+    const v4u v = *reinterpret_cast<const v4u*>(zr + 8 * c);
     v4u o;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -221,7 +217,7 @@ hipError_t launch_softcap_ce(uint16_t* z, int64_t rows, int64_t V, int64_t ldz, 
                              float softcap, const int32_t* targets, const int32_t* n_valid,
                              float* loss_rows, uint32_t* partials, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (V > kMaxRow || ldz % 8 != 0) return hipErrorInvalidValue;
+  if (V > kMaxVocab || ldz % 8 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(softcap_ce_kernel, dim3((unsigned)rows), dim3(kCeThreads), 0, st, z, V, ldz, n_classes,
                      softcap, targets, n_valid, loss_rows, partials);
   return hipGetLastError();
@@ -243,6 +239,6 @@ hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, cons
   return hipGetLastError();
 }
 
-int64_t lm_ce_max_vocab() { return kMaxRow; }
+int64_t lm_ce_max_vocab() { return kMaxVocab; }
 
 }  // namespace fp8mlp

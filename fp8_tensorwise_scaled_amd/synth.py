@@ -187,7 +187,7 @@ class LMHeadCEWorkload:
     K: int
     V: int
     n_classes: int = 50257
-    chunk: int = 2048
+    chunk: int = 4096
     softcap: float = 15.0
     sigma_w: float = 0.02
     ignored: float = 0.01

@@ -226,7 +226,7 @@ int fp8_lm_head_ce_workspace_layout(int64_t M, int64_t K, int64_t V, int64_t chu
  * scales   out (may be NULL): 2 + ceil(M / chunk) floats: sx, sw, then the
  *          dZ scale of every chunk.
  * Requirements: M, K multiples of 16 (M == 0 valid: loss 0, dw 0);
- *          1 <= n_classes <= V <= 65536; x, w, dx, dw 16-byte aligned.
+ *          1 <= n_classes <= V <= 4194304; x, w, dx, dw 16-byte aligned.
  */
 int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets, int64_t M, int64_t K,
                    int64_t V, int64_t n_classes, float softcap, int64_t chunk, float* loss, uint16_t* dx,

@@ -140,7 +140,7 @@ def test_lm_head_ce_validation():
     L = _native.lib()
     assert L.fp8_lm_head_ce_workspace_bytes(256, 256, 600, 64) > 256 * 256 * 2 + 600 * 256 * 6
     assert L.fp8_lm_head_ce_workspace_bytes(256, 256, 600, 60) == 0        # chunk % 16
-    assert L.fp8_lm_head_ce_workspace_bytes(256, 256, 70000, 64) == 0      # vocabulary beyond the LDS row
+    assert L.fp8_lm_head_ce_workspace_bytes(256, 256, 1 << 23, 64) == 0    # vocabulary beyond the limit
     n = L.fp8_lm_head_ce_workspace_bytes(256, 256, 600, 64)
     f = ctypes.c_float
     ok = [FAKE, FAKE, FAKE, 256, 256, 600, 590, f(15.0), 64, FAKE, FAKE, FAKE, None, FAKE, n, None]
