@@ -84,6 +84,8 @@ def _load():
                 fn.argtypes = [vp, i64, c_int, f32, vp, i64, c_int, f32, i64, i64, i64, vp, i64, vp, i64]
             lib.orc_gemm_tn_acc.restype = None
             lib.orc_gemm_tn_acc.argtypes = [vp, i64, c_int, f32, vp, i64, c_int, f32, i64, i64, i64, vp, i64]
+            lib.orc_rmsnorm.restype = None
+            lib.orc_rmsnorm.argtypes = [vp, i64, i64, i64, vp, f32, vp, vp]
             lib.orc_relu2.restype = None
             lib.orc_relu2.argtypes = [vp, i64, vp]
             lib.orc_relu2_bwd.restype = None
@@ -217,6 +219,33 @@ def gemm_tn_acc(a, fa, sa, b, fb, sb, acc: np.ndarray) -> None:
                             _ptr(acc), K)
 
 
+# --------------------------------------------------------------- RMSNorm
+def rmsnorm(x: np.ndarray, gamma: np.ndarray | None, eps: float):
+    """RMSNorm of bf16 rows (Llama-style, decomputer.nl appendix:
+    rms_norm_eps 1.0e-6), each step in a stated precision:
+      ms = RN32(RN64(sum_j x_j^2 / d))   (the sum in fp64)
+      r  = RN32(1 / RN32(sqrt(RN32(ms + eps))))
+      X_j = RN_bf16(RN32(RN32(x_j r) g_j))   (no g: RN_bf16(RN32(x_j r)))
+    Returns (X as bf16 bits [rows, cols], r [rows] fp32)."""
+    x = _c(x, np.uint16)
+    r, c = x.shape
+    out = np.empty((r, c), dtype=np.uint16)
+    rstd = np.empty(r, dtype=np.float32)
+    g = None if gamma is None else _c(np.asarray(gamma).reshape(-1), np.uint16)
+    if g is not None:
+        assert g.size == c
+    _load().orc_rmsnorm(_ptr(x), r, c, c, None if g is None else _ptr(g), np.float32(eps), _ptr(out), _ptr(rstd))
+    return out, rstd
+
+
+def rmsnorm_quant(x: np.ndarray, gamma: np.ndarray | None, eps: float, fmt: int):
+    """RMSNorm followed by the dynamic tensorwise quantisation of its output:
+    returns (codes, scale, amax, X bits, rstd)."""
+    xn, rstd = rmsnorm(x, gamma, eps)
+    q, s, a = quant(xn, fmt)
+    return q, s, a, xn, rstd
+
+
 # --------------------------------------------------------------- relu^2
 def relu2(h: np.ndarray) -> np.ndarray:
     h = _c(h, np.uint16)
@@ -310,6 +339,27 @@ def softcap_ce_rows(z_bits: np.ndarray, targets: np.ndarray, n_classes: int, sof
     g[:, :n_classes] = p * (1.0 - t * t) / max(n_valid, 1)
     g[~valid] = 0.0
     return loss, g, double_to_bf16(g)
+
+
+def softcap_ce_columns(zt_bits: np.ndarray, cols, lse: np.ndarray, targets: np.ndarray, n_classes: int,
+                       softcap: float, n_valid: int) -> np.ndarray:
+    """Columns `cols` of the softcapped cross-entropy's logit gradient, given
+    the logits of those columns for every row (zt_bits [ncols, R], bf16 bits,
+    i.e. transposed) and every row's log-sum-exp (lse [R], fp64, over the
+    classes).  Same formula as softcap_ce_rows; returns G^T [ncols, R] fp64
+    and its bf16 bits."""
+    cols = np.asarray(cols, dtype=np.int64)
+    z = bf16_bits_to_f64(zt_bits)
+    t = np.tanh(z / softcap)
+    s = softcap * t
+    p = np.exp(s - np.asarray(lse)[None, :])
+    tg = np.asarray(targets, dtype=np.int64)
+    valid = (tg >= 0) & (tg < n_classes)
+    p -= (tg[None, :] == cols[:, None]).astype(np.float64)
+    g = p * (1.0 - t * t) / max(n_valid, 1)
+    g[:, ~valid] = 0.0
+    g[cols >= n_classes, :] = 0.0
+    return g, double_to_bf16(g)
 
 
 def lm_head_ce(x, w, targets, n_classes: int, softcap: float = 15.0, chunk: int | None = None):

@@ -321,6 +321,38 @@ void orc_gemm_tn_acc(const uint8_t* a, int64_t lda, int fa, float sa,
 }
 
 /* ---------------------------------------------------------------------- */
+/* RMSNorm of bf16 rows (decomputer.nl, appendix: Llama-style RMSNorm,     */
+/* rms_norm_eps 1.0e-6), the step before the MLP's input quantisation:     */
+/*   ms = RN32(sum_j x_j^2 / d)       (sum in fp64)                         */
+/*   r  = RN32(1 / RN32(sqrt(RN32(ms + eps))))                              */
+/*   X_j = RN_bf16(RN32(RN32(x_j r) g_j))   (g NULL: RN_bf16(RN32(x_j r)))   */
+/* out [rows, cols] bf16 bits (dense), rstd [rows] = r.                    */
+/* ---------------------------------------------------------------------- */
+static uint16_t f32_to_bf16_bits(float f) { return orc_double_to_bf16((double)f); }
+
+void orc_rmsnorm(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const uint16_t* g,
+                 float eps, uint16_t* out, float* rstd) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < rows; ++i) {
+    double ss = 0.0;
+    for (int64_t j = 0; j < cols; ++j) {
+      const double v = (double)bf16_to_float(x[i * ld + j]);
+      ss += v * v;
+    }
+    volatile float ms = (float)(ss / (double)cols);
+    volatile float t = ms + eps;
+    volatile float sq = sqrtf(t);
+    volatile float r = 1.0f / sq;
+    rstd[i] = r;
+    for (int64_t j = 0; j < cols; ++j) {
+      volatile float y = bf16_to_float(x[i * ld + j]) * r;
+      if (g) y = y * bf16_to_float(g[j]);
+      out[i * cols + j] = f32_to_bf16_bits(y);
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------- */
 /* relu^2 and its derivative on bf16 tensors.                              */
 /*   A  = RN_bf16( relu(H)^2 )             (exact square before rounding)  */
 /*   dH = RN_bf16( 2 * relu(H) * dA )      (exact product before rounding) */
