@@ -139,6 +139,37 @@ def bench_other(args) -> int:
                                       "o 3072, relu2 MLP 12288)", "M": w.M, "gemm_flops": r.flops},
                "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
                "tokens_per_s_equiv": round(w.M / (ms * 1e-3))}
+    elif args.workload == "rmsnorm":
+        from fp8_tensorwise_scaled_amd import api
+
+        M, d = 8192, 3072
+        log(f"generating RMSNorm inputs [{M}, {d}]")
+        X = t(synth.normal_bf16((M, d), 2.5, 3001))
+        G = t(synth.normal_bf16((d,), 1.0, 3002))
+        q = torch.empty((M, d), dtype=torch.uint8, device=dev)
+        qt = torch.empty((d, M), dtype=torch.uint8, device=dev)
+        sc, am, rs = (torch.empty(n, dtype=torch.float32, device=dev) for n in (1, 1, M))
+        ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+        fused = lambda: api.fp8_rmsnorm_quant(X, G, 1e-6, api.E4M3, q=q, qt=qt, scale=sc, amax=am, rstd=rs, ws=ws)
+
+        def unfused():  # torch's RMSNorm writing X, then the quantiser reading it
+            xn = torch.nn.functional.rms_norm(X, (d,), G, 1e-6)
+            api.fp8_amax_quant(xn, api.E4M3, q=q, qt=qt, scale=sc, amax=am, ws=ws)
+        ms = _time_steps(fused, args.steps * 5, args.warmup)
+        ms_unf = _time_steps(unfused, args.steps * 5, args.warmup)
+        nbytes = M * d * 6 + M * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"RMSNorm + quantise: {ms * 1e3:.1f} us ({gbs:.0f} GB/s); torch rms_norm then quantise: "
+            f"{ms_unf * 1e3:.1f} us")
+        res = {"metric": "RMSNorm fused with FP8 tensorwise quantisation (codes + transposed codes), GB/s",
+               "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 5),
+               "data": "synthetic (seeded N(0,2.5) rows with 0.1% x100 outliers, N(0,1) weight; bf16)",
+               "config": {"workload": f"RMSNorm + E4M3 quantisation of X [{M}, {d}], eps 1e-6", "M": M, "d": d,
+                          "algorithmic_bytes": nbytes},
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+               "unfused_torch_rmsnorm_then_quantise_ms": round(ms_unf, 5)}
+        common["unit"] = "GB/s"
     elif args.workload == "lmce":
         from fp8_tensorwise_scaled_amd import api
 
@@ -203,10 +234,11 @@ def main() -> int:
     ap.add_argument("--gemm-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain device copies of 256 MiB (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead", "lmce"), default="mlp",
+    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead", "lmce", "rmsnorm"), default="mlp",
                     help="mlp: the relu2 block M=8192 (default); proj: the decoder projection set at "
                          "M=32768; lmhead: the LM head at vocabulary 50304 and 50257; lmce: the LM head "
-                         "fused with the softcapped cross-entropy (chunks of 4096 rows)")
+                         "fused with the softcapped cross-entropy (chunks of 4096 rows); rmsnorm: RMSNorm fused "
+                         "with the quantisation of the block input X [8192, 3072]")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "

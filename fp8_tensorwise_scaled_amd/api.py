@@ -33,7 +33,11 @@ def _check_dev(*ts):
 
 
 def _ld(t: torch.Tensor) -> int:
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.numel() == 0:  # empty: strides carry no layout
+        return t.shape[1]
+    if t.stride(1) != 1:
         raise ValueError("expected a 2-D tensor with unit column stride")
     return t.stride(0)
 
@@ -67,6 +71,32 @@ def fp8_amax_quant(x: torch.Tensor, fmt: int = E4M3, *, q: torch.Tensor | None =
     _native.call("fp8_amax_quant", _p(x), rows, cols, _ld(x), fmt, _p(q), 0 if q is None else _ld(q),
                  _p(qt), 0 if qt is None else _ld(qt), _p(scale), _p(amax), _p(ws), ws.numel(), _stream())
     return q, qt, scale, amax
+
+
+def fp8_rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor | None = None, eps: float = 1e-6, fmt: int = E4M3, *,
+                      q=None, qt=None, want_q: bool = True, want_qt: bool = False, scale=None, amax=None,
+                      rstd=None, ws=None):
+    """RMSNorm of the rows of x fused with the tensorwise quantisation of its
+    output.  Returns (q, qt, scale, amax, rstd)."""
+    _check_dev(x, gamma)
+    if x.dtype != torch.bfloat16 or (gamma is not None and (gamma.dtype != torch.bfloat16 or not gamma.is_contiguous())):
+        raise TypeError("x and gamma must be bfloat16 (gamma contiguous)")
+    rows, cols = x.shape
+    dev = x.device
+    if q is None and want_q:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if qt is None and want_qt:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
+    amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
+    rstd = torch.empty(rows, dtype=torch.float32, device=dev) if rstd is None else rstd
+    if ws is None:
+        ws = torch.empty(max(_native.lib().fp8_rmsnorm_quant_workspace_bytes(rows, cols), 16), dtype=torch.uint8,
+                         device=dev)
+    _native.call("fp8_rmsnorm_quant", _p(x), _p(gamma), float(eps), rows, cols, _ld(x), fmt, _p(q),
+                 0 if q is None else _ld(q), _p(qt), 0 if qt is None else _ld(qt), _p(scale), _p(amax), _p(rstd),
+                 _p(ws), ws.numel(), _stream())
+    return q, qt, scale, amax, rstd
 
 
 def _gemm(name, a, fa, sa, b, fb, sb, M, N, K, out, out_shape):

@@ -170,6 +170,45 @@ int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, i
   return hip_status(launch_cast(b, st));
 }
 
+size_t fp8_rmsnorm_quant_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return align_up((size_t)rmsnorm_parts_for(rows) * 4);
+}
+
+int fp8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t rows, int64_t cols,
+                      int64_t ldx, int fmt, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale,
+                      float* amax, float* rstd, void* ws, size_t ws_bytes, void* stream) {
+  if (!scale) return FP8MLP_EINVAL;
+  if (rows < 0 || cols < 0 || ldx < cols || !fmt_ok(fmt)) return FP8MLP_EINVAL;
+  if (!(eps >= 0.0f) || !(eps < 1e30f)) return FP8MLP_EINVAL;
+  if (rows > 0 && cols > 0) {
+    if (!x || !rstd || (!q && !qt)) return FP8MLP_EINVAL;
+    if ((q && ldq < cols) || (qt && ldqt < rows)) return FP8MLP_EINVAL;
+    if ((q && (const void*)q == (const void*)x) || (qt && (const void*)qt == (const void*)x))
+      return FP8MLP_EINVAL;
+    if (!a2(x) || !a2(gamma) || ((uintptr_t)rstd & 3u)) return FP8MLP_EALIGN;
+  }
+  if (!ws || ws_bytes < fp8_rmsnorm_quant_workspace_bytes(rows, cols)) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+  QuantBatch b{};
+  b.njobs = 1;
+  b.job[0] = make_job(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, (uint32_t*)ws,
+                      rmsnorm_parts_for(rows), kModeRmsNorm);
+  b.job[0].rstd = rstd;
+  b.job[0].gamma = gamma;
+  hipStream_t st = (hipStream_t)stream;
+  if (rows > 0 && cols > 0) {
+    if (launch_rmsnorm_amax(b.job[0], eps, rstd, st) != hipSuccess) return FP8MLP_EHIP;
+  } else {
+    // no elements: amax 0, scale 1 (the partial the cast reads is written by
+    // the plain amax pass over nothing)
+    b.job[0].mode = kModePlain;
+    b.job[0].nparts = amax_parts_for(rows, cols);
+    if (launch_amax_partials(b, st) != hipSuccess) return FP8MLP_EHIP;
+  }
+  return hip_status(launch_cast(b, st));
+}
+
 int fp8_linear_fwd(const uint8_t* xq, int64_t ldx, int fx, const float* sx, const uint8_t* wq,
                    int64_t ldw, int fw, const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
                    int64_t ldy, void* stream) {

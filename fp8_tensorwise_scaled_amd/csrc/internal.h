@@ -11,6 +11,8 @@ enum CastMode : int {
   kModePlain = 0,  // values = x (bf16); partials = per-block max of |x| as bf16 bits
   kModeRelu2 = 1,  // values = RN_bf16(relu(x)^2) with x = H; partials = per-tile
                    // max of max(H, 0) as fp32 bits (written by the up-GEMM epilogue)
+  kModeRmsNorm = 2,  // values = RN_bf16(RN32(RN32(x r_row) g_col)): RMSNorm with the
+                     // per-row r written by rmsnorm_amax; partials as plain
 };
 
 struct QuantJob {
@@ -28,6 +30,8 @@ struct QuantJob {
   int mode;
   int blk_begin;  // first block of this job inside a batched launch
   int nblocks;    // blocks given to this job
+  const float* rstd;      // kModeRmsNorm: per-row 1/rms (written by rmsnorm_amax)
+  const uint16_t* gamma;  // kModeRmsNorm: per-column weight (bf16) or nullptr
 };
 
 constexpr int kMaxJobs = 4;
@@ -41,6 +45,10 @@ int amax_parts_for(int64_t rows, int64_t cols);
 
 // amax partial kernel for every job of the batch (mode plain only).
 hipError_t launch_amax_partials(QuantBatch& b, hipStream_t st);
+// RMSNorm statistics and amax partials of one job (mode kModeRmsNorm): writes
+// rstd[row] and one partial per block of rows (rmsnorm_parts_for of them).
+int rmsnorm_parts_for(int64_t rows);
+hipError_t launch_rmsnorm_amax(QuantJob& j, float eps, float* rstd, hipStream_t st);
 // cast kernel for every job of the batch.
 hipError_t launch_cast(QuantBatch& b, hipStream_t st);
 

@@ -120,6 +120,24 @@ __device__ __forceinline__ float cast_value(uint32_t bits) {
   return f;
 }
 
+// RMSNorm output from the stored input bits, the row's r and the column's
+// weight (has_g false: no weight): RN_bf16(RN32(RN32(x r) g)), as fp32.
+__device__ __forceinline__ float norm_value(uint32_t bits, float r, float g, bool has_g) {
+  float y = bf16_to_f32(bits) * r;
+  if (has_g) y = y * g;
+  return bf16_to_f32(f32_to_bf16_rne(y));
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t quant4_norm(uint32_t w0, uint32_t w1, float r, const float g[4], bool has_g,
+                                                const Divider& d) {
+  float a = div_rn(d, norm_value(w0 & 0xFFFFu, r, g[0], has_g));
+  float b = div_rn(d, norm_value(w0 >> 16, r, g[1], has_g));
+  float c = div_rn(d, norm_value(w1 & 0xFFFFu, r, g[2], has_g));
+  float e = div_rn(d, norm_value(w1 >> 16, r, g[3], has_g));
+  return pack4_fp8<FMT>(a, b, c, e);
+}
+
 template <int FMT, int MODE>
 __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const Divider& d) {
   float a = div_rn(d, cast_value<MODE>(w0 & 0xFFFFu));
@@ -207,8 +225,19 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
         }
       }
       uint32_t code[16];  // codes of the 4 columns of each row
+      if constexpr (MODE == kModeRmsNorm) {
+        const bool has_g = jb.gamma != nullptr;
+        float g[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if (has_g) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) code[i] = quant4<FMT, MODE>(in[i][0], in[i][1], d);
+          for (int e = 0; e < 4; ++e) g[e] = bf16_to_f32(jb.gamma[cb + e]);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) code[i] = quant4_norm<FMT>(in[i][0], in[i][1], jb.rstd[rb + i], g, has_g, d);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) code[i] = quant4<FMT, MODE>(in[i][0], in[i][1], d);
+      }
       if (q) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(q + (rb + i) * jb.ldq + cb) = code[i];
@@ -249,13 +278,128 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
         const int row = e / kTC, col = e % kTC;
         if (r0 + row < rows && c0 + col < cols) {
           const uint32_t bits = x[(r0 + row) * ldx + c0 + col];
-          const uint32_t code = pack4_fp8<FMT>(div_rn(d, cast_value<MODE>(bits)), 0.f, 0.f, 0.f) & 0xFFu;
+          float v;
+          if constexpr (MODE == kModeRmsNorm) {
+            const bool has_g = jb.gamma != nullptr;
+            v = norm_value(bits, jb.rstd[r0 + row], has_g ? bf16_to_f32(jb.gamma[c0 + col]) : 1.0f, has_g);
+          } else {
+            v = cast_value<MODE>(bits);
+          }
+          const uint32_t code = pack4_fp8<FMT>(div_rn(d, v), 0.f, 0.f, 0.f) & 0xFFu;
           if (q) q[(r0 + row) * jb.ldq + c0 + col] = (uint8_t)code;
           if (qt) qt[(c0 + col) * jb.ldqt + r0 + row] = (uint8_t)code;
         }
       }
     }
   }
+}
+
+// RMSNorm statistics (RMSNorm of the decomputer.nl appendix, applied before
+// the MLP's input quantisation): one wave per row, kRmsRows rows per block;
+// rows of up to 4096 columns are read once and kept in registers.
+//   ms = RN32(RN64(sum x^2 / d))  (fp64 sum)   r = RN32(1 / RN32(sqrt(RN32(ms + eps))))
+// rstd[row] = r; the block's partial is the max of |RN_bf16(RN32(RN32(x r) g))|.
+constexpr int kRmsRows = 8;      // two rows per wave
+constexpr int kRmsRegChunks = 8;  // rows of up to 64 x 8 x 8 = 4096 columns stay in registers
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// max |RN_bf16(RN32(RN32(x r) g))| over 8 columns; gv holds the 8 weights
+// (bf16) when has_g.
+__device__ __forceinline__ uint32_t norm_max8(v4u v, float r, v4u gv, bool has_g, uint32_t m) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float y = bf16_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) * r;
+    if (has_g) y = y * bf16_to_f32((gv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    const uint32_t mag = f32_to_bf16_rne(y) & 0x7FFFu;
+    m = m > mag ? m : mag;
+  }
+  return m;
+}
+
+__device__ __forceinline__ v4u load_g8(const uint16_t* g, int64_t col, bool g_vec) {
+  if (!g) return v4u{0u, 0u, 0u, 0u};
+  if (g_vec) return *reinterpret_cast<const v4u*>(g + col);
+  v4u o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (uint32_t)g[col + 2 * e] | ((uint32_t)g[col + 2 * e + 1] << 16);
+  return o;
+}
+
+__global__ void __launch_bounds__(256) rmsnorm_amax_kernel(QuantJob jb, float eps, float* rstd) {
+  __shared__ uint32_t red[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rows = jb.rows, cols = jb.cols, ldx = jb.ldx;
+  const uint16_t* x = jb.x;
+  const uint16_t* g = jb.gamma;
+  const bool vec = aligned16(x) && (ldx % 8 == 0) && (cols % 8 == 0);
+  const bool in_regs = vec && cols <= 64 * 8 * kRmsRegChunks;
+  const bool g_vec = g != nullptr && aligned16(g);
+  const int64_t nch = cols / 8;
+  uint32_t m = 0;
+  for (int rr = wave; rr < kRmsRows; rr += 4) {
+    const int64_t row = (int64_t)blockIdx.x * kRmsRows + rr;
+    if (row >= rows) break;
+    const uint16_t* xr = x + row * ldx;
+    double ss = 0.0;
+    v4u buf[kRmsRegChunks];
+    if (in_regs) {
+#pragma unroll
+      for (int k = 0; k < kRmsRegChunks; ++k) {
+        const int64_t c = lane + 64 * k;
+        buf[k] = c < nch ? *reinterpret_cast<const v4u*>(xr + 8 * c) : v4u{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int k = 0; k < kRmsRegChunks; ++k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double f = bf16_to_f32((buf[k][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          ss += f * f;
+        }
+      }
+    } else if (vec) {
+      for (int64_t c = lane; c < nch; c += 64) {
+        const v4u v = *reinterpret_cast<const v4u*>(xr + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double f = bf16_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          ss += f * f;
+        }
+      }
+    } else {
+      for (int64_t j = lane; j < cols; j += 64) {
+        const double f = bf16_to_f32(xr[j]);
+        ss += f * f;
+      }
+    }
+    ss = wave_sum_f64(ss);
+    const float ms = (float)(ss / (double)cols);
+    const float r = 1.0f / sqrtf(ms + eps);  // correctly rounded square root and division
+    if (lane == 0) rstd[row] = r;
+    if (in_regs) {
+#pragma unroll
+      for (int k = 0; k < kRmsRegChunks; ++k) {
+        const int64_t c = lane + 64 * k;
+        if (c < nch) m = norm_max8(buf[k], r, load_g8(g, 8 * c, g_vec), g != nullptr, m);
+      }
+    } else if (vec) {
+      for (int64_t c = lane; c < nch; c += 64)
+        m = norm_max8(*reinterpret_cast<const v4u*>(xr + 8 * c), r, load_g8(g, 8 * c, g_vec), g != nullptr, m);
+    } else {
+      for (int64_t j = lane; j < cols; j += 64) {
+        float y = bf16_to_f32(xr[j]) * r;
+        if (g) y = y * bf16_to_f32(g[j]);
+        const uint32_t mag = f32_to_bf16_rne(y) & 0x7FFFu;
+        m = m > mag ? m : mag;
+      }
+    }
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) jb.partials[blockIdx.x] = m;
 }
 
 template <int FMT, int MODE>
@@ -320,6 +464,18 @@ hipError_t launch_amax_partials(QuantBatch& b, hipStream_t st) {
   return hipGetLastError();
 }
 
+int rmsnorm_parts_for(int64_t rows) {
+  const int64_t p = (rows + kRmsRows - 1) / kRmsRows;
+  return (int)(p < 1 ? 1 : p);
+}
+
+hipError_t launch_rmsnorm_amax(QuantJob& j, float eps, float* rstd, hipStream_t st) {
+  j.blk_begin = 0;
+  j.nblocks = rmsnorm_parts_for(j.rows);
+  hipLaunchKernelGGL(rmsnorm_amax_kernel, dim3(j.nblocks), dim3(256), 0, st, j, eps, rstd);
+  return hipGetLastError();
+}
+
 hipError_t launch_cast(QuantBatch& b, hipStream_t st) {
   int total = 0;
   for (int i = 0; i < b.njobs; ++i) {
@@ -330,7 +486,12 @@ hipError_t launch_cast(QuantBatch& b, hipStream_t st) {
     total += b.job[i].nblocks;
   }
   const int fmt = b.job[0].fmt, mode = b.job[0].mode;
-  if (fmt == kE4M3 && mode == kModePlain)
+  if (mode == kModeRmsNorm) {
+    if (fmt == kE4M3)
+      hipLaunchKernelGGL((cast_kernel<kE4M3, kModeRmsNorm>), dim3(total), dim3(kCastThreads), 0, st, b);
+    else
+      hipLaunchKernelGGL((cast_kernel<kE5M2, kModeRmsNorm>), dim3(total), dim3(kCastThreads), 0, st, b);
+  } else if (fmt == kE4M3 && mode == kModePlain)
     hipLaunchKernelGGL((cast_kernel<kE4M3, kModePlain>), dim3(total), dim3(kCastThreads), 0, st, b);
   else if (fmt == kE4M3)
     hipLaunchKernelGGL((cast_kernel<kE4M3, kModeRelu2>), dim3(total), dim3(kCastThreads), 0, st, b);

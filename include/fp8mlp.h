@@ -97,6 +97,23 @@ int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, i
                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale,
                    float* amax, void* ws, size_t ws_bytes, void* stream);
 
+/* RMSNorm fused with the dynamic tensorwise quantisation of its output (the
+ * MLP input X is the RMSNorm of the residual stream; decomputer.nl, appendix:
+ * Llama-style RMSNorm, rms_norm_eps 1.0e-6).  Each step in a stated precision:
+ *   ms = RN32(RN64(sum_j x_j^2 / cols))  (sum in fp64)
+ *   r  = RN32(1 / RN32(sqrt(RN32(ms + eps))))          -> rstd[row]
+ *   X_j = RN_bf16(RN32(RN32(x_j r) gamma_j))           (gamma NULL: no weight)
+ * then q / qt / scale / amax exactly as fp8_amax_quant of X.  X itself is not
+ * stored: the statistics pass takes r and the amax, the cast pass recomputes
+ * X from x, r and gamma.
+ * x [rows, cols] bf16 (ldx); gamma [cols] bf16 or NULL; rstd out [rows] fp32;
+ * ws of fp8_rmsnorm_quant_workspace_bytes(rows, cols) bytes, 16-byte aligned.
+ * Empty tensors are valid (scale 1, amax 0). */
+size_t fp8_rmsnorm_quant_workspace_bytes(int64_t rows, int64_t cols);
+int fp8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t rows, int64_t cols,
+                      int64_t ldx, int fmt, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                      float* scale, float* amax, float* rstd, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* The three FP8 GEMMs of one linear layer.                                 */
 /*                                                                          */

@@ -160,3 +160,23 @@ def test_lm_head_ce_validation():
     offs = (ctypes.c_size_t * 14)()
     assert L.fp8_lm_head_ce_workspace_layout(256, 256, 600, 64, offs, 14) == 0
     assert list(offs) == sorted(offs) and offs[0] == 0
+
+
+def test_rmsnorm_quant_validation():
+    L = _native.lib()
+    n = L.fp8_rmsnorm_quant_workspace_bytes(64, 64)
+    assert n > 0 and L.fp8_rmsnorm_quant_workspace_bytes(-1, 64) == 0
+    f = ctypes.c_float
+    ok = [FAKE, None, f(1e-6), 64, 64, 64, 0, ctypes.c_void_p(0x20000), 64, None, 0, FAKE, None, FAKE, FAKE, n,
+          None]
+    assert L.fp8_rmsnorm_quant(*ok[:7], FAKE, *ok[8:]) == 1   # codes written over x
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return L.fp8_rmsnorm_quant(*a)
+    assert call(a13=None) == 1               # rstd missing
+    assert call(a2=f(-1.0)) == 1             # negative eps
+    assert call(a5=32) == 1                  # ldx < cols
+    assert call(a15=n - 1) == 3              # workspace too small
+    assert call(a1=FAKE_ODD) == 2            # gamma not 2-byte aligned

@@ -1,0 +1,56 @@
+"""GPU parity of fp8_rmsnorm_quant (RMSNorm fused with the tensorwise
+quantisation of its output) against the oracle's rmsnorm_quant: the per-row
+1/rms, the scale, the amax and every code are bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_tensorwise_scaled_amd import synth
+from tests.gpu_util import f32, to_dev_bf16, u8
+
+pytestmark = pytest.mark.gpu
+E4, E5 = oracle.E4M3, oracle.E5M2
+
+
+def run(x, g, eps, fmt, ld=None):
+    from fp8_tensorwise_scaled_amd import api
+
+    rows, cols = x.shape
+    if ld is None:
+        xd = to_dev_bf16(x)
+    else:
+        buf = np.zeros((rows, ld), np.uint16)
+        buf[:, :cols] = x
+        xd = to_dev_bf16(buf)[:, :cols]
+    gd = None if g is None else to_dev_bf16(g)
+    q, qt, s, a, r = api.fp8_rmsnorm_quant(xd, gd, eps, fmt, want_qt=True)
+    torch.cuda.synchronize()
+    return u8(q), u8(qt), float(f32(s)[0]), float(f32(a)[0]), f32(r)
+
+
+@pytest.mark.parametrize("shape,ld,with_g,fmt", [
+    ((8192, 3072), None, True, E4),     # the MLP input of the 3.8B-model block
+    ((8192, 3072), None, False, E4),
+    ((300, 700), 701, True, E4),        # ragged tiles, odd leading dimension
+    ((256, 512), None, True, E5),
+    ((17, 3072), None, True, E4),       # fewer rows than one statistics block
+])
+def test_bit_exact(shape, ld, with_g, fmt):
+    x = synth.normal_bf16(shape, 2.5, 91, outlier_frac=1e-3)
+    g = synth.normal_bf16((shape[1],), 1.0, 92) if with_g else None
+    q, qt, s, a, r = run(x, g, 1e-6, fmt, ld)
+    rq, rs, ra, _, rr = oracle.rmsnorm_quant(x, g, 1e-6, fmt)
+    assert (r.view(np.uint32) == rr.view(np.uint32)).all(), "1/rms differs"
+    assert np.float32(s) == np.float32(rs) and np.float32(a) == np.float32(ra), (s, rs, a, ra)
+    assert (q == rq).all() and (qt == rq.T).all()
+
+
+def test_zero_rows_and_empty():
+    x = synth.normal_bf16((64, 256), 1.0, 93)
+    x[5] = 0
+    q, qt, s, a, r = run(x, None, 1e-6, E4)
+    rq, rs, ra, _, rr = oracle.rmsnorm_quant(x, None, 1e-6, E4)
+    assert (r.view(np.uint32) == rr.view(np.uint32)).all() and (q == rq).all() and s == rs
+    q, qt, s, a, r = run(np.zeros((0, 256), np.uint16), None, 1e-6, E4)
+    assert s == 1.0 and a == 0.0 and r.size == 0
