@@ -84,6 +84,8 @@ def _load():
                 fn.argtypes = [vp, i64, c_int, f32, vp, i64, c_int, f32, i64, i64, i64, vp, i64, vp, i64]
             lib.orc_gemm_tn_acc.restype = None
             lib.orc_gemm_tn_acc.argtypes = [vp, i64, c_int, f32, vp, i64, c_int, f32, i64, i64, i64, vp, i64]
+            lib.orc_gemm_nn_acc.restype = None
+            lib.orc_gemm_nn_acc.argtypes = [vp, i64, c_int, f32, vp, i64, c_int, f32, i64, i64, i64, vp, i64, vp, i64]
             lib.orc_rmsnorm.restype = None
             lib.orc_rmsnorm.argtypes = [vp, i64, i64, i64, vp, f32, vp, vp]
             lib.orc_relu2.restype = None
@@ -217,6 +219,20 @@ def gemm_tn_acc(a, fa, sa, b, fb, sb, acc: np.ndarray) -> None:
     assert M == M2 and acc.shape == (N, K) and acc.dtype == np.float64 and acc.flags.c_contiguous
     _load().orc_gemm_tn_acc(_ptr(a), N, fa, np.float32(sa), _ptr(b), K, fb, np.float32(sb), M, N, K,
                             _ptr(acc), K)
+
+
+def gemm_nn_acc(a, fa, sa, b, fb, sb, acc: np.ndarray, rows=None) -> None:
+    """acc[i,k] += RN32(sa*sb) * sum_n dec(a[m,n]) dec(b[n,k]) (m = rows[i], or
+    every row) in fp64, unrounded."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    M, N = a.shape
+    N2, K = b.shape
+    assert N == N2 and acc.dtype == np.float64 and acc.flags.c_contiguous and acc.shape[1] == K
+    idx = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    assert acc.shape[0] == (M if idx is None else idx.size)
+    _load().orc_gemm_nn_acc(_ptr(a), N, fa, np.float32(sa), _ptr(b), K, fb, np.float32(sb), M, N, K, _ptr(acc), K,
+                            None if idx is None else _ptr(idx), 0 if idx is None else idx.size)
 
 
 # --------------------------------------------------------------- RMSNorm
@@ -403,3 +419,61 @@ def lm_head_ce(x, w, targets, n_classes: int, softcap: float = 15.0, chunk: int 
     loss = float(loss_rows.sum() / n_valid) if n_valid > 0 else 0.0
     return dict(loss=loss, loss_rows=loss_rows, dx=dx, dw=double_to_bf16(acc), dw_acc=acc, xq=xq, sx=sx,
                 wq=wq, sw=sw, n_valid=n_valid, chunks=chunks)
+
+
+# ------------------------------------------------ gated (SwiGLU) MLP block
+def silu(g: np.ndarray) -> np.ndarray:
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_gate(g_bits: np.ndarray, u_bits: np.ndarray) -> np.ndarray:
+    """A = RN_bf16(silu(G) U) from bf16 G and U (fp64 before the rounding)."""
+    g, u = bf16_bits_to_f64(g_bits), bf16_bits_to_f64(u_bits)
+    return double_to_bf16(silu(g) * u)
+
+
+def swiglu_gate_bwd(g_bits, u_bits, da_bits):
+    """dG = RN_bf16(dA U silu'(G)), dU = RN_bf16(dA silu(G)), with
+    silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g)))."""
+    g, u, da = bf16_bits_to_f64(g_bits), bf16_bits_to_f64(u_bits), bf16_bits_to_f64(da_bits)
+    sg = 1.0 / (1.0 + np.exp(-g))
+    return double_to_bf16(da * u * sg * (1.0 + g * (1.0 - sg))), double_to_bf16(da * g * sg)
+
+
+def swiglu_fwd(x, w_gate, w_up, w_down):
+    """Gated MLP Y = (silu(X Wg^T) * (X Wu^T)) Wd^T with FP8 GEMMs, the SwiGLU
+    form the pages replaced by relu^2 (decomputer.nl, "Doorvoer verhogen",
+    non-gated MLP bullet: three matmuls instead of two, intermediate ratio
+    2.75).  X [M,d], Wg/Wu [h,d], Wd [d,h] bf16 bits; E4M3 for X, W and A."""
+    xq, sx, _ = quant(x, E4M3)
+    wgq, swg, _ = quant(w_gate, E4M3)
+    wuq, swu, _ = quant(w_up, E4M3)
+    wdq, swd, _ = quant(w_down, E4M3)
+    g = gemm_nt(xq, E4M3, sx, wgq, E4M3, swg)
+    u = gemm_nt(xq, E4M3, sx, wuq, E4M3, swu)
+    a = swiglu_gate(g, u)
+    aq, sa, amax_a = quant(a, E4M3)
+    y = gemm_nt(aq, E4M3, sa, wdq, E4M3, swd)
+    return dict(xq=xq, sx=sx, wgq=wgq, swg=swg, wuq=wuq, swu=swu, wdq=wdq, swd=swd, g=g, u=u, a=a, aq=aq, sa=sa,
+                amax_a=amax_a, y=y)
+
+
+def swiglu_bwd(dy, saved):
+    """Backward of the gated block (gradients E5M2):
+      Gq = Q(dY);  dWd = gemm(Gq^T, Aq);  dA = gemm(Gq, Wdq)
+      dG, dU = swiglu_gate_bwd(G, U, dA);  dGq = Q(dG), dUq = Q(dU)
+      dWg = gemm(dGq^T, Xq);  dWu = gemm(dUq^T, Xq)
+      dX = RN_bf16(RN32(sdg swg) dGq.Wgq + RN32(sdu swu) dUq.Wuq)   (one rounding)"""
+    gq, sg, _ = quant(dy, E5M2)
+    dw_down = gemm_tn(gq, E5M2, sg, saved["aq"], E4M3, saved["sa"])
+    da = gemm_nn(gq, E5M2, sg, saved["wdq"], E4M3, saved["swd"])
+    dg, du = swiglu_gate_bwd(saved["g"], saved["u"], da)
+    dgq, sdg, _ = quant(dg, E5M2)
+    duq, sdu, _ = quant(du, E5M2)
+    dw_gate = gemm_tn(dgq, E5M2, sdg, saved["xq"], E4M3, saved["sx"])
+    dw_up = gemm_tn(duq, E5M2, sdu, saved["xq"], E4M3, saved["sx"])
+    acc = np.zeros((dy.shape[0], saved["xq"].shape[1]))
+    gemm_nn_acc(dgq, E5M2, sdg, saved["wgq"], E4M3, saved["swg"], acc)
+    gemm_nn_acc(duq, E5M2, sdu, saved["wuq"], E4M3, saved["swu"], acc)
+    return dict(gq=gq, sg=sg, dw_down=dw_down, da=da, dg=dg, du=du, dgq=dgq, sdg=sdg, duq=duq, sdu=sdu,
+                dw_gate=dw_gate, dw_up=dw_up, dx=double_to_bf16(acc), dx_acc=acc)

@@ -320,6 +320,36 @@ void orc_gemm_tn_acc(const uint8_t* a, int64_t lda, int fa, float sa,
   free(bd);
 }
 
+/* NN product added to an fp64 accumulator, without rounding:              */
+/*   acc[i,k] += RN32(sa*sb) * sum_n dec(a[m,n]) dec(b[n,k]),  m = rows[i]  */
+/* for a grad-input that is the sum of two products (the gated MLP's dX    */
+/* through the gate and the up projection) rounded once to bf16.  row_idx  */
+/* may be NULL (all M rows).                                               */
+void orc_gemm_nn_acc(const uint8_t* a, int64_t lda, int fa, float sa,
+                     const uint8_t* b, int64_t ldb, int fb, float sb,
+                     int64_t M, int64_t N, int64_t K, double* acc, int64_t ldacc,
+                     const int64_t* row_idx, int64_t n_rows) {
+  double* bd = (double*)malloc(sizeof(double) * (size_t)(N * K + 1));
+  double ta[256];
+  orc_decode_table(fa, ta);
+  decode_matrix(b, N, K, ldb, fb, bd);
+  double p = (double)scale_product(sa, sb);
+  int64_t R = row_idx ? n_rows : M;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < R; ++i) {
+    int64_t m = row_idx ? row_idx[i] : i;
+    double* s = (double*)calloc((size_t)K + 1, sizeof(double));
+    for (int64_t n = 0; n < N; ++n) {
+      double av = ta[a[m * lda + n]];
+      const double* brow = bd + n * K;
+      for (int64_t k = 0; k < K; ++k) s[k] += av * brow[k];
+    }
+    for (int64_t k = 0; k < K; ++k) acc[i * ldacc + k] += s[k] * p;
+    free(s);
+  }
+  free(bd);
+}
+
 /* ---------------------------------------------------------------------- */
 /* RMSNorm of bf16 rows (decomputer.nl, appendix: Llama-style RMSNorm,     */
 /* rms_norm_eps 1.0e-6), the step before the MLP's input quantisation:     */
