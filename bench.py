@@ -170,6 +170,53 @@ def bench_other(args) -> int:
                             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
                "unfused_torch_rmsnorm_then_quantise_ms": round(ms_unf, 5)}
         common["unit"] = "GB/s"
+    elif args.workload == "swiglu":
+        from fp8_tensorwise_scaled_amd import api
+
+        w = synth.SWIGLU_3P8B
+        M, d, h = w.M, w.d, w.h
+        log(f"generating SwiGLU inputs M={M} d={d} h={h}")
+        X, WG, WU, WD, DY = (t(a) for a in w.tensors())
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        Y, DX = torch.empty((M, d), **bf), torch.empty((M, d), **bf)
+        DWG, DWU, DWD = torch.empty((h, d), **bf), torch.empty((h, d), **bf), torch.empty((d, h), **bf)
+        BSC = torch.empty(3, dtype=torch.float32, device=dev)
+        saved = api.SwigluMlpSaved.empty(M, d, h, dev)
+        ws_f = api.swiglu_mlp_workspace("fwd", M, d, h, dev)
+        ws_b = api.swiglu_mlp_workspace("bwd", M, d, h, dev)
+
+        def step():
+            api.swiglu_mlp_fwd(X, WG, WU, WD, y=Y, saved=saved, ws=ws_f)
+            api.swiglu_mlp_bwd(DY, saved, dx=DX, dw_gate=DWG, dw_up=DWU, dw_down=DWD, bwd_scales=BSC, ws=ws_b)
+        ms = _time_steps(step, args.steps, args.warmup)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        log(f"SwiGLU block: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
+        del ws_f, ws_b, saved
+        # the relu^2 block the pages chose instead, same d, 4x intermediate
+        r = synth.MLP_3P8B
+        xr, wur, wdr, dyr = (t(a) for a in r.tensors())
+        rs = api.Relu2MlpSaved.empty(r.M, r.d, r.h, dev)
+        rf, rb = api.relu2_mlp_fwd_workspace(r.M, r.d, r.h, dev), api.relu2_mlp_bwd_workspace(r.M, r.d, r.h, dev)
+        Yr, DXr = torch.empty((r.M, r.d), **bf), torch.empty((r.M, r.d), **bf)
+        DWUr, DWDr = torch.empty((r.h, r.d), **bf), torch.empty((r.d, r.h), **bf)
+        BSr = torch.empty(2, dtype=torch.float32, device=dev)
+
+        def step_r():
+            api.relu2_mlp_fwd(xr, wur, wdr, y=Yr, saved=rs, ws=rf)
+            api.relu2_mlp_bwd(dyr, rs, dx=DXr, dw_up=DWUr, dw_down=DWDr, bwd_scales=BSr, ws=rb)
+        ms_r = _time_steps(step_r, args.steps, args.warmup)
+        log(f"relu2 block h={r.h}: {ms_r:.3f} ms/step, {r.flops / (ms_r * 1e-3) / 1e12:.1f} TFLOP/s")
+        res = {"metric": "FP8 SwiGLU MLP fwd+bwd TFLOP/s (d=3072, h=8448)",
+               "value": round(tflops, 2), "ms_per_step": round(ms, 4),
+               "data": "synthetic (seeded N(0,1) X, N(0,0.02) weights, N(0,1e-3) dY with 0.1% x100 outliers; "
+                       "bf16)",
+               "config": {"workload": f"SwiGLU MLP block fwd+bwd M={M} d={d} h={h}", "M": M, "d": d, "h": h,
+                          "gemm_flops": w.flops},
+               "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+               "tokens_per_s_equiv": round(M / (ms * 1e-3)),
+               "relu2_same_width": {"h": r.h, "ms_per_step": round(ms_r, 4),
+                                    "tokens_per_s_equiv": round(r.M / (ms_r * 1e-3)),
+                                    "value": round(r.flops / (ms_r * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}}
     elif args.workload == "lmce":
         from fp8_tensorwise_scaled_amd import api
 
@@ -234,11 +281,12 @@ def main() -> int:
     ap.add_argument("--gemm-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain device copies of 256 MiB (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead", "lmce", "rmsnorm"), default="mlp",
+    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead", "lmce", "rmsnorm", "swiglu"), default="mlp",
                     help="mlp: the relu2 block M=8192 (default); proj: the decoder projection set at "
                          "M=32768; lmhead: the LM head at vocabulary 50304 and 50257; lmce: the LM head "
                          "fused with the softcapped cross-entropy (chunks of 4096 rows); rmsnorm: RMSNorm fused "
-                         "with the quantisation of the block input X [8192, 3072]")
+                         "with the quantisation of the block input X [8192, 3072]; swiglu: the gated MLP block "
+                         "M=8192 d=3072 h=8448, beside the relu2 block at the same width")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "

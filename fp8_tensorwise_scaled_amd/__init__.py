@@ -1,4 +1,4 @@
-"""MI355X-native FP8 tensorwise-scaled linear layer and relu^2 MLP block.
+"""MI355X-native FP8 tensorwise-scaled linear layer, its MLP blocks and LM head.
 
 The compute runs in libfp8mlp.so (hand-written gfx950 HIP kernels behind a C
 ABI, include/fp8mlp.h).  This package holds the build script, the ctypes
@@ -10,7 +10,9 @@ from __future__ import annotations
 _API_NAMES = (
     "fp8_amax_quant", "fp8_linear_fwd", "fp8_linear_dgrad", "fp8_linear_wgrad",
     "relu2_mlp_fwd", "relu2_mlp_bwd", "Relu2MlpSaved", "relu2_mlp_fwd_workspace",
-    "relu2_mlp_bwd_workspace", "workspace_layout", "E4M3", "E5M2",
+    "relu2_mlp_bwd_workspace", "workspace_layout", "fp8_rmsnorm_quant", "fp8_lm_head_ce",
+    "fp8_lm_head_ce_workspace", "lm_head_ce_layout", "swiglu_mlp_fwd", "swiglu_mlp_bwd", "SwigluMlpSaved",
+    "swiglu_mlp_workspace", "swiglu_workspace_layout", "E4M3", "E5M2",
 )
 
 __all__ = list(_API_NAMES)

@@ -25,6 +25,11 @@ class Relu2MlpSaved(ctypes.Structure):
     _fields_ = [("xq_t", vp), ("uq_t", vp), ("dq_t", vp), ("aq_t", vp), ("h", vp), ("scales", vp)]
 
 
+class SwigluMlpSaved(ctypes.Structure):
+    _fields_ = [("xq_t", vp), ("wgq_t", vp), ("wuq_t", vp), ("wdq_t", vp), ("aq_t", vp), ("g", vp), ("u", vp),
+                ("scales", vp)]
+
+
 _PROTOS = {
     "fp8mlp_abi_version": (c_int, []),
     "fp8mlp_status_string": (ctypes.c_char_p, [c_int]),
@@ -42,6 +47,13 @@ _PROTOS = {
     "relu2_mlp_bwd_workspace_layout": (c_int, [i64, i64, i64, ctypes.POINTER(szt), c_int]),
     "relu2_mlp_fwd": (c_int, [vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(Relu2MlpSaved), vp, szt, vp]),
     "relu2_mlp_bwd": (c_int, [vp, ctypes.POINTER(Relu2MlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, szt, vp]),
+    "swiglu_mlp_fwd_workspace_bytes": (szt, [i64, i64, i64]),
+    "swiglu_mlp_bwd_workspace_bytes": (szt, [i64, i64, i64]),
+    "swiglu_mlp_fwd_workspace_layout": (c_int, [i64, i64, i64, ctypes.POINTER(szt), c_int]),
+    "swiglu_mlp_bwd_workspace_layout": (c_int, [i64, i64, i64, ctypes.POINTER(szt), c_int]),
+    "swiglu_mlp_fwd": (c_int, [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(SwigluMlpSaved), vp, szt, vp]),
+    "swiglu_mlp_bwd": (c_int, [vp, ctypes.POINTER(SwigluMlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, vp, szt,
+                               vp]),
     "fp8_lm_head_ce_workspace_bytes": (szt, [i64, i64, i64, i64]),
     "fp8_lm_head_ce_workspace_layout": (c_int, [i64, i64, i64, i64, ctypes.POINTER(szt), c_int]),
     "fp8_lm_head_ce": (c_int, [vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i64, vp, vp, vp, vp, vp, szt, vp]),

@@ -217,6 +217,95 @@ def relu2_mlp_bwd(dy, saved: Relu2MlpSaved, *, dx=None, dw_up=None, dw_down=None
     return dx, dw_up, dw_down, bwd_scales
 
 
+@dataclass
+class SwigluMlpSaved:
+    """Forward quantities the gated block's backward pass reads."""
+    xq_t: torch.Tensor
+    wgq_t: torch.Tensor
+    wuq_t: torch.Tensor
+    wdq_t: torch.Tensor
+    aq_t: torch.Tensor
+    g: torch.Tensor
+    u: torch.Tensor
+    scales: torch.Tensor  # sx, s_gate, s_up, s_down, sa
+    M: int
+    d: int
+    hid: int
+
+    @staticmethod
+    def empty(M: int, d: int, h: int, device) -> "SwigluMlpSaved":
+        u8 = dict(dtype=torch.uint8, device=device)
+        bf = dict(dtype=torch.bfloat16, device=device)
+        return SwigluMlpSaved(torch.empty((d, M), **u8), torch.empty((d, h), **u8), torch.empty((d, h), **u8),
+                              torch.empty((h, d), **u8), torch.empty((h, M), **u8), torch.empty((M, h), **bf),
+                              torch.empty((M, h), **bf), torch.empty(5, dtype=torch.float32, device=device),
+                              M, d, h)
+
+    def c_struct(self) -> _native.SwigluMlpSaved:
+        return _native.SwigluMlpSaved(*(t.data_ptr() for t in (self.xq_t, self.wgq_t, self.wuq_t, self.wdq_t,
+                                                               self.aq_t, self.g, self.u, self.scales)))
+
+
+def swiglu_mlp_workspace(kind: str, M: int, d: int, h: int, device) -> torch.Tensor:
+    n = getattr(_native.lib(), f"swiglu_mlp_{kind}_workspace_bytes")(M, d, h)
+    if n == 0:
+        raise ValueError(f"unsupported MLP shape M={M} d={d} h={h}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def swiglu_workspace_layout(kind: str, M: int, d: int, h: int):
+    n = 11 if kind == "fwd" else 14
+    offs = (ctypes.c_size_t * n)()
+    _native.call(f"swiglu_mlp_{kind}_workspace_layout", M, d, h, offs, n)
+    return list(offs)
+
+
+def swiglu_mlp_fwd(x, w_gate, w_up, w_down, *, y=None, saved: SwigluMlpSaved | None = None, ws=None):
+    """Y = (silu(X W_gate^T) * X W_up^T) W_down^T with FP8 GEMMs.  Returns (y, saved)."""
+    _check_dev(x, w_gate, w_up, w_down)
+    M, d = x.shape
+    h = w_gate.shape[0]
+    if w_gate.shape != (h, d) or w_up.shape != (h, d) or w_down.shape != (d, h):
+        raise ValueError("shapes: x [M,d], w_gate [h,d], w_up [h,d], w_down [d,h]")
+    for t in (x, w_gate, w_up, w_down):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("x, w_gate, w_up, w_down must be contiguous bfloat16")
+    if y is None:
+        y = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    if saved is None:
+        saved = SwigluMlpSaved.empty(M, d, h, x.device)
+    if ws is None:
+        ws = swiglu_mlp_workspace("fwd", M, d, h, x.device)
+    cs = saved.c_struct()
+    _native.call("swiglu_mlp_fwd", _p(x), _p(w_gate), _p(w_up), _p(w_down), M, d, h, _p(y), ctypes.byref(cs),
+                 _p(ws), ws.numel(), _stream())
+    return y, saved
+
+
+def swiglu_mlp_bwd(dy, saved: SwigluMlpSaved, *, dx=None, dw_gate=None, dw_up=None, dw_down=None,
+                   bwd_scales=None, ws=None):
+    """Backward of the gated block.  Returns (dx, dw_gate, dw_up, dw_down,
+    bwd_scales[s_dY, s_dG, s_dU])."""
+    _check_dev(dy)
+    M, d, h = saved.M, saved.d, saved.hid
+    dev = dy.device
+    if dy.shape != (M, d) or dy.dtype != torch.bfloat16 or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous bfloat16 [M, d] tensor")
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, d), **bf) if dx is None else dx
+    dw_gate = torch.empty((h, d), **bf) if dw_gate is None else dw_gate
+    dw_up = torch.empty((h, d), **bf) if dw_up is None else dw_up
+    dw_down = torch.empty((d, h), **bf) if dw_down is None else dw_down
+    if bwd_scales is None:
+        bwd_scales = torch.empty(3, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = swiglu_mlp_workspace("bwd", M, d, h, dev)
+    cs = saved.c_struct()
+    _native.call("swiglu_mlp_bwd", _p(dy), ctypes.byref(cs), M, d, h, _p(dx), _p(dw_gate), _p(dw_up),
+                 _p(dw_down), _p(bwd_scales), _p(ws), ws.numel(), _stream())
+    return dx, dw_gate, dw_up, dw_down, bwd_scales
+
+
 def fp8_lm_head_ce_workspace(M: int, K: int, V: int, chunk: int, device) -> torch.Tensor:
     n = _native.lib().fp8_lm_head_ce_workspace_bytes(M, K, V, chunk)
     if n == 0:

@@ -96,6 +96,40 @@ QuantJob make_job(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, in
   return j;
 }
 
+// ---- gated (SwiGLU) MLP workspaces
+enum SgFwdSlot { SF_XQ, SF_WGQ, SF_WUQ, SF_WDQ, SF_A, SF_AQ, SF_PX, SF_PWG, SF_PWU, SF_PWD, SF_PA, SF_COUNT };
+enum SgBwdSlot { SB_GQ, SB_GQT, SB_DA, SB_DG, SB_DU, SB_DGQ, SB_DGQT, SB_DUQ, SB_DUQT, SB_DXF, SB_PG, SB_PDG, SB_PDU,
+                 SB_SC, SB_COUNT };
+
+size_t layout_sg_fwd(int64_t M, int64_t d, int64_t h, size_t* off) {
+  const size_t sz[SF_COUNT] = {
+      (size_t)(M * d), (size_t)(h * d), (size_t)(h * d), (size_t)(d * h), (size_t)(M * h) * 2, (size_t)(M * h),
+      (size_t)amax_parts_for(M, d) * 4, (size_t)amax_parts_for(h, d) * 4, (size_t)amax_parts_for(h, d) * 4,
+      (size_t)amax_parts_for(d, h) * 4, (size_t)swiglu_parts_for(M * h) * 4};
+  size_t o = 0;
+  for (int i = 0; i < SF_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
+  return o;
+}
+
+size_t layout_sg_bwd(int64_t M, int64_t d, int64_t h, size_t* off) {
+  const size_t mh = (size_t)(M * h);
+  const size_t sz[SB_COUNT] = {
+      (size_t)(M * d), (size_t)(d * M), mh * 2, mh * 2, mh * 2, mh, mh, mh, mh, (size_t)(M * d) * 4,
+      (size_t)amax_parts_for(M, d) * 4, (size_t)swiglu_parts_for(M * h) * 4, (size_t)swiglu_parts_for(M * h) * 4,
+      16};
+  size_t o = 0;
+  for (int i = 0; i < SB_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
+  return o;
+}
+
+GemmArgs gemm_args(const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8_t* b, int64_t ldb, int fb,
+                   const float* sb, int64_t M, int64_t N, int64_t K, int epi) {
+  GemmArgs g{};
+  g.a = a; g.lda = lda; g.fa = fa; g.sa = sa; g.b = b; g.ldb = ldb; g.fb = fb; g.sb = sb;
+  g.M = M; g.N = N; g.K = K; g.epi = epi;
+  return g;
+}
+
 // ---- LM head + softcapped cross-entropy workspace
 enum LmSlot { L_XQ, L_XQT, L_WQ, L_WQT, L_Z, L_DZQ, L_DZQT, L_DWF, L_LOSS, L_PX, L_PW, L_PZ, L_NV, L_SC, L_COUNT };
 
@@ -473,6 +507,153 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
 
   // 3. dW to bf16 (zeros without tokens) and the mean loss
   return hip_status(launch_lm_ce_finalize(M > 0 ? dwf : nullptr, dw, V * K, loss_rows, M, nv, loss, s));
+}
+
+size_t swiglu_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h) {
+  if (check_mlp_dims(M, d, h)) return 0;
+  size_t off[SF_COUNT];
+  return layout_sg_fwd(M, d, h, off);
+}
+
+size_t swiglu_mlp_bwd_workspace_bytes(int64_t M, int64_t d, int64_t h) {
+  if (check_mlp_dims(M, d, h)) return 0;
+  size_t off[SB_COUNT];
+  return layout_sg_bwd(M, d, h, off);
+}
+
+int swiglu_mlp_fwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n) {
+  if (check_mlp_dims(M, d, h) || !offsets || n < SF_COUNT) return FP8MLP_EINVAL;
+  layout_sg_fwd(M, d, h, offsets);
+  return FP8MLP_OK;
+}
+
+int swiglu_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n) {
+  if (check_mlp_dims(M, d, h) || !offsets || n < SB_COUNT) return FP8MLP_EINVAL;
+  layout_sg_bwd(M, d, h, offsets);
+  return FP8MLP_OK;
+}
+
+int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                   int64_t M, int64_t d, int64_t h, uint16_t* y, const swiglu_mlp_saved* sv, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (!w_gate || !w_up || !w_down || !sv || !sv->wgq_t || !sv->wuq_t || !sv->wdq_t || !sv->scales)
+    return FP8MLP_EINVAL;
+  int st = check_mlp_dims(M, d, h);
+  if (st) return st;
+  if (M > 0 && (!x || !y || !sv->xq_t || !sv->aq_t || !sv->g || !sv->u)) return FP8MLP_EINVAL;
+  const void* ptrs[] = {x, w_gate, w_up, w_down, y, sv->xq_t, sv->wgq_t, sv->wuq_t, sv->wdq_t, sv->aq_t, sv->g, sv->u};
+  for (const void* p : ptrs)
+    if (!a16(p)) return FP8MLP_EALIGN;
+  if ((uintptr_t)sv->scales & 3u) return FP8MLP_EALIGN;
+  size_t off[SF_COUNT];
+  if (!ws || ws_bytes < layout_sg_fwd(M, d, h, off)) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+  uint8_t* w8 = (uint8_t*)ws;
+  uint8_t *xq = w8 + off[SF_XQ], *wgq = w8 + off[SF_WGQ], *wuq = w8 + off[SF_WUQ], *wdq = w8 + off[SF_WDQ];
+  uint16_t* a = (uint16_t*)(w8 + off[SF_A]);
+  uint8_t* aq = w8 + off[SF_AQ];
+  uint32_t* pa = (uint32_t*)(w8 + off[SF_PA]);
+  float* sc = sv->scales;
+  hipStream_t s = (hipStream_t)stream;
+
+  // 1. X, W_gate, W_up, W_down (E4M3), row-major and transposed, one amax and one cast launch
+  QuantBatch b{};
+  b.njobs = 4;
+  b.job[0] = make_job(x, M, d, d, FP8MLP_E4M3, xq, d, sv->xq_t, M, &sc[0], nullptr, (uint32_t*)(w8 + off[SF_PX]),
+                      amax_parts_for(M, d), kModePlain);
+  b.job[1] = make_job(w_gate, h, d, d, FP8MLP_E4M3, wgq, d, sv->wgq_t, h, &sc[1], nullptr,
+                      (uint32_t*)(w8 + off[SF_PWG]), amax_parts_for(h, d), kModePlain);
+  b.job[2] = make_job(w_up, h, d, d, FP8MLP_E4M3, wuq, d, sv->wuq_t, h, &sc[2], nullptr,
+                      (uint32_t*)(w8 + off[SF_PWU]), amax_parts_for(h, d), kModePlain);
+  b.job[3] = make_job(w_down, d, h, h, FP8MLP_E4M3, wdq, h, sv->wdq_t, d, &sc[3], nullptr,
+                      (uint32_t*)(w8 + off[SF_PWD]), amax_parts_for(d, h), kModePlain);
+  if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 2. G and U, 3. A = silu(G) U with its amax partials
+  GemmArgs gg = gemm_args(xq, d, FP8MLP_E4M3, &sc[0], wgq, d, FP8MLP_E4M3, &sc[1], M, h, d, kEpiStore);
+  gg.c = sv->g; gg.ldc = h;
+  GemmArgs gu = gemm_args(xq, d, FP8MLP_E4M3, &sc[0], wuq, d, FP8MLP_E4M3, &sc[2], M, h, d, kEpiStore);
+  gu.c = sv->u; gu.ldc = h;
+  if (launch_gemm(gg, s) != hipSuccess || launch_gemm(gu, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_swiglu_gate(sv->g, sv->u, a, M * h, pa, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 4. Aq and its transpose, 5. Y = Aq . Wdq^T
+  QuantBatch ba{};
+  ba.njobs = 1;
+  ba.job[0] = make_job(a, M, h, h, FP8MLP_E4M3, aq, h, sv->aq_t, M, &sc[4], nullptr, pa, swiglu_parts_for(M * h),
+                       kModePlain);
+  if (launch_cast(ba, s) != hipSuccess) return FP8MLP_EHIP;
+  GemmArgs gy = gemm_args(aq, h, FP8MLP_E4M3, &sc[4], wdq, h, FP8MLP_E4M3, &sc[3], M, d, h, kEpiStore);
+  gy.c = y; gy.ldc = d;
+  return hip_status(launch_gemm(gy, s));
+}
+
+int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, int64_t d, int64_t h, uint16_t* dx,
+                   uint16_t* dw_gate, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (!sv || !dw_gate || !dw_up || !dw_down || !sv->wgq_t || !sv->wuq_t || !sv->wdq_t || !sv->scales)
+    return FP8MLP_EINVAL;
+  int st = check_mlp_dims(M, d, h);
+  if (st) return st;
+  if (M > 0 && (!dy || !dx || !sv->xq_t || !sv->aq_t || !sv->g || !sv->u)) return FP8MLP_EINVAL;
+  const void* ptrs[] = {dy, dx, dw_gate, dw_up, dw_down, sv->xq_t, sv->wgq_t, sv->wuq_t, sv->wdq_t, sv->aq_t,
+                        sv->g, sv->u};
+  for (const void* p : ptrs)
+    if (!a16(p)) return FP8MLP_EALIGN;
+  if (((uintptr_t)sv->scales & 3u) || ((uintptr_t)bwd_scales & 3u)) return FP8MLP_EALIGN;
+  size_t off[SB_COUNT];
+  if (!ws || ws_bytes < layout_sg_bwd(M, d, h, off)) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+  uint8_t* w8 = (uint8_t*)ws;
+  uint8_t *gq = w8 + off[SB_GQ], *gqt = w8 + off[SB_GQT];
+  uint16_t* da = (uint16_t*)(w8 + off[SB_DA]);
+  uint16_t* dg = (uint16_t*)(w8 + off[SB_DG]);
+  uint16_t* du = (uint16_t*)(w8 + off[SB_DU]);
+  uint8_t *dgq = w8 + off[SB_DGQ], *dgqt = w8 + off[SB_DGQT], *duq = w8 + off[SB_DUQ], *duqt = w8 + off[SB_DUQT];
+  float* dxf = (float*)(w8 + off[SB_DXF]);
+  uint32_t *pdg = (uint32_t*)(w8 + off[SB_PDG]), *pdu = (uint32_t*)(w8 + off[SB_PDU]);
+  float* bsc = bwd_scales ? bwd_scales : (float*)(w8 + off[SB_SC]);
+  const float* sc = sv->scales;
+  hipStream_t s = (hipStream_t)stream;
+
+  // 1. Gq = quant(dY) (E5M2), row-major and transposed
+  QuantBatch b{};
+  b.njobs = 1;
+  b.job[0] = make_job(dy, M, d, d, FP8MLP_E5M2, gq, d, gqt, M, &bsc[0], nullptr, (uint32_t*)(w8 + off[SB_PG]),
+                      amax_parts_for(M, d), kModePlain);
+  if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 2. dW_down = Gq^T . Aq, 3. dA = Gq . Wd
+  GemmArgs gw = gemm_args(gqt, M, FP8MLP_E5M2, &bsc[0], sv->aq_t, M, FP8MLP_E4M3, &sc[4], d, h, M, kEpiStore);
+  gw.c = dw_down; gw.ldc = h;
+  GemmArgs ga = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->wdq_t, d, FP8MLP_E4M3, &sc[3], M, h, d, kEpiStore);
+  ga.c = da; ga.ldc = h;
+  if (launch_gemm(gw, s) != hipSuccess || launch_gemm(ga, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 4. dG, dU with their amax partials, 5. their E5M2 codes (one cast launch)
+  if (launch_swiglu_gate_bwd(sv->g, sv->u, da, dg, du, M * h, pdg, pdu, s) != hipSuccess) return FP8MLP_EHIP;
+  QuantBatch bg{};
+  bg.njobs = 2;
+  bg.job[0] = make_job(dg, M, h, h, FP8MLP_E5M2, dgq, h, dgqt, M, &bsc[1], nullptr, pdg, swiglu_parts_for(M * h),
+                       kModePlain);
+  bg.job[1] = make_job(du, M, h, h, FP8MLP_E5M2, duq, h, duqt, M, &bsc[2], nullptr, pdu, swiglu_parts_for(M * h),
+                       kModePlain);
+  if (launch_cast(bg, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 6. dW_gate = dGq^T . Xq, dW_up = dUq^T . Xq
+  GemmArgs gg = gemm_args(dgqt, M, FP8MLP_E5M2, &bsc[1], sv->xq_t, M, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
+  gg.c = dw_gate; gg.ldc = d;
+  GemmArgs gu = gemm_args(duqt, M, FP8MLP_E5M2, &bsc[2], sv->xq_t, M, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
+  gu.c = dw_up; gu.ldc = d;
+  if (launch_gemm(gg, s) != hipSuccess || launch_gemm(gu, s) != hipSuccess) return FP8MLP_EHIP;
+
+  // 7. dX = dGq . Wg + dUq . Wu, summed in fp32 and rounded once
+  GemmArgs x1 = gemm_args(dgq, h, FP8MLP_E5M2, &bsc[1], sv->wgq_t, h, FP8MLP_E4M3, &sc[1], M, d, h, kEpiStoreF32);
+  x1.cf = dxf; x1.ldc = d;
+  GemmArgs x2 = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->wuq_t, h, FP8MLP_E4M3, &sc[2], M, d, h, kEpiAccF32);
+  x2.cf = dxf; x2.ldc = d;
+  if (launch_gemm(x1, s) != hipSuccess || launch_gemm(x2, s) != hipSuccess) return FP8MLP_EHIP;
+  return hip_status(launch_f32_to_bf16(M > 0 ? dxf : nullptr, dx, M * d, s));
 }
 
 }  // extern "C"

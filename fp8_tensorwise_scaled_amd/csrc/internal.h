@@ -100,4 +100,14 @@ int64_t lm_ce_max_vocab();  // largest vocabulary the row kernel takes
 hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, const float* loss_rows, int64_t M,
                                  const int32_t* n_valid, float* loss, hipStream_t st);
 
+// Gated (SwiGLU) MLP elementwise kernels (swiglu.hip); n = elements, n % 8 == 0,
+// dense tensors; one partial (max |.| as bf16 bits) per block.
+int swiglu_parts_for(int64_t n);
+hipError_t launch_swiglu_gate(const uint16_t* g, const uint16_t* u, uint16_t* a, int64_t n, uint32_t* partials,
+                              hipStream_t st);
+hipError_t launch_swiglu_gate_bwd(const uint16_t* g, const uint16_t* u, const uint16_t* da, uint16_t* dg,
+                                  uint16_t* du, int64_t n, uint32_t* pg, uint32_t* pu, hipStream_t st);
+// dst = RN_bf16(src) over n elements (n % 8 == 0); src == nullptr writes zeros.
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st);
+
 }  // namespace fp8mlp

@@ -241,4 +241,9 @@ hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, cons
 
 int64_t lm_ce_max_vocab() { return kMaxVocab; }
 
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(grid_for(n / 8, 256)), dim3(256), 0, st, src, dst, n);
+  return hipGetLastError();
+}
+
 }  // namespace fp8mlp

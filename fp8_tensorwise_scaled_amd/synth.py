@@ -79,6 +79,36 @@ class MLPWorkload:
 
 
 @dataclass
+class SwigluWorkload:
+    """Gated (SwiGLU) MLP block: X [M,d], W_gate [h,d], W_up [h,d],
+    W_down [d,h], dY [M,d]."""
+    wid: int
+    M: int
+    d: int
+    h: int
+    sigma_x: float = 1.0
+    sigma_in: float = 0.02
+    sigma_down: float = 0.02
+    sigma_dy: float = 1e-3
+    dy_outliers: float = 1e-3
+    name: str = ""
+
+    def tensors(self):
+        s = 1000 * self.wid
+        x = normal_bf16((self.M, self.d), self.sigma_x, s + 1)
+        w_gate = normal_bf16((self.h, self.d), self.sigma_in, s + 2)
+        w_up = normal_bf16((self.h, self.d), self.sigma_in, s + 3)
+        w_down = normal_bf16((self.d, self.h), self.sigma_down, s + 4)
+        dy = normal_bf16((self.M, self.d), self.sigma_dy, s + 5, self.dy_outliers)
+        return x, w_gate, w_up, w_down, dy
+
+    @property
+    def flops(self) -> int:
+        """GEMM FLOPs of one fwd+bwd: nine GEMMs of 2*M*d*h each."""
+        return 18 * self.M * self.d * self.h
+
+
+@dataclass
 class LinearWorkload:
     """Single FP8 linear forward: X [M,K], W [N,K]."""
     wid: int
@@ -218,6 +248,10 @@ LINEAR_SMALL = LinearWorkload(1, 256, 1024, 512, name="fp8 linear fwd 256x1024x5
 MLP_SMALL = MLPWorkload(2, 2048, 768, 3072, sigma_up=1 / math.sqrt(768),
                         sigma_down=1 / math.sqrt(3072), name="relu2 MLP M=2048 d=768 h=3072")
 MLP_3P8B = MLPWorkload(3, 8192, 3072, 12288, name="relu2 MLP M=8192 d=3072 h=12288")
+# intermediate ratio 2.75 (h = 2.75 d), the gated form's ratio on the pages
+SWIGLU_SMALL = SwigluWorkload(7, 2048, 768, 2112, sigma_in=1 / math.sqrt(768), sigma_down=1 / math.sqrt(2112),
+                              name="SwiGLU MLP M=2048 d=768 h=2112")
+SWIGLU_3P8B = SwigluWorkload(8, 8192, 3072, 8448, name="SwiGLU MLP M=8192 d=3072 h=8448")
 PROJ_SET = ProjectionSetWorkload(4, 32768, name="decoder projection set M=32768")
 LM_HEAD_PADDED = LMHeadWorkload(5, 16384, 3072, 50304, name="LM head M=16384 K=3072 N=50304")
 LM_HEAD_UNPADDED = LMHeadWorkload(5, 16384, 3072, 50257, name="LM head M=16384 K=3072 N=50257")

@@ -198,6 +198,51 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
                   void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Gated (SwiGLU) MLP block through the same FP8 linears, the form the      */
+/* pages replaced by relu^2 (decomputer.nl, "Doorvoer verhogen", non-gated   */
+/* MLP bullet: three matmuls instead of two, intermediate ratio 2.75):       */
+/*   X [M,d], W_gate [h,d], W_up [h,d], W_down [d,h], Y [M,d], bf16, dense.  */
+/*   Forward (E4M3):  Xq, Wgq, Wuq, Wdq = quant(X, W_gate, W_up, W_down)     */
+/*     G = gemm(Xq, Wgq), U = gemm(Xq, Wuq)       bf16 [M,h], kept for bwd   */
+/*     A = RN_bf16(RN32(RN32(G sigmoid(G)) U))    (fp32 sigmoid)             */
+/*     Aq = quant(A);  Y = gemm(Aq, Wdq)                                     */
+/*   Backward (gradients E5M2):                                              */
+/*     Gq = quant(dY);  dW_down = gemm(Gq^T, Aq^T);  dA = gemm(Gq, Wdq^T)    */
+/*     dG = RN_bf16(dA U silu'(G)),  dU = RN_bf16(dA silu(G))  (fp32)         */
+/*     dGq, dUq = quant(dG), quant(dU)                                       */
+/*     dW_gate = gemm(dGq^T, Xq^T);  dW_up = gemm(dUq^T, Xq^T)               */
+/*     dX = RN_bf16(RN32(RN32(p_g dGq.Wgq) + RN32(p_u dUq.Wuq)))  (fp32 sum) */
+/* Requirements as for the relu^2 block (M, d, h multiples of 16, M == 0    */
+/* valid, 16-byte aligned pointers).                                        */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  uint8_t* xq_t;   /* [d, M] codes of X, transposed          */
+  uint8_t* wgq_t;  /* [d, h] codes of W_gate, transposed     */
+  uint8_t* wuq_t;  /* [d, h] codes of W_up, transposed       */
+  uint8_t* wdq_t;  /* [h, d] codes of W_down, transposed     */
+  uint8_t* aq_t;   /* [h, M] codes of A, transposed          */
+  uint16_t* g;     /* [M, h] bf16 gate pre-activation G      */
+  uint16_t* u;     /* [M, h] bf16 up projection U            */
+  float* scales;   /* 5 floats: sx, s_gate, s_up, s_down, sa */
+} swiglu_mlp_saved;
+
+size_t swiglu_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
+size_t swiglu_mlp_bwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
+/* Byte offsets of the workspace regions.  Forward (n >= 11): Xq, Wgq, Wuq,
+ * Wdq, A bf16, Aq, amax partials of X, W_gate, W_up, W_down, A.  Backward
+ * (n >= 14): Gq, Gq^T, dA, dG, dU, dGq, dGq^T, dUq, dUq^T, dX fp32, amax
+ * partials of dY, dG, dU, scales. */
+int swiglu_mlp_fwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
+int swiglu_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
+int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                   int64_t M, int64_t d, int64_t h, uint16_t* y, const swiglu_mlp_saved* saved, void* ws,
+                   size_t ws_bytes, void* stream);
+/* bwd_scales (may be NULL): 3 floats, s_dY, s_dG, s_dU. */
+int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* saved, int64_t M, int64_t d, int64_t h,
+                   uint16_t* dx, uint16_t* dw_gate, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* FP8 LM head fused with the softcapped cross-entropy, chunked over rows.  */
 /*                                                                          */
 /* decomputer.nl, "Doorvoer verhogen", fused linear cross-entropy bullet:   */

@@ -1,5 +1,5 @@
 """Writes block_scales.json: the oracle's tensor-wide scales of the relu^2 MLP
-block at the full workload sizes.
+block (and of the gated SwiGLU block) at the full workload sizes.
 
 Two of the block's scales depend on a maximum over a whole intermediate
 tensor (amax of A = relu(H)^2 and amax of dH), so checking sampled rows of
@@ -29,7 +29,8 @@ import oracle  # noqa: E402
 from fp8_tensorwise_scaled_amd import synth  # noqa: E402
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_scales.json")
-WORKLOADS = {"mlp_3p8b": lambda: synth.MLP_3P8B, "proj_set_mlp": lambda: synth.PROJ_SET.mlp()}
+WORKLOADS = {"mlp_3p8b": lambda: synth.MLP_3P8B, "proj_set_mlp": lambda: synth.PROJ_SET.mlp(),
+             "swiglu_3p8b": lambda: synth.SWIGLU_3P8B}
 
 
 def f32_hex(v: float) -> str:
@@ -61,13 +62,39 @@ def block_scales(w) -> dict:
                 **{k: {"f32": f32_hex(v), "value": float(v)} for k, v in vals.items()})
 
 
+def swiglu_scales(w) -> dict:
+    """Gated block: amax of A = silu(G) U, of dG and of dU need the complete
+    G, U (two GEMMs) and dA (one GEMM)."""
+    E4, E5 = oracle.E4M3, oracle.E5M2
+    x, wg, wu, wd, dy = w.tensors()
+    t0 = time.time()
+    xq, sx, _ = oracle.quant(x, E4)
+    gq_w, swg, _ = oracle.quant(wg, E4)
+    uq_w, swu, _ = oracle.quant(wu, E4)
+    dq, swd, _ = oracle.quant(wd, E4)
+    gq, sg, _ = oracle.quant(dy, E5)
+    g = oracle.gemm_nt(xq, E4, sx, gq_w, E4, swg)
+    u = oracle.gemm_nt(xq, E4, sx, uq_w, E4, swu)
+    _, sa, amax_a = oracle.quant(oracle.swiglu_gate(g, u), E4)
+    da = oracle.gemm_nn(gq, E5, sg, dq, E4, swd)
+    dg, du = oracle.swiglu_gate_bwd(g, u, da)
+    _, sdg, amax_dg = oracle.quant(dg, E5)
+    _, sdu, amax_du = oracle.quant(du, E5)
+    vals = dict(sx=sx, swg=swg, swu=swu, swd=swd, sg=sg, amax_a=amax_a, sa=sa, amax_dg=amax_dg, sdg=sdg,
+                amax_du=amax_du, sdu=sdu)
+    return dict(M=w.M, d=w.d, h=w.h, inputs_sha256=input_digest((x, wg, wu, wd, dy)),
+                seconds=round(time.time() - t0, 1),
+                **{k: {"f32": f32_hex(v), "value": float(v)} for k, v in vals.items()})
+
+
 def main(names):
     data = json.load(open(OUT)) if os.path.exists(OUT) else {}
-    data["_about"] = ("Oracle scales of the relu^2 MLP block at full size, written by "
+    data["_about"] = ("Oracle scales of the relu^2 and SwiGLU MLP blocks at full size, written by "
                       "make_block_scales.py (oracle only).  f32 = IEEE binary32 bits.")
     for n in names:
         print(f"{n}: computing", flush=True)
-        data[n] = block_scales(WORKLOADS[n]())
+        fn = swiglu_scales if n.startswith("swiglu") else block_scales
+        data[n] = fn(WORKLOADS[n]())
         print(f"{n}: {data[n]}", flush=True)
         with open(OUT, "w") as f:
             json.dump(data, f, indent=1, sort_keys=True)

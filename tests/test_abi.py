@@ -180,3 +180,46 @@ def test_rmsnorm_quant_validation():
     assert call(a5=32) == 1                  # ldx < cols
     assert call(a15=n - 1) == 3              # workspace too small
     assert call(a1=FAKE_ODD) == 2            # gamma not 2-byte aligned
+
+
+def test_swiglu_mlp_validation():
+    L = _native.lib()
+    M, d, h = 64, 64, 256
+    nf = L.swiglu_mlp_fwd_workspace_bytes(M, d, h)
+    nb = L.swiglu_mlp_bwd_workspace_bytes(M, d, h)
+    assert nf > M * d + 3 * h * d + M * h * 3 and nb > M * d * 6 + M * h * 10
+    assert L.swiglu_mlp_fwd_workspace_bytes(100, d, h) == 0            # M % 16
+    assert L.swiglu_mlp_bwd_workspace_bytes(0, d, h) > 0               # M = 0 is a valid shape
+    saved = _native.SwigluMlpSaved(*([0x10000] * 8))
+    ok = [FAKE, FAKE, FAKE, FAKE, M, d, h, FAKE, ctypes.byref(saved), FAKE, nf, None]
+    def fwd(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return L.swiglu_mlp_fwd(*a)
+    assert fwd(a10=nf - 1) == 3              # workspace too small
+    assert fwd(a4=65) == 5                   # M % 16
+    assert fwd(a6=-16) == 1                  # h < 0
+    assert fwd(a7=None) == 1                 # y missing with M > 0
+    assert fwd(a1=None) == 1                 # w_gate missing
+    assert fwd(a2=ctypes.c_void_p(0x10008)) == 2   # w_up not 16-byte aligned
+    for i in range(8):
+        f = [0x10000] * 8
+        f[i] = 0
+        bad = _native.SwigluMlpSaved(*f)
+        assert fwd(a8=ctypes.byref(bad)) == 1, i
+    okb = [FAKE, ctypes.byref(saved), M, d, h, FAKE, FAKE, FAKE, FAKE, None, FAKE, nb, None]
+    def bwd(**kw):
+        a = list(okb)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return L.swiglu_mlp_bwd(*a)
+    assert bwd(a11=nb - 1) == 3
+    assert bwd(a5=ctypes.c_void_p(0x10008)) == 2   # dx not 16-byte aligned
+    assert bwd(a9=ctypes.c_void_p(0x10002)) == 2   # bwd_scales not 4-byte aligned
+    assert bwd(a6=None) == 1                 # dw_gate missing
+    for kind, n in (("fwd", 11), ("bwd", 14)):
+        offs = (ctypes.c_size_t * n)()
+        assert getattr(L, f"swiglu_mlp_{kind}_workspace_layout")(M, d, h, offs, n) == 0
+        assert list(offs) == sorted(offs) and offs[0] == 0 and all(o % 256 == 0 for o in offs)
+        assert getattr(L, f"swiglu_mlp_{kind}_workspace_layout")(M, d, h, offs, n - 1) == 1

@@ -168,6 +168,38 @@ def test_full_size_sampled_rows(which):
     check_gemm(bf16_bits(y)[rows], *args, which, rows=rows)
 
 
+@pytest.mark.parametrize("which", ["gate_fwd", "down_fwd", "gate_wgrad"])
+def test_gated_width_sampled_rows(which):
+    """Shapes of the gated block at d=3072, h=8448 (33 tiles of 256, 44 of
+    192 along h): G = Xq Wgq^T (N = 8448), Y = Aq Wdq^T (K = 8448) and
+    dW_gate = dGq^T Xq (8448 output rows, K = 8192), on 48 sampled output
+    rows computed by the oracle."""
+    from fp8_tensorwise_scaled_amd import api
+
+    M, d, h = 8192, 3072, 8448
+    rng = np.random.default_rng(4)
+    if which == "gate_fwd":
+        qa, sa, qb, sb = quant_pair((M, d), (h, d), E4, E4, 511)
+        y = api.fp8_linear_fwd(to_dev_u8(qa), scal(sa), to_dev_u8(qb), scal(sb))
+        rows = rng.choice(M, 48, replace=False)
+        args = ("nt", qa, E4, sa, qb, E4, sb)
+    elif which == "down_fwd":
+        qa, sa, qb, sb = quant_pair((M, h), (d, h), E4, E4, 512)
+        y = api.fp8_linear_fwd(to_dev_u8(qa), scal(sa), to_dev_u8(qb), scal(sb))
+        rows = rng.choice(M, 48, replace=False)
+        args = ("nt", qa, E4, sa, qb, E4, sb)
+    else:
+        g = synth.normal_bf16((M, h), 1e-3, 513, outlier_frac=1e-3)
+        x = synth.normal_bf16((M, d), 1.0, 514)
+        gq, sa, _ = oracle.quant(g, E5)
+        xq, sb, _ = oracle.quant(x, E4)
+        y = api.fp8_linear_wgrad(to_dev_u8(gq.T), scal(sa), to_dev_u8(xq.T), scal(sb))
+        rows = rng.choice(h, 48, replace=False)
+        args = ("tn", gq, E5, sa, xq, E4, sb)
+    torch.cuda.synchronize()
+    check_gemm(bf16_bits(y)[rows], *args, which, rows=rows)
+
+
 def test_deterministic():
     from fp8_tensorwise_scaled_amd import api
 

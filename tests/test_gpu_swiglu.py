@@ -1,0 +1,112 @@
+"""GPU parity of the gated (SwiGLU) MLP block (swiglu_mlp_fwd / swiglu_mlp_bwd).
+
+Every expected value is the oracle chain run on the same seeded bf16 inputs
+(tests/swiglu_chain.py): each stage is bit-exact (codes, scales), within the
+GEMM bound (GEMM outputs) or within the gate's bound wherever its inputs
+equal the oracle's bit for bit, and within the chain bar everywhere."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_tensorwise_scaled_amd import synth
+from tests import swiglu_chain as sc_
+from tests.gpu_util import bf16_bits, bits_f64, to_dev_bf16, ulp_bf16
+from tests.mlp_chain import golden_scales
+
+pytestmark = pytest.mark.gpu
+
+
+def run_block(w):
+    from fp8_tensorwise_scaled_amd import api
+
+    x, wg, wu, wd, dy = w.tensors()
+    M, d, h = w.M, w.d, w.h
+    dev = torch.device("cuda:0")
+    ws_f = api.swiglu_mlp_workspace("fwd", M, d, h, dev)
+    ws_b = api.swiglu_mlp_workspace("bwd", M, d, h, dev)
+    y, saved = api.swiglu_mlp_fwd(to_dev_bf16(x), to_dev_bf16(wg), to_dev_bf16(wu), to_dev_bf16(wd), ws=ws_f)
+    dx, dwg, dwu, dwd, bsc = api.swiglu_mlp_bwd(to_dev_bf16(dy), saved, ws=ws_b)
+    torch.cuda.synchronize()
+    return sc_.collect((x, wg, wu, wd, dy), y, saved, ws_f, ws_b, dx, dwg, dwu, dwd, bsc)
+
+
+@pytest.fixture(scope="module")
+def small():
+    return run_block(synth.SWIGLU_SMALL)
+
+
+@pytest.fixture(scope="module")
+def small_chain(small):
+    g = small
+    return sc_.full_chain_scales(g["x"], g["wg"], g["wu"], g["wd"], g["dy"])
+
+
+def test_small_block_every_stage(small, small_chain):
+    """M=2048, d=768, h=2112: every stage on every token row and hidden
+    column against the oracle chain run on the same bf16 inputs."""
+    g = small
+    sc, _, _ = small_chain
+    rows, cols = np.arange(g["x"].shape[0]), np.arange(g["wg"].shape[0])
+    o = sc_.sampled_chain(g["x"], g["wg"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
+    sc_.compare(g, o, sc, rows, cols)
+
+
+def test_end_to_end(small, small_chain):
+    """Outputs against the full oracle chain: relative Frobenius <= 1e-2
+    (a one-ulp difference in G, U or dA may move an FP8 code by a step)."""
+    g = small
+    _, f, b = small_chain
+    for name, got, ref in (("Y", g["y"], f["y"]), ("dX", g["dx"], b["dx"]), ("dW_gate", g["dw_gate"], b["dw_gate"]),
+                           ("dW_up", g["dw_up"], b["dw_up"]), ("dW_down", g["dw_down"], b["dw_down"])):
+        gv, rv = bits_f64(got), bits_f64(ref)
+        fro = np.linalg.norm(gv - rv) / np.linalg.norm(rv)
+        frac = float((np.abs(gv - rv) <= ulp_bf16(rv)).mean())
+        print(f"end-to-end {name}: rel fro {fro:.3g}, within 1 ulp {frac:.5f}")
+        assert fro <= 1e-2, (name, fro, frac)
+
+
+def test_3p8b_width_sampled():
+    """M=8192, d=3072, h=8448 (the gated block at the model width, ratio
+    2.75): tensor-wide scales against the stored oracle values, every stage
+    on 32 sampled token rows and 32 sampled hidden columns."""
+    w = synth.SWIGLU_3P8B
+    g = run_block(w)
+    sc = golden_scales("swiglu_3p8b", (g["x"], g["wg"], g["wu"], g["wd"], g["dy"]))
+    rng = np.random.default_rng(12)
+    rows = np.sort(rng.choice(w.M, 32, replace=False))
+    cols = np.sort(rng.choice(w.h, 32, replace=False))
+    o = sc_.sampled_chain(g["x"], g["wg"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
+    sc_.compare(g, o, sc, rows, cols)
+
+
+def test_no_tokens():
+    """M = 0: empty Y and dX, activation and gradient scales 1, weight
+    gradients zero, weight codes and scales as the oracle's."""
+    from fp8_tensorwise_scaled_amd import api
+
+    w = synth.SwigluWorkload(43, 16, 64, 176)
+    x, wg, wu, wd, dy = w.tensors()
+    f = oracle.swiglu_fwd(x[:0], wg, wu, wd)
+    b = oracle.swiglu_bwd(dy[:0], f)
+    dev = torch.device("cuda:0")
+    y, saved = api.swiglu_mlp_fwd(to_dev_bf16(x[:0]), to_dev_bf16(wg), to_dev_bf16(wu), to_dev_bf16(wd))
+    fill = lambda r, c: torch.full((r, c), 7, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    dx, dwg, dwu, dwd, bsc = api.swiglu_mlp_bwd(to_dev_bf16(dy[:0]), saved, dw_gate=fill(176, 64),
+                                                dw_up=fill(176, 64), dw_down=fill(64, 176))
+    torch.cuda.synchronize()
+    assert [float(v) for v in saved.scales.cpu().numpy()] == [f["sx"], f["swg"], f["swu"], f["swd"], f["sa"]]
+    assert [float(v) for v in bsc.cpu().numpy()] == [b["sg"], b["sdg"], b["sdu"]] == [1.0, 1.0, 1.0]
+    for t, ref in ((saved.wgq_t, f["wgq"]), (saved.wuq_t, f["wuq"]), (saved.wdq_t, f["wdq"])):
+        assert (t.cpu().numpy() == ref.T).all()
+    for t, ref in ((dwg, b["dw_gate"]), (dwu, b["dw_up"]), (dwd, b["dw_down"])):
+        assert (bf16_bits(t) == ref).all() and (ref == 0).all()
+    assert tuple(y.shape) == (0, 64) and tuple(dx.shape) == (0, 64)
+
+
+def test_deterministic_and_reuse():
+    """Two passes give identical bytes (fixed summation order everywhere)."""
+    w = synth.SwigluWorkload(22, 512, 256, 704, sigma_in=1 / 16, sigma_down=1 / 32)
+    a, b = run_block(w), run_block(w)
+    for k in ("y", "dx", "dw_gate", "dw_up", "dw_down", "g", "u", "a", "dg", "du", "dgq", "duq"):
+        assert (a[k] == b[k]).all(), k
