@@ -18,6 +18,9 @@ Sources (the pages' statement of the method):
     intermediate size, bf16 model dtype.
   * "little-lm" summary on manulx.blog (Japanese page), FP8 paragraph: the
     scaled matmul is torch._scaled_mm with dynamic per-tensor scales.
+  * Same page, "Vroege experimenten" item 2 and the appendix: Muon for the
+    matrix parameters; its Newton-Schulz orthogonalisation is taken as
+    Muon's published quintic iteration (see ``newton_schulz``).
 Readings where the pages are silent (formats, scale formula, rounding,
 saturation, zero amax, operand layouts) are listed in the C file's header.
 """
@@ -477,3 +480,81 @@ def swiglu_bwd(dy, saved):
     gemm_nn_acc(duq, E5M2, sdu, saved["wuq"], E4M3, saved["swu"], acc)
     return dict(gq=gq, sg=sg, dw_down=dw_down, da=da, dg=dg, du=du, dgq=dgq, sdg=sdg, duq=duq, sdu=sdu,
                 dw_gate=dw_gate, dw_up=dw_up, dx=double_to_bf16(acc), dx_acc=acc)
+
+
+# ------------------------------------------- Muon: Newton-Schulz iteration
+# The pages train every matrix parameter with Muon (decomputer.nl, "Vroege
+# experimenten" item 2: Muon for the matrix parameters, AdamW for the rest;
+# its Newton-Schulz orthogonalisation costs about a quarter of a step;
+# appendix: matrix optimizer Muon, lr 0.02, momentum 0.95).  The pages do
+# not print the iteration; the plain reading is Muon's published quintic
+# Newton-Schulz iteration (K. Jordan et al., "Muon: An optimizer for hidden
+# layers in neural networks", 2024): normalise by the Frobenius norm, work
+# on the wide orientation (rows <= cols), and repeat five times
+#     A = X X^T,   B = b A + c A A,   X = a X + B X
+# with (a, b, c) = (3.4445, -4.7750, 2.0315), which maps every singular
+# value s of X to a s + b s^3 + c s^5 and so drives them towards 1 while
+# keeping the singular vectors.  Precision: every tensor of the iteration is
+# bf16 (the model dtype), formed with one rounding from the exact value;
+# matrix products are fp64 BLAS products of the bf16 values (rounding error
+# below 1e-12 of sum |products|, far under one bf16 ulp).
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+NS_EPS = 1e-7
+NS_STEPS = 5
+
+
+def ns_normalise(g_bits: np.ndarray, eps: float = NS_EPS):
+    """X0 = RN_bf16(RN32(g / RN32(n + eps))), n = RN32(sqrt(sum g^2)) with the
+    sum and the square root in fp64, the division in fp32 (IEEE).  Returns
+    (X0 bits, n, the fp32 divisor)."""
+    g = bf16_bits_to_f64(_c(g_bits, np.uint16))
+    n = np.float32(np.sqrt(np.sum(g * g)))
+    den = np.float32(n + np.float32(eps))
+    x = g.astype(np.float32) / den
+    return double_to_bf16(x.astype(np.float64)), float(n), float(den)
+
+
+def ns_poly(s, steps: int = NS_STEPS, coeffs=NS_COEFFS):
+    """The scalar map the iteration applies to every singular value."""
+    a, b, c = coeffs
+    s = np.asarray(s, dtype=np.float64)
+    for _ in range(steps):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+def newton_schulz(g_bits: np.ndarray, steps: int = NS_STEPS, coeffs=NS_COEFFS, eps: float = NS_EPS,
+                  exact: bool = False, trace: bool = False):
+    """Newton-Schulz orthogonalisation of a bf16 matrix G [rows, cols].
+
+    exact=False: the iteration in the method's precision (bf16 tensors, each
+    rounded once), returning bf16 bits of G's shape.  exact=True: the same
+    steps in fp64 without any rounding (X0 = G / (||G|| + eps) in fp64),
+    returning fp64 values.  trace=True also returns the list of per-step
+    (A, B, X) in the wide orientation."""
+    g_bits = _c(g_bits, np.uint16)
+    a, b, c = coeffs
+    if exact:
+        g = bf16_bits_to_f64(g_bits)
+        x = g / (np.sqrt(np.sum(g * g)) + eps)
+        rnd = lambda v: v
+    else:
+        x = bf16_bits_to_f64(ns_normalise(g_bits, eps)[0])
+        rnd = lambda v: bf16_bits_to_f64(double_to_bf16(v))
+    tall = g_bits.shape[0] > g_bits.shape[1]
+    if tall:
+        x = np.ascontiguousarray(x.T)
+    steps_out = []
+    for _ in range(steps):
+        A = rnd(x @ x.T)
+        B = rnd(b * A + c * (A @ A))
+        x = rnd(a * x + B @ x)
+        if trace:
+            steps_out.append((A, B, x))
+    if tall:
+        x = np.ascontiguousarray(x.T)
+    out = x if exact else double_to_bf16(x)
+    if exact:
+        return (out, steps_out) if trace else out
+    conv = lambda v: double_to_bf16(v)
+    return (out, [tuple(conv(t) for t in s) for s in steps_out]) if trace else out
