@@ -503,6 +503,19 @@ NS_EPS = 1e-7
 NS_STEPS = 5
 
 
+def bf16_gemm_nt(a_bits: np.ndarray, b_bits: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
+                 aux_bits: np.ndarray | None = None) -> np.ndarray:
+    """One product of the iteration: RN_bf16(alpha A B^T + beta aux) from
+    bf16 A [M,K], B [N,K] and aux [M,N], exact up to the fp64 product (one
+    rounding at the end).  alpha and beta are taken as given (fp64)."""
+    a = bf16_bits_to_f64(_c(a_bits, np.uint16))
+    b = bf16_bits_to_f64(_c(b_bits, np.uint16))
+    v = alpha * (a @ b.T)
+    if aux_bits is not None:
+        v = v + beta * bf16_bits_to_f64(_c(aux_bits, np.uint16))
+    return double_to_bf16(v)
+
+
 def ns_normalise(g_bits: np.ndarray, eps: float = NS_EPS):
     """X0 = RN_bf16(RN32(g / RN32(n + eps))), n = RN32(sqrt(sum g^2)) with the
     sum and the square root in fp64, the division in fp32 (IEEE).  Returns

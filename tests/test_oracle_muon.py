@@ -124,3 +124,26 @@ def test_budget_catches_planted_mistakes():
                 oracle.newton_schulz(g, coeffs=(a, c, b))):            # b and c swapped (diverges)
         v = f64(bad)
         assert not np.isfinite(v).all() or _rel(v, e) > BUDGET
+
+
+def test_bf16_product_closed_forms():
+    """Small integers are exact in bf16 and their products and sums exact in
+    fp64: the product is the integer matrix product, rounded once."""
+    rng = np.random.default_rng(14)
+    ai = rng.integers(-8, 9, (24, 40)).astype(np.float64)
+    bi = rng.integers(-8, 9, (16, 40)).astype(np.float64)
+    ci = rng.integers(-100, 101, (24, 16)).astype(np.float64)
+    a, b, c = (oracle.double_to_bf16(v) for v in (ai, bi, ci))
+    want = oracle.double_to_bf16(3.0 * (ai @ bi.T) - 2.0 * ci)
+    assert (oracle.bf16_gemm_nt(a, b, 3.0, -2.0, c) == want).all()
+    assert (oracle.bf16_gemm_nt(a, b) == oracle.double_to_bf16(ai @ bi.T)).all()
+    # the iteration's first step is these products on X0
+    g = synth.normal_bf16((32, 96), 1.0, 15)
+    x0 = oracle.ns_normalise(g)[0]
+    _, tr = oracle.newton_schulz(g, steps=1, trace=True)
+    A, B, X1 = tr[0]
+    a_, b_, c_ = oracle.NS_COEFFS
+    assert (A == oracle.bf16_gemm_nt(x0, x0)).all()
+    assert (B == oracle.bf16_gemm_nt(A, np.ascontiguousarray(A.T), c_, b_, A)).all()
+    xt = np.ascontiguousarray(x0.T)
+    assert (X1 == oracle.bf16_gemm_nt(B, xt, 1.0, a_, x0)).all()
