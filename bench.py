@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 
 
 def log(msg: str) -> None:
@@ -170,6 +171,35 @@ def bench_other(args) -> int:
                             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
                "unfused_torch_rmsnorm_then_quantise_ms": round(ms_unf, 5)}
         common["unit"] = "GB/s"
+    elif args.workload == "muon":
+        from fp8_tensorwise_scaled_amd import api
+
+        rows, cols, steps = 3072, 12288, 5
+        log(f"generating Newton-Schulz input [{rows}, {cols}]")
+        res_all = {}
+        for shape in ((rows, cols), (cols, rows)):
+            G = t(synth.normal_bf16(shape, 0.02, 4001, outlier_frac=1e-3))
+            out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+            norm = torch.empty(2, dtype=torch.float32, device=dev)
+            ws = api.muon_ns_workspace(*shape, dev)
+            ms = _time_steps(lambda: api.muon_newton_schulz(G, steps, out=out, norm=norm, ws=ws), args.steps,
+                             args.warmup)
+            res_all[shape] = ms
+            log(f"Newton-Schulz {shape[0]}x{shape[1]}, {steps} steps: {ms:.3f} ms")
+            del G, out, ws
+        m, n = rows, cols
+        flops = steps * (4 * m * m * n + 2 * m * m * m)
+        ms = res_all[(rows, cols)]
+        tflops = flops / (ms * 1e-3) / 1e12
+        res = {"metric": "Muon Newton-Schulz orthogonalisation (5 steps, bf16 matrix cores), TFLOP/s",
+               "value": round(tflops, 2), "ms_per_step": round(ms, 4),
+               "data": "synthetic (seeded N(0,0.02) gradient with 0.1% x100 outliers; bf16)",
+               "config": {"workload": f"Newton-Schulz 5 steps on a {rows}x{cols} matrix (grad of W_down; "
+                                      f"the transposed W_up shape beside it)", "rows": rows, "cols": cols,
+                          "steps": steps, "flops": flops},
+               "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+               "tall": {"rows": cols, "cols": rows, "ms": round(res_all[(cols, rows)], 4)}}
+        common["dtype"] = "bf16"
     elif args.workload == "swiglu":
         from fp8_tensorwise_scaled_amd import api
 
@@ -281,12 +311,14 @@ def main() -> int:
     ap.add_argument("--gemm-reps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain device copies of 256 MiB (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead", "lmce", "rmsnorm", "swiglu"), default="mlp",
+    ap.add_argument("--workload", choices=("mlp", "proj", "lmhead", "lmce", "rmsnorm", "swiglu", "muon"),
+                    default="mlp",
                     help="mlp: the relu2 block M=8192 (default); proj: the decoder projection set at "
                          "M=32768; lmhead: the LM head at vocabulary 50304 and 50257; lmce: the LM head "
                          "fused with the softcapped cross-entropy (chunks of 4096 rows); rmsnorm: RMSNorm fused "
                          "with the quantisation of the block input X [8192, 3072]; swiglu: the gated MLP block "
-                         "M=8192 d=3072 h=8448, beside the relu2 block at the same width")
+                         "M=8192 d=3072 h=8448, beside the relu2 block at the same width; muon: Muon's "
+                         "Newton-Schulz orthogonalisation of a 3072x12288 matrix (and its transpose)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "

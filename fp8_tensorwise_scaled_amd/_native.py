@@ -54,6 +54,10 @@ _PROTOS = {
     "swiglu_mlp_fwd": (c_int, [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(SwigluMlpSaved), vp, szt, vp]),
     "swiglu_mlp_bwd": (c_int, [vp, ctypes.POINTER(SwigluMlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, vp, szt,
                                vp]),
+    "bf16_gemm_nt": (c_int, [vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float, vp, i64, vp, i64, vp,
+                             i64, vp]),
+    "muon_ns_workspace_bytes": (szt, [i64, i64]),
+    "muon_newton_schulz": (c_int, [vp, i64, i64, c_int, vp, ctypes.c_float, vp, vp, vp, szt, vp]),
     "fp8_lm_head_ce_workspace_bytes": (szt, [i64, i64, i64, i64]),
     "fp8_lm_head_ce_workspace_layout": (c_int, [i64, i64, i64, i64, ctypes.POINTER(szt), c_int]),
     "fp8_lm_head_ce": (c_int, [vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i64, vp, vp, vp, vp, vp, szt, vp]),

@@ -306,6 +306,50 @@ def swiglu_mlp_bwd(dy, saved: SwigluMlpSaved, *, dx=None, dw_gate=None, dw_up=No
     return dx, dw_gate, dw_up, dw_down, bwd_scales
 
 
+def bf16_gemm_nt(a, b, alpha: float = 1.0, beta: float = 0.0, aux=None, *, out=None, out_t=None):
+    """out = RN_bf16(alpha a b^T + beta aux) on the bf16 matrix cores
+    (a [M,K], b [N,K], aux [M,N] or None); out_t, if given, receives out^T."""
+    _check_dev(a, b)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("shapes: a [M,K], b [N,K]")
+    for t in (a, b) + ((aux,) if aux is not None else ()):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
+            raise ValueError("a, b and aux must be bfloat16 with unit column stride")
+    if aux is not None and tuple(aux.shape) != (M, N):
+        raise ValueError("aux must be [M, N]")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if out is None else out
+    _native.call("bf16_gemm_nt", _p(a), _ld(a), _p(b), _ld(b), M, N, K, float(alpha), float(beta),
+                 None if aux is None else _p(aux), 0 if aux is None else _ld(aux), _p(out), _ld(out),
+                 None if out_t is None else _p(out_t), 0 if out_t is None else _ld(out_t), _stream())
+    return out
+
+
+def muon_ns_workspace(rows: int, cols: int, device) -> torch.Tensor:
+    n = _native.lib().muon_ns_workspace_bytes(rows, cols)
+    if n == 0:
+        raise ValueError(f"unsupported Newton-Schulz shape {rows}x{cols}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def muon_newton_schulz(g, steps: int = 5, coeffs=None, eps: float = 1e-7, *, out=None, norm=None, ws=None):
+    """Muon's Newton-Schulz orthogonalisation of a dense bf16 matrix.
+    Returns (out [rows, cols] bf16, norm [2] fp32: ||G||_F and the divisor)."""
+    _check_dev(g)
+    if g.dtype != torch.bfloat16 or g.dim() != 2 or not g.is_contiguous():
+        raise ValueError("g must be a contiguous 2-D bfloat16 tensor")
+    rows, cols = g.shape
+    dev = g.device
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if out is None else out
+    norm = torch.zeros(2, dtype=torch.float32, device=dev) if norm is None else norm
+    ws = muon_ns_workspace(rows, cols, dev) if ws is None else ws
+    c = None if coeffs is None else (ctypes.c_float * 3)(*coeffs)
+    _native.call("muon_newton_schulz", _p(g), rows, cols, int(steps), c, float(eps), _p(out), _p(norm), _p(ws),
+                 ws.numel(), _stream())
+    return out, norm
+
+
 def fp8_lm_head_ce_workspace(M: int, K: int, V: int, chunk: int, device) -> torch.Tensor:
     n = _native.lib().fp8_lm_head_ce_workspace_bytes(M, K, V, chunk)
     if n == 0:

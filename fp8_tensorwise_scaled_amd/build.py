@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8mlp.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["quant.hip", "gemm.hip", "lm_head_ce.hip", "swiglu.hip", "api.hip"]
+SOURCES = ["quant.hip", "gemm.hip", "lm_head_ce.hip", "swiglu.hip", "muon.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -656,4 +656,111 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   return hip_status(launch_f32_to_bf16(M > 0 ? dxf : nullptr, dx, M * d, s));
 }
 
+int bf16_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                 float alpha, float beta, const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc,
+                 uint16_t* ct, int64_t ldct, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8MLP_EINVAL;
+  if (M == 0 || N == 0) return FP8MLP_OK;
+  if (!c || ldc < N || (aux && ldaux < N) || (ct && ldct < M)) return FP8MLP_EINVAL;
+  if (!a2(c) || (aux && !a2(aux)) || (ct && !a2(ct))) return FP8MLP_EALIGN;
+  if (K > 0) {
+    if (!a || !b || lda < K || ldb < K) return FP8MLP_EINVAL;
+    if (K % 8 != 0) return FP8MLP_ENOTSUP;
+    if (!a16(a) || !a16(b) || lda % 8 || ldb % 8) return FP8MLP_EALIGN;
+    if (!tile_range_ok(2 * lda, 2 * K) || !tile_range_ok(2 * ldb, 2 * K)) return FP8MLP_ENOTSUP;
+  }
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return FP8MLP_ENOTSUP;
+  GemmArgs g{};
+  g.a = (const uint8_t*)a; g.b = (const uint8_t*)b; g.lda = K > 0 ? lda : 0; g.ldb = K > 0 ? ldb : 0;
+  g.fa = g.fb = kBF16; g.M = M; g.N = N; g.K = K; g.epi = kEpiAxpby;
+  g.alpha = alpha; g.beta = beta; g.aux = aux; g.ldaux = ldaux; g.c = c; g.ldc = ldc; g.ct = ct; g.ldct = ldct;
+  return hip_status(launch_gemm(g, (hipStream_t)stream));
+}
+
+namespace {
+// Newton-Schulz workspace: A, A^T, B [m, m]; T0, T1 [n, m]; norm partials.
+enum NsSlot { NS_A, NS_AT, NS_B, NS_T0, NS_T1, NS_P, NS_COUNT };
+int check_ns_dims(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return FP8MLP_EINVAL;
+  if (rows % 16 || cols % 16) return FP8MLP_ENOTSUP;
+  const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
+  if (m > 16384 || n > 1048576) return FP8MLP_ENOTSUP;
+  return FP8MLP_OK;
+}
+size_t layout_ns(int64_t rows, int64_t cols, size_t* off) {
+  const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
+  const size_t sz[NS_COUNT] = {(size_t)(m * m) * 2, (size_t)(m * m) * 2, (size_t)(m * m) * 2, (size_t)(n * m) * 2,
+                               (size_t)(n * m) * 2, (size_t)ns_parts_for(rows * cols) * 8};
+  size_t o = 0;
+  for (int i = 0; i < NS_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
+  return o;
+}
+}  // namespace
+
+size_t muon_ns_workspace_bytes(int64_t rows, int64_t cols) {
+  if (check_ns_dims(rows, cols)) return 0;
+  size_t off[NS_COUNT];
+  return layout_ns(rows, cols, off);
+}
+
+int muon_newton_schulz(const uint16_t* g, int64_t rows, int64_t cols, int steps, const float* coeffs, float eps,
+                       uint16_t* out, float* norm, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_ns_dims(rows, cols);
+  if (st) return st;
+  if (steps < 0 || steps > 100 || !(eps >= 0.0f)) return FP8MLP_EINVAL;
+  if (rows == 0 || cols == 0) return FP8MLP_OK;
+  if (!g || !out) return FP8MLP_EINVAL;
+  const size_t bytes = (size_t)(rows * cols) * 2;
+  if ((const uint8_t*)g < (const uint8_t*)out + bytes && (const uint8_t*)out < (const uint8_t*)g + bytes)
+    return FP8MLP_EINVAL;  // out overlaps g
+  if (!a16(g) || !a16(out) || ((uintptr_t)norm & 3u)) return FP8MLP_EALIGN;
+  size_t off[NS_COUNT];
+  if (!ws || ws_bytes < layout_ns(rows, cols, off)) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+  const float ca = coeffs ? coeffs[0] : 3.4445f, cb = coeffs ? coeffs[1] : -4.7750f, cc = coeffs ? coeffs[2] : 2.0315f;
+  uint8_t* w8 = (uint8_t*)ws;
+  uint16_t* A = (uint16_t*)(w8 + off[NS_A]);
+  uint16_t* At = (uint16_t*)(w8 + off[NS_AT]);
+  uint16_t* B = (uint16_t*)(w8 + off[NS_B]);
+  uint16_t* T0 = (uint16_t*)(w8 + off[NS_T0]);
+  uint16_t* T1 = (uint16_t*)(w8 + off[NS_T1]);
+  double* parts = (double*)(w8 + off[NS_P]);
+  hipStream_t s = (hipStream_t)stream;
+  const bool tall = rows > cols;
+  const int64_t m = tall ? cols : rows, n = tall ? rows : cols;
+  // X [m, n] is updated in place; X^T after k steps alternates between two
+  // buffers, arranged for a tall G so that the last one is `out`.
+  uint16_t* X = tall ? T1 : out;
+  auto xt_buf = [&](int k) -> uint16_t* {
+    if (tall) return (k % 2 == steps % 2) ? out : T0;
+    return (k % 2 == 0) ? T0 : T1;
+  };
+  // X0: normalised G in G's own layout, then the other orientation
+  if (tall) {
+    if (launch_ns_normalise(g, rows * cols, eps, parts, xt_buf(0), norm, s) != hipSuccess) return FP8MLP_EHIP;
+    if (launch_transpose_bf16(xt_buf(0), n, m, X, s) != hipSuccess) return FP8MLP_EHIP;
+  } else {
+    if (launch_ns_normalise(g, rows * cols, eps, parts, X, norm, s) != hipSuccess) return FP8MLP_EHIP;
+    if (steps > 0 && launch_transpose_bf16(X, m, n, xt_buf(0), s) != hipSuccess) return FP8MLP_EHIP;
+  }
+  for (int k = 0; k < steps; ++k) {
+    GemmArgs g1{};  // A = X X^T, and A^T
+    g1.a = g1.b = (const uint8_t*)X; g1.lda = g1.ldb = n; g1.fa = g1.fb = kBF16;
+    g1.M = m; g1.N = m; g1.K = n; g1.epi = kEpiAxpby; g1.alpha = 1.0f; g1.beta = 0.0f;
+    g1.c = A; g1.ldc = m; g1.ct = At; g1.ldct = m;
+    GemmArgs g2{};  // B = c A A + b A
+    g2.a = (const uint8_t*)A; g2.b = (const uint8_t*)At; g2.lda = g2.ldb = m; g2.fa = g2.fb = kBF16;
+    g2.M = m; g2.N = m; g2.K = m; g2.epi = kEpiAxpby; g2.alpha = cc; g2.beta = cb; g2.aux = A; g2.ldaux = m;
+    g2.c = B; g2.ldc = m;
+    GemmArgs g3{};  // X = B X + a X (in place), and X^T for the next step
+    g3.a = (const uint8_t*)B; g3.b = (const uint8_t*)xt_buf(k); g3.lda = g3.ldb = m; g3.fa = g3.fb = kBF16;
+    g3.M = m; g3.N = n; g3.K = m; g3.epi = kEpiAxpby; g3.alpha = 1.0f; g3.beta = ca; g3.aux = X; g3.ldaux = n;
+    g3.c = X; g3.ldc = n;
+    if (tall || k + 1 < steps) { g3.ct = xt_buf(k + 1); g3.ldct = m; }
+    if (launch_gemm(g1, s) != hipSuccess || launch_gemm(g2, s) != hipSuccess || launch_gemm(g3, s) != hipSuccess)
+      return FP8MLP_EHIP;
+  }
+  return FP8MLP_OK;
+}
+
 }  // extern "C"

@@ -17,6 +17,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v3u __attribute__((ext_vector_type(3)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

@@ -1,5 +1,10 @@
 // FP8 GEMM on the gfx950 matrix cores:  C = RN_bf16(RN32(sa*sb) * A . B^T)
-// with A [M,K] and B [N,K] both stored K-contiguous.
+// with A [M,K] and B [N,K] both stored K-contiguous.  The same kernel also
+// multiplies bf16 matrices (format kBF16): the data path moves bytes, so a
+// bf16 row is a byte row twice as long, and each 32-byte fragment feeds two
+// v_mfma_f32_32x32x16_bf16 instead of one FP8 instruction.  Both operands'
+// fragments hold the same K positions at the same lane and register
+// offsets, so every product pairs A[i][k] with B[j][k].
 //
 // All three GEMMs of an FP8 linear layer (decomputer.nl, "Doorvoer
 // verhogen", first bullet: one forward and two backward GEMMs in FP8) map to
@@ -90,11 +95,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   const int tn = (t % in_group) / gm;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  const int K = (int)g.K;
+  // operand bytes per element: K, lda and ldb below are in bytes
+  constexpr int ES = FA == kBF16 ? 2 : 1;
+  static_assert((FA == kBF16) == (FB == kBF16), "bf16 operands come in pairs");
+  const int K = (int)g.K * ES;
+  const int64_t lda = g.lda * ES, ldb = g.ldb * ES;
   const int rows_a = (int)min<int64_t>(BM, g.M - m0);
   const int rows_b = (int)min<int64_t>(BN, g.N - n0);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a + m0 * g.lda, (uint32_t)((rows_a - 1) * g.lda + K));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b + n0 * g.ldb, (uint32_t)((rows_b - 1) * g.ldb + K));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a + m0 * lda, (uint32_t)((rows_a - 1) * lda + K));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b + n0 * ldb, (uint32_t)((rows_b - 1) * ldb + K));
 
   // Per-thread 16-byte chunks loaded each stage: chunk id = tid + THREADS*j,
   // row = id / 8, logical column chunk = id % 8 (eight lanes cover one
@@ -107,8 +116,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   static_assert((kRowStep / 2) % 8 == 0, "swizzle must repeat every load step");
   const int row0 = tid >> 3, logical0 = tid & 7;
   const int colk0 = logical0 * 16;
-  const uint32_t goff_a = (uint32_t)(row0 * g.lda) + colk0, goff_b = (uint32_t)(row0 * g.ldb) + colk0;
-  const uint32_t gstep_a = (uint32_t)(kRowStep * g.lda), gstep_b = (uint32_t)(kRowStep * g.ldb);
+  const uint32_t goff_a = (uint32_t)(row0 * lda) + colk0, goff_b = (uint32_t)(row0 * ldb) + colk0;
+  const uint32_t gstep_a = (uint32_t)(kRowStep * lda), gstep_b = (uint32_t)(kRowStep * ldb);
   const uint32_t lds0 = row0 * kBK + ((logical0 ^ swz(row0)) << 4);
 
   v4u stg[G::LOADS];  // one stage in flight in registers
@@ -153,9 +162,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
     const int i = t / G::FN, j = t % G::FN;
     const v4i* a = f[i];
     const v4i* b = f[G::FM + j];
-    const v8i av = v8i{a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
-    const v8i bv = v8i{b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], FB, FA, 0, 0, 0, 0);
+    if constexpr (FA == kBF16) {
+      // two K=16 bf16 instructions, one per 16-byte half of the fragment
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, b[hh]),
+                                                            __builtin_bit_cast(v8bf, a[hh]), acc[i][j], 0, 0, 0);
+    } else {
+      const v8i av = v8i{a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
+      const v8i bv = v8i{b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], FB, FA, 0, 0, 0, 0);
+    }
   };
 
   // Software pipeline over 128-byte K stages, two LDS buffers, one stage in
@@ -223,6 +240,62 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   if (kt + 1 < nk) { iteration(kt, T{}, F{}); ++kt; }
   iteration(kt, F{}, F{});
   __syncthreads();
+
+  // ---- alpha/beta epilogue (bf16 operands): each lane combines its four
+  // consecutive columns of a row with the same elements of aux (when given)
+  // and writes them straight from the accumulators, so the sum is rounded
+  // once.  aux may be the output itself: every element is read and then
+  // written by the same lane.  With ct, the lane also writes its four values
+  // down a column of C^T (32 lanes cover 64 contiguous bytes of a C^T row).
+  if constexpr (EPI == kEpiAxpby) {
+    const bool has_aux = g.aux != nullptr;
+    const bool vec = ((reinterpret_cast<uintptr_t>(g.c) & 7u) == 0) && (g.ldc % 4 == 0) &&
+                     (!has_aux || (((reinterpret_cast<uintptr_t>(g.aux) & 7u) == 0) && (g.ldaux % 4 == 0)));
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i) {
+      const int64_t gr = m0 + wm * G::WM + i * 32 + frow;
+      if (gr >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t gc = n0 + wn * G::WN + j * 32 + q * 8 + fhalf * 4;
+          const v16f& a = acc[i][j];
+          const uint16_t* src = g.aux + gr * g.ldaux + gc;
+          uint16_t* dst = g.c + gr * g.ldc + gc;
+          uint32_t o[4];
+          if (vec && gc + 4 <= g.N) {
+            const v2u x = has_aux ? *reinterpret_cast<const v2u*>(src) : v2u{0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t xb = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+              const float r = has_aux ? __builtin_fmaf(g.alpha, a[4 * q + e], g.beta * bf16_to_f32(xb))
+                                      : g.alpha * a[4 * q + e];
+              o[e] = f32_to_bf16_rne(r);
+            }
+            *reinterpret_cast<v2u*>(dst) = v2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[e] = 0u;
+              if (gc + e < g.N) {
+                const float r = has_aux ? __builtin_fmaf(g.alpha, a[4 * q + e], g.beta * bf16_to_f32(src[e]))
+                                        : g.alpha * a[4 * q + e];
+                o[e] = f32_to_bf16_rne(r);
+                dst[e] = (uint16_t)o[e];
+              }
+            }
+          }
+          if (g.ct) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gc + e < g.N) g.ct[(gc + e) * g.ldct + gr] = (uint16_t)o[e];
+          }
+        }
+      }
+    }
+    return;
+  }
 
   // ---- fp32 epilogues: each lane writes its four consecutive columns of a
   // row straight from the accumulators (a 256-row fp32 tile would not fit in
@@ -294,7 +367,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   if constexpr (kEarlyH) load_h();
 
   // scale, round to bf16 and stage the tile in LDS
-  const float p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
+  float p;
+  if constexpr (FA == kBF16) p = g.alpha;
+  else p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
 #pragma unroll
   for (int i = 0; i < G::FM; ++i) {
     const int row = wm * G::WM + i * 32 + frow;
@@ -413,6 +488,12 @@ int pick_bn(int64_t M, int64_t N) {
 
 template <int FA, int FB, int BN, int WGM, int WGN>
 hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
+  if constexpr (FA == kBF16) {
+    // bf16 products: plain store (scaled by alpha) or the alpha/beta epilogue
+    if (g.epi == kEpiAxpby) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAxpby>(g, st);
+    if (g.epi == kEpiStore) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStore>(g, st);
+    return hipErrorInvalidValue;
+  } else {
   switch (g.epi) {
     case kEpiRelu2Max: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Max>(g, st);
     case kEpiRelu2Bwd: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Bwd>(g, st);
@@ -427,13 +508,17 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
       }
     default: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStore>(g, st);
   }
+  }
 }
 
 template <int FA, int FB>
 hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
   // 256x192 tiles run 8 waves (4x2, 64x96 wave tiles, two waves per SIMD);
-  // 256x256 tiles 4 waves (2x2, 128x128 wave tiles)
-  return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192, 4, 2>(g, st) : launch_bn<FA, FB, 256, 2, 2>(g, st);
+  // 256x256 tiles 4 waves (2x2, 128x128 wave tiles).  bf16 products always
+  // take the 8-wave tiles: the 4-wave alpha/beta epilogue would spill.
+  if constexpr (FA == kBF16) return launch_bn<FA, FB, 192, 4, 2>(g, st);
+  else
+    return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192, 4, 2>(g, st) : launch_bn<FA, FB, 256, 2, 2>(g, st);
 }
 
 }  // namespace
@@ -445,6 +530,10 @@ int64_t gemm_num_tiles(int64_t M, int64_t N) {
 int64_t gemm_max_tiles(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+  if (g.fa == kBF16 || g.fb == kBF16) {
+    if (g.fa != g.fb) return hipErrorInvalidValue;
+    return launch_fmt<kBF16, kBF16>(g, st);
+  }
   if (g.fa == kE4M3 && g.fb == kE4M3) return launch_fmt<kE4M3, kE4M3>(g, st);
   if (g.fa == kE5M2 && g.fb == kE4M3) return launch_fmt<kE5M2, kE4M3>(g, st);
   if (g.fa == kE4M3 && g.fb == kE5M2) return launch_fmt<kE4M3, kE5M2>(g, st);

@@ -52,6 +52,9 @@ hipError_t launch_rmsnorm_amax(QuantJob& j, float eps, float* rstd, hipStream_t 
 // cast kernel for every job of the batch.
 hipError_t launch_cast(QuantBatch& b, hipStream_t st);
 
+// GEMM operand format beside E4M3 (0) and E5M2 (1): bf16, for both operands.
+constexpr int kBF16 = 2;
+
 // GEMM epilogues.
 enum Epilogue : int {
   kEpiStore = 0,      // C = RN_bf16(p * acc)
@@ -60,11 +63,13 @@ enum Epilogue : int {
                       // partial[tile] = max |dH| (bf16 bits)
   kEpiStoreF32 = 3,   // Cf = RN32(p * acc)              (fp32 output, cf)
   kEpiAccF32 = 4,     // Cf = RN32(Cf + RN32(p * acc))   (fp32 accumulation, cf)
+  kEpiAxpby = 5,      // C = RN_bf16(fma(alpha, acc, RN32(beta * aux))), aux optional,
+                      // optionally also C^T into ct   (bf16 operands only)
 };
 
 struct GemmArgs {
-  const uint8_t* a;  // [M, K] codes, K contiguous
-  const uint8_t* b;  // [N, K] codes, K contiguous
+  const uint8_t* a;  // [M, K] codes (or bf16 values), K contiguous
+  const uint8_t* b;  // [N, K] codes (or bf16 values), K contiguous
   int64_t lda, ldb;
   int fa, fb;
   const float* sa;
@@ -77,6 +82,11 @@ struct GemmArgs {
   int64_t ldaux;
   uint32_t* partials;  // one per tile for the max epilogues
   float* cf;           // [M, N] fp32 (ldc) for the fp32 epilogues
+  // bf16 operands (fa == fb == kBF16): a, b hold bf16 values, lda, ldb and K
+  // count elements, and the output scale is alpha instead of sa * sb.
+  float alpha, beta;
+  uint16_t* ct;  // kEpiAxpby: optional transposed copy of C ([N, M], ldct)
+  int64_t ldct;
 };
 
 // Number of output tiles the GEMM will use (size of `partials`).
@@ -109,5 +119,14 @@ hipError_t launch_swiglu_gate_bwd(const uint16_t* g, const uint16_t* u, const ui
                                   uint16_t* du, int64_t n, uint32_t* pg, uint32_t* pu, hipStream_t st);
 // dst = RN_bf16(src) over n elements (n % 8 == 0); src == nullptr writes zeros.
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st);
+
+// Newton-Schulz orthogonalisation helpers (muon.hip).
+int ns_parts_for(int64_t n);
+// x = RN_bf16(g / RN32(RN32(||g||_F) + eps)) over n elements (n % 8 == 0);
+// partials: ns_parts_for(n) doubles; norm_out (may be NULL): n and the divisor.
+hipError_t launch_ns_normalise(const uint16_t* g, int64_t n, float eps, double* partials, uint16_t* x,
+                               float* norm_out, hipStream_t st);
+// dst [cols, rows] = src [rows, cols]^T, both dense; rows, cols % 8 == 0.
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, hipStream_t st);
 
 }  // namespace fp8mlp

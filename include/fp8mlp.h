@@ -294,6 +294,54 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
                    int64_t V, int64_t n_classes, float softcap, int64_t chunk, float* loss, uint16_t* dx,
                    uint16_t* dw, float* scales, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Muon's Newton-Schulz orthogonalisation of a bf16 matrix.                 */
+/*                                                                          */
+/* decomputer.nl, "Vroege experimenten" item 2 and the appendix: Muon for   */
+/* the matrix parameters (lr 0.02, momentum 0.95); its Newton-Schulz        */
+/* orthogonalisation costs about a quarter of a step.  The iteration is     */
+/* Muon's published quintic one, on the wide orientation (X = G, or G^T     */
+/* when rows > cols), each bf16 tensor formed with one rounding:            */
+/*   X0 = RN_bf16(RN32(G / RN32(n + eps))),  n = RN32(||G||_F)  (fp64 sum)  */
+/*   repeat `steps` times:                                                  */
+/*     A = RN_bf16(X X^T)                                                   */
+/*     B = RN_bf16(fma(c, A A, RN32(b A)))        (fp32 sum of the terms)    */
+/*     X = RN_bf16(fma(1, B X, RN32(a X)))                                  */
+/* with (a, b, c) = coeffs as fp32 numbers.  The products accumulate in     */
+/* fp32 on the bf16 matrix cores.                                           */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 GEMM on the same matrix-core kernel as the FP8 linears:
+ *   C[r, c] = RN_bf16(fma(alpha, sum_k A[r,k] B[c,k], RN32(beta aux[r, c])))
+ * (aux NULL: RN_bf16(alpha sum)), and with ct non-NULL also ct[c, r] = C[r, c].
+ * A [M,K] (lda), B [N,K] (ldb), aux / C [M,N] (ldaux / ldc), ct [N,M] (ldct),
+ * all bf16, row-major.  aux may equal C (each element is read before it is
+ * written, by the same thread); A, B and ct must not overlap C.
+ * Requirements: K % 8 == 0; a, b 16-byte aligned, lda and ldb multiples of 8;
+ * M, N >= 0 (ragged edges masked; K == 0 gives RN_bf16(RN32(beta aux))). */
+int bf16_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                 float alpha, float beta, const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc,
+                 uint16_t* ct, int64_t ldct, void* stream);
+
+/* Workspace for muon_newton_schulz (0 if the shape is not supported): A, A^T
+ * and B [m, m], two [n, m] buffers for X^T (one holds X for a tall G), and the
+ * norm's partial sums; m = min(rows, cols), n = max(rows, cols). */
+size_t muon_ns_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * g       [rows, cols] bf16, dense (row stride cols); not overwritten.
+ * steps   0..100 (5 in Muon); steps == 0 returns X0.
+ * coeffs  host pointer to {a, b, c}, or NULL for {3.4445, -4.7750, 2.0315}.
+ * eps     added to the norm (1e-7 in Muon).
+ * out     [rows, cols] bf16, dense; must not overlap g.
+ * norm    out (device, may be NULL): 2 floats, n and the divisor RN32(n + eps).
+ * Requirements: rows, cols multiples of 16 (0 valid: nothing to do);
+ *               m <= 16384, n <= 1048576; g, out 16-byte aligned;
+ *               ws of muon_ns_workspace_bytes(rows, cols) bytes, 16-byte aligned.
+ */
+int muon_newton_schulz(const uint16_t* g, int64_t rows, int64_t cols, int steps, const float* coeffs, float eps,
+                       uint16_t* out, float* norm, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

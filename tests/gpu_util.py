@@ -121,9 +121,9 @@ def oracle_gemm(kind: str, a, fa, sa, b, fb, sb, rows=None):
     return ref, sabs, K
 
 
-def check_gemm(got_bits, kind, a, fa, sa, b, fb, sb, what, rows=None):
+def check_gemm(got_bits, kind, a, fa, sa, b, fb, sb, what, rows=None, **floors):
     ref, sabs, K = oracle_gemm(kind, a, fa, sa, b, fb, sb, rows=rows)
-    return gemm_close(got_bits, ref, what, sabs_bits=sabs, K=K)
+    return gemm_close(got_bits, ref, what, sabs_bits=sabs, K=K, **floors)
 
 
 def collect_block(inputs, y, saved, ws_f, ws_b, dx, dwu, dwd, bsc) -> dict:

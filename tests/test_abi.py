@@ -223,3 +223,37 @@ def test_swiglu_mlp_validation():
         assert getattr(L, f"swiglu_mlp_{kind}_workspace_layout")(M, d, h, offs, n) == 0
         assert list(offs) == sorted(offs) and offs[0] == 0 and all(o % 256 == 0 for o in offs)
         assert getattr(L, f"swiglu_mlp_{kind}_workspace_layout")(M, d, h, offs, n - 1) == 1
+
+
+def test_bf16_gemm_and_newton_schulz_validation():
+    L = _native.lib()
+    f = ctypes.c_float
+    ok = [FAKE, 64, FAKE, 64, 32, 48, 64, f(1.0), f(0.0), None, 0, FAKE, 48, None, 0, None]
+    def g(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return L.bf16_gemm_nt(*a)
+    assert g(a6=60) == 5                     # K % 8
+    assert g(a1=32) == 1                     # lda < K
+    assert g(a0=ctypes.c_void_p(0x10008)) == 2
+    assert g(a12=40) == 1                    # ldc < N
+    assert g(a4=-1) == 1
+    assert g(a4=0) == 0                      # empty output: nothing to do
+    n = L.muon_ns_workspace_bytes(3072, 12288)
+    assert n >= 3 * 3072 * 3072 * 2 + 2 * 3072 * 12288 * 2
+    assert L.muon_ns_workspace_bytes(100, 64) == 0     # rows % 16
+    assert L.muon_ns_workspace_bytes(32768, 32768) == 0  # m beyond the limit
+    nb = L.muon_ns_workspace_bytes(64, 128)
+    okn = [FAKE, 64, 128, 5, None, f(1e-7), ctypes.c_void_p(0x20000), None, FAKE, nb, None]
+    def ns(**kw):
+        a = list(okn)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return L.muon_newton_schulz(*a)
+    assert ns(a9=nb - 1) == 3
+    assert ns(a3=-1) == 1 and ns(a3=101) == 1
+    assert ns(a5=f(-1.0)) == 1
+    assert ns(a6=FAKE) == 1                  # out overlaps g
+    assert ns(a6=ctypes.c_void_p(0x20008)) == 2
+    assert ns(a1=0) == 0                     # empty matrix
