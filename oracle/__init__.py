@@ -516,6 +516,13 @@ def bf16_gemm_nt(a_bits: np.ndarray, b_bits: np.ndarray, alpha: float = 1.0, bet
     return double_to_bf16(v)
 
 
+def _upper_mirrored(v: np.ndarray) -> np.ndarray:
+    """X X^T and A A (A symmetric) are symmetric by definition; a BLAS
+    product may still differ in the last fp64 bit between (i, j) and (j, i),
+    so both take the value computed for the upper triangle."""
+    return np.triu(v) + np.triu(v, 1).T
+
+
 def ns_normalise(g_bits: np.ndarray, eps: float = NS_EPS):
     """X0 = RN_bf16(RN32(g / RN32(n + eps))), n = RN32(sqrt(sum g^2)) with the
     sum and the square root in fp64, the division in fp32 (IEEE).  Returns
@@ -559,8 +566,8 @@ def newton_schulz(g_bits: np.ndarray, steps: int = NS_STEPS, coeffs=NS_COEFFS, e
         x = np.ascontiguousarray(x.T)
     steps_out = []
     for _ in range(steps):
-        A = rnd(x @ x.T)
-        B = rnd(b * A + c * (A @ A))
+        A = rnd(_upper_mirrored(x @ x.T))
+        B = rnd(b * A + c * _upper_mirrored(A @ A))
         x = rnd(a * x + B @ x)
         if trace:
             steps_out.append((A, B, x))

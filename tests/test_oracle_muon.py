@@ -147,3 +147,10 @@ def test_bf16_product_closed_forms():
     assert (B == oracle.bf16_gemm_nt(A, np.ascontiguousarray(A.T), c_, b_, A)).all()
     xt = np.ascontiguousarray(x0.T)
     assert (X1 == oracle.bf16_gemm_nt(B, xt, 1.0, a_, x0)).all()
+
+
+def test_gram_products_are_exactly_symmetric():
+    g = synth.normal_bf16((64, 200), 1.0, 16)
+    _, tr = oracle.newton_schulz(g, steps=2, trace=True)
+    for A, B, _ in tr:
+        assert (A == A.T).all() and (B == B.T).all()
