@@ -12,7 +12,7 @@ _API_NAMES = (
     "relu2_mlp_fwd", "relu2_mlp_bwd", "Relu2MlpSaved", "relu2_mlp_fwd_workspace",
     "relu2_mlp_bwd_workspace", "workspace_layout", "fp8_rmsnorm_quant", "fp8_lm_head_ce",
     "fp8_lm_head_ce_workspace", "lm_head_ce_layout", "swiglu_mlp_fwd", "swiglu_mlp_bwd", "SwigluMlpSaved",
-    "swiglu_mlp_workspace", "swiglu_workspace_layout", "bf16_gemm_nt", "muon_newton_schulz", "muon_ns_workspace",
+    "swiglu_mlp_workspace", "swiglu_workspace_layout", "bf16_gemm_nt", "bf16_gemm_sym", "muon_newton_schulz", "muon_ns_workspace",
     "E4M3", "E5M2",
 )
 

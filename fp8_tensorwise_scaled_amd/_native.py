@@ -56,6 +56,8 @@ _PROTOS = {
                                vp]),
     "bf16_gemm_nt": (c_int, [vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float, vp, i64, vp, i64, vp,
                              i64, vp]),
+    "bf16_gemm_sym_workspace_bytes": (szt, [i64, i64]),
+    "bf16_gemm_sym": (c_int, [vp, i64, i64, i64, ctypes.c_float, ctypes.c_float, vp, i64, vp, i64, vp, szt, vp]),
     "muon_ns_workspace_bytes": (szt, [i64, i64]),
     "muon_newton_schulz": (c_int, [vp, i64, i64, c_int, vp, ctypes.c_float, vp, vp, vp, szt, vp]),
     "fp8_lm_head_ce_workspace_bytes": (szt, [i64, i64, i64, i64]),

@@ -326,6 +326,28 @@ def bf16_gemm_nt(a, b, alpha: float = 1.0, beta: float = 0.0, aux=None, *, out=N
     return out
 
 
+def bf16_gemm_sym(a, alpha: float = 1.0, beta: float = 0.0, aux=None, *, out=None, ws=None):
+    """Symmetric out = RN_bf16(alpha a a^T + beta aux) (aux symmetric or None),
+    upper triangle multiplied and mirrored."""
+    _check_dev(a)
+    M, K = a.shape
+    for t in (a,) + ((aux,) if aux is not None else ()):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
+            raise ValueError("a and aux must be bfloat16 with unit column stride")
+    if aux is not None and tuple(aux.shape) != (M, M):
+        raise ValueError("aux must be [M, M]")
+    out = torch.empty((M, M), dtype=torch.bfloat16, device=a.device) if out is None else out
+    if ws is None:
+        n = _native.lib().bf16_gemm_sym_workspace_bytes(M, K)
+        if n == 0:
+            raise ValueError(f"unsupported symmetric product shape {M}x{K}")
+        ws = torch.empty(n, dtype=torch.uint8, device=a.device)
+    _native.call("bf16_gemm_sym", _p(a), _ld(a), M, K, float(alpha), float(beta),
+                 None if aux is None else _p(aux), 0 if aux is None else _ld(aux), _p(out), _ld(out), _p(ws),
+                 ws.numel(), _stream())
+    return out
+
+
 def muon_ns_workspace(rows: int, cols: int, device) -> torch.Tensor:
     n = _native.lib().muon_ns_workspace_bytes(rows, cols)
     if n == 0:

@@ -677,9 +677,31 @@ int bf16_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
   return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
 
+size_t bf16_gemm_sym_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0 || M % 16 || K % 8) return 0;
+  return align_up(sym_partials_bytes(M, K) + 16);
+}
+
+int bf16_gemm_sym(const uint16_t* a, int64_t lda, int64_t M, int64_t K, float alpha, float beta,
+                  const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc, void* ws, size_t ws_bytes,
+                  void* stream) {
+  if (M < 0 || K < 0) return FP8MLP_EINVAL;
+  if (M % 16 || K % 8) return FP8MLP_ENOTSUP;
+  if (M == 0) return FP8MLP_OK;
+  if (!c || ldc < M || (aux && ldaux < M) || (K > 0 && (!a || lda < K))) return FP8MLP_EINVAL;
+  if (!a16(c) || ldc % 8 || (aux && !a2(aux)) || (K > 0 && (!a16(a) || lda % 8))) return FP8MLP_EALIGN;
+  if (K > 0 && !tile_range_ok(2 * lda, 2 * K)) return FP8MLP_ENOTSUP;
+  if (M > INT32_MAX / 2) return FP8MLP_ENOTSUP;
+  if (!ws || ws_bytes < bf16_gemm_sym_workspace_bytes(M, K)) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+  return hip_status(launch_sym_gemm(a, K > 0 ? lda : 0, M, K, alpha, beta, aux, ldaux, c, ldc, (float*)ws,
+                                    (hipStream_t)stream));
+}
+
 namespace {
-// Newton-Schulz workspace: A, A^T, B [m, m]; T0, T1 [n, m]; norm partials.
-enum NsSlot { NS_A, NS_AT, NS_B, NS_T0, NS_T1, NS_P, NS_COUNT };
+// Newton-Schulz workspace: A, B [m, m]; T0, T1 [n, m]; the symmetric
+// products' fp32 partial sums; norm partials.
+enum NsSlot { NS_A, NS_B, NS_T0, NS_T1, NS_SP, NS_P, NS_COUNT };
 int check_ns_dims(int64_t rows, int64_t cols) {
   if (rows < 0 || cols < 0) return FP8MLP_EINVAL;
   if (rows % 16 || cols % 16) return FP8MLP_ENOTSUP;
@@ -689,8 +711,9 @@ int check_ns_dims(int64_t rows, int64_t cols) {
 }
 size_t layout_ns(int64_t rows, int64_t cols, size_t* off) {
   const int64_t m = rows < cols ? rows : cols, n = rows < cols ? cols : rows;
-  const size_t sz[NS_COUNT] = {(size_t)(m * m) * 2, (size_t)(m * m) * 2, (size_t)(m * m) * 2, (size_t)(n * m) * 2,
-                               (size_t)(n * m) * 2, (size_t)ns_parts_for(rows * cols) * 8};
+  const size_t sp1 = sym_partials_bytes(m, n), sp2 = sym_partials_bytes(m, m);
+  const size_t sz[NS_COUNT] = {(size_t)(m * m) * 2, (size_t)(m * m) * 2, (size_t)(n * m) * 2, (size_t)(n * m) * 2,
+                               sp1 > sp2 ? sp1 : sp2, (size_t)ns_parts_for(rows * cols) * 8};
   size_t o = 0;
   for (int i = 0; i < NS_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
   return o;
@@ -720,8 +743,8 @@ int muon_newton_schulz(const uint16_t* g, int64_t rows, int64_t cols, int steps,
   const float ca = coeffs ? coeffs[0] : 3.4445f, cb = coeffs ? coeffs[1] : -4.7750f, cc = coeffs ? coeffs[2] : 2.0315f;
   uint8_t* w8 = (uint8_t*)ws;
   uint16_t* A = (uint16_t*)(w8 + off[NS_A]);
-  uint16_t* At = (uint16_t*)(w8 + off[NS_AT]);
   uint16_t* B = (uint16_t*)(w8 + off[NS_B]);
+  float* sp = (float*)(w8 + off[NS_SP]);
   uint16_t* T0 = (uint16_t*)(w8 + off[NS_T0]);
   uint16_t* T1 = (uint16_t*)(w8 + off[NS_T1]);
   double* parts = (double*)(w8 + off[NS_P]);
@@ -744,21 +767,17 @@ int muon_newton_schulz(const uint16_t* g, int64_t rows, int64_t cols, int steps,
     if (steps > 0 && launch_transpose_bf16(X, m, n, xt_buf(0), s) != hipSuccess) return FP8MLP_EHIP;
   }
   for (int k = 0; k < steps; ++k) {
-    GemmArgs g1{};  // A = X X^T, and A^T
-    g1.a = g1.b = (const uint8_t*)X; g1.lda = g1.ldb = n; g1.fa = g1.fb = kBF16;
-    g1.M = m; g1.N = m; g1.K = n; g1.epi = kEpiAxpby; g1.alpha = 1.0f; g1.beta = 0.0f;
-    g1.c = A; g1.ldc = m; g1.ct = At; g1.ldct = m;
-    GemmArgs g2{};  // B = c A A + b A
-    g2.a = (const uint8_t*)A; g2.b = (const uint8_t*)At; g2.lda = g2.ldb = m; g2.fa = g2.fb = kBF16;
-    g2.M = m; g2.N = m; g2.K = m; g2.epi = kEpiAxpby; g2.alpha = cc; g2.beta = cb; g2.aux = A; g2.ldaux = m;
-    g2.c = B; g2.ldc = m;
+    // A = X X^T and B = c A A + b A: symmetric, upper triangle only (A is its
+    // own transpose, so A A = A A^T is an NT product of A with itself)
+    if (launch_sym_gemm(X, n, m, n, 1.0f, 0.0f, nullptr, 0, A, m, sp, s) != hipSuccess ||
+        launch_sym_gemm(A, m, m, m, cc, cb, A, m, B, m, sp, s) != hipSuccess)
+      return FP8MLP_EHIP;
     GemmArgs g3{};  // X = B X + a X (in place), and X^T for the next step
     g3.a = (const uint8_t*)B; g3.b = (const uint8_t*)xt_buf(k); g3.lda = g3.ldb = m; g3.fa = g3.fb = kBF16;
     g3.M = m; g3.N = n; g3.K = m; g3.epi = kEpiAxpby; g3.alpha = 1.0f; g3.beta = ca; g3.aux = X; g3.ldaux = n;
     g3.c = X; g3.ldc = n;
     if (tall || k + 1 < steps) { g3.ct = xt_buf(k + 1); g3.ldct = m; }
-    if (launch_gemm(g1, s) != hipSuccess || launch_gemm(g2, s) != hipSuccess || launch_gemm(g3, s) != hipSuccess)
-      return FP8MLP_EHIP;
+    if (launch_gemm(g3, s) != hipSuccess) return FP8MLP_EHIP;
   }
   return FP8MLP_OK;
 }

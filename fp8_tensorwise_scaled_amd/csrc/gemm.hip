@@ -84,26 +84,42 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   const int wm = wid % WGM, wn = wid / WGM;
 
   // ---- tile id: XCD-contiguous runs, grouped kGroupM tile-rows deep
-  const int nt = tiles_m * tiles_n;
+  const int nt = gridDim.x;  // tiles, or work items of the upper-triangle mode
   const int bid = blockIdx.x;
   const int xcd = bid & 7, idx = bid >> 3, per = nt >> 3, rem = nt & 7;
   const int t = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-  const int in_group = kGroupM * tiles_n;
-  const int first_m = (t / in_group) * kGroupM;
-  const int gm = min(kGroupM, tiles_m - first_m);
-  const int tm = first_m + (t % in_group) % gm;
-  const int tn = (t % in_group) / gm;
+  int tm, tn;
+  int64_t kbeg = 0, kelems = g.K;
+  float* cfp = g.cf;
+  if (g.tri_tiles > 0) {
+    // upper-triangle split-K work item: triangle tile t / ksplit in row-major
+    // order over (tm <= tn), K slice t % ksplit
+    const int ks = t % g.ksplit;
+    int tri = t / g.ksplit;
+    tm = 0;
+    while (tri >= g.tri_tiles - tm) { tri -= g.tri_tiles - tm; ++tm; }
+    tn = tm + tri;
+    kbeg = ks * g.kchunk;
+    kelems = min<int64_t>(g.kchunk, g.K - kbeg);
+    cfp = g.cf + ks * g.split_stride;
+  } else {
+    const int in_group = kGroupM * tiles_n;
+    const int first_m = (t / in_group) * kGroupM;
+    const int gm = min(kGroupM, tiles_m - first_m);
+    tm = first_m + (t % in_group) % gm;
+    tn = (t % in_group) / gm;
+  }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   // operand bytes per element: K, lda and ldb below are in bytes
   constexpr int ES = FA == kBF16 ? 2 : 1;
   static_assert((FA == kBF16) == (FB == kBF16), "bf16 operands come in pairs");
-  const int K = (int)g.K * ES;
+  const int K = (int)kelems * ES;
   const int64_t lda = g.lda * ES, ldb = g.ldb * ES;
   const int rows_a = (int)min<int64_t>(BM, g.M - m0);
   const int rows_b = (int)min<int64_t>(BN, g.N - n0);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a + m0 * lda, (uint32_t)((rows_a - 1) * lda + K));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b + n0 * ldb, (uint32_t)((rows_b - 1) * ldb + K));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a + m0 * lda + kbeg * ES, (uint32_t)((rows_a - 1) * lda + K));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b + n0 * ldb + kbeg * ES, (uint32_t)((rows_b - 1) * ldb + K));
 
   // Per-thread 16-byte chunks loaded each stage: chunk id = tid + THREADS*j,
   // row = id / 8, logical column chunk = id % 8 (eight lanes cover one
@@ -164,6 +180,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
     const v4i* b = f[G::FM + j];
     if constexpr (FA == kBF16) {
       // two K=16 bf16 instructions, one per 16-byte half of the fragment
+      // (issuing the halves as two passes over the tiles measured slower)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, b[hh]),
@@ -241,55 +258,103 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   iteration(kt, F{}, F{});
   __syncthreads();
 
-  // ---- alpha/beta epilogue (bf16 operands): each lane combines its four
-  // consecutive columns of a row with the same elements of aux (when given)
-  // and writes them straight from the accumulators, so the sum is rounded
-  // once.  aux may be the output itself: every element is read and then
-  // written by the same lane.  With ct, the lane also writes its four values
-  // down a column of C^T (32 lanes cover 64 contiguous bytes of a C^T row).
+  // ---- alpha/beta epilogue (bf16 operands).  Each lane combines its four
+  // consecutive columns of a row with the same elements of aux (when given),
+  // so the sum is rounded once, and stages the bf16 result in LDS; the tile
+  // then leaves as 16-byte row chunks and, with ct, as 16-byte chunks of
+  // C^T rows (eight consecutive rows of one column).  In LDS the 16-byte
+  // chunk c8 of tile row r sits at chunk c8 ^ ((r >> 3) & 7) of its row, so
+  // that the column gathers of eight row groups hit distinct banks.  aux may
+  // be the output itself: every aux element is read before the barrier that
+  // precedes the stores, and each tile is one block's alone.
   if constexpr (EPI == kEpiAxpby) {
     const bool has_aux = g.aux != nullptr;
-    const bool vec = ((reinterpret_cast<uintptr_t>(g.c) & 7u) == 0) && (g.ldc % 4 == 0) &&
-                     (!has_aux || (((reinterpret_cast<uintptr_t>(g.aux) & 7u) == 0) && (g.ldaux % 4 == 0)));
+    const bool vaux = !has_aux || (((reinterpret_cast<uintptr_t>(g.aux) & 7u) == 0) && (g.ldaux % 4 == 0));
+    auto lds_at = [&](int row, int col) {
+      return row * G::CLD + (((col >> 3) ^ ((row >> 3) & 7)) << 4) + (col & 7) * 2;
+    };
 #pragma unroll
     for (int i = 0; i < G::FM; ++i) {
-      const int64_t gr = m0 + wm * G::WM + i * 32 + frow;
-      if (gr >= g.M) continue;
+      const int row = wm * G::WM + i * 32 + frow;
+      const int64_t gr = m0 + row;
 #pragma unroll
       for (int j = 0; j < G::FN; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t gc = n0 + wn * G::WN + j * 32 + q * 8 + fhalf * 4;
+          const int col = wn * G::WN + j * 32 + q * 8 + fhalf * 4;
+          const int64_t gc = n0 + col;
           const v16f& a = acc[i][j];
-          const uint16_t* src = g.aux + gr * g.ldaux + gc;
-          uint16_t* dst = g.c + gr * g.ldc + gc;
-          uint32_t o[4];
-          if (vec && gc + 4 <= g.N) {
-            const v2u x = has_aux ? *reinterpret_cast<const v2u*>(src) : v2u{0u, 0u};
+          uint32_t o[4] = {0u, 0u, 0u, 0u};
+          if (gr < g.M) {
+            const uint16_t* src = g.aux + gr * g.ldaux + gc;
+            if (!has_aux) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t xb = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-              const float r = has_aux ? __builtin_fmaf(g.alpha, a[4 * q + e], g.beta * bf16_to_f32(xb))
-                                      : g.alpha * a[4 * q + e];
-              o[e] = f32_to_bf16_rne(r);
-            }
-            *reinterpret_cast<v2u*>(dst) = v2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
-          } else {
+              for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_rne(g.alpha * a[4 * q + e]);
+            } else if (vaux && gc + 4 <= g.N) {
+              const v2u x = *reinterpret_cast<const v2u*>(src);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              o[e] = 0u;
-              if (gc + e < g.N) {
-                const float r = has_aux ? __builtin_fmaf(g.alpha, a[4 * q + e], g.beta * bf16_to_f32(src[e]))
-                                        : g.alpha * a[4 * q + e];
-                o[e] = f32_to_bf16_rne(r);
-                dst[e] = (uint16_t)o[e];
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t xb = (x[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                o[e] = f32_to_bf16_rne(__builtin_fmaf(g.alpha, a[4 * q + e], g.beta * bf16_to_f32(xb)));
               }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (gc + e < g.N)
+                  o[e] = f32_to_bf16_rne(__builtin_fmaf(g.alpha, a[4 * q + e], g.beta * bf16_to_f32(src[e])));
             }
           }
-          if (g.ct) {
+          *reinterpret_cast<v2u*>(smem + lds_at(row, col)) = v2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+        }
+      }
+    }
+    __syncthreads();
+    // rows of C: 16-byte chunks
+    constexpr int kCpr = BN / 8, kNch = BM * kCpr / kThreads;
+    static_assert(kNch * kThreads == BM * kCpr, "whole row chunks");
+    const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gc + e < g.N) g.ct[(gc + e) * g.ldct + gr] = (uint16_t)o[e];
+    for (int it = 0; it < kNch; ++it) {
+      const int id = tid + kThreads * it;
+      const int row = id / kCpr, c8 = id % kCpr;
+      const int64_t gr = m0 + row, gc = n0 + c8 * 8;
+      if (gr < g.M && gc < g.N) {
+        const v4u v = *reinterpret_cast<const v4u*>(smem + lds_at(row, c8 * 8));
+        uint16_t* dst = g.c + gr * g.ldc + gc;
+        if (vec_c && gc + 8 <= g.N) {
+          *reinterpret_cast<v4u*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gc + e < g.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+    // rows of C^T: lanes take 8 consecutive columns x 8 consecutive row groups
+    if (g.ct) {
+      constexpr int kRg = BM / 8, kCo = BN / 8;  // row groups, column octets
+      constexpr int kNt = BN * kRg / kThreads;
+      static_assert(kNt * kThreads == BN * kRg && kRg % 8 == 0, "whole C^T chunks");
+      const bool vec_t = ((reinterpret_cast<uintptr_t>(g.ct) & 15u) == 0) && (g.ldct % 8 == 0);
+#pragma unroll
+      for (int it = 0; it < kNt; ++it) {
+        const int id = tid + kThreads * it;
+        const int blk = id >> 6;
+        const int col = (blk % kCo) * 8 + (id & 7);
+        const int rg = (blk / kCo) * 8 + ((id >> 3) & 7);
+        const int64_t gc = n0 + col, gr0 = m0 + rg * 8;
+        if (gc < g.N && gr0 < g.M) {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = *reinterpret_cast<const uint16_t*>(smem + lds_at(rg * 8 + e, col));
+          uint16_t* dst = g.ct + gc * g.ldct + gr0;
+          if (vec_t && gr0 + 8 <= g.M) {
+            *reinterpret_cast<v4u*>(dst) = v4u{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                               h[6] | (h[7] << 16)};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (gr0 + e < g.M) dst[e] = (uint16_t)h[e];
           }
         }
       }
@@ -301,8 +366,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   // row straight from the accumulators (a 256-row fp32 tile would not fit in
   // LDS); the fp32 output is read-modify-written in place to accumulate.
   if constexpr (EPI == kEpiStoreF32 || EPI == kEpiAccF32) {
-    const float p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
-    const bool vec = ((reinterpret_cast<uintptr_t>(g.cf) & 15u) == 0) && (g.ldc % 4 == 0);
+    float p;
+    if constexpr (FA == kBF16) p = g.alpha;
+    else p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
+    const bool vec = ((reinterpret_cast<uintptr_t>(cfp) & 15u) == 0) && (g.ldc % 4 == 0);
 #pragma unroll
     for (int i = 0; i < G::FM; ++i) {
       const int64_t gr = m0 + wm * G::WM + i * 32 + frow;
@@ -314,7 +381,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
           const int64_t gc = n0 + wn * G::WN + j * 32 + q * 8 + fhalf * 4;
           const v16f& a = acc[i][j];
           v4f v = {a[4 * q + 0] * p, a[4 * q + 1] * p, a[4 * q + 2] * p, a[4 * q + 3] * p};
-          float* dst = g.cf + gr * g.ldc + gc;
+          float* dst = cfp + gr * g.ldc + gc;
           if (vec && gc + 4 <= g.N) {
             if constexpr (EPI == kEpiAccF32) v += *reinterpret_cast<const v4f*>(dst);
             *reinterpret_cast<v4f*>(dst) = v;
@@ -469,8 +536,9 @@ template <int FA, int FB, int BM, int BN, int WGM, int WGN, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   if (tiles_m == 0 || tiles_n == 0) return hipSuccess;  // empty output
-  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, BM, BN, WGM, WGN, EPI>), dim3(tiles_m * tiles_n),
-                     dim3(64 * WGM * WGN), 0, st, g, tiles_m, tiles_n);
+  const int work = g.tri_tiles > 0 ? g.tri_tiles * (g.tri_tiles + 1) / 2 * g.ksplit : tiles_m * tiles_n;
+  hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, BM, BN, WGM, WGN, EPI>), dim3(work), dim3(64 * WGM * WGN), 0, st, g,
+                     tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -489,9 +557,12 @@ int pick_bn(int64_t M, int64_t N) {
 template <int FA, int FB, int BN, int WGM, int WGN>
 hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
   if constexpr (FA == kBF16) {
-    // bf16 products: plain store (scaled by alpha) or the alpha/beta epilogue
-    if (g.epi == kEpiAxpby) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAxpby>(g, st);
-    if (g.epi == kEpiStore) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStore>(g, st);
+    // bf16 products: the alpha/beta epilogue, or fp32 tiles of the
+    // upper-triangle split-K mode
+    if constexpr (BN == 192) {  // the 4-wave alpha/beta epilogue would spill
+      if (g.epi == kEpiAxpby) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAxpby>(g, st);
+    }
+    if (g.epi == kEpiStoreF32) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStoreF32>(g, st);
     return hipErrorInvalidValue;
   } else {
   switch (g.epi) {
@@ -516,8 +587,11 @@ hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
   // 256x192 tiles run 8 waves (4x2, 64x96 wave tiles, two waves per SIMD);
   // 256x256 tiles 4 waves (2x2, 128x128 wave tiles).  bf16 products always
   // take the 8-wave tiles: the 4-wave alpha/beta epilogue would spill.
-  if constexpr (FA == kBF16) return launch_bn<FA, FB, 192, 4, 2>(g, st);
-  else
+  if constexpr (FA == kBF16) {
+    // square 256x256 tiles for the upper-triangle mode (fp32 epilogue only)
+    if (g.tri_tiles > 0) return launch_bn<FA, FB, 256, 2, 2>(g, st);
+    return launch_bn<FA, FB, 192, 4, 2>(g, st);
+  } else
     return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192, 4, 2>(g, st) : launch_bn<FA, FB, 256, 2, 2>(g, st);
 }
 
@@ -528,6 +602,38 @@ int64_t gemm_num_tiles(int64_t M, int64_t N) {
   return ((M + 255) / 256) * ((N + bn - 1) / bn);
 }
 int64_t gemm_max_tiles(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
+
+// Work split of the symmetric product: enough K slices that the triangle's
+// tiles times the slices fill the 256 CUs about once, each slice at least
+// 512 elements long and a whole number of 64-element stages.
+int sym_ksplit(int64_t M, int64_t K) {
+  const int64_t T = (M + 255) / 256, ntri = T * (T + 1) / 2;
+  if (ntri == 0) return 1;  // empty product
+  int64_t s = 256 / ntri;
+  if (s > K / 512) s = K / 512;
+  if (s > 8) s = 8;
+  return (int)(s < 1 ? 1 : s);
+}
+
+static int64_t sym_kchunk(int64_t K, int s) { return ((K + s - 1) / s + 63) / 64 * 64; }
+
+size_t sym_partials_bytes(int64_t M, int64_t K) { return (size_t)sym_ksplit(M, K) * (size_t)(M * M) * 4; }
+
+hipError_t launch_sym_gemm(const uint16_t* a, int64_t lda, int64_t M, int64_t K, float alpha, float beta,
+                           const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc, float* partials,
+                           hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const int s = sym_ksplit(M, K);
+  const int64_t kc = sym_kchunk(K, s);
+  const int nsplit = kc > 0 ? (int)((K + kc - 1) / kc) : 1;  // slices actually used
+  GemmArgs g{};
+  g.a = g.b = (const uint8_t*)a; g.lda = g.ldb = lda; g.fa = g.fb = kBF16;
+  g.M = g.N = M; g.K = K; g.epi = kEpiStoreF32; g.alpha = 1.0f; g.cf = partials; g.ldc = M;
+  g.tri_tiles = (int)((M + 255) / 256); g.ksplit = nsplit < 1 ? 1 : nsplit; g.kchunk = kc; g.split_stride = M * M;
+  hipError_t e = launch_gemm(g, st);
+  if (e != hipSuccess) return e;
+  return launch_sym_reduce(partials, g.ksplit, M * M, M, alpha, beta, aux, ldaux, c, ldc, st);
+}
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.fa == kBF16 || g.fb == kBF16) {

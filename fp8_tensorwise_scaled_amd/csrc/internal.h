@@ -87,6 +87,13 @@ struct GemmArgs {
   float alpha, beta;
   uint16_t* ct;  // kEpiAxpby: optional transposed copy of C ([N, M], ldct)
   int64_t ldct;
+  // Upper-triangle split-K mode (M == N, A and B the same matrix's rows):
+  // tri_tiles > 0 is the number of 256-wide tile rows; work item w covers
+  // triangle tile w / ksplit (tile row <= tile column) and the K range
+  // [(w % ksplit) * kchunk, +kchunk); its fp32 result goes to
+  // cf + (w % ksplit) * split_stride with the kEpiStoreF32 epilogue.
+  int tri_tiles, ksplit;
+  int64_t kchunk, split_stride;
 };
 
 // Number of output tiles the GEMM will use (size of `partials`).
@@ -128,5 +135,17 @@ hipError_t launch_ns_normalise(const uint16_t* g, int64_t n, float eps, double* 
                                float* norm_out, hipStream_t st);
 // dst [cols, rows] = src [rows, cols]^T, both dense; rows, cols % 8 == 0.
 hipError_t launch_transpose_bf16(const uint16_t* src, int64_t rows, int64_t cols, uint16_t* dst, hipStream_t st);
+
+// Symmetric product C = RN_bf16(fma(alpha, A A^T, RN32(beta aux))) (aux
+// symmetric or NULL) through the upper-triangle split-K GEMM and a reduction
+// that writes both halves from the upper one (gemm.hip + muon.hip).
+int sym_ksplit(int64_t M, int64_t K);
+size_t sym_partials_bytes(int64_t M, int64_t K);
+hipError_t launch_sym_gemm(const uint16_t* a, int64_t lda, int64_t M, int64_t K, float alpha, float beta,
+                           const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc, float* partials,
+                           hipStream_t st);
+hipError_t launch_sym_reduce(const float* parts, int nsplit, int64_t split_stride, int64_t M, float alpha,
+                             float beta, const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc,
+                             hipStream_t st);
 
 }  // namespace fp8mlp

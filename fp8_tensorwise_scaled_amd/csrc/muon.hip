@@ -113,7 +113,96 @@ __global__ void __launch_bounds__(kNsThreads) transpose_bf16_kernel(const uint16
   }
 }
 
+// C = RN_bf16(fma(alpha, S, RN32(beta aux))) with S = ((p0 + p1) + ...) the
+// fp32 partial sums of the upper-triangle split-K product, over the 64 x 64
+// blocks (bi <= bj) of the symmetric M x M result: the block and its mirror
+// are written from the same values, and a diagonal block takes its lower half
+// from its upper half, so C is symmetric bit for bit.  M % 16 == 0.
+constexpr int kSym = 64;
+constexpr int kSymPitch = kSym + 2;
+__global__ void __launch_bounds__(kNsThreads) sym_reduce_kernel(const float* parts, int nsplit, int64_t sstride,
+                                                               int64_t M, float alpha, float beta,
+                                                               const uint16_t* aux, int64_t ldaux, uint16_t* c,
+                                                               int64_t ldc) {
+  __shared__ uint16_t tile[kSym * kSymPitch];
+  const int nb = (int)((M + kSym - 1) / kSym);
+  int w = blockIdx.x, bi = 0;
+  while (w >= nb - bi) { w -= nb - bi; ++bi; }
+  const int bj = bi + w;
+  const int64_t r0 = (int64_t)bi * kSym, c0 = (int64_t)bj * kSym;
+  // 64 rows x 16 groups of 4 columns; each thread takes 4 groups
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int id = threadIdx.x + kNsThreads * it;
+    const int r = id >> 4, q = id & 15;
+    const int64_t gr = r0 + r, gc = c0 + q * 4;
+    if (gr < M && gc < M) {
+      const int64_t off = gr * M + gc;
+      v4f sacc = *reinterpret_cast<const v4f*>(parts + off);
+      for (int k = 1; k < nsplit; ++k) sacc += *reinterpret_cast<const v4f*>(parts + k * sstride + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = aux ? __builtin_fmaf(alpha, sacc[e], beta * bf16_to_f32(aux[gr * ldaux + gc + e]))
+                            : alpha * sacc[e];
+        tile[r * kSymPitch + q * 4 + e] = (uint16_t)f32_to_bf16_rne(v);
+      }
+    }
+  }
+  __syncthreads();
+  if (bi == bj) {  // lower half of a diagonal block from its upper half
+    uint16_t tmp[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int id = threadIdx.x + kNsThreads * it, r = id >> 6, cc = id & 63;
+      tmp[it] = r > cc ? tile[cc * kSymPitch + r] : tile[r * kSymPitch + cc];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int id = threadIdx.x + kNsThreads * it, r = id >> 6, cc = id & 63;
+      tile[r * kSymPitch + cc] = tmp[it];
+    }
+    __syncthreads();
+  }
+  // the block, rows of 8 columns (16 bytes)
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int id = threadIdx.x + kNsThreads * it, r = id >> 3, ch = id & 7;
+    if (r0 + r < M && c0 + ch * 8 < M) {
+      v4u o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = (uint32_t)tile[r * kSymPitch + ch * 8 + 2 * e] | ((uint32_t)tile[r * kSymPitch + ch * 8 + 2 * e + 1] << 16);
+      *reinterpret_cast<v4u*>(c + (r0 + r) * ldc + c0 + ch * 8) = o;
+    }
+  }
+  if (bi == bj) return;
+  // the mirror block: row cc of it is column cc of the tile
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int id = threadIdx.x + kNsThreads * it, cc = id >> 3, ch = id & 7;
+    if (c0 + cc < M && r0 + ch * 8 < M) {
+      v4u o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = (uint32_t)tile[(ch * 8 + 2 * e) * kSymPitch + cc] |
+               ((uint32_t)tile[(ch * 8 + 2 * e + 1) * kSymPitch + cc] << 16);
+      *reinterpret_cast<v4u*>(c + (c0 + cc) * ldc + r0 + ch * 8) = o;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sym_reduce(const float* parts, int nsplit, int64_t split_stride, int64_t M, float alpha,
+                             float beta, const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc,
+                             hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const int64_t nb = (M + kSym - 1) / kSym;
+  hipLaunchKernelGGL(sym_reduce_kernel, dim3((unsigned)(nb * (nb + 1) / 2)), dim3(kNsThreads), 0, st, parts, nsplit,
+                     split_stride, M, alpha, beta, aux, ldaux, c, ldc);
+  return hipGetLastError();
+}
 
 int ns_parts_for(int64_t n) {
   const int64_t b = (n / 8 + kNsThreads * 8 - 1) / (kNsThreads * 8);  // ~8 chunks per thread

@@ -304,11 +304,12 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
 /* when rows > cols), each bf16 tensor formed with one rounding:            */
 /*   X0 = RN_bf16(RN32(G / RN32(n + eps))),  n = RN32(||G||_F)  (fp64 sum)  */
 /*   repeat `steps` times:                                                  */
-/*     A = RN_bf16(X X^T)                                                   */
+/*     A = RN_bf16(X X^T)                          (symmetric, see below)    */
 /*     B = RN_bf16(fma(c, A A, RN32(b A)))        (fp32 sum of the terms)    */
 /*     X = RN_bf16(fma(1, B X, RN32(a X)))                                  */
 /* with (a, b, c) = coeffs as fp32 numbers.  The products accumulate in     */
-/* fp32 on the bf16 matrix cores.                                           */
+/* fp32 on the bf16 matrix cores; A and B are computed on their upper       */
+/* triangle and mirrored (bf16_gemm_sym).                                   */
 /* ------------------------------------------------------------------------ */
 
 /* bf16 GEMM on the same matrix-core kernel as the FP8 linears:
@@ -323,9 +324,24 @@ int bf16_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
                  float alpha, float beta, const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc,
                  uint16_t* ct, int64_t ldct, void* stream);
 
-/* Workspace for muon_newton_schulz (0 if the shape is not supported): A, A^T
- * and B [m, m], two [n, m] buffers for X^T (one holds X for a tall G), and the
- * norm's partial sums; m = min(rows, cols), n = max(rows, cols). */
+/* Symmetric bf16 product C = RN_bf16(fma(alpha, A A^T, RN32(beta aux))) for
+ * A [M,K] (lda) and aux [M,M] symmetric or NULL.  Only the upper triangle of
+ * 256 x 256 tiles is multiplied, its K range split so that the tiles fill the
+ * chip; the fp32 partial sums are added in a fixed order and each element
+ * (i, j), i <= j, is written to both (i, j) and (j, i), so C is symmetric bit
+ * for bit (aux contributes its (i, j) element to both).
+ * Requirements: M % 16 == 0, K % 8 == 0; a, c 16-byte aligned, lda and ldc
+ * multiples of 8; ws of bf16_gemm_sym_workspace_bytes(M, K) bytes, 16-byte
+ * aligned; c must not overlap a, aux or ws. */
+size_t bf16_gemm_sym_workspace_bytes(int64_t M, int64_t K);
+int bf16_gemm_sym(const uint16_t* a, int64_t lda, int64_t M, int64_t K, float alpha, float beta,
+                  const uint16_t* aux, int64_t ldaux, uint16_t* c, int64_t ldc, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Workspace for muon_newton_schulz (0 if the shape is not supported): A and
+ * B [m, m], two [n, m] buffers for X^T (one holds X for a tall G), the
+ * symmetric products' partial sums and the norm's partial sums;
+ * m = min(rows, cols), n = max(rows, cols). */
 size_t muon_ns_workspace_bytes(int64_t rows, int64_t cols);
 
 /*

@@ -257,3 +257,26 @@ def test_bf16_gemm_and_newton_schulz_validation():
     assert ns(a6=FAKE) == 1                  # out overlaps g
     assert ns(a6=ctypes.c_void_p(0x20008)) == 2
     assert ns(a1=0) == 0                     # empty matrix
+
+
+def test_symmetric_product_validation():
+    L = _native.lib()
+    f = ctypes.c_float
+    n = L.bf16_gemm_sym_workspace_bytes(3072, 12288)
+    assert n >= 3072 * 3072 * 4 and L.bf16_gemm_sym_workspace_bytes(100, 64) == 0
+    nb = L.bf16_gemm_sym_workspace_bytes(64, 128)
+    ok = [FAKE, 128, 64, 128, f(1.0), f(0.0), None, 0, ctypes.c_void_p(0x20000), 64, FAKE, nb, None]
+    def sym(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return L.bf16_gemm_sym(*a)
+    assert sym(a11=nb - 1) == 3
+    assert sym(a2=60) == 5                   # M % 16
+    assert sym(a1=64) == 1                   # lda < K
+    assert sym(a9=32) == 1                   # ldc < M
+    assert sym(a8=ctypes.c_void_p(0x20008)) == 2
+    assert sym(a2=0) == 0
+    # empty shapes: valid, with a (small) workspace size
+    assert L.bf16_gemm_sym_workspace_bytes(0, 64) > 0 and L.bf16_gemm_sym_workspace_bytes(64, 0) > 0
+    assert L.muon_ns_workspace_bytes(0, 64) > 0 and L.muon_ns_workspace_bytes(64, 0) > 0
