@@ -30,15 +30,6 @@ constexpr int kCeThreads = 512;
 constexpr int64_t kMaxVocab = int64_t{1} << 22;  // columns per row (int offsets, tile ranges)
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
-
-// tanh(y) = (e - 1) / (e + 1) with e = exp(2y); |y| is clamped to 20, where
-// tanh is 1 to fp32 precision.
-__device__ __forceinline__ float tanh_fast(float y) {
-  const float yc = __builtin_fminf(__builtin_fmaxf(y, -20.0f), 20.0f);
-  const float e = exp_fast(2.0f * yc);
-  return (e - 1.0f) * __builtin_amdgcn_rcpf(e + 1.0f);
-}
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
@@ -73,6 +64,14 @@ __global__ void __launch_bounds__(256) count_valid_kernel(const int32_t* targets
   if (threadIdx.x == 0) *n_valid = red[0] + red[1] + red[2] + red[3];
 }
 
+// One block per row, two sweeps over it: the sum of exp(S - c), then dZ
+// written over the logits (the second sweep reads the row again, from L2,
+// and recomputes tanh: keeping tanh in registers between the sweeps measured
+// slower, its 150 registers per lane cost more occupancy than the work saved).
+// Each element costs two exp2 and one reciprocal per sweep, with constants
+// folded:
+//   th = tanh(z / c) = (e - 1) / (e + 1),  e = exp2(clamp(z * 2 log2(e) / c))
+//   exp(c th - m) = exp2(c log2(e) th - m log2(e))
 __global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int64_t V, int64_t ldz,
                                                                 int64_t n_classes, float softcap,
                                                                 const int32_t* targets, const int32_t* n_valid,
@@ -100,33 +99,43 @@ __global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int
     return;
   }
 
-  // 1. sum exp(S - c) over the classes
-  const float inv_c = 1.0f / softcap;
-  float sum = 0.0f;
-  for (int c = tid; c < nch; c += kCeThreads) {
+  const float k2 = 2.0f * kLog2e / softcap;  // z -> 2 log2(e) z / c
+  const float clampv = 40.0f * kLog2e;        // |z / c| <= 20: tanh is 1 to fp32 precision beyond
+  const float cl = softcap * kLog2e;
+  auto tanh_of = [&](uint32_t bits) {
+    const float y = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(bits) * k2, -clampv), clampv);
+    const float e = __builtin_amdgcn_exp2f(y);
+    return (e - 1.0f) * __builtin_amdgcn_rcpf(e + 1.0f);
+  };
+  auto chunk_tanh = [&](int c, float* th) {
     const v4u v = *reinterpret_cast<const v4u*>(zr + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 8 * c + e;
-      if (j < n_classes) {
-        const float zj = bf16_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        const float s = softcap * tanh_fast(zj * inv_c);
-        sum += exp_fast(s - softcap);
-      }
-    }
+    for (int e = 0; e < 8; ++e) th[e] = tanh_of((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+  };
+
+  // 1. sum exp(S - c) over the classes
+  float sum = 0.0f;
+  auto sweep1 = [&](int c, const float* th) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (8 * c + e < n_classes) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(th[e], cl, -cl));
+  };
+  for (int c = tid; c < nch; c += kCeThreads) {
+    float th[8];
+    chunk_tanh(c, th);
+    sweep1(c, th);
   }
-  const float zt = bf16_to_f32(zr[t]);  // read before any block writes the row
-  sum = block_sum_f32(sum, redf);       // (its barriers also order the reads above before the writes below)
+  const float tht = tanh_of(zr[t]);   // read before any block writes the row
+  sum = block_sum_f32(sum, redf);     // (its barriers also order the reads above before the writes below)
   const float lse = softcap + __logf(sum);
   const float nv = (float)(*n_valid);
   const float inv_nv = nv > 0.0f ? 1.0f / nv : 0.0f;
-  if (tid == 0) loss_rows[r] = lse - softcap * tanh_fast(zt * inv_c);
+  if (tid == 0) loss_rows[r] = lse - softcap * tht;
 
-  // 2. dZ over the row, written over the logits (a second read of the row,
-  //    which the first sweep has just brought into L2)
+  // 2. dZ over the row, written over the logits
+  const float lsel = lse * kLog2e;
   uint32_t mx = 0;
-  for (int c = tid; c < nch; c += kCeThreads) {
-    const v4u v = *reinterpret_cast<const v4u*>(zr + 8 * c);
+  auto sweep2 = [&](int c, const float* th) {
     v4u o;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -136,10 +145,9 @@ __global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int
         const int j = 8 * c + 2 * h + k;
         uint32_t bits = 0;
         if (j < n_classes) {
-          const float zj = bf16_to_f32((v[h] >> (16 * k)) & 0xFFFFu);
-          const float th = tanh_fast(zj * inv_c);
-          const float p = exp_fast(softcap * th - lse);
-          const float g = ((j == t ? p - 1.0f : p) * (1.0f - th * th)) * inv_nv;
+          const float tj = th[2 * h + k];
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(tj, cl, -lsel));
+          const float g = ((j == t ? p - 1.0f : p) * (1.0f - tj * tj)) * inv_nv;
           bits = __builtin_bit_cast(unsigned short, (__bf16)g);
           mx = mx > (bits & 0x7FFFu) ? mx : (bits & 0x7FFFu);
         }
@@ -152,6 +160,11 @@ __global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int
     } else {
       for (int e = 8 * c; e < V; ++e) zr[e] = (uint16_t)(o[(e - 8 * c) >> 1] >> (16 * ((e - 8 * c) & 1)));
     }
+  };
+  for (int c = tid; c < nch; c += kCeThreads) {
+    float th[8];
+    chunk_tanh(c, th);
+    sweep2(c, th);
   }
   mx = block_max_u32(mx, redu);
   if (tid == 0) partials[r] = mx;
