@@ -32,6 +32,27 @@ def _check_dev(*ts):
             raise ValueError("tensors must be on the GPU (no CPU path)")
 
 
+def _out(t, shape, dtype, device, name: str, dense: bool = False) -> torch.Tensor:
+    """A caller-supplied output (checked: device, dtype, shape, and a layout
+    the library can address) or a new empty one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if t.device != torch.device(device) or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not dense and t.dim() == 2 and t.numel() and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t
+
+
+def _ws(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    return t
+
+
 def _ld(t: torch.Tensor) -> int:
     if t.dim() != 2:
         raise ValueError("expected a 2-D tensor")
@@ -56,18 +77,15 @@ def fp8_amax_quant(x: torch.Tensor, fmt: int = E4M3, *, q: torch.Tensor | None =
         raise TypeError("x must be bfloat16")
     rows, cols = x.shape
     dev = x.device
-    if q is None and want_q:
-        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    if qt is None and want_qt:
-        qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
-    if scale is None:
-        scale = torch.empty(1, dtype=torch.float32, device=dev)
-    if amax is None:
-        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    if q is not None or want_q:
+        q = _out(q, (rows, cols), torch.uint8, dev, "q")
+    if qt is not None or want_qt:
+        qt = _out(qt, (cols, rows), torch.uint8, dev, "qt")
+    scale = _out(scale, (1,), torch.float32, dev, "scale", dense=True)
+    amax = _out(amax, (1,), torch.float32, dev, "amax", dense=True)
     L = _native.lib()
     need = L.fp8_amax_quant_workspace_bytes(rows, cols)
-    if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if ws is None else _ws(ws)
     _native.call("fp8_amax_quant", _p(x), rows, cols, _ld(x), fmt, _p(q), 0 if q is None else _ld(q),
                  _p(qt), 0 if qt is None else _ld(qt), _p(scale), _p(amax), _p(ws), ws.numel(), _stream())
     return q, qt, scale, amax
@@ -83,16 +101,19 @@ def fp8_rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor | None = None, eps: f
         raise TypeError("x and gamma must be bfloat16 (gamma contiguous)")
     rows, cols = x.shape
     dev = x.device
-    if q is None and want_q:
-        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    if qt is None and want_qt:
-        qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
-    scale = torch.empty(1, dtype=torch.float32, device=dev) if scale is None else scale
-    amax = torch.empty(1, dtype=torch.float32, device=dev) if amax is None else amax
-    rstd = torch.empty(rows, dtype=torch.float32, device=dev) if rstd is None else rstd
+    if gamma is not None and tuple(gamma.shape) not in ((cols,), (1, cols)):
+        raise ValueError("gamma must hold one weight per column")
+    if q is not None or want_q:
+        q = _out(q, (rows, cols), torch.uint8, dev, "q")
+    if qt is not None or want_qt:
+        qt = _out(qt, (cols, rows), torch.uint8, dev, "qt")
+    scale = _out(scale, (1,), torch.float32, dev, "scale", dense=True)
+    amax = _out(amax, (1,), torch.float32, dev, "amax", dense=True)
+    rstd = _out(rstd, (rows,), torch.float32, dev, "rstd", dense=True)
     if ws is None:
         ws = torch.empty(max(_native.lib().fp8_rmsnorm_quant_workspace_bytes(rows, cols), 16), dtype=torch.uint8,
                          device=dev)
+    _ws(ws)
     _native.call("fp8_rmsnorm_quant", _p(x), _p(gamma), float(eps), rows, cols, _ld(x), fmt, _p(q),
                  0 if q is None else _ld(q), _p(qt), 0 if qt is None else _ld(qt), _p(scale), _p(amax), _p(rstd),
                  _p(ws), ws.numel(), _stream())
@@ -101,8 +122,7 @@ def fp8_rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor | None = None, eps: f
 
 def _gemm(name, a, fa, sa, b, fb, sb, M, N, K, out, out_shape):
     _check_dev(a, b, sa, sb)
-    if out is None:
-        out = torch.empty(out_shape, dtype=torch.bfloat16, device=a.device)
+    out = _out(out, out_shape, torch.bfloat16, a.device, "out")
     _native.call(name, _p(a), _ld(a), fa, _p(sa), _p(b), _ld(b), fb, _p(sb), M, N, K, _p(out), _ld(out),
                  _stream())
     return out
@@ -150,6 +170,11 @@ class Relu2MlpSaved:
                              torch.empty(4, dtype=torch.float32, device=device), M, d, h)
 
     def c_struct(self) -> _native.Relu2MlpSaved:
+        M, d, h = self.M, self.d, self.hid
+        for name, shape, dt in (("xq_t", (d, M), torch.uint8), ("uq_t", (d, h), torch.uint8),
+                                ("dq_t", (h, d), torch.uint8), ("aq_t", (h, M), torch.uint8),
+                                ("h", (M, h), torch.bfloat16), ("scales", (4,), torch.float32)):
+            _out(getattr(self, name), shape, dt, self.scales.device, "saved." + name, dense=True)
         return _native.Relu2MlpSaved(self.xq_t.data_ptr(), self.uq_t.data_ptr(), self.dq_t.data_ptr(),
                                      self.aq_t.data_ptr(), self.h.data_ptr(), self.scales.data_ptr())
 
@@ -184,12 +209,12 @@ def relu2_mlp_fwd(x, w_up, w_down, *, y=None, saved: Relu2MlpSaved | None = None
     for t in (x, w_up, w_down):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError("x, w_up, w_down must be contiguous bfloat16")
-    if y is None:
-        y = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    y = _out(y, (M, d), torch.bfloat16, x.device, "y", dense=True)
     if saved is None:
         saved = Relu2MlpSaved.empty(M, d, h, x.device)
-    if ws is None:
-        ws = relu2_mlp_fwd_workspace(M, d, h, x.device)
+    if (saved.M, saved.d, saved.hid) != (M, d, h):
+        raise ValueError("saved was made for another shape")
+    ws = relu2_mlp_fwd_workspace(M, d, h, x.device) if ws is None else _ws(ws)
     cs = saved.c_struct()
     _native.call("relu2_mlp_fwd", _p(x), _p(w_up), _p(w_down), M, d, h, _p(y), ctypes.byref(cs), _p(ws),
                  ws.numel(), _stream())
@@ -203,14 +228,12 @@ def relu2_mlp_bwd(dy, saved: Relu2MlpSaved, *, dx=None, dw_up=None, dw_down=None
     dev = dy.device
     if dy.shape != (M, d) or dy.dtype != torch.bfloat16 or not dy.is_contiguous():
         raise ValueError("dy must be a contiguous bfloat16 [M, d] tensor")
-    bf = dict(dtype=torch.bfloat16, device=dev)
-    dx = torch.empty((M, d), **bf) if dx is None else dx
-    dw_up = torch.empty((h, d), **bf) if dw_up is None else dw_up
-    dw_down = torch.empty((d, h), **bf) if dw_down is None else dw_down
-    if bwd_scales is None:
-        bwd_scales = torch.empty(2, dtype=torch.float32, device=dev)
-    if ws is None:
-        ws = relu2_mlp_bwd_workspace(M, d, h, dev)
+    bf = torch.bfloat16
+    dx = _out(dx, (M, d), bf, dev, "dx", dense=True)
+    dw_up = _out(dw_up, (h, d), bf, dev, "dw_up", dense=True)
+    dw_down = _out(dw_down, (d, h), bf, dev, "dw_down", dense=True)
+    bwd_scales = _out(bwd_scales, (2,), torch.float32, dev, "bwd_scales", dense=True)
+    ws = relu2_mlp_bwd_workspace(M, d, h, dev) if ws is None else _ws(ws)
     cs = saved.c_struct()
     _native.call("relu2_mlp_bwd", _p(dy), ctypes.byref(cs), M, d, h, _p(dx), _p(dw_up), _p(dw_down),
                  _p(bwd_scales), _p(ws), ws.numel(), _stream())
@@ -242,6 +265,12 @@ class SwigluMlpSaved:
                               M, d, h)
 
     def c_struct(self) -> _native.SwigluMlpSaved:
+        M, d, h = self.M, self.d, self.hid
+        u8, bf = torch.uint8, torch.bfloat16
+        for name, shape, dt in (("xq_t", (d, M), u8), ("wgq_t", (d, h), u8), ("wuq_t", (d, h), u8),
+                                ("wdq_t", (h, d), u8), ("aq_t", (h, M), u8), ("g", (M, h), bf), ("u", (M, h), bf),
+                                ("scales", (5,), torch.float32)):
+            _out(getattr(self, name), shape, dt, self.scales.device, "saved." + name, dense=True)
         return _native.SwigluMlpSaved(*(t.data_ptr() for t in (self.xq_t, self.wgq_t, self.wuq_t, self.wdq_t,
                                                                self.aq_t, self.g, self.u, self.scales)))
 
@@ -270,12 +299,12 @@ def swiglu_mlp_fwd(x, w_gate, w_up, w_down, *, y=None, saved: SwigluMlpSaved | N
     for t in (x, w_gate, w_up, w_down):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError("x, w_gate, w_up, w_down must be contiguous bfloat16")
-    if y is None:
-        y = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    y = _out(y, (M, d), torch.bfloat16, x.device, "y", dense=True)
     if saved is None:
         saved = SwigluMlpSaved.empty(M, d, h, x.device)
-    if ws is None:
-        ws = swiglu_mlp_workspace("fwd", M, d, h, x.device)
+    if (saved.M, saved.d, saved.hid) != (M, d, h):
+        raise ValueError("saved was made for another shape")
+    ws = swiglu_mlp_workspace("fwd", M, d, h, x.device) if ws is None else _ws(ws)
     cs = saved.c_struct()
     _native.call("swiglu_mlp_fwd", _p(x), _p(w_gate), _p(w_up), _p(w_down), M, d, h, _p(y), ctypes.byref(cs),
                  _p(ws), ws.numel(), _stream())
@@ -291,15 +320,13 @@ def swiglu_mlp_bwd(dy, saved: SwigluMlpSaved, *, dx=None, dw_gate=None, dw_up=No
     dev = dy.device
     if dy.shape != (M, d) or dy.dtype != torch.bfloat16 or not dy.is_contiguous():
         raise ValueError("dy must be a contiguous bfloat16 [M, d] tensor")
-    bf = dict(dtype=torch.bfloat16, device=dev)
-    dx = torch.empty((M, d), **bf) if dx is None else dx
-    dw_gate = torch.empty((h, d), **bf) if dw_gate is None else dw_gate
-    dw_up = torch.empty((h, d), **bf) if dw_up is None else dw_up
-    dw_down = torch.empty((d, h), **bf) if dw_down is None else dw_down
-    if bwd_scales is None:
-        bwd_scales = torch.empty(3, dtype=torch.float32, device=dev)
-    if ws is None:
-        ws = swiglu_mlp_workspace("bwd", M, d, h, dev)
+    bf = torch.bfloat16
+    dx = _out(dx, (M, d), bf, dev, "dx", dense=True)
+    dw_gate = _out(dw_gate, (h, d), bf, dev, "dw_gate", dense=True)
+    dw_up = _out(dw_up, (h, d), bf, dev, "dw_up", dense=True)
+    dw_down = _out(dw_down, (d, h), bf, dev, "dw_down", dense=True)
+    bwd_scales = _out(bwd_scales, (3,), torch.float32, dev, "bwd_scales", dense=True)
+    ws = swiglu_mlp_workspace("bwd", M, d, h, dev) if ws is None else _ws(ws)
     cs = saved.c_struct()
     _native.call("swiglu_mlp_bwd", _p(dy), ctypes.byref(cs), M, d, h, _p(dx), _p(dw_gate), _p(dw_up),
                  _p(dw_down), _p(bwd_scales), _p(ws), ws.numel(), _stream())
@@ -319,7 +346,9 @@ def bf16_gemm_nt(a, b, alpha: float = 1.0, beta: float = 0.0, aux=None, *, out=N
             raise ValueError("a, b and aux must be bfloat16 with unit column stride")
     if aux is not None and tuple(aux.shape) != (M, N):
         raise ValueError("aux must be [M, N]")
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if out is None else out
+    out = _out(out, (M, N), torch.bfloat16, a.device, "out")
+    if out_t is not None:
+        _out(out_t, (N, M), torch.bfloat16, a.device, "out_t")
     _native.call("bf16_gemm_nt", _p(a), _ld(a), _p(b), _ld(b), M, N, K, float(alpha), float(beta),
                  None if aux is None else _p(aux), 0 if aux is None else _ld(aux), _p(out), _ld(out),
                  None if out_t is None else _p(out_t), 0 if out_t is None else _ld(out_t), _stream())
@@ -336,12 +365,13 @@ def bf16_gemm_sym(a, alpha: float = 1.0, beta: float = 0.0, aux=None, *, out=Non
             raise ValueError("a and aux must be bfloat16 with unit column stride")
     if aux is not None and tuple(aux.shape) != (M, M):
         raise ValueError("aux must be [M, M]")
-    out = torch.empty((M, M), dtype=torch.bfloat16, device=a.device) if out is None else out
+    out = _out(out, (M, M), torch.bfloat16, a.device, "out")
     if ws is None:
         n = _native.lib().bf16_gemm_sym_workspace_bytes(M, K)
         if n == 0:
             raise ValueError(f"unsupported symmetric product shape {M}x{K}")
         ws = torch.empty(n, dtype=torch.uint8, device=a.device)
+    _ws(ws)
     _native.call("bf16_gemm_sym", _p(a), _ld(a), M, K, float(alpha), float(beta),
                  None if aux is None else _p(aux), 0 if aux is None else _ld(aux), _p(out), _ld(out), _p(ws),
                  ws.numel(), _stream())
@@ -363,9 +393,9 @@ def muon_newton_schulz(g, steps: int = 5, coeffs=None, eps: float = 1e-7, *, out
         raise ValueError("g must be a contiguous 2-D bfloat16 tensor")
     rows, cols = g.shape
     dev = g.device
-    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if out is None else out
-    norm = torch.zeros(2, dtype=torch.float32, device=dev) if norm is None else norm
-    ws = muon_ns_workspace(rows, cols, dev) if ws is None else ws
+    out = _out(out, (rows, cols), torch.bfloat16, dev, "out", dense=True)
+    norm = _out(norm, (2,), torch.float32, dev, "norm", dense=True)
+    ws = muon_ns_workspace(rows, cols, dev) if ws is None else _ws(ws)
     c = None if coeffs is None else (ctypes.c_float * 3)(*coeffs)
     _native.call("muon_newton_schulz", _p(g), rows, cols, int(steps), c, float(eps), _p(out), _p(norm), _p(ws),
                  ws.numel(), _stream())
@@ -402,12 +432,11 @@ def fp8_lm_head_ce(x, w, targets, n_classes: int, softcap: float = 15.0, chunk: 
             raise ValueError("x and w must be contiguous bfloat16")
     dev = x.device
     nchunks = (M + chunk - 1) // chunk if M > 0 else 0
-    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
-    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if dx is None else dx
-    dw = torch.empty((V, K), dtype=torch.bfloat16, device=dev) if dw is None else dw
-    scales = torch.empty(2 + nchunks, dtype=torch.float32, device=dev) if scales is None else scales
-    if ws is None:
-        ws = fp8_lm_head_ce_workspace(M, K, V, chunk, dev)
+    loss = _out(loss, (1,), torch.float32, dev, "loss", dense=True)
+    dx = _out(dx, (M, K), torch.bfloat16, dev, "dx", dense=True)
+    dw = _out(dw, (V, K), torch.bfloat16, dev, "dw", dense=True)
+    scales = _out(scales, (2 + nchunks,), torch.float32, dev, "scales", dense=True)
+    ws = fp8_lm_head_ce_workspace(M, K, V, chunk, dev) if ws is None else _ws(ws)
     if not targets.is_contiguous():
         raise ValueError("targets must be contiguous")
     _native.call("fp8_lm_head_ce", _p(x), _p(w), _p(targets), M, K, V, n_classes, float(softcap),

@@ -280,3 +280,25 @@ def test_symmetric_product_validation():
     # empty shapes: valid, with a (small) workspace size
     assert L.bf16_gemm_sym_workspace_bytes(0, 64) > 0 and L.bf16_gemm_sym_workspace_bytes(64, 0) > 0
     assert L.muon_ns_workspace_bytes(0, 64) > 0 and L.muon_ns_workspace_bytes(64, 0) > 0
+
+
+def test_binding_checks_caller_outputs():
+    """The Python binding refuses a caller-supplied output of the wrong
+    shape, dtype or layout before anything reaches the library."""
+    import torch
+    from fp8_tensorwise_scaled_amd import api
+
+    cpu = torch.device("cpu")
+    ok = torch.empty((4, 8), dtype=torch.bfloat16)
+    assert api._out(ok, (4, 8), torch.bfloat16, cpu, "y") is ok
+    assert api._out(None, (4, 8), torch.bfloat16, cpu, "y").shape == (4, 8)
+    wide = torch.empty((4, 16), dtype=torch.bfloat16)
+    assert api._out(wide[:, :8], (4, 8), torch.bfloat16, cpu, "y").stride() == (16, 1)   # row stride allowed
+    for bad in (torch.empty((3, 8), dtype=torch.bfloat16), torch.empty((4, 8), dtype=torch.float32),
+                torch.empty((8, 4), dtype=torch.bfloat16).t()):
+        with pytest.raises(ValueError):
+            api._out(bad, (4, 8), torch.bfloat16, cpu, "y")
+    with pytest.raises(ValueError):
+        api._out(wide[:, :8], (4, 8), torch.bfloat16, cpu, "y", dense=True)
+    with pytest.raises(ValueError):
+        api._ws(torch.empty(16, dtype=torch.float32))
