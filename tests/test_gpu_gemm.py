@@ -42,6 +42,22 @@ def test_fwd(fa, fb, MNK):
     check_gemm(bf16_bits(y), "nt", qa, fa, sa, qb, fb, sb, f"fwd {MNK}")
 
 
+def test_random_shapes():
+    """Sixteen seeded random shapes: M and N in [1, 700) (ragged tiles of
+    both tile widths), K a multiple of 16 up to 1024, random format pair."""
+    from fp8_tensorwise_scaled_amd import api
+
+    rng = np.random.default_rng(2024)
+    for i in range(16):
+        M, N = (int(v) for v in rng.integers(1, 700, 2))
+        K = 16 * int(rng.integers(1, 65))
+        fa, fb = (int(v) for v in rng.integers(0, 2, 2))
+        qa, sa, qb, sb = quant_pair((M, K), (N, K), fa, fb, 7000 + i)
+        y = api.fp8_linear_fwd(to_dev_u8(qa), scal(sa), to_dev_u8(qb), scal(sb), fa, fb)
+        torch.cuda.synchronize()
+        check_gemm(bf16_bits(y), "nt", qa, fa, sa, qb, fb, sb, f"random {M}x{N}x{K} fmt {fa}{fb}")
+
+
 def test_linear_small_workload():
     """Single linear forward: X [256x512] N(0,1), W [1024x512] N(0,0.02)."""
     from fp8_tensorwise_scaled_amd import api
