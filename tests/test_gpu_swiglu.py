@@ -110,3 +110,14 @@ def test_deterministic_and_reuse():
     a, b = run_block(w), run_block(w)
     for k in ("y", "dx", "dw_gate", "dw_up", "dw_down", "g", "u", "a", "dg", "du", "dgq", "duq"):
         assert (a[k] == b[k]).all(), k
+
+
+def test_tiny_ragged_block():
+    """M=48, d=64, h=176: every GEMM is a single ragged tile; every stage on
+    every row and column against the oracle chain."""
+    w = synth.SwigluWorkload(44, 48, 64, 176, sigma_in=1 / 8, sigma_down=1 / 13)
+    g = run_block(w)
+    sc, _, _ = sc_.full_chain_scales(g["x"], g["wg"], g["wu"], g["wd"], g["dy"])
+    rows, cols = np.arange(w.M), np.arange(w.h)
+    o = sc_.sampled_chain(g["x"], g["wg"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
+    sc_.compare(g, o, sc, rows, cols)
