@@ -1,0 +1,119 @@
+"""The library under HIP graph capture.  Each path is captured once with
+preallocated outputs and workspaces and replayed several times, with eager
+work and synchronisations in between; every replay gives the eager pass's
+bytes (the kernels are deterministic, clear nothing with memset and
+allocate nothing)."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_tensorwise_scaled_amd import synth
+from tests.gpu_util import to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _relu2():
+    from fp8_tensorwise_scaled_amd import api
+
+    w = synth.MLPWorkload(51, 512, 256, 1024, sigma_up=1 / 16, sigma_down=1 / 32)
+    x, wu, wd, dy = (to_dev_bf16(t) for t in w.tensors())
+    M, d, h = w.M, w.d, w.h
+    dev = x.device
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    outs = dict(y=torch.empty((M, d), **bf), dx=torch.empty((M, d), **bf), dwu=torch.empty((h, d), **bf),
+                dwd=torch.empty((d, h), **bf), bsc=torch.empty(2, dtype=torch.float32, device=dev))
+    saved = api.Relu2MlpSaved.empty(M, d, h, dev)
+    ws_f, ws_b = api.relu2_mlp_fwd_workspace(M, d, h, dev), api.relu2_mlp_bwd_workspace(M, d, h, dev)
+
+    def step():
+        api.relu2_mlp_fwd(x, wu, wd, y=outs["y"], saved=saved, ws=ws_f)
+        api.relu2_mlp_bwd(dy, saved, dx=outs["dx"], dw_up=outs["dwu"], dw_down=outs["dwd"],
+                          bwd_scales=outs["bsc"], ws=ws_b)
+    return step, outs
+
+
+def _swiglu():
+    from fp8_tensorwise_scaled_amd import api
+
+    w = synth.SwigluWorkload(52, 256, 128, 352, sigma_in=1 / 11, sigma_down=1 / 19)
+    x, wg, wu, wd, dy = (to_dev_bf16(t) for t in w.tensors())
+    M, d, h = w.M, w.d, w.h
+    dev = x.device
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    outs = dict(y=torch.empty((M, d), **bf), dx=torch.empty((M, d), **bf), dwg=torch.empty((h, d), **bf),
+                dwu=torch.empty((h, d), **bf), dwd=torch.empty((d, h), **bf),
+                bsc=torch.empty(3, dtype=torch.float32, device=dev))
+    saved = api.SwigluMlpSaved.empty(M, d, h, dev)
+    ws_f, ws_b = api.swiglu_mlp_workspace("fwd", M, d, h, dev), api.swiglu_mlp_workspace("bwd", M, d, h, dev)
+
+    def step():
+        api.swiglu_mlp_fwd(x, wg, wu, wd, y=outs["y"], saved=saved, ws=ws_f)
+        api.swiglu_mlp_bwd(dy, saved, dx=outs["dx"], dw_gate=outs["dwg"], dw_up=outs["dwu"], dw_down=outs["dwd"],
+                           bwd_scales=outs["bsc"], ws=ws_b)
+    return step, outs
+
+
+def _lm_head_ce():
+    from fp8_tensorwise_scaled_amd import api
+
+    wl = synth.LMHeadCEWorkload(53, 256, 256, 600, n_classes=590, chunk=64, sigma_w=0.25, ignored=0.05)
+    x, w, t = wl.tensors()
+    X, W = to_dev_bf16(x), to_dev_bf16(w)
+    T = torch.from_numpy(np.ascontiguousarray(t, dtype=np.int32)).cuda()
+    dev = X.device
+    M, K, V = wl.M, wl.K, wl.V
+    outs = dict(loss=torch.empty(1, dtype=torch.float32, device=dev),
+                dx=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                dw=torch.empty((V, K), dtype=torch.bfloat16, device=dev),
+                scales=torch.empty(2 + M // wl.chunk, dtype=torch.float32, device=dev))
+    ws = api.fp8_lm_head_ce_workspace(M, K, V, wl.chunk, dev)
+
+    def step():
+        api.fp8_lm_head_ce(X, W, T, wl.n_classes, wl.softcap, wl.chunk, ws=ws, **outs)
+    return step, outs
+
+
+def _newton_schulz():
+    from fp8_tensorwise_scaled_amd import api
+
+    G = to_dev_bf16(synth.normal_bf16((208, 720), 0.02, 54))
+    dev = G.device
+    outs = dict(out=torch.empty((208, 720), dtype=torch.bfloat16, device=dev),
+                norm=torch.empty(2, dtype=torch.float32, device=dev))
+    ws = api.muon_ns_workspace(208, 720, dev)
+
+    def step():
+        api.muon_newton_schulz(G, 5, out=outs["out"], norm=outs["norm"], ws=ws)
+    return step, outs
+
+
+def _bytes(t):
+    return t.detach().contiguous().view(torch.uint8).cpu().clone()
+
+
+@pytest.mark.parametrize("make", [_relu2, _swiglu, _lm_head_ce, _newton_schulz],
+                         ids=["relu2_block", "swiglu_block", "lm_head_ce", "newton_schulz"])
+def test_graph_replays_match_eager(make):
+    step, outs = make()
+    step()
+    torch.cuda.synchronize()
+    eager = {k: _bytes(v) for k, v in outs.items()}
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(_bytes(v), eager[k]), (rep, k)
