@@ -119,3 +119,14 @@ def test_deterministic_and_reuse():
     b = run_block(synth.MLPWorkload(21, 512, 256, 1024, sigma_up=1 / 16, sigma_down=1 / 32))
     for k in ("y", "dx", "dw_up", "dw_down", "h", "aq", "hq"):
         assert (a[k] == b[k]).all(), k
+
+
+def test_tiny_ragged_block():
+    """M=48, d=64, h=176: every GEMM is a single ragged tile; every stage on
+    every row and column against the oracle chain."""
+    w = synth.MLPWorkload(45, 48, 64, 176, sigma_up=1 / 8, sigma_down=1 / 13)
+    g = run_block(w)
+    sc, _, _ = full_chain_scales(g["x"], g["wu"], g["wd"], g["dy"])
+    rows, cols = np.arange(w.M), np.arange(w.h)
+    o = sampled_chain(g["x"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
+    compare_block(g, o, sc, rows, cols)
