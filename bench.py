@@ -60,16 +60,42 @@ def cpu_baseline(w, rows_per_gemm: int = 1536):
     oracle.gemm_nn(hq_src, 1, sg, uq, 0, su, rows=rm); flops += 2 * rows_per_gemm * w.d * w.h  # up dgrad
     t_gemm = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    model = None
+    try:
+        model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")),
+                     None)
+    except OSError:
+        pass
     return {
         "value": flops / t_gemm / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cpus": os.cpu_count(),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"{rows_per_gemm} output rows of each of the six GEMMs of the M={w.M} d={w.d} h={w.h} "
                   f"block ({flops / 1e9:.1f} GFLOP, fp64 accumulation, {t_gemm:.1f} s); the four input "
                   f"quantisations took {t_quant:.1f} s",
         "gemm_seconds": t_gemm,
     }
+
+
+def gpu_clocks():
+    """Current shader and memory clock levels from sysfs (best effort; the
+    starred level of pp_dpm_sclk / pp_dpm_mclk), or None where not exposed."""
+    import glob
+
+    out = {}
+    for kind in ("sclk", "mclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
+            try:
+                cur = [ln.strip() for ln in open(path) if ln.strip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[kind] = cur[0]
+                break
+    return out or None
 
 
 def measured_traffic():
@@ -358,16 +384,21 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clocks_before = gpu_clocks()
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
+        evs[i + 1].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = ev0.elapsed_time(ev1) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     flops = w.flops
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {t_wall / args.steps * 1e3:.3f} ms/step)")
@@ -439,6 +470,9 @@ def main() -> int:
                    "formats": "E4M3 activations/weights, E5M2 gradients, fp32 accumulate, bf16 out"},
         "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "tokens_per_s_equiv": round(M / (ms * 1e-3)),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
+        "gpu_clocks": {"before": clocks_before, "after": gpu_clocks()},
         "roofline": {
             "kernel": "gemm_nt_kernel<0,0,256,192,4,2,0> (E4M3 x E4M3, plain store, 8 waves; down-projection fwd, "
                       "M=8192 N=3072 K=12288)",
