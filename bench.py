@@ -6,8 +6,8 @@ relu^2 cast, the dY and dH casts and all six FP8 GEMMs, with inputs resident
 in HBM.  The metric counts GEMM FLOPs only (12*M*d*h per step), the
 convention of the pages' TFLOP/s figure.
 
-Prints one JSON line (rank 0).  --gpus > 1 is not supported: this build runs
-on one GPU.
+Prints one JSON line.  --gpus > 1 is not supported: the library runs the
+block on one GPU (no sharding, no collectives).
 """
 from __future__ import annotations
 
@@ -347,7 +347,7 @@ def main() -> int:
                          "Newton-Schulz orthogonalisation of a 3072x12288 matrix (and its transpose)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build runs the FP8 MLP block on one "
+        print(f"bench.py: --gpus {args.gpus} is not supported; the library runs the FP8 MLP block on one "
               "GPU (no sharding, no collectives)", file=sys.stderr)
         return 2
     if args.workload != "mlp":

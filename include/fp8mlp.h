@@ -62,7 +62,7 @@ extern "C" {
 #define FP8MLP_EALIGN 2     /* pointer or leading dimension misaligned          */
 #define FP8MLP_EWORKSPACE 3 /* workspace missing or smaller than the query      */
 #define FP8MLP_EHIP 4       /* a HIP launch failed                              */
-#define FP8MLP_ENOTSUP 5    /* shape outside what this build supports           */
+#define FP8MLP_ENOTSUP 5    /* shape outside what the library supports          */
 
 int fp8mlp_abi_version(void);
 /* Static string describing a status code (never NULL). */
