@@ -341,7 +341,7 @@ def main() -> int:
                     default="mlp",
                     help="mlp: the relu2 block M=8192 (default); proj: the decoder projection set at "
                          "M=32768; lmhead: the LM head at vocabulary 50304 and 50257; lmce: the LM head "
-                         "fused with the softcapped cross-entropy (chunks of 4096 rows); rmsnorm: RMSNorm fused "
+                         "fused with the softcapped cross-entropy (chunks of 8192 rows); rmsnorm: RMSNorm fused "
                          "with the quantisation of the block input X [8192, 3072]; swiglu: the gated MLP block "
                          "M=8192 d=3072 h=8448, beside the relu2 block at the same width; muon: Muon's "
                          "Newton-Schulz orthogonalisation of a 3072x12288 matrix (and its transpose)")

@@ -255,4 +255,7 @@ SWIGLU_3P8B = SwigluWorkload(8, 8192, 3072, 8448, name="SwiGLU MLP M=8192 d=3072
 PROJ_SET = ProjectionSetWorkload(4, 32768, name="decoder projection set M=32768")
 LM_HEAD_PADDED = LMHeadWorkload(5, 16384, 3072, 50304, name="LM head M=16384 K=3072 N=50304")
 LM_HEAD_UNPADDED = LMHeadWorkload(5, 16384, 3072, 50257, name="LM head M=16384 K=3072 N=50257")
-LM_HEAD_CE = LMHeadCEWorkload(6, 16384, 3072, 50304, name="LM head + softcapped CE M=16384 K=3072 V=50304")
+# chunks of 8192 rows: the logits buffer is half the [M, V] tensor (824 MB of
+# 288 GB); 4096-row chunks measured 7% slower, 2048-row chunks 34% slower
+LM_HEAD_CE = LMHeadCEWorkload(6, 16384, 3072, 50304, chunk=8192,
+                              name="LM head + softcapped CE M=16384 K=3072 V=50304")

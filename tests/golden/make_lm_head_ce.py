@@ -1,6 +1,6 @@
 """Writes lm_head_ce.json: the oracle's tensor-wide quantities of the FP8 LM
 head fused with the softcapped cross-entropy at full size (M=16384, K=3072,
-V=50304 with 50257 classes, chunks of 4096 rows, softcap 15).
+V=50304 with 50257 classes, chunks of 8192 rows, softcap 15).
 
 Every chunk's dZ scale depends on all its logits and every row's gradient on
 the row's log-sum-exp, so sampled checks of dX rows and dW rows at this size

@@ -183,7 +183,7 @@ def test_no_counted_rows_and_no_rows():
 
 
 def test_full_size_sampled():
-    """M=16384, K=3072, V=50304 (50257 classes), chunks of 4096: the oracle's
+    """M=16384, K=3072, V=50304 (50257 classes), chunks of 8192: the oracle's
     stored chunk scales, row log-sum-exps and loss, and 12 sampled rows of dX
     and 12 rows of dW computed by the oracle from them."""
     wl = synth.LM_HEAD_CE
