@@ -134,6 +134,28 @@ def _time_steps(step, steps, warmup):
     return ev0.elapsed_time(ev1) / steps
 
 
+def _roofline(kernel: str, bound: str, flops_or_bytes: float, us: float, peak: float, unit: str):
+    """Roofline object for one kernel: algorithmic work per launch / its
+    average launch time (HIP events on the launching stream)."""
+    achieved = flops_or_bytes / (us * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
+    return {"kernel": kernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None, "avg_launch_us": round(us, 2)}
+
+
+def _oracle_gemms_rate(jobs, what: str):
+    """cpu_baseline from timed oracle GEMMs on sampled output rows: jobs are
+    (function, args, rows, flops)."""
+    t0 = time.perf_counter()
+    flops = 0
+    for fn, a, rows, f in jobs:
+        fn(*a, rows=rows)
+        flops += f
+    sec = time.perf_counter() - t0
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+            "sample": f"{what} ({flops / 1e9:.1f} GFLOP, fp64 accumulation, {sec:.1f} s)"}
+
+
 def bench_other(args) -> int:
     """Projection set (M=32768) or LM head (padded and unpadded vocabulary):
     one step = forward + backward of every linear, quantisations included."""
@@ -186,16 +208,28 @@ def bench_other(args) -> int:
         ms_unf = _time_steps(unfused, args.steps * 5, args.warmup)
         nbytes = M * d * 6 + M * 4
         gbs = nbytes / (ms * 1e-3) / 1e9
+        cpu = None
+        if not args.no_cpu_baseline:
+            import oracle
+
+            R = 1024
+            xs, gs = synth.normal_bf16((M, d), 2.5, 3001)[:R], synth.normal_bf16((d,), 1.0, 3002)
+            t0 = time.perf_counter()
+            oracle.rmsnorm_quant(xs, gs, 1e-6, oracle.E4M3)
+            sec = time.perf_counter() - t0
+            cpu = {"value": R * d * 6 / sec / 1e9, "unit": "GB/s",
+                   "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+                   "sample": f"RMSNorm + quantisation of the first {R} rows ({sec:.2f} s)"}
         log(f"RMSNorm + quantise: {ms * 1e3:.1f} us ({gbs:.0f} GB/s); torch rms_norm then quantise: "
             f"{ms_unf * 1e3:.1f} us")
         res = {"metric": "RMSNorm fused with FP8 tensorwise quantisation (codes + transposed codes), GB/s",
                "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 5),
-               "data": "synthetic (seeded N(0,2.5) rows with 0.1% x100 outliers, N(0,1) weight; bf16)",
+               "data": "synthetic (seeded N(0,2.5) rows, N(0,1) weight; bf16)",
                "config": {"workload": f"RMSNorm + E4M3 quantisation of X [{M}, {d}], eps 1e-6", "M": M, "d": d,
                           "algorithmic_bytes": nbytes},
                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
-               "unfused_torch_rmsnorm_then_quantise_ms": round(ms_unf, 5)}
+               "unfused_torch_rmsnorm_then_quantise_ms": round(ms_unf, 5), "cpu_baseline": cpu}
         common["unit"] = "GB/s"
     elif args.workload == "muon":
         from fp8_tensorwise_scaled_amd import api
@@ -217,6 +251,30 @@ def bench_other(args) -> int:
         flops = steps * (4 * m * m * n + 2 * m * m * m)
         ms = res_all[(rows, cols)]
         tflops = flops / (ms * 1e-3) / 1e12
+        # dominant kernel: X = B X + a X (and X^T) on the bf16 matrix cores
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        Bm = (torch.randn((m, m), device=dev) / m).to(torch.bfloat16)
+        Xm = (torch.randn((m, n), device=dev) / 6000).to(torch.bfloat16)
+        Xt, Xt2 = Xm.t().contiguous(), torch.empty((n, m), **bf)
+        us = 1e3 * _time_steps(lambda: api.bf16_gemm_nt(Bm, Xt, 1.0, 3.4445, Xm, out=Xm, out_t=Xt2),
+                               args.gemm_reps, 3)
+        roof = _roofline(f"gemm_nt_kernel<2,2,256,192,4,2,5> (bf16, alpha/beta epilogue with transposed store; "
+                         f"X = B X + a X, M={m} N={n} K={m})", "mfma", 2 * m * n * m, us, PEAK_BF16_TFLOPS,
+                         "TFLOP/s")
+        log(f"X = B X + a X: {us:.1f} us, {roof['achieved']:.1f} TFLOP/s")
+        cpu = None
+        if not args.no_cpu_baseline:
+            import oracle
+
+            g = synth.normal_bf16((rows, cols), 0.02, 4001, outlier_frac=1e-3)
+            t0 = time.perf_counter()
+            oracle.newton_schulz(g)
+            sec = time.perf_counter() - t0
+            cpu = {"value": flops / sec / 1e12, "unit": "TFLOP/s",
+                   "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+                   "sample": f"the whole {rows}x{cols} orthogonalisation (fp64 BLAS products, bf16 roundings, "
+                             f"{sec:.1f} s)"}
+            log(f"oracle: {sec:.1f} s")
         res = {"metric": "Muon Newton-Schulz orthogonalisation (5 steps, bf16 matrix cores), TFLOP/s",
                "value": round(tflops, 2), "ms_per_step": round(ms, 4),
                "data": "synthetic (seeded N(0,0.02) gradient with 0.1% x100 outliers; bf16)",
@@ -224,7 +282,8 @@ def bench_other(args) -> int:
                                       f"the transposed W_up shape beside it)", "rows": rows, "cols": cols,
                           "steps": steps, "flops": flops},
                "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-               "tall": {"rows": cols, "cols": rows, "ms": round(res_all[(cols, rows)], 4)}}
+               "tall": {"rows": cols, "cols": rows, "ms": round(res_all[(cols, rows)], 4)},
+               "roofline": roof, "cpu_baseline": cpu}
         common["dtype"] = "bf16"
     elif args.workload == "swiglu":
         from fp8_tensorwise_scaled_amd import api
@@ -247,7 +306,42 @@ def bench_other(args) -> int:
         ms = _time_steps(step, args.steps, args.warmup)
         tflops = w.flops / (ms * 1e-3) / 1e12
         log(f"SwiGLU block: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
-        del ws_f, ws_b, saved
+        # dominant kernel: the gate projection G = Xq Wgq^T on the block's own codes
+        offs = api.swiglu_workspace_layout("fwd", M, d, h)
+        xq = ws_f[offs[0]:offs[0] + M * d].view(M, d)
+        wgq = ws_f[offs[1]:offs[1] + h * d].view(h, d)
+        gbuf = torch.empty((M, h), dtype=torch.bfloat16, device=dev)
+        us = 1e3 * _time_steps(lambda: api.fp8_linear_fwd(xq, saved.scales[0:1], wgq, saved.scales[1:2], out=gbuf),
+                               args.gemm_reps, 3)
+        roof = _roofline(f"gemm_nt_kernel<0,0,256,BN,..,0> (E4M3 x E4M3; gate projection M={M} N={h} K={d})",
+                         "mfma", 2 * M * h * d, us, PEAK_FP8_TFLOPS, "TFLOP/s")
+        log(f"gate projection GEMM: {us:.1f} us, {roof['achieved']:.1f} TFLOP/s")
+        del ws_f, ws_b, saved, gbuf
+        cpu = None
+        if not args.no_cpu_baseline:
+            import oracle
+
+            x, wg, wu, wd, dy = w.tensors()
+            xq_o, sx, _ = oracle.quant(x, oracle.E4M3)
+            wgq_o, swg, _ = oracle.quant(wg, oracle.E4M3)
+            wdq_o, swd, _ = oracle.quant(wd, oracle.E4M3)
+            gq_o, sg, _ = oracle.quant(dy, oracle.E5M2)
+            rng = np.random.default_rng(0)
+            R = 256
+            rm, rh, rd = (rng.choice(n, R, replace=False) for n in (M, h, d))
+            # [M, h] stand-ins with the formats of A (E4M3) and dG / dU (E5M2)
+            aq = np.ascontiguousarray(np.tile(xq_o, (1, -(-h // d)))[:, :h])
+            dgq = np.ascontiguousarray(np.tile(gq_o, (1, -(-h // d)))[:, :h])
+            E4, E5 = oracle.E4M3, oracle.E5M2
+            jobs = [(oracle.gemm_nt, (xq_o, E4, sx, wgq_o, E4, swg), rm, 2 * R * h * d)] * 2 + [
+                (oracle.gemm_nt, (aq, E4, sx, wdq_o, E4, swd), rm, 2 * R * d * h),
+                (oracle.gemm_tn, (gq_o, E5, sg, aq, E4, sx), rd, 2 * R * h * M),
+                (oracle.gemm_nn, (gq_o, E5, sg, wdq_o, E4, swd), rm, 2 * R * h * d)] + [
+                (oracle.gemm_tn, (dgq, E5, sg, xq_o, E4, sx), rh, 2 * R * d * M)] * 2 + [
+                (oracle.gemm_nn, (dgq, E5, sg, wgq_o, E4, swg), rm, 2 * R * d * h)] * 2
+            cpu = _oracle_gemms_rate(jobs, f"{R} output rows of each of the nine GEMMs of the M={M} d={d} h={h} "
+                                           "gated block")
+            log(f"oracle: {cpu['value']:.4f} TFLOP/s")
         # the relu^2 block the pages chose instead, same d, 4x intermediate
         r = synth.MLP_3P8B
         xr, wur, wdr, dyr = (t(a) for a in r.tensors())
@@ -272,7 +366,8 @@ def bench_other(args) -> int:
                "tokens_per_s_equiv": round(M / (ms * 1e-3)),
                "relu2_same_width": {"h": r.h, "ms_per_step": round(ms_r, 4),
                                     "tokens_per_s_equiv": round(r.M / (ms_r * 1e-3)),
-                                    "value": round(r.flops / (ms_r * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}}
+                                    "value": round(r.flops / (ms_r * 1e-3) / 1e12, 2), "unit": "TFLOP/s"},
+               "roofline": roof, "cpu_baseline": cpu}
     elif args.workload == "lmce":
         from fp8_tensorwise_scaled_amd import api
 
@@ -290,6 +385,30 @@ def bench_other(args) -> int:
         ms = _time_steps(step, args.steps, args.warmup)
         tflops = w.flops / (ms * 1e-3) / 1e12
         log(f"LM head + CE: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s, loss {float(out['loss'][0]):.4f}")
+        # dominant kernel: one chunk's logits GEMM on the call's own codes
+        offs = api.lm_head_ce_layout(w.M, w.K, w.V, w.chunk)
+        xq = ws[offs[0]:offs[0] + w.M * w.K].view(w.M, w.K)[:w.chunk]
+        wq = ws[offs[2]:offs[2] + w.V * w.K].view(w.V, w.K)
+        zbuf = torch.empty((w.chunk, w.V), dtype=torch.bfloat16, device=dev)
+        sc = out["scales"]
+        us = 1e3 * _time_steps(lambda: api.fp8_linear_fwd(xq, sc[0:1], wq, sc[1:2], out=zbuf), args.gemm_reps, 3)
+        roof = _roofline(f"gemm_nt_kernel<0,0,256,BN,..,0> (E4M3 x E4M3; logits of one chunk, M={w.chunk} "
+                         f"N={w.V} K={w.K})", "mfma", 2 * w.chunk * w.V * w.K, us, PEAK_FP8_TFLOPS, "TFLOP/s")
+        log(f"chunk logits GEMM: {us:.1f} us, {roof['achieved']:.1f} TFLOP/s")
+        del zbuf
+        cpu = None
+        if not args.no_cpu_baseline:
+            import oracle
+
+            R = 128
+            t0 = time.perf_counter()
+            oracle.lm_head_ce(x[:R], wt, tg[:R], w.n_classes, w.softcap)
+            sec = time.perf_counter() - t0
+            cpu = {"value": 6 * R * w.K * w.V / sec / 1e12, "unit": "TFLOP/s",
+                   "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+                   "sample": f"the whole fused head + loss on the first {R} rows (quantisation of X rows and W, "
+                             f"logits, CE, both gradient GEMMs; {sec:.1f} s)"}
+            log(f"oracle: {sec:.1f} s")
         res = {"metric": "FP8 LM head fused with softcapped cross-entropy, fwd+bwd TFLOP/s",
                "value": round(tflops, 2), "ms_per_step": round(ms, 4),
                "data": "synthetic (seeded N(0,1) X, N(0,0.02) W with zero padded rows, uniform targets, "
@@ -299,7 +418,8 @@ def bench_other(args) -> int:
                           "V": w.V, "chunk": w.chunk, "workspace_bytes": ws.numel(),
                           "logits_bytes_if_materialised": 2 * w.M * w.V},
                "pct_of_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
-               "tokens_per_s_equiv": round(w.M / (ms * 1e-3))}
+               "tokens_per_s_equiv": round(w.M / (ms * 1e-3)),
+               "roofline": roof, "cpu_baseline": cpu}
     else:
         w = synth.LM_HEAD_PADDED
         n = synth.LM_HEAD_UNPADDED.N
