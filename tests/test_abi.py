@@ -99,6 +99,10 @@ def test_gemm_validation():
     assert L.fp8_linear_fwd(*a) == 5
     a = list(base); a[5] = 1 << 24
     assert L.fp8_linear_fwd(*a) == 5
+    # the exact edge: with K = 4096, lda = 8,421,488 is the last accepted
+    # multiple of 16 (a GPU test runs it); 16 bytes more is refused
+    a = list(base); a[10] = 4096; a[1] = a[5] = 8_421_488 + 16
+    assert L.fp8_linear_fwd(*a) == 5
     # dgrad: reduction length is N (K argument is the output width)
     a = [FAKE, 40, 1, FAKE, FAKE, 40, 0, FAKE, 32, 40, 64, FAKE, 64, None]
     assert L.fp8_linear_dgrad(*a) == 5

@@ -108,6 +108,32 @@ def test_strided_output_and_operands():
     assert (Cb[:, N:] == 7).all()   # columns past N untouched
 
 
+def test_largest_operand_offsets():
+    """Operand rows spaced as far apart as the library accepts: a 256-row
+    tile spans (255 lda + K) < 2^31 bytes of 32-bit buffer offsets, and
+    lda = 8,421,488 is the largest multiple of 16 that fits with K = 4096
+    (16 bytes more is refused, tests/test_abi.py).  M = 300 and N = 200 give
+    a ragged second tile in both directions; the operands span 2.5 and
+    1.7 GB, the bytes between rows are never read."""
+    from fp8_tensorwise_scaled_amd import api
+
+    M, N, K, LD = 300, 200, 4096, 8_421_488
+    assert 255 * LD + K < 2 ** 31 <= 255 * (LD + 16) + K
+    qa, sa, qb, sb = quant_pair((M, K), (N, K), E4, E5, 4242)
+    dev = torch.device("cuda:0")
+    ra = torch.empty((M - 1) * LD + K, dtype=torch.uint8, device=dev)
+    rb = torch.empty((N - 1) * LD + K, dtype=torch.uint8, device=dev)
+    A = ra.as_strided((M, K), (LD, 1))
+    B = rb.as_strided((N, K), (LD, 1))
+    A.copy_(to_dev_u8(qa))
+    B.copy_(to_dev_u8(qb))
+    y = api.fp8_linear_fwd(A, scal(sa), B, scal(sb), E4, E5)
+    torch.cuda.synchronize()
+    check_gemm(bf16_bits(y), "nt", qa, E4, sa, qb, E5, sb, "largest offsets 300x200x4096")
+    del ra, rb, A, B
+    torch.cuda.empty_cache()
+
+
 def test_empty_sizes():
     """K = 0 writes the empty sum (+0) everywhere; M = 0 or N = 0 is a no-op.
     Each of the three GEMMs, with the oracle's result for the same shapes."""
