@@ -273,21 +273,44 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
         ++tile_parity;
       }
     } else {
-      // ragged or unaligned tile: element by element
-      for (int e = tid; e < kTR * kTC; e += kCastThreads) {
-        const int row = e / kTC, col = e % kTC;
-        if (r0 + row < rows && c0 + col < cols) {
-          const uint32_t bits = x[(r0 + row) * ldx + c0 + col];
-          float v;
+      // ragged or unaligned tile: element by element.  Each thread loads a
+      // batch of elements before it converts and stores any of them, so the
+      // batch's loads are in flight together (as far as the compiler knows
+      // the stores could alias x, which would otherwise serialise every load
+      // behind the previous store); the batch is small enough to leave the
+      // kernel's register budget unchanged.
+      constexpr int kElemBatch = MODE == kModeRmsNorm ? 2 : 4;
+      static_assert((kTR * kTC) % (kCastThreads * kElemBatch) == 0, "whole element batches");
+      const bool has_g = MODE == kModeRmsNorm && jb.gamma != nullptr;
+      for (int e0 = tid; e0 < kTR * kTC; e0 += kCastThreads * kElemBatch) {
+        uint32_t bits[kElemBatch];
+        float rs[kElemBatch], gm[kElemBatch];
+#pragma unroll
+        for (int u = 0; u < kElemBatch; ++u) {
+          const int e = e0 + u * kCastThreads;
+          const int row = e / kTC, col = e % kTC;
+          const bool ok = r0 + row < rows && c0 + col < cols;
+          bits[u] = ok ? x[(r0 + row) * ldx + c0 + col] : 0u;
           if constexpr (MODE == kModeRmsNorm) {
-            const bool has_g = jb.gamma != nullptr;
-            v = norm_value(bits, jb.rstd[r0 + row], has_g ? bf16_to_f32(jb.gamma[c0 + col]) : 1.0f, has_g);
-          } else {
-            v = cast_value<MODE>(bits);
+            rs[u] = ok ? jb.rstd[r0 + row] : 0.0f;
+            gm[u] = ok && has_g ? bf16_to_f32(jb.gamma[c0 + col]) : 1.0f;
           }
-          const uint32_t code = pack4_fp8<FMT>(div_rn(d, v), 0.f, 0.f, 0.f) & 0xFFu;
-          if (q) q[(r0 + row) * jb.ldq + c0 + col] = (uint8_t)code;
-          if (qt) qt[(c0 + col) * jb.ldqt + r0 + row] = (uint8_t)code;
+        }
+#pragma unroll
+        for (int u = 0; u < kElemBatch; ++u) {
+          const int e = e0 + u * kCastThreads;
+          const int row = e / kTC, col = e % kTC;
+          if (r0 + row < rows && c0 + col < cols) {
+            float v;
+            if constexpr (MODE == kModeRmsNorm) {
+              v = norm_value(bits[u], rs[u], gm[u], has_g);
+            } else {
+              v = cast_value<MODE>(bits[u]);
+            }
+            const uint32_t code = pack4_fp8<FMT>(div_rn(d, v), 0.f, 0.f, 0.f) & 0xFFu;
+            if (q) q[(r0 + row) * jb.ldq + c0 + col] = (uint8_t)code;
+            if (qt) qt[(c0 + col) * jb.ldqt + r0 + row] = (uint8_t)code;
+          }
         }
       }
     }
