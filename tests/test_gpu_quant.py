@@ -92,6 +92,49 @@ def test_unaligned_rows_full_tiles(fmt):
     check_against_oracle(x, fmt, ld=513, offset=3)   # whole tiles only, tensor ends mid-dword
 
 
+def test_more_than_2_31_elements():
+    """A [40000, 60000] tensor, 2.4e9 elements (4.8 GB): a seeded bf16 block
+    T [125, 600] repeated (neither period divides the 128 x 256 cast tiles),
+    and as the very last element, beyond element 2^31, -4 max|T|, which
+    alone sets amax.  Scale, amax, codes and transposed codes against the
+    oracle's quantisation of T's elements and that one."""
+    from fp8_tensorwise_scaled_amd import api
+
+    R, C, tr, tc = 40000, 60000, 125, 600
+    assert R * C > 2 ** 31 and R % tr == 0 and C % tc == 0
+    fmt = oracle.E5M2
+    T = synth.normal_bf16((tr, tc), 1.0, 77)
+    top = int((T & 0x7FFF).max())
+    last = (top + 0x100) | 0x8000  # exponent + 2: exactly -4 max|T|
+    vals = np.concatenate([T.ravel(), [last]]).astype(np.uint16).reshape(1, -1)
+    rq, rs, ra = oracle.quant(vals, fmt)
+    assert ra == 4 * float(synth.bf16_bits_to_f32(np.array([top], np.uint16))[0])
+
+    dev = torch.device("cuda:0")
+    x = to_dev_bf16(T).repeat(R // tr, C // tc)
+    x.view(torch.int16)[-1, -1] = last - 65536
+    q = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    qt = torch.empty((C, R), dtype=torch.uint8, device=dev)
+    _, _, s, a = api.fp8_amax_quant(x, fmt, q=q, qt=qt)
+    torch.cuda.synchronize()
+    del x
+    assert np.float32(f32(s)[0]) == np.float32(rs) and np.float32(f32(a)[0]) == np.float32(ra)
+    code_last = int(rq[0, -1])
+    assert int(q[-1, -1]) == code_last and int(qt[-1, -1]) == code_last
+    tq = torch.from_numpy(np.ascontiguousarray(rq[0, :-1].reshape(tr, tc))).to(dev)
+    q[-1, -1] = tq[-1, -1]  # the rest repeats T's codes
+    qt[-1, -1] = tq[-1, -1]
+    qv = q.view(R // tr, tr, C // tc, tc)
+    for i in range(0, R // tr, 40):
+        assert bool((qv[i:i + 40] == tq[None, :, None, :]).all()), ("q", i)
+    tqt = tq.t().contiguous()
+    qtv = qt.view(C // tc, tc, R // tr, tr)
+    for i in range(0, C // tc, 20):
+        assert bool((qtv[i:i + 20] == tqt[None, :, None, :]).all()), ("qt", i)
+    del q, qt, qv, qtv
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", [(0, 64), (64, 0), (0, 0)])
 def test_empty_tensor(fmt, shape):
