@@ -282,3 +282,38 @@ def test_matrix_core_group_truncation_is_within_bound():
     assert (np.abs(got - 0.96875) > 2.0 ** -8).all()           # a real deviation from the exact sum
     sabs = oracle.gemm_nt(a & 0x7F, E4, 1.0, b, E4, 1.0)
     assert (np.abs(got - 0.96875) <= gemm_bound(ref, sabs, 64)).all()
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4), (E4, E5), (E5, E5)])
+def test_subnormal_codes(fa, fb):
+    """Subnormal FP8 operands (exponent field 0) reach the matrix core as
+    their values, not flushed to zero: an all-subnormal GEMM and one where
+    half of the codes are subnormal, against the oracle within the GEMM
+    bound.  With unit scales the all-subnormal products are 2^-18 .. 2^-12
+    (E4M3) and their sums stay normal in bf16."""
+    from fp8_tensorwise_scaled_amd import api
+
+    rng = np.random.default_rng(31 + 2 * fa + fb)
+    M, N, K = 96, 80, 256
+
+    def subnormals(fmt, shape):
+        mant = 0x07 if fmt == E4 else 0x03
+        return (rng.integers(0, mant + 1, shape) | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+
+    def finite(fmt, shape):
+        c = rng.integers(0, 256, shape).astype(np.uint8)
+        nan = (c & 0x7F) == 0x7F if fmt == E4 else (c & 0x7C) == 0x7C
+        return np.where(nan, c & 0x80, c).astype(np.uint8)
+
+    sa_all, sb_all = subnormals(fa, (M, K)), subnormals(fb, (N, K))
+    assert all(oracle.decode(fa, int(c)) == 0 or abs(oracle.decode(fa, int(c))) < 2.0 ** -6 for c in np.unique(sa_all))
+    mask_a, mask_b = rng.integers(0, 2, (M, K)).astype(bool), rng.integers(0, 2, (N, K)).astype(bool)
+    mixed_a = np.where(mask_a, subnormals(fa, (M, K)), finite(fa, (M, K))).astype(np.uint8)
+    mixed_b = np.where(mask_b, subnormals(fb, (N, K)), finite(fb, (N, K))).astype(np.uint8)
+    for what, a, b in (("all subnormal", sa_all, sb_all), ("half subnormal", mixed_a, mixed_b)):
+        y = api.fp8_linear_fwd(to_dev_u8(a), scal(1.0), to_dev_u8(b), scal(1.0), fa, fb)
+        torch.cuda.synchronize()
+        got = bf16_bits(y)
+        check_gemm(got, "nt", a, fa, 1.0, b, fb, 1.0, f"{what} fmt {fa}{fb}")
+        if what == "all subnormal":
+            assert (bits_f64(got) != 0).mean() > 0.9  # not flushed
