@@ -19,7 +19,7 @@ Shapes follow the little-lm appendix configuration on the decomputer.nl page
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 import numpy as np
 

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from fp8_tensorwise_scaled_amd import synth
-from tests.gpu_util import bf16_bits, bits_f64, check_gemm, gemm_bound, gemm_close, to_dev_u8, within_floors
+from tests.gpu_util import bf16_bits, bits_f64, check_gemm, gemm_bound, to_dev_u8, within_floors
 
 pytestmark = pytest.mark.gpu
 E4, E5 = oracle.E4M3, oracle.E5M2

@@ -6,7 +6,6 @@ definition s = amax / fmax (bounded dequantised values, the amax element
 maps to the largest code, idempotence, sign symmetry, power-of-two scaling,
 per-element error bound of round-to-nearest).
 """
-import math
 
 import numpy as np
 import pytest

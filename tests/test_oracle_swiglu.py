@@ -3,7 +3,6 @@ derivative against torch fp64 autograd of silu(G) * U, closed forms, the
 fp64 two-term grad-input accumulation, and the quantised chain against the
 unquantised fp64 block within the FP8 budget, with planted mistakes."""
 import numpy as np
-import pytest
 import torch
 
 import oracle
