@@ -16,7 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     names = set()
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
-        src = open(h).read()
+        with open(h) as fh:
+            src = fh.read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**([a-z_][a-z0-9_]*)\s*\(", src, re.M):
             names.add(m.group(1))
