@@ -92,6 +92,10 @@ size_t fp8_amax_quant_workspace_bytes(int64_t rows, int64_t cols);
  * ragged edges) takes a correct element-wise path.
  * An empty tensor (rows == 0 or cols == 0) is valid: amax = 0, scale = 1,
  * no codes written.
+ * Non-finite inputs are outside the numeric contract (the pages' tensors
+ * are finite).  What is guaranteed: if x holds a NaN or an infinity, amax
+ * and scale come out non-finite (NaN orders above infinity), so a caller can
+ * detect an overflowed tensor from its scale; its codes are unspecified.
  */
 int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale,

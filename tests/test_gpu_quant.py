@@ -92,6 +92,25 @@ def test_unaligned_rows_full_tiles(fmt):
     check_against_oracle(x, fmt, ld=513, offset=3)   # whole tiles only, tensor ends mid-dword
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("bad", [0x7FC0, 0xFFC1, 0x7F80, 0xFF80], ids=["nan", "-nan", "inf", "-inf"])
+def test_non_finite_input_gives_non_finite_scale(fmt, bad):
+    """Outside the numeric contract, one guarantee: a NaN or an infinity
+    anywhere in the tensor (here in the last row tile, past the first amax
+    block) makes amax and the scale non-finite, NaN winning over infinity.
+    The call completes; the codes are not checked."""
+    x = synth.normal_bf16((300, 70000), 1.0, 61)
+    x[297, 69011] = bad
+    _, _, s, a = run_quant(x, fmt)
+    want_nan = (bad & 0x7F) != 0
+    assert not np.isfinite(s) and not np.isfinite(a), (s, a)
+    assert np.isnan(a) == want_nan and np.isnan(s) == want_nan, (s, a)
+    x[5, 3] = 0x7F80  # an infinity and a NaN together: NaN
+    if want_nan:
+        _, _, s, a = run_quant(x, fmt)
+        assert np.isnan(s) and np.isnan(a)
+
+
 def test_more_than_2_31_elements():
     """A [40000, 60000] tensor, 2.4e9 elements (4.8 GB): a seeded bf16 block
     T [125, 600] repeated (neither period divides the 128 x 256 cast tiles),
