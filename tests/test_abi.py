@@ -307,3 +307,28 @@ def test_binding_checks_caller_outputs():
         api._out(wide[:, :8], (4, 8), torch.bfloat16, cpu, "y", dense=True)
     with pytest.raises(ValueError):
         api._ws(torch.empty(16, dtype=torch.float32))
+
+
+def test_no_fallback_without_the_library_or_a_gpu():
+    """The product path has no CPU route: without the built library every
+    entry point raises ImportError, and host tensors are refused before any
+    call."""
+    import subprocess
+    import sys
+
+    code = (
+        "import torch\n"
+        "from fp8_tensorwise_scaled_amd import _native, api\n"
+        "_native.LIB_PATH = '/nonexistent/libfp8mlp.so'\n"
+        "_native._lib = None\n"
+        "try:\n"
+        "    _native.lib()\n"
+        "except ImportError as e:\n"
+        "    print('library:', 'no CPU fallback' in str(e))\n"
+        "try:\n"
+        "    api.fp8_amax_quant(torch.zeros((16, 16), dtype=torch.bfloat16))\n"
+        "except ValueError as e:\n"
+        "    print('host tensor:', 'no CPU path' in str(e))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "library: True" in r.stdout and "host tensor: True" in r.stdout, r.stdout + r.stderr
