@@ -437,6 +437,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   float p;
   if constexpr (FA == kBF16) p = g.alpha;
   else p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
+  // relu^2-max epilogue: the tile's max of H = RN_bf16(x), x = RN32(acc p),
+  // is RN_bf16 of the max of x (both roundings are monotone), so it is taken
+  // here on the fp32 values.  Accumulators of rows past M or columns past N
+  // are 0 (their operands load as zeros) and cannot raise a max that starts
+  // at 0, so they need no mask.
+  float hmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < G::FM; ++i) {
     const int row = wm * G::WM + i * 32 + frow;
@@ -446,8 +452,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
       for (int q = 0; q < 4; ++q) {
         const int col = wn * G::WN + j * 32 + q * 8 + fhalf * 4;
         const v16f& a = acc[i][j];
-        const __bf16 h0 = (__bf16)(a[4 * q + 0] * p), h1 = (__bf16)(a[4 * q + 1] * p);
-        const __bf16 h2 = (__bf16)(a[4 * q + 2] * p), h3 = (__bf16)(a[4 * q + 3] * p);
+        const float x0 = a[4 * q + 0] * p, x1 = a[4 * q + 1] * p, x2 = a[4 * q + 2] * p, x3 = a[4 * q + 3] * p;
+        if constexpr (EPI == kEpiRelu2Max)
+          hmax = __builtin_fmaxf(hmax, __builtin_fmaxf(__builtin_fmaxf(x0, x1), __builtin_fmaxf(x2, x3)));
+        const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+        const __bf16 h2 = (__bf16)x2, h3 = (__bf16)x3;
         v2u w;
         w[0] = (uint32_t)__builtin_bit_cast(unsigned short, h0) |
                ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
@@ -460,7 +469,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   __syncthreads();
   if constexpr (EPI == kEpiRelu2Bwd && !kEarlyH) load_h();
 
-  uint32_t mx = 0;  // epilogue max (bit pattern of a non-negative value)
+  // epilogue max: the fp32 bit pattern of a non-negative bf16 value
+  uint32_t mx = 0;
+  if constexpr (EPI == kEpiRelu2Max) {
+    const __bf16 hb = (__bf16)hmax;
+    mx = ((uint32_t)__builtin_bit_cast(unsigned short, hb) << 16) & 0x7FFFFFFFu;  // -0 -> +0
+  }
 #pragma unroll
   for (int it = 0; it < NCH; ++it) {
     const int id = tid + kThreads * it;
@@ -469,16 +483,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
     if (gr < g.M && gc < g.N) {
       v4u v = *reinterpret_cast<const v4u*>(smem + row * G::CLD + c8 * 16);
       const bool full = gc + 8 <= g.N && vec_c && vec_aux;
-      if constexpr (EPI == kEpiRelu2Max) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // bf16 pairs -> fp32 bit patterns; negatives (sign set) count as 0
-          const uint32_t lo = v[e] << 16, hi = v[e] & 0xFFFF0000u;
-          const bool ok_lo = full || gc + 2 * e < g.N, ok_hi = full || gc + 2 * e + 1 < g.N;
-          if (ok_lo && !(lo >> 31)) mx = mx > lo ? mx : lo;
-          if (ok_hi && !(hi >> 31)) mx = mx > hi ? mx : hi;
-        }
-      }
       if constexpr (EPI == kEpiRelu2Bwd) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
