@@ -469,8 +469,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   __syncthreads();
   if constexpr (EPI == kEpiRelu2Bwd && !kEarlyH) load_h();
 
-  // epilogue max: the fp32 bit pattern of a non-negative bf16 value
+  // epilogue max, as the partial's format wants it: relu^2-max the fp32 bit
+  // pattern of a non-negative bf16 value, relu^2-backward the bf16 magnitude
+  // bits.  The relu^2-backward max |dH| is likewise taken before rounding,
+  // max |RN_bf16(y)| = RN_bf16(max |y|); chunk elements past N hold y = 0.
   uint32_t mx = 0;
+  float dmax = 0.0f;
   if constexpr (EPI == kEpiRelu2Max) {
     const __bf16 hb = (__bf16)hmax;
     mx = ((uint32_t)__builtin_bit_cast(unsigned short, hb) << 16) & 0x7FFFFFFFu;  // -0 -> +0
@@ -492,12 +496,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
             const float h = bf16_to_f32((hv[it][e] >> (16 * hlf)) & 0xFFFFu);
             const float da = bf16_to_f32((v[e] >> (16 * hlf)) & 0xFFFFu);
             const float r = h > 0.0f ? h : 0.0f;
-            const __bf16 dh = (__bf16)((2.0f * r) * da);  // exact product, one rounding
-            const uint32_t bits = __builtin_bit_cast(unsigned short, dh);
-            out |= bits << (16 * hlf);
-            const bool ok = full || gc + 2 * e + hlf < g.N;
-            const uint32_t mag = bits & 0x7FFFu;
-            if (ok) mx = mx > mag ? mx : mag;
+            const float y = (2.0f * r) * da;  // exact product
+            dmax = __builtin_fmaxf(dmax, __builtin_fabsf(y));
+            const __bf16 dh = (__bf16)y;  // one rounding
+            out |= (uint32_t)__builtin_bit_cast(unsigned short, dh) << (16 * hlf);
           }
           v[e] = out;
         }
@@ -529,6 +531,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
           if (gc + e < g.N) g.c[gr * g.ldc + gc + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
       }
     }
+  }
+  if constexpr (EPI == kEpiRelu2Bwd) {
+    const __bf16 db = (__bf16)dmax;
+    mx = (uint32_t)__builtin_bit_cast(unsigned short, db) & 0x7FFFu;
   }
   if constexpr (EPI != kEpiStore) {
     mx = block_max_u32(mx, red);
