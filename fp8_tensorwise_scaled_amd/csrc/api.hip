@@ -105,7 +105,7 @@ size_t layout_sg_fwd(int64_t M, int64_t d, int64_t h, size_t* off) {
   const size_t sz[SF_COUNT] = {
       (size_t)(M * d), (size_t)(h * d), (size_t)(h * d), (size_t)(d * h), (size_t)(M * h) * 2, (size_t)(M * h),
       (size_t)amax_parts_for(M, d) * 4, (size_t)amax_parts_for(h, d) * 4, (size_t)amax_parts_for(h, d) * 4,
-      (size_t)amax_parts_for(d, h) * 4, (size_t)swiglu_parts_for(M * h) * 4};
+      (size_t)amax_parts_for(d, h) * 4, (size_t)gemm_swiglu_tiles(M, h) * 4};
   size_t o = 0;
   for (int i = 0; i < SF_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
   return o;
@@ -569,19 +569,18 @@ int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_
                       (uint32_t*)(w8 + off[SF_PWD]), amax_parts_for(d, h), kModePlain);
   if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 2. G and U, 3. A = silu(G) U with its amax partials
-  GemmArgs gg = gemm_args(xq, d, FP8MLP_E4M3, &sc[0], wgq, d, FP8MLP_E4M3, &sc[1], M, h, d, kEpiStore);
-  gg.c = sv->g; gg.ldc = h;
-  GemmArgs gu = gemm_args(xq, d, FP8MLP_E4M3, &sc[0], wuq, d, FP8MLP_E4M3, &sc[2], M, h, d, kEpiStore);
-  gu.c = sv->u; gu.ldc = h;
-  if (launch_gemm(gg, s) != hipSuccess || launch_gemm(gu, s) != hipSuccess) return FP8MLP_EHIP;
-  if (launch_swiglu_gate(sv->g, sv->u, a, M * h, pa, s) != hipSuccess) return FP8MLP_EHIP;
+  // 2. G, U and A = silu(G) U in one GEMM over the gate and up codes, with
+  //    the per-tile max |A| partials
+  GemmArgs gs = gemm_args(xq, d, FP8MLP_E4M3, &sc[0], wgq, d, FP8MLP_E4M3, &sc[1], M, h, d, kEpiSwiGLU);
+  gs.b2 = wuq; gs.sb2 = &sc[2];
+  gs.c = sv->g; gs.c2 = sv->u; gs.c3 = a; gs.ldc = h; gs.partials = pa;
+  if (launch_gemm(gs, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 4. Aq and its transpose, 5. Y = Aq . Wdq^T
+  // 3. Aq and its transpose, 4. Y = Aq . Wdq^T
   QuantBatch ba{};
   ba.njobs = 1;
-  ba.job[0] = make_job(a, M, h, h, FP8MLP_E4M3, aq, h, sv->aq_t, M, &sc[4], nullptr, pa, swiglu_parts_for(M * h),
-                       kModePlain);
+  ba.job[0] = make_job(a, M, h, h, FP8MLP_E4M3, aq, h, sv->aq_t, M, &sc[4], nullptr, pa,
+                       (int)gemm_swiglu_tiles(M, h), kModePlain);
   if (launch_cast(ba, s) != hipSuccess) return FP8MLP_EHIP;
   GemmArgs gy = gemm_args(aq, h, FP8MLP_E4M3, &sc[4], wdq, h, FP8MLP_E4M3, &sc[3], M, d, h, kEpiStore);
   gy.c = y; gy.ldc = d;

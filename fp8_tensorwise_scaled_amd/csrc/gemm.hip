@@ -39,6 +39,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "swiglu_math.h"
 
 namespace fp8mlp {
 
@@ -109,7 +110,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
     tm = first_m + (t % in_group) % gm;
     tn = (t % in_group) / gm;
   }
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  // kEpiSwiGLU: a tile's BN B rows are BN/2 rows of the gate weights and the
+  // same BN/2 rows of the up weights, so it covers BN/2 output columns
+  constexpr bool kSwiGLU = EPI == kEpiSwiGLU;
+  constexpr int BNO = kSwiGLU ? BN / 2 : BN;  // output columns per tile
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNO;
 
   // operand bytes per element: K, lda and ldb below are in bytes
   constexpr int ES = FA == kBF16 ? 2 : 1;
@@ -117,9 +122,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   const int K = (int)kelems * ES;
   const int64_t lda = g.lda * ES, ldb = g.ldb * ES;
   const int rows_a = (int)min<int64_t>(BM, g.M - m0);
-  const int rows_b = (int)min<int64_t>(BN, g.N - n0);
+  const int rows_b = (int)min<int64_t>(BNO, g.N - n0);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a + m0 * lda + kbeg * ES, (uint32_t)((rows_a - 1) * lda + K));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b + n0 * ldb + kbeg * ES, (uint32_t)((rows_b - 1) * ldb + K));
+  const __amdgpu_buffer_rsrc_t rb2 =
+      kSwiGLU ? make_rsrc(g.b2 + n0 * ldb + kbeg * ES, (uint32_t)((rows_b - 1) * ldb + K)) : rb;
 
   // Per-thread 16-byte chunks loaded each stage: chunk id = tid + THREADS*j,
   // row = id / 8, logical column chunk = id % 8 (eight lanes cover one
@@ -137,13 +144,19 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   const uint32_t lds0 = row0 * kBK + ((logical0 ^ swz(row0)) << 4);
 
   v4u stg[G::LOADS];  // one stage in flight in registers
+  // kEpiSwiGLU: B loads jj < B_LOADS/2 fill the gate half of the stage, the
+  // rest the up half, from the same rows of the other operand
+  static_assert(!kSwiGLU || (G::B_LOADS % 2 == 0 && (G::B_LOADS / 2) * kRowStep == BN / 2),
+                "each B load must lie in one half");
   auto gload_one = [&](int j, int kt) {
     const int k0 = kt * kBK;
     const bool is_a = j < G::A_LOADS;
-    const int jj = is_a ? j : j - G::A_LOADS;
+    const int jb = j - G::A_LOADS;
+    const bool up = kSwiGLU && !is_a && jb >= G::B_LOADS / 2;
+    const int jj = is_a ? j : (up ? jb - G::B_LOADS / 2 : jb);
     const uint32_t base = is_a ? goff_a + jj * gstep_a : goff_b + jj * gstep_b;
     const uint32_t off = (k0 + colk0 < K) ? base + k0 : 0x80000000u;  // out of range -> 0
-    stg[j] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra : rb, off, 0, 0);
+    stg[j] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra : (up ? rb2 : rb), off, 0, 0);
   };
   auto swrite_one = [&](int j, int buf) {
     const bool is_a = j < G::A_LOADS;
@@ -434,8 +447,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   if constexpr (kEarlyH) load_h();
 
   // scale, round to bf16 and stage the tile in LDS
+  static_assert(!kSwiGLU || G::WN * 2 == BN, "kEpiSwiGLU: one wave column per half");
   float p;
   if constexpr (FA == kBF16) p = g.alpha;
+  else if constexpr (kSwiGLU) p = (*g.sa) * (wn == 0 ? *g.sb : *g.sb2);  // gate or up half
   else p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
   // relu^2-max epilogue: the tile's max of H = RN_bf16(x), x = RN32(acc p),
   // is RN_bf16 of the max of x (both roundings are monotone), so it is taken
@@ -468,6 +483,56 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   }
   __syncthreads();
   if constexpr (EPI == kEpiRelu2Bwd && !kEarlyH) load_h();
+
+  if constexpr (kSwiGLU) {
+    // Chunk pairs: row id / CPH, gate chunk id % CPH of the staged row and
+    // the up chunk CPH chunks further along it.  G, U and A = RN_bf16(silu(G)
+    // U) are written; the partial is the tile's max |A| (bf16 bits).
+    constexpr int CPH = BN / 16;  // 16-byte chunks per half row
+    constexpr int NP = BM * CPH / kThreads;
+    static_assert(NP * kThreads == BM * CPH, "whole chunk pairs");
+    const bool vec3 = vec_c && ((reinterpret_cast<uintptr_t>(g.c2) & 15u) == 0) &&
+                      ((reinterpret_cast<uintptr_t>(g.c3) & 15u) == 0);
+    uint32_t amx = 0;
+#pragma unroll
+    for (int it = 0; it < NP; ++it) {
+      const int id = tid + kThreads * it;
+      const int row = id / CPH, c8 = id % CPH;
+      const int64_t gr = m0 + row, gc = n0 + c8 * 8;
+      if (gr < g.M && gc < g.N) {
+        const v4u gv = *reinterpret_cast<const v4u*>(smem + row * G::CLD + c8 * 16);
+        const v4u uv = *reinterpret_cast<const v4u*>(smem + row * G::CLD + (c8 + CPH) * 16);
+        v4u av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t a0 = swiglu_a_bits(bf16_to_f32(gv[e] & 0xFFFFu), bf16_to_f32(uv[e] & 0xFFFFu));
+          const uint32_t a1 = swiglu_a_bits(bf16_to_f32(gv[e] >> 16), bf16_to_f32(uv[e] >> 16));
+          av[e] = a0 | (a1 << 16);
+          if (gc + 2 * e < g.N) amx = amx > (a0 & 0x7FFFu) ? amx : (a0 & 0x7FFFu);
+          if (gc + 2 * e + 1 < g.N) amx = amx > (a1 & 0x7FFFu) ? amx : (a1 & 0x7FFFu);
+        }
+        const int64_t o = gr * g.ldc + gc;
+        if (gc + 8 <= g.N && vec3) {
+          *reinterpret_cast<v4u*>(g.c + o) = gv;
+          *reinterpret_cast<v4u*>(g.c2 + o) = uv;
+          *reinterpret_cast<v4u*>(g.c3 + o) = av;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (gc + e < g.N) {
+              const int sh = 16 * (e & 1);
+              g.c[o + e] = (uint16_t)(gv[e >> 1] >> sh);
+              g.c2[o + e] = (uint16_t)(uv[e >> 1] >> sh);
+              g.c3[o + e] = (uint16_t)(av[e >> 1] >> sh);
+            }
+          }
+        }
+      }
+    }
+    amx = block_max_u32(amx, red);
+    if (tid == 0) g.partials[t] = amx;
+    return;
+  }
 
   // epilogue max, as the partial's format wants it: relu^2-max the fp32 bit
   // pattern of a non-negative bf16 value, relu^2-backward the bf16 magnitude
@@ -544,7 +609,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
 
 template <int FA, int FB, int BM, int BN, int WGM, int WGN, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
-  const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
+  constexpr int BNO = EPI == kEpiSwiGLU ? BN / 2 : BN;  // output columns per tile
+  const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BNO - 1) / BNO);
   if (tiles_m == 0 || tiles_n == 0) return hipSuccess;  // empty output
   const int work = g.tri_tiles > 0 ? g.tri_tiles * (g.tri_tiles + 1) / 2 * g.ksplit : tiles_m * tiles_n;
   hipLaunchKernelGGL((gemm_nt_kernel<FA, FB, BM, BN, WGM, WGN, EPI>), dim3(work), dim3(64 * WGM * WGN), 0, st, g,
@@ -578,6 +644,13 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
   switch (g.epi) {
     case kEpiRelu2Max: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Max>(g, st);
     case kEpiRelu2Bwd: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Bwd>(g, st);
+    case kEpiSwiGLU:
+      // merged gate/up projection: E4M3 x E4M3 on 256x256 tiles (128 output columns)
+      if constexpr (FA == kE4M3 && FB == kE4M3 && BN == 256) {
+        return launch_cfg<FA, FB, 256, 256, 2, 2, kEpiSwiGLU>(g, st);
+      } else {
+        return hipErrorInvalidValue;
+      }
     case kEpiStoreF32:
     case kEpiAccF32:
       // fp32 outputs are only produced for E5M2 x E4M3 (gradient x activation)
@@ -601,8 +674,10 @@ hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
     // square 256x256 tiles for the upper-triangle mode (fp32 epilogue only)
     if (g.tri_tiles > 0) return launch_bn<FA, FB, 256, 2, 2>(g, st);
     return launch_bn<FA, FB, 192, 4, 2>(g, st);
-  } else
+  } else {
+    if (g.epi == kEpiSwiGLU) return launch_bn<FA, FB, 256, 2, 2>(g, st);
     return pick_bn(g.M, g.N) == 192 ? launch_bn<FA, FB, 192, 4, 2>(g, st) : launch_bn<FA, FB, 256, 2, 2>(g, st);
+  }
 }
 
 }  // namespace
@@ -612,6 +687,7 @@ int64_t gemm_num_tiles(int64_t M, int64_t N) {
   return ((M + 255) / 256) * ((N + bn - 1) / bn);
 }
 int64_t gemm_max_tiles(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
+int64_t gemm_swiglu_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 127) / 128); }
 
 // Work split of the symmetric product: enough K slices that the triangle's
 // tiles times the slices fill the 256 CUs about once, each slice at least

@@ -65,6 +65,12 @@ enum Epilogue : int {
   kEpiAccF32 = 4,     // Cf = RN32(Cf + RN32(p * acc))   (fp32 accumulation, cf)
   kEpiAxpby = 5,      // C = RN_bf16(fma(alpha, acc, RN32(beta * aux))), aux optional,
                       // optionally also C^T into ct   (bf16 operands only)
+  kEpiSwiGLU = 6,     // merged gate/up projection of the gated MLP: a tile covers
+                      // BN/2 output columns n; its first half multiplies B rows
+                      // of b (gate), its second half the same rows of b2 (up).
+                      // G = RN_bf16(RN32(sa sb) acc) -> c, U = RN_bf16(RN32(sa sb2)
+                      // acc) -> c2, A = RN_bf16(silu(G) U) -> c3 (all ldc);
+                      // partial[tile] = max |A| (bf16 bits)
 };
 
 struct GemmArgs {
@@ -87,6 +93,12 @@ struct GemmArgs {
   float alpha, beta;
   uint16_t* ct;  // kEpiAxpby: optional transposed copy of C ([N, M], ldct)
   int64_t ldct;
+  // kEpiSwiGLU: the up projection's codes [N, K] (ldb) and scale, and the U
+  // and A outputs ([M, N], ldc)
+  const uint8_t* b2;
+  const float* sb2;
+  uint16_t* c2;
+  uint16_t* c3;
   // Upper-triangle split-K mode (M == N, A and B the same matrix's rows):
   // tri_tiles > 0 is the number of 256-wide tile rows; work item w covers
   // triangle tile w / ksplit (tile row <= tile column) and the K range
@@ -98,6 +110,7 @@ struct GemmArgs {
 
 // Number of output tiles the GEMM will use (size of `partials`).
 int64_t gemm_num_tiles(int64_t M, int64_t N);
+int64_t gemm_swiglu_tiles(int64_t M, int64_t N);  // kEpiSwiGLU with N output columns
 int64_t gemm_max_tiles(int64_t M, int64_t N);  // upper bound over tile configurations
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 
@@ -117,11 +130,9 @@ int64_t lm_ce_max_vocab();  // largest vocabulary the row kernel takes
 hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, const float* loss_rows, int64_t M,
                                  const int32_t* n_valid, float* loss, hipStream_t st);
 
-// Gated (SwiGLU) MLP elementwise kernels (swiglu.hip); n = elements, n % 8 == 0,
-// dense tensors; one partial (max |.| as bf16 bits) per block.
+// Gated (SwiGLU) MLP backward elementwise kernel (swiglu.hip); n = elements,
+// n % 8 == 0, dense tensors; one partial (max |.| as bf16 bits) per block.
 int swiglu_parts_for(int64_t n);
-hipError_t launch_swiglu_gate(const uint16_t* g, const uint16_t* u, uint16_t* a, int64_t n, uint32_t* partials,
-                              hipStream_t st);
 hipError_t launch_swiglu_gate_bwd(const uint16_t* g, const uint16_t* u, const uint16_t* da, uint16_t* dg,
                                   uint16_t* du, int64_t n, uint32_t* pg, uint32_t* pu, hipStream_t st);
 // dst = RN_bf16(src) over n elements (n % 8 == 0); src == nullptr writes zeros.

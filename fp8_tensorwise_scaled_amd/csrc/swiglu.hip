@@ -1,4 +1,4 @@
-// Elementwise kernels of the gated (SwiGLU) MLP block on gfx950.
+// Elementwise backward kernel of the gated (SwiGLU) MLP block on gfx950.
 //
 // The pages replaced this block by the non-gated relu^2 MLP (decomputer.nl,
 // "Het trainen van een 3.8B LLM tot 0.384 CORE voor $998", "Doorvoer
@@ -6,6 +6,7 @@
 // SwiGLU intermediate ratio of 2.75 replaced by 4x); the gated form runs here
 // through the same FP8 linears so the two can be compared on MI355X.
 //   forward:   A  = RN_bf16(silu(G) U),            silu(g) = g sigmoid(g)
+//              (applied in the epilogue of the merged G/U GEMM, gemm.hip)
 //   backward:  dG = RN_bf16(dA U silu'(G)),        silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g)))
 //              dU = RN_bf16(dA silu(G))
 // in fp32, with each output's per-block max |.| (bf16 magnitude bits) for the
@@ -13,6 +14,7 @@
 // per step, grid-stride over the dense [M, h] tensors.
 #include "device_common.h"
 #include "internal.h"
+#include "swiglu_math.h"
 
 namespace fp8mlp {
 
@@ -20,38 +22,8 @@ namespace {
 
 constexpr int kGateThreads = 256;
 
-__device__ __forceinline__ float sigmoid_f(float g) {
-  // 1 / (1 + e^-g); e^-g = +inf for very negative g gives 0
-  return __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
-
 __device__ __forceinline__ float lo16(uint32_t w) { return bf16_to_f32(w & 0xFFFFu); }
 __device__ __forceinline__ float hi16(uint32_t w) { return bf16_to_f32(w >> 16); }
-
-__global__ void __launch_bounds__(kGateThreads) swiglu_gate_kernel(const uint16_t* g, const uint16_t* u,
-                                                                   uint16_t* a, int64_t n, uint32_t* partials) {
-  __shared__ uint32_t red[kGateThreads / 64];
-  uint32_t m = 0;
-  const int64_t n8 = n / 8;
-  for (int64_t i = (int64_t)blockIdx.x * kGateThreads + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kGateThreads) {
-    const v4u gv = reinterpret_cast<const v4u*>(g)[i];
-    const v4u uv = reinterpret_cast<const v4u*>(u)[i];
-    v4u o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float g0 = lo16(gv[k]), g1 = hi16(gv[k]);
-      const uint32_t a0 = f32_to_bf16_rne(g0 * sigmoid_f(g0) * lo16(uv[k]));
-      const uint32_t a1 = f32_to_bf16_rne(g1 * sigmoid_f(g1) * hi16(uv[k]));
-      o[k] = a0 | (a1 << 16);
-      const uint32_t m0 = a0 & 0x7FFFu, m1 = a1 & 0x7FFFu;
-      m = m > m0 ? m : m0;
-      m = m > m1 ? m : m1;
-    }
-    reinterpret_cast<v4u*>(a)[i] = o;
-  }
-  m = block_max_u32(m, red);
-  if (threadIdx.x == 0) partials[blockIdx.x] = m;
-}
 
 __global__ void __launch_bounds__(kGateThreads) swiglu_gate_bwd_kernel(const uint16_t* g, const uint16_t* u,
                                                                        const uint16_t* da, uint16_t* dg,
@@ -100,13 +72,6 @@ __global__ void __launch_bounds__(kGateThreads) swiglu_gate_bwd_kernel(const uin
 int swiglu_parts_for(int64_t n) {
   const int64_t b = (n / 8 + kGateThreads * 4 - 1) / (kGateThreads * 4);  // ~4 steps per thread
   return (int)(b < 1 ? 1 : (b > 1024 ? 1024 : b));
-}
-
-hipError_t launch_swiglu_gate(const uint16_t* g, const uint16_t* u, uint16_t* a, int64_t n, uint32_t* partials,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(swiglu_gate_kernel, dim3(swiglu_parts_for(n)), dim3(kGateThreads), 0, st, g, u, a, n,
-                     partials);
-  return hipGetLastError();
 }
 
 hipError_t launch_swiglu_gate_bwd(const uint16_t* g, const uint16_t* u, const uint16_t* da, uint16_t* dg,
