@@ -306,17 +306,21 @@ def bench_other(args) -> int:
         ms = _time_steps(step, args.steps, args.warmup)
         tflops = w.flops / (ms * 1e-3) / 1e12
         log(f"SwiGLU block: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
-        # dominant kernel: the gate projection G = Xq Wgq^T on the block's own codes
+        # dominant kernel: the merged gate/up projection (G, U and A from one
+        # GEMM, as in the block's forward) on the block's own codes
         offs = api.swiglu_workspace_layout("fwd", M, d, h)
         xq = ws_f[offs[0]:offs[0] + M * d].view(M, d)
         wgq = ws_f[offs[1]:offs[1] + h * d].view(h, d)
-        gbuf = torch.empty((M, h), dtype=torch.bfloat16, device=dev)
-        us = 1e3 * _time_steps(lambda: api.fp8_linear_fwd(xq, saved.scales[0:1], wgq, saved.scales[1:2], out=gbuf),
-                               args.gemm_reps, 3)
-        roof = _roofline(f"gemm_nt_kernel<0,0,256,BN,..,0> (E4M3 x E4M3; gate projection M={M} N={h} K={d})",
-                         "mfma", 2 * M * h * d, us, PEAK_FP8_TFLOPS, "TFLOP/s")
-        log(f"gate projection GEMM: {us:.1f} us, {roof['achieved']:.1f} TFLOP/s")
-        del ws_f, ws_b, saved, gbuf
+        wuq = ws_f[offs[2]:offs[2] + h * d].view(h, d)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        gb, ub, ab = torch.empty((M, h), **bf), torch.empty((M, h), **bf), torch.empty((M, h), **bf)
+        sc = saved.scales
+        us = 1e3 * _time_steps(lambda: api.fp8_gated_linear_fwd(xq, sc[0:1], wgq, sc[1:2], wuq, sc[2:3],
+                                                                g=gb, u=ub, a=ab), args.gemm_reps, 3)
+        roof = _roofline(f"gemm_nt_kernel<0,0,256,256,2,2,6> (E4M3 x E4M3; merged gate/up projection with the gate "
+                         f"epilogue, M={M} N=2x{h} K={d})", "mfma", 2 * M * 2 * h * d, us, PEAK_FP8_TFLOPS, "TFLOP/s")
+        log(f"merged gate/up GEMM: {us:.1f} us, {roof['achieved']:.1f} TFLOP/s")
+        del ws_f, ws_b, saved, gb, ub, ab
         cpu = None
         if not args.no_cpu_baseline:
             import oracle

@@ -8,7 +8,7 @@ is imported lazily so that ``synth`` works without torch's GPU runtime.
 from __future__ import annotations
 
 _API_NAMES = (
-    "fp8_amax_quant", "fp8_linear_fwd", "fp8_linear_dgrad", "fp8_linear_wgrad",
+    "fp8_amax_quant", "fp8_linear_fwd", "fp8_linear_dgrad", "fp8_linear_wgrad", "fp8_gated_linear_fwd",
     "relu2_mlp_fwd", "relu2_mlp_bwd", "Relu2MlpSaved", "relu2_mlp_fwd_workspace",
     "relu2_mlp_bwd_workspace", "workspace_layout", "fp8_rmsnorm_quant", "fp8_lm_head_ce",
     "fp8_lm_head_ce_workspace", "lm_head_ce_layout", "swiglu_mlp_fwd", "swiglu_mlp_bwd", "SwigluMlpSaved",

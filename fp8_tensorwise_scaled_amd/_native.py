@@ -54,6 +54,7 @@ _PROTOS = {
     "swiglu_mlp_fwd": (c_int, [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(SwigluMlpSaved), vp, szt, vp]),
     "swiglu_mlp_bwd": (c_int, [vp, ctypes.POINTER(SwigluMlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, vp, szt,
                                vp]),
+    "fp8_gated_linear_fwd": (c_int, [vp, i64, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, i64, vp]),
     "bf16_gemm_nt": (c_int, [vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float, vp, i64, vp, i64, vp,
                              i64, vp]),
     "bf16_gemm_sym_workspace_bytes": (szt, [i64, i64]),

@@ -149,6 +149,28 @@ def fp8_linear_wgrad(dyqt, sdy, xqt, sx, fdy: int = E5M2, fx: int = E4M3, out=No
     return _gemm("fp8_linear_wgrad", dyqt, fdy, sdy, xqt, fx, sx, M, N, K, out, (N, K))
 
 
+def fp8_gated_linear_fwd(xq, sx, wgq, sg, wuq, su, *, g=None, u=None, a=None):
+    """The gated block's gate and up projections in one FP8 GEMM (E4M3 codes):
+    G = RN_bf16(RN32(sx*sg) Xq Wgq^T), U = RN_bf16(RN32(sx*su) Xq Wuq^T),
+    A = RN_bf16(silu(G) U).  Returns (g, u, a), each [M, N] bf16."""
+    _check_dev(xq, sx, wgq, sg, wuq, su)
+    M, K = xq.shape
+    N = wgq.shape[0]
+    if tuple(wuq.shape) != (N, K) or wgq.shape[1] != K:
+        raise ValueError("shapes: xq [M, K], wgq and wuq [N, K]")
+    if _ld(wuq) != _ld(wgq):
+        raise ValueError("wgq and wuq must share a leading dimension")
+    bf = torch.bfloat16
+    g = _out(g, (M, N), bf, xq.device, "g")
+    u = _out(u, (M, N), bf, xq.device, "u")
+    a = _out(a, (M, N), bf, xq.device, "a")
+    if not (_ld(g) == _ld(u) == _ld(a)):
+        raise ValueError("g, u and a must share a leading dimension")
+    _native.call("fp8_gated_linear_fwd", _p(xq), _ld(xq), _p(sx), _p(wgq), _p(sg), _p(wuq), _p(su), _ld(wgq),
+                 M, N, K, _p(g), _p(u), _p(a), _ld(g), _stream())
+    return g, u, a
+
+
 @dataclass
 class Relu2MlpSaved:
     """Forward quantities the backward pass reads (device tensors)."""

@@ -263,6 +263,23 @@ int fp8_linear_wgrad(const uint8_t* dyqt, int64_t lddyt, int fdy, const float* s
   return run_gemm(dyqt, lddyt, fdy, sdy, xqt, ldxt, fx, sx, N, K, M, dw, lddw, stream);
 }
 
+int fp8_gated_linear_fwd(const uint8_t* xq, int64_t ldx, const float* sx, const uint8_t* wgq, const float* sg,
+                         const uint8_t* wuq, const float* su, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                         uint16_t* g, uint16_t* u, uint16_t* a, int64_t ldo, void* stream) {
+  int st = check_gemm(xq, ldx, FP8MLP_E4M3, sx, wgq, ldw, FP8MLP_E4M3, sg, M, N, K, g, ldo);
+  if (st) return st;
+  if (!su) return FP8MLP_EINVAL;
+  if (M == 0 || N == 0) return FP8MLP_OK;
+  if (!u || !a) return FP8MLP_EINVAL;
+  if (!a2(u) || !a2(a)) return FP8MLP_EALIGN;
+  if (K > 0 && !wuq) return FP8MLP_EINVAL;
+  if (K > 0 && !a16(wuq)) return FP8MLP_EALIGN;
+  GemmArgs gs = gemm_args(xq, ldx, FP8MLP_E4M3, sx, wgq, ldw, FP8MLP_E4M3, sg, M, N, K, kEpiSwiGLU);
+  gs.b2 = wuq; gs.sb2 = su; gs.c = g; gs.c2 = u; gs.c3 = a; gs.ldc = ldo;
+  if (K == 0) gs.lda = gs.ldb = 0;  // operand descriptors cover no bytes: G = U = A = 0
+  return hip_status(launch_gemm(gs, (hipStream_t)stream));
+}
+
 size_t relu2_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h) {
   if (check_mlp_dims(M, d, h)) return 0;
   size_t off[F_COUNT];

@@ -530,7 +530,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
       }
     }
     amx = block_max_u32(amx, red);
-    if (tid == 0) g.partials[t] = amx;
+    if (tid == 0 && g.partials) g.partials[t] = amx;
     return;
   }
 

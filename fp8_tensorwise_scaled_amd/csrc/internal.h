@@ -70,7 +70,7 @@ enum Epilogue : int {
                       // of b (gate), its second half the same rows of b2 (up).
                       // G = RN_bf16(RN32(sa sb) acc) -> c, U = RN_bf16(RN32(sa sb2)
                       // acc) -> c2, A = RN_bf16(silu(G) U) -> c3 (all ldc);
-                      // partial[tile] = max |A| (bf16 bits)
+                      // partial[tile] = max |A| (bf16 bits) when partials is set
 };
 
 struct GemmArgs {

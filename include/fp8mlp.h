@@ -246,6 +246,22 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* saved, int64_t M,
                    uint16_t* dx, uint16_t* dw_gate, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* The gate and up projections of the gated block as one FP8 GEMM (the first
+ * step of swiglu_mlp_fwd, usable on its own).  For E4M3 codes Xq [M,K] and
+ * Wgq, Wuq [N,K] (one leading dimension ldw for both):
+ *   G = RN_bf16(RN32(sx*sg) Xq.Wgq^T),   U = RN_bf16(RN32(sx*su) Xq.Wuq^T),
+ *   A = RN_bf16(RN32(RN32(G sigmoid(G)) U))        (fp32 sigmoid),
+ * all [M,N] bf16 with leading dimension ldo.  Each output tile pairs 128
+ * rows of Wgq with the same rows of Wuq, so G, U and A leave one kernel.
+ * Requirements as for fp8_linear_fwd (K % 16 == 0, 16-byte aligned operands
+ * with leading dimensions that are multiples of 16); g, u and a 2-byte
+ * aligned (16-byte aligned with ldo % 8 == 0 for full-width stores), not
+ * overlapping each other or the operands.  M == 0 or N == 0 writes nothing;
+ * K == 0 writes zeros. */
+int fp8_gated_linear_fwd(const uint8_t* xq, int64_t ldx, const float* sx, const uint8_t* wgq, const float* sg,
+                         const uint8_t* wuq, const float* su, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                         uint16_t* g, uint16_t* u, uint16_t* a, int64_t ldo, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* FP8 LM head fused with the softcapped cross-entropy, chunked over rows.  */
 /*                                                                          */

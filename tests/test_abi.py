@@ -112,6 +112,26 @@ def test_gemm_validation():
     assert L.fp8_linear_wgrad(*a) == 5
 
 
+def test_gated_linear_validation():
+    L = _native.lib()
+    fn = L.fp8_gated_linear_fwd
+    base = [FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 32, 48, 64, FAKE, FAKE, FAKE, 48, None]
+    a = list(base); a[6] = None
+    assert fn(*a) == 1                              # no up scale
+    a = list(base); a[13] = None
+    assert fn(*a) == 1                              # no A output
+    a = list(base); a[5] = None
+    assert fn(*a) == 1                              # no up codes
+    a = list(base); a[5] = ctypes.c_void_p(0x10008)
+    assert fn(*a) == 2                              # up codes not 16-byte aligned
+    a = list(base); a[10] = 40; a[1] = a[7] = 48
+    assert fn(*a) == 5                              # K % 16
+    a = list(base); a[8] = 0
+    assert fn(*a) == 0                              # M = 0: nothing written
+    a = list(base); a[14] = 40
+    assert fn(*a) == 1                              # ldo < N
+
+
 def test_mlp_validation():
     L = _native.lib()
     assert L.relu2_mlp_fwd_workspace_bytes(2048, 768, 3072) > 2048 * 768 + 3072 * 768 * 2

@@ -121,3 +121,56 @@ def test_tiny_ragged_block():
     rows, cols = np.arange(w.M), np.arange(w.h)
     o = sc_.sampled_chain(g["x"], g["wg"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
     sc_.compare(g, o, sc, rows, cols)
+
+
+@pytest.mark.parametrize("M,N,K,ld_pad", [(300, 200, 160, 0), (256, 384, 512, 24), (96, 1000, 3072, 0)])
+def test_gated_linear_fwd(M, N, K, ld_pad):
+    """fp8_gated_linear_fwd on its own: G and U within the GEMM bound of the
+    oracle's products of the same codes; A within one bf16 ulp of the
+    oracle's gate applied to the GPU's own G and U (fp32 against fp64
+    evaluation), equal on at least 99.9%.  Ragged M and N (N = 200 leaves a
+    partial second 128-column tile); with ld_pad the outputs are strided and
+    the columns past N must stay untouched."""
+    from fp8_tensorwise_scaled_amd import api
+    from tests.gpu_util import check_gemm, to_dev_u8
+
+    E4 = oracle.E4M3
+    x = synth.normal_bf16((M, K), 1.0, 900 + M, outlier_frac=1e-3)
+    wg = synth.normal_bf16((N, K), 0.02, 901 + N)
+    wu = synth.normal_bf16((N, K), 0.02, 902 + N)
+    xq, sx, _ = oracle.quant(x, E4)
+    gq, sg, _ = oracle.quant(wg, E4)
+    uq, su, _ = oracle.quant(wu, E4)
+    dev = torch.device("cuda:0")
+    s = lambda v: torch.tensor([v], dtype=torch.float32, device=dev)
+    ld = N + ld_pad
+    bufs = [torch.full((M, ld), 7, dtype=torch.int16, device=dev).view(torch.bfloat16) for _ in range(3)]
+    g, u, a = api.fp8_gated_linear_fwd(to_dev_u8(xq), s(sx), to_dev_u8(gq), s(sg), to_dev_u8(uq), s(su),
+                                       g=bufs[0][:, :N], u=bufs[1][:, :N], a=bufs[2][:, :N])
+    torch.cuda.synchronize()
+    gb, ub, ab = bf16_bits(g), bf16_bits(u), bf16_bits(a)
+    check_gemm(gb, "nt", xq, E4, sx, gq, E4, sg, f"gated G {M}x{N}x{K}")
+    check_gemm(ub, "nt", xq, E4, sx, uq, E4, su, f"gated U {M}x{N}x{K}")
+    ref_a = oracle.swiglu_gate(gb, ub)
+    err = np.abs(bits_f64(ab) - bits_f64(ref_a))
+    assert (err <= ulp_bf16(bits_f64(ref_a))).all()
+    eq = float((ab == ref_a).mean())
+    print(f"[gated] {M}x{N}x{K}: A equal to the oracle gate on {eq:.6f}")
+    assert eq >= 0.999
+    if ld_pad:
+        for t in bufs:
+            assert (t.view(torch.int16)[:, N:] == 7).all()
+
+
+def test_gated_linear_fwd_empty_reduction():
+    """K = 0: G = U = 0 (empty sums) and A = silu(0) 0 = 0."""
+    from fp8_tensorwise_scaled_amd import api
+
+    dev = torch.device("cuda:0")
+    s = torch.ones(1, dtype=torch.float32, device=dev)
+    e = lambda r: torch.empty((r, 0), dtype=torch.uint8, device=dev)
+    g, u, a = api.fp8_gated_linear_fwd(e(40), s, e(24), s, e(24), s,
+                                       g=torch.full((40, 24), 7, dtype=torch.int16, device=dev).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    for t in (g, u, a):
+        assert (bf16_bits(t) == 0).all()
