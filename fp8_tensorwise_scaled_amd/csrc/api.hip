@@ -515,15 +515,21 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
     gd.b = wqt; gd.ldb = Vp; gd.fb = FP8MLP_E4M3; gd.sb = &sc[1];
     gd.M = rows; gd.N = K; gd.K = Vp; gd.c = dx + c0 * K; gd.ldc = K; gd.epi = kEpiStore;
     if (launch_gemm(gd, s) != hipSuccess) return FP8MLP_EHIP;
-    GemmArgs gw{};  // dW (+)= RN32(s_k sx) dZq_k^T . Xq_k   (fp32, reduction over the chunk's rows)
+    GemmArgs gw{};  // dW (+)= RN32(s_k sx) dZq_k^T . Xq_k   (reduction over the chunk's rows)
     gw.a = dzqt; gw.lda = C; gw.fa = FP8MLP_E5M2; gw.sa = &sc[2 + k];
     gw.b = xqt + c0; gw.ldb = M; gw.fb = FP8MLP_E4M3; gw.sb = &sc[0];
-    gw.M = V; gw.N = K; gw.K = rows; gw.cf = dwf; gw.ldc = K; gw.epi = k == 0 ? kEpiStoreF32 : kEpiAccF32;
+    gw.M = V; gw.N = K; gw.K = rows; gw.cf = dwf; gw.ldc = K;
+    // fp32 accumulation over the chunks; the last chunk adds its product and
+    // rounds the sum once to bf16 into dw (a single chunk rounds directly)
+    const bool last = c0 + C >= M;
+    gw.epi = !last ? (k == 0 ? kEpiStoreF32 : kEpiAccF32) : (k == 0 ? kEpiStore : kEpiAccF32Bf16);
+    if (last) gw.c = dw;
     if (launch_gemm(gw, s) != hipSuccess) return FP8MLP_EHIP;
   }
 
-  // 3. dW to bf16 (zeros without tokens) and the mean loss
-  return hip_status(launch_lm_ce_finalize(M > 0 ? dwf : nullptr, dw, V * K, loss_rows, M, nv, loss, s));
+  // 3. dW is zero without tokens; the mean loss
+  if (M == 0 && launch_f32_to_bf16(nullptr, dw, V * K, s) != hipSuccess) return FP8MLP_EHIP;
+  return hip_status(launch_lm_ce_loss(loss_rows, M, nv, loss, s));
 }
 
 size_t swiglu_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h) {
@@ -666,10 +672,11 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   // 7. dX = dGq . Wg + dUq . Wu, summed in fp32 and rounded once
   GemmArgs x1 = gemm_args(dgq, h, FP8MLP_E5M2, &bsc[1], sv->wgq_t, h, FP8MLP_E4M3, &sc[1], M, d, h, kEpiStoreF32);
   x1.cf = dxf; x1.ldc = d;
-  GemmArgs x2 = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->wuq_t, h, FP8MLP_E4M3, &sc[2], M, d, h, kEpiAccF32);
-  x2.cf = dxf; x2.ldc = d;
+  GemmArgs x2 = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->wuq_t, h, FP8MLP_E4M3, &sc[2], M, d, h,
+                          kEpiAccF32Bf16);  // adds to the first product and rounds once into dx
+  x2.cf = dxf; x2.c = dx; x2.ldc = d;
   if (launch_gemm(x1, s) != hipSuccess || launch_gemm(x2, s) != hipSuccess) return FP8MLP_EHIP;
-  return hip_status(launch_f32_to_bf16(M > 0 ? dxf : nullptr, dx, M * d, s));
+  return FP8MLP_OK;
 }
 
 int bf16_gemm_nt(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, int64_t M, int64_t N, int64_t K,

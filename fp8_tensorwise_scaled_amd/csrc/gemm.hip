@@ -378,11 +378,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
   // ---- fp32 epilogues: each lane writes its four consecutive columns of a
   // row straight from the accumulators (a 256-row fp32 tile would not fit in
   // LDS); the fp32 output is read-modify-written in place to accumulate.
-  if constexpr (EPI == kEpiStoreF32 || EPI == kEpiAccF32) {
+  if constexpr (EPI == kEpiStoreF32 || EPI == kEpiAccF32 || EPI == kEpiAccF32Bf16) {
     float p;
     if constexpr (FA == kBF16) p = g.alpha;
     else p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
-    const bool vec = ((reinterpret_cast<uintptr_t>(cfp) & 15u) == 0) && (g.ldc % 4 == 0);
+    const bool vec = ((reinterpret_cast<uintptr_t>(cfp) & 15u) == 0) && (g.ldc % 4 == 0) &&
+                     (EPI != kEpiAccF32Bf16 || (reinterpret_cast<uintptr_t>(g.c) & 7u) == 0);
 #pragma unroll
     for (int i = 0; i < G::FM; ++i) {
       const int64_t gr = m0 + wm * G::WM + i * 32 + frow;
@@ -395,7 +396,19 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_nt_kernel(GemmArgs g, 
           const v16f& a = acc[i][j];
           v4f v = {a[4 * q + 0] * p, a[4 * q + 1] * p, a[4 * q + 2] * p, a[4 * q + 3] * p};
           float* dst = cfp + gr * g.ldc + gc;
-          if (vec && gc + 4 <= g.N) {
+          if constexpr (EPI == kEpiAccF32Bf16) {
+            // the accumulated fp32 sum rounded once to bf16 (same ldc)
+            uint16_t* out = g.c + gr * g.ldc + gc;
+            if (vec && gc + 4 <= g.N) {
+              v += *reinterpret_cast<const v4f*>(dst);
+              *reinterpret_cast<v2u*>(out) = v2u{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                                 f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (gc + e < g.N) out[e] = (uint16_t)f32_to_bf16_rne(dst[e] + v[e]);
+            }
+          } else if (vec && gc + 4 <= g.N) {
             if constexpr (EPI == kEpiAccF32) v += *reinterpret_cast<const v4f*>(dst);
             *reinterpret_cast<v4f*>(dst) = v;
           } else {
@@ -653,10 +666,12 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
       }
     case kEpiStoreF32:
     case kEpiAccF32:
+    case kEpiAccF32Bf16:
       // fp32 outputs are only produced for E5M2 x E4M3 (gradient x activation)
       if constexpr (FA == kE5M2 && FB == kE4M3) {
-        return g.epi == kEpiStoreF32 ? launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStoreF32>(g, st)
-                                     : launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAccF32>(g, st);
+        if (g.epi == kEpiStoreF32) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStoreF32>(g, st);
+        if (g.epi == kEpiAccF32) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAccF32>(g, st);
+        return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAccF32Bf16>(g, st);
       } else {
         return hipErrorInvalidValue;
       }

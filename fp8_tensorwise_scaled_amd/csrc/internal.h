@@ -65,6 +65,8 @@ enum Epilogue : int {
   kEpiAccF32 = 4,     // Cf = RN32(Cf + RN32(p * acc))   (fp32 accumulation, cf)
   kEpiAxpby = 5,      // C = RN_bf16(fma(alpha, acc, RN32(beta * aux))), aux optional,
                       // optionally also C^T into ct   (bf16 operands only)
+  kEpiAccF32Bf16 = 7, // C = RN_bf16(RN32(Cf + RN32(p * acc)))  (reads cf, writes bf16 c;
+                      // the last of several fp32-accumulated products, ldc for both)
   kEpiSwiGLU = 6,     // merged gate/up projection of the gated MLP: a tile covers
                       // BN/2 output columns n; its first half multiplies B rows
                       // of b (gate), its second half the same rows of b2 (up).
@@ -125,10 +127,10 @@ hipError_t launch_softcap_ce(uint16_t* z, int64_t rows, int64_t V, int64_t ldz, 
                              float* loss_rows, uint32_t* partials, hipStream_t st);
 // Zero columns [c0, c1) of a [rows, ld] byte matrix.
 hipError_t launch_zero_cols(uint8_t* base, int64_t rows, int64_t ld, int64_t c0, int64_t c1, hipStream_t st);
-// dw = RN_bf16(dwf) over n elements; loss = sum(loss_rows) / n_valid (0 if none).
 int64_t lm_ce_max_vocab();  // largest vocabulary the row kernel takes
-hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, const float* loss_rows, int64_t M,
-                                 const int32_t* n_valid, float* loss, hipStream_t st);
+// loss = sum(loss_rows) / n_valid (0 if none).
+hipError_t launch_lm_ce_loss(const float* loss_rows, int64_t M, const int32_t* n_valid, float* loss,
+                             hipStream_t st);
 
 // Gated (SwiGLU) MLP backward elementwise kernel (swiglu.hip); n = elements,
 // n % 8 == 0, dense tensors; one partial (max |.| as bf16 bits) per block.

@@ -243,11 +243,8 @@ hipError_t launch_zero_cols(uint8_t* base, int64_t rows, int64_t ld, int64_t c0,
   return hipGetLastError();
 }
 
-hipError_t launch_lm_ce_finalize(const float* dwf, uint16_t* dw, int64_t n, const float* loss_rows, int64_t M,
-                                 const int32_t* n_valid, float* loss, hipStream_t st) {
-  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(grid_for(n / 8, 256)), dim3(256), 0, st, dwf, dw, n);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_lm_ce_loss(const float* loss_rows, int64_t M, const int32_t* n_valid, float* loss,
+                             hipStream_t st) {
   hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(256), 0, st, loss_rows, M, n_valid, loss);
   return hipGetLastError();
 }
