@@ -35,6 +35,13 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs; tile ids are
 //    remapped so each XCD works on a contiguous run of tiles, grouped 4 tile
 //    rows deep, so concurrently running tiles share operands in that XCD's L2.
+//  * Epilogues (enum Epilogue in internal.h): plain bf16 store; the relu^2
+//    block's relu^2-max and relu^2-backward fusions, whose tile maxima are
+//    taken on fp32 values before the (monotone) bf16 rounding; fp32 store and
+//    accumulate, and accumulate-then-round-to-bf16 for the last of several
+//    summed products; the gated block's merged gate/up projection with the
+//    gate applied; and, for bf16 operands, alpha/beta with an optional
+//    transposed store and the upper-triangle split-K mode.
 #include <type_traits>
 
 #include "device_common.h"
