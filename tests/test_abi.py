@@ -348,7 +348,13 @@ def test_no_fallback_without_the_library_or_a_gpu():
         "try:\n"
         "    api.fp8_amax_quant(torch.zeros((16, 16), dtype=torch.bfloat16))\n"
         "except ValueError as e:\n"
-        "    print('host tensor:', 'no CPU path' in str(e))\n")
+        "    print('host tensor:', 'no CPU path' in str(e))\n"
+        "from fp8_tensorwise_scaled_amd import modules\n"
+        "try:\n"
+        "    modules.fp8_linear(torch.zeros((16, 16), dtype=torch.bfloat16), torch.zeros((16, 16), dtype=torch.bfloat16))\n"
+        "except ValueError as e:\n"
+        "    print('module on host:', 'no CPU path' in str(e))\n")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert "library: True" in r.stdout and "host tensor: True" in r.stdout, r.stdout + r.stderr
+    assert "module on host: True" in r.stdout, r.stdout + r.stderr

@@ -1,0 +1,82 @@
+"""The autograd modules (fp8_tensorwise_scaled_amd/modules.py) are marshalling
+only: forward and backward through them give the same bytes as calling the
+C-ABI entry points directly, and a few optimiser steps reduce a loss."""
+import pytest
+import torch
+
+from fp8_tensorwise_scaled_amd import synth
+from tests.gpu_util import to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def test_relu2_mlp_module_matches_direct_calls():
+    from fp8_tensorwise_scaled_amd import api, modules
+
+    w = synth.MLPWorkload(61, 256, 128, 512, sigma_up=1 / 11, sigma_down=1 / 23)
+    x, wu, wd, dy = (to_dev_bf16(t) for t in w.tensors())
+    mod = modules.Relu2MLP(128, 512, device="cuda:0")
+    with torch.no_grad():
+        mod.w_up.copy_(wu)
+        mod.w_down.copy_(wd)
+    xin = x.reshape(4, 64, 128).clone().requires_grad_(True)  # leading dims are flattened to rows
+    y = mod(xin)
+    y.backward(dy.reshape(4, 64, 128))
+    torch.cuda.synchronize()
+    y_ref, saved = api.relu2_mlp_fwd(x, wu, wd)
+    dx_ref, dwu_ref, dwd_ref, _ = api.relu2_mlp_bwd(dy, saved)
+    torch.cuda.synchronize()
+    eq = lambda a, b: torch.equal(a.reshape(b.shape).view(torch.int16), b.view(torch.int16))
+    assert eq(y.detach(), y_ref) and eq(xin.grad, dx_ref)
+    assert eq(mod.w_up.grad, dwu_ref) and eq(mod.w_down.grad, dwd_ref)
+
+
+def test_fp8_linear_module_matches_direct_calls():
+    from fp8_tensorwise_scaled_amd import api, modules
+
+    x = to_dev_bf16(synth.normal_bf16((192, 256), 1.0, 62))
+    wt = to_dev_bf16(synth.normal_bf16((320, 256), 0.05, 63))
+    dy = to_dev_bf16(synth.normal_bf16((192, 320), 1e-3, 64))
+    lin = modules.FP8Linear(256, 320, device="cuda:0")
+    with torch.no_grad():
+        lin.weight.copy_(wt)
+    xin = x.reshape(3, 64, 256).clone().requires_grad_(True)
+    y = lin(xin)
+    y.backward(dy.reshape(3, 64, 320))
+    torch.cuda.synchronize()
+    xq, xqt, sx, _ = api.fp8_amax_quant(x, api.E4M3, want_qt=True)
+    wq, wqt, sw, _ = api.fp8_amax_quant(wt, api.E4M3, want_qt=True)
+    gq, gqt, sg, _ = api.fp8_amax_quant(dy, api.E5M2, want_qt=True)
+    y_ref = api.fp8_linear_fwd(xq, sx, wq, sw)
+    dx_ref = api.fp8_linear_dgrad(gq, sg, wqt, sw)
+    dw_ref = api.fp8_linear_wgrad(gqt, sg, xqt, sx)
+    torch.cuda.synchronize()
+    eq = lambda a, b: torch.equal(a.reshape(b.shape).view(torch.int16), b.view(torch.int16))
+    assert eq(y.detach(), y_ref) and eq(xin.grad, dx_ref) and eq(lin.weight.grad, dw_ref)
+
+
+def test_training_steps_reduce_the_loss():
+    """Thirty SGD steps (lr 0.05) of a relu^2 block plus an FP8 linear head
+    on a fixed seeded regression problem: the mean squared error stays
+    finite and falls (the same model in fp32 goes from 3.6 to 1.9)."""
+    from fp8_tensorwise_scaled_amd import modules
+
+    torch.manual_seed(65)
+    dev = torch.device("cuda:0")
+    x = torch.randn(512, 128, device=dev).to(torch.bfloat16)
+    target = torch.randn(512, 64, device=dev)
+    mlp = modules.Relu2MLP(128, 512, device=dev)
+    head = modules.FP8Linear(128, 64, device=dev)
+    params = list(mlp.parameters()) + list(head.parameters())
+    opt = torch.optim.SGD(params, lr=0.05)
+    losses = []
+    for _ in range(30):
+        opt.zero_grad()
+        out = head(x + mlp(x)).float()
+        loss = ((out - target) ** 2).mean()
+        loss.backward()
+        opt.step()
+        losses.append(float(loss.detach()))
+    print(f"[modules] loss {losses[0]:.4f} -> {losses[-1]:.4f}")
+    assert all(l == l and l < float("inf") for l in losses), losses
+    assert losses[-1] < 0.8 * losses[0]
