@@ -125,7 +125,8 @@ __device__ __forceinline__ float cast_value(uint32_t bits) {
 __device__ __forceinline__ float norm_value(uint32_t bits, float r, float g, bool has_g) {
   float y = bf16_to_f32(bits) * r;
   if (has_g) y = y * g;
-  return bf16_to_f32(f32_to_bf16_rne(y));
+  const __bf16 b = (__bf16)y;  // v_cvt_pk_bf16_f32: round to nearest even
+  return bf16_to_f32(__builtin_bit_cast(unsigned short, b));
 }
 
 template <int FMT>
@@ -318,11 +319,15 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
 }
 
 // RMSNorm statistics (RMSNorm of the decomputer.nl appendix, applied before
-// the MLP's input quantisation): one wave per row, kRmsRows rows per block;
-// rows of up to 4096 columns are read once and kept in registers.
+// the MLP's input quantisation): each wave takes two rows, kRmsRows rows per
+// block; rows of up to 4096 columns are read once, both rows' loads in flight
+// together, and kept in registers.
 //   ms = RN32(RN64(sum x^2 / d))  (fp64 sum)   r = RN32(1 / RN32(sqrt(RN32(ms + eps))))
-// rstd[row] = r; the block's partial is the max of |RN_bf16(RN32(RN32(x r) g))|.
-constexpr int kRmsRows = 8;      // two rows per wave
+// rstd[row] = r; the block's partial is the max of |RN_bf16(RN32(RN32(x r) g))|,
+// taken as RN_bf16 of the largest |RN32(RN32(x r) g)| (rounding to bf16 is
+// monotone and odd), an integer max of the fp32 magnitude bits.
+constexpr int kRmsRowsPerWave = 2;
+constexpr int kRmsRows = 4 * kRmsRowsPerWave;  // four waves per block
 constexpr int kRmsRegChunks = 8;  // rows of up to 64 x 8 x 8 = 4096 columns stay in registers
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -344,6 +349,29 @@ __device__ __forceinline__ uint32_t norm_max8(v4u v, float r, v4u gv, bool has_g
   return m;
 }
 
+// Largest fp32 magnitude bits of RN32(RN32(x r) g) over 8 columns; gf holds
+// the 8 weights as fp32 (all 1 without a weight: the product is then exact).
+__device__ __forceinline__ uint32_t norm_maxbits8(v4u v, float r, const float gf[8], uint32_t m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16) * r * gf[2 * i];
+    const float hi = __uint_as_float(v[i] & 0xFFFF0000u) * r * gf[2 * i + 1];
+    const uint32_t a = __float_as_uint(lo) & 0x7FFFFFFFu, b = __float_as_uint(hi) & 0x7FFFFFFFu;
+    m = max(m, max(a, b));
+  }
+  return m;
+}
+
+__device__ __forceinline__ double sumsq8(v4u v, double ss) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xFFFF0000u);
+    ss = __builtin_fma(lo, lo, ss);  // lo * lo is exact in fp64
+    ss = __builtin_fma(hi, hi, ss);
+  }
+  return ss;
+}
+
 __device__ __forceinline__ v4u load_g8(const uint16_t* g, int64_t col, bool g_vec) {
   if (!g) return v4u{0u, 0u, 0u, 0u};
   if (g_vec) return *reinterpret_cast<const v4u*>(g + col);
@@ -353,38 +381,75 @@ __device__ __forceinline__ v4u load_g8(const uint16_t* g, int64_t col, bool g_ve
   return o;
 }
 
+// IN_REGS (rows of at most 4096 columns, 16-byte aligned, as the host checks)
+// is its own instance so that the register-resident path's registers do not
+// lower the occupancy of the streaming path for longer rows.
+template <bool IN_REGS>
 __global__ void __launch_bounds__(256) rmsnorm_amax_kernel(QuantJob jb, float eps, float* rstd) {
   __shared__ uint32_t red[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave: keep it (and the row descriptors) scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rows = jb.rows, cols = jb.cols, ldx = jb.ldx;
   const uint16_t* x = jb.x;
   const uint16_t* g = jb.gamma;
   const bool vec = aligned16(x) && (ldx % 8 == 0) && (cols % 8 == 0);
-  const bool in_regs = vec && cols <= 64 * 8 * kRmsRegChunks;
+  const bool in_regs = IN_REGS;
   const bool g_vec = g != nullptr && aligned16(g);
   const int64_t nch = cols / 8;
   uint32_t m = 0;
-  for (int rr = wave; rr < kRmsRows; rr += 4) {
+  if (in_regs) {
+    // this wave's rows base + wave + 4 i; the later ones may lie past the end
+    // (a wave-uniform test); buffer loads past a row's end, or of a missing
+    // row, return zeros
+    const uint32_t row_bytes = (uint32_t)(2 * cols);
+    int64_t row[kRmsRowsPerWave];
+    bool has[kRmsRowsPerWave];
+    v4u buf[kRmsRowsPerWave][kRmsRegChunks];
+#pragma unroll
+    for (int i = 0; i < kRmsRowsPerWave; ++i) {
+      row[i] = (int64_t)blockIdx.x * kRmsRows + wave + 4 * i;
+      has[i] = row[i] < rows;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + (has[i] ? row[i] : 0) * ldx, has[i] ? row_bytes : 0u);
+#pragma unroll
+      for (int k = 0; k < kRmsRegChunks; ++k)
+        buf[i][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16u * (uint32_t)(lane + 64 * k), 0, 0);
+    }
+    float r[kRmsRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRmsRowsPerWave; ++i) {
+      double ss = 0.0;
+#pragma unroll
+      for (int k = 0; k < kRmsRegChunks; ++k) ss = sumsq8(buf[i][k], ss);
+      ss = wave_sum_f64(ss);
+      // correctly rounded square root and division
+      r[i] = 1.0f / sqrtf((float)(ss / (double)cols) + eps);
+      if (lane == 0 && has[i]) rstd[row[i]] = r[i];
+    }
+    uint32_t mb = 0;  // fp32 magnitude bits
+#pragma unroll
+    for (int k = 0; k < kRmsRegChunks; ++k) {
+      const int64_t c = lane + 64 * k;
+      if (c < nch) {
+        float gf[8];
+        const v4u gv = load_g8(g, 8 * c, g_vec);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gf[2 * e] = g ? __uint_as_float(gv[e] << 16) : 1.0f;
+          gf[2 * e + 1] = g ? __uint_as_float(gv[e] & 0xFFFF0000u) : 1.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kRmsRowsPerWave; ++i)
+          if (has[i]) mb = norm_maxbits8(buf[i][k], r[i], gf, mb);
+      }
+    }
+    m = f32_to_bf16_rne(__uint_as_float(mb)) & 0x7FFFu;
+  }
+  for (int rr = wave; rr < kRmsRows && !in_regs; rr += 4) {
     const int64_t row = (int64_t)blockIdx.x * kRmsRows + rr;
     if (row >= rows) break;
     const uint16_t* xr = x + row * ldx;
     double ss = 0.0;
-    v4u buf[kRmsRegChunks];
-    if (in_regs) {
-#pragma unroll
-      for (int k = 0; k < kRmsRegChunks; ++k) {
-        const int64_t c = lane + 64 * k;
-        buf[k] = c < nch ? *reinterpret_cast<const v4u*>(xr + 8 * c) : v4u{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int k = 0; k < kRmsRegChunks; ++k) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double f = bf16_to_f32((buf[k][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          ss += f * f;
-        }
-      }
-    } else if (vec) {
+    if (vec) {
       for (int64_t c = lane; c < nch; c += 64) {
         const v4u v = *reinterpret_cast<const v4u*>(xr + 8 * c);
 #pragma unroll
@@ -403,13 +468,7 @@ __global__ void __launch_bounds__(256) rmsnorm_amax_kernel(QuantJob jb, float ep
     const float ms = (float)(ss / (double)cols);
     const float r = 1.0f / sqrtf(ms + eps);  // correctly rounded square root and division
     if (lane == 0) rstd[row] = r;
-    if (in_regs) {
-#pragma unroll
-      for (int k = 0; k < kRmsRegChunks; ++k) {
-        const int64_t c = lane + 64 * k;
-        if (c < nch) m = norm_max8(buf[k], r, load_g8(g, 8 * c, g_vec), g != nullptr, m);
-      }
-    } else if (vec) {
+    if (vec) {
       for (int64_t c = lane; c < nch; c += 64)
         m = norm_max8(*reinterpret_cast<const v4u*>(xr + 8 * c), r, load_g8(g, 8 * c, g_vec), g != nullptr, m);
     } else {
@@ -495,7 +554,12 @@ int rmsnorm_parts_for(int64_t rows) {
 hipError_t launch_rmsnorm_amax(QuantJob& j, float eps, float* rstd, hipStream_t st) {
   j.blk_begin = 0;
   j.nblocks = rmsnorm_parts_for(j.rows);
-  hipLaunchKernelGGL(rmsnorm_amax_kernel, dim3(j.nblocks), dim3(256), 0, st, j, eps, rstd);
+  const bool in_regs = (reinterpret_cast<uintptr_t>(j.x) & 15u) == 0 && j.ldx % 8 == 0 && j.cols % 8 == 0 &&
+                       j.cols <= 64 * 8 * kRmsRegChunks;
+  if (in_regs)
+    hipLaunchKernelGGL(rmsnorm_amax_kernel<true>, dim3(j.nblocks), dim3(256), 0, st, j, eps, rstd);
+  else
+    hipLaunchKernelGGL(rmsnorm_amax_kernel<false>, dim3(j.nblocks), dim3(256), 0, st, j, eps, rstd);
   return hipGetLastError();
 }
 

@@ -35,6 +35,9 @@ def run(x, g, eps, fmt, ld=None):
     ((300, 700), 701, True, E4),        # ragged tiles, odd leading dimension
     ((256, 512), None, True, E5),
     ((17, 3072), None, True, E4),       # fewer rows than one statistics block
+    ((33, 1000), None, True, E5),       # rows in registers, 125 16-byte chunks (not whole waves)
+    ((40, 5120), None, True, E4),       # rows longer than the register path takes
+    ((6, 4096), None, False, E4),       # the longest rows the register path takes; one block
 ])
 def test_bit_exact(shape, ld, with_g, fmt):
     x = synth.normal_bf16(shape, 2.5, 91, outlier_frac=1e-3)
