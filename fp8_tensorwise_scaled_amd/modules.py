@@ -36,11 +36,12 @@ class _Fp8LinearFn(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dy):
         xqt, sx, wqt, sw = ctx.saved_tensors
+        need_dx, need_dw = ctx.needs_input_grad
         dy2 = _rows(dy.to(torch.bfloat16))
-        gq, gqt, sg, _ = api.fp8_amax_quant(dy2, api.E5M2, want_qt=True)
-        dx = api.fp8_linear_dgrad(gq, sg, wqt, sw)
-        dw = api.fp8_linear_wgrad(gqt, sg, xqt, sx)
-        return dx.reshape(ctx.x_shape), dw
+        gq, gqt, sg, _ = api.fp8_amax_quant(dy2, api.E5M2, want_q=need_dx, want_qt=need_dw)
+        dx = api.fp8_linear_dgrad(gq, sg, wqt, sw).reshape(ctx.x_shape) if need_dx else None
+        dw = api.fp8_linear_wgrad(gqt, sg, xqt, sx) if need_dw else None
+        return dx, dw
 
 
 class _Relu2MlpFn(torch.autograd.Function):
@@ -56,6 +57,9 @@ class _Relu2MlpFn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, dy):
+        if ctx.saved is None:
+            raise RuntimeError("relu2_mlp: the saved FP8 codes are released by the first backward; "
+                               "a second backward through the same forward is not supported")
         dx, dw_up, dw_down, _ = api.relu2_mlp_bwd(_rows(dy.to(torch.bfloat16)), ctx.saved)
         ctx.saved = None
         return dx.reshape(ctx.x_shape), dw_up, dw_down

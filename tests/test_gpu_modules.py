@@ -54,6 +54,29 @@ def test_fp8_linear_module_matches_direct_calls():
     eq = lambda a, b: torch.equal(a.reshape(b.shape).view(torch.int16), b.view(torch.int16))
     assert eq(y.detach(), y_ref) and eq(xin.grad, dx_ref) and eq(lin.weight.grad, dw_ref)
 
+    # an input that needs no gradient: only the weight gradient is computed, same bytes
+    lin.weight.grad = None
+    lin(x.reshape(3, 64, 256)).backward(dy.reshape(3, 64, 320))
+    torch.cuda.synchronize()
+    assert eq(lin.weight.grad, dw_ref)
+    # a frozen weight: only the input gradient
+    lin.weight.requires_grad_(False)
+    xin2 = x.reshape(3, 64, 256).clone().requires_grad_(True)
+    lin(xin2).backward(dy.reshape(3, 64, 320))
+    torch.cuda.synchronize()
+    assert eq(xin2.grad, dx_ref)
+
+
+def test_relu2_mlp_second_backward_is_refused():
+    from fp8_tensorwise_scaled_amd import modules
+
+    mod = modules.Relu2MLP(128, 512, device="cuda:0")
+    x = torch.randn(64, 128, device="cuda:0").to(torch.bfloat16).requires_grad_(True)
+    y = mod(x).float().sum()
+    y.backward(retain_graph=True)
+    with pytest.raises(RuntimeError, match="second backward"):
+        y.backward()
+
 
 def test_training_steps_reduce_the_loss():
     """Thirty SGD steps (lr 0.05) of a relu^2 block plus an FP8 linear head
