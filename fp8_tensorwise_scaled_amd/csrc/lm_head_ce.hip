@@ -29,6 +29,8 @@ namespace {
 constexpr int kCeThreads = 512;
 constexpr int64_t kMaxVocab = int64_t{1} << 22;  // columns per row (int offsets, tile ranges)
 constexpr float kLog2e = 1.4426950408889634f;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -66,12 +68,10 @@ __global__ void __launch_bounds__(256) count_valid_kernel(const int32_t* targets
 
 // One block per row, two sweeps over it: the sum of exp(S - c), then dZ
 // written over the logits (the second sweep reads the row again, from L2,
-// and recomputes tanh: keeping tanh in registers between the sweeps measured
-// slower, its 150 registers per lane cost more occupancy than the work saved).
-// Each element costs two exp2 and one reciprocal per sweep, with constants
-// folded:
-//   th = tanh(z / c) = (e - 1) / (e + 1),  e = exp2(clamp(z * 2 log2(e) / c))
-//   exp(c th - m) = exp2(c log2(e) th - m log2(e))
+// and recomputes its terms: keeping them in registers between the sweeps
+// measured slower, the registers cost more occupancy than the work saved).
+// The kernel is bound by its per-element VALU work, so tanh is never formed:
+// everything is written in terms of e = exp(2 z / c) and w = 1 / (e + 1).
 __global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int64_t V, int64_t ldz,
                                                                 int64_t n_classes, float softcap,
                                                                 const int32_t* targets, const int32_t* n_valid,
@@ -99,74 +99,97 @@ __global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int
     return;
   }
 
-  const float k2 = 2.0f * kLog2e / softcap;  // z -> 2 log2(e) z / c
-  const float clampv = 40.0f * kLog2e;        // |z / c| <= 20: tanh is 1 to fp32 precision beyond
-  const float cl = softcap * kLog2e;
-  auto tanh_of = [&](uint32_t bits) {
-    const float y = __builtin_fminf(__builtin_fmaxf(bf16_to_f32(bits) * k2, -clampv), clampv);
-    const float e = __builtin_amdgcn_exp2f(y);
-    return (e - 1.0f) * __builtin_amdgcn_rcpf(e + 1.0f);
+  // With e = exp(2 z / c) (clamped where tanh is 1 to fp32 precision) and
+  // w = 1 / (e + 1):
+  //   tanh(z / c) = 1 - 2 w,   S - c = -2 c w,   1 - tanh^2(z / c) = 4 e w^2
+  // so exp(S - c) = exp2(-2 c log2(e) w), and the last form keeps its
+  // relative precision where tanh saturates on either side.  Per element:
+  // three transcendentals (exp2, reciprocal, exp2) and a few multiplies.
+  const float k2 = 2.0f * kLog2e / softcap;   // z -> log2(e) 2 z / c
+  const float clampv = 40.0f * kLog2e;         // |z / c| <= 20
+  const float m2cl = -2.0f * softcap * kLog2e;
+  auto ew_of = [&](uint32_t bits, float& e, float& w) {
+    e = __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(bf16_to_f32(bits) * k2, -clampv, clampv));
+    w = __builtin_amdgcn_rcpf(e + 1.0f);
   };
-  auto chunk_tanh = [&](int c, float* th) {
-    const v4u v = *reinterpret_cast<const v4u*>(zr + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) th[e] = tanh_of((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-  };
+  auto elem = [](const v4u& v, int i) { return (v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu; };
 
   // 1. sum exp(S - c) over the classes
   float sum = 0.0f;
-  auto sweep1 = [&](int c, const float* th) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (8 * c + e < n_classes) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(th[e], cl, -cl));
-  };
   for (int c = tid; c < nch; c += kCeThreads) {
-    float th[8];
-    chunk_tanh(c, th);
-    sweep1(c, th);
+    const v4u v = *reinterpret_cast<const v4u*>(zr + 8 * c);
+    if (8 * c + 8 <= n_classes) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float e, w;
+        ew_of(elem(v, i), e, w);
+        sum += __builtin_amdgcn_exp2f(w * m2cl);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (8 * c + i < n_classes) {
+          float e, w;
+          ew_of(elem(v, i), e, w);
+          sum += __builtin_amdgcn_exp2f(w * m2cl);
+        }
+      }
+    }
   }
-  const float tht = tanh_of(zr[t]);   // read before any block writes the row
+  float et, wt;
+  ew_of(zr[t], et, wt);               // read before any block writes the row
   sum = block_sum_f32(sum, redf);     // (its barriers also order the reads above before the writes below)
-  const float lse = softcap + __logf(sum);
+  const float l2s = __log2f(sum);     // log2 of sum exp(S - c)
   const float nv = (float)(*n_valid);
   const float inv_nv = nv > 0.0f ? 1.0f / nv : 0.0f;
-  if (tid == 0) loss_rows[r] = lse - softcap * tht;
+  // loss = c + log(sum) - S_t = log(sum) + 2 c w_t
+  if (tid == 0) loss_rows[r] = l2s / kLog2e + 2.0f * softcap * wt;
 
-  // 2. dZ over the row, written over the logits
-  const float lsel = lse * kLog2e;
-  uint32_t mx = 0;
-  auto sweep2 = [&](int c, const float* th) {
+  // 2. dZ over the row, written over the logits:
+  //   dZ = (p - [j = t]) 4 e w^2 / n_valid,  p = exp(S - lse) = exp2(-2 c log2(e) w - l2s)
+  // off the target, 4 / n_valid joins the exponent's constant term.
+  const float k4 = 4.0f * inv_nv;
+  const float cst = -l2s + __log2f(k4);  // -inf when no row counts: dZ = 0
+  const int ct = t >> 3;                 // the target's chunk
+  float mxf = 0.0f;                      // max |dZ| before the bf16 rounding
+  for (int c = tid; c < nch; c += kCeThreads) {
+    const v4u v = *reinterpret_cast<const v4u*>(zr + 8 * c);
+    float gv[8];
+    if (8 * c + 8 <= n_classes && c != ct) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float e, w;
+        ew_of(elem(v, i), e, w);
+        gv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(w, m2cl, cst)) * ((e * w) * w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = 8 * c + i;
+        float e, w;
+        ew_of(elem(v, i), e, w);
+        const float q = (e * w) * w;
+        float g = __builtin_amdgcn_exp2f(__builtin_fmaf(w, m2cl, cst)) * q;
+        if (j == t) g = (__builtin_amdgcn_exp2f(__builtin_fmaf(w, m2cl, -l2s)) - 1.0f) * q * k4;
+        gv[i] = j < n_classes ? g : 0.0f;
+      }
+    }
     v4u o;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int j = 8 * c + 2 * h + k;
-        uint32_t bits = 0;
-        if (j < n_classes) {
-          const float tj = th[2 * h + k];
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(tj, cl, -lsel));
-          const float g = ((j == t ? p - 1.0f : p) * (1.0f - tj * tj)) * inv_nv;
-          bits = __builtin_bit_cast(unsigned short, (__bf16)g);
-          mx = mx > (bits & 0x7FFFu) ? mx : (bits & 0x7FFFu);
-        }
-        w |= bits << (16 * k);
-      }
-      o[h] = w;
+      const f2 pr = {gv[2 * h], gv[2 * h + 1]};
+      o[h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));  // round to nearest even
+      mxf = __builtin_fmaxf(mxf, __builtin_fmaxf(__builtin_fabsf(gv[2 * h]), __builtin_fabsf(gv[2 * h + 1])));
     }
     if (8 * c + 8 <= V) {
       *reinterpret_cast<v4u*>(zr + 8 * c) = o;
     } else {
       for (int e = 8 * c; e < V; ++e) zr[e] = (uint16_t)(o[(e - 8 * c) >> 1] >> (16 * ((e - 8 * c) & 1)));
     }
-  };
-  for (int c = tid; c < nch; c += kCeThreads) {
-    float th[8];
-    chunk_tanh(c, th);
-    sweep2(c, th);
   }
-  mx = block_max_u32(mx, redu);
+  // max |RN_bf16(dZ)| = RN_bf16(max |dZ|): the rounding is monotone and odd
+  const __bf16 mb = (__bf16)mxf;
+  const uint32_t mx = block_max_u32(__builtin_bit_cast(unsigned short, mb) & 0x7FFFu, redu);
   if (tid == 0) partials[r] = mx;
 }
 
