@@ -116,13 +116,37 @@ def dz_bound(z_bits, b, t, n, softcap, n_valid):
     y[np.arange(len(t))[valid], t[valid]] = 1.0
     bb = b[:, :n]
     E = bb.max(axis=1, keepdims=True)
-    d = 1.0 - th * th
+    with np.errstate(over="ignore"):
+        d = 1.0 / np.cosh(z / softcap) ** 2   # 1 - tanh^2 without its cancellation at saturation
     g = (p - y) * d / n_valid
     dev = (p * np.expm1(bb + E) * d + np.abs(p - y) * (2.0 / softcap) * np.abs(th) * d * bb) / n_valid
     bound = np.full(z_bits.shape, 1e-30)
     bound[:, :n] = dev * 1.01 + ulp_bf16(g) + 4e-6 * (p + y) * d / n_valid + 1e-30
     bound[~valid] = 1e-30
     return bound
+
+
+def test_saturated_logits_dz():
+    """Logits far beyond the cap (|Z / c| up to about 20): where tanh
+    saturates, 1 - tanh^2 must keep its relative precision (the bound allows
+    4e-6 of it beyond what the logits' GEMM bound implies)."""
+    wl = synth.LMHeadCEWorkload(66, 128, 256, 600, n_classes=590, chunk=64, sigma_w=4.0, ignored=0.05)
+    x, w, t = wl.tensors()
+    g = run(x, w, t, wl.n_classes, wl.chunk)
+    r = oracle.lm_head_ce(x, w, t, wl.n_classes, wl.softcap, wl.chunk)
+    n = wl.n_classes
+    ch = r["chunks"][-1]
+    c0 = x.shape[0] - g["last"]
+    _, sabs, K = oracle_gemm("nt", r["xq"][c0:], E4, r["sx"], r["wq"], E4, r["sw"])
+    z = bits_f64(ch["z"])[:, :n]
+    sat = float((np.abs(z / wl.softcap) > 5.0).mean())
+    nv = int(((t >= 0) & (t < n)).sum())
+    bound = dz_bound(ch["z"], gemm_bound(ch["z"], sabs, K), t[c0:], n, wl.softcap, nv)
+    err = np.abs(bits_f64(g["dz_last"]) - bits_f64(ch["dz"]))
+    print(f"saturated dZ: |Z/c| > 5 for {sat:.2%} of logits, max err / bound {float((err / bound).max()):.3g}")
+    assert sat > 0.2
+    assert (err <= bound).all()
+    assert abs(g["loss"] - r["loss"]) <= 1e-3 * abs(r["loss"]), (g["loss"], r["loss"])
 
 
 def test_last_chunk_stages(small):

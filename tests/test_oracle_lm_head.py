@@ -45,6 +45,28 @@ def test_rows_against_torch_autograd(scale):
     assert (dz == oracle.double_to_bf16(g)).all()
 
 
+def test_saturated_rows_against_torch_autograd():
+    """Logits far past the cap: the softcap written as c - 2c / (exp(2z/c) + 1)
+    (the same function) gives torch's autograd a derivative without the
+    cancellation of 1 - tanh^2; the oracle's gradient must follow it where
+    tanh is 1 to fp64 precision."""
+    R, V, n = 16, 256, 250
+    z = _logits(R, V, 72, 250.0)
+    zf = oracle.bf16_bits_to_f64(z)[:, :n]
+    assert (np.abs(zf / 15.0) > 18.7).mean() > 0.2
+    rng = np.random.default_rng(6)
+    t = rng.integers(0, n, R)
+    zt = torch.from_numpy(zf).requires_grad_(True)
+    s = 15.0 - 30.0 / (torch.exp(2.0 * zt / 15.0) + 1.0)
+    loss = torch.nn.functional.cross_entropy(s, torch.from_numpy(t), reduction="mean")
+    loss.backward()
+    loss_r, g, _ = oracle.softcap_ce_rows(z, t, n, 15.0, R)
+    assert abs(loss_r.mean() - float(loss.detach())) <= 1e-12 * abs(float(loss.detach()))
+    ref = zt.grad.numpy()
+    assert (ref != 0).all() and (g[:, :n] != 0).all()
+    assert np.allclose(g[:, :n], ref, rtol=1e-9, atol=0.0)
+
+
 def test_closed_forms():
     R, V, n = 6, 64, 50
     z = np.zeros((R, V), np.uint16)
