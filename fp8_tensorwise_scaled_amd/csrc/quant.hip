@@ -203,11 +203,20 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
   int tile_parity = 0;  // LDS image buffer of the next transposed tile
   for (int64_t t = lb; t < ntiles; t += jb.nblocks) {
     const int64_t r0 = (t / ntc) * kTR, c0 = (t % ntc) * kTC;
-    const bool full = r0 + kTR <= rows && c0 + kTC <= cols && (vec_in || buf_in) && vec_q && vec_qt;
+    // A tile whose rows are all present takes the vector path when its width
+    // is whole 4-column lane groups: lanes past the last column load nothing
+    // and store nothing (the last column tile of a ragged width, e.g. 128 of
+    // the 50304-column logits).
+    const int64_t wv = cols - c0 < kTC ? cols - c0 : kTC;  // valid columns
+    const bool full = r0 + kTR <= rows && wv % 4 == 0 && (vec_in || buf_in) && vec_q && vec_qt;
     if (full) {
       const int64_t rb = r0 + wave * 16, cb = c0 + lane * 4;
+      const bool lane_ok = lane * 4 < wv;
       v2u in[16];
-      if (vec_in) {
+      if (!lane_ok) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) in[i] = v2u{0u, 0u};
+      } else if (vec_in) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           in[i] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(x + (rb + i) * ldx + cb));
@@ -229,7 +238,7 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
       if constexpr (MODE == kModeRmsNorm) {
         const bool has_g = jb.gamma != nullptr;
         float g[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if (has_g) {
+        if (has_g && lane_ok) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) g[e] = bf16_to_f32(jb.gamma[cb + e]);
         }
@@ -239,7 +248,7 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
 #pragma unroll
         for (int i = 0; i < 16; ++i) code[i] = quant4<FMT, MODE>(in[i][0], in[i][1], d);
       }
-      if (q) {
+      if (q && lane_ok) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) *reinterpret_cast<uint32_t*>(q + (rb + i) * jb.ldq + cb) = code[i];
       }
@@ -269,7 +278,7 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
           const int id = tid + kCastThreads * i;
           const int c = id >> 3, k = id & 7;
           const v4u o = *reinterpret_cast<const v4u*>(img + timg_off(c, k));
-          *reinterpret_cast<v4u*>(qt + (c0 + c) * jb.ldqt + r0 + 16 * k) = o;
+          if (c < wv) *reinterpret_cast<v4u*>(qt + (c0 + c) * jb.ldqt + r0 + 16 * k) = o;
         }
         ++tile_parity;
       }

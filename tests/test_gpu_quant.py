@@ -62,7 +62,8 @@ def test_exhaustive_bf16_patterns(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("shape", [(256, 512), (1024, 512), (300, 200), (1, 8), (129, 130), (7, 1000)])
+@pytest.mark.parametrize("shape", [(256, 512), (1024, 512), (300, 200), (1, 8), (129, 130), (7, 1000),
+                                   (256, 384), (128, 260), (384, 1020)])  # last column tile 128, 4, 252 wide
 def test_workload_like_shapes(fmt, shape):
     sigma = 1.0 if fmt == oracle.E4M3 else 1e-3
     x = synth.normal_bf16(shape, sigma, 1000 + shape[0] * 7 + shape[1], outlier_frac=1e-3)

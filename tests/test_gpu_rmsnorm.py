@@ -38,6 +38,7 @@ def run(x, g, eps, fmt, ld=None):
     ((33, 1000), None, True, E5),       # rows in registers, 125 16-byte chunks (not whole waves)
     ((40, 5120), None, True, E4),       # rows longer than the register path takes
     ((6, 4096), None, False, E4),       # the longest rows the register path takes; one block
+    ((256, 392), None, True, E4),       # last column tile 136 wide: vector cast path with idle lanes
 ])
 def test_bit_exact(shape, ld, with_g, fmt):
     x = synth.normal_bf16(shape, 2.5, 91, outlier_frac=1e-3)
