@@ -88,12 +88,63 @@ def _newton_schulz():
     return step, outs
 
 
+def _rmsnorm():
+    from fp8_tensorwise_scaled_amd import _native, api
+
+    rows, cols = 300, 392  # ragged row tiles and a 136-column last column tile
+    x = to_dev_bf16(synth.normal_bf16((rows, cols), 2.0, 55))
+    g = to_dev_bf16(synth.normal_bf16((cols,), 1.0, 56))
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    outs = dict(q=torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                qt=torch.empty((cols, rows), dtype=torch.uint8, device=dev),
+                scale=torch.empty(1, **f32), amax=torch.empty(1, **f32), rstd=torch.empty(rows, **f32))
+    ws = torch.empty(max(_native.lib().fp8_rmsnorm_quant_workspace_bytes(rows, cols), 16), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        api.fp8_rmsnorm_quant(x, g, 1e-6, api.E4M3, ws=ws, **outs)
+    return step, outs
+
+
+def _fp8_linear():
+    """One FP8 linear layer's three GEMMs with their quantisations."""
+    from fp8_tensorwise_scaled_amd import _native, api
+
+    M, K, N = 384, 256, 320
+    x = to_dev_bf16(synth.normal_bf16((M, K), 1.0, 57))
+    w = to_dev_bf16(synth.normal_bf16((N, K), 0.05, 58))
+    dy = to_dev_bf16(synth.normal_bf16((M, N), 1e-3, 59))
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    L = _native.lib()
+    codes = {k: (torch.empty(shape, **u8), torch.empty(shape[::-1], **u8), torch.empty(1, **f32),
+                 torch.empty(1, **f32), torch.empty(max(L.fp8_amax_quant_workspace_bytes(*shape), 16), **u8))
+             for k, shape in (("x", (M, K)), ("w", (N, K)), ("g", (M, N)))}
+    outs = dict(y=torch.empty((M, N), **bf), dx=torch.empty((M, K), **bf), dw=torch.empty((N, K), **bf))
+    for k, (q, qt, sc, am, _) in codes.items():  # the codes and scales are cleared between replays too
+        outs.update({k + "_q": q, k + "_qt": qt, k + "_scale": sc, k + "_amax": am})
+
+    def step():
+        for k, src, fmt in (("x", x, api.E4M3), ("w", w, api.E4M3), ("g", dy, api.E5M2)):
+            q, qt, sc, am, ws = codes[k]
+            api.fp8_amax_quant(src, fmt, q=q, qt=qt, scale=sc, amax=am, ws=ws)
+        (xq, xqt, sx, _, _), (wq, wqt, sw, _, _), (gq, gqt, sg, _, _) = codes["x"], codes["w"], codes["g"]
+        api.fp8_linear_fwd(xq, sx, wq, sw, out=outs["y"])
+        api.fp8_linear_dgrad(gq, sg, wqt, sw, out=outs["dx"])
+        api.fp8_linear_wgrad(gqt, sg, xqt, sx, out=outs["dw"])
+    return step, outs
+
+
 def _bytes(t):
     return t.detach().contiguous().view(torch.uint8).cpu().clone()
 
 
-@pytest.mark.parametrize("make", [_relu2, _swiglu, _lm_head_ce, _newton_schulz],
-                         ids=["relu2_block", "swiglu_block", "lm_head_ce", "newton_schulz"])
+@pytest.mark.parametrize("make", [_relu2, _swiglu, _lm_head_ce, _newton_schulz, _rmsnorm, _fp8_linear],
+                         ids=["relu2_block", "swiglu_block", "lm_head_ce", "newton_schulz", "rmsnorm_quant",
+                              "fp8_linear"])
 def test_graph_replays_match_eager(make):
     step, outs = make()
     step()
