@@ -70,6 +70,22 @@ def test_workload_like_shapes(fmt, shape):
     check_against_oracle(x, fmt)
 
 
+def test_random_shapes():
+    """Thirty seeded random cases: rows in [1, 700), cols in [1, 1100), a
+    leading dimension equal to cols, padded, or odd, a base offset of 0 to 3
+    elements, and a random format: every tile kind (whole, partial width,
+    ragged rows, realigned rows, element path) against the oracle."""
+    rng = np.random.default_rng(4242)
+    for i in range(30):
+        rows, cols = int(rng.integers(1, 700)), int(rng.integers(1, 1100))
+        ld = [cols, cols + int(rng.integers(1, 40)), cols | 1][int(rng.integers(0, 3))]
+        offset = int(rng.integers(0, 4))
+        fmt = FMTS[int(rng.integers(0, 2))]
+        x = synth.normal_bf16((rows, cols), 1.0 if fmt == oracle.E4M3 else 1e-3, 9000 + i, outlier_frac=1e-3)
+        print(f"[quant random] {i}: {rows}x{cols} ld {ld} offset {offset} fmt {fmt}", flush=True)
+        check_against_oracle(x, fmt, ld=ld, offset=offset)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_strided_and_unaligned(fmt):
     x = synth.normal_bf16((200, 333), 1.0, 77)
