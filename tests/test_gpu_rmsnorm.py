@@ -50,6 +50,25 @@ def test_bit_exact(shape, ld, with_g, fmt):
     assert (q == rq).all() and (qt == rq.T).all()
 
 
+def test_random_shapes():
+    """Twenty seeded random cases: rows in [1, 600), cols in [1, 5000) (both
+    statistics paths), a padded or odd leading dimension, with and without
+    the weight, either format; r, the scale and every code bit-identical."""
+    rng = np.random.default_rng(777)
+    for i in range(20):
+        rows, cols = int(rng.integers(1, 600)), int(rng.integers(1, 5000))
+        ld = [None, cols + int(rng.integers(1, 24)), cols | 1][int(rng.integers(0, 3))]
+        fmt = [E4, E5][int(rng.integers(0, 2))]
+        x = synth.normal_bf16((rows, cols), float(rng.uniform(0.1, 4.0)), 9500 + i, outlier_frac=1e-3)
+        g = synth.normal_bf16((cols,), 1.0, 9600 + i) if rng.integers(0, 2) else None
+        q, qt, s, a, r = run(x, g, 1e-6, fmt, ld)
+        rq, rs, ra, _, rr = oracle.rmsnorm_quant(x, g, 1e-6, fmt)
+        what = (i, rows, cols, ld, fmt, g is not None)
+        assert (r.view(np.uint32) == rr.view(np.uint32)).all(), what
+        assert np.float32(s) == np.float32(rs) and np.float32(a) == np.float32(ra), what
+        assert (q == rq).all() and (qt == rq.T).all(), what
+
+
 def test_zero_rows_and_empty():
     x = synth.normal_bf16((64, 256), 1.0, 93)
     x[5] = 0
