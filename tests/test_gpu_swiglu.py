@@ -123,7 +123,9 @@ def test_tiny_ragged_block():
     sc_.compare(g, o, sc, rows, cols)
 
 
-@pytest.mark.parametrize("M,N,K,ld_pad", [(300, 200, 160, 0), (256, 384, 512, 24), (96, 1000, 3072, 0)])
+@pytest.mark.parametrize("M,N,K,ld_pad", [(300, 200, 160, 0), (256, 384, 512, 24), (96, 1000, 3072, 0),
+                                           (1, 8, 16, 0), (257, 136, 64, 8), (513, 264, 400, 0),
+                                           (64, 200, 128, 1)])  # last: odd leading dimension, narrow stores
 def test_gated_linear_fwd(M, N, K, ld_pad):
     """fp8_gated_linear_fwd on its own: G and U within the GEMM bound of the
     oracle's products of the same codes; A within one bf16 ulp of the
