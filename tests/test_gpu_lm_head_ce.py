@@ -263,3 +263,19 @@ def test_wide_vocabulary_few_rows():
     chain_close(g["dx"], r["dx"], "dX (wide vocabulary)")
     chain_close(g["dw"], r["dw"], "dW (wide vocabulary)")
     assert (g["dw"][wl.n_classes:] == 0).all()
+
+
+@pytest.mark.parametrize("M,K,V,n,chunk", [(208, 96, 333, 333, 48), (144, 64, 1000, 997, 128), (64, 48, 260, 250, 64)])
+def test_ragged_chunks_and_vocabulary(M, K, V, n, chunk):
+    """A last chunk shorter than the others, an odd or ragged vocabulary
+    (last column tiles 77, 232 and 4 wide), a single chunk covering all rows:
+    loss within 1e-3 relative of the oracle's, gradients within the chain
+    bar, padded rows of dW zero."""
+    wl = synth.LMHeadCEWorkload(67 + M, M, K, V, n_classes=n, chunk=chunk, sigma_w=0.25, ignored=0.05)
+    x, w, t = wl.tensors()
+    g = run(x, w, t, wl.n_classes, wl.chunk)
+    r = oracle.lm_head_ce(x, w, t, wl.n_classes, wl.softcap, wl.chunk)
+    assert abs(g["loss"] - r["loss"]) <= 1e-3 * abs(r["loss"]), (g["loss"], r["loss"])
+    chain_close(g["dx"], r["dx"], f"dX ({M}x{K}x{V}, chunk {chunk})")
+    chain_close(g["dw"], r["dw"], f"dW ({M}x{K}x{V}, chunk {chunk})")
+    assert (g["dw"][n:] == 0).all()
