@@ -15,6 +15,11 @@ LIB_PATH = os.path.join(HERE, "libfp8mlp.so")
 E4M3 = 0
 E5M2 = 1
 
+# FP8 GEMM accumulation: the FP8 matrix cores (group-truncated sums) or exact
+# products with fp32 accumulation (codes decoded to bf16, bf16 matrix cores)
+ACCUM_FAST = 0
+ACCUM_EXACT = 1
+
 _lock = threading.Lock()
 _lib = None
 
@@ -38,23 +43,25 @@ _PROTOS = {
     "fp8_rmsnorm_quant_workspace_bytes": (szt, [i64, i64]),
     "fp8_rmsnorm_quant": (c_int, [vp, vp, ctypes.c_float, i64, i64, i64, c_int, vp, i64, vp, i64, vp, vp, vp, vp,
                                   szt, vp]),
-    "fp8_linear_fwd": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, vp]),
-    "fp8_linear_dgrad": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, vp]),
-    "fp8_linear_wgrad": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, vp]),
+    "fp8_linear_fwd": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, c_int, vp]),
+    "fp8_linear_dgrad": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, c_int, vp]),
+    "fp8_linear_wgrad": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, c_int, vp]),
     "relu2_mlp_fwd_workspace_bytes": (szt, [i64, i64, i64]),
     "relu2_mlp_bwd_workspace_bytes": (szt, [i64, i64, i64]),
     "relu2_mlp_fwd_workspace_layout": (c_int, [i64, i64, i64, ctypes.POINTER(szt), c_int]),
     "relu2_mlp_bwd_workspace_layout": (c_int, [i64, i64, i64, ctypes.POINTER(szt), c_int]),
-    "relu2_mlp_fwd": (c_int, [vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(Relu2MlpSaved), vp, szt, vp]),
-    "relu2_mlp_bwd": (c_int, [vp, ctypes.POINTER(Relu2MlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, szt, vp]),
+    "relu2_mlp_fwd": (c_int, [vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(Relu2MlpSaved), vp, szt, c_int, vp]),
+    "relu2_mlp_bwd": (c_int, [vp, ctypes.POINTER(Relu2MlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, szt, c_int,
+                              vp]),
     "swiglu_mlp_fwd_workspace_bytes": (szt, [i64, i64, i64]),
     "swiglu_mlp_bwd_workspace_bytes": (szt, [i64, i64, i64]),
     "swiglu_mlp_fwd_workspace_layout": (c_int, [i64, i64, i64, ctypes.POINTER(szt), c_int]),
     "swiglu_mlp_bwd_workspace_layout": (c_int, [i64, i64, i64, ctypes.POINTER(szt), c_int]),
-    "swiglu_mlp_fwd": (c_int, [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(SwigluMlpSaved), vp, szt, vp]),
-    "swiglu_mlp_bwd": (c_int, [vp, ctypes.POINTER(SwigluMlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, vp, szt,
+    "swiglu_mlp_fwd": (c_int, [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(SwigluMlpSaved), vp, szt, c_int,
                                vp]),
-    "fp8_gated_linear_fwd": (c_int, [vp, i64, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, i64, vp]),
+    "swiglu_mlp_bwd": (c_int, [vp, ctypes.POINTER(SwigluMlpSaved), i64, i64, i64, vp, vp, vp, vp, vp, vp, szt,
+                               c_int, vp]),
+    "fp8_gated_linear_fwd": (c_int, [vp, i64, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, i64, c_int, vp]),
     "bf16_gemm_nt": (c_int, [vp, i64, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_float, vp, i64, vp, i64, vp,
                              i64, vp]),
     "bf16_gemm_sym_workspace_bytes": (szt, [i64, i64]),
@@ -63,7 +70,8 @@ _PROTOS = {
     "muon_newton_schulz": (c_int, [vp, i64, i64, c_int, vp, ctypes.c_float, vp, vp, vp, szt, vp]),
     "fp8_lm_head_ce_workspace_bytes": (szt, [i64, i64, i64, i64]),
     "fp8_lm_head_ce_workspace_layout": (c_int, [i64, i64, i64, i64, ctypes.POINTER(szt), c_int]),
-    "fp8_lm_head_ce": (c_int, [vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i64, vp, vp, vp, vp, vp, szt, vp]),
+    "fp8_lm_head_ce": (c_int, [vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i64, vp, vp, vp, vp, vp, szt,
+                               c_int, vp]),
 }
 
 EXPORTS = tuple(_PROTOS)

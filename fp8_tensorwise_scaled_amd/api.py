@@ -13,7 +13,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _native
-from ._native import E4M3, E5M2
+from ._native import ACCUM_EXACT, ACCUM_FAST, E4M3, E5M2
 
 FMAX = {E4M3: 448.0, E5M2: 57344.0}
 
@@ -120,36 +120,40 @@ def fp8_rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor | None = None, eps: f
     return q, qt, scale, amax, rstd
 
 
-def _gemm(name, a, fa, sa, b, fb, sb, M, N, K, out, out_shape):
+def _gemm(name, a, fa, sa, b, fb, sb, M, N, K, out, out_shape, accum):
     _check_dev(a, b, sa, sb)
     out = _out(out, out_shape, torch.bfloat16, a.device, "out")
     _native.call(name, _p(a), _ld(a), fa, _p(sa), _p(b), _ld(b), fb, _p(sb), M, N, K, _p(out), _ld(out),
-                 _stream())
+                 int(accum), _stream())
     return out
 
 
-def fp8_linear_fwd(xq, sx, wq, sw, fx: int = E4M3, fw: int = E4M3, out=None):
-    """Y[M,N] = RN_bf16(RN32(sx*sw) * Xq[M,K] . Wq[N,K]^T)."""
+def fp8_linear_fwd(xq, sx, wq, sw, fx: int = E4M3, fw: int = E4M3, out=None, *, accum: int = ACCUM_FAST):
+    """Y[M,N] = RN_bf16(RN32(sx*sw) * Xq[M,K] . Wq[N,K]^T)  (NT)."""
     M, K = xq.shape
     N = wq.shape[0]
-    return _gemm("fp8_linear_fwd", xq, fx, sx, wq, fw, sw, M, N, K, out, (M, N))
+    return _gemm("fp8_linear_fwd", xq, fx, sx, wq, fw, sw, M, N, K, out, (M, N), accum)
 
 
-def fp8_linear_dgrad(dyq, sdy, wqt, sw, fdy: int = E5M2, fw: int = E4M3, out=None):
-    """dX[M,K] = RN_bf16(RN32(sdy*sw) * dYq[M,N] . W[N,K]); wqt = W codes transposed [K,N]."""
+def fp8_linear_dgrad(dyq, sdy, wq, sw, fdy: int = E5M2, fw: int = E4M3, out=None, *, accum: int = ACCUM_FAST):
+    """dX[M,K] = RN_bf16(RN32(sdy*sw) * dYq[M,N] . Wq[N,K])  (NN; the forward's weight codes)."""
     M, N = dyq.shape
-    K = wqt.shape[0]
-    return _gemm("fp8_linear_dgrad", dyq, fdy, sdy, wqt, fw, sw, M, N, K, out, (M, K))
+    K = wq.shape[1]
+    if wq.shape[0] != N:
+        raise ValueError("shapes: dyq [M, N], wq [N, K]")
+    return _gemm("fp8_linear_dgrad", dyq, fdy, sdy, wq, fw, sw, M, N, K, out, (M, K), accum)
 
 
-def fp8_linear_wgrad(dyqt, sdy, xqt, sx, fdy: int = E5M2, fx: int = E4M3, out=None):
-    """dW[N,K] = RN_bf16(RN32(sdy*sx) * dY^T . X); dyqt [N,M], xqt [K,M] transposed codes."""
-    N, M = dyqt.shape
-    K = xqt.shape[0]
-    return _gemm("fp8_linear_wgrad", dyqt, fdy, sdy, xqt, fx, sx, M, N, K, out, (N, K))
+def fp8_linear_wgrad(dyq, sdy, xq, sx, fdy: int = E5M2, fx: int = E4M3, out=None, *, accum: int = ACCUM_FAST):
+    """dW[N,K] = RN_bf16(RN32(sdy*sx) * dYq[M,N]^T . Xq[M,K])  (TN; the forward's input codes)."""
+    M, N = dyq.shape
+    K = xq.shape[1]
+    if xq.shape[0] != M:
+        raise ValueError("shapes: dyq [M, N], xq [M, K]")
+    return _gemm("fp8_linear_wgrad", dyq, fdy, sdy, xq, fx, sx, M, N, K, out, (N, K), accum)
 
 
-def fp8_gated_linear_fwd(xq, sx, wgq, sg, wuq, su, *, g=None, u=None, a=None):
+def fp8_gated_linear_fwd(xq, sx, wgq, sg, wuq, su, *, g=None, u=None, a=None, accum: int = ACCUM_FAST):
     """The gated block's gate and up projections in one FP8 GEMM (E4M3 codes):
     G = RN_bf16(RN32(sx*sg) Xq Wgq^T), U = RN_bf16(RN32(sx*su) Xq Wuq^T),
     A = RN_bf16(silu(G) U).  Returns (g, u, a), each [M, N] bf16."""
@@ -167,7 +171,7 @@ def fp8_gated_linear_fwd(xq, sx, wgq, sg, wuq, su, *, g=None, u=None, a=None):
     if not (_ld(g) == _ld(u) == _ld(a)):
         raise ValueError("g, u and a must share a leading dimension")
     _native.call("fp8_gated_linear_fwd", _p(xq), _ld(xq), _p(sx), _p(wgq), _p(sg), _p(wuq), _p(su), _ld(wgq),
-                 M, N, K, _p(g), _p(u), _p(a), _ld(g), _stream())
+                 M, N, K, _p(g), _p(u), _p(a), _ld(g), int(accum), _stream())
     return g, u, a
 
 
@@ -221,7 +225,8 @@ def workspace_layout(kind: str, M: int, d: int, h: int):
     return list(offs)
 
 
-def relu2_mlp_fwd(x, w_up, w_down, *, y=None, saved: Relu2MlpSaved | None = None, ws=None):
+def relu2_mlp_fwd(x, w_up, w_down, *, y=None, saved: Relu2MlpSaved | None = None, ws=None,
+                  accum: int = ACCUM_FAST):
     """Y = relu(X W_up^T)^2 W_down^T with FP8 GEMMs.  Returns (y, saved)."""
     _check_dev(x, w_up, w_down)
     M, d = x.shape
@@ -239,11 +244,12 @@ def relu2_mlp_fwd(x, w_up, w_down, *, y=None, saved: Relu2MlpSaved | None = None
     ws = relu2_mlp_fwd_workspace(M, d, h, x.device) if ws is None else _ws(ws)
     cs = saved.c_struct()
     _native.call("relu2_mlp_fwd", _p(x), _p(w_up), _p(w_down), M, d, h, _p(y), ctypes.byref(cs), _p(ws),
-                 ws.numel(), _stream())
+                 ws.numel(), int(accum), _stream())
     return y, saved
 
 
-def relu2_mlp_bwd(dy, saved: Relu2MlpSaved, *, dx=None, dw_up=None, dw_down=None, bwd_scales=None, ws=None):
+def relu2_mlp_bwd(dy, saved: Relu2MlpSaved, *, dx=None, dw_up=None, dw_down=None, bwd_scales=None, ws=None,
+                  accum: int = ACCUM_FAST):
     """Backward of the block.  Returns (dx, dw_up, dw_down, bwd_scales[sg, sh])."""
     _check_dev(dy)
     M, d, h = saved.M, saved.d, saved.hid
@@ -258,7 +264,7 @@ def relu2_mlp_bwd(dy, saved: Relu2MlpSaved, *, dx=None, dw_up=None, dw_down=None
     ws = relu2_mlp_bwd_workspace(M, d, h, dev) if ws is None else _ws(ws)
     cs = saved.c_struct()
     _native.call("relu2_mlp_bwd", _p(dy), ctypes.byref(cs), M, d, h, _p(dx), _p(dw_up), _p(dw_down),
-                 _p(bwd_scales), _p(ws), ws.numel(), _stream())
+                 _p(bwd_scales), _p(ws), ws.numel(), int(accum), _stream())
     return dx, dw_up, dw_down, bwd_scales
 
 
@@ -311,7 +317,8 @@ def swiglu_workspace_layout(kind: str, M: int, d: int, h: int):
     return list(offs)
 
 
-def swiglu_mlp_fwd(x, w_gate, w_up, w_down, *, y=None, saved: SwigluMlpSaved | None = None, ws=None):
+def swiglu_mlp_fwd(x, w_gate, w_up, w_down, *, y=None, saved: SwigluMlpSaved | None = None, ws=None,
+                   accum: int = ACCUM_FAST):
     """Y = (silu(X W_gate^T) * X W_up^T) W_down^T with FP8 GEMMs.  Returns (y, saved)."""
     _check_dev(x, w_gate, w_up, w_down)
     M, d = x.shape
@@ -329,12 +336,12 @@ def swiglu_mlp_fwd(x, w_gate, w_up, w_down, *, y=None, saved: SwigluMlpSaved | N
     ws = swiglu_mlp_workspace("fwd", M, d, h, x.device) if ws is None else _ws(ws)
     cs = saved.c_struct()
     _native.call("swiglu_mlp_fwd", _p(x), _p(w_gate), _p(w_up), _p(w_down), M, d, h, _p(y), ctypes.byref(cs),
-                 _p(ws), ws.numel(), _stream())
+                 _p(ws), ws.numel(), int(accum), _stream())
     return y, saved
 
 
 def swiglu_mlp_bwd(dy, saved: SwigluMlpSaved, *, dx=None, dw_gate=None, dw_up=None, dw_down=None,
-                   bwd_scales=None, ws=None):
+                   bwd_scales=None, ws=None, accum: int = ACCUM_FAST):
     """Backward of the gated block.  Returns (dx, dw_gate, dw_up, dw_down,
     bwd_scales[s_dY, s_dG, s_dU])."""
     _check_dev(dy)
@@ -351,7 +358,7 @@ def swiglu_mlp_bwd(dy, saved: SwigluMlpSaved, *, dx=None, dw_gate=None, dw_up=No
     ws = swiglu_mlp_workspace("bwd", M, d, h, dev) if ws is None else _ws(ws)
     cs = saved.c_struct()
     _native.call("swiglu_mlp_bwd", _p(dy), ctypes.byref(cs), M, d, h, _p(dx), _p(dw_gate), _p(dw_up),
-                 _p(dw_down), _p(bwd_scales), _p(ws), ws.numel(), _stream())
+                 _p(dw_down), _p(bwd_scales), _p(ws), ws.numel(), int(accum), _stream())
     return dx, dw_gate, dw_up, dw_down, bwd_scales
 
 
@@ -438,7 +445,7 @@ def lm_head_ce_layout(M: int, K: int, V: int, chunk: int):
 
 
 def fp8_lm_head_ce(x, w, targets, n_classes: int, softcap: float = 15.0, chunk: int = 2048, *, loss=None,
-                   dx=None, dw=None, scales=None, ws=None):
+                   dx=None, dw=None, scales=None, ws=None, accum: int = ACCUM_FAST):
     """FP8 LM head fused with the softcapped cross-entropy, chunked over rows.
 
     x [M, K] bf16, w [V, K] bf16, targets [M] int32 (ids outside
@@ -462,5 +469,5 @@ def fp8_lm_head_ce(x, w, targets, n_classes: int, softcap: float = 15.0, chunk: 
     if not targets.is_contiguous():
         raise ValueError("targets must be contiguous")
     _native.call("fp8_lm_head_ce", _p(x), _p(w), _p(targets), M, K, V, n_classes, float(softcap),
-                 chunk, _p(loss), _p(dx), _p(dw), _p(scales), _p(ws), ws.numel(), _stream())
+                 chunk, _p(loss), _p(dx), _p(dw), _p(scales), _p(ws), ws.numel(), int(accum), _stream())
     return loss, dx, dw, scales

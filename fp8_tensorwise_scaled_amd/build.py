@@ -13,7 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8mlp.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["quant.hip", "gemm.hip", "lm_head_ce.hip", "swiglu.hip", "muon.hip", "api.hip"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_nt_fast.hip", "gemm_nt_exact.hip", "gemm_nn_fast.hip",
+           "gemm_nn_exact.hip", "gemm_tn_fast.hip", "gemm_tn_exact.hip", "lm_head_ce.hip", "swiglu.hip",
+           "muon.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -33,7 +35,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4, 16)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -20,37 +20,48 @@ bool fmt_ok(int f) { return f == FP8MLP_E4M3 || f == FP8MLP_E5M2; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8MLP_OK : FP8MLP_EHIP; }
 
-// GEMM operand tiles are addressed with 32-bit buffer offsets.
+bool accum_ok(int a) { return a == FP8MLP_ACCUM_FAST || a == FP8MLP_ACCUM_EXACT; }
+
+// GEMM operand tiles are addressed with 32-bit buffer offsets: a K-major
+// operand from the first of a tile's 256 rows to the end of its last row, an
+// MN-major one over every reduction row (plus one stage of 128 rows read
+// past the end as zeros).
 constexpr int64_t kTileRows = 256;
 bool tile_range_ok(int64_t ld, int64_t K) { return (kTileRows - 1) * ld + K < (int64_t(1) << 31); }
+bool mn_range_ok(int64_t ld, int64_t K) { return (K + 128) * ld + kTileRows < (int64_t(1) << 31); }
 
-int check_gemm(const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8_t* b, int64_t ldb,
-               int fb, const float* sb, int64_t M, int64_t N, int64_t K, const uint16_t* c,
-               int64_t ldc) {
+// FP8 GEMM C[M,N] = op(A) op(B) in `layout` (kLayNT / kLayNN / kLayTN): a
+// K-major operand has rows of K codes (ld >= K), an MN-major one K rows of
+// M (N) codes (ld >= M (N)).
+int check_gemm(int layout, const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8_t* b,
+               int64_t ldb, int fb, const float* sb, int64_t M, int64_t N, int64_t K, const uint16_t* c,
+               int64_t ldc, int accum) {
   if (!sa || !sb) return FP8MLP_EINVAL;
   if (M < 0 || N < 0 || K < 0) return FP8MLP_EINVAL;
-  if (!fmt_ok(fa) || !fmt_ok(fb)) return FP8MLP_EINVAL;
+  if (!fmt_ok(fa) || !fmt_ok(fb) || !accum_ok(accum)) return FP8MLP_EINVAL;
   if (M == 0 || N == 0) return FP8MLP_OK;  // empty output: nothing read or written
   if (!c || ldc < N) return FP8MLP_EINVAL;
   if (!a2(c)) return FP8MLP_EALIGN;
   if (K == 0) return FP8MLP_OK;  // empty sums: C = 0, the operands are not read
-  if (!a || !b || lda < K || ldb < K) return FP8MLP_EINVAL;
-  if (K % 16 != 0) return FP8MLP_ENOTSUP;
+  const bool amn = (layout & 1) != 0, bmn = (layout & 2) != 0;
+  if (!a || !b || lda < (amn ? M : K) || ldb < (bmn ? N : K)) return FP8MLP_EINVAL;
   if (!a16(a) || !a16(b) || lda % 16 || ldb % 16) return FP8MLP_EALIGN;
-  if (!tile_range_ok(lda, K) || !tile_range_ok(ldb, K)) return FP8MLP_ENOTSUP;
-  if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return FP8MLP_ENOTSUP;
+  if (!(amn ? mn_range_ok(lda, K) : tile_range_ok(lda, K)) || !(bmn ? mn_range_ok(ldb, K) : tile_range_ok(ldb, K)))
+    return FP8MLP_ENOTSUP;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FP8MLP_ENOTSUP;
   return FP8MLP_OK;
 }
 
-int run_gemm(const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8_t* b, int64_t ldb,
-             int fb, const float* sb, int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc,
+int run_gemm(int layout, const uint8_t* a, int64_t lda, int fa, const float* sa, const uint8_t* b, int64_t ldb,
+             int fb, const float* sb, int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc, int accum,
              void* stream) {
-  int st = check_gemm(a, lda, fa, sa, b, ldb, fb, sb, M, N, K, c, ldc);
+  int st = check_gemm(layout, a, lda, fa, sa, b, ldb, fb, sb, M, N, K, c, ldc, accum);
   if (st) return st;
   if (M == 0 || N == 0) return FP8MLP_OK;  // empty output; K == 0 writes zeros
   GemmArgs g{};
   g.a = a; g.b = b; g.lda = lda; g.ldb = ldb; g.fa = fa; g.fb = fb; g.sa = sa; g.sb = sb;
-  if (K == 0) g.lda = g.ldb = 0;  // operand descriptors cover no bytes
+  g.layout = layout; g.accum = accum;
+  if (K == 0) { g.lda = g.ldb = 0; g.layout = kLayNT; }  // operand descriptors cover no bytes
   g.M = M; g.N = N; g.K = K; g.c = c; g.ldc = ldc; g.epi = kEpiStore;
   return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
@@ -170,7 +181,7 @@ const char* fp8mlp_status_string(int status) {
     case FP8MLP_EALIGN: return "misaligned pointer or leading dimension";
     case FP8MLP_EWORKSPACE: return "workspace missing or too small";
     case FP8MLP_EHIP: return "HIP launch failed";
-    case FP8MLP_ENOTSUP: return "shape not supported (K % 16, or tile offsets beyond 2 GiB)";
+    case FP8MLP_ENOTSUP: return "shape not supported (operand offsets beyond 2 GiB, or a size limit)";
     default: return "unknown status";
   }
 }
@@ -245,37 +256,39 @@ int fp8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64
 
 int fp8_linear_fwd(const uint8_t* xq, int64_t ldx, int fx, const float* sx, const uint8_t* wq,
                    int64_t ldw, int fw, const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                   int64_t ldy, void* stream) {
-  return run_gemm(xq, ldx, fx, sx, wq, ldw, fw, sw, M, N, K, y, ldy, stream);
+                   int64_t ldy, int accum, void* stream) {
+  // Y[M,N] = sum_k X[m,k] W[n,k]: NT
+  return run_gemm(kLayNT, xq, ldx, fx, sx, wq, ldw, fw, sw, M, N, K, y, ldy, accum, stream);
 }
 
-int fp8_linear_dgrad(const uint8_t* dyq, int64_t lddy, int fdy, const float* sdy, const uint8_t* wqt,
-                     int64_t ldwt, int fw, const float* sw, int64_t M, int64_t N, int64_t K,
-                     uint16_t* dx, int64_t lddx, void* stream) {
-  // dX[M,K] = sum_n dY[m,n] W^T[k,n]: an NT GEMM with reduction length N
-  return run_gemm(dyq, lddy, fdy, sdy, wqt, ldwt, fw, sw, M, K, N, dx, lddx, stream);
+int fp8_linear_dgrad(const uint8_t* dyq, int64_t lddy, int fdy, const float* sdy, const uint8_t* wq,
+                     int64_t ldw, int fw, const float* sw, int64_t M, int64_t N, int64_t K,
+                     uint16_t* dx, int64_t lddx, int accum, void* stream) {
+  // dX[M,K] = sum_n dY[m,n] W[n,k]: NN with reduction length N
+  return run_gemm(kLayNN, dyq, lddy, fdy, sdy, wq, ldw, fw, sw, M, K, N, dx, lddx, accum, stream);
 }
 
-int fp8_linear_wgrad(const uint8_t* dyqt, int64_t lddyt, int fdy, const float* sdy, const uint8_t* xqt,
-                     int64_t ldxt, int fx, const float* sx, int64_t M, int64_t N, int64_t K,
-                     uint16_t* dw, int64_t lddw, void* stream) {
-  // dW[N,K] = sum_m dY^T[n,m] X^T[k,m]: an NT GEMM with reduction length M
-  return run_gemm(dyqt, lddyt, fdy, sdy, xqt, ldxt, fx, sx, N, K, M, dw, lddw, stream);
+int fp8_linear_wgrad(const uint8_t* dyq, int64_t lddy, int fdy, const float* sdy, const uint8_t* xq,
+                     int64_t ldx, int fx, const float* sx, int64_t M, int64_t N, int64_t K,
+                     uint16_t* dw, int64_t lddw, int accum, void* stream) {
+  // dW[N,K] = sum_m dY[m,n] X[m,k]: TN with reduction length M
+  return run_gemm(kLayTN, dyq, lddy, fdy, sdy, xq, ldx, fx, sx, N, K, M, dw, lddw, accum, stream);
 }
 
 int fp8_gated_linear_fwd(const uint8_t* xq, int64_t ldx, const float* sx, const uint8_t* wgq, const float* sg,
                          const uint8_t* wuq, const float* su, int64_t ldw, int64_t M, int64_t N, int64_t K,
-                         uint16_t* g, uint16_t* u, uint16_t* a, int64_t ldo, void* stream) {
-  int st = check_gemm(xq, ldx, FP8MLP_E4M3, sx, wgq, ldw, FP8MLP_E4M3, sg, M, N, K, g, ldo);
+                         uint16_t* g, uint16_t* u, uint16_t* a, int64_t ldo, int accum, void* stream) {
+  int st = check_gemm(kLayNT, xq, ldx, FP8MLP_E4M3, sx, wgq, ldw, FP8MLP_E4M3, sg, M, N, K, g, ldo, accum);
   if (st) return st;
   if (!su) return FP8MLP_EINVAL;
   if (M == 0 || N == 0) return FP8MLP_OK;
+  if (K % 16) return FP8MLP_ENOTSUP;  // the merged projection takes whole 16-byte chunks of both weights
   if (!u || !a) return FP8MLP_EINVAL;
   if (!a2(u) || !a2(a)) return FP8MLP_EALIGN;
   if (K > 0 && !wuq) return FP8MLP_EINVAL;
   if (K > 0 && !a16(wuq)) return FP8MLP_EALIGN;
   GemmArgs gs = gemm_args(xq, ldx, FP8MLP_E4M3, sx, wgq, ldw, FP8MLP_E4M3, sg, M, N, K, kEpiSwiGLU);
-  gs.b2 = wuq; gs.sb2 = su; gs.c = g; gs.c2 = u; gs.c3 = a; gs.ldc = ldo;
+  gs.b2 = wuq; gs.sb2 = su; gs.c = g; gs.c2 = u; gs.c3 = a; gs.ldc = ldo; gs.accum = accum;
   if (K == 0) gs.lda = gs.ldb = 0;  // operand descriptors cover no bytes: G = U = A = 0
   return hip_status(launch_gemm(gs, (hipStream_t)stream));
 }
@@ -306,8 +319,9 @@ int relu2_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offs
 
 int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_down, int64_t M,
                   int64_t d, int64_t h, uint16_t* y, const relu2_mlp_saved* saved, void* ws,
-                  size_t ws_bytes, void* stream) {
+                  size_t ws_bytes, int accum, void* stream) {
   if (!w_up || !w_down || !saved || !saved->uq_t || !saved->dq_t || !saved->scales) return FP8MLP_EINVAL;
+  if (!accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
   // buffers with M rows may be NULL when M == 0 (no tokens)
@@ -347,6 +361,7 @@ int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_dow
   g.a = xq; g.lda = d; g.fa = FP8MLP_E4M3; g.sa = &sc[0];
   g.b = uq; g.ldb = d; g.fb = FP8MLP_E4M3; g.sb = &sc[1];
   g.M = M; g.N = h; g.K = d; g.c = saved->h; g.ldc = h; g.epi = kEpiRelu2Max; g.partials = ph;
+  g.accum = accum;
   if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 4. Aq = quant(RN_bf16(relu(H)^2)), amax from the epilogue's partials
@@ -361,13 +376,15 @@ int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_dow
   g2.a = aq; g2.lda = h; g2.fa = FP8MLP_E4M3; g2.sa = &sc[3];
   g2.b = dq; g2.ldb = h; g2.fb = FP8MLP_E4M3; g2.sb = &sc[2];
   g2.M = M; g2.N = d; g2.K = h; g2.c = y; g2.ldc = d; g2.epi = kEpiStore;
+  g2.accum = accum;
   return hip_status(launch_gemm(g2, s));
 }
 
 int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, int64_t d, int64_t h,
                   uint16_t* dx, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales, void* ws,
-                  size_t ws_bytes, void* stream) {
+                  size_t ws_bytes, int accum, void* stream) {
   if (!saved || !dw_up || !dw_down || !saved->uq_t || !saved->dq_t || !saved->scales) return FP8MLP_EINVAL;
+  if (!accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
   if (M > 0 && (!dy || !dx || !saved->xq_t || !saved->aq_t || !saved->h)) return FP8MLP_EINVAL;
@@ -403,6 +420,7 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
   g.a = gqt; g.lda = M; g.fa = FP8MLP_E5M2; g.sa = &bsc[0];
   g.b = saved->aq_t; g.ldb = M; g.fb = FP8MLP_E4M3; g.sb = &sc[3];
   g.M = d; g.N = h; g.K = M; g.c = dw_down; g.ldc = h; g.epi = kEpiStore;
+  g.accum = accum;
   if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 3. dA = Gq . Dq (reduction over d), fused dH = RN_bf16(2 relu(H) dA) and max |dH|
@@ -411,6 +429,7 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
   g2.b = saved->dq_t; g2.ldb = d; g2.fb = FP8MLP_E4M3; g2.sb = &sc[2];
   g2.M = M; g2.N = h; g2.K = d; g2.c = dh; g2.ldc = h; g2.epi = kEpiRelu2Bwd;
   g2.aux = saved->h; g2.ldaux = h; g2.partials = pdh;
+  g2.accum = accum;
   if (launch_gemm(g2, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 4. Hq = quant(dH) (E5M2), amax from the epilogue's partials
@@ -425,6 +444,7 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
   g3.a = hqt; g3.lda = M; g3.fa = FP8MLP_E5M2; g3.sa = &bsc[1];
   g3.b = saved->xq_t; g3.ldb = M; g3.fb = FP8MLP_E4M3; g3.sb = &sc[0];
   g3.M = h; g3.N = d; g3.K = M; g3.c = dw_up; g3.ldc = d; g3.epi = kEpiStore;
+  g3.accum = accum;
   if (launch_gemm(g3, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 6. dX[M,d] = Hq . Uq   (reduction over h)
@@ -432,6 +452,7 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
   g4.a = hq; g4.lda = h; g4.fa = FP8MLP_E5M2; g4.sa = &bsc[1];
   g4.b = saved->uq_t; g4.ldb = h; g4.fb = FP8MLP_E4M3; g4.sb = &sc[1];
   g4.M = M; g4.N = d; g4.K = h; g4.c = dx; g4.ldc = d; g4.epi = kEpiStore;
+  g4.accum = accum;
   return hip_status(launch_gemm(g4, s));
 }
 
@@ -449,8 +470,8 @@ int fp8_lm_head_ce_workspace_layout(int64_t M, int64_t K, int64_t V, int64_t chu
 
 int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets, int64_t M, int64_t K,
                    int64_t V, int64_t n_classes, float softcap, int64_t chunk, float* loss, uint16_t* dx,
-                   uint16_t* dw, float* scales, void* ws, size_t ws_bytes, void* stream) {
-  if (!w || !dw || !loss) return FP8MLP_EINVAL;
+                   uint16_t* dw, float* scales, void* ws, size_t ws_bytes, int accum, void* stream) {
+  if (!w || !dw || !loss || !accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_lm_ce_dims(M, K, V, n_classes, chunk);
   if (st) return st;
   if (!(softcap > 0.0f) || !(softcap < 1e30f)) return FP8MLP_EINVAL;
@@ -501,6 +522,7 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
     g.a = xq + c0 * K; g.lda = K; g.fa = FP8MLP_E4M3; g.sa = &sc[0];
     g.b = wq; g.ldb = K; g.fb = FP8MLP_E4M3; g.sb = &sc[1];
     g.M = rows; g.N = V; g.K = K; g.c = zb; g.ldc = Vp; g.epi = kEpiStore;
+    g.accum = accum;
     if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
     if (launch_softcap_ce(zb, rows, V, Vp, n_classes, softcap, targets + c0, nv, loss_rows + c0, pz, s) !=
         hipSuccess)
@@ -514,6 +536,7 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
     gd.a = dzq; gd.lda = Vp; gd.fa = FP8MLP_E5M2; gd.sa = &sc[2 + k];
     gd.b = wqt; gd.ldb = Vp; gd.fb = FP8MLP_E4M3; gd.sb = &sc[1];
     gd.M = rows; gd.N = K; gd.K = Vp; gd.c = dx + c0 * K; gd.ldc = K; gd.epi = kEpiStore;
+    gd.accum = accum;
     if (launch_gemm(gd, s) != hipSuccess) return FP8MLP_EHIP;
     GemmArgs gw{};  // dW (+)= RN32(s_k sx) dZq_k^T . Xq_k   (reduction over the chunk's rows)
     gw.a = dzqt; gw.lda = C; gw.fa = FP8MLP_E5M2; gw.sa = &sc[2 + k];
@@ -524,6 +547,7 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
     const bool last = c0 + C >= M;
     gw.epi = !last ? (k == 0 ? kEpiStoreF32 : kEpiAccF32) : (k == 0 ? kEpiStore : kEpiAccF32Bf16);
     if (last) gw.c = dw;
+    gw.accum = accum;
     if (launch_gemm(gw, s) != hipSuccess) return FP8MLP_EHIP;
   }
 
@@ -558,9 +582,10 @@ int swiglu_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* off
 
 int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                    int64_t M, int64_t d, int64_t h, uint16_t* y, const swiglu_mlp_saved* sv, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   size_t ws_bytes, int accum, void* stream) {
   if (!w_gate || !w_up || !w_down || !sv || !sv->wgq_t || !sv->wuq_t || !sv->wdq_t || !sv->scales)
     return FP8MLP_EINVAL;
+  if (!accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
   if (M > 0 && (!x || !y || !sv->xq_t || !sv->aq_t || !sv->g || !sv->u)) return FP8MLP_EINVAL;
@@ -597,6 +622,7 @@ int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_
   GemmArgs gs = gemm_args(xq, d, FP8MLP_E4M3, &sc[0], wgq, d, FP8MLP_E4M3, &sc[1], M, h, d, kEpiSwiGLU);
   gs.b2 = wuq; gs.sb2 = &sc[2];
   gs.c = sv->g; gs.c2 = sv->u; gs.c3 = a; gs.ldc = h; gs.partials = pa;
+  gs.accum = accum;
   if (launch_gemm(gs, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 3. Aq and its transpose, 4. Y = Aq . Wdq^T
@@ -607,14 +633,16 @@ int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_
   if (launch_cast(ba, s) != hipSuccess) return FP8MLP_EHIP;
   GemmArgs gy = gemm_args(aq, h, FP8MLP_E4M3, &sc[4], wdq, h, FP8MLP_E4M3, &sc[3], M, d, h, kEpiStore);
   gy.c = y; gy.ldc = d;
+  gy.accum = accum;
   return hip_status(launch_gemm(gy, s));
 }
 
 int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, int64_t d, int64_t h, uint16_t* dx,
                    uint16_t* dw_gate, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   size_t ws_bytes, int accum, void* stream) {
   if (!sv || !dw_gate || !dw_up || !dw_down || !sv->wgq_t || !sv->wuq_t || !sv->wdq_t || !sv->scales)
     return FP8MLP_EINVAL;
+  if (!accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
   if (M > 0 && (!dy || !dx || !sv->xq_t || !sv->aq_t || !sv->g || !sv->u)) return FP8MLP_EINVAL;
@@ -650,6 +678,8 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   gw.c = dw_down; gw.ldc = h;
   GemmArgs ga = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->wdq_t, d, FP8MLP_E4M3, &sc[3], M, h, d, kEpiStore);
   ga.c = da; ga.ldc = h;
+  gw.accum = accum;
+  ga.accum = accum;
   if (launch_gemm(gw, s) != hipSuccess || launch_gemm(ga, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 4. dG, dU with their amax partials, 5. their E5M2 codes (one cast launch)
@@ -667,6 +697,8 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   gg.c = dw_gate; gg.ldc = d;
   GemmArgs gu = gemm_args(duqt, M, FP8MLP_E5M2, &bsc[2], sv->xq_t, M, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
   gu.c = dw_up; gu.ldc = d;
+  gg.accum = accum;
+  gu.accum = accum;
   if (launch_gemm(gg, s) != hipSuccess || launch_gemm(gu, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 7. dX = dGq . Wg + dUq . Wu, summed in fp32 and rounded once
@@ -675,6 +707,8 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   GemmArgs x2 = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->wuq_t, h, FP8MLP_E4M3, &sc[2], M, d, h,
                           kEpiAccF32Bf16);  // adds to the first product and rounds once into dx
   x2.cf = dxf; x2.c = dx; x2.ldc = d;
+  x1.accum = accum;
+  x2.accum = accum;
   if (launch_gemm(x1, s) != hipSuccess || launch_gemm(x2, s) != hipSuccess) return FP8MLP_EHIP;
   return FP8MLP_OK;
 }

@@ -10,8 +10,10 @@ constexpr int kE5M2 = 1;
 constexpr float kFmaxE4M3 = 448.0f;
 constexpr float kFmaxE5M2 = 57344.0f;
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));

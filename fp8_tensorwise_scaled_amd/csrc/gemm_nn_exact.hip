@@ -1,0 +1,10 @@
+// FP8 GEMM instances: NN layout, exact-product accumulation.
+#include "gemm_kernel.h"
+
+namespace fp8mlp {
+
+hipError_t launch_gemm_nn_exact(const GemmArgs& g, hipStream_t st) {
+  return gemm_detail::launch_layout<kLayNN, kAccExact>(g, st);
+}
+
+}  // namespace fp8mlp

@@ -1,0 +1,10 @@
+// FP8 GEMM instances: TN layout, FP8 matrix-core accumulation.
+#include "gemm_kernel.h"
+
+namespace fp8mlp {
+
+hipError_t launch_gemm_tn_fast(const GemmArgs& g, hipStream_t st) {
+  return gemm_detail::launch_layout<kLayTN, kAccFast>(g, st);
+}
+
+}  // namespace fp8mlp

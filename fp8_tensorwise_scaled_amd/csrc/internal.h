@@ -75,10 +75,26 @@ enum Epilogue : int {
                       // partial[tile] = max |A| (bf16 bits) when partials is set
 };
 
+// GEMM operand layouts: bit 0 set = A is MN-major ([K, M], the output index
+// contiguous), bit 1 set = B is MN-major ([K, N]); otherwise K-major.
+enum GemmLayout : int {
+  kLayNT = 0,  // A [M, K], B [N, K]: forward
+  kLayNN = 2,  // A [M, K], B [K, N]: grad-input
+  kLayTN = 3,  // A [K, M], B [K, N]: grad-weight
+};
+
+// Accumulation of FP8 products (the FP8MLP_ACCUM_* values of the C ABI).
+enum GemmAccum : int {
+  kAccFast = 0,   // FP8 matrix cores (group-truncated sums)
+  kAccExact = 1,  // codes decoded to bf16, exact products on the bf16 matrix cores
+};
+
 struct GemmArgs {
-  const uint8_t* a;  // [M, K] codes (or bf16 values), K contiguous
-  const uint8_t* b;  // [N, K] codes (or bf16 values), K contiguous
+  const uint8_t* a;  // [M, K] (K-major) or [K, M] (MN-major) codes, or bf16 values [M, K]
+  const uint8_t* b;  // [N, K] (K-major) or [K, N] (MN-major) codes, or bf16 values [N, K]
   int64_t lda, ldb;
+  int layout;  // GemmLayout (bf16 operands: NT only)
+  int accum;   // GemmAccum (FP8 operands)
   int fa, fb;
   const float* sa;
   const float* sb;
@@ -112,6 +128,13 @@ struct GemmArgs {
 
 // Number of output tiles the GEMM will use (size of `partials`).
 int64_t gemm_num_tiles(int64_t M, int64_t N);
+// FP8 products of one layout and accumulation mode (one translation unit each).
+hipError_t launch_gemm_nt_fast(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_nt_exact(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_nn_fast(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_nn_exact(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_tn_fast(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_tn_exact(const GemmArgs& g, hipStream_t st);
 int64_t gemm_swiglu_tiles(int64_t M, int64_t N);  // kEpiSwiGLU with N output columns
 int64_t gemm_max_tiles(int64_t M, int64_t N);  // upper bound over tile configurations
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);

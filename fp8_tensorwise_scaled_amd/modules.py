@@ -21,26 +21,26 @@ def _rows(x: torch.Tensor) -> torch.Tensor:
 
 class _Fp8LinearFn(torch.autograd.Function):
     """y = x W^T with E4M3 x and W; backward with E5M2 dy:
-    dx = dy W (codes of W transposed), dW = dy^T x (codes of dy and x transposed)."""
+    dx = dy W (NN) and dW = dy^T x (TN), both on the forward's row-major codes."""
 
     @staticmethod
     def forward(ctx, x, w):
         x2 = _rows(x)
-        xq, xqt, sx, _ = api.fp8_amax_quant(x2, api.E4M3, want_qt=True)
-        wq, wqt, sw, _ = api.fp8_amax_quant(w.contiguous(), api.E4M3, want_qt=True)
+        xq, _, sx, _ = api.fp8_amax_quant(x2, api.E4M3)
+        wq, _, sw, _ = api.fp8_amax_quant(w.contiguous(), api.E4M3)
         y = api.fp8_linear_fwd(xq, sx, wq, sw)
-        ctx.save_for_backward(xqt, sx, wqt, sw)
+        ctx.save_for_backward(xq, sx, wq, sw)
         ctx.x_shape = x.shape
         return y.reshape(*x.shape[:-1], w.shape[0])
 
     @staticmethod
     def backward(ctx, dy):
-        xqt, sx, wqt, sw = ctx.saved_tensors
+        xq, sx, wq, sw = ctx.saved_tensors
         need_dx, need_dw = ctx.needs_input_grad
         dy2 = _rows(dy.to(torch.bfloat16))
-        gq, gqt, sg, _ = api.fp8_amax_quant(dy2, api.E5M2, want_q=need_dx, want_qt=need_dw)
-        dx = api.fp8_linear_dgrad(gq, sg, wqt, sw).reshape(ctx.x_shape) if need_dx else None
-        dw = api.fp8_linear_wgrad(gqt, sg, xqt, sx) if need_dw else None
+        gq, _, sg, _ = api.fp8_amax_quant(dy2, api.E5M2)
+        dx = api.fp8_linear_dgrad(gq, sg, wq, sw).reshape(ctx.x_shape) if need_dx else None
+        dw = api.fp8_linear_wgrad(gq, sg, xq, sx) if need_dw else None
         return dx, dw
 
 

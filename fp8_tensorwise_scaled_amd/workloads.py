@@ -39,36 +39,32 @@ def _f32(n, device):
 
 @dataclass
 class QuantOut:
-    """Codes of a [rows, cols] tensor: q [rows, ld_q], qt [cols, ld_qt], scale."""
+    """Row-major codes of a [rows, cols] tensor (q [rows, ld]) and its scale."""
     q: torch.Tensor
-    qt: torch.Tensor
     scale: torch.Tensor
     amax: torch.Tensor
     ws: torch.Tensor
 
     @staticmethod
-    def alloc(rows, cols, device, pad_cols_to=1, pad_rows_to=1):
-        """Row-major codes padded to a multiple of pad_cols_to columns and
-        transposed codes padded to pad_rows_to, padding zero-filled."""
-        cp = -(-cols // pad_cols_to) * pad_cols_to
-        rp = -(-rows // pad_rows_to) * pad_rows_to
-        q = _u8((rows, cp), device, zero=cp != cols)
-        qt = _u8((cols, rp), device, zero=rp != rows)
+    def alloc(rows, cols, device, ld_multiple=1):
+        """Codes with a leading dimension rounded up to ld_multiple (the
+        columns past cols are never read: every GEMM masks its reduction)."""
+        ld = -(-cols // ld_multiple) * ld_multiple
         ws = torch.empty(max(api._native.lib().fp8_amax_quant_workspace_bytes(rows, cols), 16),
                          dtype=torch.uint8, device=device)
-        return QuantOut(q, qt, _f32(1, device), _f32(1, device), ws)
+        return QuantOut(_u8((rows, ld), device), _f32(1, device), _f32(1, device), ws)
 
-    def run(self, x, fmt, rows, cols):
-        api.fp8_amax_quant(x, fmt, q=self.q[:, :cols], qt=self.qt[:, :rows], scale=self.scale,
-                           amax=self.amax, ws=self.ws)
+    def run(self, x, fmt, cols):
+        api.fp8_amax_quant(x, fmt, q=self.q[:, :cols], scale=self.scale, amax=self.amax, ws=self.ws)
         return self
 
 
 class LinearSet:
-    """Buffers and calls for one FP8 linear: Y = X W^T, dX = dY W, dW = dY^T X."""
+    """Buffers and calls for one FP8 linear: Y = X W^T (NT), dX = dY W (NN),
+    dW = dY^T X (TN), all three on the row-major codes of X, W and dY."""
 
-    def __init__(self, M, n_in, n_out, device, x_quant: QuantOut | None = None):
-        self.M, self.n_in, self.n_out = M, n_in, n_out
+    def __init__(self, M, n_in, n_out, device, x_quant: QuantOut | None = None, accum=api.ACCUM_FAST):
+        self.M, self.n_in, self.n_out, self.accum = M, n_in, n_out, accum
         self.xq = x_quant or QuantOut.alloc(M, n_in, device)
         self.wq = QuantOut.alloc(n_out, n_in, device)
         self.gq = QuantOut.alloc(M, n_out, device)
@@ -78,18 +74,18 @@ class LinearSet:
 
     def forward(self, x, w, quantize_x=True):
         if quantize_x:
-            self.xq.run(x, E4M3, self.M, self.n_in)
-        self.wq.run(w, E4M3, self.n_out, self.n_in)
+            self.xq.run(x, E4M3, self.n_in)
+        self.wq.run(w, E4M3, self.n_in)
         api.fp8_linear_fwd(self.xq.q[:, :self.n_in], self.xq.scale, self.wq.q[:, :self.n_in], self.wq.scale,
-                           out=self.y)
+                           out=self.y, accum=self.accum)
         return self.y
 
     def backward(self, dy):
-        self.gq.run(dy, E5M2, self.M, self.n_out)
-        api.fp8_linear_dgrad(self.gq.q[:, :self.n_out], self.gq.scale, self.wq.qt[:, :self.n_out],
-                             self.wq.scale, out=self.dx)
-        api.fp8_linear_wgrad(self.gq.qt[:, :self.M], self.gq.scale, self.xq.qt[:, :self.M], self.xq.scale,
-                             out=self.dw)
+        self.gq.run(dy, E5M2, self.n_out)
+        api.fp8_linear_dgrad(self.gq.q[:, :self.n_out], self.gq.scale, self.wq.q[:, :self.n_in], self.wq.scale,
+                             out=self.dx, accum=self.accum)
+        api.fp8_linear_wgrad(self.gq.q[:, :self.n_out], self.gq.scale, self.xq.q[:, :self.n_in], self.xq.scale,
+                             out=self.dw, accum=self.accum)
         return self.dx, self.dw
 
     @property
@@ -100,13 +96,13 @@ class LinearSet:
 class ProjectionSetRunner:
     """Q, K, V (shared input), O and the relu^2 MLP block of one decoder layer."""
 
-    def __init__(self, M, device, d=3072, q_dim=3072, kv_dim=1024, h=12288):
-        self.M, self.d, self.h = M, d, h
+    def __init__(self, M, device, d=3072, q_dim=3072, kv_dim=1024, h=12288, accum=api.ACCUM_FAST):
+        self.M, self.d, self.h, self.accum = M, d, h, accum
         self.x_attn_q = QuantOut.alloc(M, d, device)
-        self.q = LinearSet(M, d, q_dim, device, x_quant=self.x_attn_q)
-        self.k = LinearSet(M, d, kv_dim, device, x_quant=self.x_attn_q)
-        self.v = LinearSet(M, d, kv_dim, device, x_quant=self.x_attn_q)
-        self.o = LinearSet(M, q_dim, d, device)
+        self.q = LinearSet(M, d, q_dim, device, x_quant=self.x_attn_q, accum=accum)
+        self.k = LinearSet(M, d, kv_dim, device, x_quant=self.x_attn_q, accum=accum)
+        self.v = LinearSet(M, d, kv_dim, device, x_quant=self.x_attn_q, accum=accum)
+        self.o = LinearSet(M, q_dim, d, device, accum=accum)
         self.saved = api.Relu2MlpSaved.empty(M, d, h, device)
         self.ws_f = api.relu2_mlp_fwd_workspace(M, d, h, device)
         self.ws_b = api.relu2_mlp_bwd_workspace(M, d, h, device)
@@ -119,18 +115,19 @@ class ProjectionSetRunner:
     def step(self, t):
         """t: dict of bf16 tensors x_attn, w_q, w_k, w_v, x_o, w_o, x_mlp, w_up, w_down,
         dq, dk, dv, do, dy_mlp.  One forward and backward of all six projections."""
-        self.x_attn_q.run(t["x_attn"], E4M3, self.M, self.d)
+        self.x_attn_q.run(t["x_attn"], E4M3, self.d)
         self.q.forward(None, t["w_q"], quantize_x=False)
         self.k.forward(None, t["w_k"], quantize_x=False)
         self.v.forward(None, t["w_v"], quantize_x=False)
         self.o.forward(t["x_o"], t["w_o"])
-        api.relu2_mlp_fwd(t["x_mlp"], t["w_up"], t["w_down"], y=self.y_mlp, saved=self.saved, ws=self.ws_f)
+        api.relu2_mlp_fwd(t["x_mlp"], t["w_up"], t["w_down"], y=self.y_mlp, saved=self.saved, ws=self.ws_f,
+                          accum=self.accum)
         self.q.backward(t["dq"])
         self.k.backward(t["dk"])
         self.v.backward(t["dv"])
         self.o.backward(t["do"])
         api.relu2_mlp_bwd(t["dy_mlp"], self.saved, dx=self.dx_mlp, dw_up=self.dw_up, dw_down=self.dw_down,
-                          bwd_scales=self.bsc, ws=self.ws_b)
+                          bwd_scales=self.bsc, ws=self.ws_b, accum=self.accum)
 
     @property
     def flops(self):
@@ -140,30 +137,28 @@ class ProjectionSetRunner:
 class LMHeadRunner:
     """LM head fwd+bwd for vocabulary N (padded or not).
 
-    The grad-input GEMM reduces over the vocabulary, which the kernel needs
-    in multiples of 16: the codes of dLogits and of W^T are written into
-    zero-filled buffers padded to a multiple of 16 along that axis, so the
-    reduction runs over the padded length with exact zeros past N."""
+    The unpadded vocabulary's codes of dLogits get a leading dimension
+    rounded up to 16 (the GEMMs read 16-byte rows); the grad-input GEMM
+    reduces over exactly N of them, the kernel masking the tail."""
 
-    def __init__(self, M, K, N, device):
-        self.M, self.K, self.N = M, K, N
-        self.Np = -(-N // 16) * 16
+    def __init__(self, M, K, N, device, accum=api.ACCUM_FAST):
+        self.M, self.K, self.N, self.accum = M, K, N, accum
         self.xq = QuantOut.alloc(M, K, device)
-        self.wq = QuantOut.alloc(N, K, device, pad_rows_to=16)       # wq.qt: [K, Np]
-        self.gq = QuantOut.alloc(M, N, device, pad_cols_to=16)       # gq.q:  [M, Np]
+        self.wq = QuantOut.alloc(N, K, device)
+        self.gq = QuantOut.alloc(M, N, device, ld_multiple=16)
         self.y = _bf16((M, N), device)
         self.dx = _bf16((M, K), device)
         self.dw = _bf16((N, K), device)
 
     def step(self, x, w, dlogits):
-        M, K, N, Np = self.M, self.K, self.N, self.Np
-        self.xq.run(x, E4M3, M, K)
-        self.wq.run(w, E4M3, N, K)
-        api.fp8_linear_fwd(self.xq.q, self.xq.scale, self.wq.q, self.wq.scale, out=self.y)
-        self.gq.run(dlogits, E5M2, M, N)
-        api.fp8_linear_dgrad(self.gq.q[:, :Np], self.gq.scale, self.wq.qt[:, :Np], self.wq.scale,
-                             out=self.dx)
-        api.fp8_linear_wgrad(self.gq.qt, self.gq.scale, self.xq.qt, self.xq.scale, out=self.dw)
+        K, N = self.K, self.N
+        self.xq.run(x, E4M3, K)
+        self.wq.run(w, E4M3, K)
+        api.fp8_linear_fwd(self.xq.q, self.xq.scale, self.wq.q, self.wq.scale, out=self.y, accum=self.accum)
+        self.gq.run(dlogits, E5M2, N)
+        g = self.gq.q[:, :N]
+        api.fp8_linear_dgrad(g, self.gq.scale, self.wq.q, self.wq.scale, out=self.dx, accum=self.accum)
+        api.fp8_linear_wgrad(g, self.gq.scale, self.xq.q, self.xq.scale, out=self.dw, accum=self.accum)
 
     @property
     def flops(self):

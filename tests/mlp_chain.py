@@ -104,13 +104,12 @@ def chain_close(got, ref, what):
     assert fro <= 1e-2, (what, fro, mrel, frac)
 
 
-def _strict_rows(got, ref, ref_abs, K, same_rows, what, **floors):
-    """GEMM bound on the rows whose operand row equals the oracle's
-    (`floors`: min_within1 / min_within2 passed on to gemm_close)."""
+def _strict_rows(got, ref, ref_abs, K, same_rows, what):
+    """GEMM bound on the rows whose operand row equals the oracle's."""
     n = int(same_rows.sum())
     print(f"[stage] {what}: {n}/{same_rows.size} rows with identical FP8 operands")
     if n:
-        gemm_close(got[same_rows], ref[same_rows], what, sabs_bits=ref_abs[same_rows], K=K, **floors)
+        gemm_close(got[same_rows], ref[same_rows], what, sabs_bits=ref_abs[same_rows], K=K)
     chain_close(got, ref, what)
 
 

@@ -22,8 +22,7 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
-from tests.gpu_util import (bf16_bits, bits_f64, f32, gemm_bound, gemm_close, oracle_gemm, u8, ulp_bf16,
-                            within_floors)
+from tests.gpu_util import bf16_bits, bits_f64, f32, gemm_bound, gemm_close, oracle_gemm, u8, ulp_bf16
 from tests.mlp_chain import _codes_equal_where, _strict_rows, chain_close
 
 E4, E5 = oracle.E4M3, oracle.E5M2
@@ -195,18 +194,9 @@ def compare(g: dict, o: dict, sc: dict, rows, cols):
                     "columns")
     _codes_equal_where(g["dgq_t"][cols], o["dGqt_c"], dgt == o["dGt_c"], "dGq columns")
     _codes_equal_where(g["duq_t"][cols], o["dUqt_c"], dut == o["dUt_c"], "dUq columns")
-    # The three weight gradients reduce over tokens, and their token-side
-    # operand (dG, dU, A) is a product of two roughly Gaussian factors (dA or
-    # G with U, times dY's 0.1% x100 outlier rows): a few tokens dominate
-    # sum|products|, which the matrix core's truncation error scales with,
-    # so fewer outputs land within one or two ulps although every one stays
-    # inside the element-wise bound.  Measured at M=2048: 99.60% / 99.77%
-    # within one / two ulps for dW_gate.  Floors as for other outlier-heavy
-    # grad-weight reductions.
-    wf = dict(zip(("min_within1", "min_within2"), within_floors(None, heavy_tailed=True)))
     _strict_rows(g["dw_gate"][cols], o["dWg_c"], o["dWg_c_abs"], o["dW_K"],
-                 (g["dgq_t"][cols] == o["dGqt_c"]).all(1), "dW_gate rows", **wf)
+                 (g["dgq_t"][cols] == o["dGqt_c"]).all(1), "dW_gate rows")
     _strict_rows(g["dw_up"][cols], o["dWu_c"], o["dWu_c_abs"], o["dW_K"],
-                 (g["duq_t"][cols] == o["dUqt_c"]).all(1), "dW_up rows", **wf)
+                 (g["duq_t"][cols] == o["dUqt_c"]).all(1), "dW_up rows")
     _strict_rows(np.ascontiguousarray(g["dw_down"][:, cols].T), o["dWdT_c"], o["dWdT_c_abs"], o["dW_K"],
-                 (g["aq_t"][cols] == o["Aqt_c"]).all(1), "dW_down columns", **wf)
+                 (g["aq_t"][cols] == o["Aqt_c"]).all(1), "dW_down columns")

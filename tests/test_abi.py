@@ -35,7 +35,7 @@ def test_header_exports_all_symbols():
 
 def test_abi_version_and_status_strings():
     L = _native.lib()
-    assert L.fp8mlp_abi_version() == 1
+    assert L.fp8mlp_abi_version() == 2
     for s in range(0, 7):
         assert len(_native.status_string(s)) > 0
 
@@ -74,7 +74,8 @@ def test_quant_validation():
 
 def test_gemm_validation():
     L = _native.lib()
-    base = [FAKE, 64, 0, FAKE, FAKE, 64, 0, FAKE, 32, 48, 64, FAKE, 48, None]
+    # fwd (NT): A [M,K], B [N,K];  M=32, N=48, K=64
+    base = [FAKE, 64, 0, FAKE, FAKE, 64, 0, FAKE, 32, 48, 64, FAKE, 48, 0, None]
     for fn in (L.fp8_linear_fwd,):
         assert fn(*[None] + base[1:]) == 1
         a = list(base); a[8] = -1
@@ -85,8 +86,6 @@ def test_gemm_validation():
         assert fn(*a) == 0                          # N = 0
         a = list(base); a[1] = 32
         assert fn(*a) == 1                          # lda < K
-        a = list(base); a[10] = 40; a[1] = 48; a[5] = 48
-        assert fn(*a) == 5                          # K % 16
         a = list(base); a[1] = 72
         assert fn(*a) == 2                          # lda % 16
         a = list(base); a[0] = ctypes.c_void_p(0x10008)
@@ -95,6 +94,10 @@ def test_gemm_validation():
         assert fn(*a) == 1                          # unknown format
         a = list(base); a[12] = 40
         assert fn(*a) == 1                          # ldc < N
+        a = list(base); a[13] = 2
+        assert fn(*a) == 1                          # unknown accumulation mode
+        a = list(base); a[13] = -1
+        assert fn(*a) == 1
     # tile offsets are 32-bit: 255 rows of a 2^24-byte leading dimension do not fit
     a = list(base); a[1] = 1 << 24
     assert L.fp8_linear_fwd(*a) == 5
@@ -104,18 +107,37 @@ def test_gemm_validation():
     # multiple of 16 (a GPU test runs it); 16 bytes more is refused
     a = list(base); a[10] = 4096; a[1] = a[5] = 8_421_488 + 16
     assert L.fp8_linear_fwd(*a) == 5
-    # dgrad: reduction length is N (K argument is the output width)
-    a = [FAKE, 40, 1, FAKE, FAKE, 40, 0, FAKE, 32, 40, 64, FAKE, 64, None]
+    # dgrad (NN): dY [M,N] K-major (ld >= N), W [N,K] MN-major (ld >= K); M=32, N=40, K=64
+    d = [FAKE, 48, 1, FAKE, FAKE, 64, 0, FAKE, 32, 40, 64, FAKE, 64, 0, None]
+    a = list(d); a[1] = 32
+    assert L.fp8_linear_dgrad(*a) == 1              # lddy < N
+    a = list(d); a[5] = 48
+    assert L.fp8_linear_dgrad(*a) == 1              # ldw < K
+    a = list(d); a[5] = 72
+    assert L.fp8_linear_dgrad(*a) == 2              # ldw % 16
+    a = list(d); a[13] = 5
+    assert L.fp8_linear_dgrad(*a) == 1              # unknown accumulation mode
+    # MN-major operands span every reduction row: (N + 128) ldw + 256 < 2^31
+    a = list(d); a[9] = 4096; a[1] = 4096; a[5] = 2 ** 31 // (4096 + 128) // 16 * 16 + 16
     assert L.fp8_linear_dgrad(*a) == 5
-    # wgrad: reduction length is M
-    a = [FAKE, 40, 1, FAKE, FAKE, 40, 0, FAKE, 40, 64, 64, FAKE, 64, None]
+    # wgrad (TN): dY [M,N] and X [M,K] both MN-major; M=40 (reduction), N=48, K=64
+    w = [FAKE, 48, 1, FAKE, FAKE, 64, 0, FAKE, 40, 48, 64, FAKE, 64, 0, None]
+    a = list(w); a[1] = 32
+    assert L.fp8_linear_wgrad(*a) == 1              # lddy < N
+    a = list(w); a[5] = 32
+    assert L.fp8_linear_wgrad(*a) == 1              # ldx < K
+    a = list(w); a[0] = ctypes.c_void_p(0x10008)
+    assert L.fp8_linear_wgrad(*a) == 2              # dY codes not 16-byte aligned
+    # the exact MN-major edge that a GPU test runs: reduction 272, ld 5,368,704;
+    # 16 bytes more is refused
+    a = list(w); a[8] = 272; a[1] = a[5] = 5_368_704 + 16
     assert L.fp8_linear_wgrad(*a) == 5
 
 
 def test_gated_linear_validation():
     L = _native.lib()
     fn = L.fp8_gated_linear_fwd
-    base = [FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 32, 48, 64, FAKE, FAKE, FAKE, 48, None]
+    base = [FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 32, 48, 64, FAKE, FAKE, FAKE, 48, 0, None]
     a = list(base); a[6] = None
     assert fn(*a) == 1                              # no up scale
     a = list(base); a[13] = None
@@ -124,12 +146,16 @@ def test_gated_linear_validation():
     assert fn(*a) == 1                              # no up codes
     a = list(base); a[5] = ctypes.c_void_p(0x10008)
     assert fn(*a) == 2                              # up codes not 16-byte aligned
+    a = list(base); a[1] = a[7] = 72
+    assert fn(*a) == 2                              # leading dimensions % 16
     a = list(base); a[10] = 40; a[1] = a[7] = 48
     assert fn(*a) == 5                              # K % 16
     a = list(base); a[8] = 0
     assert fn(*a) == 0                              # M = 0: nothing written
     a = list(base); a[14] = 40
     assert fn(*a) == 1                              # ldo < N
+    a = list(base); a[15] = 3
+    assert fn(*a) == 1                              # unknown accumulation mode
 
 
 def test_mlp_validation():
@@ -139,22 +165,24 @@ def test_mlp_validation():
     assert L.relu2_mlp_fwd_workspace_bytes(100, 768, 3072) == 0      # M % 16
     saved = _native.Relu2MlpSaved(0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000)
     n = L.relu2_mlp_fwd_workspace_bytes(64, 64, 256)
-    args = [FAKE, FAKE, FAKE, 64, 64, 256, FAKE, ctypes.byref(saved), FAKE, n - 1, None]
+    args = [FAKE, FAKE, FAKE, 64, 64, 256, FAKE, ctypes.byref(saved), FAKE, n - 1, 0, None]
     assert L.relu2_mlp_fwd(*args) == 3
     args[3] = 65
     assert L.relu2_mlp_fwd(*args) == 5
-    args = [FAKE, FAKE, FAKE, 64, 64, 256, None, ctypes.byref(saved), FAKE, n, None]
+    args = [FAKE, FAKE, FAKE, 64, 64, 256, None, ctypes.byref(saved), FAKE, n, 0, None]
     assert L.relu2_mlp_fwd(*args) == 1                               # y missing with M > 0
-    args = [FAKE, FAKE, FAKE, -16, 64, 256, FAKE, ctypes.byref(saved), FAKE, n, None]
+    args = [FAKE, FAKE, FAKE, -16, 64, 256, FAKE, ctypes.byref(saved), FAKE, n, 0, None]
     assert L.relu2_mlp_fwd(*args) == 1                               # M < 0
     assert L.relu2_mlp_fwd_workspace_bytes(0, 64, 256) > 0           # M = 0 is a valid shape
     bad_saved = _native.Relu2MlpSaved(0x10000, 0, 0x10000, 0x10000, 0x10000, 0x10000)
-    args = [FAKE, FAKE, FAKE, 64, 64, 256, FAKE, ctypes.byref(bad_saved), FAKE, n, None]
+    args = [FAKE, FAKE, FAKE, 64, 64, 256, FAKE, ctypes.byref(bad_saved), FAKE, n, 0, None]
     assert L.relu2_mlp_fwd(*args) == 1
+    args = [FAKE, FAKE, FAKE, 64, 64, 256, FAKE, ctypes.byref(saved), FAKE, n, 7, None]
+    assert L.relu2_mlp_fwd(*args) == 1                               # unknown accumulation mode
     nb = L.relu2_mlp_bwd_workspace_bytes(64, 64, 256)
-    args = [FAKE, ctypes.byref(saved), 64, 64, 256, FAKE, FAKE, FAKE, None, FAKE, nb - 1, None]
+    args = [FAKE, ctypes.byref(saved), 64, 64, 256, FAKE, FAKE, FAKE, None, FAKE, nb - 1, 0, None]
     assert L.relu2_mlp_bwd(*args) == 3
-    args = [FAKE, ctypes.byref(saved), 64, 64, 256, ctypes.c_void_p(0x10008), FAKE, FAKE, None, FAKE, nb, None]
+    args = [FAKE, ctypes.byref(saved), 64, 64, 256, ctypes.c_void_p(0x10008), FAKE, FAKE, None, FAKE, nb, 0, None]
     assert L.relu2_mlp_bwd(*args) == 2
     offs = (ctypes.c_size_t * 8)()
     assert L.relu2_mlp_bwd_workspace_layout(64, 64, 256, offs, 8) == 0
@@ -168,7 +196,7 @@ def test_lm_head_ce_validation():
     assert L.fp8_lm_head_ce_workspace_bytes(256, 256, 1 << 23, 64) == 0    # vocabulary beyond the limit
     n = L.fp8_lm_head_ce_workspace_bytes(256, 256, 600, 64)
     f = ctypes.c_float
-    ok = [FAKE, FAKE, FAKE, 256, 256, 600, 590, f(15.0), 64, FAKE, FAKE, FAKE, None, FAKE, n, None]
+    ok = [FAKE, FAKE, FAKE, 256, 256, 600, 590, f(15.0), 64, FAKE, FAKE, FAKE, None, FAKE, n, 0, None]
     def call(**kw):
         a = list(ok)
         for k, v in kw.items():
@@ -182,6 +210,7 @@ def test_lm_head_ce_validation():
     assert call(a9=None) == 1                # loss missing
     assert call(a14=n - 1) == 3              # workspace too small
     assert call(a0=ctypes.c_void_p(0x10008)) == 2   # x not 16-byte aligned
+    assert call(a15=4) == 1                  # unknown accumulation mode
     offs = (ctypes.c_size_t * 14)()
     assert L.fp8_lm_head_ce_workspace_layout(256, 256, 600, 64, offs, 14) == 0
     assert list(offs) == sorted(offs) and offs[0] == 0
@@ -216,7 +245,7 @@ def test_swiglu_mlp_validation():
     assert L.swiglu_mlp_fwd_workspace_bytes(100, d, h) == 0            # M % 16
     assert L.swiglu_mlp_bwd_workspace_bytes(0, d, h) > 0               # M = 0 is a valid shape
     saved = _native.SwigluMlpSaved(*([0x10000] * 8))
-    ok = [FAKE, FAKE, FAKE, FAKE, M, d, h, FAKE, ctypes.byref(saved), FAKE, nf, None]
+    ok = [FAKE, FAKE, FAKE, FAKE, M, d, h, FAKE, ctypes.byref(saved), FAKE, nf, 0, None]
     def fwd(**kw):
         a = list(ok)
         for k, v in kw.items():
@@ -233,7 +262,7 @@ def test_swiglu_mlp_validation():
         f[i] = 0
         bad = _native.SwigluMlpSaved(*f)
         assert fwd(a8=ctypes.byref(bad)) == 1, i
-    okb = [FAKE, ctypes.byref(saved), M, d, h, FAKE, FAKE, FAKE, FAKE, None, FAKE, nb, None]
+    okb = [FAKE, ctypes.byref(saved), M, d, h, FAKE, FAKE, FAKE, FAKE, None, FAKE, nb, 0, None]
     def bwd(**kw):
         a = list(okb)
         for k, v in kw.items():

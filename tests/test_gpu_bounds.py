@@ -62,9 +62,9 @@ def codes(shape, fmt, seed):
 
 
 def test_gemm_outputs_stay_in_bounds():
-    """fwd / dgrad / wgrad, M=304, N=208, K=160 (every reduction length a
-    multiple of 16, every output dimension a ragged tile), outputs with a
-    leading dimension 40 elements wider than the row."""
+    """fwd / dgrad / wgrad, M=304, N=208, K=160 (every output dimension a
+    ragged tile), outputs with a leading dimension 40 elements wider than the
+    row."""
     from fp8_tensorwise_scaled_amd import api
 
     M, N, K = 304, 208, 160
@@ -73,17 +73,19 @@ def test_gemm_outputs_stay_in_bounds():
     wq, sw = codes((N, K), E4, 2)
     gq, sg = codes((M, N), E5, 3)
     calls = (
-        ("fwd", (M, N), lambda out: api.fp8_linear_fwd(to_dev_u8(xq), scal(sx), to_dev_u8(wq), scal(sw), out=out)),
-        ("dgrad", (M, K), lambda out: api.fp8_linear_dgrad(to_dev_u8(gq), scal(sg), to_dev_u8(np.ascontiguousarray(wq.T)),
-                                                           scal(sw), out=out)),
-        ("wgrad", (N, K), lambda out: api.fp8_linear_wgrad(to_dev_u8(np.ascontiguousarray(gq.T)), scal(sg),
-                                                           to_dev_u8(np.ascontiguousarray(xq.T)), scal(sx), out=out)),
+        ("fwd", (M, N), lambda out, acc: api.fp8_linear_fwd(to_dev_u8(xq), scal(sx), to_dev_u8(wq), scal(sw),
+                                                            out=out, accum=acc)),
+        ("dgrad", (M, K), lambda out, acc: api.fp8_linear_dgrad(to_dev_u8(gq), scal(sg), to_dev_u8(wq), scal(sw),
+                                                                out=out, accum=acc)),
+        ("wgrad", (N, K), lambda out, acc: api.fp8_linear_wgrad(to_dev_u8(gq), scal(sg), to_dev_u8(xq), scal(sx),
+                                                                out=out, accum=acc)),
     )
-    for name, (r, c), call in calls:
-        g = Guarded(r, c, torch.bfloat16, ld=c + 40)
-        call(g.view)
-        torch.cuda.synchronize()
-        assert g.intact(), name
+    for accum in (0, 1):
+        for name, (r, c), call in calls:
+            g = Guarded(r, c, torch.bfloat16, ld=c + 40)
+            call(g.view, accum)
+            torch.cuda.synchronize()
+            assert g.intact(), (name, accum)
 
 
 def test_quantiser_outputs_stay_in_bounds():

@@ -133,8 +133,8 @@ def _fp8_linear():
             api.fp8_amax_quant(src, fmt, q=q, qt=qt, scale=sc, amax=am, ws=ws)
         (xq, xqt, sx, _, _), (wq, wqt, sw, _, _), (gq, gqt, sg, _, _) = codes["x"], codes["w"], codes["g"]
         api.fp8_linear_fwd(xq, sx, wq, sw, out=outs["y"])
-        api.fp8_linear_dgrad(gq, sg, wqt, sw, out=outs["dx"])
-        api.fp8_linear_wgrad(gqt, sg, xqt, sx, out=outs["dw"])
+        api.fp8_linear_dgrad(gq, sg, wq, sw, out=outs["dx"])
+        api.fp8_linear_wgrad(gq, sg, xq, sx, out=outs["dw"])
     return step, outs
 
 

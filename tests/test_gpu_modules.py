@@ -44,12 +44,12 @@ def test_fp8_linear_module_matches_direct_calls():
     y = lin(xin)
     y.backward(dy.reshape(3, 64, 320))
     torch.cuda.synchronize()
-    xq, xqt, sx, _ = api.fp8_amax_quant(x, api.E4M3, want_qt=True)
-    wq, wqt, sw, _ = api.fp8_amax_quant(wt, api.E4M3, want_qt=True)
-    gq, gqt, sg, _ = api.fp8_amax_quant(dy, api.E5M2, want_qt=True)
+    xq, _, sx, _ = api.fp8_amax_quant(x, api.E4M3)
+    wq, _, sw, _ = api.fp8_amax_quant(wt, api.E4M3)
+    gq, _, sg, _ = api.fp8_amax_quant(dy, api.E5M2)
     y_ref = api.fp8_linear_fwd(xq, sx, wq, sw)
-    dx_ref = api.fp8_linear_dgrad(gq, sg, wqt, sw)
-    dw_ref = api.fp8_linear_wgrad(gqt, sg, xqt, sx)
+    dx_ref = api.fp8_linear_dgrad(gq, sg, wq, sw)
+    dw_ref = api.fp8_linear_wgrad(gq, sg, xq, sx)
     torch.cuda.synchronize()
     eq = lambda a, b: torch.equal(a.reshape(b.shape).view(torch.int16), b.view(torch.int16))
     assert eq(y.detach(), y_ref) and eq(xin.grad, dx_ref) and eq(lin.weight.grad, dw_ref)
