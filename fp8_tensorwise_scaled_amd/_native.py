@@ -27,11 +27,11 @@ i64, f32p, vp, c_int, szt = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ct
 
 
 class Relu2MlpSaved(ctypes.Structure):
-    _fields_ = [("xq_t", vp), ("uq_t", vp), ("dq_t", vp), ("aq_t", vp), ("h", vp), ("scales", vp)]
+    _fields_ = [("xq", vp), ("uq", vp), ("dq", vp), ("aq", vp), ("h", vp), ("scales", vp)]
 
 
 class SwigluMlpSaved(ctypes.Structure):
-    _fields_ = [("xq_t", vp), ("wgq_t", vp), ("wuq_t", vp), ("wdq_t", vp), ("aq_t", vp), ("g", vp), ("u", vp),
+    _fields_ = [("xq", vp), ("wgq", vp), ("wuq", vp), ("wdq", vp), ("aq", vp), ("g", vp), ("u", vp),
                 ("scales", vp)]
 
 

@@ -177,11 +177,12 @@ def fp8_gated_linear_fwd(xq, sx, wgq, sg, wuq, su, *, g=None, u=None, a=None, ac
 
 @dataclass
 class Relu2MlpSaved:
-    """Forward quantities the backward pass reads (device tensors)."""
-    xq_t: torch.Tensor
-    uq_t: torch.Tensor
-    dq_t: torch.Tensor
-    aq_t: torch.Tensor
+    """Forward quantities the backward pass reads (device tensors): the
+    row-major codes of X, W_up, W_down and A, H and the four scales."""
+    xq: torch.Tensor
+    uq: torch.Tensor
+    dq: torch.Tensor
+    aq: torch.Tensor
     h: torch.Tensor
     scales: torch.Tensor  # sx, su, sd, sa
     M: int
@@ -191,18 +192,18 @@ class Relu2MlpSaved:
     @staticmethod
     def empty(M: int, d: int, h: int, device) -> "Relu2MlpSaved":
         u8 = dict(dtype=torch.uint8, device=device)
-        return Relu2MlpSaved(torch.empty((d, M), **u8), torch.empty((d, h), **u8), torch.empty((h, d), **u8),
-                             torch.empty((h, M), **u8), torch.empty((M, h), dtype=torch.bfloat16, device=device),
+        return Relu2MlpSaved(torch.empty((M, d), **u8), torch.empty((h, d), **u8), torch.empty((d, h), **u8),
+                             torch.empty((M, h), **u8), torch.empty((M, h), dtype=torch.bfloat16, device=device),
                              torch.empty(4, dtype=torch.float32, device=device), M, d, h)
 
     def c_struct(self) -> _native.Relu2MlpSaved:
         M, d, h = self.M, self.d, self.hid
-        for name, shape, dt in (("xq_t", (d, M), torch.uint8), ("uq_t", (d, h), torch.uint8),
-                                ("dq_t", (h, d), torch.uint8), ("aq_t", (h, M), torch.uint8),
+        for name, shape, dt in (("xq", (M, d), torch.uint8), ("uq", (h, d), torch.uint8),
+                                ("dq", (d, h), torch.uint8), ("aq", (M, h), torch.uint8),
                                 ("h", (M, h), torch.bfloat16), ("scales", (4,), torch.float32)):
             _out(getattr(self, name), shape, dt, self.scales.device, "saved." + name, dense=True)
-        return _native.Relu2MlpSaved(self.xq_t.data_ptr(), self.uq_t.data_ptr(), self.dq_t.data_ptr(),
-                                     self.aq_t.data_ptr(), self.h.data_ptr(), self.scales.data_ptr())
+        return _native.Relu2MlpSaved(self.xq.data_ptr(), self.uq.data_ptr(), self.dq.data_ptr(),
+                                     self.aq.data_ptr(), self.h.data_ptr(), self.scales.data_ptr())
 
 
 def relu2_mlp_fwd_workspace(M: int, d: int, h: int, device) -> torch.Tensor:
@@ -220,8 +221,9 @@ def relu2_mlp_bwd_workspace(M: int, d: int, h: int, device) -> torch.Tensor:
 
 
 def workspace_layout(kind: str, M: int, d: int, h: int):
-    offs = (ctypes.c_size_t * 8)()
-    _native.call(f"relu2_mlp_{kind}_workspace_layout", M, d, h, offs, 8)
+    n = 4 if kind == "fwd" else 6
+    offs = (ctypes.c_size_t * n)()
+    _native.call(f"relu2_mlp_{kind}_workspace_layout", M, d, h, offs, n)
     return list(offs)
 
 
@@ -270,12 +272,13 @@ def relu2_mlp_bwd(dy, saved: Relu2MlpSaved, *, dx=None, dw_up=None, dw_down=None
 
 @dataclass
 class SwigluMlpSaved:
-    """Forward quantities the gated block's backward pass reads."""
-    xq_t: torch.Tensor
-    wgq_t: torch.Tensor
-    wuq_t: torch.Tensor
-    wdq_t: torch.Tensor
-    aq_t: torch.Tensor
+    """Forward quantities the gated block's backward pass reads: the
+    row-major codes of X, W_gate, W_up, W_down and A, G, U and five scales."""
+    xq: torch.Tensor
+    wgq: torch.Tensor
+    wuq: torch.Tensor
+    wdq: torch.Tensor
+    aq: torch.Tensor
     g: torch.Tensor
     u: torch.Tensor
     scales: torch.Tensor  # sx, s_gate, s_up, s_down, sa
@@ -287,20 +290,20 @@ class SwigluMlpSaved:
     def empty(M: int, d: int, h: int, device) -> "SwigluMlpSaved":
         u8 = dict(dtype=torch.uint8, device=device)
         bf = dict(dtype=torch.bfloat16, device=device)
-        return SwigluMlpSaved(torch.empty((d, M), **u8), torch.empty((d, h), **u8), torch.empty((d, h), **u8),
-                              torch.empty((h, d), **u8), torch.empty((h, M), **u8), torch.empty((M, h), **bf),
+        return SwigluMlpSaved(torch.empty((M, d), **u8), torch.empty((h, d), **u8), torch.empty((h, d), **u8),
+                              torch.empty((d, h), **u8), torch.empty((M, h), **u8), torch.empty((M, h), **bf),
                               torch.empty((M, h), **bf), torch.empty(5, dtype=torch.float32, device=device),
                               M, d, h)
 
     def c_struct(self) -> _native.SwigluMlpSaved:
         M, d, h = self.M, self.d, self.hid
         u8, bf = torch.uint8, torch.bfloat16
-        for name, shape, dt in (("xq_t", (d, M), u8), ("wgq_t", (d, h), u8), ("wuq_t", (d, h), u8),
-                                ("wdq_t", (h, d), u8), ("aq_t", (h, M), u8), ("g", (M, h), bf), ("u", (M, h), bf),
+        for name, shape, dt in (("xq", (M, d), u8), ("wgq", (h, d), u8), ("wuq", (h, d), u8),
+                                ("wdq", (d, h), u8), ("aq", (M, h), u8), ("g", (M, h), bf), ("u", (M, h), bf),
                                 ("scales", (5,), torch.float32)):
             _out(getattr(self, name), shape, dt, self.scales.device, "saved." + name, dense=True)
-        return _native.SwigluMlpSaved(*(t.data_ptr() for t in (self.xq_t, self.wgq_t, self.wuq_t, self.wdq_t,
-                                                               self.aq_t, self.g, self.u, self.scales)))
+        return _native.SwigluMlpSaved(*(t.data_ptr() for t in (self.xq, self.wgq, self.wuq, self.wdq,
+                                                               self.aq, self.g, self.u, self.scales)))
 
 
 def swiglu_mlp_workspace(kind: str, M: int, d: int, h: int, device) -> torch.Tensor:
@@ -311,7 +314,7 @@ def swiglu_mlp_workspace(kind: str, M: int, d: int, h: int, device) -> torch.Ten
 
 
 def swiglu_workspace_layout(kind: str, M: int, d: int, h: int):
-    n = 11 if kind == "fwd" else 14
+    n = 6 if kind == "fwd" else 11
     offs = (ctypes.c_size_t * n)()
     _native.call(f"swiglu_mlp_{kind}_workspace_layout", M, d, h, offs, n)
     return list(offs)
@@ -439,8 +442,8 @@ def fp8_lm_head_ce_workspace(M: int, K: int, V: int, chunk: int, device) -> torc
 
 
 def lm_head_ce_layout(M: int, K: int, V: int, chunk: int):
-    offs = (ctypes.c_size_t * 14)()
-    _native.call("fp8_lm_head_ce_workspace_layout", M, K, V, chunk, offs, 14)
+    offs = (ctypes.c_size_t * 11)()
+    _native.call("fp8_lm_head_ce_workspace_layout", M, K, V, chunk, offs, 11)
     return list(offs)
 
 

@@ -66,24 +66,23 @@ int run_gemm(int layout, const uint8_t* a, int64_t lda, int fa, const float* sa,
   return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
 
-// ---- MLP workspace layouts (offsets in bytes from ws)
-enum FwdSlot { F_XQ, F_UQ, F_DQ, F_AQ, F_PX, F_PU, F_PD, F_PH, F_COUNT };
-enum BwdSlot { B_GQ, B_GQT, B_DH, B_HQ, B_HQT, B_PG, B_PDH, B_SC, B_COUNT };
+// ---- MLP workspace layouts (offsets in bytes from ws).  The forward's codes
+// and H live in the caller's saved set; the workspaces hold what one pass
+// needs for itself.
+enum FwdSlot { F_PX, F_PU, F_PD, F_PH, F_COUNT };
+enum BwdSlot { B_GQ, B_DH, B_HQ, B_PG, B_PDH, B_SC, B_COUNT };
 
 size_t layout_fwd(int64_t M, int64_t d, int64_t h, size_t* off) {
-  const size_t sz[F_COUNT] = {
-      (size_t)(M * d), (size_t)(h * d), (size_t)(d * h), (size_t)(M * h),
-      (size_t)amax_parts_for(M, d) * 4, (size_t)amax_parts_for(h, d) * 4,
-      (size_t)amax_parts_for(d, h) * 4, (size_t)gemm_max_tiles(M, h) * 4};
+  const size_t sz[F_COUNT] = {(size_t)amax_parts_for(M, d) * 4, (size_t)amax_parts_for(h, d) * 4,
+                              (size_t)amax_parts_for(d, h) * 4, (size_t)gemm_max_tiles(M, h) * 4};
   size_t o = 0;
   for (int i = 0; i < F_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
   return o;
 }
 
 size_t layout_bwd(int64_t M, int64_t d, int64_t h, size_t* off) {
-  const size_t sz[B_COUNT] = {
-      (size_t)(M * d), (size_t)(d * M), (size_t)(M * h) * 2, (size_t)(M * h), (size_t)(h * M),
-      (size_t)amax_parts_for(M, d) * 4, (size_t)gemm_max_tiles(M, h) * 4, 8};
+  const size_t sz[B_COUNT] = {(size_t)(M * d), (size_t)(M * h) * 2, (size_t)(M * h),
+                              (size_t)amax_parts_for(M, d) * 4, (size_t)gemm_max_tiles(M, h) * 4, 8};
   size_t o = 0;
   for (int i = 0; i < B_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
   return o;
@@ -107,16 +106,15 @@ QuantJob make_job(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, in
   return j;
 }
 
-// ---- gated (SwiGLU) MLP workspaces
-enum SgFwdSlot { SF_XQ, SF_WGQ, SF_WUQ, SF_WDQ, SF_A, SF_AQ, SF_PX, SF_PWG, SF_PWU, SF_PWD, SF_PA, SF_COUNT };
-enum SgBwdSlot { SB_GQ, SB_GQT, SB_DA, SB_DG, SB_DU, SB_DGQ, SB_DGQT, SB_DUQ, SB_DUQT, SB_DXF, SB_PG, SB_PDG, SB_PDU,
-                 SB_SC, SB_COUNT };
+// ---- gated (SwiGLU) MLP workspaces (the forward's codes, G and U live in
+// the caller's saved set)
+enum SgFwdSlot { SF_A, SF_PX, SF_PWG, SF_PWU, SF_PWD, SF_PA, SF_COUNT };
+enum SgBwdSlot { SB_GQ, SB_DA, SB_DG, SB_DU, SB_DGQ, SB_DUQ, SB_DXF, SB_PG, SB_PDG, SB_PDU, SB_SC, SB_COUNT };
 
 size_t layout_sg_fwd(int64_t M, int64_t d, int64_t h, size_t* off) {
   const size_t sz[SF_COUNT] = {
-      (size_t)(M * d), (size_t)(h * d), (size_t)(h * d), (size_t)(d * h), (size_t)(M * h) * 2, (size_t)(M * h),
-      (size_t)amax_parts_for(M, d) * 4, (size_t)amax_parts_for(h, d) * 4, (size_t)amax_parts_for(h, d) * 4,
-      (size_t)amax_parts_for(d, h) * 4, (size_t)gemm_swiglu_tiles(M, h) * 4};
+      (size_t)(M * h) * 2, (size_t)amax_parts_for(M, d) * 4, (size_t)amax_parts_for(h, d) * 4,
+      (size_t)amax_parts_for(h, d) * 4, (size_t)amax_parts_for(d, h) * 4, (size_t)gemm_swiglu_tiles(M, h) * 4};
   size_t o = 0;
   for (int i = 0; i < SF_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
   return o;
@@ -125,9 +123,8 @@ size_t layout_sg_fwd(int64_t M, int64_t d, int64_t h, size_t* off) {
 size_t layout_sg_bwd(int64_t M, int64_t d, int64_t h, size_t* off) {
   const size_t mh = (size_t)(M * h);
   const size_t sz[SB_COUNT] = {
-      (size_t)(M * d), (size_t)(d * M), mh * 2, mh * 2, mh * 2, mh, mh, mh, mh, (size_t)(M * d) * 4,
-      (size_t)amax_parts_for(M, d) * 4, (size_t)swiglu_parts_for(M * h) * 4, (size_t)swiglu_parts_for(M * h) * 4,
-      16};
+      (size_t)(M * d), mh * 2, mh * 2, mh * 2, mh, mh, (size_t)(M * d) * 4, (size_t)amax_parts_for(M, d) * 4,
+      (size_t)swiglu_parts_for(M * h) * 4, (size_t)swiglu_parts_for(M * h) * 4, 16};
   size_t o = 0;
   for (int i = 0; i < SB_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
   return o;
@@ -142,16 +139,15 @@ GemmArgs gemm_args(const uint8_t* a, int64_t lda, int fa, const float* sa, const
 }
 
 // ---- LM head + softcapped cross-entropy workspace
-enum LmSlot { L_XQ, L_XQT, L_WQ, L_WQT, L_Z, L_DZQ, L_DZQT, L_DWF, L_LOSS, L_PX, L_PW, L_PZ, L_NV, L_SC, L_COUNT };
+enum LmSlot { L_XQ, L_WQ, L_Z, L_DZQ, L_DWF, L_LOSS, L_PX, L_PW, L_PZ, L_NV, L_SC, L_COUNT };
 
 int64_t pad16(int64_t v) { return (v + 15) / 16 * 16; }
 
 size_t layout_lm_ce(int64_t M, int64_t K, int64_t V, int64_t C, size_t* off) {
   const int64_t Vp = pad16(V), nchunks = M > 0 ? (M + C - 1) / C : 0;
   const size_t sz[L_COUNT] = {
-      (size_t)(M * K), (size_t)(K * M), (size_t)(V * K), (size_t)(K * Vp), (size_t)(C * Vp) * 2,
-      (size_t)(C * Vp), (size_t)(V * C), (size_t)(V * K) * 4, (size_t)M * 4,
-      (size_t)amax_parts_for(M, K) * 4, (size_t)amax_parts_for(V, K) * 4, (size_t)C * 4, 16,
+      (size_t)(M * K), (size_t)(V * K), (size_t)(C * Vp) * 2, (size_t)(C * Vp), (size_t)(V * K) * 4,
+      (size_t)M * 4, (size_t)amax_parts_for(M, K) * 4, (size_t)amax_parts_for(V, K) * 4, (size_t)C * 4, 16,
       (size_t)(2 + nchunks) * 4};
   size_t o = 0;
   for (int i = 0; i < L_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
@@ -320,13 +316,13 @@ int relu2_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offs
 int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_down, int64_t M,
                   int64_t d, int64_t h, uint16_t* y, const relu2_mlp_saved* saved, void* ws,
                   size_t ws_bytes, int accum, void* stream) {
-  if (!w_up || !w_down || !saved || !saved->uq_t || !saved->dq_t || !saved->scales) return FP8MLP_EINVAL;
+  if (!w_up || !w_down || !saved || !saved->uq || !saved->dq || !saved->scales) return FP8MLP_EINVAL;
   if (!accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
   // buffers with M rows may be NULL when M == 0 (no tokens)
-  if (M > 0 && (!x || !y || !saved->xq_t || !saved->aq_t || !saved->h)) return FP8MLP_EINVAL;
-  const void* ptrs[] = {x, w_up, w_down, y, saved->xq_t, saved->uq_t, saved->dq_t, saved->aq_t, saved->h};
+  if (M > 0 && (!x || !y || !saved->xq || !saved->aq || !saved->h)) return FP8MLP_EINVAL;
+  const void* ptrs[] = {x, w_up, w_down, y, saved->xq, saved->uq, saved->dq, saved->aq, saved->h};
   for (const void* p : ptrs)
     if (!a16(p)) return FP8MLP_EALIGN;
   if (((uintptr_t)saved->scales & 3u) != 0) return FP8MLP_EALIGN;
@@ -336,7 +332,6 @@ int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_dow
   if (!a16(ws)) return FP8MLP_EALIGN;
 
   uint8_t* w8 = (uint8_t*)ws;
-  uint8_t *xq = w8 + off[F_XQ], *uq = w8 + off[F_UQ], *dq = w8 + off[F_DQ], *aq = w8 + off[F_AQ];
   uint32_t* px = (uint32_t*)(w8 + off[F_PX]);
   uint32_t* pu = (uint32_t*)(w8 + off[F_PU]);
   uint32_t* pd = (uint32_t*)(w8 + off[F_PD]);
@@ -347,49 +342,43 @@ int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_dow
   // 1-2. quantise X, W_up, W_down (E4M3) in one amax launch and one cast launch
   QuantBatch b{};
   b.njobs = 3;
-  b.job[0] = make_job(x, M, d, d, FP8MLP_E4M3, xq, d, saved->xq_t, M, &sc[0], nullptr, px,
+  b.job[0] = make_job(x, M, d, d, FP8MLP_E4M3, saved->xq, d, nullptr, 0, &sc[0], nullptr, px,
                       amax_parts_for(M, d), kModePlain);
-  b.job[1] = make_job(w_up, h, d, d, FP8MLP_E4M3, uq, d, saved->uq_t, h, &sc[1], nullptr, pu,
+  b.job[1] = make_job(w_up, h, d, d, FP8MLP_E4M3, saved->uq, d, nullptr, 0, &sc[1], nullptr, pu,
                       amax_parts_for(h, d), kModePlain);
-  b.job[2] = make_job(w_down, d, h, h, FP8MLP_E4M3, dq, h, saved->dq_t, d, &sc[2], nullptr, pd,
+  b.job[2] = make_job(w_down, d, h, h, FP8MLP_E4M3, saved->dq, h, nullptr, 0, &sc[2], nullptr, pd,
                       amax_parts_for(d, h), kModePlain);
   if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
   if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 3. H = Xq . Uq^T with the relu^2 max epilogue
-  GemmArgs g{};
-  g.a = xq; g.lda = d; g.fa = FP8MLP_E4M3; g.sa = &sc[0];
-  g.b = uq; g.ldb = d; g.fb = FP8MLP_E4M3; g.sb = &sc[1];
-  g.M = M; g.N = h; g.K = d; g.c = saved->h; g.ldc = h; g.epi = kEpiRelu2Max; g.partials = ph;
-  g.accum = accum;
+  // 3. H = Xq . Uq^T (NT) with the relu^2 max epilogue
+  GemmArgs g = gemm_args(saved->xq, d, FP8MLP_E4M3, &sc[0], saved->uq, d, FP8MLP_E4M3, &sc[1], M, h, d,
+                         kEpiRelu2Max);
+  g.c = saved->h; g.ldc = h; g.partials = ph; g.accum = accum;
   if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 4. Aq = quant(RN_bf16(relu(H)^2)), amax from the epilogue's partials
   QuantBatch ba{};
   ba.njobs = 1;
-  ba.job[0] = make_job(saved->h, M, h, h, FP8MLP_E4M3, aq, h, saved->aq_t, M, &sc[3], nullptr, ph,
+  ba.job[0] = make_job(saved->h, M, h, h, FP8MLP_E4M3, saved->aq, h, nullptr, 0, &sc[3], nullptr, ph,
                        (int)gemm_num_tiles(M, h), kModeRelu2);
   if (launch_cast(ba, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 5. Y = Aq . Dq^T
-  GemmArgs g2{};
-  g2.a = aq; g2.lda = h; g2.fa = FP8MLP_E4M3; g2.sa = &sc[3];
-  g2.b = dq; g2.ldb = h; g2.fb = FP8MLP_E4M3; g2.sb = &sc[2];
-  g2.M = M; g2.N = d; g2.K = h; g2.c = y; g2.ldc = d; g2.epi = kEpiStore;
-  g2.accum = accum;
+  // 5. Y = Aq . Dq^T (NT)
+  GemmArgs g2 = gemm_args(saved->aq, h, FP8MLP_E4M3, &sc[3], saved->dq, h, FP8MLP_E4M3, &sc[2], M, d, h, kEpiStore);
+  g2.c = y; g2.ldc = d; g2.accum = accum;
   return hip_status(launch_gemm(g2, s));
 }
 
 int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, int64_t d, int64_t h,
                   uint16_t* dx, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales, void* ws,
                   size_t ws_bytes, int accum, void* stream) {
-  if (!saved || !dw_up || !dw_down || !saved->uq_t || !saved->dq_t || !saved->scales) return FP8MLP_EINVAL;
+  if (!saved || !dw_up || !dw_down || !saved->uq || !saved->dq || !saved->scales) return FP8MLP_EINVAL;
   if (!accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
-  if (M > 0 && (!dy || !dx || !saved->xq_t || !saved->aq_t || !saved->h)) return FP8MLP_EINVAL;
-  const void* ptrs[] = {dy, dx, dw_up, dw_down, saved->xq_t, saved->uq_t, saved->dq_t, saved->aq_t,
-                        saved->h};
+  if (M > 0 && (!dy || !dx || !saved->xq || !saved->aq || !saved->h)) return FP8MLP_EINVAL;
+  const void* ptrs[] = {dy, dx, dw_up, dw_down, saved->xq, saved->uq, saved->dq, saved->aq, saved->h};
   for (const void* p : ptrs)
     if (!a16(p)) return FP8MLP_EALIGN;
   if (((uintptr_t)saved->scales & 3u) != 0 || ((uintptr_t)bwd_scales & 3u) != 0) return FP8MLP_EALIGN;
@@ -399,7 +388,7 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
   if (!a16(ws)) return FP8MLP_EALIGN;
 
   uint8_t* w8 = (uint8_t*)ws;
-  uint8_t *gq = w8 + off[B_GQ], *gqt = w8 + off[B_GQT], *hq = w8 + off[B_HQ], *hqt = w8 + off[B_HQT];
+  uint8_t *gq = w8 + off[B_GQ], *hq = w8 + off[B_HQ];
   uint16_t* dh = (uint16_t*)(w8 + off[B_DH]);
   uint32_t* pg = (uint32_t*)(w8 + off[B_PG]);
   uint32_t* pdh = (uint32_t*)(w8 + off[B_PDH]);
@@ -407,52 +396,39 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
   const float* sc = saved->scales;
   hipStream_t s = (hipStream_t)stream;
 
-  // 1. Gq = quant(dY) (E5M2), row-major and transposed
+  // 1. Gq = quant(dY) (E5M2)
   QuantBatch b{};
   b.njobs = 1;
-  b.job[0] = make_job(dy, M, d, d, FP8MLP_E5M2, gq, d, gqt, M, &bsc[0], nullptr, pg,
-                      amax_parts_for(M, d), kModePlain);
+  b.job[0] = make_job(dy, M, d, d, FP8MLP_E5M2, gq, d, nullptr, 0, &bsc[0], nullptr, pg, amax_parts_for(M, d),
+                      kModePlain);
   if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
   if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 2. dW_down[d,h] = Gq^T . Aq   (reduction over the M tokens)
-  GemmArgs g{};
-  g.a = gqt; g.lda = M; g.fa = FP8MLP_E5M2; g.sa = &bsc[0];
-  g.b = saved->aq_t; g.ldb = M; g.fb = FP8MLP_E4M3; g.sb = &sc[3];
-  g.M = d; g.N = h; g.K = M; g.c = dw_down; g.ldc = h; g.epi = kEpiStore;
-  g.accum = accum;
+  // 2. dW_down[d,h] = Gq^T . Aq (TN, reduction over the M tokens)
+  GemmArgs g = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], saved->aq, h, FP8MLP_E4M3, &sc[3], d, h, M, kEpiStore);
+  g.layout = kLayTN; g.c = dw_down; g.ldc = h; g.accum = accum;
   if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 3. dA = Gq . Dq (reduction over d), fused dH = RN_bf16(2 relu(H) dA) and max |dH|
-  GemmArgs g2{};
-  g2.a = gq; g2.lda = d; g2.fa = FP8MLP_E5M2; g2.sa = &bsc[0];
-  g2.b = saved->dq_t; g2.ldb = d; g2.fb = FP8MLP_E4M3; g2.sb = &sc[2];
-  g2.M = M; g2.N = h; g2.K = d; g2.c = dh; g2.ldc = h; g2.epi = kEpiRelu2Bwd;
-  g2.aux = saved->h; g2.ldaux = h; g2.partials = pdh;
-  g2.accum = accum;
+  // 3. dA = Gq . Dq (NN, reduction over d), fused dH = RN_bf16(2 relu(H) dA) and max |dH|
+  GemmArgs g2 = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], saved->dq, h, FP8MLP_E4M3, &sc[2], M, h, d, kEpiRelu2Bwd);
+  g2.layout = kLayNN; g2.c = dh; g2.ldc = h; g2.aux = saved->h; g2.ldaux = h; g2.partials = pdh; g2.accum = accum;
   if (launch_gemm(g2, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 4. Hq = quant(dH) (E5M2), amax from the epilogue's partials
   QuantBatch bh{};
   bh.njobs = 1;
-  bh.job[0] = make_job(dh, M, h, h, FP8MLP_E5M2, hq, h, hqt, M, &bsc[1], nullptr, pdh,
-                       (int)gemm_num_tiles(M, h), kModePlain);
+  bh.job[0] = make_job(dh, M, h, h, FP8MLP_E5M2, hq, h, nullptr, 0, &bsc[1], nullptr, pdh, (int)gemm_num_tiles(M, h),
+                       kModePlain);
   if (launch_cast(bh, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 5. dW_up[h,d] = Hq^T . Xq   (reduction over the M tokens)
-  GemmArgs g3{};
-  g3.a = hqt; g3.lda = M; g3.fa = FP8MLP_E5M2; g3.sa = &bsc[1];
-  g3.b = saved->xq_t; g3.ldb = M; g3.fb = FP8MLP_E4M3; g3.sb = &sc[0];
-  g3.M = h; g3.N = d; g3.K = M; g3.c = dw_up; g3.ldc = d; g3.epi = kEpiStore;
-  g3.accum = accum;
+  // 5. dW_up[h,d] = Hq^T . Xq (TN, reduction over the M tokens)
+  GemmArgs g3 = gemm_args(hq, h, FP8MLP_E5M2, &bsc[1], saved->xq, d, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
+  g3.layout = kLayTN; g3.c = dw_up; g3.ldc = d; g3.accum = accum;
   if (launch_gemm(g3, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 6. dX[M,d] = Hq . Uq   (reduction over h)
-  GemmArgs g4{};
-  g4.a = hq; g4.lda = h; g4.fa = FP8MLP_E5M2; g4.sa = &bsc[1];
-  g4.b = saved->uq_t; g4.ldb = h; g4.fb = FP8MLP_E4M3; g4.sb = &sc[1];
-  g4.M = M; g4.N = d; g4.K = h; g4.c = dx; g4.ldc = d; g4.epi = kEpiStore;
-  g4.accum = accum;
+  // 6. dX[M,d] = Hq . Uq (NN, reduction over h)
+  GemmArgs g4 = gemm_args(hq, h, FP8MLP_E5M2, &bsc[1], saved->uq, d, FP8MLP_E4M3, &sc[1], M, d, h, kEpiStore);
+  g4.layout = kLayNN; g4.c = dx; g4.ldc = d; g4.accum = accum;
   return hip_status(launch_gemm(g4, s));
 }
 
@@ -487,9 +463,9 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
 
   const int64_t Vp = pad16(V), C = chunk;
   uint8_t* w8 = (uint8_t*)ws;
-  uint8_t *xq = w8 + off[L_XQ], *xqt = w8 + off[L_XQT], *wq = w8 + off[L_WQ], *wqt = w8 + off[L_WQT];
+  uint8_t *xq = w8 + off[L_XQ], *wq = w8 + off[L_WQ];
   uint16_t* zb = (uint16_t*)(w8 + off[L_Z]);
-  uint8_t *dzq = w8 + off[L_DZQ], *dzqt = w8 + off[L_DZQT];
+  uint8_t* dzq = w8 + off[L_DZQ];
   float* dwf = (float*)(w8 + off[L_DWF]);
   float* loss_rows = (float*)(w8 + off[L_LOSS]);
   uint32_t* px = (uint32_t*)(w8 + off[L_PX]);
@@ -499,55 +475,47 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
   float* sc = scales ? scales : (float*)(w8 + off[L_SC]);
   hipStream_t s = (hipStream_t)stream;
 
-  // 1. targets that count, then X and W quantised tensorwise (E4M3), both
-  //    row-major and transposed, in one amax and one cast launch
+  // 1. targets that count, then X and W quantised tensorwise (E4M3) in one
+  //    amax and one cast launch
   if (launch_count_valid(targets, M, n_classes, nv, s) != hipSuccess) return FP8MLP_EHIP;
   QuantBatch b{};
   b.njobs = 2;
-  b.job[0] = make_job(x, M, K, K, FP8MLP_E4M3, xq, K, xqt, M, &sc[0], nullptr, px, amax_parts_for(M, K),
+  b.job[0] = make_job(x, M, K, K, FP8MLP_E4M3, xq, K, nullptr, 0, &sc[0], nullptr, px, amax_parts_for(M, K),
                       kModePlain);
-  b.job[1] = make_job(w, V, K, K, FP8MLP_E4M3, wq, K, wqt, Vp, &sc[1], nullptr, pw, amax_parts_for(V, K),
+  b.job[1] = make_job(w, V, K, K, FP8MLP_E4M3, wq, K, nullptr, 0, &sc[1], nullptr, pw, amax_parts_for(V, K),
                       kModePlain);
   if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
   if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
-  // reduction columns past V of the grad-input operands hold zero codes
-  if (launch_zero_cols(wqt, K, Vp, V, Vp, s) != hipSuccess) return FP8MLP_EHIP;
-  if (launch_zero_cols(dzq, C, Vp, V, Vp, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 2. chunks of C rows: logits, loss and dZ, dZ codes, grad-input, grad-weight
   int64_t k = 0;
   for (int64_t c0 = 0; c0 < M; c0 += C, ++k) {
     const int64_t rows = M - c0 < C ? M - c0 : C;
-    GemmArgs g{};  // Z = Xq_k . Wq^T  (bf16, leading dimension Vp)
-    g.a = xq + c0 * K; g.lda = K; g.fa = FP8MLP_E4M3; g.sa = &sc[0];
-    g.b = wq; g.ldb = K; g.fb = FP8MLP_E4M3; g.sb = &sc[1];
-    g.M = rows; g.N = V; g.K = K; g.c = zb; g.ldc = Vp; g.epi = kEpiStore;
-    g.accum = accum;
+    // Z = Xq_k . Wq^T (NT; bf16, leading dimension Vp)
+    GemmArgs g = gemm_args(xq + c0 * K, K, FP8MLP_E4M3, &sc[0], wq, K, FP8MLP_E4M3, &sc[1], rows, V, K, kEpiStore);
+    g.c = zb; g.ldc = Vp; g.accum = accum;
     if (launch_gemm(g, s) != hipSuccess) return FP8MLP_EHIP;
     if (launch_softcap_ce(zb, rows, V, Vp, n_classes, softcap, targets + c0, nv, loss_rows + c0, pz, s) !=
         hipSuccess)
       return FP8MLP_EHIP;
     QuantBatch bz{};  // dZ codes with this chunk's own scale (row partials)
     bz.njobs = 1;
-    bz.job[0] = make_job(zb, rows, V, Vp, FP8MLP_E5M2, dzq, Vp, dzqt, C, &sc[2 + k], nullptr, pz, (int)rows,
+    bz.job[0] = make_job(zb, rows, V, Vp, FP8MLP_E5M2, dzq, Vp, nullptr, 0, &sc[2 + k], nullptr, pz, (int)rows,
                          kModePlain);
     if (launch_cast(bz, s) != hipSuccess) return FP8MLP_EHIP;
-    GemmArgs gd{};  // dX_k = dZq_k . Wq   (reduction over the padded vocabulary)
-    gd.a = dzq; gd.lda = Vp; gd.fa = FP8MLP_E5M2; gd.sa = &sc[2 + k];
-    gd.b = wqt; gd.ldb = Vp; gd.fb = FP8MLP_E4M3; gd.sb = &sc[1];
-    gd.M = rows; gd.N = K; gd.K = Vp; gd.c = dx + c0 * K; gd.ldc = K; gd.epi = kEpiStore;
-    gd.accum = accum;
+    // dX_k = dZq_k . Wq (NN, reduction over the V classes' rows of the vocabulary)
+    GemmArgs gd = gemm_args(dzq, Vp, FP8MLP_E5M2, &sc[2 + k], wq, K, FP8MLP_E4M3, &sc[1], rows, K, V, kEpiStore);
+    gd.layout = kLayNN; gd.c = dx + c0 * K; gd.ldc = K; gd.accum = accum;
     if (launch_gemm(gd, s) != hipSuccess) return FP8MLP_EHIP;
-    GemmArgs gw{};  // dW (+)= RN32(s_k sx) dZq_k^T . Xq_k   (reduction over the chunk's rows)
-    gw.a = dzqt; gw.lda = C; gw.fa = FP8MLP_E5M2; gw.sa = &sc[2 + k];
-    gw.b = xqt + c0; gw.ldb = M; gw.fb = FP8MLP_E4M3; gw.sb = &sc[0];
-    gw.M = V; gw.N = K; gw.K = rows; gw.cf = dwf; gw.ldc = K;
+    // dW (+)= RN32(s_k sx) dZq_k^T . Xq_k (TN, reduction over the chunk's rows)
+    GemmArgs gw = gemm_args(dzq, Vp, FP8MLP_E5M2, &sc[2 + k], xq + c0 * K, K, FP8MLP_E4M3, &sc[0], V, K, rows,
+                            kEpiStore);
+    gw.layout = kLayTN; gw.cf = dwf; gw.ldc = K; gw.accum = accum;
     // fp32 accumulation over the chunks; the last chunk adds its product and
     // rounds the sum once to bf16 into dw (a single chunk rounds directly)
     const bool last = c0 + C >= M;
     gw.epi = !last ? (k == 0 ? kEpiStoreF32 : kEpiAccF32) : (k == 0 ? kEpiStore : kEpiAccF32Bf16);
     if (last) gw.c = dw;
-    gw.accum = accum;
     if (launch_gemm(gw, s) != hipSuccess) return FP8MLP_EHIP;
   }
 
@@ -583,13 +551,12 @@ int swiglu_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* off
 int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                    int64_t M, int64_t d, int64_t h, uint16_t* y, const swiglu_mlp_saved* sv, void* ws,
                    size_t ws_bytes, int accum, void* stream) {
-  if (!w_gate || !w_up || !w_down || !sv || !sv->wgq_t || !sv->wuq_t || !sv->wdq_t || !sv->scales)
-    return FP8MLP_EINVAL;
+  if (!w_gate || !w_up || !w_down || !sv || !sv->wgq || !sv->wuq || !sv->wdq || !sv->scales) return FP8MLP_EINVAL;
   if (!accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
-  if (M > 0 && (!x || !y || !sv->xq_t || !sv->aq_t || !sv->g || !sv->u)) return FP8MLP_EINVAL;
-  const void* ptrs[] = {x, w_gate, w_up, w_down, y, sv->xq_t, sv->wgq_t, sv->wuq_t, sv->wdq_t, sv->aq_t, sv->g, sv->u};
+  if (M > 0 && (!x || !y || !sv->xq || !sv->aq || !sv->g || !sv->u)) return FP8MLP_EINVAL;
+  const void* ptrs[] = {x, w_gate, w_up, w_down, y, sv->xq, sv->wgq, sv->wuq, sv->wdq, sv->aq, sv->g, sv->u};
   for (const void* p : ptrs)
     if (!a16(p)) return FP8MLP_EALIGN;
   if ((uintptr_t)sv->scales & 3u) return FP8MLP_EALIGN;
@@ -597,57 +564,51 @@ int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_
   if (!ws || ws_bytes < layout_sg_fwd(M, d, h, off)) return FP8MLP_EWORKSPACE;
   if (!a16(ws)) return FP8MLP_EALIGN;
   uint8_t* w8 = (uint8_t*)ws;
-  uint8_t *xq = w8 + off[SF_XQ], *wgq = w8 + off[SF_WGQ], *wuq = w8 + off[SF_WUQ], *wdq = w8 + off[SF_WDQ];
   uint16_t* a = (uint16_t*)(w8 + off[SF_A]);
-  uint8_t* aq = w8 + off[SF_AQ];
   uint32_t* pa = (uint32_t*)(w8 + off[SF_PA]);
   float* sc = sv->scales;
   hipStream_t s = (hipStream_t)stream;
 
-  // 1. X, W_gate, W_up, W_down (E4M3), row-major and transposed, one amax and one cast launch
+  // 1. X, W_gate, W_up, W_down (E4M3), one amax and one cast launch
   QuantBatch b{};
   b.njobs = 4;
-  b.job[0] = make_job(x, M, d, d, FP8MLP_E4M3, xq, d, sv->xq_t, M, &sc[0], nullptr, (uint32_t*)(w8 + off[SF_PX]),
+  b.job[0] = make_job(x, M, d, d, FP8MLP_E4M3, sv->xq, d, nullptr, 0, &sc[0], nullptr, (uint32_t*)(w8 + off[SF_PX]),
                       amax_parts_for(M, d), kModePlain);
-  b.job[1] = make_job(w_gate, h, d, d, FP8MLP_E4M3, wgq, d, sv->wgq_t, h, &sc[1], nullptr,
+  b.job[1] = make_job(w_gate, h, d, d, FP8MLP_E4M3, sv->wgq, d, nullptr, 0, &sc[1], nullptr,
                       (uint32_t*)(w8 + off[SF_PWG]), amax_parts_for(h, d), kModePlain);
-  b.job[2] = make_job(w_up, h, d, d, FP8MLP_E4M3, wuq, d, sv->wuq_t, h, &sc[2], nullptr,
+  b.job[2] = make_job(w_up, h, d, d, FP8MLP_E4M3, sv->wuq, d, nullptr, 0, &sc[2], nullptr,
                       (uint32_t*)(w8 + off[SF_PWU]), amax_parts_for(h, d), kModePlain);
-  b.job[3] = make_job(w_down, d, h, h, FP8MLP_E4M3, wdq, h, sv->wdq_t, d, &sc[3], nullptr,
+  b.job[3] = make_job(w_down, d, h, h, FP8MLP_E4M3, sv->wdq, h, nullptr, 0, &sc[3], nullptr,
                       (uint32_t*)(w8 + off[SF_PWD]), amax_parts_for(d, h), kModePlain);
   if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 2. G, U and A = silu(G) U in one GEMM over the gate and up codes, with
+  // 2. G, U and A = silu(G) U in one NT GEMM over the gate and up codes, with
   //    the per-tile max |A| partials
-  GemmArgs gs = gemm_args(xq, d, FP8MLP_E4M3, &sc[0], wgq, d, FP8MLP_E4M3, &sc[1], M, h, d, kEpiSwiGLU);
-  gs.b2 = wuq; gs.sb2 = &sc[2];
-  gs.c = sv->g; gs.c2 = sv->u; gs.c3 = a; gs.ldc = h; gs.partials = pa;
-  gs.accum = accum;
+  GemmArgs gs = gemm_args(sv->xq, d, FP8MLP_E4M3, &sc[0], sv->wgq, d, FP8MLP_E4M3, &sc[1], M, h, d, kEpiSwiGLU);
+  gs.b2 = sv->wuq; gs.sb2 = &sc[2];
+  gs.c = sv->g; gs.c2 = sv->u; gs.c3 = a; gs.ldc = h; gs.partials = pa; gs.accum = accum;
   if (launch_gemm(gs, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 3. Aq and its transpose, 4. Y = Aq . Wdq^T
+  // 3. Aq, 4. Y = Aq . Wdq^T (NT)
   QuantBatch ba{};
   ba.njobs = 1;
-  ba.job[0] = make_job(a, M, h, h, FP8MLP_E4M3, aq, h, sv->aq_t, M, &sc[4], nullptr, pa,
+  ba.job[0] = make_job(a, M, h, h, FP8MLP_E4M3, sv->aq, h, nullptr, 0, &sc[4], nullptr, pa,
                        (int)gemm_swiglu_tiles(M, h), kModePlain);
   if (launch_cast(ba, s) != hipSuccess) return FP8MLP_EHIP;
-  GemmArgs gy = gemm_args(aq, h, FP8MLP_E4M3, &sc[4], wdq, h, FP8MLP_E4M3, &sc[3], M, d, h, kEpiStore);
-  gy.c = y; gy.ldc = d;
-  gy.accum = accum;
+  GemmArgs gy = gemm_args(sv->aq, h, FP8MLP_E4M3, &sc[4], sv->wdq, h, FP8MLP_E4M3, &sc[3], M, d, h, kEpiStore);
+  gy.c = y; gy.ldc = d; gy.accum = accum;
   return hip_status(launch_gemm(gy, s));
 }
 
 int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, int64_t d, int64_t h, uint16_t* dx,
                    uint16_t* dw_gate, uint16_t* dw_up, uint16_t* dw_down, float* bwd_scales, void* ws,
                    size_t ws_bytes, int accum, void* stream) {
-  if (!sv || !dw_gate || !dw_up || !dw_down || !sv->wgq_t || !sv->wuq_t || !sv->wdq_t || !sv->scales)
-    return FP8MLP_EINVAL;
+  if (!sv || !dw_gate || !dw_up || !dw_down || !sv->wgq || !sv->wuq || !sv->wdq || !sv->scales) return FP8MLP_EINVAL;
   if (!accum_ok(accum)) return FP8MLP_EINVAL;
   int st = check_mlp_dims(M, d, h);
   if (st) return st;
-  if (M > 0 && (!dy || !dx || !sv->xq_t || !sv->aq_t || !sv->g || !sv->u)) return FP8MLP_EINVAL;
-  const void* ptrs[] = {dy, dx, dw_gate, dw_up, dw_down, sv->xq_t, sv->wgq_t, sv->wuq_t, sv->wdq_t, sv->aq_t,
-                        sv->g, sv->u};
+  if (M > 0 && (!dy || !dx || !sv->xq || !sv->aq || !sv->g || !sv->u)) return FP8MLP_EINVAL;
+  const void* ptrs[] = {dy, dx, dw_gate, dw_up, dw_down, sv->xq, sv->wgq, sv->wuq, sv->wdq, sv->aq, sv->g, sv->u};
   for (const void* p : ptrs)
     if (!a16(p)) return FP8MLP_EALIGN;
   if (((uintptr_t)sv->scales & 3u) || ((uintptr_t)bwd_scales & 3u)) return FP8MLP_EALIGN;
@@ -655,60 +616,54 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   if (!ws || ws_bytes < layout_sg_bwd(M, d, h, off)) return FP8MLP_EWORKSPACE;
   if (!a16(ws)) return FP8MLP_EALIGN;
   uint8_t* w8 = (uint8_t*)ws;
-  uint8_t *gq = w8 + off[SB_GQ], *gqt = w8 + off[SB_GQT];
+  uint8_t* gq = w8 + off[SB_GQ];
   uint16_t* da = (uint16_t*)(w8 + off[SB_DA]);
   uint16_t* dg = (uint16_t*)(w8 + off[SB_DG]);
   uint16_t* du = (uint16_t*)(w8 + off[SB_DU]);
-  uint8_t *dgq = w8 + off[SB_DGQ], *dgqt = w8 + off[SB_DGQT], *duq = w8 + off[SB_DUQ], *duqt = w8 + off[SB_DUQT];
+  uint8_t *dgq = w8 + off[SB_DGQ], *duq = w8 + off[SB_DUQ];
   float* dxf = (float*)(w8 + off[SB_DXF]);
   uint32_t *pdg = (uint32_t*)(w8 + off[SB_PDG]), *pdu = (uint32_t*)(w8 + off[SB_PDU]);
   float* bsc = bwd_scales ? bwd_scales : (float*)(w8 + off[SB_SC]);
   const float* sc = sv->scales;
   hipStream_t s = (hipStream_t)stream;
 
-  // 1. Gq = quant(dY) (E5M2), row-major and transposed
+  // 1. Gq = quant(dY) (E5M2)
   QuantBatch b{};
   b.njobs = 1;
-  b.job[0] = make_job(dy, M, d, d, FP8MLP_E5M2, gq, d, gqt, M, &bsc[0], nullptr, (uint32_t*)(w8 + off[SB_PG]),
+  b.job[0] = make_job(dy, M, d, d, FP8MLP_E5M2, gq, d, nullptr, 0, &bsc[0], nullptr, (uint32_t*)(w8 + off[SB_PG]),
                       amax_parts_for(M, d), kModePlain);
   if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 2. dW_down = Gq^T . Aq, 3. dA = Gq . Wd
-  GemmArgs gw = gemm_args(gqt, M, FP8MLP_E5M2, &bsc[0], sv->aq_t, M, FP8MLP_E4M3, &sc[4], d, h, M, kEpiStore);
-  gw.c = dw_down; gw.ldc = h;
-  GemmArgs ga = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->wdq_t, d, FP8MLP_E4M3, &sc[3], M, h, d, kEpiStore);
-  ga.c = da; ga.ldc = h;
-  gw.accum = accum;
-  ga.accum = accum;
+  // 2. dW_down = Gq^T . Aq (TN), 3. dA = Gq . Wd (NN)
+  GemmArgs gw = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->aq, h, FP8MLP_E4M3, &sc[4], d, h, M, kEpiStore);
+  gw.layout = kLayTN; gw.c = dw_down; gw.ldc = h; gw.accum = accum;
+  GemmArgs ga = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->wdq, h, FP8MLP_E4M3, &sc[3], M, h, d, kEpiStore);
+  ga.layout = kLayNN; ga.c = da; ga.ldc = h; ga.accum = accum;
   if (launch_gemm(gw, s) != hipSuccess || launch_gemm(ga, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 4. dG, dU with their amax partials, 5. their E5M2 codes (one cast launch)
   if (launch_swiglu_gate_bwd(sv->g, sv->u, da, dg, du, M * h, pdg, pdu, s) != hipSuccess) return FP8MLP_EHIP;
   QuantBatch bg{};
   bg.njobs = 2;
-  bg.job[0] = make_job(dg, M, h, h, FP8MLP_E5M2, dgq, h, dgqt, M, &bsc[1], nullptr, pdg, swiglu_parts_for(M * h),
+  bg.job[0] = make_job(dg, M, h, h, FP8MLP_E5M2, dgq, h, nullptr, 0, &bsc[1], nullptr, pdg, swiglu_parts_for(M * h),
                        kModePlain);
-  bg.job[1] = make_job(du, M, h, h, FP8MLP_E5M2, duq, h, duqt, M, &bsc[2], nullptr, pdu, swiglu_parts_for(M * h),
+  bg.job[1] = make_job(du, M, h, h, FP8MLP_E5M2, duq, h, nullptr, 0, &bsc[2], nullptr, pdu, swiglu_parts_for(M * h),
                        kModePlain);
   if (launch_cast(bg, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 6. dW_gate = dGq^T . Xq, dW_up = dUq^T . Xq
-  GemmArgs gg = gemm_args(dgqt, M, FP8MLP_E5M2, &bsc[1], sv->xq_t, M, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
-  gg.c = dw_gate; gg.ldc = d;
-  GemmArgs gu = gemm_args(duqt, M, FP8MLP_E5M2, &bsc[2], sv->xq_t, M, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
-  gu.c = dw_up; gu.ldc = d;
-  gg.accum = accum;
-  gu.accum = accum;
+  // 6. dW_gate = dGq^T . Xq, dW_up = dUq^T . Xq (TN)
+  GemmArgs gg = gemm_args(dgq, h, FP8MLP_E5M2, &bsc[1], sv->xq, d, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
+  gg.layout = kLayTN; gg.c = dw_gate; gg.ldc = d; gg.accum = accum;
+  GemmArgs gu = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->xq, d, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
+  gu.layout = kLayTN; gu.c = dw_up; gu.ldc = d; gu.accum = accum;
   if (launch_gemm(gg, s) != hipSuccess || launch_gemm(gu, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 7. dX = dGq . Wg + dUq . Wu, summed in fp32 and rounded once
-  GemmArgs x1 = gemm_args(dgq, h, FP8MLP_E5M2, &bsc[1], sv->wgq_t, h, FP8MLP_E4M3, &sc[1], M, d, h, kEpiStoreF32);
-  x1.cf = dxf; x1.ldc = d;
-  GemmArgs x2 = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->wuq_t, h, FP8MLP_E4M3, &sc[2], M, d, h,
+  // 7. dX = dGq . Wg + dUq . Wu (NN), summed in fp32 and rounded once
+  GemmArgs x1 = gemm_args(dgq, h, FP8MLP_E5M2, &bsc[1], sv->wgq, d, FP8MLP_E4M3, &sc[1], M, d, h, kEpiStoreF32);
+  x1.layout = kLayNN; x1.cf = dxf; x1.ldc = d; x1.accum = accum;
+  GemmArgs x2 = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->wuq, d, FP8MLP_E4M3, &sc[2], M, d, h,
                           kEpiAccF32Bf16);  // adds to the first product and rounds once into dx
-  x2.cf = dxf; x2.c = dx; x2.ldc = d;
-  x1.accum = accum;
-  x2.accum = accum;
+  x2.layout = kLayNN; x2.cf = dxf; x2.c = dx; x2.ldc = d; x2.accum = accum;
   if (launch_gemm(x1, s) != hipSuccess || launch_gemm(x2, s) != hipSuccess) return FP8MLP_EHIP;
   return FP8MLP_OK;
 }

@@ -148,8 +148,6 @@ hipError_t launch_count_valid(const int32_t* targets, int64_t M, int64_t n_class
 hipError_t launch_softcap_ce(uint16_t* z, int64_t rows, int64_t V, int64_t ldz, int64_t n_classes,
                              float softcap, const int32_t* targets, const int32_t* n_valid,
                              float* loss_rows, uint32_t* partials, hipStream_t st);
-// Zero columns [c0, c1) of a [rows, ld] byte matrix.
-hipError_t launch_zero_cols(uint8_t* base, int64_t rows, int64_t ld, int64_t c0, int64_t c1, hipStream_t st);
 int64_t lm_ce_max_vocab();  // largest vocabulary the row kernel takes
 // loss = sum(loss_rows) / n_valid (0 if none).
 hipError_t launch_lm_ce_loss(const float* loss_rows, int64_t M, const int32_t* n_valid, float* loss,

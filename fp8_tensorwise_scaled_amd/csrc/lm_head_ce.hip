@@ -106,7 +106,11 @@ __global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int
   // relative precision where tanh saturates on either side.  Per element:
   // three transcendentals (exp2, reciprocal, exp2) and a few multiplies.
   const float k2 = 2.0f * kLog2e / softcap;   // z -> log2(e) 2 z / c
-  const float clampv = 40.0f * kLog2e;         // |z / c| <= 20
+  // The exponent is clamped at +-125: e stays finite and (e w) w a normal
+  // fp32 number (>= 2^-125) for |z / c| up to 125 / (2 log2(e)) = 43.3.
+  // Beyond that the clamped form overstates 1 - tanh^2, but |dZ| is below
+  // 2^-123 there.
+  const float clampv = 125.0f;
   const float m2cl = -2.0f * softcap * kLog2e;
   auto ew_of = [&](uint32_t bits, float& e, float& w) {
     e = __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(bf16_to_f32(bits) * k2, -clampv, clampv));
@@ -193,12 +197,6 @@ __global__ void __launch_bounds__(kCeThreads) softcap_ce_kernel(uint16_t* z, int
   if (tid == 0) partials[r] = mx;
 }
 
-__global__ void __launch_bounds__(256) zero_cols_kernel(uint8_t* base, int64_t rows, int64_t ld, int64_t c0,
-                                                        int64_t c1) {
-  const int64_t w = c1 - c0, n = rows * w;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    base[(i / w) * ld + c0 + i % w] = 0;
-}
 
 // dw = RN_bf16(dwf), 8 elements per thread step (n % 8 == 0); dwf == nullptr
 // writes zeros.
@@ -256,13 +254,6 @@ hipError_t launch_softcap_ce(uint16_t* z, int64_t rows, int64_t V, int64_t ldz, 
   if (V > kMaxVocab || ldz % 8 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(softcap_ce_kernel, dim3((unsigned)rows), dim3(kCeThreads), 0, st, z, V, ldz, n_classes,
                      softcap, targets, n_valid, loss_rows, partials);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_cols(uint8_t* base, int64_t rows, int64_t ld, int64_t c0, int64_t c1, hipStream_t st) {
-  if (rows <= 0 || c1 <= c0) return hipSuccess;
-  hipLaunchKernelGGL(zero_cols_kernel, dim3(grid_for(rows * (c1 - c0), 256)), dim3(256), 0, st, base, rows,
-                     ld, c0, c1);
   return hipGetLastError();
 }
 

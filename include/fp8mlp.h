@@ -177,41 +177,43 @@ int fp8_linear_wgrad(const uint8_t* dyq, int64_t lddy, int fdy, const float* sdy
                      int64_t N, int64_t K, uint16_t* dw, int64_t lddw, int accum, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* Non-gated relu^2 MLP block: Y = relu(X W_up^T)^2 W_down^T, FP8 GEMMs.    */
+/* Non-gated relu^2 MLP block: Y = relu(X W_up^T)^2 W_down^T, FP8 GEMMs     */
+/* (decomputer.nl, "Doorvoer verhogen", non-gated MLP bullet; appendix:     */
+/* hidden_act relu2, intermediate 12288 for hidden 3072).                   */
 /*   X [M,d], W_up [h,d], W_down [d,h], Y [M,d], all bf16, densely packed.  */
 /*   Forward (E4M3 everywhere):                                             */
 /*     Xq,Uq,Dq = quant(X), quant(W_up), quant(W_down)                      */
-/*     H  = gemm(Xq, Uq)                     bf16 [M,h]                     */
+/*     H  = NT(Xq, Uq)                       bf16 [M,h]                     */
 /*     A  = RN_bf16(relu(H)^2)               (fused: never stored)          */
-/*     Aq = quant(A);  Y = gemm(Aq, Dq)                                     */
+/*     Aq = quant(A);  Y = NT(Aq, Dq)                                       */
 /*   Backward (gradients E5M2):                                             */
-/*     Gq = quant(dY);  dW_down = gemm(Gq^T, Aq^T)                          */
-/*     dA = gemm(Gq, Dq^T);  dH = RN_bf16(2 relu(H) dA)  (fused epilogue)   */
-/*     Hq = quant(dH);  dW_up = gemm(Hq^T, Xq^T);  dX = gemm(Hq, Uq^T)      */
+/*     Gq = quant(dY);  dW_down = TN(Gq, Aq)                                */
+/*     dA = NN(Gq, Dq);  dH = RN_bf16(2 relu(H) dA)  (fused epilogue)       */
+/*     Hq = quant(dH);  dW_up = TN(Hq, Xq);  dX = NN(Hq, Uq)                */
 /* Requirements: M, d, h multiples of 16 (d, h >= 16; M == 0, no tokens, is  */
 /* valid: Y and dX are empty, dW_up and dW_down zero, scales of X, A, dY    */
 /* and dH are 1); all pointers 16-byte aligned.                             */
 /* ------------------------------------------------------------------------ */
 
-/* Forward quantities the backward pass reads.  Caller-allocated device
+/* Forward quantities the backward pass reads: the row-major codes of every
+ * GEMM operand of the forward, H and the scales.  Caller-allocated device
  * buffers, all densely packed; written by relu2_mlp_fwd. */
 typedef struct {
-  uint8_t* xq_t; /* [d, M] E4M3 codes of X, transposed      */
-  uint8_t* uq_t; /* [d, h] E4M3 codes of W_up, transposed   */
-  uint8_t* dq_t; /* [h, d] E4M3 codes of W_down, transposed */
-  uint8_t* aq_t; /* [h, M] E4M3 codes of A, transposed      */
-  uint16_t* h;   /* [M, h] bf16 pre-activation H            */
-  float* scales; /* [4]: sx, su, sd, sa                     */
+  uint8_t* xq;   /* [M, d] E4M3 codes of X      */
+  uint8_t* uq;   /* [h, d] E4M3 codes of W_up   */
+  uint8_t* dq;   /* [d, h] E4M3 codes of W_down */
+  uint8_t* aq;   /* [M, h] E4M3 codes of A      */
+  uint16_t* h;   /* [M, h] bf16 pre-activation H */
+  float* scales; /* [4]: sx, su, sd, sa         */
 } relu2_mlp_saved;
 
 size_t relu2_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
 size_t relu2_mlp_bwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
 
-/* Byte offsets of the intermediates inside the workspaces, for inspection.
- * Forward (n >= 8): Xq [M,d], Uq [h,d], Dq [d,h], Aq [M,h] codes, then the
- * amax partials of X, W_up, W_down and the per-tile max(H) partials.
- * Backward (n >= 8): Gq [M,d], Gq^T [d,M], dH [M,h] bf16, Hq [M,h],
- * Hq^T [h,M], the amax partials of dY and of dH, 2 floats of scales. */
+/* Byte offsets of the regions inside the workspaces, for inspection.
+ * Forward (n >= 4): the amax partials of X, W_up, W_down and the per-tile
+ * max(H) partials.  Backward (n >= 6): Gq [M,d], dH [M,h] bf16, Hq [M,h],
+ * the amax partials of dY and of dH, 2 floats of scales. */
 int relu2_mlp_fwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
 int relu2_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
 
@@ -231,24 +233,24 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
 /* MLP bullet: three matmuls instead of two, intermediate ratio 2.75):       */
 /*   X [M,d], W_gate [h,d], W_up [h,d], W_down [d,h], Y [M,d], bf16, dense.  */
 /*   Forward (E4M3):  Xq, Wgq, Wuq, Wdq = quant(X, W_gate, W_up, W_down)     */
-/*     G = gemm(Xq, Wgq), U = gemm(Xq, Wuq)       bf16 [M,h], kept for bwd   */
+/*     G = NT(Xq, Wgq), U = NT(Xq, Wuq)           bf16 [M,h], kept for bwd   */
 /*     A = RN_bf16(RN32(RN32(G sigmoid(G)) U))    (fp32 sigmoid)             */
-/*     Aq = quant(A);  Y = gemm(Aq, Wdq)                                     */
+/*     Aq = quant(A);  Y = NT(Aq, Wdq)                                       */
 /*   Backward (gradients E5M2):                                              */
-/*     Gq = quant(dY);  dW_down = gemm(Gq^T, Aq^T);  dA = gemm(Gq, Wdq^T)    */
+/*     Gq = quant(dY);  dW_down = TN(Gq, Aq);  dA = NN(Gq, Wdq)              */
 /*     dG = RN_bf16(dA U silu'(G)),  dU = RN_bf16(dA silu(G))  (fp32)         */
 /*     dGq, dUq = quant(dG), quant(dU)                                       */
-/*     dW_gate = gemm(dGq^T, Xq^T);  dW_up = gemm(dUq^T, Xq^T)               */
-/*     dX = RN_bf16(RN32(RN32(p_g dGq.Wgq) + RN32(p_u dUq.Wuq)))  (fp32 sum) */
+/*     dW_gate = TN(dGq, Xq);  dW_up = TN(dUq, Xq)                           */
+/*     dX = RN_bf16(RN32(RN32(p_g NN(dGq,Wgq)) + RN32(p_u NN(dUq,Wuq))))      */
 /* Requirements as for the relu^2 block (M, d, h multiples of 16, M == 0    */
 /* valid, 16-byte aligned pointers).                                        */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-  uint8_t* xq_t;   /* [d, M] codes of X, transposed          */
-  uint8_t* wgq_t;  /* [d, h] codes of W_gate, transposed     */
-  uint8_t* wuq_t;  /* [d, h] codes of W_up, transposed       */
-  uint8_t* wdq_t;  /* [h, d] codes of W_down, transposed     */
-  uint8_t* aq_t;   /* [h, M] codes of A, transposed          */
+  uint8_t* xq;     /* [M, d] codes of X                      */
+  uint8_t* wgq;    /* [h, d] codes of W_gate                 */
+  uint8_t* wuq;    /* [h, d] codes of W_up                   */
+  uint8_t* wdq;    /* [d, h] codes of W_down                 */
+  uint8_t* aq;     /* [M, h] codes of A                      */
   uint16_t* g;     /* [M, h] bf16 gate pre-activation G      */
   uint16_t* u;     /* [M, h] bf16 up projection U            */
   float* scales;   /* 5 floats: sx, s_gate, s_up, s_down, sa */
@@ -256,10 +258,9 @@ typedef struct {
 
 size_t swiglu_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
 size_t swiglu_mlp_bwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
-/* Byte offsets of the workspace regions.  Forward (n >= 11): Xq, Wgq, Wuq,
- * Wdq, A bf16, Aq, amax partials of X, W_gate, W_up, W_down, A.  Backward
- * (n >= 14): Gq, Gq^T, dA, dG, dU, dGq, dGq^T, dUq, dUq^T, dX fp32, amax
- * partials of dY, dG, dU, scales. */
+/* Byte offsets of the workspace regions.  Forward (n >= 6): A bf16, amax
+ * partials of X, W_gate, W_up, W_down, A.  Backward (n >= 11): Gq, dA, dG,
+ * dU, dGq, dUq, dX fp32, amax partials of dY, dG, dU, scales. */
 int swiglu_mlp_fwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
 int swiglu_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
 int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
@@ -309,15 +310,14 @@ int fp8_gated_linear_fwd(const uint8_t* xq, int64_t ldx, const float* sx, const 
 /* ------------------------------------------------------------------------ */
 
 /* Workspace for fp8_lm_head_ce (0 if the shape is not supported).  Holds Xq,
- * Xq^T, Wq, Wq^T, one chunk of logits (bf16, chunk x V rounded up to 16) and
- * its codes, the fp32 dW accumulator and small per-row / per-chunk arrays. */
+ * Wq, one chunk of logits (bf16, chunk x V rounded up to 16) and its codes,
+ * the fp32 dW accumulator and small per-row / per-chunk arrays. */
 size_t fp8_lm_head_ce_workspace_bytes(int64_t M, int64_t K, int64_t V, int64_t chunk);
 
-/* Byte offsets (n >= 14) of the workspace regions, in this order: Xq [M,K],
- * Xq^T [K,M], Wq [V,K], Wq^T [K,Vp], logits/dZ of the last chunk (bf16
- * [chunk,Vp]), dZ codes [chunk,Vp], dZ^T codes [V,chunk], dW fp32 [V,K], row
- * losses [M] fp32, amax partials of X and W, row partials, the valid-row
- * count, scales; Vp = V rounded up to 16. */
+/* Byte offsets (n >= 11) of the workspace regions, in this order: Xq [M,K],
+ * Wq [V,K], logits/dZ of the last chunk (bf16 [chunk,Vp]), dZ codes
+ * [chunk,Vp], dW fp32 [V,K], row losses [M] fp32, amax partials of X and W,
+ * row partials, the valid-row count, scales; Vp = V rounded up to 16. */
 int fp8_lm_head_ce_workspace_layout(int64_t M, int64_t K, int64_t V, int64_t chunk, size_t* offsets, int n);
 
 /*

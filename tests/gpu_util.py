@@ -137,22 +137,19 @@ def check_gemm(got_bits, kind, a, fa, sa, b, fb, sb, what, rows=None, accum=ACC_
 
 def collect_block(inputs, y, saved, ws_f, ws_b, dx, dwu, dwd, bsc) -> dict:
     """Host copies of one relu^2 block pass: inputs, outputs, the saved
-    forward quantities and the workspace intermediates (codes, dH)."""
+    forward quantities (codes of X, W_up, W_down, A and H) and the backward
+    workspace's intermediates (codes of dY, dH and its codes)."""
     from fp8_tensorwise_scaled_amd import api
 
     x, wu, wd, dy = inputs
     M, d = x.shape
     h = wu.shape[0]
-    of = api.workspace_layout("fwd", M, d, h)
     ob = api.workspace_layout("bwd", M, d, h)
-    wf, wb = ws_f.cpu().numpy(), ws_b.cpu().numpy()
+    wb = ws_b.cpu().numpy()
     sl = lambda buf, o, n: buf[o:o + n]
     return dict(
         x=x, wu=wu, wd=wd, dy=dy, y=bf16_bits(y), dx=bf16_bits(dx), dw_up=bf16_bits(dwu),
         dw_down=bf16_bits(dwd), h=bf16_bits(saved.h), scales=f32(saved.scales), bsc=f32(bsc),
-        xq_t=u8(saved.xq_t), uq_t=u8(saved.uq_t), dq_t=u8(saved.dq_t), aq_t=u8(saved.aq_t),
-        xq=sl(wf, of[0], M * d).reshape(M, d), uq=sl(wf, of[1], h * d).reshape(h, d),
-        dq=sl(wf, of[2], d * h).reshape(d, h), aq=sl(wf, of[3], M * h).reshape(M, h),
-        gq=sl(wb, ob[0], M * d).reshape(M, d), gq_t=sl(wb, ob[1], d * M).reshape(d, M),
-        dh=sl(wb, ob[2], 2 * M * h).view(np.uint16).reshape(M, h), hq=sl(wb, ob[3], M * h).reshape(M, h),
-        hq_t=sl(wb, ob[4], h * M).reshape(h, M))
+        xq=u8(saved.xq), uq=u8(saved.uq), dq=u8(saved.dq), aq=u8(saved.aq),
+        gq=sl(wb, ob[0], M * d).reshape(M, d), dh=sl(wb, ob[1], 2 * M * h).view(np.uint16).reshape(M, h),
+        hq=sl(wb, ob[2], M * h).reshape(M, h))

@@ -124,13 +124,13 @@ def test_relu2_block_stays_in_bounds():
     M, d, h = w.M, w.d, w.h
     L = _native.lib()
     gs = {}
-    gs["xq_t"], xq_t = dense((d, M), torch.uint8)
-    gs["uq_t"], uq_t = dense((d, h), torch.uint8)
-    gs["dq_t"], dq_t = dense((h, d), torch.uint8)
-    gs["aq_t"], aq_t = dense((h, M), torch.uint8)
+    gs["xq"], xq = dense((M, d), torch.uint8)
+    gs["uq"], uq = dense((h, d), torch.uint8)
+    gs["dq"], dq = dense((d, h), torch.uint8)
+    gs["aq"], aq = dense((M, h), torch.uint8)
     gs["h"], hh = dense((M, h), torch.bfloat16)
     gs["scales"], sc = dense((4,), torch.float32)
-    saved = api.Relu2MlpSaved(xq_t, uq_t, dq_t, aq_t, hh, sc, M, d, h)
+    saved = api.Relu2MlpSaved(xq, uq, dq, aq, hh, sc, M, d, h)
     gs["y"], y = dense((M, d), torch.bfloat16)
     gs["dx"], dx = dense((M, d), torch.bfloat16)
     gs["dwu"], dwu = dense((h, d), torch.bfloat16)
@@ -154,15 +154,15 @@ def test_swiglu_block_stays_in_bounds():
     M, d, h = w.M, w.d, w.h
     L = _native.lib()
     gs = {}
-    gs["xq_t"], xq_t = dense((d, M), torch.uint8)
-    gs["wgq_t"], wgq_t = dense((d, h), torch.uint8)
-    gs["wuq_t"], wuq_t = dense((d, h), torch.uint8)
-    gs["wdq_t"], wdq_t = dense((h, d), torch.uint8)
-    gs["aq_t"], aq_t = dense((h, M), torch.uint8)
+    gs["xq"], xq = dense((M, d), torch.uint8)
+    gs["wgq"], wgq = dense((h, d), torch.uint8)
+    gs["wuq"], wuq = dense((h, d), torch.uint8)
+    gs["wdq"], wdq = dense((d, h), torch.uint8)
+    gs["aq"], aq = dense((M, h), torch.uint8)
     gs["g"], gg = dense((M, h), torch.bfloat16)
     gs["u"], uu = dense((M, h), torch.bfloat16)
     gs["scales"], sc = dense((5,), torch.float32)
-    saved = api.SwigluMlpSaved(xq_t, wgq_t, wuq_t, wdq_t, aq_t, gg, uu, sc, M, d, h)
+    saved = api.SwigluMlpSaved(xq, wgq, wuq, wdq, aq, gg, uu, sc, M, d, h)
     gs["y"], y = dense((M, d), torch.bfloat16)
     gs["dx"], dx = dense((M, d), torch.bfloat16)
     gs["dwg"], dwg = dense((h, d), torch.bfloat16)

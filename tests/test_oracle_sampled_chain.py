@@ -3,9 +3,11 @@ full oracle chain bit for bit on its rows and columns (transposed products
 sum the same exact products in the same order), so sampled checks at
 M=8192 / 32768 carry the same expected values a full run would."""
 import numpy as np
+import pytest
 
 import oracle
 from fp8_tensorwise_scaled_amd import synth
+from tests.gpu_util import bits_f64
 from tests.mlp_chain import compare_block, full_chain_scales, sampled_chain
 
 
@@ -40,25 +42,31 @@ def _as_gpu_dict(x, wu, wd, dy, f, b):
     return dict(x=x, wu=wu, wd=wd, dy=dy, y=f["y"], dx=b["dx"], dw_up=b["dw_up"], dw_down=b["dw_down"],
                 h=f["h"], scales=np.array([f["sx"], f["su"], f["sd"], f["sa"]], np.float32),
                 bsc=np.array([b["sg"], b["sh"]], np.float32), xq=f["xq"], uq=f["uq"], dq=f["dq"], aq=f["aq"],
-                xq_t=f["xq"].T, uq_t=f["uq"].T, dq_t=f["dq"].T, aq_t=f["aq"].T, gq=b["gq"], gq_t=b["gq"].T,
-                dh=b["dh"], hq=b["hq"], hq_t=b["hq"].T)
+                gq=b["gq"], dh=b["dh"], hq=b["hq"])
 
 
-def test_compare_block_accepts_the_oracle_and_rejects_a_planted_error():
+@pytest.mark.parametrize("accum", [0, 1], ids=["fast", "exact"])
+def test_compare_block_accepts_the_oracle_and_rejects_planted_errors(accum):
+    """The comparison passes the oracle's own chain in both accumulation
+    modes, and fails on one flipped A code, on one dX element moved by a few
+    ulps, and on one dW_down element moved likewise."""
     x, wu, wd, dy = _block()
     sc, f, b = full_chain_scales(x, wu, wd, dy)
     rows, cols = np.arange(192), np.arange(384)
     o = sampled_chain(x, wu, wd, dy, sc, rows, cols)
     g = _as_gpu_dict(x, wu, wd, dy, f, b)
-    compare_block(g, o, sc, rows, cols)
-    # one wrong A code where H is identical must fail
-    bad = dict(g)
-    bad["aq"] = g["aq"].copy()
-    i = np.argwhere(g["aq"] != 0)[0]
-    bad["aq"][tuple(i)] ^= 1
-    try:
-        compare_block(bad, o, sc, rows, cols)
-    except AssertionError:
-        pass
-    else:
-        raise AssertionError("a flipped A code went unnoticed")
+    compare_block(g, o, sc, rows, cols, accum)
+
+    def planted(key, i, delta):
+        bad = dict(g)
+        bad[key] = g[key].copy()
+        bad[key][i] = (bad[key][i].astype(np.int64) + delta).astype(bad[key].dtype)
+        return bad
+
+    i = tuple(np.argwhere(g["aq"] != 0)[0])
+    j = tuple(np.argwhere(np.abs(bits_f64(g["dx"])) > 0)[3])
+    k = tuple(np.argwhere(np.abs(bits_f64(g["dw_down"])) > 0)[5])
+    for what, bad in (("A code", planted("aq", i, 1)), ("dX element", planted("dx", j, 40)),
+                      ("dW_down element", planted("dw_down", k, 40))):
+        with pytest.raises(AssertionError):
+            compare_block(bad, o, sc, rows, cols, accum)
