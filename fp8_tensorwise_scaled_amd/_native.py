@@ -40,6 +40,7 @@ _PROTOS = {
     "fp8mlp_status_string": (ctypes.c_char_p, [c_int]),
     "fp8_amax_quant_workspace_bytes": (szt, [i64, i64]),
     "fp8_amax_quant": (c_int, [vp, i64, i64, i64, c_int, vp, i64, vp, i64, vp, vp, vp, szt, vp]),
+    "fp8_amax_quant_noalloc": (c_int, [vp, i64, i64, i64, c_int, vp, i64, vp, i64, vp, vp, vp]),
     "fp8_rmsnorm_quant_workspace_bytes": (szt, [i64, i64]),
     "fp8_rmsnorm_quant": (c_int, [vp, vp, ctypes.c_float, i64, i64, i64, c_int, vp, i64, vp, i64, vp, vp, vp, vp,
                                   szt, vp]),

@@ -4,12 +4,40 @@
 // Every entry point validates its arguments on the host before enqueuing
 // anything, never allocates, never synchronises, and launches only on the
 // caller's stream.
+#include <mutex>
+
 #include "../../include/fp8mlp.h"
 #include "internal.h"
 
 using namespace fp8mlp;
 
 namespace {
+
+// Scratch memory of fp8_amax_quant_noalloc: the per-block amax partials
+// (amax_parts_for() never exceeds 1024) in a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code uses the array only
+// through the device address hipGetSymbolAddress returns for each GPU.
+constexpr int kNoAllocScratchWords = 1024;
+static __device__ __align__(256) uint32_t scratch[kNoAllocScratchWords];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+int scratch_of_current_device(uint32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8MLP_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return FP8MLP_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP8MLP_EHIP;
+    g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FP8MLP_OK;
+}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -164,6 +192,34 @@ int check_lm_ce_dims(int64_t M, int64_t K, int64_t V, int64_t n_classes, int64_t
   return FP8MLP_OK;
 }
 
+// Argument checks shared by fp8_amax_quant and fp8_amax_quant_noalloc.
+int check_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, const uint8_t* q,
+                     int64_t ldq, const uint8_t* qt, int64_t ldqt, const float* scale) {
+  if (!scale) return FP8MLP_EINVAL;
+  if (rows < 0 || cols < 0 || ldx < cols || !fmt_ok(fmt)) return FP8MLP_EINVAL;
+  if (rows > 0 && cols > 0) {  // an empty tensor only gets its scale (1) and amax (0)
+    if (!x || (!q && !qt)) return FP8MLP_EINVAL;
+    if ((q && ldq < cols) || (qt && ldqt < rows)) return FP8MLP_EINVAL;
+    if ((q && (const void*)q == (const void*)x) || (qt && (const void*)qt == (const void*)x))
+      return FP8MLP_EINVAL;
+    if (!a2(x)) return FP8MLP_EALIGN;
+  }
+  return FP8MLP_OK;
+}
+
+// The amax pass and the cast of one tensor, with `partials` holding
+// amax_parts_for(rows, cols) u32.
+int run_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q, int64_t ldq,
+                   uint8_t* qt, int64_t ldqt, float* scale, float* amax, uint32_t* partials, void* stream) {
+  QuantBatch b{};
+  b.njobs = 1;
+  b.job[0] = make_job(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, partials, amax_parts_for(rows, cols),
+                      kModePlain);
+  hipStream_t st = (hipStream_t)stream;
+  if (launch_amax_partials(b, st) != hipSuccess) return FP8MLP_EHIP;
+  return hip_status(launch_cast(b, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,25 +246,24 @@ size_t fp8_amax_quant_workspace_bytes(int64_t rows, int64_t cols) {
 int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
                    int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale, float* amax, void* ws,
                    size_t ws_bytes, void* stream) {
-  if (!scale) return FP8MLP_EINVAL;
-  if (rows < 0 || cols < 0 || ldx < cols || !fmt_ok(fmt)) return FP8MLP_EINVAL;
-  if (rows > 0 && cols > 0) {  // an empty tensor only gets its scale (1) and amax (0)
-    if (!x || (!q && !qt)) return FP8MLP_EINVAL;
-    if ((q && ldq < cols) || (qt && ldqt < rows)) return FP8MLP_EINVAL;
-    if ((q && (const void*)q == (const void*)x) || (qt && (const void*)qt == (const void*)x))
-      return FP8MLP_EINVAL;
-    if (!a2(x)) return FP8MLP_EALIGN;
-  }
+  int st = check_amax_quant(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale);
+  if (st) return st;
   if (!ws || ws_bytes < fp8_amax_quant_workspace_bytes(rows, cols)) return FP8MLP_EWORKSPACE;
   if (!a16(ws)) return FP8MLP_EALIGN;
-  QuantBatch b{};
-  b.njobs = 1;
-  b.job[0] = make_job(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, (uint32_t*)ws,
-                      amax_parts_for(rows, cols), kModePlain);
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_amax_partials(b, st);
-  if (e != hipSuccess) return FP8MLP_EHIP;
-  return hip_status(launch_cast(b, st));
+  return run_amax_quant(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, (uint32_t*)ws, stream);
+}
+
+int fp8_amax_quant_noalloc(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                           int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale, float* amax, void* stream) {
+  int st = check_amax_quant(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale);
+  if (st) return st;
+  if ((size_t)amax_parts_for(rows, cols) * 4 > sizeof(scratch)) return FP8MLP_ENOTSUP;
+  uint32_t* parts = nullptr;
+  st = scratch_of_current_device(&parts);
+  if (st) return st;
+  // every partial the cast reads is written by this call's amax pass first:
+  // nothing in the scratch has to start at zero
+  return run_amax_quant(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, parts, stream);
 }
 
 size_t fp8_rmsnorm_quant_workspace_bytes(int64_t rows, int64_t cols) {

@@ -121,6 +121,21 @@ int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, i
                    uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale,
                    float* amax, void* ws, size_t ws_bytes, void* stream);
 
+/* fp8_amax_quant for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and errors as
+ * fp8_amax_quant without ws / ws_bytes.  The amax partials live in a
+ * library-owned static device array of 4 KB (1024 u32; no tensor needs
+ * more), one per GPU, held until the process ends and found on the first
+ * call on each GPU (hipGetSymbolAddress) with that GPU current.  The call
+ * allocates nothing.  Calls on one GPU share that array: calls that overlap
+ * on one GPU (different streams, or host threads) race and must be
+ * serialised by the caller.  Nothing in the array has to start at zero: each
+ * call writes every partial it reads. */
+int fp8_amax_quant_noalloc(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                           uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt, float* scale,
+                           float* amax, void* stream);
+
 /* RMSNorm fused with the dynamic tensorwise quantisation of its output (the
  * MLP input X is the RMSNorm of the residual stream; decomputer.nl, appendix:
  * Llama-style RMSNorm, rms_norm_eps 1.0e-6).  Each step in a stated precision:
