@@ -314,7 +314,7 @@ def swiglu_mlp_workspace(kind: str, M: int, d: int, h: int, device) -> torch.Ten
 
 
 def swiglu_workspace_layout(kind: str, M: int, d: int, h: int):
-    n = 6 if kind == "fwd" else 11
+    n = 6 if kind == "fwd" else 10
     offs = (ctypes.c_size_t * n)()
     _native.call(f"swiglu_mlp_{kind}_workspace_layout", M, d, h, offs, n)
     return list(offs)

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp8mlp.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["quant.hip", "gemm.hip", "gemm_nt_fast.hip", "gemm_nt_exact.hip", "gemm_nn_fast.hip",
-           "gemm_nn_exact.hip", "gemm_tn_fast.hip", "gemm_tn_exact.hip", "lm_head_ce.hip", "swiglu.hip",
+           "gemm_nn_exact.hip", "gemm_tn_fast.hip", "gemm_tn_exact.hip", "lm_head_ce.hip",
            "muon.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -137,7 +137,7 @@ QuantJob make_job(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, in
 // ---- gated (SwiGLU) MLP workspaces (the forward's codes, G and U live in
 // the caller's saved set)
 enum SgFwdSlot { SF_A, SF_PX, SF_PWG, SF_PWU, SF_PWD, SF_PA, SF_COUNT };
-enum SgBwdSlot { SB_GQ, SB_DA, SB_DG, SB_DU, SB_DGQ, SB_DUQ, SB_DXF, SB_PG, SB_PDG, SB_PDU, SB_SC, SB_COUNT };
+enum SgBwdSlot { SB_GQ, SB_DG, SB_DU, SB_DGQ, SB_DUQ, SB_DXF, SB_PG, SB_PDG, SB_PDU, SB_SC, SB_COUNT };
 
 size_t layout_sg_fwd(int64_t M, int64_t d, int64_t h, size_t* off) {
   const size_t sz[SF_COUNT] = {
@@ -151,8 +151,8 @@ size_t layout_sg_fwd(int64_t M, int64_t d, int64_t h, size_t* off) {
 size_t layout_sg_bwd(int64_t M, int64_t d, int64_t h, size_t* off) {
   const size_t mh = (size_t)(M * h);
   const size_t sz[SB_COUNT] = {
-      (size_t)(M * d), mh * 2, mh * 2, mh * 2, mh, mh, (size_t)(M * d) * 4, (size_t)amax_parts_for(M, d) * 4,
-      (size_t)swiglu_parts_for(M * h) * 4, (size_t)swiglu_parts_for(M * h) * 4, 16};
+      (size_t)(M * d), mh * 2, mh * 2, mh, mh, (size_t)(M * d) * 4, (size_t)amax_parts_for(M, d) * 4,
+      (size_t)gemm_num_tiles(M, h) * 4, (size_t)gemm_num_tiles(M, h) * 4, 16};
   size_t o = 0;
   for (int i = 0; i < SB_COUNT; ++i) { off[i] = o; o = align_up(o + sz[i]); }
   return o;
@@ -672,7 +672,6 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   if (!a16(ws)) return FP8MLP_EALIGN;
   uint8_t* w8 = (uint8_t*)ws;
   uint8_t* gq = w8 + off[SB_GQ];
-  uint16_t* da = (uint16_t*)(w8 + off[SB_DA]);
   uint16_t* dg = (uint16_t*)(w8 + off[SB_DG]);
   uint16_t* du = (uint16_t*)(w8 + off[SB_DU]);
   uint8_t *dgq = w8 + off[SB_DGQ], *duq = w8 + off[SB_DUQ];
@@ -689,21 +688,21 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
                       amax_parts_for(M, d), kModePlain);
   if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 2. dW_down = Gq^T . Aq (TN), 3. dA = Gq . Wd (NN)
+  // 2. dW_down = Gq^T . Aq (TN)
   GemmArgs gw = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->aq, h, FP8MLP_E4M3, &sc[4], d, h, M, kEpiStore);
   gw.layout = kLayTN; gw.c = dw_down; gw.ldc = h; gw.accum = accum;
-  GemmArgs ga = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->wdq, h, FP8MLP_E4M3, &sc[3], M, h, d, kEpiStore);
-  ga.layout = kLayNN; ga.c = da; ga.ldc = h; ga.accum = accum;
+  // 3. dA = Gq . Wd (NN), and in its epilogue 4. dG, dU with their tile maxima
+  GemmArgs ga = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->wdq, h, FP8MLP_E4M3, &sc[3], M, h, d, kEpiSwiGLUBwd);
+  ga.layout = kLayNN; ga.aux = sv->g; ga.aux2 = sv->u; ga.ldaux = h; ga.c = dg; ga.c2 = du; ga.ldc = h;
+  ga.partials = pdg; ga.partials2 = pdu; ga.accum = accum;
   if (launch_gemm(gw, s) != hipSuccess || launch_gemm(ga, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 4. dG, dU with their amax partials, 5. their E5M2 codes (one cast launch)
-  if (launch_swiglu_gate_bwd(sv->g, sv->u, da, dg, du, M * h, pdg, pdu, s) != hipSuccess) return FP8MLP_EHIP;
+  // 5. the E5M2 codes of dG and dU (one cast launch)
+  const int ptiles = (int)gemm_num_tiles(M, h);
   QuantBatch bg{};
   bg.njobs = 2;
-  bg.job[0] = make_job(dg, M, h, h, FP8MLP_E5M2, dgq, h, nullptr, 0, &bsc[1], nullptr, pdg, swiglu_parts_for(M * h),
-                       kModePlain);
-  bg.job[1] = make_job(du, M, h, h, FP8MLP_E5M2, duq, h, nullptr, 0, &bsc[2], nullptr, pdu, swiglu_parts_for(M * h),
-                       kModePlain);
+  bg.job[0] = make_job(dg, M, h, h, FP8MLP_E5M2, dgq, h, nullptr, 0, &bsc[1], nullptr, pdg, ptiles, kModePlain);
+  bg.job[1] = make_job(du, M, h, h, FP8MLP_E5M2, duq, h, nullptr, 0, &bsc[2], nullptr, pdu, ptiles, kModePlain);
   if (launch_cast(bg, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 6. dW_gate = dGq^T . Xq, dW_up = dUq^T . Xq (TN)

@@ -53,8 +53,10 @@
 //    taken on fp32 values before the (monotone) bf16 rounding; fp32 store and
 //    accumulate, and accumulate-then-round-to-bf16 for the last of several
 //    summed products; the gated block's merged gate/up projection with the
-//    gate applied; and, for bf16 operands, alpha/beta with an optional
-//    transposed store and the upper-triangle split-K mode.
+//    gate applied, and its grad-input with the gate's derivative applied
+//    (dG and dU leave the kernel, dA is never stored); and, for bf16
+//    operands, alpha/beta with an optional transposed store and the
+//    upper-triangle split-K mode.
 #pragma once
 #include <type_traits>
 
@@ -606,33 +608,40 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(GemmArgs g, int
   constexpr int NCH = BM * CPR / kThreads;
   static_assert(NCH * kThreads == BM * CPR, "whole epilogue chunks");
   const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
-  const bool vec_aux = EPI != kEpiRelu2Bwd ||
-                       (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0));
+  constexpr bool kSgBwd = EPI == kEpiSwiGLUBwd;
+  const bool vec_aux = (EPI != kEpiRelu2Bwd && !kSgBwd) ||
+                       (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0) &&
+                        (!kSgBwd || (((reinterpret_cast<uintptr_t>(g.aux2) & 15u) == 0) &&
+                                     ((reinterpret_cast<uintptr_t>(g.c2) & 15u) == 0))));
   // The relu^2-backward epilogue needs H at its chunks.  With two waves per
   // SIMD (THREADS = 512) the loads are issued first, in flight while the tile
   // is staged in LDS; the 4-wave layout has no registers to spare next to its
   // 256 accumulators and issues them after staging.
   constexpr bool kEarlyH = EPI == kEpiRelu2Bwd && kThreads == 512;
-  v4u hv[EPI == kEpiRelu2Bwd ? NCH : 1];
-  auto load_h = [&]() {
+  // chunk `it` of a bf16 [M, N] input with leading dimension ldaux; zeros
+  // past N and for rows past M
+  auto load_chunk = [&](const uint16_t* src, int it) {
+    const int id = tid + kThreads * it;
+    const int64_t gr = m0 + id / CPR, gc = n0 + (id % CPR) * 8;
+    v4u v = v4u{0u, 0u, 0u, 0u};
+    if (gr < g.M && gc < g.N) {
+      if (gc + 8 <= g.N && vec_c && vec_aux) {
+        v = *reinterpret_cast<const v4u*>(src + gr * g.ldaux + gc);
+      } else {
 #pragma unroll
-    for (int it = 0; it < NCH; ++it) {
-      const int id = tid + kThreads * it;
-      const int64_t gr = m0 + id / CPR, gc = n0 + (id % CPR) * 8;
-      hv[it] = v4u{0u, 0u, 0u, 0u};
-      if (gr < g.M && gc < g.N) {
-        if (gc + 8 <= g.N && vec_c && vec_aux) {
-          hv[it] = *reinterpret_cast<const v4u*>(g.aux + gr * g.ldaux + gc);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = gc + 2 * e < g.N ? g.aux[gr * g.ldaux + gc + 2 * e] : 0u;
-            const uint32_t hi = gc + 2 * e + 1 < g.N ? g.aux[gr * g.ldaux + gc + 2 * e + 1] : 0u;
-            hv[it][e] = lo | (hi << 16);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = gc + 2 * e < g.N ? src[gr * g.ldaux + gc + 2 * e] : 0u;
+          const uint32_t hi = gc + 2 * e + 1 < g.N ? src[gr * g.ldaux + gc + 2 * e + 1] : 0u;
+          v[e] = lo | (hi << 16);
         }
       }
     }
+    return v;
+  };
+  v4u hv[EPI == kEpiRelu2Bwd ? NCH : 1];
+  auto load_h = [&]() {
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) hv[it] = load_chunk(g.aux, it);
   };
   if constexpr (kEarlyH) load_h();
 
@@ -724,11 +733,44 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(GemmArgs g, int
     return;
   }
 
+  // One 16-byte chunk of bf16 outputs at (gr, gc) of an [M, N] output with
+  // leading dimension ldc: one vector store when the chunk is whole and
+  // aligned, the widest stores its alignment allows when it is whole but not
+  // 16-byte aligned (an odd or unaligned leading dimension), else elements.
+  auto store_chunk = [&](uint16_t* base, int64_t gr, int64_t gc, const v4u& v, bool full) {
+    uint16_t* dst = base + gr * g.ldc + gc;
+    if (full) {
+      *reinterpret_cast<v4u*>(dst) = v;
+    } else if (gc + 8 <= g.N) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+      if ((a & 7u) == 0) {
+        reinterpret_cast<v2u*>(dst)[0] = v2u{v[0], v[1]};
+        reinterpret_cast<v2u*>(dst)[1] = v2u{v[2], v[3]};
+      } else if ((a & 3u) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) reinterpret_cast<uint32_t*>(dst)[e] = v[e];
+      } else {
+        dst[0] = (uint16_t)v[0];
+        uint32_t* mid = reinterpret_cast<uint32_t*>(dst + 1);
+        mid[0] = __builtin_amdgcn_alignbyte(v[1], v[0], 2);
+        mid[1] = __builtin_amdgcn_alignbyte(v[2], v[1], 2);
+        mid[2] = __builtin_amdgcn_alignbyte(v[3], v[2], 2);
+        dst[7] = (uint16_t)(v[3] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gc + e < g.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+  };
+
   // epilogue max, as the partial's format wants it: relu^2-max the fp32 bit
-  // pattern of a non-negative bf16 value, relu^2-backward the bf16 magnitude
-  // bits.  The relu^2-backward max |dH| is likewise taken before rounding,
-  // max |RN_bf16(y)| = RN_bf16(max |y|); chunk elements past N hold y = 0.
-  uint32_t mx = 0;
+  // pattern of a non-negative bf16 value, relu^2-backward and the gated
+  // backward the bf16 magnitude bits.  The relu^2-backward max |dH| is taken
+  // before rounding, max |RN_bf16(y)| = RN_bf16(max |y|); chunk elements past
+  // N hold y = 0.  The gated backward's inputs past N load as zeros, so its
+  // outputs there are +-0 and their magnitude bits 0.
+  uint32_t mx = 0, mx2 = 0;
   float dmax = 0.0f;
   if constexpr (EPI == kEpiRelu2Max) {
     const __bf16 hb = (__bf16)hmax;
@@ -742,48 +784,48 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(GemmArgs g, int
     if (gr < g.M && gc < g.N) {
       v4u v = *reinterpret_cast<const v4u*>(smem + row * G::CLD + c8 * 16);
       const bool full = gc + 8 <= g.N && vec_c && vec_aux;
-      if constexpr (EPI == kEpiRelu2Bwd) {
+      if constexpr (kSgBwd) {
+        // dA (staged bf16) with G and U at the same chunk
+        const v4u gv = load_chunk(g.aux, it), uv = load_chunk(g.aux2, it);
+        v4u dgv, duv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          uint32_t out = 0;
+          uint32_t wg = 0, wu = 0;
 #pragma unroll
           for (int hlf = 0; hlf < 2; ++hlf) {
-            const float h = bf16_to_f32((hv[it][e] >> (16 * hlf)) & 0xFFFFu);
-            const float da = bf16_to_f32((v[e] >> (16 * hlf)) & 0xFFFFu);
-            const float r = h > 0.0f ? h : 0.0f;
-            const float y = (2.0f * r) * da;  // exact product
-            dmax = __builtin_fmaxf(dmax, __builtin_fabsf(y));
-            const __bf16 dh = (__bf16)y;  // one rounding
-            out |= (uint32_t)__builtin_bit_cast(unsigned short, dh) << (16 * hlf);
+            const int sh = 16 * hlf;
+            uint32_t bg, bu;
+            swiglu_bwd_bits(bf16_to_f32((gv[e] >> sh) & 0xFFFFu), bf16_to_f32((uv[e] >> sh) & 0xFFFFu),
+                            bf16_to_f32((v[e] >> sh) & 0xFFFFu), bg, bu);
+            mx = mx > (bg & 0x7FFFu) ? mx : (bg & 0x7FFFu);
+            mx2 = mx2 > (bu & 0x7FFFu) ? mx2 : (bu & 0x7FFFu);
+            wg |= bg << sh;
+            wu |= bu << sh;
           }
-          v[e] = out;
+          dgv[e] = wg;
+          duv[e] = wu;
         }
-      }
-      if (full) {
-        *reinterpret_cast<v4u*>(g.c + gr * g.ldc + gc) = v;
-      } else if (gc + 8 <= g.N) {
-        // whole chunk, destination not 16-byte aligned (an odd or unaligned
-        // leading dimension): the widest stores its alignment allows
-        uint16_t* dst = g.c + gr * g.ldc + gc;
-        const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
-        if ((a & 7u) == 0) {
-          reinterpret_cast<v2u*>(dst)[0] = v2u{v[0], v[1]};
-          reinterpret_cast<v2u*>(dst)[1] = v2u{v[2], v[3]};
-        } else if ((a & 3u) == 0) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) reinterpret_cast<uint32_t*>(dst)[e] = v[e];
-        } else {
-          dst[0] = (uint16_t)v[0];
-          uint32_t* mid = reinterpret_cast<uint32_t*>(dst + 1);
-          mid[0] = __builtin_amdgcn_alignbyte(v[1], v[0], 2);
-          mid[1] = __builtin_amdgcn_alignbyte(v[2], v[1], 2);
-          mid[2] = __builtin_amdgcn_alignbyte(v[3], v[2], 2);
-          dst[7] = (uint16_t)(v[3] >> 16);
-        }
+        store_chunk(g.c, gr, gc, dgv, full);
+        store_chunk(g.c2, gr, gc, duv, full);
       } else {
+        if constexpr (EPI == kEpiRelu2Bwd) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (gc + e < g.N) g.c[gr * g.ldc + gc + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+          for (int e = 0; e < 4; ++e) {
+            uint32_t out = 0;
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+              const float h = bf16_to_f32((hv[it][e] >> (16 * hlf)) & 0xFFFFu);
+              const float da = bf16_to_f32((v[e] >> (16 * hlf)) & 0xFFFFu);
+              const float r = h > 0.0f ? h : 0.0f;
+              const float y = (2.0f * r) * da;  // exact product
+              dmax = __builtin_fmaxf(dmax, __builtin_fabsf(y));
+              const __bf16 dh = (__bf16)y;  // one rounding
+              out |= (uint32_t)__builtin_bit_cast(unsigned short, dh) << (16 * hlf);
+            }
+            v[e] = out;
+          }
+        }
+        store_chunk(g.c, gr, gc, v, full);
       }
     }
   }
@@ -794,6 +836,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(GemmArgs g, int
   if constexpr (EPI != kEpiStore) {
     mx = block_max_u32(mx, red);
     if (tid == 0) g.partials[t] = mx;
+  }
+  if constexpr (kSgBwd) {
+    mx2 = block_max_u32(mx2, red);
+    if (tid == 0) g.partials2[t] = mx2;
   }
 }
 
@@ -823,8 +869,9 @@ inline int pick_bn(int64_t M, int64_t N) {
 // FP8 products of one layout and accumulation mode.  Epilogues beyond the
 // plain store exist for the format pairs and layouts that use them: the
 // relu^2 block's forward (E4M3 x E4M3, NT) and backward (E5M2 x E4M3, NT or
-// NN), the gated projection (E4M3 x E4M3, NT), and the fp32 store and
-// accumulate epilogues of summed gradient products (E5M2 x E4M3).
+// NN), the gated block's projection (E4M3 x E4M3, NT) and backward (E5M2 x
+// E4M3, NN), and the fp32 store and accumulate epilogues of summed gradient
+// products (E5M2 x E4M3).
 template <int LAY, int ACC, int FA, int FB, int BN, int WGM, int WGN>
 hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
   switch (g.epi) {
@@ -840,6 +887,10 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
     case kEpiSwiGLU:
       if constexpr (LAY == 0 && FA == kE4M3 && FB == kE4M3 && BN == 256)
         return launch_cfg<FA, FB, 256, 256, 2, 2, kEpiSwiGLU, LAY, ACC>(g, st);
+      break;
+    case kEpiSwiGLUBwd:
+      if constexpr (LAY == 2 && FA == kE5M2 && FB == kE4M3)
+        return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiSwiGLUBwd, LAY, ACC>(g, st);
       break;
     case kEpiStoreF32:
     case kEpiAccF32:

@@ -73,6 +73,10 @@ enum Epilogue : int {
                       // G = RN_bf16(RN32(sa sb) acc) -> c, U = RN_bf16(RN32(sa sb2)
                       // acc) -> c2, A = RN_bf16(silu(G) U) -> c3 (all ldc);
                       // partial[tile] = max |A| (bf16 bits) when partials is set
+  kEpiSwiGLUBwd = 8,  // gated MLP backward: dA = RN_bf16(p * acc) (not stored), with G
+                      // (aux) and U (aux2): dG = RN_bf16(dA U silu'(G)) -> c,
+                      // dU = RN_bf16(dA silu(G)) -> c2 (ldc); partial[tile] =
+                      // max |dG|, partials2[tile] = max |dU| (bf16 bits)
 };
 
 // GEMM operand layouts: bit 0 set = A is MN-major ([K, M], the output index
@@ -102,9 +106,11 @@ struct GemmArgs {
   uint16_t* c;  // [M, N] bf16
   int64_t ldc;
   int epi;
-  const uint16_t* aux;  // H for kEpiRelu2Bwd ([M, N], ldaux)
+  const uint16_t* aux;  // H for kEpiRelu2Bwd, G for kEpiSwiGLUBwd ([M, N], ldaux)
+  const uint16_t* aux2;  // U for kEpiSwiGLUBwd ([M, N], ldaux)
   int64_t ldaux;
-  uint32_t* partials;  // one per tile for the max epilogues
+  uint32_t* partials;   // one per tile for the max epilogues
+  uint32_t* partials2;  // kEpiSwiGLUBwd: the second output's, one per tile
   float* cf;           // [M, N] fp32 (ldc) for the fp32 epilogues
   // bf16 operands (fa == fb == kBF16): a, b hold bf16 values, lda, ldb and K
   // count elements, and the output scale is alpha instead of sa * sb.
@@ -112,7 +118,7 @@ struct GemmArgs {
   uint16_t* ct;  // kEpiAxpby: optional transposed copy of C ([N, M], ldct)
   int64_t ldct;
   // kEpiSwiGLU: the up projection's codes [N, K] (ldb) and scale, and the U
-  // and A outputs ([M, N], ldc)
+  // and A outputs ([M, N], ldc); kEpiSwiGLUBwd: the dU output in c2
   const uint8_t* b2;
   const float* sb2;
   uint16_t* c2;
@@ -153,11 +159,6 @@ int64_t lm_ce_max_vocab();  // largest vocabulary the row kernel takes
 hipError_t launch_lm_ce_loss(const float* loss_rows, int64_t M, const int32_t* n_valid, float* loss,
                              hipStream_t st);
 
-// Gated (SwiGLU) MLP backward elementwise kernel (swiglu.hip); n = elements,
-// n % 8 == 0, dense tensors; one partial (max |.| as bf16 bits) per block.
-int swiglu_parts_for(int64_t n);
-hipError_t launch_swiglu_gate_bwd(const uint16_t* g, const uint16_t* u, const uint16_t* da, uint16_t* dg,
-                                  uint16_t* du, int64_t n, uint32_t* pg, uint32_t* pu, hipStream_t st);
 // dst = RN_bf16(src) over n elements (n % 8 == 0); src == nullptr writes zeros.
 hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t st);
 

@@ -65,7 +65,9 @@
 extern "C" {
 #endif
 
-#define FP8MLP_ABI_VERSION 2
+/* Version 3: the gated block's backward workspace holds no dA buffer (its
+ * grad-input GEMM applies the gate's derivative in the epilogue). */
+#define FP8MLP_ABI_VERSION 3
 
 /* FP8 GEMM accumulation modes (see the numeric contract above). */
 #define FP8MLP_ACCUM_FAST 0
@@ -252,8 +254,9 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
 /*     A = RN_bf16(RN32(RN32(G sigmoid(G)) U))    (fp32 sigmoid)             */
 /*     Aq = quant(A);  Y = NT(Aq, Wdq)                                       */
 /*   Backward (gradients E5M2):                                              */
-/*     Gq = quant(dY);  dW_down = TN(Gq, Aq);  dA = NN(Gq, Wdq)              */
-/*     dG = RN_bf16(dA U silu'(G)),  dU = RN_bf16(dA silu(G))  (fp32)         */
+/*     Gq = quant(dY);  dW_down = TN(Gq, Aq);  dA = NN(Gq, Wdq), not stored: */
+/*     dG = RN_bf16(dA U silu'(G)),  dU = RN_bf16(dA silu(G))  (fp32, in the  */
+/*     epilogue of the dA GEMM; silu'(g) = s (1 + g (1 - s)), s = sigmoid(g)) */
 /*     dGq, dUq = quant(dG), quant(dU)                                       */
 /*     dW_gate = TN(dGq, Xq);  dW_up = TN(dUq, Xq)                           */
 /*     dX = RN_bf16(RN32(RN32(p_g NN(dGq,Wgq)) + RN32(p_u NN(dUq,Wuq))))      */
@@ -274,8 +277,8 @@ typedef struct {
 size_t swiglu_mlp_fwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
 size_t swiglu_mlp_bwd_workspace_bytes(int64_t M, int64_t d, int64_t h);
 /* Byte offsets of the workspace regions.  Forward (n >= 6): A bf16, amax
- * partials of X, W_gate, W_up, W_down, A.  Backward (n >= 11): Gq, dA, dG,
- * dU, dGq, dUq, dX fp32, amax partials of dY, dG, dU, scales. */
+ * partials of X, W_gate, W_up, W_down, A.  Backward (n >= 10): Gq, dG, dU,
+ * dGq, dUq, dX fp32, amax partials of dY, dG, dU, scales. */
 int swiglu_mlp_fwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
 int swiglu_mlp_bwd_workspace_layout(int64_t M, int64_t d, int64_t h, size_t* offsets, int n);
 int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,

@@ -113,8 +113,8 @@ def collect(inputs, y, saved, ws_f, ws_b, dx, dwg, dwu, dwd, bsc) -> dict:
         dw_up=bf16_bits(dwu), dw_down=bf16_bits(dwd), g=bf16_bits(saved.g), u=bf16_bits(saved.u),
         scales=f32(saved.scales), bsc=f32(bsc), xq=u8(saved.xq), wgq=u8(saved.wgq), wuq=u8(saved.wuq),
         wdq=u8(saved.wdq), aq=u8(saved.aq), a=sl(wf, of[0], (M, h), True),
-        gq=sl(wb, ob[0], (M, d)), da=sl(wb, ob[1], (M, h), True), dg=sl(wb, ob[2], (M, h), True),
-        du=sl(wb, ob[3], (M, h), True), dgq=sl(wb, ob[4], (M, h)), duq=sl(wb, ob[5], (M, h)))
+        gq=sl(wb, ob[0], (M, d)), dg=sl(wb, ob[1], (M, h), True), du=sl(wb, ob[2], (M, h), True),
+        dgq=sl(wb, ob[3], (M, h)), duq=sl(wb, ob[4], (M, h)))
 
 
 def _silu_d(g):
@@ -191,8 +191,9 @@ def compare(g: dict, o: dict, sc: dict, rows, cols, accum=ACC_FAST):
     _gate_close(a_c, g_c, u_c, "A columns")
     assert (aq_r == oracle.cast(a_r, sa, E4)).all() and (aq_c == oracle.cast(a_c, sa, E4)).all(), "Aq: cast of A"
     stage_gemm(g["y"][rows], "nt", aq_r, E4, sa, wdq, E4, swd, "Y rows", accum)
-    stage_gemm(g["da"][rows], "nn", gq, E5, sg, wdq, E4, swd, "dA rows", accum, rows=rows)
-    stage_gemm(T(g["da"]), "tn", wdq, E4, swd, np.ascontiguousarray(gq.T), E5, sg, "dA columns", accum, rows=cols)
+    # dA lives only inside the grad-input GEMM's epilogue: dG and dU are held
+    # to the oracle's gate derivative of the oracle's dA (same Gq and Wdq
+    # codes), within dA's GEMM bound carried through the derivative
     _gate_bwd_close(dg_r, du_r, g_r, u_r, o["dA_r"], o["dA_r_abs"], o["dA_K"], accum, "rows")
     _gate_bwd_close(dg_c, du_c, g_c, u_c, o["dAt_c"], o["dAt_c_abs"], d, accum, "columns")
     for name, q, v, s in (("dGq rows", dgq_r, dg_r, sdg), ("dUq rows", duq_r, du_r, sdu),
