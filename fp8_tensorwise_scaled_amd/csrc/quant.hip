@@ -10,10 +10,14 @@
 //   1. amax_partials: every block writes the max of |x| over its slice, taken
 //      as an integer max of the bf16 magnitude bits (monotone in the value,
 //      order independent, hence bit-deterministic);
-//   2. cast: every block first reduces the (<= 2048) partials of its tensor,
-//      derives s itself, then streams 128x256 tiles: row-major codes go
-//      straight to HBM, the transposed codes are built by byte permutes in
-//      registers, so both outputs are written in full 128-byte lines.
+//   2. cast: every block first reduces the partials of its tensor, derives s
+//      itself, then streams 128x256 tiles.  Codes alone (the common case):
+//      each lane turns one 16-byte load of 8 values into one 8-byte store, a
+//      half-wave covering 256 contiguous columns of a row.  With transposed
+//      codes as well, a lane takes 4 columns of 16 rows, the row-major codes
+//      go straight to HBM and the transposed ones are built by byte permutes
+//      in registers and an LDS image of the tile (allocated only for such a
+//      launch), so both outputs are written in full 128-byte lines.
 #include "device_common.h"
 #include "internal.h"
 
@@ -199,6 +203,9 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
       make_rsrc(reinterpret_cast<const void*>(xa - dlt), buf_in ? (uint32_t)((xbytes + 3) & ~int64_t{3}) : 0u);
   const bool vec_q = q == nullptr || (((reinterpret_cast<uintptr_t>(q) & 3u) == 0) && (jb.ldq % 4 == 0));
   const bool vec_qt = qt == nullptr || (aligned16(qt) && (jb.ldqt % 16 == 0));
+  // codes only, 16-byte aligned rows of x, 8-byte aligned rows of q
+  const bool rows_only = qt == nullptr && q != nullptr && aligned16(x) && ldx % 8 == 0 &&
+                         ((reinterpret_cast<uintptr_t>(q) & 7u) == 0) && jb.ldq % 8 == 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tile_parity = 0;  // LDS image buffer of the next transposed tile
   for (int64_t t = lb; t < ntiles; t += jb.nblocks) {
@@ -209,7 +216,44 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
     // the 50304-column logits).
     const int64_t wv = cols - c0 < kTC ? cols - c0 : kTC;  // valid columns
     const bool full = r0 + kTR <= rows && wv % 4 == 0 && (vec_in || buf_in) && vec_q && vec_qt;
-    if (full) {
+    if (rows_only && r0 + kTR <= rows && wv % 8 == 0) {
+      // codes only: lane takes 8 columns (one 16-byte load, one 8-byte
+      // store) of rows 2i + half of the wave's 16; a half-wave covers 256
+      // contiguous columns of one row
+      const int half = lane >> 5, l32 = lane & 31;
+      const int64_t cb = c0 + l32 * 8;
+      const bool lane_ok = l32 * 8 < wv;
+      const int64_t rb = r0 + wave * 16 + half;
+      v4u in[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        in[i] = lane_ok ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + (rb + 2 * i) * ldx + cb))
+                        : v4u{0u, 0u, 0u, 0u};
+      if (lane_ok) {
+        float g[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+        bool has_g = false;
+        if constexpr (MODE == kModeRmsNorm) {
+          has_g = jb.gamma != nullptr;
+          if (has_g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) g[e] = bf16_to_f32(jb.gamma[cb + e]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t lo, hi;
+          if constexpr (MODE == kModeRmsNorm) {
+            const float r = jb.rstd[rb + 2 * i];
+            lo = quant4_norm<FMT>(in[i][0], in[i][1], r, g, has_g, d);
+            hi = quant4_norm<FMT>(in[i][2], in[i][3], r, g + 4, has_g, d);
+          } else {
+            lo = quant4<FMT, MODE>(in[i][0], in[i][1], d);
+            hi = quant4<FMT, MODE>(in[i][2], in[i][3], d);
+          }
+          *reinterpret_cast<v2u*>(q + (rb + 2 * i) * jb.ldq + cb) = v2u{lo, hi};
+        }
+      }
+    } else if (full) {
       const int64_t rb = r0 + wave * 16, cb = c0 + lane * 4;
       const bool lane_ok = lane * 4 < wv;
       v2u in[16];
@@ -496,7 +540,7 @@ __global__ void __launch_bounds__(256) rmsnorm_amax_kernel(QuantJob jb, float ep
 template <int FMT, int MODE>
 __global__ void __launch_bounds__(kCastThreads) cast_kernel(QuantBatch b) {
   __shared__ uint32_t red[kCastThreads / 64];
-  __shared__ __attribute__((aligned(16))) uint8_t tbuf[2 * kTImage];  // double-buffered transposed tile
+  extern __shared__ __attribute__((aligned(16))) uint8_t tbuf[];  // double-buffered transposed tile (when qt)
   int lb;
   const QuantJob& jb = job_of(b, lb);
   // 1. amax from the partials (integer max of non-negative bit patterns)
@@ -582,19 +626,22 @@ hipError_t launch_cast(QuantBatch& b, hipStream_t st) {
     total += b.job[i].nblocks;
   }
   const int fmt = b.job[0].fmt, mode = b.job[0].mode;
+  bool any_qt = false;
+  for (int i = 0; i < b.njobs; ++i) any_qt = any_qt || b.job[i].qt != nullptr;
+  const unsigned sh = any_qt ? 2 * kTImage : 0;
   if (mode == kModeRmsNorm) {
     if (fmt == kE4M3)
-      hipLaunchKernelGGL((cast_kernel<kE4M3, kModeRmsNorm>), dim3(total), dim3(kCastThreads), 0, st, b);
+      hipLaunchKernelGGL((cast_kernel<kE4M3, kModeRmsNorm>), dim3(total), dim3(kCastThreads), sh, st, b);
     else
-      hipLaunchKernelGGL((cast_kernel<kE5M2, kModeRmsNorm>), dim3(total), dim3(kCastThreads), 0, st, b);
+      hipLaunchKernelGGL((cast_kernel<kE5M2, kModeRmsNorm>), dim3(total), dim3(kCastThreads), sh, st, b);
   } else if (fmt == kE4M3 && mode == kModePlain)
-    hipLaunchKernelGGL((cast_kernel<kE4M3, kModePlain>), dim3(total), dim3(kCastThreads), 0, st, b);
+    hipLaunchKernelGGL((cast_kernel<kE4M3, kModePlain>), dim3(total), dim3(kCastThreads), sh, st, b);
   else if (fmt == kE4M3)
-    hipLaunchKernelGGL((cast_kernel<kE4M3, kModeRelu2>), dim3(total), dim3(kCastThreads), 0, st, b);
+    hipLaunchKernelGGL((cast_kernel<kE4M3, kModeRelu2>), dim3(total), dim3(kCastThreads), sh, st, b);
   else if (mode == kModePlain)
-    hipLaunchKernelGGL((cast_kernel<kE5M2, kModePlain>), dim3(total), dim3(kCastThreads), 0, st, b);
+    hipLaunchKernelGGL((cast_kernel<kE5M2, kModePlain>), dim3(total), dim3(kCastThreads), sh, st, b);
   else
-    hipLaunchKernelGGL((cast_kernel<kE5M2, kModeRelu2>), dim3(total), dim3(kCastThreads), 0, st, b);
+    hipLaunchKernelGGL((cast_kernel<kE5M2, kModeRelu2>), dim3(total), dim3(kCastThreads), sh, st, b);
   return hipGetLastError();
 }
 

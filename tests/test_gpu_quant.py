@@ -31,13 +31,17 @@ def run_quant(x_np, fmt, ld=None, qt=True, offset=0):
 
 
 def check_against_oracle(x_np, fmt, **kw):
-    q, qt, s, a = run_quant(x_np, fmt, **kw)
+    """Scale, amax and codes against the oracle, with and without the
+    transposed codes (the two are different cast paths) unless `qt` is
+    given."""
     rq, rs, ra = oracle.quant(x_np, fmt)
-    assert np.float32(s) == np.float32(rs) and np.float32(a) == np.float32(ra), (s, rs, a, ra)
-    bad = np.argwhere(q != rq)
-    assert bad.size == 0, [(tuple(i), hex(x_np[tuple(i)]), q[tuple(i)], rq[tuple(i)]) for i in bad[:5]]
-    if qt is not None:
-        assert (qt == rq.T).all()
+    for want_qt in ((kw.pop("qt"),) if "qt" in kw else (True, False)):
+        q, qt, s, a = run_quant(x_np, fmt, qt=want_qt, **kw)
+        assert np.float32(s) == np.float32(rs) and np.float32(a) == np.float32(ra), (want_qt, s, rs, a, ra)
+        bad = np.argwhere(q != rq)
+        assert bad.size == 0, [(want_qt, tuple(i), hex(x_np[tuple(i)]), q[tuple(i)], rq[tuple(i)]) for i in bad[:5]]
+        if qt is not None:
+            assert (qt == rq.T).all()
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 E4, E5 = oracle.E4M3, oracle.E5M2
 
 
-def run(x, g, eps, fmt, ld=None):
+def run(x, g, eps, fmt, ld=None, want_qt=True):
+    """want_qt: also the transposed codes (a different cast path)."""
     from fp8_tensorwise_scaled_amd import api
 
     rows, cols = x.shape
@@ -24,9 +25,9 @@ def run(x, g, eps, fmt, ld=None):
         buf[:, :cols] = x
         xd = to_dev_bf16(buf)[:, :cols]
     gd = None if g is None else to_dev_bf16(g)
-    q, qt, s, a, r = api.fp8_rmsnorm_quant(xd, gd, eps, fmt, want_qt=True)
+    q, qt, s, a, r = api.fp8_rmsnorm_quant(xd, gd, eps, fmt, want_qt=want_qt)
     torch.cuda.synchronize()
-    return u8(q), u8(qt), float(f32(s)[0]), float(f32(a)[0]), f32(r)
+    return u8(q), (u8(qt) if want_qt else None), float(f32(s)[0]), float(f32(a)[0]), f32(r)
 
 
 @pytest.mark.parametrize("shape,ld,with_g,fmt", [
@@ -43,11 +44,13 @@ def run(x, g, eps, fmt, ld=None):
 def test_bit_exact(shape, ld, with_g, fmt):
     x = synth.normal_bf16(shape, 2.5, 91, outlier_frac=1e-3)
     g = synth.normal_bf16((shape[1],), 1.0, 92) if with_g else None
-    q, qt, s, a, r = run(x, g, 1e-6, fmt, ld)
     rq, rs, ra, _, rr = oracle.rmsnorm_quant(x, g, 1e-6, fmt)
-    assert (r.view(np.uint32) == rr.view(np.uint32)).all(), "1/rms differs"
-    assert np.float32(s) == np.float32(rs) and np.float32(a) == np.float32(ra), (s, rs, a, ra)
-    assert (q == rq).all() and (qt == rq.T).all()
+    for want_qt in (True, False):
+        q, qt, s, a, r = run(x, g, 1e-6, fmt, ld, want_qt)
+        assert (r.view(np.uint32) == rr.view(np.uint32)).all(), "1/rms differs"
+        assert np.float32(s) == np.float32(rs) and np.float32(a) == np.float32(ra), (s, rs, a, ra)
+        assert (q == rq).all(), want_qt
+        assert qt is None or (qt == rq.T).all()
 
 
 def test_random_shapes():
@@ -61,12 +64,13 @@ def test_random_shapes():
         fmt = [E4, E5][int(rng.integers(0, 2))]
         x = synth.normal_bf16((rows, cols), float(rng.uniform(0.1, 4.0)), 9500 + i, outlier_frac=1e-3)
         g = synth.normal_bf16((cols,), 1.0, 9600 + i) if rng.integers(0, 2) else None
-        q, qt, s, a, r = run(x, g, 1e-6, fmt, ld)
+        want_qt = bool(i % 2)
+        q, qt, s, a, r = run(x, g, 1e-6, fmt, ld, want_qt)
         rq, rs, ra, _, rr = oracle.rmsnorm_quant(x, g, 1e-6, fmt)
-        what = (i, rows, cols, ld, fmt, g is not None)
+        what = (i, rows, cols, ld, fmt, g is not None, want_qt)
         assert (r.view(np.uint32) == rr.view(np.uint32)).all(), what
         assert np.float32(s) == np.float32(rs) and np.float32(a) == np.float32(ra), what
-        assert (q == rq).all() and (qt == rq.T).all(), what
+        assert (q == rq).all() and (qt is None or (qt == rq.T).all()), what
 
 
 def test_zero_rows_and_empty():
