@@ -396,7 +396,9 @@ def bench_mlp_small(args) -> int:
 
 def bench_linear(args) -> int:
     """One FP8 linear forward: X [256,512] N(0,1), W [1024,512] N(0,0.02), both
-    quantised per call (E4M3), Y [256,1024] bf16: latency in us."""
+    quantised per call (E4M3), Y [256,1024] bf16: latency in us.  The step is
+    fp8_linear_fwd_bf16 (one amax launch and one cast launch for X and W, then
+    the GEMM); the five-launch sequence of separate calls is timed beside it."""
     import torch
 
     from fp8_tensorwise_scaled_amd import api, synth
@@ -412,27 +414,35 @@ def bench_linear(args) -> int:
     f32 = dict(dtype=torch.float32, device=dev)
     xq, wq = torch.empty((M, K), **u8), torch.empty((N, K), **u8)
     sx, sw, ax, aw = (torch.empty(1, **f32) for _ in range(4))
+    sc = torch.empty(2, **f32)
     L = api._native.lib()
     wsx = torch.empty(max(L.fp8_amax_quant_workspace_bytes(M, K), 16), **u8)
     wsw = torch.empty(max(L.fp8_amax_quant_workspace_bytes(N, K), 16), **u8)
+    ws = torch.empty(max(L.fp8_linear_fwd_bf16_workspace_bytes(M, N, K), 16), **u8)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     def step():
+        api.fp8_linear_fwd_bf16(X, W, xq=xq, wq=wq, scales=sc, out=Y, ws=ws, accum=args.accum)
+
+    def step_separate():
         api.fp8_amax_quant(X, api.E4M3, q=xq, scale=sx, amax=ax, ws=wsx)
         api.fp8_amax_quant(W, api.E4M3, q=wq, scale=sw, amax=aw, ws=wsw)
         api.fp8_linear_fwd(xq, sx, wq, sw, out=Y, accum=args.accum)
 
     ms, per, wall, clocks = _timed_region(step, args.steps, args.warmup)
-    gemm_us = _after_steps(step, {"g": lambda: api.fp8_linear_fwd(xq, sx, wq, sw, out=Y, accum=args.accum)},
-                           args.gemm_reps)["g"]
+    ms_sep = _time_steps(step_separate, args.steps, args.warmup)
+    gemm_us = _after_steps(step, {"g": lambda: api.fp8_linear_fwd(xq, sc[0:1], wq, sc[1:2], out=Y,
+                                                                 accum=args.accum)}, args.gemm_reps)["g"]
     flops = 2 * M * N * K
-    log(f"linear fwd: {ms * 1e3:.2f} us per forward (GEMM alone {gemm_us:.2f} us)")
+    log(f"linear fwd: {ms * 1e3:.2f} us per forward (separate calls {ms_sep * 1e3:.2f} us; GEMM alone "
+        f"{gemm_us:.2f} us)")
     res = {"metric": "FP8 tensorwise-scaled linear forward latency (X [256,512], W [1024,512], quantisation "
                      "included), us",
            "value": round(ms * 1e3, 3), "ms_per_step": round(ms, 6),
            "data": "synthetic (seeded N(0,1) X, N(0,0.02) W; bf16)",
            "config": {"workload": "FP8 linear forward M=256 N=1024 K=512 (quantise X, quantise W, NT GEMM)",
-                      "M": M, "N": N, "K": K, "gemm_flops": flops},
+                      "M": M, "N": N, "K": K, "gemm_flops": flops, "entry_point": "fp8_linear_fwd_bf16"},
+           "us_separate_calls": round(ms_sep * 1e3, 3),
            "us_median": round(per[len(per) // 2] * 1e3, 3), "us_min": round(per[0] * 1e3, 3),
            "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
            "roofline": _roofline("gemm_kernel<0,0,256,*,*,*,0,0,%d> (E4M3 x E4M3, NT, one wave of tiles; "

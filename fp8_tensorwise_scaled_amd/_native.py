@@ -45,6 +45,9 @@ _PROTOS = {
     "fp8_rmsnorm_quant": (c_int, [vp, vp, ctypes.c_float, i64, i64, i64, c_int, vp, i64, vp, i64, vp, vp, vp, vp,
                                   szt, vp]),
     "fp8_linear_fwd": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, c_int, vp]),
+    "fp8_linear_fwd_bf16_workspace_bytes": (szt, [i64, i64, i64]),
+    "fp8_linear_fwd_bf16": (c_int, [vp, i64, vp, i64, i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, vp, szt, c_int,
+                                    vp]),
     "fp8_linear_dgrad": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, c_int, vp]),
     "fp8_linear_wgrad": (c_int, [vp, i64, c_int, vp, vp, i64, c_int, vp, i64, i64, i64, vp, i64, c_int, vp]),
     "relu2_mlp_fwd_workspace_bytes": (szt, [i64, i64, i64]),

@@ -135,6 +135,39 @@ def fp8_linear_fwd(xq, sx, wq, sw, fx: int = E4M3, fw: int = E4M3, out=None, *, 
     return _gemm("fp8_linear_fwd", xq, fx, sx, wq, fw, sw, M, N, K, out, (M, N), accum)
 
 
+def _codes16(rows: int, cols: int, device) -> torch.Tensor:
+    """[rows, cols] uint8 codes whose leading dimension is a multiple of 16
+    (what the GEMMs read)."""
+    ld = max(16, -(-cols // 16) * 16)
+    return torch.empty((rows, ld), dtype=torch.uint8, device=device)[:, :cols]
+
+
+def fp8_linear_fwd_bf16(x, w, *, xq=None, wq=None, scales=None, out=None, ws=None, accum: int = ACCUM_FAST):
+    """One FP8 linear forward from bf16 X [M,K] and W [N,K]: both quantised
+    to E4M3 with their own tensorwise scales (one amax launch and one cast
+    launch for the two), then Y = RN_bf16(RN32(sx*sw) Xq . Wq^T).  Returns
+    (y, xq, wq, scales) with scales = [sx, sw] (float32, on the device)."""
+    _check_dev(x, w)
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("x and w must be bfloat16")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w must have the same number of columns")
+    dev = x.device
+    xq = _codes16(M, K, dev) if xq is None else _out(xq, (M, K), torch.uint8, dev, "xq")
+    wq = _codes16(N, K, dev) if wq is None else _out(wq, (N, K), torch.uint8, dev, "wq")
+    scales = _out(scales, (2,), torch.float32, dev, "scales", dense=True)
+    out = _out(out, (M, N), torch.bfloat16, dev, "out")
+    if ws is None:
+        ws = torch.empty(max(_native.lib().fp8_linear_fwd_bf16_workspace_bytes(M, N, K), 16), dtype=torch.uint8,
+                         device=dev)
+    _ws(ws)
+    _native.call("fp8_linear_fwd_bf16", _p(x), _ld(x), _p(w), _ld(w), M, N, K, _p(xq), _ld(xq), _p(wq), _ld(wq),
+                 _p(scales), _p(out), _ld(out), _p(ws), ws.numel(), int(accum), _stream())
+    return out, xq, wq, scales
+
+
 def fp8_linear_dgrad(dyq, sdy, wq, sw, fdy: int = E5M2, fw: int = E4M3, out=None, *, accum: int = ACCUM_FAST):
     """dX[M,K] = RN_bf16(RN32(sdy*sw) * dYq[M,N] . Wq[N,K])  (NN; the forward's weight codes)."""
     M, N = dyq.shape

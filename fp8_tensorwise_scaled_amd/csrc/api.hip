@@ -312,6 +312,39 @@ int fp8_linear_fwd(const uint8_t* xq, int64_t ldx, int fx, const float* sx, cons
   return run_gemm(kLayNT, xq, ldx, fx, sx, wq, ldw, fw, sw, M, N, K, y, ldy, accum, stream);
 }
 
+size_t fp8_linear_fwd_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  return align_up((size_t)amax_parts_for(M, K) * 4) + align_up((size_t)amax_parts_for(N, K) * 4);
+}
+
+int fp8_linear_fwd_bf16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t M, int64_t N,
+                        int64_t K, uint8_t* xq, int64_t ldxq, uint8_t* wq, int64_t ldwq, float* scales,
+                        uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes, int accum, void* stream) {
+  if (!scales) return FP8MLP_EINVAL;
+  if ((uintptr_t)scales & 3u) return FP8MLP_EALIGN;
+  int st = check_amax_quant(x, M, K, ldx, FP8MLP_E4M3, xq, ldxq, nullptr, 0, &scales[0]);
+  if (!st) st = check_amax_quant(w, N, K, ldw, FP8MLP_E4M3, wq, ldwq, nullptr, 0, &scales[1]);
+  if (!st) st = check_gemm(kLayNT, xq, ldxq, FP8MLP_E4M3, &scales[0], wq, ldwq, FP8MLP_E4M3, &scales[1], M, N, K, y,
+                           ldy, accum);
+  if (st) return st;
+  if (M > 0 && N > 0 && K > 0 && (const void*)xq == (const void*)wq) return FP8MLP_EINVAL;
+  if (!ws || ws_bytes < fp8_linear_fwd_bf16_workspace_bytes(M, N, K)) return FP8MLP_EWORKSPACE;
+  if (!a16(ws)) return FP8MLP_EALIGN;
+  // 1. amax of X and W in one launch, 2. both casts in one launch, 3. Y = Xq . Wq^T (NT)
+  uint32_t* px = (uint32_t*)ws;
+  uint32_t* pw = (uint32_t*)((uint8_t*)ws + align_up((size_t)amax_parts_for(M, K) * 4));
+  QuantBatch b{};
+  b.njobs = 2;
+  b.job[0] = make_job(x, M, K, ldx, FP8MLP_E4M3, xq, ldxq, nullptr, 0, &scales[0], nullptr, px, amax_parts_for(M, K),
+                      kModePlain);
+  b.job[1] = make_job(w, N, K, ldw, FP8MLP_E4M3, wq, ldwq, nullptr, 0, &scales[1], nullptr, pw, amax_parts_for(N, K),
+                      kModePlain);
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+  return run_gemm(kLayNT, xq, ldxq, FP8MLP_E4M3, &scales[0], wq, ldwq, FP8MLP_E4M3, &scales[1], M, N, K, y, ldy,
+                  accum, stream);
+}
+
 int fp8_linear_dgrad(const uint8_t* dyq, int64_t lddy, int fdy, const float* sdy, const uint8_t* wq,
                      int64_t ldw, int fw, const float* sw, int64_t M, int64_t N, int64_t K,
                      uint16_t* dx, int64_t lddx, int accum, void* stream) {

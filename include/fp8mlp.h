@@ -193,6 +193,25 @@ int fp8_linear_wgrad(const uint8_t* dyq, int64_t lddy, int fdy, const float* sdy
                      const uint8_t* xq, int64_t ldx, int fx, const float* sx, int64_t M,
                      int64_t N, int64_t K, uint16_t* dw, int64_t lddw, int accum, void* stream);
 
+/* The forward of one FP8 linear layer from its bf16 tensors, the way the
+ * pages run a linear's forward (decomputer.nl, "Vroege experimenten" item 4:
+ * dynamic tensorwise scaling of input and weight on every call): X [M,K]
+ * (ldx) and W [N,K] (ldw) bf16 are quantised to E4M3 with their own
+ * tensorwise scales, then Y [M,N] = RN_bf16(RN32(sx*sw) Xq . Wq^T) (ldy).
+ * Three launches: one amax pass over both tensors, one cast of both, the
+ * GEMM.  Outputs, all caller-owned, for the backward to reuse: the codes xq
+ * [M,K] (ldxq) and wq [N,K] (ldwq), and scales[0] = sx, scales[1] = sw
+ * (device, 4-byte aligned).  Results are bit-identical to fp8_amax_quant of
+ * X and of W followed by fp8_linear_fwd.  Requirements: x, w 2-byte
+ * aligned; xq, wq as fp8_linear_fwd's operands (16-byte aligned, leading
+ * dimensions multiples of 16), not overlapping each other or x, w; ws
+ * 16-byte aligned with fp8_linear_fwd_bf16_workspace_bytes(M, N, K) bytes.
+ * Empty X or W get scale 1; M == 0 or N == 0 writes no Y, K == 0 zeros. */
+size_t fp8_linear_fwd_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int fp8_linear_fwd_bf16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw, int64_t M, int64_t N,
+                        int64_t K, uint8_t* xq, int64_t ldxq, uint8_t* wq, int64_t ldwq, float* scales,
+                        uint16_t* y, int64_t ldy, void* ws, size_t ws_bytes, int accum, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Non-gated relu^2 MLP block: Y = relu(X W_up^T)^2 W_down^T, FP8 GEMMs     */
 /* (decomputer.nl, "Doorvoer verhogen", non-gated MLP bullet; appendix:     */

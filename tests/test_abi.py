@@ -72,6 +72,37 @@ def test_quant_validation():
     assert q(*a) == 1                             # ldqt < rows
 
 
+def test_linear_fwd_bf16_validation():
+    """Every case below fails validation, so nothing is launched."""
+    L = _native.lib()
+    P = [ctypes.c_void_p(0x10000 * k) for k in range(1, 8)]  # distinct, never dereferenced
+    nws = L.fp8_linear_fwd_bf16_workspace_bytes(32, 48, 64)
+    assert nws >= 8 and L.fp8_linear_fwd_bf16_workspace_bytes(-1, 48, 64) == 0
+    # x [32,64], w [48,64], xq (ld 64), wq (ld 64), scales, y [32,48], ws
+    base = [P[0], 64, P[1], 64, 32, 48, 64, P[2], 64, P[3], 64, P[4], P[5], 48, P[6], nws, 0, None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return L.fp8_linear_fwd_bf16(*a)
+    assert call(a11=None) == 1                            # scales missing
+    assert call(a11=ctypes.c_void_p(0x10002)) == 2        # scales not 4-byte aligned
+    assert call(a1=32) == 1                               # ldx < K
+    assert call(a3=32) == 1                               # ldw < K
+    assert call(a7=None) == 1                             # xq missing
+    assert call(a8=72) == 2                               # ldxq % 16
+    assert call(a9=ctypes.c_void_p(0x20008)) == 2         # wq not 16-byte aligned
+    assert call(a9=P[2]) == 1                             # xq and wq the same buffer
+    assert call(a7=P[0]) == 1                             # xq is x
+    assert call(a13=40) == 1                              # ldy < N
+    assert call(a16=2) == 1                               # unknown accumulation mode
+    assert call(a14=None) == 3                            # no workspace
+    assert call(a15=nws - 1) == 3                         # workspace too small
+    assert call(a14=ctypes.c_void_p(0x10008)) == 2        # workspace not 16-byte aligned
+    assert call(a4=-1) == 1                               # M < 0
+
+
 def test_gemm_validation():
     L = _native.lib()
     # fwd (NT): A [M,K], B [N,K];  M=32, N=48, K=64

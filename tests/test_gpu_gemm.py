@@ -147,6 +147,53 @@ def test_linear_small_workload(accum):
 
 
 @pytest.mark.parametrize("accum", ACCUMS)
+@pytest.mark.parametrize("MNK", [(256, 1024, 512), (300, 200, 37), (1, 48, 16), (513, 257, 400)])
+def test_linear_fwd_bf16(accum, MNK):
+    """The linear forward from bf16 (both quantisations batched, then the
+    GEMM): codes and scales bit-exact against the oracle's quantiser, Y at
+    the GEMM bar on those codes, and every output byte-identical to the
+    separate calls (fp8_amax_quant of X and of W, then fp8_linear_fwd)."""
+    from fp8_tensorwise_scaled_amd import api
+    from tests.gpu_util import to_dev_bf16
+
+    M, N, K = MNK
+    x = synth.normal_bf16((M, K), 1.0, 4100 + M, outlier_frac=1e-3)
+    w = synth.normal_bf16((N, K), 0.02, 4200 + N)
+    xd, wd = to_dev_bf16(x), to_dev_bf16(w)
+    y, xq, wq, sc = api.fp8_linear_fwd_bf16(xd, wd, accum=accum)
+    xq2, _, sx2, _ = api.fp8_amax_quant(xd, E4, q=padded(np.zeros((M, K), np.uint8)))
+    wq2, _, sw2, _ = api.fp8_amax_quant(wd, E4, q=padded(np.zeros((N, K), np.uint8)))
+    y2 = api.fp8_linear_fwd(xq2, sx2, wq2, sw2, accum=accum)
+    torch.cuda.synchronize()
+    rx, rsx, _ = oracle.quant(x, E4)
+    rw, rsw, _ = oracle.quant(w, E4)
+    scales = sc.cpu().numpy()
+    assert (xq.cpu().numpy() == rx).all() and (wq.cpu().numpy() == rw).all()
+    assert scales[0] == np.float32(rsx) and scales[1] == np.float32(rsw)
+    check_gemm(bf16_bits(y), "nt", rx, E4, rsx, rw, E4, rsw, f"linear from bf16 {MNK}", accum=accum)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(xq, xq2) and torch.equal(wq, wq2)
+    assert scales[0] == float(sx2.cpu()[0]) and scales[1] == float(sw2.cpu()[0])
+
+
+def test_linear_fwd_bf16_empty():
+    """No tokens: both scales written (X's is 1), no Y; no reduction: Y = 0."""
+    from fp8_tensorwise_scaled_amd import api
+    from tests.gpu_util import to_dev_bf16
+
+    w = synth.normal_bf16((48, 64), 0.02, 4300)
+    y, xq, wq, sc = api.fp8_linear_fwd_bf16(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda:0"),
+                                            to_dev_bf16(w))
+    torch.cuda.synchronize()
+    assert y.shape == (0, 48)
+    assert sc.cpu().numpy()[0] == 1.0 and sc.cpu().numpy()[1] == np.float32(oracle.quant(w, E4)[1])
+    y, _, _, sc = api.fp8_linear_fwd_bf16(torch.empty((32, 0), dtype=torch.bfloat16, device="cuda:0"),
+                                          torch.empty((48, 0), dtype=torch.bfloat16, device="cuda:0"))
+    torch.cuda.synchronize()
+    assert (y.float() == 0).all() and (sc.cpu().numpy() == 1.0).all()
+
+
+@pytest.mark.parametrize("accum", ACCUMS)
 @pytest.mark.parametrize("MNK", [(256, 512, 384), (208, 160, 96), (2048, 768, 3072)])
 def test_dgrad_wgrad(accum, MNK):
     """dX = dY . W (NN) and dW = dY^T . X (TN) on the row-major codes of a
