@@ -366,8 +366,8 @@ def bench_mlp_small(args) -> int:
     us = _after_steps(step, {"g": lambda: api.fp8_linear_wgrad(gq, BSC[0:1], saved.aq, saved.scales[3:4], api.E5M2,
                                                                api.E4M3, out=out, accum=args.accum)},
                       args.gemm_reps)["g"]
-    roof = _roofline(f"gemm_kernel<1,0,256,*,*,*,0,3,{args.accum}> (E5M2 x E4M3, TN grad-weight dW_down "
-                     f"[{d},{h}], reduction over M={M})", "mfma", 2 * M * d * h, us, PEAK_FP8_TFLOPS, "TFLOP/s")
+    roof = _roofline(f"gemm_kernel<1,0,128,128,2,2,0,3,{args.accum}> (E5M2 x E4M3, TN grad-weight dW_down "
+                     f"[{d},{h}], reduction over M={M}; 144 tiles of 128x128, two blocks per CU)", "mfma", 2 * M * d * h, us, PEAK_FP8_TFLOPS, "TFLOP/s")
     res = {"metric": "FP8 relu² MLP fwd+bwd TFLOP/s, small block (M=2048, d=768, h=3072)",
            "value": round(tflops, 2), "ms_per_step": round(ms, 5),
            "data": "synthetic (seeded N(0,1) X, N(0,1/sqrt(fan_in)) weights, N(0,1e-3) dY with 0.1% x100 "
@@ -445,7 +445,7 @@ def bench_linear(args) -> int:
            "us_separate_calls": round(ms_sep * 1e3, 3),
            "us_median": round(per[len(per) // 2] * 1e3, 3), "us_min": round(per[0] * 1e3, 3),
            "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
-           "roofline": _roofline("gemm_kernel<0,0,256,*,*,*,0,0,%d> (E4M3 x E4M3, NT, one wave of tiles; "
+           "roofline": _roofline("gemm_kernel<0,0,128,128,2,2,0,0,%d> (E4M3 x E4M3, NT, 16 tiles of 128x128; "
                                  "latency-bound below the machine balance)" % args.accum, "mfma", flops, gemm_us,
                                  PEAK_FP8_TFLOPS, "TFLOP/s"),
            "gpu_clocks": clocks}
@@ -494,7 +494,7 @@ def bench_other(args) -> int:
         q = r.q
         us = _after_steps(step, {"g": lambda: api.fp8_linear_wgrad(q.gq.q, q.gq.scale, q.xq.q, q.xq.scale,
                                                                    out=q.dw, accum=args.accum)}, args.gemm_reps)["g"]
-        roof = _roofline(f"gemm_kernel<1,0,256,*,*,*,0,3,{args.accum}> (E5M2 x E4M3, TN grad-weight of the Q "
+        roof = _roofline(f"gemm_kernel<1,0,256,192,4,2,0,3,{args.accum}> (E5M2 x E4M3, TN grad-weight of the Q "
                          f"projection, dW [3072,3072], reduction over M={w.M})", "mfma", 2 * w.M * 3072 * 3072, us,
                          PEAK_FP8_TFLOPS, "TFLOP/s")
         res = {"metric": "FP8 decoder projection set fwd+bwd TFLOP/s (Q,K,V,O + relu2 MLP)",

@@ -25,8 +25,9 @@ hipError_t launch_bf16(const GemmArgs& g, hipStream_t st) {
 }  // namespace
 
 int64_t gemm_num_tiles(int64_t M, int64_t N) {
-  const int bn = gemm_detail::pick_bn(M, N);
-  return ((M + 255) / 256) * ((N + bn - 1) / bn);
+  const int tile = gemm_detail::pick_tile(M, N);
+  const int bm = tile == 128 ? 128 : 256, bn = tile;
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 int64_t gemm_max_tiles(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 63) / 64); }
 int64_t gemm_swiglu_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 127) / 128); }

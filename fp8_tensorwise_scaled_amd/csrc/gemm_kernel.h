@@ -130,17 +130,20 @@ struct Gemm {
   static_assert(A_LOADS * THREADS * 16 == BM * kBK && B_LOADS * THREADS * 16 == BN * kBK, "whole loads");
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int CLD = BN * 2 + 16;  // epilogue C tile row stride (bytes)
-  static constexpr int LDS = (2 * STAGE > BM * CLD) ? 2 * STAGE : BM * CLD;
+  // LDS: two stages, or the staged C tile plus the epilogue's reduction
+  // slots (RED, past the C tile), whichever is larger
+  static constexpr int LDS = (2 * STAGE > BM * CLD + 64) ? 2 * STAGE : BM * CLD + 64;
+  static constexpr int RED = LDS - 64;
   static_assert(LDS <= 160 * 1024 - 64, "LDS budget");
 };
 
 template <int FA, int FB, int BM, int BN, int WGM, int WGN, int EPI, int LAY, int ACC>
-__global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
+__global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel(GemmArgs g, int tiles_m, int tiles_n) {
   using G = Gemm<FA, FB, BM, BN, WGM, WGN, EPI, LAY, ACC>;
   constexpr int kThreads = G::THREADS;
   constexpr bool AMN = G::AMN, BMN = G::BMN;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
-  __shared__ uint32_t red[kThreads / 64];
+  uint32_t* red = reinterpret_cast<uint32_t*>(smem + G::RED);  // epilogue reductions only
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid % WGM, wn = wid / WGM;
@@ -165,9 +168,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) gemm_kernel(GemmArgs g, int
     kelems = min<int64_t>(g.kchunk, g.K - kbeg);
     cfp = g.cf + ks * g.split_stride;
   } else {
-    const int in_group = kGroupM * tiles_n;
-    const int first_m = (t / in_group) * kGroupM;
-    const int gm = min(kGroupM, tiles_m - first_m);
+    constexpr int kGM = kGroupM * 256 / BM;  // tile rows per group: 1024 output rows
+    const int in_group = kGM * tiles_n;
+    const int first_m = (t / in_group) * kGM;
+    const int gm = min(kGM, tiles_m - first_m);
     tm = first_m + (t % in_group) % gm;
     tn = (t % in_group) / gm;
   }
@@ -866,39 +870,50 @@ inline int pick_bn(int64_t M, int64_t N) {
   return eff(192) > eff(256) * 1.02 ? 192 : 256;
 }
 
+// Block tile of an FP8 product with an M x N output: 128 for 128x128 tiles,
+// else the width of a 256-row tile (pick_bn).  128x128 tiles (a third more
+// LDS reads per MFMA, two blocks per CU) are taken when 256-row tiles would
+// leave a quarter of the 256 CUs or more without a tile, e.g. a 1024 x 3072
+// grad-weight (64 tiles of 256x192, 192 of 128x128).
+inline int pick_tile(int64_t M, int64_t N) {
+  const int bn = pick_bn(M, N);
+  const int64_t t = ((M + 255) / 256) * ((N + bn - 1) / bn);
+  return t < 192 ? 128 : bn;
+}
+
 // FP8 products of one layout and accumulation mode.  Epilogues beyond the
 // plain store exist for the format pairs and layouts that use them: the
 // relu^2 block's forward (E4M3 x E4M3, NT) and backward (E5M2 x E4M3, NT or
 // NN), the gated block's projection (E4M3 x E4M3, NT) and backward (E5M2 x
 // E4M3, NN), and the fp32 store and accumulate epilogues of summed gradient
 // products (E5M2 x E4M3).
-template <int LAY, int ACC, int FA, int FB, int BN, int WGM, int WGN>
+template <int LAY, int ACC, int FA, int FB, int BM, int BN, int WGM, int WGN>
 hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
   switch (g.epi) {
-    case kEpiStore: return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStore, LAY, ACC>(g, st);
+    case kEpiStore: return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiStore, LAY, ACC>(g, st);
     case kEpiRelu2Max:
       if constexpr (LAY == 0 && FA == kE4M3 && FB == kE4M3)
-        return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Max, LAY, ACC>(g, st);
+        return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiRelu2Max, LAY, ACC>(g, st);
       break;
     case kEpiRelu2Bwd:
       if constexpr (LAY != 3 && FA == kE5M2 && FB == kE4M3)
-        return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiRelu2Bwd, LAY, ACC>(g, st);
+        return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiRelu2Bwd, LAY, ACC>(g, st);
       break;
     case kEpiSwiGLU:
-      if constexpr (LAY == 0 && FA == kE4M3 && FB == kE4M3 && BN == 256)
+      if constexpr (LAY == 0 && FA == kE4M3 && FB == kE4M3 && BM == 256 && BN == 256)
         return launch_cfg<FA, FB, 256, 256, 2, 2, kEpiSwiGLU, LAY, ACC>(g, st);
       break;
     case kEpiSwiGLUBwd:
       if constexpr (LAY == 2 && FA == kE5M2 && FB == kE4M3)
-        return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiSwiGLUBwd, LAY, ACC>(g, st);
+        return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiSwiGLUBwd, LAY, ACC>(g, st);
       break;
     case kEpiStoreF32:
     case kEpiAccF32:
     case kEpiAccF32Bf16:
       if constexpr (FA == kE5M2 && FB == kE4M3) {
-        if (g.epi == kEpiStoreF32) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiStoreF32, LAY, ACC>(g, st);
-        if (g.epi == kEpiAccF32) return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAccF32, LAY, ACC>(g, st);
-        return launch_cfg<FA, FB, 256, BN, WGM, WGN, kEpiAccF32Bf16, LAY, ACC>(g, st);
+        if (g.epi == kEpiStoreF32) return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiStoreF32, LAY, ACC>(g, st);
+        if (g.epi == kEpiAccF32) return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiAccF32, LAY, ACC>(g, st);
+        return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiAccF32Bf16, LAY, ACC>(g, st);
       }
       break;
     default: break;
@@ -909,10 +924,14 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
 template <int LAY, int ACC, int FA, int FB>
 hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
   // 256x192 tiles run 8 waves (4x2, 64x96 wave tiles, two waves per SIMD);
-  // 256x256 tiles 4 waves (2x2, 128x128 wave tiles)
-  if (g.epi == kEpiSwiGLU) return launch_bn<LAY, ACC, FA, FB, 256, 2, 2>(g, st);
-  return pick_bn(g.M, g.N) == 192 ? launch_bn<LAY, ACC, FA, FB, 192, 4, 2>(g, st)
-                                  : launch_bn<LAY, ACC, FA, FB, 256, 2, 2>(g, st);
+  // 256x256 tiles 4 waves (2x2, 128x128 wave tiles); 128x128 tiles 4 waves
+  // (2x2, 64x64 wave tiles), two blocks per CU
+  if (g.epi == kEpiSwiGLU) return launch_bn<LAY, ACC, FA, FB, 256, 256, 2, 2>(g, st);
+  switch (pick_tile(g.M, g.N)) {
+    case 128: return launch_bn<LAY, ACC, FA, FB, 128, 128, 2, 2>(g, st);
+    case 192: return launch_bn<LAY, ACC, FA, FB, 256, 192, 4, 2>(g, st);
+    default: return launch_bn<LAY, ACC, FA, FB, 256, 256, 2, 2>(g, st);
+  }
 }
 
 template <int LAY, int ACC>
