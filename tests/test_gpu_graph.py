@@ -138,13 +138,44 @@ def _fp8_linear():
     return step, outs
 
 
+def _fp8_linear_from_bf16():
+    """A linear's forward from bf16 X and W (batched quantisation, then the
+    GEMM) followed by its two backward GEMMs on the codes it wrote."""
+    from fp8_tensorwise_scaled_amd import _native, api
+
+    M, K, N = 300, 200, 272
+    x = to_dev_bf16(synth.normal_bf16((M, K), 1.0, 61))
+    w = to_dev_bf16(synth.normal_bf16((N, K), 0.05, 62))
+    dy = to_dev_bf16(synth.normal_bf16((M, N), 1e-3, 63))
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    L = _native.lib()
+    ld = -(-K // 16) * 16
+    outs = dict(y=torch.empty((M, N), **bf), xq=torch.empty((M, ld), **u8)[:, :K], wq=torch.empty((N, ld), **u8)[:, :K],
+                scales=torch.empty(2, **f32), gq=torch.empty((M, N), **u8), sg=torch.empty(1, **f32),
+                ag=torch.empty(1, **f32), dx=torch.empty((M, K), **bf), dw=torch.empty((N, K), **bf))
+    ws = torch.empty(max(L.fp8_linear_fwd_bf16_workspace_bytes(M, N, K), 16), **u8)
+    wsg = torch.empty(max(L.fp8_amax_quant_workspace_bytes(M, N), 16), **u8)
+
+    def step():
+        api.fp8_linear_fwd_bf16(x, w, xq=outs["xq"], wq=outs["wq"], scales=outs["scales"], out=outs["y"], ws=ws)
+        api.fp8_amax_quant(dy, api.E5M2, q=outs["gq"], scale=outs["sg"], amax=outs["ag"], ws=wsg)
+        sx, sw = outs["scales"][0:1], outs["scales"][1:2]
+        api.fp8_linear_dgrad(outs["gq"], outs["sg"], outs["wq"], sw, out=outs["dx"])
+        api.fp8_linear_wgrad(outs["gq"], outs["sg"], outs["xq"], sx, out=outs["dw"])
+    return step, outs
+
+
 def _bytes(t):
     return t.detach().contiguous().view(torch.uint8).cpu().clone()
 
 
-@pytest.mark.parametrize("make", [_relu2, _swiglu, _lm_head_ce, _newton_schulz, _rmsnorm, _fp8_linear],
+@pytest.mark.parametrize("make", [_relu2, _swiglu, _lm_head_ce, _newton_schulz, _rmsnorm, _fp8_linear,
+                                  _fp8_linear_from_bf16],
                          ids=["relu2_block", "swiglu_block", "lm_head_ce", "newton_schulz", "rmsnorm_quant",
-                              "fp8_linear"])
+                              "fp8_linear", "fp8_linear_from_bf16"])
 def test_graph_replays_match_eager(make):
     step, outs = make()
     step()
