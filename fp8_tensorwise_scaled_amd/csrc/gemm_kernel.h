@@ -26,7 +26,9 @@
 //    tile (4x4 MFMA tiles, 256 accumulator registers: LDS traffic per MFMA
 //    at its lowest).  256x192 tiles run 8 waves in a 4x2 grid of 64x96 wave
 //    tiles, two waves per SIMD, so one wave's LDS and barrier waits overlap
-//    the other's MFMAs.
+//    the other's MFMAs.  Small outputs, which 256-row tiles would spread
+//    over too few CUs, take 128x128 tiles: 4 waves of 64x64, two blocks per
+//    CU.
 //  * K is consumed 128 codes per stage; stages are double-buffered in LDS,
 //    loaded with 16-byte buffer loads into registers one stage ahead.
 //    K-major tiles are 128-byte rows; the 16-byte chunk c of row r is stored
@@ -46,8 +48,9 @@
 //    consecutive output columns of one row: the epilogue packs them to bf16,
 //    stages the tile in LDS and writes 16-byte row chunks to HBM.
 //  * Workgroups are dispatched round-robin over the 8 XCDs; tile ids are
-//    remapped so each XCD works on a contiguous run of tiles, grouped 4 tile
-//    rows deep, so concurrently running tiles share operands in that XCD's L2.
+//    remapped so each XCD works on a contiguous run of tiles, grouped 1024
+//    output rows deep, so concurrently running tiles share operands in that
+//    XCD's L2.
 //  * Epilogues (enum Epilogue in internal.h): plain bf16 store; the relu^2
 //    block's relu^2-max and relu^2-backward fusions, whose tile maxima are
 //    taken on fp32 values before the (monotone) bf16 rounding; fp32 store and
@@ -148,7 +151,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid % WGM, wn = wid / WGM;
 
-  // ---- tile id: XCD-contiguous runs, grouped kGroupM tile-rows deep
+  // ---- tile id: XCD-contiguous runs, grouped 1024 output rows deep
   const int nt = gridDim.x;  // tiles, or work items of the upper-triangle mode
   const int bid = blockIdx.x;
   const int xcd = bid & 7, idx = bid >> 3, per = nt >> 3, rem = nt & 7;
