@@ -99,6 +99,25 @@ def test_random_shapes(accum):
                    accum=accum)
 
 
+@pytest.mark.parametrize("accum", ACCUMS)
+@pytest.mark.parametrize("kind", LAYOUTS)
+def test_tile_threshold_shapes(accum, kind):
+    """Output shapes on both sides of the switch between 256-row tiles and
+    128x128 tiles (192 tiles of 256x192): 2816 x 3072 (176 tiles of 256x192,
+    so 528 of 128x128), 3072 x 3072 (192 tiles of 256x192), and ragged
+    neighbours of both; a reduction of 390 (not a multiple of 16).  Checked
+    on sampled output rows, the first and last included."""
+    rng = np.random.default_rng(31 + LAYOUTS.index(kind) + 10 * accum)
+    for M, N in ((2816, 3072), (3072, 3072), (2811, 3000), (3059, 3112)):
+        R = 390
+        qa, sa, qb, sb = operands(kind, M, N, R, E5, E4, 8100 + M + N)
+        y = run(kind, padded(qa), E5, sa, padded(qb), E4, sb, accum)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 22, replace=False)]))
+        got = bf16_bits(y)[rows]
+        check_gemm(got, kind, qa, E5, sa, qb, E4, sb, f"threshold {kind} {M}x{N}x{R}", rows=rows, accum=accum)
+
+
 @pytest.mark.parametrize("kind", LAYOUTS)
 def test_exactly_representable_sums(kind):
     """Codes of magnitude in [1, 4) with unit scales: every product is a
