@@ -745,7 +745,15 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   gu.layout = kLayTN; gu.c = dw_up; gu.ldc = d; gu.accum = accum;
   if (launch_gemm(gg, s) != hipSuccess || launch_gemm(gu, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 7. dX = dGq . Wg + dUq . Wu (NN), summed in fp32 and rounded once
+  // 7. dX = dGq . Wg + dUq . Wu (NN), summed in fp32 and rounded once: one
+  // launch over both products when h is a whole number of 128-deep stages,
+  // else the first product stored in fp32 and the second added to it
+  if (h % 128 == 0) {
+    GemmArgs x = gemm_args(dgq, h, FP8MLP_E5M2, &bsc[1], sv->wgq, d, FP8MLP_E4M3, &sc[1], M, d, 2 * h, kEpiStore2);
+    x.layout = kLayNN; x.a_2 = duq; x.b_2 = sv->wuq; x.sa_2 = &bsc[2]; x.sb_2 = &sc[2];
+    x.c = dx; x.ldc = d; x.accum = accum;
+    return launch_gemm(x, s) != hipSuccess ? FP8MLP_EHIP : FP8MLP_OK;
+  }
   GemmArgs x1 = gemm_args(dgq, h, FP8MLP_E5M2, &bsc[1], sv->wgq, d, FP8MLP_E4M3, &sc[1], M, d, h, kEpiStoreF32);
   x1.layout = kLayNN; x1.cf = dxf; x1.ldc = d; x1.accum = accum;
   GemmArgs x2 = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->wuq, d, FP8MLP_E4M3, &sc[2], M, d, h,

@@ -189,7 +189,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   constexpr int ES = FA == kBF16 ? 2 : 1;
   static_assert((FA == kBF16) == (FB == kBF16), "bf16 operands come in pairs");
   static_assert(FA != kBF16 || (LAY == 0 && ACC == 0), "bf16 operands: NT products only");
+  // kEpiStore2: two segments of K/2 (a multiple of kBK), each with its own
+  // operands; descriptors span one segment
+  constexpr bool kSeg2 = EPI == kEpiStore2;
+  static_assert(!kSeg2 || (LAY == 2 && FA != kBF16), "two-segment products: NN FP8 only");
+  if constexpr (kSeg2) kelems = g.K / 2;
   const int K = (int)kelems * ES;
+  const int nseg1 = kSeg2 ? K / kBK : 0;  // stages of the first segment
   const int64_t lda = g.lda * ES, ldb = g.ldb * ES;
   const int rows_a = (int)min<int64_t>(BM, g.M - m0);
   const int rows_b = (int)min<int64_t>(BNO, g.N - n0);
@@ -204,6 +210,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   const __amdgpu_buffer_rsrc_t ra = rsrc_of(g.a, lda, m0, rows_a, AMN);
   const __amdgpu_buffer_rsrc_t rb = rsrc_of(g.b, ldb, n0, rows_b, BMN);
   const __amdgpu_buffer_rsrc_t rb2 = kSwiGLU ? rsrc_of(g.b2, ldb, n0, rows_b, false) : rb;
+  const __amdgpu_buffer_rsrc_t ra_2 = kSeg2 ? rsrc_of(g.a_2, lda, m0, rows_a, AMN) : ra;
+  const __amdgpu_buffer_rsrc_t rb_2 = kSeg2 ? rsrc_of(g.b_2, ldb, n0, rows_b, BMN) : rb;
 
   // K-major loads.  Per-thread 16-byte chunks each stage: chunk id =
   // tid + THREADS*j, row = id / 8, logical column chunk = id % 8 (eight lanes
@@ -235,7 +243,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
     c = id % cpr;
   };
   const uint32_t kstep_a = (uint32_t)(kBK * lda), kstep_b = (uint32_t)(kBK * ldb);
-  const int nk = (K + kBK - 1) / kBK;
+  const int nk = (K + kBK - 1) / kBK * (kSeg2 ? 2 : 1);
 
   // The chunk that holds the last byte of an operand's descriptor range E
   // (the end of the last row it reads): when E is not a multiple of 4 the
@@ -288,7 +296,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   // rest the up half, from the same rows of the other operand
   static_assert(!kSwiGLU || (G::B_LOADS % 2 == 0 && (G::B_LOADS / 2) * kRowStep == BN / 2),
                 "each B load must lie in one half");
-  auto gload_one = [&](int j, int kt) {
+  auto gload_one = [&](int j, int ktg) {
+    // stage ktg of the reduction; with two segments, stage kt of segment s
+    const bool s2 = kSeg2 && ktg >= nseg1;
+    const int kt = s2 ? ktg - nseg1 : ktg;
+    const __amdgpu_buffer_rsrc_t& rsa = s2 ? ra_2 : ra;
+    const __amdgpu_buffer_rsrc_t& rsb = s2 ? rb_2 : rb;
     const int k0 = kt * kBK;
     const bool is_a = j < G::A_LOADS;
     const int jb = j - G::A_LOADS;
@@ -299,13 +312,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
       const bool inside = (is_a ? m0 : n0) + c * 16 < (is_a ? g.M : g.N);
       const uint32_t off = inside ? (uint32_t)(krow * (is_a ? lda : ldb)) + c * 16 + kt * (is_a ? kstep_a : kstep_b)
                                   : 0x80000000u;
-      stg[j] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra : rb, off, 0, 0);
+      stg[j] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? rsa : rsb, off, 0, 0);
     } else {
       const bool up = kSwiGLU && !is_a && jb >= G::B_LOADS / 2;
       const int jj = is_a ? j : (up ? jb - G::B_LOADS / 2 : jb);
       const uint32_t base = is_a ? goff_a + jj * gstep_a : goff_b + jj * gstep_b;
       const uint32_t off = (k0 + colk0 < K) ? base + k0 : 0x80000000u;  // out of range -> 0
-      stg[j] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra : (up ? rb2 : rb), off, 0, 0);
+      stg[j] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? rsa : (up ? rb2 : rsb), off, 0, 0);
     }
   };
   // last: the stage written is the last one of the reduction
@@ -451,9 +464,25 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   };
   using T = std::true_type;
   using F = std::false_type;
+  // kEpiStore2: at the first stage of the second segment the accumulators
+  // hold the first segment's sum; scaled by RN32(p1 / p2) they continue as
+  // if its products carried the second segment's scale
+  auto boundary = [&](int kt) {
+    if constexpr (kSeg2) {
+      if (kt == nseg1) {
+        const float p1 = (*g.sa) * (*g.sb), p2 = (*g.sa_2) * (*g.sb_2);
+        const float r = p1 / p2;
+#pragma unroll
+        for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < G::FN; ++j) acc[i][j] *= r;
+      }
+    }
+  };
   int kt = 0;
-  for (; kt + 2 < nk; ++kt) iteration(kt, T{}, T{});
-  if (kt + 1 < nk) { iteration(kt, T{}, F{}); ++kt; }
+  for (; kt + 2 < nk; ++kt) { boundary(kt); iteration(kt, T{}, T{}); }
+  if (kt + 1 < nk) { boundary(kt); iteration(kt, T{}, F{}); ++kt; }
+  boundary(kt);
   iteration(kt, F{}, F{});
   __syncthreads();
 
@@ -657,6 +686,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   float p;
   if constexpr (FA == kBF16) p = g.alpha;
   else if constexpr (kSwiGLU) p = (*g.sa) * (wn == 0 ? *g.sb : *g.sb2);  // gate or up half
+  else if constexpr (kSeg2) p = (*g.sa_2) * (*g.sb_2);  // the second segment's scale
   else p = (*g.sa) * (*g.sb);  // RN32(sa * sb)
   // relu^2-max epilogue: the tile's max of H = RN_bf16(x), x = RN32(acc p),
   // is RN_bf16 of the max of x (both roundings are monotone), so it is taken
@@ -840,7 +870,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
     const __bf16 db = (__bf16)dmax;
     mx = (uint32_t)__builtin_bit_cast(unsigned short, db) & 0x7FFFu;
   }
-  if constexpr (EPI != kEpiStore) {
+  if constexpr (EPI == kEpiRelu2Max || EPI == kEpiRelu2Bwd || kSgBwd) {
     mx = block_max_u32(mx, red);
     if (tid == 0) g.partials[t] = mx;
   }
@@ -906,6 +936,10 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
       if constexpr (LAY == 0 && FA == kE4M3 && FB == kE4M3 && BM == 256 && BN == 256)
         return launch_cfg<FA, FB, 256, 256, 2, 2, kEpiSwiGLU, LAY, ACC>(g, st);
       break;
+    case kEpiStore2:  // not on 4-wave 256x256 tiles, whose registers hold no second descriptor set
+      if constexpr (LAY == 2 && FA == kE5M2 && FB == kE4M3 && !(BM == 256 && BN == 256))
+        return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiStore2, LAY, ACC>(g, st);
+      break;
     case kEpiSwiGLUBwd:
       if constexpr (LAY == 2 && FA == kE5M2 && FB == kE4M3)
         return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiSwiGLUBwd, LAY, ACC>(g, st);
@@ -933,7 +967,9 @@ hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
   switch (pick_tile(g.M, g.N)) {
     case 128: return launch_bn<LAY, ACC, FA, FB, 128, 128, 2, 2>(g, st);
     case 192: return launch_bn<LAY, ACC, FA, FB, 256, 192, 4, 2>(g, st);
-    default: return launch_bn<LAY, ACC, FA, FB, 256, 256, 2, 2>(g, st);
+    default:
+      if (g.epi == kEpiStore2) return launch_bn<LAY, ACC, FA, FB, 256, 192, 4, 2>(g, st);
+      return launch_bn<LAY, ACC, FA, FB, 256, 256, 2, 2>(g, st);
   }
 }
 

@@ -73,6 +73,9 @@ enum Epilogue : int {
                       // G = RN_bf16(RN32(sa sb) acc) -> c, U = RN_bf16(RN32(sa sb2)
                       // acc) -> c2, A = RN_bf16(silu(G) U) -> c3 (all ldc);
                       // partial[tile] = max |A| (bf16 bits) when partials is set
+  kEpiStore2 = 9,     // two reduction segments (a, b then a_2, b_2, each K/2 long):
+                      // C = RN_bf16(p2 (acc_2 + RN32(p1 / p2) acc_1)),
+                      // p1 = RN32(sa sb), p2 = RN32(sa_2 sb_2)  (NN only)
   kEpiSwiGLUBwd = 8,  // gated MLP backward: dA = RN_bf16(p * acc) (not stored), with G
                       // (aux) and U (aux2): dG = RN_bf16(dA U silu'(G)) -> c,
                       // dU = RN_bf16(dA silu(G)) -> c2 (ldc); partial[tile] =
@@ -123,6 +126,12 @@ struct GemmArgs {
   const float* sb2;
   uint16_t* c2;
   uint16_t* c3;
+  // kEpiStore2: the second segment's operands (same leading dimensions) and
+  // scales
+  const uint8_t* a_2;
+  const uint8_t* b_2;
+  const float* sa_2;
+  const float* sb_2;
   // Upper-triangle split-K mode (M == N, A and B the same matrix's rows):
   // tri_tiles > 0 is the number of 256-wide tile rows; work item w covers
   // triangle tile w / ksplit (tile row <= tile column) and the K range

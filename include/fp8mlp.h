@@ -279,6 +279,8 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
 /*     dGq, dUq = quant(dG), quant(dU)                                       */
 /*     dW_gate = TN(dGq, Xq);  dW_up = TN(dUq, Xq)                           */
 /*     dX = RN_bf16(RN32(RN32(p_g NN(dGq,Wgq)) + RN32(p_u NN(dUq,Wuq))))      */
+/*       (h a multiple of 128: one fp32 accumulation of both products,     */
+/*       dX = RN_bf16(p_u (NN(dUq,Wuq) + RN32(p_g / p_u) NN(dGq,Wgq))))       */
 /* Requirements as for the relu^2 block (M, d, h multiples of 16, M == 0    */
 /* valid, 16-byte aligned pointers).                                        */
 /* ------------------------------------------------------------------------ */

@@ -122,6 +122,19 @@ def test_deterministic_and_reuse():
 
 
 @pytest.mark.parametrize("accum", ACCUMS, ids=["fast", "exact"])
+def test_whole_stage_width_block(accum):
+    """M=256, d=192, h=384: h is a whole number of 128-deep stages, so dX is
+    one launch over both products; every stage on every row and column
+    against the oracle."""
+    w = synth.SwigluWorkload(45, 256, 192, 384, sigma_in=1 / np.sqrt(192), sigma_down=1 / np.sqrt(384))
+    g = run_block(w, accum)
+    sc, _, b = sc_.full_chain_scales(g["x"], g["wg"], g["wu"], g["wd"], g["dy"])
+    rows, cols = np.arange(w.M), np.arange(w.h)
+    o = sc_.sampled_chain(g["x"], g["wg"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
+    sc_.compare(g, o, sc, rows, cols, accum)
+
+
+@pytest.mark.parametrize("accum", ACCUMS, ids=["fast", "exact"])
 def test_tiny_ragged_block(accum):
     """M=48, d=64, h=176: every GEMM is a single ragged tile; every stage on
     every row and column against the oracle."""
