@@ -345,6 +345,57 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
 #pragma unroll
     for (int j = 0; j < G::FN; ++j) acc[i][j] = v16f{};
 
+  // Epilogue chunks: each thread owns NCH 16-byte chunks of the output tile,
+  // chunk id tid + THREADS*it being row id / CPR, 8-column group id % CPR.
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  constexpr int NCH = BM * CPR / kThreads;
+  static_assert(NCH * kThreads == BM * CPR, "whole epilogue chunks");
+  const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
+  constexpr bool kSgBwd = EPI == kEpiSwiGLUBwd;
+  const bool vec_aux = (EPI != kEpiRelu2Bwd && !kSgBwd) ||
+                       (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0) &&
+                        (!kSgBwd || (((reinterpret_cast<uintptr_t>(g.aux2) & 15u) == 0) &&
+                                     ((reinterpret_cast<uintptr_t>(g.c2) & 15u) == 0))));
+  // chunk `it` of a bf16 [M, N] input with leading dimension ldaux; zeros
+  // past N and for rows past M
+  auto load_chunk = [&](const uint16_t* src, int it) {
+    const int id = tid + kThreads * it;
+    const int64_t gr = m0 + id / CPR, gc = n0 + (id % CPR) * 8;
+    v4u v = v4u{0u, 0u, 0u, 0u};
+    if (gr < g.M && gc < g.N) {
+      if (gc + 8 <= g.N && vec_c && vec_aux) {
+        v = *reinterpret_cast<const v4u*>(src + gr * g.ldaux + gc);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = gc + 2 * e < g.N ? src[gr * g.ldaux + gc + 2 * e] : 0u;
+          const uint32_t hi = gc + 2 * e + 1 < g.N ? src[gr * g.ldaux + gc + 2 * e + 1] : 0u;
+          v[e] = lo | (hi << 16);
+        }
+      }
+    }
+    return v;
+  };
+  // The relu^2-backward epilogue reads H at its chunks.  H is prefetched in
+  // the last two iterations of the main loop, where every CU would otherwise
+  // wait for it at once after the loop.  Chunk t < kPf1 is loaded as soon as
+  // the stage register it reuses has been written to LDS (the second-to-last
+  // iteration issues no global loads); with two waves per SIMD the next kPf2
+  // chunks are loaded during the last iteration.  Only for tiles whose every
+  // chunk takes the vector path; the other chunks are loaded after the loop.
+  // (The gated backward's G and U, prefetched the same way, measured slower
+  // than loading them chunk by chunk in the epilogue.)
+  constexpr bool kPfH = EPI == kEpiRelu2Bwd;
+  v4u hv[kPfH ? NCH : 1];
+  constexpr int kPf1 = NCH < G::LOADS ? NCH : G::LOADS;
+  constexpr int kPf2Max = kThreads == 512 ? 5 : 0;  // register budget of the last iteration
+  constexpr int kPf2 = NCH - kPf1 < kPf2Max ? NCH - kPf1 : kPf2Max;
+  const bool pf_h = kPfH && m0 + BM <= g.M && n0 + BN <= g.N && vec_c && vec_aux;
+  auto h_vec = [&](int it) {
+    const int id = tid + kThreads * it;
+    return *reinterpret_cast<const v4u*>(g.aux + (m0 + id / CPR) * g.ldaux + n0 + (id % CPR) * 8);
+  };
+
   // Fragments: lane reads output index (lane & 31) of a 32-wide block, the
   // 32 reduction values starting at ks*64 + (lane >> 5)*32, in two 16-byte
   // halves: one ds_read_b128 each from a K-major tile, two transposing
@@ -416,6 +467,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   // sched_barrier fences keep this order through instruction scheduling.
   constexpr int kTail = 4;
   constexpr int STEPS_A = NM > NR ? (NM > G::LOADS ? NM : G::LOADS) : (NR > G::LOADS ? NR : G::LOADS);
+  static_assert(kPf2 <= STEPS_A, "the last iteration issues one H prefetch per step");
   Frag f0, f1;
 
 #pragma unroll
@@ -442,7 +494,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
         if (t < G::LOADS) {
           swrite_one(t, nxt, !HN2);  // stage kt+1 is the last one when kt+2 does not exist
           if constexpr (HN2) gload_one(t, kt + 2);
+          if constexpr (kPfH && !HN2) {
+            if (t < kPf1 && pf_h) hv[t] = h_vec(t);
+          }
         }
+      }
+      if constexpr (kPfH && !HN && kPf2 > 0) {
+        if (t < kPf2 && pf_h) hv[kPf1 + t] = h_vec(kPf1 + t);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -638,46 +696,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   }
 
   // ---- epilogue
-  // Each thread owns NCH 16-byte chunks of the output tile: chunk id
-  // tid + THREADS*it is row id / CPR, 8-column group id % CPR.
-  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
-  constexpr int NCH = BM * CPR / kThreads;
-  static_assert(NCH * kThreads == BM * CPR, "whole epilogue chunks");
-  const bool vec_c = ((reinterpret_cast<uintptr_t>(g.c) & 15u) == 0) && (g.ldc % 8 == 0);
-  constexpr bool kSgBwd = EPI == kEpiSwiGLUBwd;
-  const bool vec_aux = (EPI != kEpiRelu2Bwd && !kSgBwd) ||
-                       (((reinterpret_cast<uintptr_t>(g.aux) & 15u) == 0) && (g.ldaux % 8 == 0) &&
-                        (!kSgBwd || (((reinterpret_cast<uintptr_t>(g.aux2) & 15u) == 0) &&
-                                     ((reinterpret_cast<uintptr_t>(g.c2) & 15u) == 0))));
-  // The relu^2-backward epilogue needs H at its chunks.  With two waves per
-  // SIMD (THREADS = 512) the loads are issued first, in flight while the tile
-  // is staged in LDS; the 4-wave layout has no registers to spare next to its
-  // 256 accumulators and issues them after staging.
-  constexpr bool kEarlyH = EPI == kEpiRelu2Bwd && kThreads == 512;
-  // chunk `it` of a bf16 [M, N] input with leading dimension ldaux; zeros
-  // past N and for rows past M
-  auto load_chunk = [&](const uint16_t* src, int it) {
-    const int id = tid + kThreads * it;
-    const int64_t gr = m0 + id / CPR, gc = n0 + (id % CPR) * 8;
-    v4u v = v4u{0u, 0u, 0u, 0u};
-    if (gr < g.M && gc < g.N) {
-      if (gc + 8 <= g.N && vec_c && vec_aux) {
-        v = *reinterpret_cast<const v4u*>(src + gr * g.ldaux + gc);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = gc + 2 * e < g.N ? src[gr * g.ldaux + gc + 2 * e] : 0u;
-          const uint32_t hi = gc + 2 * e + 1 < g.N ? src[gr * g.ldaux + gc + 2 * e + 1] : 0u;
-          v[e] = lo | (hi << 16);
-        }
-      }
-    }
-    return v;
-  };
-  v4u hv[EPI == kEpiRelu2Bwd ? NCH : 1];
+  // H chunks the main loop did not prefetch are loaded here: with two waves
+  // per SIMD (THREADS = 512) before the tile is staged in LDS, so that they
+  // are in flight while it is; the 4-wave layout has no registers to spare
+  // next to its 256 accumulators and loads them after staging.
+  constexpr bool kEarlyH = kPfH && kThreads == 512;
   auto load_h = [&]() {
 #pragma unroll
-    for (int it = 0; it < NCH; ++it) hv[it] = load_chunk(g.aux, it);
+    for (int it = 0; it < NCH; ++it) {
+      const bool pre = pf_h && (it < kPf1 ? nk >= 2 : it < kPf1 + kPf2);
+      if (!pre) hv[it] = load_chunk(g.aux, it);
+    }
   };
   if constexpr (kEarlyH) load_h();
 
@@ -718,7 +747,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
     }
   }
   __syncthreads();
-  if constexpr (EPI == kEpiRelu2Bwd && !kEarlyH) load_h();
+  if constexpr (kPfH && !kEarlyH) load_h();
 
   if constexpr (kSwiGLU) {
     // Chunk pairs: row id / CPH, gate chunk id % CPH of the staged row and
