@@ -222,7 +222,7 @@ def compare(g: dict, o: dict, sc: dict, rows, cols, accum=ACC_FAST):
     _codes_equal_where(duq_c, o["dUqt_c"], du_c == o["dUt_c"], "dUq columns")
 
     # ---- end to end against the oracle chain
-    moved = lambda q, r: (int((q != r).any(1).sum()), q.shape[0])
+    moved = lambda q, r: (q != r).any(1)
     chain_close(g["y"][rows], o["Y_r"], "Y rows", accum, moved(aq_r, o["Aq_r"]))
     chain_close(g["dx"][rows], o["dX_r"], "dX rows", accum,
                 moved(np.concatenate([dgq_r, duq_r], 1), np.concatenate([o["dGq_r"], o["dUq_r"]], 1)))

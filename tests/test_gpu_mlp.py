@@ -136,3 +136,27 @@ def test_tiny_ragged_block(accum):
     rows, cols = np.arange(w.M), np.arange(w.h)
     o = sampled_chain(g["x"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
     compare_block(g, o, sc, rows, cols, accum)
+
+
+# (M, d, h, accum): the relu^2-backward GEMM dA [M, h] (K = d) on 256-row
+# tiles whose interior tiles prefetch H in the main loop's last two
+# iterations and whose ragged edge tiles load it after the loop:
+# 4-wave 256x256 tiles with 3 reduction stages, the same with one stage
+# (nothing prefetched before the last iteration), 8-wave 256x192 tiles
+# (which also prefetch during the last iteration)
+PREFETCH_CASES = [(2096, 384, 6208, ACC_FAST), (2096, 384, 6208, ACC_EXACT), (2096, 128, 6208, ACC_FAST),
+                  (2096, 384, 4624, ACC_FAST)]
+
+
+@pytest.mark.parametrize("M,d,h,accum", PREFETCH_CASES,
+                         ids=["256x256-fast", "256x256-exact", "256x256-one-stage", "256x192-fast"])
+def test_relu2_backward_prefetch_tiles(M, d, h, accum):
+    """Every stage against the oracle on sampled rows and columns that cover
+    interior and edge tiles of the relu^2-backward GEMM."""
+    w = synth.MLPWorkload(M + d + h, M, d, h, sigma_up=d ** -0.5, sigma_down=h ** -0.5)
+    g = run_block(w, accum)
+    sc, _, _ = full_chain_scales(g["x"], g["wu"], g["wd"], g["dy"])
+    rows = np.unique(np.concatenate([np.arange(0, M, 37), np.arange(M - 45, M), np.arange(250, 262)]))
+    cols = np.unique(np.concatenate([np.arange(0, h, 29), np.arange(h - 60, h), np.arange(186, 198)]))
+    o = sampled_chain(g["x"], g["wu"], g["wd"], g["dy"], sc, rows, cols)
+    compare_block(g, o, sc, rows, cols, accum)

@@ -70,3 +70,29 @@ def test_compare_block_accepts_the_oracle_and_rejects_planted_errors(accum):
                       ("dW_down element", planted("dw_down", k, 40))):
         with pytest.raises(AssertionError):
             compare_block(bad, o, sc, rows, cols, accum)
+
+
+def test_chain_bar_exempts_only_rows_downstream_of_a_moved_code():
+    """Exact mode holds every output row to the max-relative bar except the
+    rows marked as downstream of a moved code; the Frobenius bar holds for
+    all rows."""
+    from tests.mlp_chain import chain_close
+
+    rng = np.random.default_rng(7)
+    ref32 = rng.standard_normal((64, 96)).astype(np.float32)
+    to_bits = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ref = to_bits(ref32)
+    got = ref.copy()
+    got[5] = to_bits(bits_f64(ref[5]) * 1.02)  # one row off by 2% (a moved code's worth)
+    marked = np.zeros(64, bool)
+    marked[5] = True
+    chain_close(got, ref, "planted row, marked", accum=1, moved=marked)
+    chain_close(got, ref, "planted row, fast mode", accum=0)
+    with pytest.raises(AssertionError):
+        chain_close(got, ref, "planted row, unmarked", accum=1)
+    with pytest.raises(AssertionError):
+        chain_close(got, ref, "planted row, another row marked", accum=1, moved=np.roll(marked, 1))
+    wide = ref.copy()
+    wide[:] = to_bits(bits_f64(ref) * 1.05)  # every row off: the Frobenius bar fails
+    with pytest.raises(AssertionError):
+        chain_close(wide, ref, "every row off", accum=1, moved=np.ones(64, bool))
