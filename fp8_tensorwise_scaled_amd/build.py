@@ -42,6 +42,14 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # Resolve every symbol now, in a child process: a kernel template whose
+    # host pass failed silently leaves its launch stub undefined, which would
+    # otherwise surface only when the library is first loaded.
+    chk = subprocess.run([sys.executable, "-c", "import ctypes, os, sys; ctypes.CDLL(sys.argv[1], mode=os.RTLD_NOW)",
+                          tmp], capture_output=True, text=True)
+    if chk.returncode != 0:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load:\n{chk.stderr}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
