@@ -575,9 +575,16 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
   if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
   if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 2. chunks of C rows: logits, loss and dZ, dZ codes, grad-input, grad-weight
+  // 2. chunks of C rows: logits, loss and dZ, dZ codes, grad-input, grad-weight.
+  //    Two equal chunks (a multiple of 128 rows, V a multiple of 4, so that
+  //    both reduction segments end on whole stages and dwords) keep the first
+  //    chunk's dZ codes in the fp32 slot, which they then do not need, and
+  //    take dW as one two-segment product after the loop:
+  //    dW = RN_bf16(p_2 (S_2 + RN32(p_1 / p_2) S_1)), p_k = RN32(s_k sx).
+  const bool seg2 = M == 2 * C && C % 128 == 0 && V % 4 == 0 && C * Vp <= V * K * 4;
   int64_t k = 0;
   for (int64_t c0 = 0; c0 < M; c0 += C, ++k) {
+    uint8_t* dzk = (seg2 && k == 0) ? reinterpret_cast<uint8_t*>(dwf) : dzq;  // this chunk's dZ codes
     const int64_t rows = M - c0 < C ? M - c0 : C;
     // Z = Xq_k . Wq^T (NT; bf16, leading dimension Vp)
     GemmArgs g = gemm_args(xq + c0 * K, K, FP8MLP_E4M3, &sc[0], wq, K, FP8MLP_E4M3, &sc[1], rows, V, K, kEpiStore);
@@ -588,13 +595,14 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
       return FP8MLP_EHIP;
     QuantBatch bz{};  // dZ codes with this chunk's own scale (row partials)
     bz.njobs = 1;
-    bz.job[0] = make_job(zb, rows, V, Vp, FP8MLP_E5M2, dzq, Vp, nullptr, 0, &sc[2 + k], nullptr, pz, (int)rows,
+    bz.job[0] = make_job(zb, rows, V, Vp, FP8MLP_E5M2, dzk, Vp, nullptr, 0, &sc[2 + k], nullptr, pz, (int)rows,
                          kModePlain);
     if (launch_cast(bz, s) != hipSuccess) return FP8MLP_EHIP;
     // dX_k = dZq_k . Wq (NN, reduction over the V classes' rows of the vocabulary)
-    GemmArgs gd = gemm_args(dzq, Vp, FP8MLP_E5M2, &sc[2 + k], wq, K, FP8MLP_E4M3, &sc[1], rows, K, V, kEpiStore);
+    GemmArgs gd = gemm_args(dzk, Vp, FP8MLP_E5M2, &sc[2 + k], wq, K, FP8MLP_E4M3, &sc[1], rows, K, V, kEpiStore);
     gd.layout = kLayNN; gd.c = dx + c0 * K; gd.ldc = K; gd.accum = accum;
     if (launch_gemm(gd, s) != hipSuccess) return FP8MLP_EHIP;
+    if (seg2) continue;
     // dW (+)= RN32(s_k sx) dZq_k^T . Xq_k (TN, reduction over the chunk's rows)
     GemmArgs gw = gemm_args(dzq, Vp, FP8MLP_E5M2, &sc[2 + k], xq + c0 * K, K, FP8MLP_E4M3, &sc[0], V, K, rows,
                             kEpiStore);
@@ -604,6 +612,14 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
     const bool last = c0 + C >= M;
     gw.epi = !last ? (k == 0 ? kEpiStoreF32 : kEpiAccF32) : (k == 0 ? kEpiStore : kEpiAccF32Bf16);
     if (last) gw.c = dw;
+    if (launch_gemm(gw, s) != hipSuccess) return FP8MLP_EHIP;
+  }
+
+  if (seg2) {
+    GemmArgs gw = gemm_args(reinterpret_cast<const uint8_t*>(dwf), Vp, FP8MLP_E5M2, &sc[2], xq, K, FP8MLP_E4M3,
+                            &sc[0], V, K, M, kEpiStore2);
+    gw.layout = kLayTN; gw.a_2 = dzq; gw.b_2 = xq + C * K; gw.sa_2 = &sc[3]; gw.sb_2 = &sc[0];
+    gw.c = dw; gw.ldc = K; gw.accum = accum;
     if (launch_gemm(gw, s) != hipSuccess) return FP8MLP_EHIP;
   }
 

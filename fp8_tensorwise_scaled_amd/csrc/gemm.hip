@@ -64,7 +64,19 @@ hipError_t launch_sym_gemm(const uint16_t* a, int64_t lda, int64_t M, int64_t K,
   return launch_sym_reduce(partials, g.ksplit, M * M, M, alpha, beta, aux, ldaux, c, ldc, st);
 }
 
+// Two-segment sums: each segment a whole number of 128-deep stages, and the
+// descriptor ranges of both operands ending on dword boundaries (the kernel
+// patches the bytes of a straddling dword only at the last stage of the
+// whole reduction).  MN-major operands end at their last row's M (N)
+// extent, K-major ones at their rows' K/2.
+bool seg2_ok(const GemmArgs& g) {
+  if (g.K % 256 != 0 || g.lda % 4 != 0 || g.ldb % 4 != 0) return false;
+  const bool amn = g.layout == kLayTN, bmn = g.layout == kLayNN || g.layout == kLayTN;
+  return (!amn || g.M % 4 == 0) && (!bmn || g.N % 4 == 0) && g.a_2 && g.b_2 && g.sa_2 && g.sb_2;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+  if (g.epi == kEpiStore2 && (!seg2_ok(g) || (g.layout != kLayNN && g.layout != kLayTN))) return hipErrorInvalidValue;
   if (g.fa == kBF16 || g.fb == kBF16) {
     if (g.fa != g.fb || g.layout != kLayNT) return hipErrorInvalidValue;
     return launch_bf16(g, st);

@@ -192,7 +192,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   // kEpiStore2: two segments of K/2 (a multiple of kBK), each with its own
   // operands; descriptors span one segment
   constexpr bool kSeg2 = EPI == kEpiStore2;
-  static_assert(!kSeg2 || (LAY == 2 && FA != kBF16), "two-segment products: NN FP8 only");
+  // (the last stage of each segment needs no byte patch: the caller keeps
+  // both operands' descriptor ends dword-aligned)
+  static_assert(!kSeg2 || ((LAY == 2 || LAY == 3) && FA != kBF16), "two-segment products: NN or TN FP8 only");
   if constexpr (kSeg2) kelems = g.K / 2;
   const int K = (int)kelems * ES;
   const int nseg1 = kSeg2 ? K / kBK : 0;  // stages of the first segment
@@ -947,8 +949,8 @@ inline int pick_tile(int64_t M, int64_t N) {
 // plain store exist for the format pairs and layouts that use them: the
 // relu^2 block's forward (E4M3 x E4M3, NT) and backward (E5M2 x E4M3, NT or
 // NN), the gated block's projection (E4M3 x E4M3, NT) and backward (E5M2 x
-// E4M3, NN), and the fp32 store and accumulate epilogues of summed gradient
-// products (E5M2 x E4M3).
+// E4M3, NN), and the summed gradient products (E5M2 x E4M3): fp32 store and
+// accumulate epilogues, and two-segment sums (NN, TN).
 template <int LAY, int ACC, int FA, int FB, int BM, int BN, int WGM, int WGN>
 hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
   switch (g.epi) {
@@ -966,7 +968,7 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
         return launch_cfg<FA, FB, 256, 256, 2, 2, kEpiSwiGLU, LAY, ACC>(g, st);
       break;
     case kEpiStore2:  // not on 4-wave 256x256 tiles, whose registers hold no second descriptor set
-      if constexpr (LAY == 2 && FA == kE5M2 && FB == kE4M3 && !(BM == 256 && BN == 256))
+      if constexpr ((LAY == 2 || LAY == 3) && FA == kE5M2 && FB == kE4M3 && !(BM == 256 && BN == 256))
         return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiStore2, LAY, ACC>(g, st);
       break;
     case kEpiSwiGLUBwd:

@@ -75,7 +75,8 @@ enum Epilogue : int {
                       // partial[tile] = max |A| (bf16 bits) when partials is set
   kEpiStore2 = 9,     // two reduction segments (a, b then a_2, b_2, each K/2 long):
                       // C = RN_bf16(p2 (acc_2 + RN32(p1 / p2) acc_1)),
-                      // p1 = RN32(sa sb), p2 = RN32(sa_2 sb_2)  (NN only)
+                      // p1 = RN32(sa sb), p2 = RN32(sa_2 sb_2)  (NN or TN; K/2 a
+                      // multiple of 128 and dword-aligned operand ends)
   kEpiSwiGLUBwd = 8,  // gated MLP backward: dA = RN_bf16(p * acc) (not stored), with G
                       // (aux) and U (aux2): dG = RN_bf16(dA U silu'(G)) -> c,
                       // dU = RN_bf16(dA silu(G)) -> c2 (ldc); partial[tile] =

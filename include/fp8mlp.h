@@ -342,6 +342,11 @@ int fp8_gated_linear_fwd(const uint8_t* xq, int64_t ldx, const float* sx, const 
 /*   dX_k = RN_bf16(RN32(s_k*sw) dZq . Wq)         grad-input (bf16)         */
 /*   dW  += RN32(s_k*sx) dZq^T . Xq_k              fp32, rounded once at end  */
 /* with Xq, sx and Wq, sw the E4M3 tensorwise quantisations of X and W.      */
+/* Two equal chunks (M == 2 chunk, chunk a multiple of 128, V a multiple of  */
+/* 4, chunk x Vp bytes within the fp32 region) take dW in one product over   */
+/* both chunks instead, with p_k = RN32(s_k*sx) and S_k the chunk's fp32     */
+/* sum: dW = RN_bf16(p_2 (S_2 + RN32(p_1/p_2) S_1)); the first chunk's codes */
+/* then sit at the start of the fp32 region.                                 */
 /* Rows whose target lies outside [0, n_classes) are ignored; n_valid counts */
 /* the others; loss = sum of row losses / n_valid (0 when n_valid == 0).     */
 /* The softmax, tanh and exp run in fp32; sums in a fixed order, so results  */
@@ -354,8 +359,9 @@ int fp8_gated_linear_fwd(const uint8_t* xq, int64_t ldx, const float* sx, const 
 size_t fp8_lm_head_ce_workspace_bytes(int64_t M, int64_t K, int64_t V, int64_t chunk);
 
 /* Byte offsets (n >= 11) of the workspace regions, in this order: Xq [M,K],
- * Wq [V,K], logits/dZ of the last chunk (bf16 [chunk,Vp]), dZ codes
- * [chunk,Vp], dW fp32 [V,K], row losses [M] fp32, amax partials of X and W,
+ * Wq [V,K], logits/dZ of the last chunk (bf16 [chunk,Vp]), dZ codes of the
+ * last chunk [chunk,Vp], dW fp32 [V,K] (with two equal chunks: the first
+ * chunk's dZ codes), row losses [M] fp32, amax partials of X and W,
  * row partials, the valid-row count, scales; Vp = V rounded up to 16. */
 int fp8_lm_head_ce_workspace_layout(int64_t M, int64_t K, int64_t V, int64_t chunk, size_t* offsets, int n);
 

@@ -18,7 +18,8 @@ import torch
 
 import oracle
 from fp8_tensorwise_scaled_amd import synth
-from tests.gpu_util import bf16_bits, bits_f64, f32, gemm_bound, gemm_close, oracle_gemm, to_dev_bf16, ulp_bf16
+from tests.gpu_util import (abs_codes, bf16_bits, bits_f64, f32, gemm_bound, gemm_close, oracle_gemm, to_dev_bf16,
+                            ulp_bf16)
 from tests.mlp_chain import chain_close
 
 pytestmark = pytest.mark.gpu
@@ -310,3 +311,39 @@ def test_single_chunk_gradients_on_own_codes(accum):
     gemm_close(g["dx"], ref, "dX (one chunk)", sabs_bits=sab, K=K, accum=accum)
     ref, sab, K = oracle_gemm("tn", dzq, E5, sk, xq, E4, sx)
     gemm_close(g["dw"], ref, "dW (one chunk)", sabs_bits=sab, K=K, accum=accum)
+
+
+@pytest.mark.parametrize("accum", [0, 1], ids=["fast", "exact"])
+def test_two_chunks_grad_weight_on_own_codes(accum):
+    """Two equal chunks of 128 rows (V a multiple of 4): dW is one
+    two-segment product, RN_bf16(p_2 (S_2 + RN32(p_1 / p_2) S_1)), the first
+    chunk's dZ codes kept where the fp32 sum would otherwise go.  dW against
+    the oracle's exact sum of both chunks' products on the GPU's own codes
+    and scales, in the accumulation mode (exact: the benchmark spec's bar); the bound
+    counts 2C + 128 reduction steps (the rescale adds two roundings)."""
+    wl = synth.LMHeadCEWorkload(69, 256, 96, 600, n_classes=590, chunk=128, sigma_w=0.25, ignored=0.05)
+    x, w, t = wl.tensors()
+    g = run(x, w, t, wl.n_classes, wl.chunk, accum=accum)
+    from fp8_tensorwise_scaled_amd import api
+
+    M, K, V, C = 256, 96, 600, 128
+    Vp = pad16(V)
+    offs = api.lm_head_ce_layout(M, K, V, C)
+    wsn = g["ws"].cpu().numpy()
+    dzq = [wsn[offs[4]:offs[4] + C * Vp].reshape(C, Vp)[:, :V], g["dzq_last"]]
+    xq, sx, _ = oracle.quant(x, E4)
+    assert (g["xq"] == xq).all()
+    for k in range(2):
+        assert (dzq[k][:, wl.n_classes:] == 0).all()
+    acc, acc_abs = np.zeros((V, K)), np.zeros((V, K))
+    for k in range(2):
+        sk = float(g["sc"][2 + k])
+        oracle.gemm_tn_acc(np.ascontiguousarray(dzq[k]), E5, sk, xq[k * C:(k + 1) * C], E4, sx, acc)
+        oracle.gemm_tn_acc(abs_codes(np.ascontiguousarray(dzq[k])), E5, sk, abs_codes(xq[k * C:(k + 1) * C]), E4, sx,
+                           acc_abs)
+    gemm_close(g["dw"], oracle.double_to_bf16(acc), "dW (two chunks, one launch)",
+               sabs_bits=oracle.double_to_bf16(acc_abs), K=2 * C + 128, accum=accum)
+    # dX of the first chunk read its codes from the same place
+    ref, sab, KK = oracle_gemm("nn", np.ascontiguousarray(dzq[0]), E5, float(g["sc"][2]), g["wq"], E4,
+                               float(g["sc"][1]))
+    gemm_close(g["dx"][:C], ref, "dX (first chunk)", sabs_bits=sab, K=KK, accum=accum)
