@@ -53,13 +53,16 @@
 //    XCD's L2.
 //  * Epilogues (enum Epilogue in internal.h): plain bf16 store; the relu^2
 //    block's relu^2-max and relu^2-backward fusions, whose tile maxima are
-//    taken on fp32 values before the (monotone) bf16 rounding; fp32 store and
-//    accumulate, and accumulate-then-round-to-bf16 for the last of several
-//    summed products; the gated block's merged gate/up projection with the
-//    gate applied, and its grad-input with the gate's derivative applied
-//    (dG and dU leave the kernel, dA is never stored); and, for bf16
-//    operands, alpha/beta with an optional transposed store and the
-//    upper-triangle split-K mode.
+//    taken on fp32 values before the (monotone) bf16 rounding, the backward
+//    one with H prefetched into the stage registers during the main loop's
+//    last two iterations; fp32 store and accumulate, and
+//    accumulate-then-round-to-bf16 for the last of several summed products;
+//    two reduction segments with their own operands and scales, the first
+//    segment's sum rescaled at the boundary, for a sum of two products (NN,
+//    TN); the gated block's merged gate/up projection with the gate applied,
+//    and its grad-input with the gate's derivative applied (dG and dU leave
+//    the kernel, dA is never stored); and, for bf16 operands, alpha/beta
+//    with an optional transposed store and the upper-triangle split-K mode.
 #pragma once
 #include <type_traits>
 
