@@ -737,16 +737,13 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
                       amax_parts_for(M, d), kModePlain);
   if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 2. dW_down = Gq^T . Aq (TN)
-  GemmArgs gw = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->aq, h, FP8MLP_E4M3, &sc[4], d, h, M, kEpiStore);
-  gw.layout = kLayTN; gw.c = dw_down; gw.ldc = h; gw.accum = accum;
-  // 3. dA = Gq . Wd (NN), and in its epilogue 4. dG, dU with their tile maxima
+  // 2. dA = Gq . Wd (NN), and in its epilogue 3. dG, dU with their tile maxima
   GemmArgs ga = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->wdq, h, FP8MLP_E4M3, &sc[3], M, h, d, kEpiSwiGLUBwd);
   ga.layout = kLayNN; ga.aux = sv->g; ga.aux2 = sv->u; ga.ldaux = h; ga.c = dg; ga.c2 = du; ga.ldc = h;
   ga.partials = pdg; ga.partials2 = pdu; ga.accum = accum;
-  if (launch_gemm(gw, s) != hipSuccess || launch_gemm(ga, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_gemm(ga, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 5. the E5M2 codes of dG and dU (one cast launch)
+  // 4. the E5M2 codes of dG and dU (one cast launch)
   const int ptiles = (int)gemm_num_tiles(M, h);
   QuantBatch bg{};
   bg.njobs = 2;
@@ -754,14 +751,18 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   bg.job[1] = make_job(du, M, h, h, FP8MLP_E5M2, duq, h, nullptr, 0, &bsc[2], nullptr, pdu, ptiles, kModePlain);
   if (launch_cast(bg, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 6. dW_gate = dGq^T . Xq, dW_up = dUq^T . Xq (TN)
-  GemmArgs gg = gemm_args(dgq, h, FP8MLP_E5M2, &bsc[1], sv->xq, d, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
-  gg.layout = kLayTN; gg.c = dw_gate; gg.ldc = d; gg.accum = accum;
-  GemmArgs gu = gemm_args(duq, h, FP8MLP_E5M2, &bsc[2], sv->xq, d, FP8MLP_E4M3, &sc[0], h, d, M, kEpiStore);
-  gu.layout = kLayTN; gu.c = dw_up; gu.ldc = d; gu.accum = accum;
-  if (launch_gemm(gg, s) != hipSuccess || launch_gemm(gu, s) != hipSuccess) return FP8MLP_EHIP;
+  // 5. the three grad-weights in one launch, so that their tiles fill the
+  // CUs together (TN, reduction over the M tokens):
+  //    dW_down = Gq^T . Aq, dW_gate = dGq^T . Xq, dW_up = dUq^T . Xq
+  GemmArgs gw = gemm_args(nullptr, 0, FP8MLP_E5M2, nullptr, nullptr, 0, FP8MLP_E4M3, nullptr, 0, 0, M,
+                          kEpiStoreGroup);
+  gw.layout = kLayTN; gw.accum = accum; gw.ngroup = 3;
+  gw.grp[0] = GemmProblem{gq, sv->aq, &bsc[0], &sc[4], dw_down, d, h, h, d, h};
+  gw.grp[1] = GemmProblem{dgq, sv->xq, &bsc[1], &sc[0], dw_gate, h, d, d, h, d};
+  gw.grp[2] = GemmProblem{duq, sv->xq, &bsc[2], &sc[0], dw_up, h, d, d, h, d};
+  if (launch_gemm(gw, s) != hipSuccess) return FP8MLP_EHIP;
 
-  // 7. dX = dGq . Wg + dUq . Wu (NN), summed in fp32 and rounded once: one
+  // 6. dX = dGq . Wg + dUq . Wu (NN), summed in fp32 and rounded once: one
   // launch over both products when h is a whole number of 128-deep stages,
   // else the first product stored in fp32 and the second added to it
   if (h % 128 == 0) {

@@ -77,6 +77,13 @@ bool seg2_ok(const GemmArgs& g) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.epi == kEpiStore2 && (!seg2_ok(g) || (g.layout != kLayNN && g.layout != kLayTN))) return hipErrorInvalidValue;
+  if (g.epi == kEpiStoreGroup) {  // one to three TN problems over the same K, E5M2 x E4M3
+    if (g.layout != kLayTN || g.ngroup < 1 || g.ngroup > 3 || g.fa != kE5M2 || g.fb != kE4M3) return hipErrorInvalidValue;
+    for (int p = 0; p < g.ngroup; ++p) {
+      const GemmProblem& q = g.grp[p];
+      if (q.M < 0 || q.N < 0 || !q.sa || !q.sb || (q.M > 0 && q.N > 0 && (!q.c || q.ldc < q.N))) return hipErrorInvalidValue;
+    }
+  }
   if (g.fa == kBF16 || g.fb == kBF16) {
     if (g.fa != g.fb || g.layout != kLayNT) return hipErrorInvalidValue;
     return launch_bf16(g, st);

@@ -59,10 +59,12 @@
 //    accumulate-then-round-to-bf16 for the last of several summed products;
 //    two reduction segments with their own operands and scales, the first
 //    segment's sum rescaled at the boundary, for a sum of two products (NN,
-//    TN); the gated block's merged gate/up projection with the gate applied,
-//    and its grad-input with the gate's derivative applied (dG and dU leave
-//    the kernel, dA is never stored); and, for bf16 operands, alpha/beta
-//    with an optional transposed store and the upper-triangle split-K mode.
+//    TN); up to three TN products with a shared reduction in one grouped
+//    launch, so that their tiles fill the CUs together; the gated block's
+//    merged gate/up projection with the gate applied, and its grad-input
+//    with the gate's derivative applied (dG and dU leave the kernel, dA is
+//    never stored); and, for bf16 operands, alpha/beta with an optional
+//    transposed store and the upper-triangle split-K mode.
 #pragma once
 #include <type_traits>
 
@@ -159,6 +161,24 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
   const int bid = blockIdx.x;
   const int xcd = bid & 7, idx = bid >> 3, per = nt >> 3, rem = nt & 7;
   const int t = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  // kEpiStoreGroup: this tile's problem replaces the operands, scales,
+  // output and shape (selected with constant indices, so the arguments stay
+  // in scalar registers), and its tile id and grid are the problem's own
+  int tt = t, tms = tiles_m, tns = tiles_n;
+  if constexpr (EPI == kEpiStoreGroup) {
+    static_assert(LAY == 3 && FA != kBF16, "grouped products: TN FP8 only");
+    const int p = (g.ngroup > 2 && t >= g.grp_first[2]) ? 2 : ((g.ngroup > 1 && t >= g.grp_first[1]) ? 1 : 0);
+    auto take = [&](const GemmProblem& q) {
+      g.a = q.a; g.b = q.b; g.sa = q.sa; g.sb = q.sb; g.c = q.c;
+      g.lda = q.lda; g.ldb = q.ldb; g.ldc = q.ldc; g.M = q.M; g.N = q.N;
+    };
+    if (p == 2) take(g.grp[2]);
+    else if (p == 1) take(g.grp[1]);
+    else take(g.grp[0]);
+    tt = t - (p == 2 ? g.grp_first[2] : (p == 1 ? g.grp_first[1] : 0));
+    tms = (int)((g.M + BM - 1) / BM);
+    tns = (int)((g.N + BN - 1) / BN);
+  }
   int tm, tn;
   int64_t kbeg = 0, kelems = g.K;
   float* cfp = g.cf;
@@ -175,11 +195,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, BM == 128 ? 2 : 1) gemm_kernel
     cfp = g.cf + ks * g.split_stride;
   } else {
     constexpr int kGM = kGroupM * 256 / BM;  // tile rows per group: 1024 output rows
-    const int in_group = kGM * tiles_n;
-    const int first_m = (t / in_group) * kGM;
-    const int gm = min(kGM, tiles_m - first_m);
-    tm = first_m + (t % in_group) % gm;
-    tn = (t % in_group) / gm;
+    const int in_group = kGM * tns;
+    const int first_m = (tt / in_group) * kGM;
+    const int gm = min(kGM, tms - first_m);
+    tm = first_m + (tt % in_group) % gm;
+    tn = (tt % in_group) / gm;
   }
   // kEpiSwiGLU: a tile's BN B rows are BN/2 rows of the gate weights and the
   // same BN/2 rows of the up weights, so it covers BN/2 output columns
@@ -925,6 +945,23 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// A grouped launch: the problems' tiles one after another, grp_first set
+// here; every problem reduces over the same K.
+template <int FA, int FB, int BM, int BN, int WGM, int WGN, int LAY, int ACC>
+hipError_t launch_group(const GemmArgs& g0, hipStream_t st) {
+  GemmArgs g = g0;
+  int total = 0;
+  for (int p = 0; p < g.ngroup; ++p) {
+    g.grp_first[p] = total;
+    total += (int)(((g.grp[p].M + BM - 1) / BM) * ((g.grp[p].N + BN - 1) / BN));
+  }
+  g.grp_first[g.ngroup] = total;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_kernel<FA, FB, BM, BN, WGM, WGN, kEpiStoreGroup, LAY, ACC>), dim3(total),
+                     dim3(64 * WGM * WGN), 0, st, g, 0, 0);
+  return hipGetLastError();
+}
+
 // Block tile width: 256x192 tiles when they fill the 256 CUs in whole waves
 // better than 256x256 (e.g. an 8192x3072 output is 384 tiles of 256x256 =
 // 1.5 waves, but 512 tiles of 256x192 = 2 waves).
@@ -978,6 +1015,10 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
       if constexpr (LAY == 2 && FA == kE5M2 && FB == kE4M3)
         return launch_cfg<FA, FB, BM, BN, WGM, WGN, kEpiSwiGLUBwd, LAY, ACC>(g, st);
       break;
+    case kEpiStoreGroup:
+      if constexpr (LAY == 3 && FA == kE5M2 && FB == kE4M3 && BM == 256)
+        return launch_group<FA, FB, BM, BN, WGM, WGN, LAY, ACC>(g, st);
+      break;
     case kEpiStoreF32:
     case kEpiAccF32:
     case kEpiAccF32Bf16:
@@ -998,6 +1039,20 @@ hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
   // 256x256 tiles 4 waves (2x2, 128x128 wave tiles); 128x128 tiles 4 waves
   // (2x2, 64x64 wave tiles), two blocks per CU
   if (g.epi == kEpiSwiGLU) return launch_bn<LAY, ACC, FA, FB, 256, 256, 2, 2>(g, st);
+  if (g.epi == kEpiStoreGroup) {
+    // the tile width that fills whole waves best over all the problems' tiles
+    auto eff = [&](int bn) {
+      int64_t t = 0, work = 0;
+      for (int p = 0; p < g.ngroup; ++p) {
+        t += ((g.grp[p].M + 255) / 256) * ((g.grp[p].N + bn - 1) / bn);
+        work += g.grp[p].M * g.grp[p].N;
+      }
+      const int64_t waves = (t + 255) / 256;
+      return waves > 0 ? (double)work / (double)(waves * 256 * 256 * bn) : 1.0;
+    };
+    if (eff(192) > eff(256) * 1.02) return launch_bn<LAY, ACC, FA, FB, 256, 192, 4, 2>(g, st);
+    return launch_bn<LAY, ACC, FA, FB, 256, 256, 2, 2>(g, st);
+  }
   switch (pick_tile(g.M, g.N)) {
     case 128: return launch_bn<LAY, ACC, FA, FB, 128, 128, 2, 2>(g, st);
     case 192: return launch_bn<LAY, ACC, FA, FB, 256, 192, 4, 2>(g, st);

@@ -77,6 +77,10 @@ enum Epilogue : int {
                       // C = RN_bf16(p2 (acc_2 + RN32(p1 / p2) acc_1)),
                       // p1 = RN32(sa sb), p2 = RN32(sa_2 sb_2)  (NN or TN; K/2 a
                       // multiple of 128 and dword-aligned operand ends)
+  kEpiStoreGroup = 10,  // plain bf16 store of up to three TN products in one launch
+                        // (grp[0..ngroup), each with its own operands, scales, output
+                        // and shape; the reduction length K shared): the launch's tile
+                        // t belongs to the problem p with grp_first[p] <= t < grp_first[p+1]
   kEpiSwiGLUBwd = 8,  // gated MLP backward: dA = RN_bf16(p * acc) (not stored), with G
                       // (aux) and U (aux2): dG = RN_bf16(dA U silu'(G)) -> c,
                       // dU = RN_bf16(dA silu(G)) -> c2 (ldc); partial[tile] =
@@ -95,6 +99,16 @@ enum GemmLayout : int {
 enum GemmAccum : int {
   kAccFast = 0,   // FP8 matrix cores (group-truncated sums)
   kAccExact = 1,  // codes decoded to bf16, exact products on the bf16 matrix cores
+};
+
+// One problem of a grouped launch (kEpiStoreGroup).
+struct GemmProblem {
+  const uint8_t* a;
+  const uint8_t* b;
+  const float* sa;
+  const float* sb;
+  uint16_t* c;
+  int64_t lda, ldb, ldc, M, N;
 };
 
 struct GemmArgs {
@@ -140,6 +154,10 @@ struct GemmArgs {
   // cf + (w % ksplit) * split_stride with the kEpiStoreF32 epilogue.
   int tri_tiles, ksplit;
   int64_t kchunk, split_stride;
+  // kEpiStoreGroup: the problems and their first tiles (set by the launcher)
+  int ngroup;
+  int grp_first[4];
+  GemmProblem grp[3];
 };
 
 // Number of output tiles the GEMM will use (size of `partials`).

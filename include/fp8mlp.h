@@ -277,7 +277,7 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
 /*     dG = RN_bf16(dA U silu'(G)),  dU = RN_bf16(dA silu(G))  (fp32, in the  */
 /*     epilogue of the dA GEMM; silu'(g) = s (1 + g (1 - s)), s = sigmoid(g)) */
 /*     dGq, dUq = quant(dG), quant(dU)                                       */
-/*     dW_gate = TN(dGq, Xq);  dW_up = TN(dUq, Xq)                           */
+/*     dW_gate = TN(dGq, Xq);  dW_up = TN(dUq, Xq)  (one launch with dW_down) */
 /*     dX = RN_bf16(RN32(RN32(p_g NN(dGq,Wgq)) + RN32(p_u NN(dUq,Wuq))))      */
 /*       (h a multiple of 128: one fp32 accumulation of both products,     */
 /*       dX = RN_bf16(p_u (NN(dUq,Wuq) + RN32(p_g / p_u) NN(dGq,Wgq))))       */
