@@ -41,10 +41,10 @@ def ulp_bf16(v: np.ndarray) -> np.ndarray:
 ACC_FAST, ACC_EXACT = 0, 1
 ACCUMS = (ACC_FAST, ACC_EXACT)
 
-# North star's GEMM parity bar: max|gpu - oracle| / max|oracle| <= 5e-3 and at
+# The strict GEMM parity bar: max|gpu - oracle| / max|oracle| <= 5e-3 and at
 # least 99.9% of the elements within one bf16 ulp of the oracle.
-NS_MAX_REL = 5e-3
-NS_WITHIN1 = 0.999
+STRICT_MAX_REL = 5e-3
+STRICT_WITHIN1 = 0.999
 
 # Accuracy of the gfx950 FP8 matrix core (measured on the hardware): the 64
 # products of one v_mfma_f32_32x32x64_f8f6f4 are summed in aligned groups of 8
@@ -90,7 +90,7 @@ def gemm_close(got_bits: np.ndarray, ref_bits: np.ndarray, what: str = "", *, sa
     """GEMM output parity against the oracle on identical FP8 operands.
 
     Both modes: every element within gemm_bound (or an explicit `bound`).
-    Exact mode: also the benchmark spec's bar, max|gpu - oracle| / max|oracle| <= 5e-3
+    Exact mode: also the strict bar, max|gpu - oracle| / max|oracle| <= 5e-3
     and >= 99.9% of the elements within one bf16 ulp.  The fast mode's
     truncating group sums fall short of that bar by design (its element-wise
     bound is what the arithmetic guarantees); its max-relative error and
@@ -109,8 +109,8 @@ def gemm_close(got_bits: np.ndarray, ref_bits: np.ndarray, what: str = "", *, sa
     assert not over.any(), f"{what}: {int(over.sum())} elements beyond the bound, e.g. " + str(
         [(float(g.flat[i]), float(r.flat[i]), float(bound.flat[i])) for i in np.flatnonzero(over)[:4]])
     if accum == ACC_EXACT:
-        assert rel <= NS_MAX_REL, f"{what}: max|gpu - oracle| / max|oracle| = {rel:.3g} > {NS_MAX_REL}"
-        assert within >= NS_WITHIN1, f"{what}: {within:.6f} of the elements within one ulp < {NS_WITHIN1}"
+        assert rel <= STRICT_MAX_REL, f"{what}: max|gpu - oracle| / max|oracle| = {rel:.3g} > {STRICT_MAX_REL}"
+        assert within >= STRICT_WITHIN1, f"{what}: {within:.6f} of the elements within one ulp < {STRICT_WITHIN1}"
     return rel, within
 
 

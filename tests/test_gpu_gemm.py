@@ -3,7 +3,7 @@
 fp8_linear_fwd (NT), fp8_linear_dgrad (NN) and fp8_linear_wgrad (TN) on
 row-major codes, in both accumulation modes.  Inputs are FP8 codes and
 scales produced by the oracle's quantiser, so both sides see identical
-operands.  Exact mode: the benchmark spec's bar (max|gpu - oracle| / max|oracle| <=
+operands.  Exact mode: the strict bar (max|gpu - oracle| / max|oracle| <=
 5e-3, >= 99.9% of the elements within one bf16 ulp) and its accumulation
 bound.  Fast mode: the element-wise bound of the FP8 matrix core's truncating
 group sums (tests/gpu_util.py, gemm_bound).
@@ -476,7 +476,7 @@ def test_subnormal_codes(fa, fb, accum):
 def test_fast_mode_statistics_reported():
     """The fast mode's one-ulp fraction and max-relative error on the 3.8B
     down-projection shape, printed beside the exact mode's for the same
-    operands (the exact mode holds the benchmark spec's bar; the fast mode holds its
+    operands (the exact mode holds the strict bar; the fast mode holds its
     truncation bound, asserted in check_gemm)."""
     from fp8_tensorwise_scaled_amd import api
 

@@ -296,7 +296,7 @@ def test_single_chunk_gradients_on_own_codes(accum):
     """One chunk covering all rows (the grad-weight product is stored
     directly, no fp32 accumulation across chunks): dX and dW against the
     oracle GEMMs of the GPU's own dZ codes and scale, in the accumulation
-    mode (exact: the benchmark spec's bar); an odd vocabulary (V = 333, 323 classes)
+    mode (exact: the strict bar); an odd vocabulary (V = 333, 323 classes)
     so that both reductions over the vocabulary end in a masked tail."""
     wl = synth.LMHeadCEWorkload(68, 96, 80, 333, n_classes=323, chunk=96, sigma_w=0.25, ignored=0.05)
     x, w, t = wl.tensors()
@@ -319,7 +319,7 @@ def test_two_chunks_grad_weight_on_own_codes(accum):
     two-segment product, RN_bf16(p_2 (S_2 + RN32(p_1 / p_2) S_1)), the first
     chunk's dZ codes kept where the fp32 sum would otherwise go.  dW against
     the oracle's exact sum of both chunks' products on the GPU's own codes
-    and scales, in the accumulation mode (exact: the benchmark spec's bar); the bound
+    and scales, in the accumulation mode (exact: the strict bar); the bound
     counts 2C + 128 reduction steps (the rescale adds two roundings)."""
     wl = synth.LMHeadCEWorkload(69, 256, 96, 600, n_classes=590, chunk=128, sigma_w=0.25, ignored=0.05)
     x, w, t = wl.tensors()
