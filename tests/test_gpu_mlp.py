@@ -2,8 +2,8 @@
 both accumulation modes.
 
 Every expected value is the oracle (tests/mlp_chain.py): each GEMM stage
-against the oracle GEMM of the GPU's own FP8 operands (exact mode: north
-star's bar), each cast bit-exact given its own bf16 input and equal to the
+against the oracle GEMM of the GPU's own FP8 operands (exact mode: the
+strict bar), each cast bit-exact given its own bf16 input and equal to the
 oracle chain's codes wherever that input agrees, the end-to-end outputs
 against the oracle chain run from the same bf16 inputs (exact mode:
 max-relative error <= 5e-3)."""

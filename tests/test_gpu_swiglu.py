@@ -2,8 +2,8 @@
 in both accumulation modes.
 
 Every expected value is the oracle (tests/swiglu_chain.py): each GEMM stage
-against the oracle GEMM of the GPU's own FP8 operands (exact mode: north
-star's bar), each cast bit-exact given its own input, the gate within the
+against the oracle GEMM of the GPU's own FP8 operands (exact mode: the
+strict bar), each cast bit-exact given its own input, the gate within the
 bound of its fp32 evaluation, codes equal to the oracle chain's where their
 input agrees, and the outputs against the oracle chain."""
 import numpy as np
@@ -200,3 +200,27 @@ def test_gated_linear_fwd_empty_reduction():
     torch.cuda.synchronize()
     for t in (g, u, a):
         assert (bf16_bits(t) == 0).all()
+
+
+def test_grouped_grad_weights_equal_separate_launches(small):
+    """The block's three grad-weights come out of one grouped launch; each is
+    byte-identical to fp8_linear_wgrad on the same codes and scales (a tile's
+    sums run over the same reduction in the same order whichever launch holds
+    it), so grouping changes no value the oracle checks elsewhere."""
+    from fp8_tensorwise_scaled_amd import api
+
+    accum, g = small
+    dev = torch.device("cuda:0")
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    f1 = lambda v: torch.tensor([float(v)], dtype=torch.float32, device=dev)
+    sx, sa = g["scales"][0], g["scales"][4]
+    for key, codes, s_codes, other, s_other in (("dw_down", g["gq"], g["bsc"][0], g["aq"], sa),
+                                                ("dw_gate", g["dgq"], g["bsc"][1], g["xq"], sx),
+                                                ("dw_up", g["duq"], g["bsc"][2], g["xq"], sx)):
+        sep = api.fp8_linear_wgrad(u8(codes), f1(s_codes), u8(other), f1(s_other), api.E5M2, api.E4M3,
+                                   accum=accum)
+        torch.cuda.synchronize()
+        got = bf16_bits(sep)
+        print(f"{key}: grouped equal to separate on {float((got == g[key]).mean()):.6f}")
+        assert got.shape == g[key].shape, key
+        assert (got == g[key]).all(), key
