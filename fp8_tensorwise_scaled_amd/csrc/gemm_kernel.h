@@ -26,7 +26,9 @@
 //    tile (4x4 MFMA tiles, 256 accumulator registers: LDS traffic per MFMA
 //    at its lowest).  256x192 tiles run 8 waves in a 4x2 grid of 64x96 wave
 //    tiles, two waves per SIMD, so one wave's LDS and barrier waits overlap
-//    the other's MFMAs.  Small outputs, which 256-row tiles would spread
+//    the other's MFMAs; so do the 256x256 tiles of NT FP8 products with a
+//    plain or relu^2-max epilogue (64x128 wave tiles), the only ones whose
+//    main loop fits the 256 registers of two waves per SIMD.  Small outputs, which 256-row tiles would spread
 //    over too few CUs, take 128x128 tiles: 4 waves of 64x64, two blocks per
 //    CU.
 //  * K is consumed 128 codes per stage; stages are double-buffered in LDS,
@@ -1036,8 +1038,11 @@ hipError_t launch_bn(const GemmArgs& g, hipStream_t st) {
 template <int LAY, int ACC, int FA, int FB>
 hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
   // 256x192 tiles run 8 waves (4x2, 64x96 wave tiles, two waves per SIMD);
-  // 256x256 tiles 4 waves (2x2, 128x128 wave tiles); 128x128 tiles 4 waves
-  // (2x2, 64x64 wave tiles), two blocks per CU
+  // 256x256 tiles 4 waves (2x2, 128x128 wave tiles), except the NT FP8
+  // plain-store and relu^2-max products, which run 8 waves (4x2, 64x128 wave
+  // tiles: their main loop fits 256 registers with both operands K-major;
+  // with an MN-major operand, exact products or the other epilogues it
+  // spills); 128x128 tiles 4 waves (2x2, 64x64 wave tiles), two blocks per CU
   if (g.epi == kEpiSwiGLU) return launch_bn<LAY, ACC, FA, FB, 256, 256, 2, 2>(g, st);
   if (g.epi == kEpiStoreGroup) {
     // the tile width that fills whole waves best over all the problems' tiles
@@ -1058,6 +1063,12 @@ hipError_t launch_fmt(const GemmArgs& g, hipStream_t st) {
     case 192: return launch_bn<LAY, ACC, FA, FB, 256, 192, 4, 2>(g, st);
     default:
       if (g.epi == kEpiStore2) return launch_bn<LAY, ACC, FA, FB, 256, 192, 4, 2>(g, st);
+      if constexpr (LAY == 0 && ACC == 0 && FA != kBF16) {
+        if (g.epi == kEpiStore) return launch_cfg<FA, FB, 256, 256, 4, 2, kEpiStore, LAY, ACC>(g, st);
+        if constexpr (FA == kE4M3 && FB == kE4M3) {
+          if (g.epi == kEpiRelu2Max) return launch_cfg<FA, FB, 256, 256, 4, 2, kEpiRelu2Max, LAY, ACC>(g, st);
+        }
+      }
       return launch_bn<LAY, ACC, FA, FB, 256, 256, 2, 2>(g, st);
   }
 }

@@ -118,6 +118,25 @@ def test_tile_threshold_shapes(accum, kind):
         check_gemm(got, kind, qa, E5, sa, qb, E4, sb, f"threshold {kind} {M}x{N}x{R}", rows=rows, accum=accum)
 
 
+@pytest.mark.parametrize("accum", ACCUMS)
+@pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4)])
+def test_nt_wide_tiles_ragged(accum, fa, fb):
+    """NT products that take 256x256 tiles (fast mode: 8 waves of 64x128;
+    exact mode: 4 waves of 128x128): 2087 x 6199 is 9 x 25 = 225 such tiles,
+    one wave over the CUs, ragged in M (39 rows) and N (55 columns), with a
+    reduction of 390 (not a multiple of 16) and 2096 x 6208 x 3072 with whole
+    16-byte chunks.  Checked on sampled output rows, the first and the last
+    included."""
+    rng = np.random.default_rng(77 + fa + 2 * fb + 10 * accum)
+    for M, N, R in ((2087, 6199, 390), (2096, 6208, 3072)):
+        qa, sa, qb, sb = operands("nt", M, N, R, fa, fb, 8300 + M + R)
+        y = run("nt", padded(qa), fa, sa, padded(qb), fb, sb, accum)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 22, replace=False)]))
+        check_gemm(bf16_bits(y)[rows], "nt", qa, fa, sa, qb, fb, sb, f"wide tiles nt {M}x{N}x{R} fmt {fa}{fb}",
+                   rows=rows, accum=accum)
+
+
 @pytest.mark.parametrize("kind", LAYOUTS)
 def test_exactly_representable_sums(kind):
     """Codes of magnitude in [1, 4) with unit scales: every product is a
