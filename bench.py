@@ -165,6 +165,12 @@ def hbm_practical(dev, nbytes=1 << 30, reps=10):
     return out
 
 
+def _nt_waves(accum: int) -> str:
+    """Wave grid of a 256x256 NT FP8 tile: 4x2 waves on the FP8 matrix cores,
+    2x2 for exact products."""
+    return "4,2" if accum == 0 else "2,2"
+
+
 def _roofline(kernel: str, bound: str, work: float, us: float, peak: float, unit: str, traffic=None, **extra):
     """Roofline object for one kernel: algorithmic work per launch / its
     average launch time (HIP events on the launching stream)."""
@@ -547,7 +553,7 @@ def bench_other(args) -> int:
                 us = _after_steps(lambda: r.step(X, W, G),
                                   {"g": lambda: api.fp8_linear_fwd(r.xq.q, r.xq.scale, r.wq.q, r.wq.scale, out=r.y,
                                                                    accum=args.accum)}, args.gemm_reps)["g"]
-                roof = _roofline(f"gemm_kernel<0,0,256,256,2,2,0,0,{args.accum}> (E4M3 x E4M3, NT logits "
+                roof = _roofline(f"gemm_kernel<0,0,256,256,{_nt_waves(args.accum)},0,0,{args.accum}> (E4M3 x E4M3, NT logits "
                                  f"[{w.M},{w.N}], K={w.K})", "mfma", 2 * w.M * w.N * w.K, us, PEAK_FP8_TFLOPS,
                                  "TFLOP/s")
             del W, G, r
@@ -764,7 +770,7 @@ def bench_other(args) -> int:
         sc = out["scales"]
         us = _after_steps(step, {"g": lambda: api.fp8_linear_fwd(xq, sc[0:1], wq, sc[1:2], out=zbuf,
                                                                  accum=args.accum)}, args.gemm_reps)["g"]
-        roof = _roofline(f"gemm_kernel<0,0,256,256,2,2,0,0,{args.accum}> (E4M3 x E4M3; logits of one chunk, "
+        roof = _roofline(f"gemm_kernel<0,0,256,256,{_nt_waves(args.accum)},0,0,{args.accum}> (E4M3 x E4M3; logits of one chunk, "
                          f"M={w.chunk} N={w.V} K={w.K})", "mfma", 2 * w.chunk * w.V * w.K, us, PEAK_FP8_TFLOPS,
                          "TFLOP/s")
         log(f"chunk logits GEMM: {us:.1f} us, {roof['achieved']:.1f} TFLOP/s")
