@@ -119,7 +119,7 @@ def test_tile_threshold_shapes(accum, kind):
 
 
 @pytest.mark.parametrize("accum", ACCUMS)
-@pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4)])
+@pytest.mark.parametrize("fa,fb", FORMATS)
 def test_nt_wide_tiles_ragged(accum, fa, fb):
     """NT products that take 256x256 tiles (fast mode: 8 waves of 64x128;
     exact mode: 4 waves of 128x128): 2087 x 6199 is 9 x 25 = 225 such tiles,
