@@ -138,14 +138,17 @@ class LMHeadRunner:
     """LM head fwd+bwd for vocabulary N (padded or not).
 
     The unpadded vocabulary's codes of dLogits get a leading dimension
-    rounded up to 16 (the GEMMs read 16-byte rows); the grad-input GEMM
-    reduces over exactly N of them, the kernel masking the tail."""
+    rounded up to 128, so that every row starts on a 128-byte line as the
+    padded vocabulary's rows do (the grad-input GEMM reads each row 128
+    bytes per stage; rows on a 16-byte multiple only would straddle two
+    lines per read); the grad-input GEMM reduces over exactly N of them,
+    the kernel masking the tail."""
 
     def __init__(self, M, K, N, device, accum=api.ACCUM_FAST):
         self.M, self.K, self.N, self.accum = M, K, N, accum
         self.xq = QuantOut.alloc(M, K, device)
         self.wq = QuantOut.alloc(N, K, device)
-        self.gq = QuantOut.alloc(M, N, device, ld_multiple=16)
+        self.gq = QuantOut.alloc(M, N, device, ld_multiple=128)
         self.y = _bf16((M, N), device)
         self.dx = _bf16((M, K), device)
         self.dw = _bf16((N, K), device)
