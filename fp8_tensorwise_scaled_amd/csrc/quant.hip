@@ -203,9 +203,11 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
       make_rsrc(reinterpret_cast<const void*>(xa - dlt), buf_in ? (uint32_t)((xbytes + 3) & ~int64_t{3}) : 0u);
   const bool vec_q = q == nullptr || (((reinterpret_cast<uintptr_t>(q) & 3u) == 0) && (jb.ldq % 4 == 0));
   const bool vec_qt = qt == nullptr || (aligned16(qt) && (jb.ldqt % 16 == 0));
-  // codes only, 16-byte aligned rows of x, 8-byte aligned rows of q
-  const bool rows_only = qt == nullptr && q != nullptr && aligned16(x) && ldx % 8 == 0 &&
-                         ((reinterpret_cast<uintptr_t>(q) & 7u) == 0) && jb.ldq % 8 == 0;
+  // codes only, 8-byte aligned rows of q; rows of x 16-byte aligned, or
+  // read through the buffer descriptor when they are not (row_buf)
+  const bool q8 = q != nullptr && ((reinterpret_cast<uintptr_t>(q) & 7u) == 0) && jb.ldq % 8 == 0;
+  const bool row_vec = aligned16(x) && ldx % 8 == 0;
+  const bool rows_only = qt == nullptr && q8 && (row_vec || buf_in);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tile_parity = 0;  // LDS image buffer of the next transposed tile
   for (int64_t t = lb; t < ntiles; t += jb.nblocks) {
@@ -225,10 +227,28 @@ __device__ void cast_tiles(const QuantJob& jb, int lb, const Divider& d, uint8_t
       const bool lane_ok = l32 * 8 < wv;
       const int64_t rb = r0 + wave * 16 + half;
       v4u in[8];
+      if (row_vec) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        in[i] = lane_ok ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + (rb + 2 * i) * ldx + cb))
-                        : v4u{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 8; ++i)
+          in[i] = lane_ok ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + (rb + 2 * i) * ldx + cb))
+                          : v4u{0u, 0u, 0u, 0u};
+      } else {
+        // rows not 16-byte aligned: a lane's 16 bytes start on a dword or
+        // mid-dword (by row: with an odd leading dimension the two
+        // half-waves differ), so every lane loads the 16 bytes from the
+        // dword that holds its first byte and the dword after them, and
+        // shifts by its own phase (0 or 2 bytes).  Bytes past the
+        // descriptor's range load as zeros and are not used.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t off = dlt + 2u * (uint32_t)((rb + 2 * i) * ldx + cb);
+          const uint32_t base = off & ~3u, sh = off & 3u;
+          const v4u w = lane_ok ? __builtin_amdgcn_raw_buffer_load_b128(rx, base, 0, 0) : v4u{0u, 0u, 0u, 0u};
+          const uint32_t w4 = lane_ok ? __builtin_amdgcn_raw_buffer_load_b32(rx, base + 16u, 0, 0) : 0u;
+          in[i] = v4u{__builtin_amdgcn_alignbyte(w[1], w[0], sh), __builtin_amdgcn_alignbyte(w[2], w[1], sh),
+                      __builtin_amdgcn_alignbyte(w[3], w[2], sh), __builtin_amdgcn_alignbyte(w4, w[3], sh)};
+        }
+      }
       if (lane_ok) {
         float g[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
         bool has_g = false;

@@ -103,7 +103,15 @@ def test_strided_and_unaligned(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_unaligned_rows_full_tiles(fmt):
     """Rows that are not 8-byte aligned go through the realigning buffer-load
-    path on whole tiles (and the element path on the ragged edge)."""
+    paths on whole tiles (and the element path on the ragged edge): with
+    transposed codes or rows of codes off 8 bytes, 4 columns per lane;
+    codes-only on 8-byte rows of codes, 16 bytes per lane shifted by the
+    row's phase (an odd leading dimension alternates it row by row, base
+    offsets 1-3 move it, 776 columns end in an 8-column tile)."""
+    x = synth.normal_bf16((300, 776), 1.0, 82)
+    for off in (1, 2, 3):
+        check_against_oracle(x, fmt, ld=777, offset=off, qt=False)
+    check_against_oracle(x, fmt, ld=780, offset=1, qt=False)  # even leading dimension, base off a dword
     x = synth.normal_bf16((300, 700), 1.0, 79)
     check_against_oracle(x, fmt, ld=701)             # odd leading dimension
     check_against_oracle(x, fmt, ld=702, offset=1)   # base off a dword boundary
