@@ -337,10 +337,12 @@ def test_empty_sizes():
     assert tuple(y.shape) == (0, 24) and tuple(y2.shape) == (40, 0) and tuple(y3.shape) == (0, 24)
 
 
-@pytest.mark.parametrize("kind", ["nt", "nn"])
+@pytest.mark.parametrize("kind", LAYOUTS)
 def test_output_rows_not_16_byte_aligned(kind):
-    """Odd leading dimension and a base 2 bytes off a dword: every store
-    alignment (2, 4, 8, 16 bytes) occurs among the rows."""
+    """Odd leading dimension and a base 2 bytes off a dword: every row phase
+    (0-14 bytes past a 16-byte boundary) occurs among the rows, so every
+    store width the epilogue picks by alignment (2, 4, 8, 16 bytes) is used;
+    the last column tile is 8 columns wide."""
     M, N, R = 264, 392, 256
     qa, sa, qb, sb = operands(kind, M, N, R, E4, E5, 98)
     ldc = 401
@@ -350,6 +352,26 @@ def test_output_rows_not_16_byte_aligned(kind):
     torch.cuda.synchronize()
     Cb = bf16_bits(C)
     check_gemm(Cb[:, :N], kind, qa, E4, sa, qb, E5, sb, f"odd ldc {kind}")
+    assert (Cb[:, N:] == 7).all() and int(bf16_bits(flat[:1])[0]) == 7   # nothing outside written
+
+
+@pytest.mark.parametrize("accum", ACCUMS)
+def test_wide_tiles_output_rows_not_16_byte_aligned(accum):
+    """The unpadded-vocabulary case on 256x256 NT tiles: 2087 x 6199 outputs
+    (ragged in both directions) into rows 6201 elements apart, 2 bytes past
+    a dword.  Sampled rows against the oracle, the first and last included;
+    no byte outside the output is written."""
+    M, N, R = 2087, 6199, 272
+    qa, sa, qb, sb = operands("nt", M, N, R, E4, E4, 8400 + accum)
+    ldc = 6201
+    flat = torch.full((1 + M * ldc,), 7, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    C = flat[1:].view(M, ldc)
+    run("nt", padded(qa), E4, sa, padded(qb), E4, sb, accum, out=C[:, :N])
+    torch.cuda.synchronize()
+    Cb = bf16_bits(C)
+    rng = np.random.default_rng(91 + accum)
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rng.choice(M, 20, replace=False)]))
+    check_gemm(Cb[rows, :N], "nt", qa, E4, sa, qb, E4, sb, "wide tiles, odd ldc", rows=rows, accum=accum)
     assert (Cb[:, N:] == 7).all() and int(bf16_bits(flat[:1])[0]) == 7   # nothing outside written
 
 
