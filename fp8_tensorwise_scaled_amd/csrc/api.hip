@@ -210,12 +210,14 @@ int check_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
 // The amax pass and the cast of one tensor, with `partials` holding
 // amax_parts_for(rows, cols) u32.
 int run_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q, int64_t ldq,
-                   uint8_t* qt, int64_t ldqt, float* scale, float* amax, uint32_t* partials, void* stream) {
+                   uint8_t* qt, int64_t ldqt, float* scale, float* amax, uint32_t* partials, void* stream,
+                   bool two_launches = false) {
   QuantBatch b{};
   b.njobs = 1;
   b.job[0] = make_job(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, partials, amax_parts_for(rows, cols),
                       kModePlain);
   hipStream_t st = (hipStream_t)stream;
+  if (!two_launches) return hip_status(launch_amax_cast(b, st));
   if (launch_amax_partials(b, st) != hipSuccess) return FP8MLP_EHIP;
   return hip_status(launch_cast(b, st));
 }
@@ -263,7 +265,7 @@ int fp8_amax_quant_noalloc(const uint16_t* x, int64_t rows, int64_t cols, int64_
   if (st) return st;
   // every partial the cast reads is written by this call's amax pass first:
   // nothing in the scratch has to start at zero
-  return run_amax_quant(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, parts, stream);
+  return run_amax_quant(x, rows, cols, ldx, fmt, q, ldq, qt, ldqt, scale, amax, parts, stream, true);
 }
 
 size_t fp8_rmsnorm_quant_workspace_bytes(int64_t rows, int64_t cols) {
@@ -340,7 +342,7 @@ int fp8_linear_fwd_bf16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64
   b.job[1] = make_job(w, N, K, ldw, FP8MLP_E4M3, wq, ldwq, nullptr, 0, &scales[1], nullptr, pw, amax_parts_for(N, K),
                       kModePlain);
   hipStream_t s = (hipStream_t)stream;
-  if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_amax_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
   return run_gemm(kLayNT, xq, ldxq, FP8MLP_E4M3, &scales[0], wq, ldwq, FP8MLP_E4M3, &scales[1], M, N, K, y, ldy,
                   accum, stream);
 }
@@ -436,8 +438,7 @@ int relu2_mlp_fwd(const uint16_t* x, const uint16_t* w_up, const uint16_t* w_dow
                       amax_parts_for(h, d), kModePlain);
   b.job[2] = make_job(w_down, d, h, h, FP8MLP_E4M3, saved->dq, h, nullptr, 0, &sc[2], nullptr, pd,
                       amax_parts_for(d, h), kModePlain);
-  if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
-  if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_amax_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 3. H = Xq . Uq^T (NT) with the relu^2 max epilogue
   GemmArgs g = gemm_args(saved->xq, d, FP8MLP_E4M3, &sc[0], saved->uq, d, FP8MLP_E4M3, &sc[1], M, h, d,
@@ -489,8 +490,7 @@ int relu2_mlp_bwd(const uint16_t* dy, const relu2_mlp_saved* saved, int64_t M, i
   b.njobs = 1;
   b.job[0] = make_job(dy, M, d, d, FP8MLP_E5M2, gq, d, nullptr, 0, &bsc[0], nullptr, pg, amax_parts_for(M, d),
                       kModePlain);
-  if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
-  if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_amax_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 2. dW_down[d,h] = Gq^T . Aq (TN, reduction over the M tokens)
   GemmArgs g = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], saved->aq, h, FP8MLP_E4M3, &sc[3], d, h, M, kEpiStore);
@@ -572,8 +572,7 @@ int fp8_lm_head_ce(const uint16_t* x, const uint16_t* w, const int32_t* targets,
                       kModePlain);
   b.job[1] = make_job(w, V, K, K, FP8MLP_E4M3, wq, K, nullptr, 0, &sc[1], nullptr, pw, amax_parts_for(V, K),
                       kModePlain);
-  if (launch_amax_partials(b, s) != hipSuccess) return FP8MLP_EHIP;
-  if (launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_amax_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 2. chunks of C rows: logits, loss and dZ, dZ codes, grad-input, grad-weight.
   //    Two equal chunks (a multiple of 128 rows, V a multiple of 4, so that
@@ -684,7 +683,7 @@ int swiglu_mlp_fwd(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_
                       (uint32_t*)(w8 + off[SF_PWU]), amax_parts_for(h, d), kModePlain);
   b.job[3] = make_job(w_down, d, h, h, FP8MLP_E4M3, sv->wdq, h, nullptr, 0, &sc[3], nullptr,
                       (uint32_t*)(w8 + off[SF_PWD]), amax_parts_for(d, h), kModePlain);
-  if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_amax_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 2. G, U and A = silu(G) U in one NT GEMM over the gate and up codes, with
   //    the per-tile max |A| partials
@@ -735,7 +734,7 @@ int swiglu_mlp_bwd(const uint16_t* dy, const swiglu_mlp_saved* sv, int64_t M, in
   b.njobs = 1;
   b.job[0] = make_job(dy, M, d, d, FP8MLP_E5M2, gq, d, nullptr, 0, &bsc[0], nullptr, (uint32_t*)(w8 + off[SB_PG]),
                       amax_parts_for(M, d), kModePlain);
-  if (launch_amax_partials(b, s) != hipSuccess || launch_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
+  if (launch_amax_cast(b, s) != hipSuccess) return FP8MLP_EHIP;
 
   // 2. dA = Gq . Wd (NN), and in its epilogue 3. dG, dU with their tile maxima
   GemmArgs ga = gemm_args(gq, d, FP8MLP_E5M2, &bsc[0], sv->wdq, h, FP8MLP_E4M3, &sc[3], M, h, d, kEpiSwiGLUBwd);

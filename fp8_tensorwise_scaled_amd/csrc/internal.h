@@ -45,6 +45,13 @@ int amax_parts_for(int64_t rows, int64_t cols);
 
 // amax partial kernel for every job of the batch (mode plain only).
 hipError_t launch_amax_partials(QuantBatch& b, hipStream_t st);
+// amax and cast of every job of the batch (mode plain): one pass over the
+// data (a one-block clear, then one grid that holds part of the tensors in
+// registers across a grid-wide wait) when every job is dense, 16-byte
+// aligned and codes-only and the stream is not capturing, else
+// launch_amax_partials then launch_cast.  Uses at most each job's nparts
+// partials.
+hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st);
 // RMSNorm statistics and amax partials of one job (mode kModeRmsNorm): writes
 // rstd[row] and one partial per block of rows (rmsnorm_parts_for of them).
 int rmsnorm_parts_for(int64_t rows);

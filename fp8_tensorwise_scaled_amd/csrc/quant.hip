@@ -18,6 +18,18 @@
 //      go straight to HBM and the transposed ones are built by byte permutes
 //      in registers and an LDS image of the tile (allocated only for such a
 //      launch), so both outputs are written in full 128-byte lines.
+//
+// One pass per batch where every tensor is dense, 16-byte aligned and wants
+// codes only (the MLP blocks' inputs, weights and dY): one grid reads each
+// tensor once for its amax, keeping the first 21 chunks of 8 values per
+// thread in registers (about 88 MB over the 256 CUs' register files), waits
+// at one grid-wide barrier, and casts the held chunks without reading them
+// again; only the rest is read a second time.  Same amax, same scale, same
+// element-wise cast: the codes are those of the two launches.
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -591,6 +603,228 @@ __global__ void __launch_bounds__(kCastThreads) cast_kernel(QuantBatch b) {
   cast_tiles<FMT, MODE>(jb, lb, d, tbuf);
 }
 
+// Single-pass amax + cast of dense, codes-only jobs (plain mode).
+//
+// Work units: unit u of a batch is slice `local` = u - blk_begin of its job
+// (nblocks slices per job): the 16-byte chunks local*T + tid + k*nblocks*T.
+// Each unit has one slot word (the job's partials[local], cleared by
+// quant_resident_clear just before): bit 31 arrived, bit 30 held, bit 29
+// claimed, bits 15-28 the block that processes it, bits 0-14 the max |x| as
+// bf16 magnitude bits.  Block u claims unit u with a compare-and-swap on its
+// slot and holds it: the first kResChunks chunks per thread stay in
+// registers.  It publishes the unit's max with one agent-scope atomic store,
+// so no cache-wide fence is needed, and waits until every slot has arrived.
+// A waiting block that finds a unit still unclaimed (its block has not
+// started) claims and processes it itself, without holding it, so the wait
+// ends whether or not all blocks are resident at once.  Then each block
+// casts the chunks it holds from registers and reads again the rest of each
+// unit it processed.
+constexpr int kResThreads = 512;
+constexpr int kResChunks = 21;
+constexpr uint32_t kSlotArrived = 0x80000000u, kSlotHeld = 0x40000000u, kSlotClaimed = 0x20000000u;
+constexpr int kSlotProcShift = 15;
+constexpr uint32_t kSlotProcMask = 0x3FFFu, kSlotMaxMask = 0x7FFFu;
+constexpr int kResMaxUnits = kResThreads;  // one slot watched per thread
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool claim_agent(uint32_t* p, uint32_t v) {
+  uint32_t expected = 0u;
+  return __hip_atomic_compare_exchange_strong(p, &expected, v, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Job of unit u (units are numbered job by job) and the unit's slice index.
+__device__ __forceinline__ int unit_job(const QuantBatch& b, int u, int& local) {
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxJobs; ++i)
+    if (i < b.njobs && u >= b.job[i].blk_begin) j = i;
+  local = u - b.job[j].blk_begin;
+  return j;
+}
+
+__global__ void __launch_bounds__(256) quant_resident_clear(QuantBatch b) {
+  for (int j = 0; j < b.njobs; ++j)
+    for (int i = threadIdx.x; i < b.job[j].nblocks; i += 256) b.job[j].partials[i] = 0u;
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4)))
+quant_resident_kernel(QuantBatch b, int units) {
+  __shared__ uint32_t red[kResThreads / 64];
+  __shared__ int s_flag, s_pick;
+  __shared__ uint32_t s_jmax[kMaxJobs];
+  __shared__ float s_scale[kMaxJobs], s_amax[kMaxJobs];
+  const int tid = threadIdx.x;
+  const uint32_t me = (uint32_t)blockIdx.x << kSlotProcShift;
+  auto slot_of = [&](int u) {
+    int local;
+    const QuantJob& jb = b.job[unit_job(b, u, local)];
+    return jb.partials + local;
+  };
+  // one unit's max over chunks k >= k0 of this thread's slice
+  auto stream_max = [&](const QuantJob& jb, int local, int k0) {
+    const int64_t nch = jb.rows * jb.cols / 8;
+    const v4u* xv = reinterpret_cast<const v4u*>(jb.x);
+    const int64_t stride = (int64_t)jb.nblocks * kResThreads;
+    int64_t i = (int64_t)local * kResThreads + tid + (int64_t)k0 * stride;
+    uint32_t m = 0;
+    for (; i + 3 * stride < nch; i += 4 * stride) {
+      const v4u a0 = __builtin_nontemporal_load(xv + i), a1 = __builtin_nontemporal_load(xv + i + stride);
+      const v4u a2 = __builtin_nontemporal_load(xv + i + 2 * stride);
+      const v4u a3 = __builtin_nontemporal_load(xv + i + 3 * stride);
+      uint32_t t0 = absmax8(a0), t1 = absmax8(a1), t2 = absmax8(a2), t3 = absmax8(a3);
+      t0 = t0 > t1 ? t0 : t1;
+      t2 = t2 > t3 ? t2 : t3;
+      t0 = t0 > t2 ? t0 : t2;
+      m = m > t0 ? m : t0;
+    }
+    for (; i < nch; i += stride) {
+      const uint32_t t = absmax8(__builtin_nontemporal_load(xv + i));
+      m = m > t ? m : t;
+    }
+    return m;
+  };
+  // the rest of a unit (chunks k >= k0) read again and cast
+  auto stream_cast = [&](const QuantJob& jb, int local, int k0, const Divider& d) {
+    const int64_t nch = jb.rows * jb.cols / 8;
+    const v4u* xv = reinterpret_cast<const v4u*>(jb.x);
+    v2u* qv = reinterpret_cast<v2u*>(jb.q);
+    const int64_t stride = (int64_t)jb.nblocks * kResThreads;
+    int64_t i = (int64_t)local * kResThreads + tid + (int64_t)k0 * stride;
+    for (; i + stride < nch; i += 2 * stride) {
+      const v4u a0 = __builtin_nontemporal_load(xv + i), a1 = __builtin_nontemporal_load(xv + i + stride);
+      qv[i] = v2u{quant4<FMT, kModePlain>(a0[0], a0[1], d), quant4<FMT, kModePlain>(a0[2], a0[3], d)};
+      qv[i + stride] = v2u{quant4<FMT, kModePlain>(a1[0], a1[1], d), quant4<FMT, kModePlain>(a1[2], a1[3], d)};
+    }
+    if (i < nch) {
+      const v4u a0 = __builtin_nontemporal_load(xv + i);
+      qv[i] = v2u{quant4<FMT, kModePlain>(a0[0], a0[1], d), quant4<FMT, kModePlain>(a0[2], a0[3], d)};
+    }
+  };
+
+  // 1. claim the block's own unit and hold it: its first kResChunks chunks
+  // are loaded through a buffer descriptor with 32-bit offsets (the tensor
+  // is under 2 GiB; offsets past it load zeros), all in flight together and
+  // issued behind the claim, not after its answer (a unit another block has
+  // claimed is loaded for nothing)
+  int held_local = 0;
+  const int held_job = unit_job(b, blockIdx.x, held_local);
+  if (tid == 0) s_flag = claim_agent(slot_of(blockIdx.x), kSlotClaimed | me) ? 1 : 0;
+  if (tid < kMaxJobs) s_jmax[tid] = 0u;
+  v4u v[kResChunks];
+  {
+    const QuantJob& jb = b.job[held_job];
+    const uint32_t nbytes = (uint32_t)(jb.rows * jb.cols * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(jb.x, nbytes);
+    const uint32_t s16 = (uint32_t)jb.nblocks * kResThreads * 16u;
+    const uint32_t o0 = ((uint32_t)held_local * kResThreads + tid) * 16u;
+#pragma unroll
+    for (int k = 0; k < kResChunks; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, o0 + k * s16, 0, 0);
+  }
+  __syncthreads();
+  const bool holds = s_flag != 0;
+  if (holds) {
+    const QuantJob& jb = b.job[held_job];
+    uint32_t m = stream_max(jb, held_local, kResChunks);
+#pragma unroll
+    for (int k = 0; k < kResChunks; ++k) {
+      const uint32_t t = absmax8(v[k]);
+      m = m > t ? m : t;
+    }
+    m = block_max_u32(m, red);
+    if (tid == 0) st_agent(jb.partials + held_local, kSlotArrived | kSlotHeld | kSlotClaimed | me | m);
+  }
+  // 2. wait until every slot has arrived.  Thread t watches unit t and
+  // stops loading its slot once it has arrived.  An unclaimed unit is
+  // claimed and processed here (max only).  The bound only guards against a
+  // fault.
+  bool seen = tid >= units;
+  bool stole = false;
+  uint32_t mine = 0u;  // the watched slot once arrived
+  for (int spin = 0; spin < (1 << 20); ++spin) {
+    uint32_t sv = 0u;
+    if (!seen) {
+      sv = ld_agent(slot_of(tid));
+      seen = (sv & kSlotArrived) != 0u;
+      mine = sv;
+    }
+    if (tid == 0) s_pick = units;
+    __syncthreads();
+    if (!seen && sv == 0u) atomicMin(&s_pick, tid);
+    const bool all = __syncthreads_and(seen);
+    if (all) break;
+    const int u = s_pick;  // an unclaimed unit, if any
+    if (u < units) {
+      if (tid == 0) s_flag = claim_agent(slot_of(u), kSlotClaimed | me) ? 1 : 0;
+      __syncthreads();
+      if (s_flag) {
+        int local;
+        const QuantJob& jb = b.job[unit_job(b, u, local)];
+        const uint32_t m = block_max_u32(stream_max(jb, local, 0), red);
+        if (tid == 0) st_agent(jb.partials + local, kSlotArrived | kSlotClaimed | me | m);
+        stole = true;
+      }
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  // every job's amax and scale, from the slots the threads watched
+  if (tid < units) {
+    int local;
+    atomicMax(&s_jmax[unit_job(b, tid, local)], mine & kSlotMaxMask);
+  }
+  __syncthreads();
+  if (tid < b.njobs) {
+    const float amax = bf16_to_f32(s_jmax[tid]);
+    constexpr float fm = FMT == kE4M3 ? kFmaxE4M3 : kFmaxE5M2;
+    s_amax[tid] = amax;
+    s_scale[tid] = amax == 0.0f ? 1.0f : amax / fm;  // IEEE division, correctly rounded
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid < b.njobs) {
+    *b.job[tid].scale = s_scale[tid];
+    if (b.job[tid].amax_out) *b.job[tid].amax_out = s_amax[tid];
+  }
+  // 3. cast.  Held chunks from registers (offsets recomputed here, not kept
+  // live from step 1), then the rest of the held unit read again.
+  if (holds) {
+    const QuantJob& jb = b.job[held_job];
+    const Divider d = make_divider(s_scale[held_job], s_amax[held_job]);
+    const uint32_t nbytes = (uint32_t)(jb.rows * jb.cols * 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(jb.q, nbytes / 2);
+    const uint32_t s16 = (uint32_t)jb.nblocks * kResThreads * 16u;
+    uint32_t o = ((uint32_t)held_local * kResThreads + tid) * 16u;
+    asm volatile("" : "+v"(o));
+#pragma unroll
+    for (int k = 0; k < kResChunks; ++k) {
+      if (o < nbytes) {
+        const v2u c = v2u{quant4<FMT, kModePlain>(v[k][0], v[k][1], d), quant4<FMT, kModePlain>(v[k][2], v[k][3], d)};
+        __builtin_amdgcn_raw_buffer_store_b64(c, rq, o >> 1, 0, 0);
+      }
+      o += s16;
+    }
+    stream_cast(jb, held_local, kResChunks, d);
+  }
+  // units this block claimed while waiting: cast whole
+  if (__syncthreads_or(stole)) {
+    for (int u = 0; u < units; ++u) {
+      const uint32_t sv = ld_agent(slot_of(u));
+      if ((sv & kSlotHeld) == 0u && ((sv >> kSlotProcShift) & kSlotProcMask) == blockIdx.x) {
+        int local;
+        const int j = unit_job(b, u, local);
+        stream_cast(b.job[j], local, 0, make_divider(s_scale[j], s_amax[j]));
+      }
+    }
+  }
+}
+
 int cast_blocks_for(int64_t rows, int64_t cols) {
   const int64_t tiles = ((rows + kTR - 1) / kTR) * ((cols + kTC - 1) / kTC);
   // at least one block: block 0 writes the scale even for an empty tensor
@@ -634,6 +868,130 @@ hipError_t launch_rmsnorm_amax(QuantJob& j, float eps, float* rstd, hipStream_t 
   else
     hipLaunchKernelGGL(rmsnorm_amax_kernel<false>, dim3(j.nblocks), dim3(256), 0, st, j, eps, rstd);
   return hipGetLastError();
+}
+
+namespace {
+
+// Blocks of quant_resident_kernel<FMT> that fit on the device at once, per
+// device, found once.
+constexpr int kResMaxDevices = 64;
+std::mutex g_res_mutex;
+int g_res_cap[kResMaxDevices][2];
+bool g_res_known[kResMaxDevices][2];
+
+int resident_capacity(int fmt) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kResMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_res_mutex);
+  if (!g_res_known[dev][fmt]) {
+    int cus = 0, per_cu = 0;
+    const void* k = fmt == kE4M3 ? reinterpret_cast<const void*>(&quant_resident_kernel<kE4M3>)
+                                 : reinterpret_cast<const void*>(&quant_resident_kernel<kE5M2>);
+    int cap = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kResThreads, 0) == hipSuccess)
+      cap = cus * per_cu;
+    (void)hipGetLastError();
+    g_res_cap[dev][fmt] = cap;
+    g_res_known[dev][fmt] = true;
+  }
+  return g_res_cap[dev][fmt];
+}
+
+// FP8MLP_QUANT_PATH selects the quantiser's form for tests: "two" always
+// takes the two launches, "single" makes a batch that cannot take the
+// single launch an error instead; unset (or anything else): automatic.
+int quant_path_override() {
+  const char* env = getenv("FP8MLP_QUANT_PATH");
+  if (!env) return 0;
+  if (strcmp(env, "two") == 0) return 2;
+  if (strcmp(env, "single") == 0) return 1;
+  return 0;
+}
+
+bool resident_eligible(const QuantBatch& b, hipStream_t st) {
+  if (b.njobs < 1) return false;
+  for (int i = 0; i < b.njobs; ++i) {
+    const QuantJob& j = b.job[i];
+    const int64_t n = j.rows * j.cols;
+    if (j.mode != kModePlain || j.fmt != b.job[0].fmt || j.qt != nullptr || j.q == nullptr) return false;
+    if (n <= 0 || n % 8 != 0 || (j.rows > 1 && (j.ldx != j.cols || j.ldq != j.cols))) return false;
+    if (n > (int64_t{1} << 30) - 8) return false;  // 32-bit byte offsets (with headroom past the end)
+    if ((reinterpret_cast<uintptr_t>(j.x) & 15u) != 0 || (reinterpret_cast<uintptr_t>(j.q) & 7u) != 0) return false;
+    if (j.nparts < 3) return false;  // small tensors: the two launches
+  }
+  // a captured stream takes the two launches (graphs hold ordinary kernel nodes)
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs == hipStreamCaptureStatusNone;
+}
+
+// Units per job: at most the job's partial count, at least one,
+// enough for one chunk per thread where the job is small; scaled down in
+// proportion to the jobs' sizes when the total exceeds the blocks the device
+// holds at once (one block per unit).
+bool resident_blocks(QuantBatch& b, int cap) {
+  int64_t want[kMaxJobs], total = 0, nch_all = 0;
+  for (int i = 0; i < b.njobs; ++i) {
+    const int64_t nch = b.job[i].rows * b.job[i].cols / 8;
+    const int64_t w = (nch + kResThreads - 1) / kResThreads;
+    want[i] = w < b.job[i].nparts ? w : b.job[i].nparts;
+    total += want[i];
+    nch_all += nch;
+  }
+  if (total > cap) {
+    if (cap < b.njobs) return false;
+    total = 0;
+    for (int i = 0; i < b.njobs; ++i) {
+      const int64_t nch = b.job[i].rows * b.job[i].cols / 8;
+      int64_t w = (int64_t)((double)cap * (double)nch / (double)nch_all);
+      if (w < 1) w = 1;
+      if (w < want[i]) want[i] = w;
+      total += want[i];
+    }
+    while (total > cap) {  // rounding: take blocks from the largest job
+      int big = 0;
+      for (int i = 1; i < b.njobs; ++i)
+        if (want[i] > want[big]) big = i;
+      if (want[big] <= 1) return false;
+      --want[big];
+      --total;
+    }
+  }
+  int begin = 0;
+  for (int i = 0; i < b.njobs; ++i) {
+    b.job[i].blk_begin = begin;
+    b.job[i].nblocks = (int)want[i];
+    begin += (int)want[i];
+  }
+  return true;
+}
+
+}  // namespace
+
+hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st) {
+  const int force = quant_path_override();
+  if (force != 2 && resident_eligible(b, st)) {
+    const int fmt = b.job[0].fmt;
+    int cap = resident_capacity(fmt);
+    cap = cap < kResMaxUnits ? cap : kResMaxUnits;
+    if (cap > 0 && resident_blocks(b, cap)) {
+      const int units = b.job[b.njobs - 1].blk_begin + b.job[b.njobs - 1].nblocks;
+      hipLaunchKernelGGL(quant_resident_clear, dim3(1), dim3(256), 0, st, b);
+      if (fmt == kE4M3)
+        hipLaunchKernelGGL(quant_resident_kernel<kE4M3>, dim3(units), dim3(kResThreads), 0, st, b, units);
+      else
+        hipLaunchKernelGGL(quant_resident_kernel<kE5M2>, dim3(units), dim3(kResThreads), 0, st, b, units);
+      return hipGetLastError();
+    }
+  }
+  if (force == 1) return hipErrorNotSupported;
+  hipError_t e = launch_amax_partials(b, st);
+  if (e != hipSuccess) return e;
+  return launch_cast(b, st);
 }
 
 hipError_t launch_cast(QuantBatch& b, hipStream_t st) {
