@@ -625,6 +625,7 @@ constexpr uint32_t kSlotArrived = 0x80000000u, kSlotHeld = 0x40000000u, kSlotCla
 constexpr int kSlotProcShift = 15;
 constexpr uint32_t kSlotProcMask = 0x3FFFu, kSlotMaxMask = 0x7FFFu;
 constexpr int kResMaxUnits = kResThreads;  // one slot watched per thread
+constexpr int kNT = 2;                      // buffer-load cache policy: non-temporal
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -690,19 +691,24 @@ quant_resident_kernel(QuantBatch b, int units) {
     }
     return m;
   };
-  // the rest of a unit (chunks k >= k0) read again and cast
+  // the rest of a unit (chunks k >= k0) read again and cast, eight loads in
+  // flight per thread (the held registers are free by then)
   auto stream_cast = [&](const QuantJob& jb, int local, int k0, const Divider& d) {
     const int64_t nch = jb.rows * jb.cols / 8;
     const v4u* xv = reinterpret_cast<const v4u*>(jb.x);
     v2u* qv = reinterpret_cast<v2u*>(jb.q);
     const int64_t stride = (int64_t)jb.nblocks * kResThreads;
     int64_t i = (int64_t)local * kResThreads + tid + (int64_t)k0 * stride;
-    for (; i + stride < nch; i += 2 * stride) {
-      const v4u a0 = __builtin_nontemporal_load(xv + i), a1 = __builtin_nontemporal_load(xv + i + stride);
-      qv[i] = v2u{quant4<FMT, kModePlain>(a0[0], a0[1], d), quant4<FMT, kModePlain>(a0[2], a0[3], d)};
-      qv[i + stride] = v2u{quant4<FMT, kModePlain>(a1[0], a1[1], d), quant4<FMT, kModePlain>(a1[2], a1[3], d)};
+    for (; i + 7 * stride < nch; i += 8 * stride) {
+      v4u a[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) a[r] = __builtin_nontemporal_load(xv + i + r * stride);
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        qv[i + r * stride] =
+            v2u{quant4<FMT, kModePlain>(a[r][0], a[r][1], d), quant4<FMT, kModePlain>(a[r][2], a[r][3], d)};
     }
-    if (i < nch) {
+    for (; i < nch; i += stride) {
       const v4u a0 = __builtin_nontemporal_load(xv + i);
       qv[i] = v2u{quant4<FMT, kModePlain>(a0[0], a0[1], d), quant4<FMT, kModePlain>(a0[2], a0[3], d)};
     }
@@ -725,7 +731,7 @@ quant_resident_kernel(QuantBatch b, int units) {
     const uint32_t s16 = (uint32_t)jb.nblocks * kResThreads * 16u;
     const uint32_t o0 = ((uint32_t)held_local * kResThreads + tid) * 16u;
 #pragma unroll
-    for (int k = 0; k < kResChunks; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, o0 + k * s16, 0, 0);
+    for (int k = 0; k < kResChunks; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, o0 + k * s16, 0, kNT);
   }
   __syncthreads();
   const bool holds = s_flag != 0;
