@@ -48,9 +48,8 @@ hipError_t launch_amax_partials(QuantBatch& b, hipStream_t st);
 // amax and cast of every job of the batch (mode plain): one pass over the
 // data (a one-block clear, then one grid that holds part of the tensors in
 // registers across a grid-wide wait) when every job is dense, 16-byte
-// aligned and codes-only and the stream is not capturing, else
-// launch_amax_partials then launch_cast.  Uses at most each job's nparts
-// partials.
+// aligned and codes-only, else launch_amax_partials then launch_cast.  Uses
+// at most each job's nparts partials.
 hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st);
 // RMSNorm statistics and amax partials of one job (mode kModeRmsNorm): writes
 // rstd[row] and one partial per block of rows (rmsnorm_parts_for of them).

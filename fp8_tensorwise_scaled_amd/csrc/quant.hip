@@ -915,7 +915,7 @@ int quant_path_override() {
   return 0;
 }
 
-bool resident_eligible(const QuantBatch& b, hipStream_t st) {
+bool resident_eligible(const QuantBatch& b) {
   if (b.njobs < 1) return false;
   for (int i = 0; i < b.njobs; ++i) {
     const QuantJob& j = b.job[i];
@@ -926,13 +926,7 @@ bool resident_eligible(const QuantBatch& b, hipStream_t st) {
     if ((reinterpret_cast<uintptr_t>(j.x) & 15u) != 0 || (reinterpret_cast<uintptr_t>(j.q) & 7u) != 0) return false;
     if (j.nparts < 3) return false;  // small tensors: the two launches
   }
-  // a captured stream takes the two launches (graphs hold ordinary kernel nodes)
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
-    (void)hipGetLastError();
-    return false;
-  }
-  return cs == hipStreamCaptureStatusNone;
+  return true;
 }
 
 // Units per job: at most the job's partial count, at least one,
@@ -980,7 +974,7 @@ bool resident_blocks(QuantBatch& b, int cap) {
 
 hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st) {
   const int force = quant_path_override();
-  if (force != 2 && resident_eligible(b, st)) {
+  if (force != 2 && resident_eligible(b)) {
     const int fmt = b.job[0].fmt;
     int cap = resident_capacity(fmt);
     cap = cap < kResMaxUnits ? cap : kResMaxUnits;
