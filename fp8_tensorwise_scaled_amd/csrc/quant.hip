@@ -656,7 +656,7 @@ __global__ void __launch_bounds__(256) quant_resident_clear(QuantBatch b) {
 
 template <int FMT>
 __global__ void __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4)))
-quant_resident_kernel(QuantBatch b, int units) {
+quant_resident_kernel(QuantBatch b, int units, int spin_limit) {
   __shared__ uint32_t red[kResThreads / 64];
   __shared__ int s_flag, s_pick;
   __shared__ uint32_t s_jmax[kMaxJobs];
@@ -713,6 +713,14 @@ quant_resident_kernel(QuantBatch b, int units) {
       qv[i] = v2u{quant4<FMT, kModePlain>(a0[0], a0[1], d), quant4<FMT, kModePlain>(a0[2], a0[3], d)};
     }
   };
+  // NaN codes over chunks k >= k0 of a unit (the wait's bound was reached)
+  auto stream_nan = [&](const QuantJob& jb, int local, int k0) {
+    const int64_t nch = jb.rows * jb.cols / 8;
+    v2u* qv = reinterpret_cast<v2u*>(jb.q);
+    const int64_t stride = (int64_t)jb.nblocks * kResThreads;
+    for (int64_t i = (int64_t)local * kResThreads + tid + (int64_t)k0 * stride; i < nch; i += stride)
+      qv[i] = v2u{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+  };
 
   // 1. claim the block's own unit and hold it: its first kResChunks chunks
   // are loaded through a buffer descriptor with 32-bit offsets (the tensor
@@ -748,12 +756,15 @@ quant_resident_kernel(QuantBatch b, int units) {
   }
   // 2. wait until every slot has arrived.  Thread t watches unit t and
   // stops loading its slot once it has arrived.  An unclaimed unit is
-  // claimed and processed here (max only).  The bound only guards against a
-  // fault.
+  // claimed and processed here (max only).  The bound (spin_limit polls,
+  // several seconds by default) only guards against a fault: a block that reaches it writes NaN codes
+  // (0x7F is NaN in both formats) for the chunks it holds, and block 0 a
+  // NaN scale, so that an incomplete amax shows in the outputs.
   bool seen = tid >= units;
   bool stole = false;
+  bool all = false;
   uint32_t mine = 0u;  // the watched slot once arrived
-  for (int spin = 0; spin < (1 << 20); ++spin) {
+  for (int spin = 0; spin < spin_limit && !all; ++spin) {
     uint32_t sv = 0u;
     if (!seen) {
       sv = ld_agent(slot_of(tid));
@@ -763,7 +774,7 @@ quant_resident_kernel(QuantBatch b, int units) {
     if (tid == 0) s_pick = units;
     __syncthreads();
     if (!seen && sv == 0u) atomicMin(&s_pick, tid);
-    const bool all = __syncthreads_and(seen);
+    all = __syncthreads_and(seen);
     if (all) break;
     const int u = s_pick;  // an unclaimed unit, if any
     if (u < units) {
@@ -795,7 +806,7 @@ quant_resident_kernel(QuantBatch b, int units) {
   }
   __syncthreads();
   if (blockIdx.x == 0 && tid < b.njobs) {
-    *b.job[tid].scale = s_scale[tid];
+    *b.job[tid].scale = all ? s_scale[tid] : __builtin_nanf("");
     if (b.job[tid].amax_out) *b.job[tid].amax_out = s_amax[tid];
   }
   // 3. cast.  Held chunks from registers (offsets recomputed here, not kept
@@ -811,12 +822,16 @@ quant_resident_kernel(QuantBatch b, int units) {
 #pragma unroll
     for (int k = 0; k < kResChunks; ++k) {
       if (o < nbytes) {
-        const v2u c = v2u{quant4<FMT, kModePlain>(v[k][0], v[k][1], d), quant4<FMT, kModePlain>(v[k][2], v[k][3], d)};
+        const v2u c = all ? v2u{quant4<FMT, kModePlain>(v[k][0], v[k][1], d), quant4<FMT, kModePlain>(v[k][2], v[k][3], d)}
+                          : v2u{0x7F7F7F7Fu, 0x7F7F7F7Fu};
         __builtin_amdgcn_raw_buffer_store_b64(c, rq, o >> 1, 0, 0);
       }
       o += s16;
     }
-    stream_cast(jb, held_local, kResChunks, d);
+    if (all)
+      stream_cast(jb, held_local, kResChunks, d);
+    else
+      stream_nan(jb, held_local, kResChunks);
   }
   // units this block claimed while waiting: cast whole
   if (__syncthreads_or(stole)) {
@@ -825,7 +840,10 @@ quant_resident_kernel(QuantBatch b, int units) {
       if ((sv & kSlotHeld) == 0u && ((sv >> kSlotProcShift) & kSlotProcMask) == blockIdx.x) {
         int local;
         const int j = unit_job(b, u, local);
-        stream_cast(b.job[j], local, 0, make_divider(s_scale[j], s_amax[j]));
+        if (all)
+          stream_cast(b.job[j], local, 0, make_divider(s_scale[j], s_amax[j]));
+        else
+          stream_nan(b.job[j], local, 0);
       }
     }
   }
@@ -915,6 +933,14 @@ int quant_path_override() {
   return 0;
 }
 
+// Polls of the single pass's wait before it gives up (its outputs then
+// carry NaN); FP8MLP_QUANT_SPIN_LIMIT sets it for tests of that path.
+int quant_spin_limit() {
+  const char* env = getenv("FP8MLP_QUANT_SPIN_LIMIT");
+  if (env && env[0]) return atoi(env);
+  return 1 << 23;
+}
+
 bool resident_eligible(const QuantBatch& b) {
   if (b.njobs < 1) return false;
   for (int i = 0; i < b.njobs; ++i) {
@@ -982,9 +1008,11 @@ hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st) {
       const int units = b.job[b.njobs - 1].blk_begin + b.job[b.njobs - 1].nblocks;
       hipLaunchKernelGGL(quant_resident_clear, dim3(1), dim3(256), 0, st, b);
       if (fmt == kE4M3)
-        hipLaunchKernelGGL(quant_resident_kernel<kE4M3>, dim3(units), dim3(kResThreads), 0, st, b, units);
+        hipLaunchKernelGGL(quant_resident_kernel<kE4M3>, dim3(units), dim3(kResThreads), 0, st, b, units,
+                           quant_spin_limit());
       else
-        hipLaunchKernelGGL(quant_resident_kernel<kE5M2>, dim3(units), dim3(kResThreads), 0, st, b, units);
+        hipLaunchKernelGGL(quant_resident_kernel<kE5M2>, dim3(units), dim3(kResThreads), 0, st, b, units,
+                           quant_spin_limit());
       return hipGetLastError();
     }
   }

@@ -123,3 +123,22 @@ def test_block_batches_single_vs_two(monkeypatch, wl):
         assert torch.equal(getattr(r1[1], name), getattr(r2[1], name)), name
     for i, name in ((0, "y"), (2, "dx"), (3, "dw_up"), (4, "dw_down"), (5, "bwd_scales")):
         assert torch.equal(r1[i], r2[i]), name
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_wait_bound_reached_gives_nan(monkeypatch, fmt):
+    """The single pass's wait is bounded.  With the bound set to zero polls
+    (a host-side setting: no block waits, every kernel ends normally) no
+    block can know the amax, and every output must show it: all codes NaN
+    (0x7F) and the scale NaN.  The next call with the default bound is
+    correct again."""
+    x = synth.normal_bf16((2048, 768), 1.0, 7400 + fmt)
+    xd = to_dev_bf16(x)
+    monkeypatch.setenv("FP8MLP_QUANT_SPIN_LIMIT", "0")
+    q, s, _ = with_path(monkeypatch, "single", lambda: quant(xd, fmt))
+    monkeypatch.delenv("FP8MLP_QUANT_SPIN_LIMIT")
+    assert (u8(q) == 0x7F).all()
+    assert np.isnan(f32(s)[0])
+    q, s, _ = with_path(monkeypatch, "single", lambda: quant(xd, fmt))
+    rq, rs, _ = oracle.quant(x, fmt)
+    assert (u8(q) == rq).all() and np.float32(f32(s)[0]) == np.float32(rs)
