@@ -295,9 +295,8 @@ int fp8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64
   b.job[0].rstd = rstd;
   b.job[0].gamma = gamma;
   hipStream_t st = (hipStream_t)stream;
-  if (rows > 0 && cols > 0) {
-    if (launch_rmsnorm_amax(b.job[0], eps, rstd, st) != hipSuccess) return FP8MLP_EHIP;
-  } else {
+  if (rows > 0 && cols > 0) return hip_status(launch_rmsnorm_quant(b, eps, rstd, st));
+  {
     // no elements: amax 0, scale 1 (the partial the cast reads is written by
     // the plain amax pass over nothing)
     b.job[0].mode = kModePlain;

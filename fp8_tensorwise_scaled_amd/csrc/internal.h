@@ -51,6 +51,12 @@ hipError_t launch_amax_partials(QuantBatch& b, hipStream_t st);
 // aligned and codes-only, else launch_amax_partials then launch_cast.  Uses
 // at most each job's nparts partials.
 hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st);
+// RMSNorm statistics, amax and cast of one job (mode kModeRmsNorm): one pass
+// (a one-block clear, then a grid that holds 16 rows per block in registers
+// across a grid-wide wait) for dense rows of at most 3072 columns with codes
+// only, else launch_rmsnorm_amax then launch_cast.  Uses at most the job's
+// nparts partials.
+hipError_t launch_rmsnorm_quant(QuantBatch& b, float eps, float* rstd, hipStream_t st);
 // RMSNorm statistics and amax partials of one job (mode kModeRmsNorm): writes
 // rstd[row] and one partial per block of rows (rmsnorm_parts_for of them).
 int rmsnorm_parts_for(int64_t rows);

@@ -649,6 +649,48 @@ __device__ __forceinline__ int unit_job(const QuantBatch& b, int u, int& local) 
   return j;
 }
 
+// The single pass's grid-wide wait.  Thread t watches unit t's slot and
+// stops loading it once it has arrived.  A unit found unclaimed (its block
+// has not started) is claimed here and handed to steal(u), which processes
+// it and publishes its slot, so the wait ends whether or not all blocks are
+// resident at once.  Returns true when every slot arrived within spin_limit
+// polls (a bound that only guards against a fault); `mine` receives the
+// watched slot, `stole` whether this block processed a unit here.
+template <class SlotOf, class Steal>
+__device__ bool resident_wait(int units, int spin_limit, uint32_t me, SlotOf slot_of, Steal steal, uint32_t& mine,
+                              bool& stole) {
+  __shared__ int s_pick, s_won;
+  const int tid = threadIdx.x;
+  bool seen = tid >= units;
+  bool all = false;
+  for (int spin = 0; spin < spin_limit && !all; ++spin) {
+    uint32_t sv = 0u;
+    if (!seen) {
+      sv = ld_agent(slot_of(tid));
+      seen = (sv & kSlotArrived) != 0u;
+      mine = sv;
+    }
+    if (tid == 0) s_pick = units;
+    __syncthreads();
+    if (!seen && sv == 0u) atomicMin(&s_pick, tid);
+    all = __syncthreads_and(seen);
+    if (all) break;
+    const int u = s_pick;  // an unclaimed unit, if any
+    if (u < units) {
+      if (tid == 0) s_won = claim_agent(slot_of(u), kSlotClaimed | me) ? 1 : 0;
+      __syncthreads();
+      if (s_won) {
+        steal(u);
+        stole = true;
+      }
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  return all;
+}
+
 __global__ void __launch_bounds__(256) quant_resident_clear(QuantBatch b) {
   for (int j = 0; j < b.njobs; ++j)
     for (int i = threadIdx.x; i < b.job[j].nblocks; i += 256) b.job[j].partials[i] = 0u;
@@ -658,7 +700,7 @@ template <int FMT>
 __global__ void __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4)))
 quant_resident_kernel(QuantBatch b, int units, int spin_limit) {
   __shared__ uint32_t red[kResThreads / 64];
-  __shared__ int s_flag, s_pick;
+  __shared__ int s_flag;
   __shared__ uint32_t s_jmax[kMaxJobs];
   __shared__ float s_scale[kMaxJobs], s_amax[kMaxJobs];
   const int tid = threadIdx.x;
@@ -754,44 +796,18 @@ quant_resident_kernel(QuantBatch b, int units, int spin_limit) {
     m = block_max_u32(m, red);
     if (tid == 0) st_agent(jb.partials + held_local, kSlotArrived | kSlotHeld | kSlotClaimed | me | m);
   }
-  // 2. wait until every slot has arrived.  Thread t watches unit t and
-  // stops loading its slot once it has arrived.  An unclaimed unit is
-  // claimed and processed here (max only).  The bound (spin_limit polls,
-  // several seconds by default) only guards against a fault: a block that reaches it writes NaN codes
-  // (0x7F is NaN in both formats) for the chunks it holds, and block 0 a
-  // NaN scale, so that an incomplete amax shows in the outputs.
-  bool seen = tid >= units;
+  // 2. wait until every slot has arrived; a unit still unclaimed is
+  // processed here (max only).  A block whose wait reaches the bound writes
+  // NaN codes (0x7F is NaN in both formats) for the chunks it holds, and
+  // block 0 a NaN scale, so that an incomplete amax shows in the outputs.
   bool stole = false;
-  bool all = false;
   uint32_t mine = 0u;  // the watched slot once arrived
-  for (int spin = 0; spin < spin_limit && !all; ++spin) {
-    uint32_t sv = 0u;
-    if (!seen) {
-      sv = ld_agent(slot_of(tid));
-      seen = (sv & kSlotArrived) != 0u;
-      mine = sv;
-    }
-    if (tid == 0) s_pick = units;
-    __syncthreads();
-    if (!seen && sv == 0u) atomicMin(&s_pick, tid);
-    all = __syncthreads_and(seen);
-    if (all) break;
-    const int u = s_pick;  // an unclaimed unit, if any
-    if (u < units) {
-      if (tid == 0) s_flag = claim_agent(slot_of(u), kSlotClaimed | me) ? 1 : 0;
-      __syncthreads();
-      if (s_flag) {
-        int local;
-        const QuantJob& jb = b.job[unit_job(b, u, local)];
-        const uint32_t m = block_max_u32(stream_max(jb, local, 0), red);
-        if (tid == 0) st_agent(jb.partials + local, kSlotArrived | kSlotClaimed | me | m);
-        stole = true;
-      }
-      __syncthreads();
-    } else {
-      __builtin_amdgcn_s_sleep(4);
-    }
-  }
+  const bool all = resident_wait(units, spin_limit, me, slot_of, [&](int u) {
+    int local;
+    const QuantJob& jb = b.job[unit_job(b, u, local)];
+    const uint32_t m = block_max_u32(stream_max(jb, local, 0), red);
+    if (tid == 0) st_agent(jb.partials + local, kSlotArrived | kSlotClaimed | me | m);
+  }, mine, stole);
   // every job's amax and scale, from the slots the threads watched
   if (tid < units) {
     int local;
@@ -849,6 +865,188 @@ quant_resident_kernel(QuantBatch b, int units, int spin_limit) {
   }
 }
 
+// Single-pass RMSNorm + quantisation of rows of up to 64 * 8 * kRmsResChunks
+// = 3072 columns (16-byte aligned, codes only).  Unit u is rows 16u .. 16u + 15;
+// wave w of its block holds rows 16u + w and 16u + w + 8 in registers, lane
+// l the 16-byte chunks l + 64k of each, so the per-row sums of squares, r,
+// and the max |X| are computed exactly as rmsnorm_amax_kernel does.  The
+// block publishes the unit's max in its slot (partials[u]) and waits for
+// every unit, as quant_resident_kernel does, then casts its rows from
+// registers: X is recomputed from x, r and g as the two-launch cast does, so
+// r, the scale and the codes are those of the two launches.  A unit
+// processed while waiting (its block had not started) is streamed twice.
+constexpr int kRmsResRows = 16;
+constexpr int kRmsResChunks = 6;  // per lane and row (8 would spill)
+
+template <int FMT>
+__global__ void __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4)))
+rmsnorm_resident_kernel(QuantJob jb, float eps, float* rstd, int units, int spin_limit) {
+  __shared__ uint32_t red[kResThreads / 64];
+  __shared__ int s_flag;
+  __shared__ uint32_t s_max;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t me = (uint32_t)blockIdx.x << kSlotProcShift;
+  const int64_t rows = jb.rows, cols = jb.cols, ldx = jb.ldx;
+  const uint16_t* g = jb.gamma;
+  const bool g_vec = g != nullptr && aligned16(g);
+  const int64_t nch = cols / 8;
+  const uint32_t row_bytes = (uint32_t)(2 * cols);
+  auto slot_of = [&](int u) { return jb.partials + u; };
+  auto row_of = [&](int u, int i) { return (int64_t)u * kRmsResRows + wave + 8 * i; };
+  auto weights = [&](int64_t c, float gf[8]) {
+    const v4u gv = load_g8(g, 8 * c, g_vec);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gf[2 * e] = g ? __uint_as_float(gv[e] << 16) : 1.0f;
+      gf[2 * e + 1] = g ? __uint_as_float(gv[e] & 0xFFFF0000u) : 1.0f;
+    }
+  };
+  auto r_of = [&](double ss) { return 1.0f / sqrtf((float)(ss / (double)cols) + eps); };
+  // a row's chunk k of this lane, zeros past the row or for a missing row
+  auto load_chunk = [&](int64_t row, int k) {
+    const bool has = row < rows;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(jb.x + (has ? row : 0) * ldx, has ? row_bytes : 0u);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, 16u * (uint32_t)(lane + 64 * k), 0, kNT);
+  };
+  // streamed form (a unit processed while waiting): r of a row, then the
+  // max fp32 magnitude bits of its X; the same sums in the same order
+  auto stream_r = [&](int64_t row) {
+    double ss = 0.0;
+#pragma unroll 1
+    for (int k = 0; k < kRmsResChunks; ++k) ss = sumsq8(load_chunk(row, k), ss);
+    return r_of(wave_sum_f64(ss));
+  };
+
+  // 1. the block's own rows, held
+  if (tid == 0) {
+    s_flag = claim_agent(slot_of(blockIdx.x), kSlotClaimed | me) ? 1 : 0;
+    s_max = 0u;
+  }
+  v4u buf[2][kRmsResChunks];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int k = 0; k < kRmsResChunks; ++k) buf[i][k] = load_chunk(row_of(blockIdx.x, i), k);
+  __syncthreads();
+  const bool holds = s_flag != 0;
+  float r[2] = {1.0f, 1.0f};
+  if (holds) {
+    uint32_t mb = 0;  // fp32 magnitude bits
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = row_of(blockIdx.x, i);
+      double ss = 0.0;
+#pragma unroll
+      for (int k = 0; k < kRmsResChunks; ++k) ss = sumsq8(buf[i][k], ss);
+      r[i] = r_of(wave_sum_f64(ss));
+      if (lane == 0 && row < rows) rstd[row] = r[i];
+    }
+#pragma unroll
+    for (int k = 0; k < kRmsResChunks; ++k) {
+      const int64_t c = lane + 64 * k;
+      if (c < nch) {
+        float gf[8];
+        weights(c, gf);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (row_of(blockIdx.x, i) < rows) mb = norm_maxbits8(buf[i][k], r[i], gf, mb);
+      }
+    }
+    const uint32_t m = block_max_u32(f32_to_bf16_rne(__uint_as_float(mb)) & 0x7FFFu, red);
+    if (tid == 0) st_agent(slot_of(blockIdx.x), kSlotArrived | kSlotHeld | kSlotClaimed | me | m);
+  }
+  // 2. wait for every unit (see quant_resident_kernel for the bound)
+  bool stole = false;
+  uint32_t mine = 0u;
+  const bool all = resident_wait(units, spin_limit, me, slot_of, [&](int u) {
+    uint32_t mb = 0;
+#pragma unroll 1
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = row_of(u, i);
+      const float rr = stream_r(row);
+      if (lane == 0 && row < rows) rstd[row] = rr;
+#pragma unroll 1
+      for (int k = 0; k < kRmsResChunks; ++k) {
+        const int64_t c = lane + 64 * k;
+        if (c < nch && row < rows) {
+          float gf[8];
+          weights(c, gf);
+          mb = norm_maxbits8(load_chunk(row, k), rr, gf, mb);
+        }
+      }
+    }
+    const uint32_t m = block_max_u32(f32_to_bf16_rne(__uint_as_float(mb)) & 0x7FFFu, red);
+    if (tid == 0) st_agent(slot_of(u), kSlotArrived | kSlotClaimed | me | m);
+  }, mine, stole);
+  if (tid < units) atomicMax(&s_max, mine & kSlotMaxMask);
+  __syncthreads();
+  const float amax = bf16_to_f32(s_max);
+  constexpr float fm = FMT == kE4M3 ? kFmaxE4M3 : kFmaxE5M2;
+  const float sc = amax == 0.0f ? 1.0f : amax / fm;  // IEEE division, correctly rounded
+  if (blockIdx.x == 0 && tid == 0) {
+    *jb.scale = all ? sc : __builtin_nanf("");
+    if (jb.amax_out) *jb.amax_out = amax;
+  }
+  const Divider d = make_divider(sc, amax);
+  // 3. cast: held rows from registers (NaN codes if the wait gave up)
+  auto cast_row = [&](int64_t row, float rr, auto&& chunk) {
+    if (row >= rows) return;
+    uint8_t* qr = jb.q + row * jb.ldq;
+#pragma unroll 1
+    for (int k = 0; k < kRmsResChunks; ++k) {
+      const int64_t c = lane + 64 * k;
+      if (c < nch) {
+        v2u o = v2u{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+        if (all) {
+          float gf[8];
+          weights(c, gf);
+          const v4u v = chunk(k);
+          o = v2u{quant4_norm<FMT>(v[0], v[1], rr, gf, g != nullptr, d),
+                  quant4_norm<FMT>(v[2], v[3], rr, gf + 4, g != nullptr, d)};
+        }
+        *reinterpret_cast<v2u*>(qr + 8 * c) = o;
+      }
+    }
+  };
+  if (holds) {
+    // the held chunks, indexed by compile-time k and i once unrolled; one
+    // chunk's weights serve both rows
+#pragma unroll
+    for (int k = 0; k < kRmsResChunks; ++k) {
+      const int64_t c = lane + 64 * k;
+      if (c < nch) {
+        float gf[8];
+        weights(c, gf);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int64_t row = row_of(blockIdx.x, i);
+          if (row < rows) {
+            v2u o = v2u{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+            if (all)
+              o = v2u{quant4_norm<FMT>(buf[i][k][0], buf[i][k][1], r[i], gf, g != nullptr, d),
+                      quant4_norm<FMT>(buf[i][k][2], buf[i][k][3], r[i], gf + 4, g != nullptr, d)};
+            *reinterpret_cast<v2u*>(jb.q + row * jb.ldq + 8 * c) = o;
+          }
+        }
+      }
+    }
+  }
+  // rows of units this block processed while waiting: read twice more
+  if (__syncthreads_or(stole)) {
+    for (int u = 0; u < units; ++u) {
+      const uint32_t sv = ld_agent(slot_of(u));
+      if ((sv & kSlotHeld) == 0u && ((sv >> kSlotProcShift) & kSlotProcMask) == blockIdx.x) {
+#pragma unroll 1
+        for (int i = 0; i < 2; ++i) {
+          const int64_t row = row_of(u, i);
+          const float rr = stream_r(row);
+          cast_row(row, rr, [&](int k) { return load_chunk(row, k); });
+        }
+      }
+    }
+  }
+}
+
 int cast_blocks_for(int64_t rows, int64_t cols) {
   const int64_t tiles = ((rows + kTR - 1) / kTR) * ((cols + kTC - 1) / kTC);
   // at least one block: block 0 writes the scale even for an empty tensor
@@ -900,26 +1098,29 @@ namespace {
 // device, found once.
 constexpr int kResMaxDevices = 64;
 std::mutex g_res_mutex;
-int g_res_cap[kResMaxDevices][2];
-bool g_res_known[kResMaxDevices][2];
+int g_res_cap[kResMaxDevices][4];
+bool g_res_known[kResMaxDevices][4];
 
-int resident_capacity(int fmt) {
+// kind: fmt for quant_resident_kernel<fmt>, 2 + fmt for rmsnorm_resident_kernel<fmt>
+int resident_capacity(int kind) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kResMaxDevices) return 0;
   std::lock_guard<std::mutex> lock(g_res_mutex);
-  if (!g_res_known[dev][fmt]) {
+  if (!g_res_known[dev][kind]) {
     int cus = 0, per_cu = 0;
-    const void* k = fmt == kE4M3 ? reinterpret_cast<const void*>(&quant_resident_kernel<kE4M3>)
-                                 : reinterpret_cast<const void*>(&quant_resident_kernel<kE5M2>);
+    const void* k = kind == 0   ? reinterpret_cast<const void*>(&quant_resident_kernel<kE4M3>)
+                    : kind == 1 ? reinterpret_cast<const void*>(&quant_resident_kernel<kE5M2>)
+                    : kind == 2 ? reinterpret_cast<const void*>(&rmsnorm_resident_kernel<kE4M3>)
+                                : reinterpret_cast<const void*>(&rmsnorm_resident_kernel<kE5M2>);
     int cap = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kResThreads, 0) == hipSuccess)
       cap = cus * per_cu;
     (void)hipGetLastError();
-    g_res_cap[dev][fmt] = cap;
-    g_res_known[dev][fmt] = true;
+    g_res_cap[dev][kind] = cap;
+    g_res_known[dev][kind] = true;
   }
-  return g_res_cap[dev][fmt];
+  return g_res_cap[dev][kind];
 }
 
 // FP8MLP_QUANT_PATH selects the quantiser's form for tests: "two" always
@@ -1018,6 +1219,37 @@ hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st) {
   }
   if (force == 1) return hipErrorNotSupported;
   hipError_t e = launch_amax_partials(b, st);
+  if (e != hipSuccess) return e;
+  return launch_cast(b, st);
+}
+
+hipError_t launch_rmsnorm_quant(QuantBatch& b, float eps, float* rstd, hipStream_t st) {
+  const int force = quant_path_override();
+  QuantJob& j = b.job[0];
+  const int64_t units = (j.rows + kRmsResRows - 1) / kRmsResRows;
+  const bool eligible = b.njobs == 1 && j.mode == kModeRmsNorm && j.qt == nullptr && j.q != nullptr &&
+                        j.rows > 0 && j.cols > 0 && j.cols % 8 == 0 && j.cols <= 64 * 8 * kRmsResChunks &&
+                        (reinterpret_cast<uintptr_t>(j.x) & 15u) == 0 && j.ldx % 8 == 0 &&
+                        (reinterpret_cast<uintptr_t>(j.q) & 7u) == 0 && j.ldq % 8 == 0 && units >= 3 &&
+                        units <= j.nparts;
+  if (force != 2 && eligible) {
+    int cap = resident_capacity(2 + j.fmt);
+    cap = cap < kResMaxUnits ? cap : kResMaxUnits;
+    if (units <= cap) {
+      j.blk_begin = 0;
+      j.nblocks = (int)units;
+      hipLaunchKernelGGL(quant_resident_clear, dim3(1), dim3(256), 0, st, b);
+      if (j.fmt == kE4M3)
+        hipLaunchKernelGGL(rmsnorm_resident_kernel<kE4M3>, dim3(units), dim3(kResThreads), 0, st, j, eps, rstd,
+                           (int)units, quant_spin_limit());
+      else
+        hipLaunchKernelGGL(rmsnorm_resident_kernel<kE5M2>, dim3(units), dim3(kResThreads), 0, st, j, eps, rstd,
+                           (int)units, quant_spin_limit());
+      return hipGetLastError();
+    }
+  }
+  if (force == 1) return hipErrorNotSupported;
+  hipError_t e = launch_rmsnorm_amax(j, eps, rstd, st);
   if (e != hipSuccess) return e;
   return launch_cast(b, st);
 }
