@@ -48,13 +48,15 @@ hipError_t launch_amax_partials(QuantBatch& b, hipStream_t st);
 // amax and cast of every job of the batch (mode plain): one pass over the
 // data (a one-block clear, then one grid that holds part of the tensors in
 // registers across a grid-wide wait) when every job is dense, 16-byte
-// aligned and codes-only, else launch_amax_partials then launch_cast.  Uses
+// aligned and codes-only and the batch gives at least 256 work units, else
+// launch_amax_partials then launch_cast.  Uses
 // at most each job's nparts partials.
 hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st);
 // RMSNorm statistics, amax and cast of one job (mode kModeRmsNorm): one pass
 // (a one-block clear, then a grid that holds 16 rows per block in registers
 // across a grid-wide wait) for dense rows of at most 3072 columns with codes
-// only, else launch_rmsnorm_amax then launch_cast.  Uses at most the job's
+// only and at least 256 units of 16 rows, else launch_rmsnorm_amax then
+// launch_cast.  Uses at most the job's
 // nparts partials.
 hipError_t launch_rmsnorm_quant(QuantBatch& b, float eps, float* rstd, hipStream_t st);
 // RMSNorm statistics and amax partials of one job (mode kModeRmsNorm): writes

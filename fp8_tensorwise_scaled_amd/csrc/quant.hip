@@ -20,7 +20,8 @@
 //      launch), so both outputs are written in full 128-byte lines.
 //
 // One pass per batch where every tensor is dense, 16-byte aligned and wants
-// codes only (the MLP blocks' inputs, weights and dY): one grid reads each
+// codes only and the batch is large enough to fill the CUs (the 3.8B-model
+// block's inputs, weights and dY; the LM head's): one grid reads each
 // tensor once for its amax, keeping the first 21 chunks of 8 values per
 // thread in registers (about 88 MB over the 256 CUs' register files), waits
 // at one grid-wide barrier, and casts the held chunks without reading them
@@ -625,6 +626,10 @@ constexpr uint32_t kSlotArrived = 0x80000000u, kSlotHeld = 0x40000000u, kSlotCla
 constexpr int kSlotProcShift = 15;
 constexpr uint32_t kSlotProcMask = 0x3FFFu, kSlotMaxMask = 0x7FFFu;
 constexpr int kResMaxUnits = kResThreads;  // one slot watched per thread
+// Fewer units than this leave CUs idle, and the two launches are faster
+// there (the small block's inputs: 24-90 units); the automatic choice then
+// takes the two launches, FP8MLP_QUANT_PATH=single still the single pass.
+constexpr int kResMinUnits = 256;
 constexpr int kNT = 2;                      // buffer-load cache policy: non-temporal
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
@@ -1205,7 +1210,8 @@ hipError_t launch_amax_cast(QuantBatch& b, hipStream_t st) {
     const int fmt = b.job[0].fmt;
     int cap = resident_capacity(fmt);
     cap = cap < kResMaxUnits ? cap : kResMaxUnits;
-    if (cap > 0 && resident_blocks(b, cap)) {
+    if (cap > 0 && resident_blocks(b, cap) &&
+        (force == 1 || b.job[b.njobs - 1].blk_begin + b.job[b.njobs - 1].nblocks >= kResMinUnits)) {
       const int units = b.job[b.njobs - 1].blk_begin + b.job[b.njobs - 1].nblocks;
       hipLaunchKernelGGL(quant_resident_clear, dim3(1), dim3(256), 0, st, b);
       if (fmt == kE4M3)
@@ -1235,7 +1241,7 @@ hipError_t launch_rmsnorm_quant(QuantBatch& b, float eps, float* rstd, hipStream
   if (force != 2 && eligible) {
     int cap = resident_capacity(2 + j.fmt);
     cap = cap < kResMaxUnits ? cap : kResMaxUnits;
-    if (units <= cap) {
+    if (units <= cap && (force == 1 || units >= kResMinUnits)) {
       j.blk_begin = 0;
       j.nblocks = (int)units;
       hipLaunchKernelGGL(quant_resident_clear, dim3(1), dim3(256), 0, st, b);
