@@ -114,6 +114,16 @@ size_t fp8_amax_quant_workspace_bytes(int64_t rows, int64_t cols);
  * ragged edges) takes a correct element-wise path.
  * An empty tensor (rows == 0 or cols == 0) is valid: amax = 0, scale = 1,
  * no codes written.
+ * A dense tensor (ldx == ldq == cols, x 16-byte aligned) that wants q only
+ * and gives at least 256 work units (about 17 M elements) takes one pass:
+ * one grid takes the amax, waits once grid-wide and casts, holding part of
+ * x in registers across the wait; otherwise an amax launch and a cast
+ * launch.  Both forms give the same bytes.  The single pass's wait is
+ * bounded; should it ever give up (a fault, not a load condition), the
+ * scale is NaN and the codes it could not finish are NaN (0x7F).  For
+ * tests, the environment variable FP8MLP_QUANT_PATH=two|single forces a
+ * form (single: an error where it cannot apply) and FP8MLP_QUANT_SPIN_LIMIT
+ * sets the wait's bound.  Calls that share one workspace must not overlap.
  * Non-finite inputs are outside the numeric contract (the pages' tensors
  * are finite).  What is guaranteed: if x holds a NaN or an infinity, amax
  * and scale come out non-finite (NaN orders above infinity), so a caller can
@@ -130,7 +140,7 @@ int fp8_amax_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, i
  * library-owned static device array of 4 KB (1024 u32; no tensor needs
  * more), one per GPU, held until the process ends and found on the first
  * call on each GPU (hipGetSymbolAddress) with that GPU current.  The call
- * allocates nothing.  Calls on one GPU share that array: calls that overlap
+ * allocates nothing and always takes the amax launch and the cast launch.  Calls on one GPU share that array: calls that overlap
  * on one GPU (different streams, or host threads) race and must be
  * serialised by the caller.  Nothing in the array has to start at zero: each
  * call writes every partial it reads. */
@@ -146,7 +156,10 @@ int fp8_amax_quant_noalloc(const uint16_t* x, int64_t rows, int64_t cols, int64_
  *   X_j = RN_bf16(RN32(RN32(x_j r) gamma_j))           (gamma NULL: no weight)
  * then q / qt / scale / amax exactly as fp8_amax_quant of X.  X itself is not
  * stored: the statistics pass takes r and the amax, the cast pass recomputes
- * X from x, r and gamma.
+ * X from x, r and gamma.  Rows of at most 3072 columns (16-byte aligned,
+ * q only, 4096 rows or more) take both in one pass, each block holding 16
+ * rows in registers across one grid-wide wait, with the same results and
+ * the same bounded-wait behaviour as fp8_amax_quant.
  * x [rows, cols] bf16 (ldx); gamma [cols] bf16 or NULL; rstd out [rows] fp32;
  * ws of fp8_rmsnorm_quant_workspace_bytes(rows, cols) bytes, 16-byte aligned.
  * Empty tensors are valid (scale 1, amax 0). */
