@@ -330,9 +330,9 @@ def bench_mlp(args) -> int:
         "kernels": kernels,
         "quantize": {"what": f"fp8_amax_quant of a [{M}, {h}] bf16 tensor (the dH shape) to E5M2 codes in one "
                              "pass (amax, grid-wide wait, cast); algorithmic bytes of the two passes: the amax "
-                             "reads 2 B/elem, the cast 2 B read + 1 B written per element; the kernel holds 21 "
-                             "chunks of 8 values per thread in registers across the wait and reads only the "
-                             "rest again (traffic: the counters)",
+                             "reads 2 B/elem, the cast 2 B read + 1 B written per element; the kernel holds 28 "
+                             "chunks of 8 values per thread on chip (19 in registers, 9 in LDS) across the "
+                             "wait and reads only the rest again (traffic: the counters)",
                      "bound": "hbm", "achieved_GBps": round(q_gbs, 1), "peak_GBps": PEAK_HBM_GBS,
                      "frac": round(q_gbs / PEAK_HBM_GBS, 4), "us": round(us["quantise_MxH"], 2),
                      "algorithmic_bytes": q_bytes,

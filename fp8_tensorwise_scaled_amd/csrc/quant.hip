@@ -22,8 +22,9 @@
 // One pass per batch where every tensor is dense, 16-byte aligned and wants
 // codes only and the batch is large enough to fill the CUs (the 3.8B-model
 // block's inputs, weights and dY; the LM head's): one grid reads each
-// tensor once for its amax, keeping the first 21 chunks of 8 values per
-// thread in registers (about 88 MB over the 256 CUs' register files), waits
+// tensor once for its amax, keeping the first 28 chunks of 8 values per
+// thread on chip, 19 in registers and 9 in LDS (about 117 MB over the 256
+// CUs' register files and LDS), waits
 // at one grid-wide barrier, and casts the held chunks without reading them
 // again; only the rest is read a second time.  Same amax, same scale, same
 // element-wise cast: the codes are those of the two launches.
@@ -613,7 +614,7 @@ __global__ void __launch_bounds__(kCastThreads) cast_kernel(QuantBatch b) {
 // claimed, bits 15-28 the block that processes it, bits 0-14 the max |x| as
 // bf16 magnitude bits.  Block u claims unit u with a compare-and-swap on its
 // slot and holds it: the first kResChunks chunks per thread stay in
-// registers.  It publishes the unit's max with one agent-scope atomic store,
+// registers and the next kLdsChunks in LDS.  It publishes the unit's max with one agent-scope atomic store,
 // so no cache-wide fence is needed, and waits until every slot has arrived.
 // A waiting block that finds a unit still unclaimed (its block has not
 // started) claims and processes it itself, without holding it, so the wait
@@ -621,7 +622,9 @@ __global__ void __launch_bounds__(kCastThreads) cast_kernel(QuantBatch b) {
 // casts the chunks it holds from registers and reads again the rest of each
 // unit it processed.
 constexpr int kResThreads = 512;
-constexpr int kResChunks = 21;
+constexpr int kResChunks = 19;             // held in registers per thread
+constexpr int kLdsChunks = 9;              // held in LDS per thread (72 KB per block, two blocks per CU)
+constexpr int kHeldChunks = kResChunks + kLdsChunks;
 constexpr uint32_t kSlotArrived = 0x80000000u, kSlotHeld = 0x40000000u, kSlotClaimed = 0x20000000u;
 constexpr int kSlotProcShift = 15;
 constexpr uint32_t kSlotProcMask = 0x3FFFu, kSlotMaxMask = 0x7FFFu;
@@ -705,6 +708,7 @@ template <int FMT>
 __global__ void __launch_bounds__(kResThreads) __attribute__((amdgpu_waves_per_eu(4)))
 quant_resident_kernel(QuantBatch b, int units, int spin_limit) {
   __shared__ uint32_t red[kResThreads / 64];
+  __shared__ v4u s_hold[kLdsChunks * kResThreads];  // thread t's LDS chunk j at j * kResThreads + t
   __shared__ int s_flag;
   __shared__ uint32_t s_jmax[kMaxJobs];
   __shared__ float s_scale[kMaxJobs], s_amax[kMaxJobs];
@@ -792,7 +796,29 @@ quant_resident_kernel(QuantBatch b, int units, int spin_limit) {
   const bool holds = s_flag != 0;
   if (holds) {
     const QuantJob& jb = b.job[held_job];
-    uint32_t m = stream_max(jb, held_local, kResChunks);
+    // the next kLdsChunks chunks go to LDS, three loads in flight, through
+    // the same descriptor as the held ones (offsets past the tensor load
+    // zeros)
+    const uint32_t nbytes = (uint32_t)(jb.rows * jb.cols * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(jb.x, nbytes);
+    const uint32_t s16 = (uint32_t)jb.nblocks * kResThreads * 16u;
+    const uint32_t o0 = ((uint32_t)held_local * kResThreads + tid) * 16u;
+    uint32_t m = 0;
+#pragma unroll 1
+    for (int g = 0; g < kLdsChunks; g += 3) {
+      v4u a[3];
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        a[r] = __builtin_amdgcn_raw_buffer_load_b128(rx, o0 + (kResChunks + g + r) * s16, 0, kNT);
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        s_hold[(g + r) * kResThreads + tid] = a[r];
+        const uint32_t t = absmax8(a[r]);
+        m = m > t ? m : t;
+      }
+    }
+    const uint32_t ms = stream_max(jb, held_local, kHeldChunks);
+    m = m > ms ? m : ms;
 #pragma unroll
     for (int k = 0; k < kResChunks; ++k) {
       const uint32_t t = absmax8(v[k]);
@@ -849,10 +875,25 @@ quant_resident_kernel(QuantBatch b, int units, int spin_limit) {
       }
       o += s16;
     }
-    if (all)
-      stream_cast(jb, held_local, kResChunks, d);
-    else
+    if (all) {
+      // the LDS chunks (each thread reads back only what it wrote), then
+      // the rest read again
+      const int64_t nch = jb.rows * jb.cols / 8;
+      v2u* qv = reinterpret_cast<v2u*>(jb.q);
+      const int64_t stride = (int64_t)jb.nblocks * kResThreads;
+      const int64_t i0 = (int64_t)held_local * kResThreads + tid;
+#pragma unroll 1
+      for (int j = 0; j < kLdsChunks; ++j) {
+        const int64_t i = i0 + (int64_t)(kResChunks + j) * stride;
+        if (i < nch) {
+          const v4u a = s_hold[j * kResThreads + tid];
+          qv[i] = v2u{quant4<FMT, kModePlain>(a[0], a[1], d), quant4<FMT, kModePlain>(a[2], a[3], d)};
+        }
+      }
+      stream_cast(jb, held_local, kHeldChunks, d);
+    } else {
       stream_nan(jb, held_local, kResChunks);
+    }
   }
   // units this block claimed while waiting: cast whole
   if (__syncthreads_or(stole)) {
