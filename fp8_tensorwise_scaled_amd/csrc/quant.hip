@@ -159,6 +159,20 @@ __device__ __forceinline__ uint32_t quant4_norm(uint32_t w0, uint32_t w1, float 
 
 template <int FMT, int MODE>
 __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const Divider& d) {
+  if constexpr (MODE == kModeRelu2) {
+    // cast_value<kModeRelu2> of the four values, the bf16 roundings two at a
+    // time (one v_cvt_pk_bf16_f32 per pair, the instruction a single
+    // conversion uses, so the values are the same)
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const float h0 = __builtin_fmaxf(__uint_as_float(w0 << 16), 0.0f);
+    const float h1 = __builtin_fmaxf(__uint_as_float(w0 & 0xFFFF0000u), 0.0f);
+    const float h2 = __builtin_fmaxf(__uint_as_float(w1 << 16), 0.0f);
+    const float h3 = __builtin_fmaxf(__uint_as_float(w1 & 0xFFFF0000u), 0.0f);
+    const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{h0 * h0, h1 * h1}, v2bf));
+    const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{h2 * h2, h3 * h3}, v2bf));
+    return pack4_fp8<FMT>(div_rn(d, __uint_as_float(p0 << 16)), div_rn(d, __uint_as_float(p0 & 0xFFFF0000u)),
+                          div_rn(d, __uint_as_float(p1 << 16)), div_rn(d, __uint_as_float(p1 & 0xFFFF0000u)));
+  }
   float a = div_rn(d, cast_value<MODE>(w0 & 0xFFFFu));
   float b = div_rn(d, cast_value<MODE>(w0 >> 16));
   float c = div_rn(d, cast_value<MODE>(w1 & 0xFFFFu));
